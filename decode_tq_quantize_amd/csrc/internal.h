@@ -1,0 +1,41 @@
+// Interfaces between the C-ABI layer (tq_api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+namespace tqk {
+
+// Tile sizes of the packed layouts (see tq.h).
+constexpr int kKeysTile = 16;
+constexpr int kValuesTile = 32;
+
+inline int planes_of(const tq_quantizer& q) { return q.mse_bits + (q.variant == TQ_PROD ? 1 : 0); }
+
+hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
+                           int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s);
+
+// Decode: workspace sizing and launch. Shapes are validated by the caller.
+struct DecodePlan {
+  int head_chunk;   // query heads per workgroup
+  int n_chunks;     // head chunks per KV head
+  int splits;       // sequence splits per (batch, KV head)
+  int split_len;    // tokens per split (multiple of 256)
+  int D;            // key channels
+  int Dv;           // value channels
+  size_t qprep_floats;
+  size_t partial_floats;
+};
+DecodePlan plan_decode(const tq_kv_desc& k, const tq_kv_desc& v, int B, int Hq, int Hkv, int T_max);
+hipError_t launch_decode(const tq_kv_desc& k, const tq_kv_desc& v, const void* q, tq_dtype qdt, int B, int Hq,
+                         int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out, float* scores_out,
+                         void* ws, const DecodePlan& plan, hipStream_t s);
+
+// Search.
+size_t search_workspace_bytes(const tq_group& db, int64_t N, int Q, int k);
+hipError_t launch_search(const tq_group& db, int64_t N, const float* queries, int Q, int k, int64_t* out_idx,
+                         float* out_score, void* ws, hipStream_t s);
+
+}  // namespace tqk

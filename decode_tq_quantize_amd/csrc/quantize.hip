@@ -1,0 +1,226 @@
+// Online TurboQuant compression of KV vectors (gfx950).
+//
+// riverfrot "TurboQuant" post, section 4.1: x~ = R (x / |x|) with a random
+// orthogonal R; section 4.2: each coordinate is mapped to the index of the
+// Lloyd-Max interval it falls in (boundaries compared, codebook looked up);
+// section 4.3: the residual r~ = x~ - c[idx] is projected with a Gaussian
+// matrix S and only the signs are kept (1 bit each), together with |r~|.
+//
+// One workgroup quantises a tile of TV vectors. The tile is staged in LDS
+// coordinate-major; each d x d product is computed as a tile GEMM in fp32
+// FMA (fp32 accumulation, fixed summation order j = 0..d-1) with the matrix
+// streamed through LDS in 128 x 32 chunks. Codes, signs and norms are then
+// packed into the requested layout with one word per thread.
+#include "device_common.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kIC = 128;       // output coordinates per chunk (one per thread column)
+constexpr int kJC = 32;        // input coordinates per chunk
+constexpr int kMtStride = kIC + 1;
+
+struct QArgs {
+  const void* x;
+  int64_t n;
+  int64_t stride;
+  int bf16;
+  const float* R;
+  const float* S;
+  int d;
+  int B;
+  int prod;
+  int layout;
+  float cent[TQ_MAX_LEVELS];
+  float thr[TQ_MAX_LEVELS - 1];
+  uint32_t* packed;
+  uint16_t* norm;
+  uint16_t* rnorm;
+};
+
+// Out[j][v] = sum_k M[j][k] In[k][v] for the TV vectors of the tile (arrays
+// coordinate-major, row stride TV). Thread (ii, vh) owns output coordinate
+// i0 + ii of vectors vh*TV/2 .. vh*TV/2 + TV/2 - 1.
+template <int TV>
+__device__ void matvec_tile(const float* __restrict__ M, int d, const float* In, float* Out, float* Mt) {
+  const int tid = threadIdx.x;
+  const int ii = tid % kIC;
+  const int vh = tid / kIC;
+  constexpr int VH = TV / 2;
+  for (int i0 = 0; i0 < d; i0 += kIC) {
+    float acc[VH];
+#pragma unroll
+    for (int k = 0; k < VH; ++k) acc[k] = 0.f;
+    for (int j0 = 0; j0 < d; j0 += kJC) {
+      __syncthreads();
+      for (int e = tid; e < kIC * kJC; e += kThreads) {
+        const int r = e / kJC, jj = e % kJC;
+        const int i = i0 + r;
+        Mt[jj * kMtStride + r] = (i < d) ? M[(int64_t)i * d + j0 + jj] : 0.f;
+      }
+      __syncthreads();
+      if (i0 + ii < d) {
+        for (int jj = 0; jj < kJC; ++jj) {
+          const float m = Mt[jj * kMtStride + ii];
+          const float* in = In + (j0 + jj) * TV + vh * VH;
+#pragma unroll
+          for (int k = 0; k < VH; ++k) acc[k] = fmaf(m, in[k], acc[k]);
+        }
+      }
+    }
+    if (i0 + ii < d) {
+#pragma unroll
+      for (int k = 0; k < VH; ++k) Out[(i0 + ii) * TV + vh * VH + k] = acc[k];
+    }
+  }
+  __syncthreads();
+}
+
+template <int TV>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QArgs a) {
+  extern __shared__ float smem[];
+  __shared__ float nrm[TV], rho[TV];
+  __shared__ float cent[TQ_MAX_LEVELS], thr[TQ_MAX_LEVELS];
+  const int d = a.d;
+  float* Mt = smem;
+  float* In = Mt + kJC * kMtStride;
+  float* Out = In + d * TV;
+  uint8_t* C = reinterpret_cast<uint8_t*>(Out + d * TV);
+  const int tid = threadIdx.x, lane = tid % tqd::kWave, wv = tid / tqd::kWave;
+  const int64_t v0 = (int64_t)blockIdx.x * TV;
+  const int L = 1 << a.B;
+
+  if (tid < TQ_MAX_LEVELS) {
+    cent[tid] = a.cent[tid];
+    thr[tid] = tid < TQ_MAX_LEVELS - 1 ? a.thr[tid] : 0.f;
+  }
+  // 1. load the tile, coordinate-major (vectors past n are zero)
+  for (int e = tid; e < TV * d; e += kThreads) {
+    const int v = e / d, j = e % d;
+    const int64_t gv = v0 + v;
+    In[j * TV + v] = gv < a.n ? tqd::load_elem(a.x, gv * a.stride + j, a.bf16) : 0.f;
+  }
+  __syncthreads();
+  // 2. norms
+  for (int v = wv; v < TV; v += kThreads / tqd::kWave) {
+    float s = 0.f;
+    for (int j = lane; j < d; j += tqd::kWave) s = fmaf(In[j * TV + v], In[j * TV + v], s);
+    s = tqd::wave_sum(s);
+    if (lane == 0) nrm[v] = sqrtf(s);
+  }
+  // 3. rotation (unnormalised: R x, divided by |x| below)
+  matvec_tile<TV>(a.R, d, In, Out, Mt);
+  // 4. codes; the rotated residual replaces the input tile
+  for (int e = tid; e < TV * d; e += kThreads) {
+    const int v = e % TV;
+    const float n = nrm[v];
+    const float u = n > 0.f ? Out[e] / n : 0.f;
+    int idx = 0;
+    for (int k = 0; k < L - 1; ++k) idx += (u >= thr[k]) ? 1 : 0;
+    if (!(n > 0.f)) idx = L / 2;
+    C[e] = (uint8_t)idx;
+    In[e] = n > 0.f ? u - cent[idx] : 0.f;
+  }
+  __syncthreads();
+  if (a.prod) {
+    for (int v = wv; v < TV; v += kThreads / tqd::kWave) {
+      float s = 0.f;
+      for (int j = lane; j < d; j += tqd::kWave) s = fmaf(In[j * TV + v], In[j * TV + v], s);
+      s = tqd::wave_sum(s);
+      if (lane == 0) rho[v] = sqrtf(s);
+    }
+    // 5. QJL projection of the residual; keep the signs (sign(0) -> +)
+    matvec_tile<TV>(a.S, d, In, Out, Mt);
+    for (int e = tid; e < TV * d; e += kThreads) {
+      const int v = e % TV;
+      const bool z = (Out[e] >= 0.f) || !(nrm[v] > 0.f);
+      C[e] |= (uint8_t)(z ? 16 : 0);
+    }
+    __syncthreads();
+  }
+  // 6. pack
+  const int P = a.B + a.prod;
+  if (a.layout == TQ_LAYOUT_KEYS) {
+    const int G = d / 32;
+    const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
+    for (int e = tid; e < TV * G * P; e += kThreads) {
+      const int p = e % P, g = (e / P) % G, v = e / (P * G);
+      const int64_t gv = v0 + v;
+      if (gv >= nround) continue;
+      uint32_t w = 0;
+      if (gv < a.n) {
+        const int sh = p < a.B ? p : 4;
+        for (int i = 0; i < 32; ++i) w |= (uint32_t)((C[(32 * g + i) * TV + v] >> sh) & 1) << i;
+      }
+      const int64_t tile = gv / tqk::kKeysTile;
+      const int t = (int)(gv % tqk::kKeysTile);
+      a.packed[((tile * G + g) * tqk::kKeysTile + t) * P + p] = w;
+    }
+  } else {
+    // TV == 32 == the values tile; v0 is tile aligned
+    const int64_t tile = v0 / tqk::kValuesTile;
+    for (int e = tid; e < d * P; e += kThreads) {
+      const int p = e % P, j = e / P;
+      const int sh = p < a.B ? p : 4;
+      uint32_t w = 0;
+      for (int v = 0; v < TV; ++v)
+        if (v0 + v < a.n) w |= (uint32_t)((C[j * TV + v] >> sh) & 1) << v;
+      a.packed[(tile * d + j) * P + p] = w;
+    }
+  }
+  // 7. norms as IEEE half
+  for (int v = tid; v < TV; v += kThreads) {
+    const int64_t gv = v0 + v;
+    if (gv < a.n) {
+      a.norm[gv] = tqd::f32_to_half_bits(nrm[v]);
+      if (a.prod) a.rnorm[gv] = tqd::f32_to_half_bits(rho[v]);
+    }
+  }
+}
+
+size_t lds_bytes(int d, int TV) { return (size_t)(kJC * kMtStride + 2 * d * TV) * 4 + (size_t)d * TV; }
+
+template <int TV>
+hipError_t launch_tv(const QArgs& a, int64_t nround, hipStream_t s) {
+  const size_t lds = lds_bytes(a.d, TV);
+  hipError_t e = hipFuncSetAttribute((const void*)quantize_kernel<TV>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = (nround + TV - 1) / TV;
+  hipLaunchKernelGGL(quantize_kernel<TV>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace tqk {
+
+hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
+                           int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s) {
+  QArgs a{};
+  a.x = x;
+  a.n = n;
+  a.stride = stride;
+  a.bf16 = dt == TQ_BF16;
+  a.R = q.R;
+  a.S = q.S;
+  a.d = q.d;
+  a.B = q.mse_bits;
+  a.prod = q.variant == TQ_PROD;
+  a.layout = layout;
+  for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = q.centroids[i];
+  for (int i = 0; i < TQ_MAX_LEVELS - 1; ++i) a.thr[i] = q.thresholds[i];
+  a.packed = static_cast<uint32_t*>(packed);
+  a.norm = norm;
+  a.rnorm = rnorm;
+  const int tile = layout == TQ_LAYOUT_KEYS ? kKeysTile : kValuesTile;
+  const int64_t nround = (n + tile - 1) / tile * tile;
+  const size_t limit = 150 * 1024;
+  if (layout == TQ_LAYOUT_VALUES || lds_bytes(q.d, 32) <= limit) return launch_tv<32>(a, nround, s);
+  if (lds_bytes(q.d, 16) <= limit) return launch_tv<16>(a, nround, s);
+  if (lds_bytes(q.d, 8) <= limit) return launch_tv<8>(a, nround, s);
+  return launch_tv<4>(a, nround, s);
+}
+
+}  // namespace tqk

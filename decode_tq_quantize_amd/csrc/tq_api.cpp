@@ -1,0 +1,166 @@
+// libtq C ABI: argument validation, workspace sizing and kernel dispatch.
+// Every check runs before the first device call; on error nothing is written.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "internal.h"
+#include "tq.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape, pointer and codebook checks of one quantiser.
+int check_quantizer(const tq_quantizer* q) {
+  if (!q) return TQ_ERR_INVALID_ARG;
+  if (q->d < 32 || q->d > TQ_MAX_DIM || (q->d % 32) != 0) return TQ_ERR_UNSUPPORTED;
+  if (q->mse_bits < 1 || q->mse_bits > TQ_MAX_MSE_BITS) return TQ_ERR_UNSUPPORTED;
+  if (q->variant != TQ_MSE && q->variant != TQ_PROD) return TQ_ERR_INVALID_ARG;
+  if (!q->R || (q->variant == TQ_PROD && !q->S)) return TQ_ERR_INVALID_ARG;
+  if (!aligned16(q->R) || (q->S && !aligned16(q->S))) return TQ_ERR_MISALIGNED;
+  const int L = 1 << q->mse_bits;
+  for (int i = 0; i < L; ++i) {
+    if (!std::isfinite(q->centroids[i])) return TQ_ERR_INVALID_ARG;
+    if (i > 0 && !(q->centroids[i] > q->centroids[i - 1])) return TQ_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < L - 1; ++i) {
+    if (!std::isfinite(q->thresholds[i])) return TQ_ERR_INVALID_ARG;
+    if (i > 0 && !(q->thresholds[i] > q->thresholds[i - 1])) return TQ_ERR_INVALID_ARG;
+  }
+  return TQ_OK;
+}
+
+// The estimator kernels rely on the mirror symmetry of the codebook.
+bool symmetric(const tq_quantizer& q) {
+  const int L = 1 << q.mse_bits;
+  for (int i = 0; i < L; ++i)
+    if (q.centroids[i] != -q.centroids[L - 1 - i]) return false;
+  return true;
+}
+
+int check_desc(const tq_kv_desc* k, bool values, int* total_d) {
+  if (!k || k->n_groups < 1 || k->n_groups > TQ_MAX_GROUPS) return TQ_ERR_INVALID_ARG;
+  int ch = 0;
+  for (int i = 0; i < k->n_groups; ++i) {
+    const tq_group& g = k->g[i];
+    int rc = check_quantizer(&g.q);
+    if (rc != TQ_OK) return rc;
+    if (!symmetric(g.q)) return TQ_ERR_INVALID_ARG;
+    if (g.ch_offset != ch) return TQ_ERR_INVALID_ARG;
+    if (values && g.q.variant != TQ_MSE) return TQ_ERR_UNSUPPORTED;
+    if (!g.packed || !g.norm || (g.q.variant == TQ_PROD && !g.rnorm)) return TQ_ERR_INVALID_ARG;
+    if (!aligned16(g.packed) || !aligned16(g.norm) || (g.rnorm && !aligned16(g.rnorm))) return TQ_ERR_MISALIGNED;
+    if (g.seq_stride <= 0 || (g.seq_stride % tqk::kValuesTile) != 0) return TQ_ERR_INVALID_ARG;
+    ch += g.q.d;
+  }
+  *total_d = ch;
+  return TQ_OK;
+}
+
+int check_decode(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq, int Hkv, int T_max, int* D, int* Dv) {
+  int rc = check_desc(k, false, D);
+  if (rc != TQ_OK) return rc;
+  rc = check_desc(v, true, Dv);
+  if (rc != TQ_OK) return rc;
+  if (*D > 256 || *Dv > 256) return TQ_ERR_UNSUPPORTED;
+  if (B < 1 || Hq < 1 || Hkv < 1 || (Hq % Hkv) != 0 || T_max < 1) return TQ_ERR_INVALID_ARG;
+  for (int i = 0; i < k->n_groups; ++i)
+    if (k->g[i].seq_stride < T_max) return TQ_ERR_INVALID_ARG;
+  for (int i = 0; i < v->n_groups; ++i)
+    if (v->g[i].seq_stride < T_max) return TQ_ERR_INVALID_ARG;
+  return TQ_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" const char* tq_status_string(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported dimension or bit width";
+    case TQ_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case TQ_ERR_NO_CONVERGE: return "Lloyd-Max iteration did not converge";
+    case TQ_ERR_HIP: return "HIP launch failed";
+    case TQ_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+extern "C" size_t tq_packed_bytes(int d, int mse_bits, tq_variant variant, tq_layout layout, int64_t n) {
+  if (d < 32 || d > TQ_MAX_DIM || (d % 32) != 0 || mse_bits < 1 || mse_bits > TQ_MAX_MSE_BITS || n < 0) return 0;
+  if (variant != TQ_MSE && variant != TQ_PROD) return 0;
+  if (layout != TQ_LAYOUT_KEYS && layout != TQ_LAYOUT_VALUES) return 0;
+  const int P = mse_bits + (variant == TQ_PROD ? 1 : 0);
+  const int64_t tile = layout == TQ_LAYOUT_KEYS ? tqk::kKeysTile : tqk::kValuesTile;
+  const int64_t nr = (n + tile - 1) / tile * tile;
+  return (size_t)nr * (size_t)P * (size_t)d / 8;
+}
+
+extern "C" int tq_quantize_kv(const tq_quantizer* q, tq_layout layout, tq_dtype in_dtype, const void* x, int64_t n,
+                              int64_t x_stride_elems, void* packed, uint16_t* norm, uint16_t* rnorm, void* stream) {
+  int rc = check_quantizer(q);
+  if (rc != TQ_OK) return rc;
+  if (layout != TQ_LAYOUT_KEYS && layout != TQ_LAYOUT_VALUES) return TQ_ERR_INVALID_ARG;
+  if (in_dtype != TQ_F32 && in_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (n < 0 || x_stride_elems < q->d) return TQ_ERR_INVALID_ARG;
+  if (layout == TQ_LAYOUT_VALUES && q->d > 256) return TQ_ERR_UNSUPPORTED;
+  if (n == 0) return TQ_OK;
+  if (!x || !packed || !norm || (q->variant == TQ_PROD && !rnorm)) return TQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(norm) || (rnorm && !aligned16(rnorm)))
+    return TQ_ERR_MISALIGNED;
+  return hip_status(tqk::launch_quantize(*q, layout, in_dtype, x, n, x_stride_elems, packed, norm,
+                                         q->variant == TQ_PROD ? rnorm : nullptr,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+extern "C" size_t tq_decode_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq, int Hkv,
+                                            int T_max) {
+  int D = 0, Dv = 0;
+  if (check_decode(k, v, B, Hq, Hkv, T_max, &D, &Dv) != TQ_OK) return 0;
+  const tqk::DecodePlan p = tqk::plan_decode(*k, *v, B, Hq, Hkv, T_max);
+  return (p.qprep_floats + p.partial_floats) * sizeof(float);
+}
+
+extern "C" int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype, int B,
+                              int Hq, int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out,
+                              float* scores_out, void* ws, size_t ws_bytes, void* stream) {
+  int D = 0, Dv = 0;
+  int rc = check_decode(k, v, B, Hq, Hkv, T_max, &D, &Dv);
+  if (rc != TQ_OK) return rc;
+  if (!q || !out) return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || (scores_out && !aligned16(scores_out)) ||
+      (seq_lens && !aligned16(seq_lens)) || (ws && !aligned16(ws)))
+    return TQ_ERR_MISALIGNED;
+  const tqk::DecodePlan p = tqk::plan_decode(*k, *v, B, Hq, Hkv, T_max);
+  if (!ws || ws_bytes < (p.qprep_floats + p.partial_floats) * sizeof(float)) return TQ_ERR_WORKSPACE;
+  return hip_status(tqk::launch_decode(*k, *v, q, q_dtype, B, Hq, Hkv, T_max, seq_lens, scale, out, scores_out,
+                                       ws, p, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" size_t tq_search_workspace_bytes(const tq_group* db, int64_t N, int Q, int k) {
+  if (!db || check_quantizer(&db->q) != TQ_OK || N < 1 || Q < 1 || k < 1 || k > 64 || k > N) return 0;
+  return tqk::search_workspace_bytes(*db, N, Q, k);
+}
+
+extern "C" int tq_search_topk(const tq_group* db, int64_t N, const float* queries, int Q, int k, int64_t* out_idx,
+                              float* out_score, void* ws, size_t ws_bytes, void* stream) {
+  if (!db) return TQ_ERR_INVALID_ARG;
+  int rc = check_quantizer(&db->q);
+  if (rc != TQ_OK) return rc;
+  if (!symmetric(db->q)) return TQ_ERR_INVALID_ARG;
+  if (N < 1 || Q < 1 || k < 1 || k > 64 || k > N) return TQ_ERR_INVALID_ARG;
+  if (!db->packed || !db->norm || (db->q.variant == TQ_PROD && !db->rnorm) || !queries || !out_idx || !out_score)
+    return TQ_ERR_INVALID_ARG;
+  if (!aligned16(db->packed) || !aligned16(db->norm) || (db->rnorm && !aligned16(db->rnorm)) ||
+      !aligned16(queries) || !aligned16(out_idx) || !aligned16(out_score) || (ws && !aligned16(ws)))
+    return TQ_ERR_MISALIGNED;
+  if (!ws || ws_bytes < tqk::search_workspace_bytes(*db, N, Q, k)) return TQ_ERR_WORKSPACE;
+  return hip_status(tqk::launch_search(*db, N, queries, Q, k, out_idx, out_score, ws,
+                                       static_cast<hipStream_t>(stream)));
+}

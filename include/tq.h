@@ -1,0 +1,192 @@
+/*
+ * libtq — TurboQuant KV-cache compression, compressed-KV decode attention and
+ * inner-product search for AMD MI355X (gfx950).
+ *
+ * The method (riverfrot "TurboQuant" post, sections 4.1-4.3; uiyeonassociation
+ * "TurboQuant" post, two-stage compression): a vector x is stored as its norm
+ * n = |x|, the Lloyd-Max codes of the rotated unit vector x~ = R (x / n), and —
+ * for the inner-product ("PROD") variant — the norm rho of the rotated
+ * residual r~ = x~ - c[idx] plus the signs of S r~ (the QJL sketch). The
+ * inner product with an unquantised y is then estimated without bias as
+ *
+ *     <y, x>  ~  n * ( <R y, c[idx]> + gamma * rho * <S R y, 2 z - 1> ),
+ *     gamma = sqrt(pi / 2) / d.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All device buffers are owned by the caller; libtq never allocates device
+ *    memory and keeps no mutable global state, so calls are thread-safe.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *    device entry point only enqueues work on it and returns; nothing
+ *    synchronises.
+ *  - Validation happens before any device call; on error nothing is written
+ *    and the return value is negative (see tq_status). No C++ exception
+ *    crosses the ABI.
+ *  - Device base pointers must be 16-byte aligned (TQ_ERR_MISALIGNED).
+ *  - Inputs must be finite; this is a precondition, not checked on the GPU.
+ *    Norms must stay below 65504 (they are stored as IEEE half).
+ *
+ * Packed layouts (this library's own; the pages only require that no
+ * per-block scale or zero-point be stored, riverfrot section 4.2). A code of
+ * B bits is stored as B bit-planes (plane p = bit p of the code, LSB first);
+ * PROD adds one sign plane (p = B, bit = 1 when (S r~)_j >= 0). P = B + [PROD].
+ *  - TQ_LAYOUT_KEYS (coordinate-contiguous; keys and search databases):
+ *    tiles of 16 vectors; uint32 word index ((tile * d/32 + g) * 16 + t) * P + p
+ *    holds coordinates 32 g .. 32 g + 31 (bit i = coordinate 32 g + i) of
+ *    vector 16 tile + t.
+ *  - TQ_LAYOUT_VALUES (token-contiguous; values): tiles of 32 vectors;
+ *    word index (tile * d + j) * P + p holds coordinate j of vectors
+ *    32 tile .. 32 tile + 31 (bit i = vector 32 tile + i).
+ *  Vectors past n in the last tile are all-zero bits. Norms are separate
+ *  arrays of IEEE half (uint16 bits), one per vector.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = -1,  /* null pointer, negative size, inconsistent shapes */
+  TQ_ERR_UNSUPPORTED = -2,  /* d not a multiple of 32 or out of range, bits out of range */
+  TQ_ERR_MISALIGNED = -3,   /* a device base pointer is not 16-byte aligned */
+  TQ_ERR_NO_CONVERGE = -4,  /* Lloyd-Max did not converge within max_iter */
+  TQ_ERR_HIP = -5,          /* a HIP launch failed */
+  TQ_ERR_WORKSPACE = -6     /* workspace missing or smaller than the size query says */
+} tq_status;
+
+typedef enum { TQ_MSE = 0, TQ_PROD = 1 } tq_variant;
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+typedef enum { TQ_LAYOUT_KEYS = 0, TQ_LAYOUT_VALUES = 1 } tq_layout;
+
+#define TQ_MAX_MSE_BITS 4
+#define TQ_MAX_LEVELS 16
+#define TQ_MAX_GROUPS 4
+#define TQ_MAX_DIM 2048
+
+/* One quantiser (riverfrot sections 4.1-4.3). The codebook is held by value
+ * (ascending, 2^mse_bits centroids and 2^mse_bits - 1 thresholds; entries past
+ * those are ignored); R and S are device pointers to d x d row-major fp32
+ * matrices owned by the caller (R orthogonal, S i.i.d. N(0,1); S is NULL for
+ * TQ_MSE). The decode and search kernels require the mirror-symmetric
+ * codebook tq_quantizer_init produces (c_i = -c_{L-1-i}). */
+typedef struct {
+  int d;             /* vector dimension: multiple of 32, 32..2048 */
+  int mse_bits;      /* B: Lloyd-Max bits per coordinate, 1..4 */
+  tq_variant variant;
+  const float* R;
+  const float* S;
+  float centroids[TQ_MAX_LEVELS];
+  float thresholds[TQ_MAX_LEVELS - 1];
+} tq_quantizer;
+
+/* One channel group of a compressed KV cache: channels
+ * [ch_offset, ch_offset + q.d) of every head vector, quantised by q.
+ * Sequence (b, kv_head) starts at vector (b * Hkv + kv_head) * seq_stride;
+ * token t of it is vector (b * Hkv + kv_head) * seq_stride + t in `packed`
+ * (layout TQ_LAYOUT_KEYS for keys, TQ_LAYOUT_VALUES for values), `norm` and
+ * `rnorm`. seq_stride must be a multiple of 32. */
+typedef struct {
+  tq_quantizer q;
+  int ch_offset;
+  const void* packed;
+  const uint16_t* norm;   /* half |x| per vector */
+  const uint16_t* rnorm;  /* half rho per vector (PROD), NULL for MSE */
+  int64_t seq_stride;
+} tq_group;
+
+/* A compressed K or V cache: 1..TQ_MAX_GROUPS groups tiling the head
+ * channels 0..D-1 in order (config "outlier 32 channels at 3 bits, the rest at
+ * 2 bits" is two groups after the caller permutes the outlier channels first). */
+typedef struct {
+  int n_groups;
+  tq_group g[TQ_MAX_GROUPS];
+} tq_kv_desc;
+
+/* ---------------------------------------------------------------- host only */
+
+/* Lloyd-Max codebook for the marginal of one coordinate of a uniformly
+ * random unit vector in R^d, f_d(x) ~ (1 - x^2)^((d-3)/2) on [-1, 1]
+ * (riverfrot section 4.1: rotated coordinates follow one Beta-type law;
+ * section 4.2: Lloyd-Max takes the density and 2^b levels and returns the
+ * boundaries {t_i} and representatives {c_i}, computed once per (d, b)).
+ * Writes 2^mse_bits ascending centroids and 2^mse_bits - 1 thresholds (the
+ * midpoints), mirror-symmetric, and optionally the total squared error D of
+ * a unit vector. max_iter = 0 selects the default (200000). Host pointers.
+ * Errors: INVALID_ARG (null outputs), UNSUPPORTED (d < 3 or > 2048, bits
+ * outside 1..4), NO_CONVERGE. */
+int tq_build_codebook(int d, int mse_bits, double* centroids, double* thresholds,
+                      double* mse_out, int max_iter);
+
+/* Fill *q: d, bits, variant, the device pointers R and S (not dereferenced
+ * here), and the fp32-rounded codebook of tq_build_codebook. */
+int tq_quantizer_init(tq_quantizer* q, int d, int mse_bits, tq_variant variant,
+                      const float* R, const float* S);
+
+/* Bytes of the packed codes of n vectors in `layout`, including the padding
+ * of the last tile: ceil(n / tile) * tile * P * d / 8. 0 on bad arguments. */
+size_t tq_packed_bytes(int d, int mse_bits, tq_variant variant, tq_layout layout, int64_t n);
+
+/* Human-readable text for a tq_status value. */
+const char* tq_status_string(int status);
+
+/* ------------------------------------------------------------ device calls */
+
+/* Quantise n vectors x[i * x_stride_elems + 0 .. d-1] (fp32 or bf16, device)
+ * (riverfrot sections 4.1-4.3, the online compression of each new K/V vector):
+ *   n_i = |x_i|; x~ = R x_i / n_i; idx_j = #{k : x~_j >= t_k};
+ *   PROD: r~ = x~ - c[idx], rho_i = |r~|, z_j = [(S r~)_j >= 0].
+ * A zero vector stores n = 0, rho = 0, codes 2^B / 2 and signs 1.
+ * Outputs (device): `packed` (tq_packed_bytes bytes, layout as above; it must
+ * start at a tile boundary of the cache it belongs to), `norm` [n] half,
+ * `rnorm` [n] half (PROD only; NULL for MSE). TQ_LAYOUT_VALUES needs d <= 512.
+ * Contractions accumulate in fp32. */
+int tq_quantize_kv(const tq_quantizer* q, tq_layout layout, tq_dtype in_dtype,
+                   const void* x, int64_t n, int64_t x_stride_elems, void* packed,
+                   uint16_t* norm, uint16_t* rnorm, void* stream);
+
+/* Workspace bytes tq_decode_attn needs for these shapes (0 on bad arguments). */
+size_t tq_decode_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq,
+                                 int Hkv, int T_max);
+
+/* Decode attention straight from the compressed cache (riverfrot sections
+ * 2.2-2.3: the new query attends to every cached token, softmax(q K^T /
+ * sqrt(d)) V; section 4.3: scores from the unbiased estimator with the query
+ * unquantised; GQA: query head h reads KV head h / (Hq / Hkv)).
+ *   q        [B, Hq, D] fp32 or bf16, D = total key channels (<= 256)
+ *   seq_lens [B] int32 device, or NULL for T_max everywhere (0 <= len <= T_max)
+ *   scale    logit scale, normally 1/sqrt(D)
+ *   out      [B, Hq, Dv] fp32: sum_t softmax_t(scale * s_t) * v^_t with
+ *            v^_t = n_t R_v^T c_v[idx_t] per value group (zeros if len = 0)
+ *   scores_out NULL or [B, Hq, T_max] fp32: the raw estimates s_t (t < len)
+ *   ws, ws_bytes: device workspace of at least tq_decode_workspace_bytes.
+ * Keys must use TQ_LAYOUT_KEYS, values TQ_LAYOUT_VALUES and TQ_MSE.
+ * Accumulation is fp32; results match an fp64 evaluation to about 1e-4
+ * relative (normwise). */
+int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype,
+                   int B, int Hq, int Hkv, int T_max, const int32_t* seq_lens, float scale,
+                   float* out, float* scores_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes tq_search_topk needs. */
+size_t tq_search_workspace_bytes(const tq_group* db, int64_t N, int Q, int k);
+
+/* Top-k database vectors by estimated inner product with each query
+ * (uiyeonassociation post: TurboQuant codes used for vector search).
+ *   db        one group, TQ_LAYOUT_KEYS, seq_stride ignored (vectors 0..N-1)
+ *   queries   [Q, d] fp32 device
+ *   out_idx   [Q, k] int64, out_score [Q, k] fp32: descending score, equal
+ *             scores in ascending index order. 1 <= k <= 64, k <= N.
+ * Scores are the same estimator as decode, accumulated in fp32. */
+int tq_search_topk(const tq_group* db, int64_t N, const float* queries, int Q, int k,
+                   int64_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,344 @@
+"""GPU parity of libtq against the fp64 oracle (calls go through the C ABI).
+
+Each kernel is checked element by element on seeded inputs at sizes that
+span several tiles and a ragged tail; decode and search are run both on
+oracle-packed inputs and on GPU-packed inputs decoded by the oracle's own
+unpacker, so a quantiser mismatch cannot hide a decode or search bug.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import tq as otq
+from parity import (REL_TOL, assert_codes_match, assert_topk_match, normwise_rel_err, rowmax_rel_err,
+                          torch_dev)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import decode_tq_quantize_amd as tq
+    tq.lib()  # fail loudly if the library is missing on a GPU machine
+
+
+def _variant(prod):
+    return tq.TQ_PROD if prod else tq.TQ_MSE
+
+
+class GpuQuantizer:
+    """Device copies of R and S plus the library quantiser that points at them."""
+
+    def __init__(self, d, B, prod, seed, r_stream=synth.STREAM_R, s_stream=synth.STREAM_S):
+        self.R32 = synth.haar_orthogonal(d, seed, r_stream)
+        self.S32 = synth.gaussian_matrix(d, d, seed, s_stream) if prod else None
+        self.Rt = torch_dev(self.R32)
+        self.St = torch_dev(self.S32) if prod else None
+        self.q = tq.tq_quantizer_init(d, B, _variant(prod), self.Rt, self.St)
+        self.d, self.B, self.prod = d, B, prod
+        self.oq = otq.make_quantizer(d, B, prod, self.R32, self.S32)
+
+
+def gpu_quantize(gq: GpuQuantizer, x_t, n, stride, layout, dtype):
+    nbytes = tq.tq_packed_bytes(gq.d, gq.B, _variant(gq.prod), layout, n)
+    packed = torch.full((nbytes // 4,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    norm = torch.zeros(n, dtype=torch.int16, device="cuda")
+    rnorm = torch.zeros(n, dtype=torch.int16, device="cuda") if gq.prod else None
+    tq.tq_quantize_kv(gq.q, layout, dtype, x_t, n, stride, packed, norm, rnorm)
+    return packed, norm, rnorm
+
+
+def to_np_u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def to_np_f16(t):
+    return None if t is None else t.cpu().numpy().view(np.float16)
+
+
+def lay_name(layout):
+    return "keys" if layout == tq.TQ_LAYOUT_KEYS else "values"
+
+
+# --------------------------------------------------------------------------
+# quantize
+# --------------------------------------------------------------------------
+
+QUANT_CASES = [
+    (128, 3, True, "keys", 1000, "bf16"),
+    (128, 2, True, "keys", 37, "f32"),
+    (128, 3, False, "values", 1000, "bf16"),
+    (32, 2, True, "keys", 100, "f32"),
+    (96, 1, True, "keys", 100, "bf16"),
+    (96, 2, False, "values", 77, "f32"),
+    (256, 4, True, "keys", 50, "f32"),
+    (64, 4, False, "values", 64, "bf16"),
+    (1536, 3, True, "keys", 40, "f32"),
+    (2048, 1, True, "keys", 5, "f32"),
+]
+
+
+@pytest.mark.parametrize("d,B,prod,lay,N,dt", QUANT_CASES)
+def test_quantize_matches_oracle(d, B, prod, lay, N, dt):
+    print(f"quantize d={d} B={B} prod={prod} {lay} N={N} {dt}", flush=True)
+    gq = GpuQuantizer(d, B, prod, seed=d + B)
+    x = synth.unit_gaussian(N, d, 11) * synth.rng(12, 0).lognormal(0, 0.5, (N, 1)).astype(np.float32)
+    x[min(3, N - 1)] = 0.0  # the zero-vector convention
+    if dt == "bf16":
+        x = synth.bf16_bits_to_f32(synth.to_bf16_bits(x))
+    layout = tq.TQ_LAYOUT_KEYS if lay == "keys" else tq.TQ_LAYOUT_VALUES
+    x_t = torch_dev(x, torch.bfloat16 if dt == "bf16" else torch.float32)
+    packed, norm, rnorm = gpu_quantize(gq, x_t, N, d, layout, tq.TQ_BF16 if dt == "bf16" else tq.TQ_F32)
+    torch.cuda.synchronize()
+    words = to_np_u32(packed)
+    idx, z = otq.unpack(words, N, d, B, prod, lay)
+    codes = otq.quantize(x.astype(np.float64), gq.oq)
+    assert_codes_match(idx, z, to_np_f16(norm), to_np_f16(rnorm), codes, gq.oq)
+    # padding vectors of the last tile are zero bits
+    tile = otq.KEYS_TILE if lay == "keys" else otq.VALUES_TILE
+    n_round = -(-N // tile) * tile
+    pidx, pz = otq.unpack(words, n_round, d, B, prod, lay)
+    assert not pidx[N:].any() and (pz is None or not pz[N:].any())
+
+
+def test_quantize_strided_channel_group():
+    # quantise channels 32..127 of 128-channel rows (a channel group)
+    N, D = 200, 128
+    gq = GpuQuantizer(96, 1, True, seed=5)
+    x = synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.rng(3, 0).standard_normal((N, D)).astype(np.float32)))
+    x_t = torch_dev(x, torch.bfloat16)
+    packed, norm, rnorm = gpu_quantize(gq, x_t[:, 32:], N, D, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16)
+    torch.cuda.synchronize()
+    idx, z = otq.unpack(to_np_u32(packed), N, 96, 1, True, "keys")
+    assert_codes_match(idx, z, to_np_f16(norm), to_np_f16(rnorm), otq.quantize(x[:, 32:].astype(np.float64), gq.oq),
+                       gq.oq)
+
+
+def test_quantize_is_deterministic():
+    gq = GpuQuantizer(128, 3, True, seed=1)
+    x_t = torch_dev(synth.unit_gaussian(4096, 128, 2))
+    a = gpu_quantize(gq, x_t, 4096, 128, tq.TQ_LAYOUT_KEYS, tq.TQ_F32)
+    b = gpu_quantize(gq, x_t, 4096, 128, tq.TQ_LAYOUT_KEYS, tq.TQ_F32)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+# --------------------------------------------------------------------------
+# decode attention
+# --------------------------------------------------------------------------
+
+class Cache:
+    """One compressed K or V channel group of a [B, Hkv, T_cap] cache, on the device."""
+
+    def __init__(self, gq: GpuQuantizer, ch, codes: otq.Codes, T_cap, layout):
+        B, H, T, d = codes.idx.shape
+        n_all = B * H * T_cap
+        idx = np.zeros((B, H, T_cap, d), np.uint8)
+        idx[:, :, :T] = codes.idx
+        z = None
+        if gq.prod:
+            z = np.zeros((B, H, T_cap, d), bool)
+            z[:, :, :T] = codes.z
+        n16 = np.zeros((B, H, T_cap), np.float16)
+        n16[:, :, :T] = codes.n16
+        r16 = np.zeros((B, H, T_cap), np.float16)
+        r16[:, :, :T] = codes.rho16
+        words = otq.pack(idx.reshape(n_all, d), None if z is None else z.reshape(n_all, d), gq.B, layout)
+        self.packed = torch_dev(words.view(np.int32))
+        self.norm = torch_dev(n16.reshape(-1).view(np.int16))
+        self.rnorm = torch_dev(r16.reshape(-1).view(np.int16)) if gq.prod else None
+        self.group = tq.make_group(gq.q, ch, self.packed, self.norm, self.rnorm, T_cap)
+
+
+def run_decode(kcaches, vcaches, qry, Hkv, T_cap, seq_lens, qdt, scores=True):
+    B, Hq, D = qry.shape
+    Dv = sum(c.group.q.d for c in vcaches)
+    kd = tq.make_desc([c.group for c in kcaches])
+    vd = tq.make_desc([c.group for c in vcaches])
+    ws_bytes = tq.tq_decode_workspace_bytes(kd, vd, B, Hq, Hkv, T_cap)
+    ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
+    q_t = torch_dev(qry.astype(np.float32), torch.bfloat16 if qdt == "bf16" else torch.float32)
+    out = torch.full((B, Hq, Dv), float("nan"), dtype=torch.float32, device="cuda")
+    sc = torch.full((B, Hq, T_cap), float("nan"), dtype=torch.float32, device="cuda") if scores else None
+    sl = torch_dev(np.asarray(seq_lens, np.int32)) if seq_lens is not None else None
+    tq.tq_decode_attn(kd, vd, q_t, tq.TQ_BF16 if qdt == "bf16" else tq.TQ_F32, B, Hq, Hkv, T_cap, sl,
+                      1.0 / math.sqrt(D), out, sc, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), None if sc is None else sc.cpu().numpy()
+
+
+def check_decode(out, sc, kgroups, vgroups, qry, Hkv, seq_lens):
+    B, Hq, D = qry.shape
+    o_out, o_sc = otq.decode_attention(qry.astype(np.float64), kgroups, vgroups, Hkv, seq_lens,
+                                       1.0 / math.sqrt(D))
+    lens = seq_lens if seq_lens is not None else [o_sc.shape[2]] * B
+    for b in range(B):
+        L = int(lens[b])
+        if L == 0:
+            assert np.all(out[b] == 0)
+            continue
+        e_out = normwise_rel_err(out[b], o_out[b])
+        assert e_out <= REL_TOL, f"batch {b}: output error {e_out}"
+        if sc is not None:
+            e_sc = rowmax_rel_err(sc[b, :, :L], o_sc[b, :, :L])
+            assert e_sc <= REL_TOL, f"batch {b}: score error {e_sc}"
+    return o_out, o_sc
+
+
+def make_kv(B, Hkv, T, d, seed):
+    K = synth.kv_with_outliers(B, Hkv, T, d, 4, 10.0, seed, synth.STREAM_DATA, synth.STREAM_OUTLIER)
+    V = synth.kv_with_outliers(B, Hkv, T, d, 4, 10.0, seed, synth.STREAM_NORM, synth.STREAM_R_V)
+    return K, V
+
+
+DECODE_CASES = [
+    # B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt
+    (2, 8, 2, 300, 320, [300, 123], 3, 3, "bf16"),
+    (1, 32, 8, 1024, 1024, None, 3, 3, "bf16"),
+    (3, 4, 1, 65, 96, [1, 64, 65], 2, 2, "f32"),
+    (2, 4, 2, 63, 64, [0, 63], 1, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,T_cap,seq_lens,kB,vB,qdt", DECODE_CASES)
+def test_decode_matches_oracle_on_oracle_packed_cache(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt):
+    print(f"decode B={B} Hq={Hq} Hkv={Hkv} T={T} lens={seq_lens}", flush=True)
+    d = 128
+    K, V = make_kv(B, Hkv, T, d, seed=T)
+    gk = GpuQuantizer(d, kB, True, seed=1)
+    gv = GpuQuantizer(d, vB, False, seed=2, r_stream=synth.STREAM_R_V)
+    ck, cv = otq.quantize(K, gk.oq), otq.quantize(V, gv.oq)
+    qry = synth.rng(T, 30).standard_normal((B, Hq, d)).astype(np.float32)
+    if qdt == "bf16":
+        qry = synth.bf16_bits_to_f32(synth.to_bf16_bits(qry))
+    kc = Cache(gk, 0, ck, T_cap, "keys")
+    vc = Cache(gv, 0, cv, T_cap, "values")
+    out, sc = run_decode([kc], [vc], qry, Hkv, T_cap, seq_lens, qdt)
+    check_decode(out, sc, [otq.Group(0, gk.oq, ck)], [otq.Group(0, gv.oq, cv)], qry, Hkv, seq_lens)
+
+
+@pytest.mark.parametrize("b_total", [2, 3, 4])
+def test_score_matrix_tiny_workload(b_total):
+    # 4096 unit keys, 64 unit queries, d = 128, TurboQuant_prod at b = 2, 3, 4
+    # (b - 1 MSE bits + 1 QJL bit), 64 x 4096 score matrix, seed 0.
+    d, N, Q = 128, 4096, 64
+    keys = synth.unit_gaussian(N, d, 0, synth.STREAM_DATA)
+    qry = synth.unit_gaussian(Q, d, 0, synth.STREAM_QUERY)
+    gk = GpuQuantizer(d, b_total - 1, True, seed=0)
+    gv = GpuQuantizer(d, 2, False, seed=0, r_stream=synth.STREAM_R_V)
+    ck = otq.quantize(keys[None, None], gk.oq)
+    cv = otq.quantize(keys[None, None], gv.oq)
+    kc = Cache(gk, 0, ck, N, "keys")
+    vc = Cache(gv, 0, cv, N, "values")
+    out, sc = run_decode([kc], [vc], qry[None], 1, N, None, "f32")
+    check_decode(out, sc, [otq.Group(0, gk.oq, ck)], [otq.Group(0, gv.oq, cv)], qry[None], 1, None)
+
+
+def test_decode_two_channel_groups():
+    # 2.5 bits per channel: 32 outlier channels (keys 2+1 bits, values 3 bits)
+    # and 96 others (keys 1+1, values 2), each group with its own norms.
+    B, Hq, Hkv, T, T_cap = 2, 8, 2, 200, 224
+    K, V = make_kv(B, Hkv, T, 128, seed=4)
+    ka, kb = GpuQuantizer(32, 2, True, 1), GpuQuantizer(96, 1, True, 2)
+    va, vb = GpuQuantizer(32, 3, False, 3), GpuQuantizer(96, 2, False, 4)
+    cka, ckb = otq.quantize(K[..., :32], ka.oq), otq.quantize(K[..., 32:], kb.oq)
+    cva, cvb = otq.quantize(V[..., :32], va.oq), otq.quantize(V[..., 32:], vb.oq)
+    qry = synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.rng(9, 0).standard_normal((B, Hq, 128)).astype(np.float32)))
+    kcs = [Cache(ka, 0, cka, T_cap, "keys"), Cache(kb, 32, ckb, T_cap, "keys")]
+    vcs = [Cache(va, 0, cva, T_cap, "values"), Cache(vb, 32, cvb, T_cap, "values")]
+    out, sc = run_decode(kcs, vcs, qry, Hkv, T_cap, [200, 150], "bf16")
+    check_decode(out, sc, [otq.Group(0, ka.oq, cka), otq.Group(32, kb.oq, ckb)],
+                 [otq.Group(0, va.oq, cva), otq.Group(32, vb.oq, cvb)], qry, Hkv, [200, 150])
+
+
+def test_decode_on_gpu_quantized_cache():
+    # stage isolation: the GPU quantiser writes the cache, the oracle decodes
+    # the GPU's own codes, and the GPU decode must agree with that.
+    B, Hq, Hkv, T = 1, 8, 2, 512
+    d = 128
+    K, V = make_kv(B, Hkv, T, d, seed=8)
+    gk = GpuQuantizer(d, 3, True, seed=1)
+    gv = GpuQuantizer(d, 3, False, seed=2, r_stream=synth.STREAM_R_V)
+    n = B * Hkv * T
+    kp, kn, kr = gpu_quantize(gk, torch_dev(K.reshape(n, d), torch.bfloat16), n, d, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16)
+    vp, vn, _ = gpu_quantize(gv, torch_dev(V.reshape(n, d), torch.bfloat16), n, d, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16)
+    torch.cuda.synchronize()
+    ki, kz = otq.unpack(to_np_u32(kp), n, d, 3, True, "keys")
+    vi, _ = otq.unpack(to_np_u32(vp), n, d, 3, False, "values")
+    shp = (B, Hkv, T)
+    ck = otq.Codes(ki.reshape(shp + (d,)), kz.reshape(shp + (d,)), None, None, to_np_f16(kn).reshape(shp),
+                   to_np_f16(kr).reshape(shp), None, None)
+    cv = otq.Codes(vi.reshape(shp + (d,)), None, None, None, to_np_f16(vn).reshape(shp), np.zeros(shp, np.float16),
+                   None, None)
+    qry = synth.rng(1, 31).standard_normal((B, Hq, d)).astype(np.float32)
+    kd = tq.make_group(gk.q, 0, kp, kn, kr, T)
+    vd = tq.make_group(gv.q, 0, vp, vn, None, T)
+
+    class _C:
+        pass
+
+    kc, vc = _C(), _C()
+    kc.group, vc.group = kd, vd
+    out, sc = run_decode([kc], [vc], qry, Hkv, T, None, "f32")
+    check_decode(out, sc, [otq.Group(0, gk.oq, ck)], [otq.Group(0, gv.oq, cv)], qry, Hkv, None)
+
+
+def test_decode_is_deterministic():
+    B, Hq, Hkv, T = 1, 32, 8, 2048
+    K, V = make_kv(B, Hkv, T, 128, seed=3)
+    gk = GpuQuantizer(128, 3, True, seed=1)
+    gv = GpuQuantizer(128, 3, False, seed=2, r_stream=synth.STREAM_R_V)
+    kc = Cache(gk, 0, otq.quantize(K, gk.oq), T, "keys")
+    vc = Cache(gv, 0, otq.quantize(V, gv.oq), T, "values")
+    qry = synth.rng(2, 0).standard_normal((B, Hq, 128)).astype(np.float32)
+    a = run_decode([kc], [vc], qry, Hkv, T, None, "f32")
+    b = run_decode([kc], [vc], qry, Hkv, T, None, "f32")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# --------------------------------------------------------------------------
+# search
+# --------------------------------------------------------------------------
+
+def run_search(gq, packed, norm, rnorm, N, queries, k):
+    db = tq.make_group(gq.q, 0, packed, norm, rnorm, 0)
+    Q = queries.shape[0]
+    ws_bytes = tq.tq_search_workspace_bytes(db, N, Q, k)
+    ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
+    oi = torch.full((Q, k), -7, dtype=torch.int64, device="cuda")
+    osc = torch.empty((Q, k), dtype=torch.float32, device="cuda")
+    tq.tq_search_topk(db, N, torch_dev(queries.astype(np.float32)), Q, k, oi, osc, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return oi.cpu().numpy(), osc.cpu().numpy()
+
+
+@pytest.mark.parametrize("d,B,N,Q,k", [(128, 3, 3001, 16, 10), (256, 2, 777, 5, 64), (96, 1, 100, 3, 100 // 2)])
+def test_search_matches_oracle_on_oracle_packed_db(d, B, N, Q, k):
+    gq = GpuQuantizer(d, B, True, seed=d)
+    db, means = synth.gaussian_mixture(N, d, 16, seed=d)
+    qs, _ = synth.gaussian_mixture(Q, d, 16, seed=d, stream=synth.STREAM_QUERY, means=means)
+    codes = otq.quantize(db.astype(np.float64), gq.oq)
+    words = otq.pack(codes.idx, codes.z, B, "keys")
+    gi, gs = run_search(gq, torch_dev(words.view(np.int32)), torch_dev(codes.n16.view(np.int16)),
+                        torch_dev(codes.rho16.view(np.int16)), N, qs, k)
+    full = otq.estimate_ip(qs.astype(np.float64), codes, gq.oq)
+    assert_topk_match(gi, gs, full, k)
+
+
+def test_search_on_gpu_quantized_db_d1536():
+    d, N, Q, k = 1536, 2000, 8, 10
+    gq = GpuQuantizer(d, 3, True, seed=7)
+    db, means = synth.gaussian_mixture(N, d, 32, seed=7)
+    qs, _ = synth.gaussian_mixture(Q, d, 32, seed=7, stream=synth.STREAM_QUERY, means=means)
+    packed, norm, rnorm = gpu_quantize(gq, torch_dev(db), N, d, tq.TQ_LAYOUT_KEYS, tq.TQ_F32)
+    torch.cuda.synchronize()
+    idx, z = otq.unpack(to_np_u32(packed), N, d, 3, True, "keys")
+    codes = otq.Codes(idx, z, None, None, to_np_f16(norm), to_np_f16(rnorm), None, None)
+    gi, gs = run_search(gq, packed, norm, rnorm, N, qs, k)
+    full = otq.estimate_ip(qs.astype(np.float64), codes, gq.oq)
+    assert_topk_match(gi, gs, full, k)
+    # recall against exact inner products is reported, not pinned
+    truth, _ = otq.exact_topk(qs, db, k)
+    print("recall@10", otq.recall_at_k(gi, truth))
