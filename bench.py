@@ -1,0 +1,401 @@
+#!/usr/bin/env python3
+"""Benchmark of the TurboQuant hot path (libtq) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+
+One step is one compressed-KV decode-attention call on the Llama-3.1-8B
+single-layer shape (batch 1, 32 query / 8 KV heads, head_dim 128, 32768
+cached tokens; keys 4-bit TurboQuant_prod = 3 Lloyd-Max bits + 1 QJL bit,
+values 3-bit MSE-only). Inputs are resident in HBM; the timed steps rotate
+over 24 copies of the compressed cache (742 MB, larger than the 256 MB
+Infinity Cache) inside one captured HIP graph, so the number is HBM-bound
+streaming rather than cache hits or Python launch overhead.
+
+The printed JSON line also carries:
+  roofline      decode bytes per call / per-call time from HIP events on the
+                launch stream, against 8 TB/s
+  cpu_baseline  the fp64 oracle timed on this host's cores on the same workload
+  extras        prefill quantize tokens/s (16 seq x 8192 tok x 32 layers x 8 KV
+                heads, K 3-bit prod, V 3-bit MSE), long-context batched decode
+                (batch 64 x 131072 tokens, 2.5 bits/channel in two channel
+                groups) and inner-product search QPS (1M x 1536, 1024 queries,
+                top-10, with recall@10 on a query sample)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+METRIC = "compressed-KV decode attn HBM GB/s (% of peak); quantize tokens/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=24)
+    p.add_argument("--no-extras", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--only", default="", help="comma list of extras to run: quantize,longctx,search")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream libtq launches on)."""
+
+    def __init__(self):
+        import torch
+
+        self.t = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.t.cuda.synchronize()
+        self.wall0 = time.perf_counter()
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.t.cuda.synchronize()
+        self.wall = time.perf_counter() - self.wall0
+        self.ms = self.a.elapsed_time(self.b)
+
+
+def dev(a, dtype=None):
+    import numpy as np
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return (t.to(dtype) if dtype is not None else t).cuda()
+
+
+# --------------------------------------------------------------------------
+# single-layer decode (the headline)
+# --------------------------------------------------------------------------
+
+def decode_single_layer(args):
+    import numpy as np
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+
+    B, Hq, Hkv, T, d = 1, 32, 8, 32768, 128
+    n = B * Hkv * T
+    log("decode: generating inputs")
+    K = synth.kv_with_outliers(B, Hkv, T, d, 4, 10.0, 2, synth.STREAM_DATA, synth.STREAM_OUTLIER)
+    V = synth.kv_with_outliers(B, Hkv, T, d, 4, 10.0, 2, synth.STREAM_NORM, synth.STREAM_R_V)
+    qry = synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.rng(2, synth.STREAM_QUERY).standard_normal(
+        (B, Hq, d)).astype(np.float32)))
+    Rk, Sk = synth.haar_orthogonal(d, 2), synth.gaussian_matrix(d, d, 2)
+    Rv = synth.haar_orthogonal(d, 2, synth.STREAM_R_V)
+    Rk_t, Sk_t, Rv_t = dev(Rk), dev(Sk), dev(Rv)
+    qk = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, Rk_t, Sk_t)
+    qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
+    kp = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, n) // 4, dtype=torch.int32, device="cuda")
+    vp = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, n) // 4, dtype=torch.int32, device="cuda")
+    kn, kr, vn = (torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(3))
+    tq.tq_quantize_kv(qk, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, dev(K.reshape(n, d), torch.bfloat16), n, d, kp, kn, kr)
+    tq.tq_quantize_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, dev(V.reshape(n, d), torch.bfloat16), n, d, vp, vn)
+    copies = []
+    for c in range(args.copies):
+        bufs = [x.clone() for x in (kp, kn, kr, vp, vn)]
+        kd = tq.make_desc([tq.make_group(qk, 0, bufs[0], bufs[1], bufs[2], T)])
+        vd = tq.make_desc([tq.make_group(qv, 0, bufs[3], bufs[4], None, T)])
+        copies.append((bufs, kd, vd))
+    q_t = dev(qry, torch.bfloat16)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    ws_bytes = tq.tq_decode_workspace_bytes(copies[0][1], copies[0][2], B, Hq, Hkv, T)
+    ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+
+    def call(i):
+        _, kd, vd = copies[i % len(copies)]
+        tq.tq_decode_attn(kd, vd, q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, scale, out, None, ws, ws_bytes)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    log(f"decode: capturing {args.steps} calls into one graph")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(args.steps):
+                call(i)
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()  # one untimed replay
+    with Timer() as tm:
+        graph.replay()
+    per_call_ms = tm.ms / args.steps
+    bytes_per_call = n * (48 + 16 + 4 + 48 + 2) + B * Hq * d * (2 + 4)
+    gbs = bytes_per_call / (per_call_ms * 1e-3) / 1e9
+    log(f"decode: {per_call_ms * 1e3:.2f} us/call, {gbs:.1f} GB/s")
+    res = dict(per_call_ms=per_call_ms, wall_ms=tm.wall * 1e3 / args.steps, gbs=gbs, bytes=bytes_per_call)
+    res["oracle_inputs"] = (K, V, qry, Rk, Sk, Rv)
+    return res
+
+
+def cpu_baseline_decode(inputs, bytes_per_call):
+    import numpy as np
+
+    import synth  # noqa: F401
+    from oracle import tq as otq
+
+    K, V, qry, Rk, Sk, Rv = inputs
+    cores = len(os.sched_getaffinity(0))
+    log(f"cpu baseline: oracle decode on {cores} cores")
+    oqk = otq.make_quantizer(128, 3, True, Rk, Sk)
+    oqv = otq.make_quantizer(128, 3, False, Rv)
+    ck, cv = otq.quantize(K, oqk), otq.quantize(V, oqv)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        otq.decode_attention(qry.astype(np.float64), [otq.Group(0, oqk, ck)], [otq.Group(0, oqv, cv)], 8)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 3:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": round(bytes_per_call / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"the full single-layer decode step (32 heads x 32768 tokens), {reps} repetition(s), "
+                      f"{dt:.2f} s each; codes from the oracle's own quantiser (untimed)"}
+
+
+# --------------------------------------------------------------------------
+# extras
+# --------------------------------------------------------------------------
+
+def quantize_prefill(steps=2):
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+    from synth import device as sdev
+
+    L, S, Tq, H, d = 32, 16, 8192, 8, 128
+    n = S * Tq * H
+    log("quantize: generating 17.2 GB of bf16 K/V on the device")
+    X = torch.empty((L, 2, n, d), dtype=torch.bfloat16, device="cuda")
+    for l in range(L):
+        for t in range(2):
+            sdev.lognormal_norm_vectors(n, d, seed=1000 + 2 * l + t, out=X[l, t])
+    Rk_t, Sk_t = dev(synth.haar_orthogonal(d, 3)), dev(synth.gaussian_matrix(d, d, 3))
+    Rv_t = dev(synth.haar_orthogonal(d, 3, synth.STREAM_R_V))
+    qk = tq.tq_quantizer_init(d, 2, tq.TQ_PROD, Rk_t, Sk_t)
+    qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
+    kb = tq.tq_packed_bytes(d, 2, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, n)
+    vb = tq.tq_packed_bytes(d, 3, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, n)
+    kp = torch.empty((L, kb // 4), dtype=torch.int32, device="cuda")
+    vp = torch.empty((L, vb // 4), dtype=torch.int32, device="cuda")
+    kn = torch.empty((L, n), dtype=torch.int16, device="cuda")
+    kr = torch.empty((L, n), dtype=torch.int16, device="cuda")
+    vn = torch.empty((L, n), dtype=torch.int16, device="cuda")
+
+    def step():
+        for l in range(L):
+            tq.tq_quantize_kv(qk, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, X[l, 0], n, d, kp[l], kn[l], kr[l])
+            tq.tq_quantize_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, X[l, 1], n, d, vp[l], vn[l])
+
+    step()
+    with Timer() as tm:
+        for _ in range(steps):
+            step()
+    sec = tm.ms * 1e-3 / steps
+    tokens = S * Tq
+    flops = tokens * L * H * (2 * 2 * d * d + 2 * d * d)
+    bytes_ = tokens * L * H * (2 * d * 2 + (3 * 16 + 4) + (3 * 16 + 2))
+    res = {"tokens_per_s": round(tokens / sec, 1), "ms_per_step": round(sec * 1e3, 3),
+           "workload": "16 seq x 8192 tok x 32 layers x 8 KV heads, d=128, bf16; K 3-bit prod, V 3-bit MSE",
+           "achieved_tflops": round(flops / sec / 1e12, 2), "hbm_gbs": round(bytes_ / sec / 1e9, 1),
+           "flops_roofline_frac_fp32_vector": round(flops / sec / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
+           "hbm_roofline_frac": round(bytes_ / sec / 1e9 / HBM_PEAK_GBS, 4)}
+    del X
+    torch.cuda.empty_cache()
+    return res
+
+
+def longctx_decode(steps=5):
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+    from synth import device as sdev
+
+    B, Hq, Hkv, T, d = 64, 32, 8, 131072, 128
+    n = B * Hkv * T
+    groups_k = [(0, 32, 2, tq.TQ_PROD), (32, 96, 1, tq.TQ_PROD)]
+    groups_v = [(0, 32, 3, tq.TQ_MSE), (32, 96, 2, tq.TQ_MSE)]
+    keep = []
+    descs = {}
+    for name, groups, layout, stream in (("k", groups_k, tq.TQ_LAYOUT_KEYS, 11), ("v", groups_v, tq.TQ_LAYOUT_VALUES, 12)):
+        log(f"longctx: generating {name} ({n * d * 2 / 1e9:.1f} GB bf16), outlier channels first")
+        X = sdev.kv_with_outliers(B, Hkv, T, d, 0, 1.0, seed=4, stream=stream)
+        X[..., :32] *= 10  # the 32 outlier channels, already permuted to the front
+        X = X.view(n, d)
+        gl = []
+        for gi, (ch, gd, bits, var) in enumerate(groups):
+            R_t = dev(synth.haar_orthogonal(gd, 40 + gi + 10 * stream))
+            S_t = dev(synth.gaussian_matrix(gd, gd, 40 + gi + 10 * stream)) if var == tq.TQ_PROD else None
+            q = tq.tq_quantizer_init(gd, bits, var, R_t, S_t)
+            pk = torch.empty(tq.tq_packed_bytes(gd, bits, var, layout, n) // 4, dtype=torch.int32, device="cuda")
+            nr = torch.empty(n, dtype=torch.int16, device="cuda")
+            rr = torch.empty(n, dtype=torch.int16, device="cuda") if var == tq.TQ_PROD else None
+            tq.tq_quantize_kv(q, layout, tq.TQ_BF16, X[:, ch:], n, d, pk, nr, rr)
+            keep += [R_t, S_t, pk, nr, rr]
+            gl.append(tq.make_group(q, ch, pk, nr, rr, T))
+        torch.cuda.synchronize()
+        del X
+        torch.cuda.empty_cache()
+        descs[name] = tq.make_desc(gl)
+    q_t = torch.randn((B, Hq, d), generator=sdev.generator(4, 13), device="cuda").to(torch.bfloat16)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    wsb = tq.tq_decode_workspace_bytes(descs["k"], descs["v"], B, Hq, Hkv, T)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+
+    def call():
+        tq.tq_decode_attn(descs["k"], descs["v"], q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, 1 / math.sqrt(d), out,
+                          None, ws, wsb)
+
+    call()
+    with Timer() as tm:
+        for _ in range(steps):
+            call()
+    ms = tm.ms / steps
+    bytes_ = n * 84 + B * Hq * d * 6
+    bf16_bytes = n * d * 2 * 2
+    res = {"ms_per_call": round(ms, 4), "gbs": round(bytes_ / ms / 1e6, 1),
+           "hbm_roofline_frac": round(bytes_ / ms / 1e6 / HBM_PEAK_GBS, 4),
+           "bf16_attention_roofline_ms": round(bf16_bytes / HBM_PEAK_GBS / 1e6, 4),
+           "speedup_vs_bf16_roofline": round(bf16_bytes / HBM_PEAK_GBS / 1e6 / ms, 3),
+           "workload": "batch 64 x 131072 tokens, 32 q / 8 KV heads, d=128; keys: 32 outlier channels 2+1 bits, "
+                       "96 channels 1+1 bits; values 3 / 2 bits MSE; 84 B per token-head"}
+    del keep, descs
+    torch.cuda.empty_cache()
+    return res
+
+
+def vector_search(steps=2):
+    import numpy as np
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+    from oracle import tq as otq
+    from synth import device as sdev
+
+    N, d, Q, k = 1 << 20, 1536, 1024, 10
+    log("search: generating the 1M x 1536 database")
+    db, means = sdev.gaussian_mixture(N, d, 256, seed=5, stream=0)
+    qs, _ = sdev.gaussian_mixture(Q, d, 256, seed=5, stream=1, means=means)
+    R_t, S_t = dev(synth.haar_orthogonal(d, 5)), dev(synth.gaussian_matrix(d, d, 5))
+    q = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, R_t, S_t)
+    pk = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, N) // 4, dtype=torch.int32, device="cuda")
+    nr = torch.empty(N, dtype=torch.int16, device="cuda")
+    rr = torch.empty(N, dtype=torch.int16, device="cuda")
+    with Timer() as tq_build:
+        tq.tq_quantize_kv(q, tq.TQ_LAYOUT_KEYS, tq.TQ_F32, db, N, d, pk, nr, rr)
+    g = tq.make_group(q, 0, pk, nr, rr, 0)
+    wsb = tq.tq_search_workspace_bytes(g, N, Q, k)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+    oi = torch.empty((Q, k), dtype=torch.int64, device="cuda")
+    osc = torch.empty((Q, k), dtype=torch.float32, device="cuda")
+    tq.tq_search_topk(g, N, qs, Q, k, oi, osc, ws, wsb)
+    with Timer() as tm:
+        for _ in range(steps):
+            tq.tq_search_topk(g, N, qs, Q, k, oi, osc, ws, wsb)
+    sec = tm.ms * 1e-3 / steps
+    # recall@10 against exact fp64 inner products on a 64-query sample
+    sample = 64
+    exact = (qs[:sample].double() @ db.double().T)
+    top = torch.topk(exact, k, dim=1).indices.cpu().numpy()
+    rec = otq.recall_at_k(oi[:sample].cpu().numpy(), top)
+    res = {"qps": round(Q / sec, 1), "ms_per_batch": round(sec * 1e3, 3), "recall_at_10": round(rec, 4),
+           "db_quantize_ms": round(tq_build.ms, 3),
+           "streamed_db_bytes": N * (4 * 1536 // 8 + 4),
+           "workload": "1M x 1536 fp32 256-component Gaussian mixture, unit-normalised; 1024 queries; "
+                       "4-bit prod (3+1) codes; top-10"}
+    del db, pk, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the hot path on a single MI355X and launches no "
+              "multi-GPU job; the sharding plan is written up in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import decode_tq_quantize_amd as tq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    tq.lib()
+    torch.cuda.set_device(0)
+    main_res = decode_single_layer(args)
+    extras = {}
+    only = set(x for x in args.only.split(",") if x)
+    if not args.no_extras:
+        for name, fn in (("quantize_prefill", quantize_prefill), ("longctx_decode", longctx_decode),
+                         ("vector_search", vector_search)):
+            key = name.split("_")[0]
+            if only and key not in only and name not in only:
+                continue
+            try:
+                extras[name] = fn()
+            except Exception as e:  # an extra that fails is reported, not hidden
+                extras[name] = {"error": repr(e)}
+            log(f"{name}: {extras[name]}")
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline_decode(main_res["oracle_inputs"], main_res["bytes"])
+    gbs = main_res["gbs"]
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["wall_ms"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": "single-layer decode attention from compressed KV, Llama-3.1-8B shape",
+                   "batch": 1, "seq_len": 32768, "q_heads": 32, "kv_heads": 8, "head_dim": 128,
+                   "keys": "TurboQuant_prod 4-bit (3 Lloyd-Max + 1 QJL)", "values": "TurboQuant_mse 3-bit",
+                   "kv_copies_rotated": args.copies, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "tq_decode_attn call (qprep + decode + combine kernels), HIP events per call",
+                     "bytes_per_call": main_res["bytes"], "us_per_call": round(main_res["per_call_ms"] * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,6 +33,13 @@ hipError_t launch_decode(const tq_kv_desc& k, const tq_kv_desc& v, const void* q
                          int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out, float* scores_out,
                          void* ws, const DecodePlan& plan, hipStream_t s);
 
+// Matrix-core decode for 128-channel heads (decode_mfma.hip).
+bool mfma_decode_supported(const tq_kv_desc& k, const tq_kv_desc& v);
+DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int Hq, int Hkv, int T_max);
+hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const void* q, tq_dtype qdt, int B, int Hq,
+                              int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out,
+                              float* scores_out, void* ws, const DecodePlan& plan, hipStream_t s);
+
 // Search.
 size_t search_workspace_bytes(const tq_group& db, int64_t N, int Q, int k);
 hipError_t launch_search(const tq_group& db, int64_t N, const float* queries, int Q, int k, int64_t* out_idx,

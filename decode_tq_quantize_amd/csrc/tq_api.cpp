@@ -75,6 +75,13 @@ int check_decode(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq, int Hk
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
 
+// 128-channel heads run on the matrix cores; other head sizes on the
+// general kernel of decode.hip.
+tqk::DecodePlan decode_plan(const tq_kv_desc& k, const tq_kv_desc& v, int B, int Hq, int Hkv, int T_max) {
+  return tqk::mfma_decode_supported(k, v) ? tqk::plan_decode_mfma(k, v, B, Hq, Hkv, T_max)
+                                          : tqk::plan_decode(k, v, B, Hq, Hkv, T_max);
+}
+
 }  // namespace
 
 extern "C" const char* tq_status_string(int status) {
@@ -121,7 +128,7 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_kv_desc* k, const tq_kv_des
                                             int T_max) {
   int D = 0, Dv = 0;
   if (check_decode(k, v, B, Hq, Hkv, T_max, &D, &Dv) != TQ_OK) return 0;
-  const tqk::DecodePlan p = tqk::plan_decode(*k, *v, B, Hq, Hkv, T_max);
+  const tqk::DecodePlan p = decode_plan(*k, *v, B, Hq, Hkv, T_max);
   return (p.qprep_floats + p.partial_floats) * sizeof(float);
 }
 
@@ -137,8 +144,11 @@ extern "C" int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const vo
   if (!aligned16(q) || !aligned16(out) || (scores_out && !aligned16(scores_out)) ||
       (seq_lens && !aligned16(seq_lens)) || (ws && !aligned16(ws)))
     return TQ_ERR_MISALIGNED;
-  const tqk::DecodePlan p = tqk::plan_decode(*k, *v, B, Hq, Hkv, T_max);
+  const tqk::DecodePlan p = decode_plan(*k, *v, B, Hq, Hkv, T_max);
   if (!ws || ws_bytes < (p.qprep_floats + p.partial_floats) * sizeof(float)) return TQ_ERR_WORKSPACE;
+  if (tqk::mfma_decode_supported(*k, *v))
+    return hip_status(tqk::launch_decode_mfma(*k, *v, q, q_dtype, B, Hq, Hkv, T_max, seq_lens, scale, out,
+                                              scores_out, ws, p, static_cast<hipStream_t>(stream)));
   return hip_status(tqk::launch_decode(*k, *v, q, q_dtype, B, Hq, Hkv, T_max, seq_lens, scale, out, scores_out,
                                        ws, p, static_cast<hipStream_t>(stream)));
 }

@@ -205,7 +205,18 @@ DECODE_CASES = [
 @pytest.mark.parametrize("B,Hq,Hkv,T,T_cap,seq_lens,kB,vB,qdt", DECODE_CASES)
 def test_decode_matches_oracle_on_oracle_packed_cache(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt):
     print(f"decode B={B} Hq={Hq} Hkv={Hkv} T={T} lens={seq_lens}", flush=True)
-    d = 128
+    _decode_case(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt, 128)
+
+
+@pytest.mark.parametrize("d,Hq,Hkv,kB,vB", [(64, 8, 2, 3, 2), (256, 4, 2, 2, 3), (128, 16, 2, 4, 4), (128, 6, 2, 1, 1)])
+def test_decode_other_head_sizes_and_tiles(d, Hq, Hkv, kB, vB):
+    # head sizes other than 128 (general kernel), GQA groups of 8 (two
+    # head tiles), groups of 3 (a partial tile) and 4-bit codebooks
+    print(f"decode d={d} Hq={Hq} Hkv={Hkv} kB={kB} vB={vB}", flush=True)
+    _decode_case(2, Hq, Hkv, 700, 736, [700, 333], kB, vB, "bf16", d)
+
+
+def _decode_case(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt, d):
     K, V = make_kv(B, Hkv, T, d, seed=T)
     gk = GpuQuantizer(d, kB, True, seed=1)
     gv = GpuQuantizer(d, vB, False, seed=2, r_stream=synth.STREAM_R_V)
