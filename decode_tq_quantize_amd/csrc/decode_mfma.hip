@@ -166,91 +166,250 @@ __device__ __forceinline__ int exponent_of(float x) {
 }
 
 // ------------------------------------------------------------------ qprep
+constexpr int kPrepThreads = 512;
+
+// out[h][ch + i] = sum_j M[i][j] in[h][ch + j] for the 4 heads of a tile and
+// the d rows of one d x d matrix. Each wave takes 16 rows per pass; lane
+// (row lane/4, quarter lane%4) sums a quarter of the row with float4 loads
+// (matrix from global, query from LDS) and the quarters are combined with
+// two shuffles.
+__device__ void matvec_heads(const float* __restrict__ M, int d, int ch, const float (*in)[kD], float (*out)[kD]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = kPrepThreads / 64;
+  const int rr = lane >> 2, qtr = lane & 3;
+  const int span = d >> 2;  // multiple of 8
+  for (int r0 = 16 * wv; r0 < d; r0 += 16 * nw) {
+    const int i = r0 + rr;
+    float acc[kHT] = {0.f, 0.f, 0.f, 0.f};
+    if (i < d) {
+      const float4* row = reinterpret_cast<const float4*>(M + (int64_t)i * d + qtr * span);
+      const int j0 = ch + qtr * span;
+      for (int j4 = 0; j4 < span / 4; ++j4) {
+        const float4 m4 = row[j4];
+#pragma unroll
+        for (int h = 0; h < kHT; ++h) {
+          const float4 x = *reinterpret_cast<const float4*>(&in[h][j0 + 4 * j4]);
+          acc[h] = fmaf(m4.x, x.x, acc[h]);
+          acc[h] = fmaf(m4.y, x.y, acc[h]);
+          acc[h] = fmaf(m4.z, x.z, acc[h]);
+          acc[h] = fmaf(m4.w, x.w, acc[h]);
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kHT; ++h) {
+      acc[h] += __shfl_xor(acc[h], 1, 64);
+      acc[h] += __shfl_xor(acc[h], 2, 64);
+    }
+    if (i < d && qtr == 0) {
+#pragma unroll
+      for (int h = 0; h < kHT; ++h) out[h][ch + i] = acc[h];
+    }
+  }
+}
+
 // One workgroup per (batch, KV head, head tile): q~ = R q and q^ = S q~ per key
-// group, then the fp8 digit operands of every slot.
-__global__ __launch_bounds__(kThreads) void qprep_kernel(Args a) {
-  __shared__ float qin[kHT][kD], qt[kHT][kD], qh[kHT][kD];
+// group, power-of-two scales, then the fp8 digit operands of every slot: each
+// value's four digits are written straight to their operand bytes in LDS
+// (row 4 h + m of lane group and byte given by the k-index of the value's
+// coordinate) and the operands are copied out as dwords.
+__global__ __launch_bounds__(kPrepThreads) void qprep_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) float qin[kHT][kD];
+  __shared__ __attribute__((aligned(16))) float qt[kHT][kD];
+  __shared__ __attribute__((aligned(16))) float qh[kHT][kD];
   __shared__ float smse[kHT][kMaxKG], sqjl[kHT][kMaxKG];
+  __shared__ __attribute__((aligned(16))) uint8_t opb[kMaxSlots][64][32];
   const int key = blockIdx.x;
   const int b = key / (a.Hkv * a.HT);
   const int g = (key / a.HT) % a.Hkv;
   const int ht = key % a.HT;
   const int h0 = g * a.G + ht * kHT;
   const int nh = min(kHT, a.G - ht * kHT);
-  const int tid = threadIdx.x;
-  for (int e = tid; e < kHT * kD; e += kThreads) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int e = tid; e < kHT * kD; e += kPrepThreads) {
     const int h = e / kD, c = e % kD;
     qin[h][c] = h < nh ? tqd::load_elem(a.q, ((int64_t)b * a.Hq + h0 + h) * kD + c, a.qbf16) : 0.f;
     qh[h][c] = 0.f;
   }
   __syncthreads();
-  for (int gi = 0; gi < a.nk; ++gi) {
-    const KGroup& kg = a.k[gi];
-    for (int e = tid; e < kHT * kg.d; e += kThreads) {
-      const int h = e / kg.d, i = e % kg.d;
-      float s = 0.f;
-      for (int j = 0; j < kg.d; ++j) s = fmaf(kg.R[(int64_t)i * kg.d + j], qin[h][kg.ch + j], s);
-      qt[h][kg.ch + i] = s;
-    }
-  }
+  for (int gi = 0; gi < a.nk; ++gi) matvec_heads(a.k[gi].R, a.k[gi].d, a.k[gi].ch, qin, qt);
   __syncthreads();
-  for (int gi = 0; gi < a.nk; ++gi) {
-    const KGroup& kg = a.k[gi];
-    if (!kg.prod) continue;
-    for (int e = tid; e < kHT * kg.d; e += kThreads) {
-      const int h = e / kg.d, i = e % kg.d;
-      float s = 0.f;
-      for (int j = 0; j < kg.d; ++j) s = fmaf(kg.S[(int64_t)i * kg.d + j], qt[h][kg.ch + j], s);
-      qh[h][kg.ch + i] = s;
-    }
-  }
+  for (int gi = 0; gi < a.nk; ++gi)
+    if (a.k[gi].prod) matvec_heads(a.k[gi].S, a.k[gi].d, a.k[gi].ch, qt, qh);
   __syncthreads();
-  // power-of-two scales that bring each (head, group) operand to at most 128
-  if (tid < kHT * kMaxKG) {
-    const int h = tid / kMaxKG, gi = tid % kMaxKG;
-    float smx = 1.f, qmx = 1.f;
-    if (gi < a.nk) {
-      float amax = 0.f;
-      for (int s = 0; s < a.nslots; ++s)
-        if (a.slot[s].group == gi && !a.slot[s].qjl) amax = fmaxf(amax, fabsf(a.slot[s].alpha));
-      float mt = 0.f, mh = 0.f;
-      for (int c = a.k[gi].ch; c < a.k[gi].ch + a.k[gi].d; ++c) {
-        mt = fmaxf(mt, fabsf(qt[h][c]));
-        mh = fmaxf(mh, fabsf(qh[h][c]));
+  // power-of-two scales that bring each (head, group) operand below 128;
+  // wave wv < 4 handles head wv
+  if (wv < kHT) {
+    for (int gi = 0; gi < kMaxKG; ++gi) {
+      float smx = 1.f, qmx = 1.f;
+      if (gi < a.nk) {
+        float amax = 0.f;
+        for (int s = 0; s < a.nslots; ++s)
+          if (a.slot[s].group == gi && !a.slot[s].qjl) amax = fmaxf(amax, fabsf(a.slot[s].alpha));
+        float mt = 0.f, mh = 0.f;
+        for (int c = a.k[gi].ch + lane; c < a.k[gi].ch + a.k[gi].d; c += 64) {
+          mt = fmaxf(mt, fabsf(qt[wv][c]));
+          mh = fmaxf(mh, fabsf(qh[wv][c]));
+        }
+        mt = tqd::wave_max(mt);
+        mh = tqd::wave_max(mh);
+        const float vm = mt * amax;
+        smx = vm > 0.f ? ldexpf(1.f, 7 - exponent_of(vm)) : 1.f;
+        qmx = mh > 0.f ? ldexpf(1.f, 7 - exponent_of(mh)) : 1.f;
       }
-      const float vm = mt * amax;
-      smx = vm > 0.f ? ldexpf(1.f, 7 - exponent_of(vm)) : 1.f;
-      qmx = mh > 0.f ? ldexpf(1.f, 7 - exponent_of(mh)) : 1.f;
+      if (lane == 0) {
+        smse[wv][gi] = smx;
+        sqjl[wv][gi] = qmx;
+        a.ascale[(((int64_t)key * kHT + wv) * kMaxKG + gi) * 2 + 0] = 1.f / smx;
+        a.ascale[(((int64_t)key * kHT + wv) * kMaxKG + gi) * 2 + 1] = 1.f / qmx;
+      }
     }
-    smse[h][gi] = smx;
-    sqjl[h][gi] = qmx;
-    a.ascale[(((int64_t)key * kHT + h) * kMaxKG + gi) * 2 + 0] = 1.f / smx;
-    a.ascale[(((int64_t)key * kHT + h) * kMaxKG + gi) * 2 + 1] = 1.f / qmx;
   }
   __syncthreads();
-  for (int e = tid; e < a.nslots * 64 * 8; e += kThreads) {
-    const int s = e / 512, L = (e / 8) % 64, dw = e % 8;
-    const int r = L % 16, h = r / 4, m = r % 4, gp = L / 16;
+  // digits: one value per (slot, head, coordinate)
+  for (int e = tid; e < a.nslots * kHT * kD; e += kPrepThreads) {
+    const int s = e / (kHT * kD), h = (e / kD) % kHT, c = e % kD;
     const Slot sl = a.slot[s];
     const KGroup& kg = a.k[sl.group];
-    uint32_t word = 0;
-    for (int bb = 0; bb < 4; ++bb) {
-      const int c = coord_of_kappa(kappa_of_fp8(gp, dw * 4 + bb));
-      float v = 0.f;
-      if (h < nh && c >= kg.ch && c < kg.ch + kg.d)
-        v = sl.qjl ? qh[h][c] * sqjl[h][sl.group] : sl.alpha * qt[h][c] * smse[h][sl.group];
-      word |= fp8_digit(v, m) << (8 * bb);
+    float v = 0.f;
+    if (h < nh && c >= kg.ch && c < kg.ch + kg.d)
+      v = sl.qjl ? qh[h][c] * sqjl[h][sl.group] : sl.alpha * qt[h][c] * smse[h][sl.group];
+    // k-index of coordinate c in the fp4 operand, and its fp8 byte position
+    const int cg = c >> 5, cw = c & 31;
+    const int kappa = 32 * cg + 8 * (cw & 3) + (cw >> 2);
+    const int gp = (kappa & 63) >> 4, byte = (kappa & 15) + 16 * (kappa >> 6);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t d8 = fp8_of(v);
+      v -= f32_of_fp8(d8);
+      opb[s][16 * gp + 4 * h + m][byte] = (uint8_t)d8;
     }
-    a.aops[(((int64_t)key * a.nslots + s) * 64 + L) * 8 + dw] = word;
   }
+  __syncthreads();
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(&opb[0][0][0]);
+  uint32_t* dst = a.aops + (int64_t)key * a.nslots * 512;
+  for (int e = tid; e < a.nslots * 512; e += kPrepThreads) dst[e] = src[e];
 }
 
 // ------------------------------------------------------------------ decode
-template <int NS, int VT, int NKG>
-__global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t wbuf[2][kMaxVG][2][16][128];  // fp8 weight digits [buf][vgroup][k-step][row][kappa]
+// Odd subsets of B code planes, in ascending bitmask order (the host builds
+// the query slots in the same order).
+__host__ __device__ constexpr int n_odd(int B) { return B > 0 ? 1 << (B - 1) : 0; }
+__host__ __device__ constexpr int odd_mask(int B, int t) {
+  int n = 0;
+  for (int S = 1; S < (1 << B); ++S) {
+    int pc = 0;
+    for (int x = S; x; x >>= 1) pc += x & 1;
+    if (pc & 1) {
+      if (n == t) return S;
+      ++n;
+    }
+  }
+  return 0;
+}
+
+constexpr int kMaxVG2 = 2;  // value groups supported by this kernel
+
+// Per-lane data of one chunk for the score phase: the key plane words of the
+// lane's coordinate word for its 4 tokens, the key norms and the value norms.
+struct KChunk {
+  uint32_t w[4][5];
+  float n[kMaxKG][4], r[kMaxKG][4];
+  float nv[kMaxVG2][4];
+};
+
+template <int NK>
+__device__ __forceinline__ void load_k(KChunk& kc, const Args& a, int c0, int te, int bg, int w, int tl,
+                                       const uint32_t* kpk, int64_t kstride, int kGw, int kwg, int kP) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = c0 + 64 * w + 16 * i + tl;
+    const bool valid = tok < te;
+#pragma unroll
+    for (int pp = 0; pp < 5; ++pp) kc.w[i][pp] = 0u;
+    if (valid) {
+      const int64_t vi = (int64_t)bg * kstride + tok;
+      const uint32_t* p = kpk + (((vi >> 4) * kGw + kwg) * 16 + (vi & 15)) * kP;
+      if (kP == 4) {
+        const uint4 q4 = *reinterpret_cast<const uint4*>(p);
+        kc.w[i][0] = q4.x; kc.w[i][1] = q4.y; kc.w[i][2] = q4.z; kc.w[i][3] = q4.w;
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < 5; ++pp)
+          if (pp < kP) kc.w[i][pp] = p[pp];
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < NK; ++gi) {
+      float n = 0.f, r = 0.f;
+      if (valid) {
+        const int64_t vi = (int64_t)bg * a.k[gi].seq_stride + tok;
+        n = tqd::half_bits_to_f32(a.k[gi].norm[vi]);
+        if (a.k[gi].prod) r = tqd::half_bits_to_f32(a.k[gi].rnorm[vi]);
+      }
+      kc.n[gi][i] = n;
+      kc.r[gi][i] = r;
+    }
+#pragma unroll
+    for (int gv = 0; gv < kMaxVG2; ++gv) {
+      float nv = 0.f;
+      if (gv < a.nv && valid) nv = tqd::half_bits_to_f32(a.v[gv].norm[(int64_t)bg * a.v[gv].seq_stride + tok]);
+      kc.nv[gv][i] = nv;
+    }
+  }
+}
+
+// Value plane words of this wave's 32 coordinates for the chunk's two 128-token steps.
+struct VChunk {
+  uint32_t w[2][2][4];
+};
+
+__device__ __forceinline__ void load_v(VChunk& vc, const VGroup& vme, int c0, int te, int bg, int lane, int vjl0) {
+  const int gp = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int tblk = c0 + 128 * ks + 32 * gp;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) vc.w[ks][tt][pp] = 0u;
+      if (tblk < te) {
+        const int64_t vt = ((int64_t)bg * vme.seq_stride + tblk) >> 5;
+        const int jl = vjl0 + 16 * tt + (lane & 15);
+        const uint32_t* pw = vme.packed + (vt * vme.d + jl) * vme.B;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp)
+          if (pp < vme.B) vc.w[ks][tt][pp] = pw[pp];
+      }
+    }
+  }
+}
+
+// Value sums of one 128-token step for a value group of VB bits.
+template <int VB, int VT>
+__device__ __forceinline__ void value_step(v4f (&vacc)[2][VT], const v8i& aw, const uint32_t (&vw)[2][4]) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const uint32_t w5[5] = {vw[tt][0], vw[tt][1], vw[tt][2], vw[tt][3], 0u};
+#pragma unroll
+    for (int t = 0; t < n_odd(VB); ++t) {
+      uint32_t word = 0;
+      const int m = odd_mask(VB, t);
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        if ((m >> p) & 1) word ^= w5[p];
+      vacc[tt][t] = mfma_fp8_fp4(aw, expand_pm1(word), vacc[tt][t]);
+    }
+  }
+}
+
+template <int KB0, int KP0, int KB1, int KP1, int VT>
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
+  constexpr int NK = KB1 > 0 ? 2 : 1;
+  constexpr int NS0 = n_odd(KB0) + KP0;
+  constexpr int NS = NS0 + (KB1 > 0 ? n_odd(KB1) + KP1 : 0);
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf[2][kMaxVG2][2][16][128];  // [buf][vgroup][step][row][kappa]
   __shared__ float red_m[4][kHT];
-  __shared__ int red_e[4][kMaxVG];
+  __shared__ int red_e[4][kMaxVG2];
   __shared__ float fin_l[4][kHT];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -264,38 +423,37 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   const int ts = split * a.split_len;
   const int te = min(ts + a.split_len, len);
 
+  // this lane's coordinate word of the key layout (score-phase B operand)
+  const int W = lane >> 4;
+  const int kgi = (NK == 2 && 32 * W >= a.k[NK - 1].ch) ? 1 : 0;
+  const uint32_t* kpk = kgi ? a.k[NK - 1].packed : a.k[0].packed;
+  const int64_t kstride = kgi ? a.k[NK - 1].seq_stride : a.k[0].seq_stride;
+  const int kGw = (kgi ? a.k[NK - 1].d : a.k[0].d) >> 5;
+  const int kwg = W - ((kgi ? a.k[NK - 1].ch : a.k[0].ch) >> 5);
+  const int kP = kgi ? (KB1 + KP1) : (KB0 + KP0);
+  // this wave's value coordinates 32 w .. 32 w + 31 belong to one value group
+  const int vgi = (a.nv > 1 && 32 * w >= a.v[1].ch) ? 1 : 0;
+  const VGroup& vme = a.v[vgi];
+  const int vjl0 = 32 * w - vme.ch;
+
+  KChunk kc;
+  if (ts < te) load_k<NK>(kc, a, ts, te, bg, w, tl, kpk, kstride, kGw, kwg, kP);
+
   // query operands of this head tile
   v8i aop[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    if (s < a.nslots) {
-      const v4i* src = reinterpret_cast<const v4i*>(a.aops + (((int64_t)key * a.nslots + s) * 64 + lane) * 8);
-      const v4i lo = src[0], hi = src[1];
-      aop[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    } else {
-      aop[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    const v4i* src = reinterpret_cast<const v4i*>(a.aops + (((int64_t)key * NS + s) * 64 + lane) * 8);
+    const v4i lo = src[0], hi = src[1];
+    aop[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
-  float inv_mse[NKG], inv_qjl[NKG];
+  float inv_mse[NK], inv_qjl[NK], gam[NK];
 #pragma unroll
-  for (int gi = 0; gi < NKG; ++gi) {
+  for (int gi = 0; gi < NK; ++gi) {
     inv_mse[gi] = a.ascale[(((int64_t)key * kHT + hl) * kMaxKG + gi) * 2 + 0];
     inv_qjl[gi] = a.ascale[(((int64_t)key * kHT + hl) * kMaxKG + gi) * 2 + 1];
+    gam[gi] = a.k[gi].gamma;
   }
-  // this lane's coordinate word of the key layout (K-score B operand)
-  const int W = lane >> 4;
-  int kgi = 0;
-#pragma unroll
-  for (int gi = 1; gi < NKG; ++gi)
-    if (gi < a.nk && 32 * W >= a.k[gi].ch) kgi = gi;
-  const KGroup& kme = a.k[kgi];
-  const int kGw = kme.d / 32, kwg = W - kme.ch / 32, kP = kme.B + kme.prod;
-  // this wave's value coordinates: 32 w .. 32 w + 31, one value group
-  int vgi = 0;
-  for (int gi = 1; gi < a.nv; ++gi)
-    if (32 * w >= a.v[gi].ch) vgi = gi;
-  const VGroup& vme = a.v[vgi];
-  const int vjl0 = 32 * w - vme.ch;  // first group-local coordinate of this wave
 
   v4f vacc[2][VT];
 #pragma unroll
@@ -303,86 +461,70 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
 #pragma unroll
     for (int s = 0; s < VT; ++s) vacc[tt][s] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  int e_run[kMaxVG];
-#pragma unroll
-  for (int gv = 0; gv < kMaxVG; ++gv) e_run[gv] = -60;
+  int e_run[kMaxVG2] = {-60, -60};
 
   int buf = 0;
   for (int c0 = ts; c0 < te; c0 += kChunk, buf ^= 1) {
+    // issue the loads that overlap this chunk's compute
+    VChunk vc;
+    load_v(vc, vme, c0, te, bg, lane, vjl0);
+    KChunk kn;
+    const bool more = c0 + kChunk < te;
+    if (more) load_k<NK>(kn, a, c0 + kChunk, te, bg, w, tl, kpk, kstride, kGw, kwg, kP);
+
     // ---------------- scores for this wave's 64 tokens
     float lg[4];
-    float nvv[4][kMaxVG];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = c0 + 64 * w + 16 * i + tl;
-      const bool valid = tok < te;
-      uint32_t wds[5] = {0u, 0u, 0u, 0u, 0u};
-      {
-        const int tokl = c0 + 64 * w + 16 * i + (lane & 15);
-        if (tokl < te) {
-          const int64_t vi = (int64_t)bg * kme.seq_stride + tokl;
-          const uint32_t* p = kme.packed + (((vi >> 4) * kGw + kwg) * 16 + (vi & 15)) * kP;
+      const uint32_t(&wd)[5] = kc.w[i];
+      v4f dm[NK], dq[NK];
 #pragma unroll
-          for (int pp = 0; pp < 5; ++pp)
-            if (pp < kP) wds[pp] = p[pp];
-        }
+      for (int gi = 0; gi < NK; ++gi) dm[gi] = dq[gi] = v4f{0.f, 0.f, 0.f, 0.f};
+      // group 0 slots
+#pragma unroll
+      for (int t = 0; t < n_odd(KB0); ++t) {
+        uint32_t word = 0;
+        const int m = odd_mask(KB0, t);
+#pragma unroll
+        for (int p = 0; p < 5; ++p)
+          if ((m >> p) & 1) word ^= wd[p];
+        dm[0] = mfma_fp8_fp4(aop[t], expand_pm1(word), dm[0]);
       }
-      v4f dm[NKG], dq[NKG];
+      if constexpr (KP0) dq[0] = mfma_fp8_fp4(aop[n_odd(KB0)], expand_pm1(wd[KB0]), dq[0]);
+      if constexpr (KB1 > 0) {
 #pragma unroll
-      for (int gi = 0; gi < NKG; ++gi) dm[gi] = dq[gi] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        if (s < a.nslots) {
-          const Slot sl = a.slot[s];
+        for (int t = 0; t < n_odd(KB1); ++t) {
           uint32_t word = 0;
+          const int m = odd_mask(KB1, t);
 #pragma unroll
-          for (int pp = 0; pp < 5; ++pp)
-            if ((sl.mask >> pp) & 1) word ^= wds[pp];
-          const v8i bop = expand_pm1(word);
-#pragma unroll
-          for (int gi = 0; gi < NKG; ++gi) {
-            if (sl.group == gi) {
-              if (sl.qjl)
-                dq[gi] = mfma_fp8_fp4(aop[s], bop, dq[gi]);
-              else
-                dm[gi] = mfma_fp8_fp4(aop[s], bop, dm[gi]);
-            }
-          }
+          for (int p = 0; p < 5; ++p)
+            if ((m >> p) & 1) word ^= wd[p];
+          dm[NK - 1] = mfma_fp8_fp4(aop[NS0 + t], expand_pm1(word), dm[NK - 1]);
         }
+        if constexpr (KP1) dq[NK - 1] = mfma_fp8_fp4(aop[NS0 + n_odd(KB1)], expand_pm1(wd[KB1]), dq[NK - 1]);
       }
       float sc = 0.f;
 #pragma unroll
-      for (int gi = 0; gi < NKG; ++gi) {
-        if (gi < a.nk && valid) {
-          const KGroup& kg = a.k[gi];
-          const int64_t vi = (int64_t)bg * kg.seq_stride + tok;
-          const float n = tqd::half_bits_to_f32(kg.norm[vi]);
-          const float mse = (dm[gi][0] + dm[gi][1] + dm[gi][2] + dm[gi][3]) * inv_mse[gi];
-          float part = mse;
-          if (kg.prod) {
-            const float rho = tqd::half_bits_to_f32(kg.rnorm[vi]);
-            const float qjl = (dq[gi][0] + dq[gi][1] + dq[gi][2] + dq[gi][3]) * inv_qjl[gi];
-            part = fmaf(kg.gamma * rho, qjl, mse);
-          }
-          sc = fmaf(n, part, sc);
+      for (int gi = 0; gi < NK; ++gi) {
+        float part = (dm[gi][0] + dm[gi][1] + dm[gi][2] + dm[gi][3]) * inv_mse[gi];
+        if ((gi == 0 && KP0) || (gi == 1 && KP1)) {
+          const float qjl = (dq[gi][0] + dq[gi][1] + dq[gi][2] + dq[gi][3]) * inv_qjl[gi];
+          part = fmaf(gam[gi] * kc.r[gi][i], qjl, part);
         }
+        sc = fmaf(kc.n[gi][i], part, sc);
       }
-      if (valid && hl < nh && a.scores_out) a.scores_out[((int64_t)b * a.Hq + h0 + hl) * a.T_max + tok] = sc;
-      lg[i] = (valid && hl < nh) ? sc * a.scale_log2 : -INFINITY;
-#pragma unroll
-      for (int gv = 0; gv < kMaxVG; ++gv) {
-        float nv = 0.f;
-        if (gv < a.nv && valid) nv = tqd::half_bits_to_f32(a.v[gv].norm[(int64_t)bg * a.v[gv].seq_stride + tok]);
-        nvv[i][gv] = nv;
-      }
+      const int tok = c0 + 64 * w + 16 * i + tl;
+      const bool valid = tok < te && hl < nh;
+      if (valid && a.scores_out) a.scores_out[((int64_t)b * a.Hq + h0 + hl) * a.T_max + tok] = sc;
+      lg[i] = valid ? sc * a.scale_log2 : -INFINITY;
     }
     // ---------------- chunk statistics shared by the four waves
     float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
     mx = row16_max(mx);
     if (tl == 0) red_m[w][hl] = mx;
 #pragma unroll
-    for (int gv = 0; gv < kMaxVG; ++gv) {
-      float vm = fmaxf(fmaxf(nvv[0][gv], nvv[1][gv]), fmaxf(nvv[2][gv], nvv[3][gv]));
+    for (int gv = 0; gv < kMaxVG2; ++gv) {
+      float vm = fmaxf(fmaxf(kc.nv[gv][0], kc.nv[gv][1]), fmaxf(kc.nv[gv][2], kc.nv[gv][3]));
       vm = tqd::wave_max(vm);
       if (lane == 0) red_e[w][gv] = exponent_of(vm);
     }
@@ -391,15 +533,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
     const float m_new = fmaxf(m_run, cm);
     const bool live = m_new != -INFINITY;
     const float corr = (live && m_run != -INFINITY) ? exp2f(m_run - m_new) : (live ? 0.f : 1.f);
-    int e_new[kMaxVG];
+    int e_new[kMaxVG2];
 #pragma unroll
-    for (int gv = 0; gv < kMaxVG; ++gv)
+    for (int gv = 0; gv < kMaxVG2; ++gv)
       e_new[gv] = max(max(max(red_e[0][gv], red_e[1][gv]), max(red_e[2][gv], red_e[3][gv])), e_run[gv]);
-    // rescale this wave's value accumulators (softmax shift and weight scale)
-    int eshift = 0;
-#pragma unroll
-    for (int gv = 0; gv < kMaxVG; ++gv)
-      if (gv == vgi) eshift = e_run[gv] - e_new[gv];
+    const int eshift = vgi ? e_run[1] - e_new[1] : e_run[0] - e_new[0];
     const float vcorr = corr * ldexpf(1.f, eshift);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -415,63 +553,44 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
     }
     // weights -> fp8 digits in LDS
 #pragma unroll
-    for (int gv = 0; gv < kMaxVG; ++gv) {
-      if (gv >= a.nv) continue;
-      const float sv = ldexpf(1.f, 7 - e_new[gv]);
+    for (int gv = 0; gv < kMaxVG2; ++gv) {
+      if (gv < a.nv) {
+        const float sv = ldexpf(1.f, 7 - e_new[gv]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tau = 64 * w + 16 * i + tl;
-        const int ks = tau >> 7, tp = tau & 127;
-        const int kappa = 32 * (tp >> 5) + 8 * (tp & 3) + ((tp & 31) >> 2);
-        float r = p[i] * nvv[i][gv] * sv;
+        for (int i = 0; i < 4; ++i) {
+          const int tau = 64 * w + 16 * i + tl;
+          const int ks = tau >> 7, tp = tau & 127;
+          const int kappa = 32 * (tp >> 5) + 8 * (tp & 3) + ((tp & 31) >> 2);
+          float r = p[i] * kc.nv[gv][i] * sv;
+          uint8_t* dst = &wbuf[buf][gv][ks][4 * hl][kappa];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t d = fp8_of(r);
-          r -= f32_of_fp8(d);
-          wbuf[buf][gv][ks][4 * hl + m][kappa] = (uint8_t)d;
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t d = fp8_of(r);
+            r -= f32_of_fp8(d);
+            dst[128 * m] = (uint8_t)d;
+          }
         }
       }
       e_run[gv] = e_new[gv];
     }
-#pragma unroll
-    for (int gv = 0; gv < kMaxVG; ++gv)
-      if (gv >= a.nv) e_run[gv] = e_new[gv];
     __syncthreads();
     // ---------------- values: this wave's 32 coordinates over the 256 tokens
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int tok0 = c0 + 128 * ks;
-      if (tok0 >= te) break;
+      if (c0 + 128 * ks >= te) break;
       const uint8_t* wrow = &wbuf[buf][vgi][ks][lane & 15][0];
       const int gp = lane >> 4;
       const v4i lo = *reinterpret_cast<const v4i*>(wrow + 16 * gp);
       const v4i hi = *reinterpret_cast<const v4i*>(wrow + 64 + 16 * gp);
       const v8i aw = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const int vP = vme.B;
-      const int tblk = tok0 + 32 * gp;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        uint32_t wds[4] = {0u, 0u, 0u, 0u};
-        if (tblk < te) {
-          const int64_t vt = ((int64_t)bg * vme.seq_stride + tblk) >> 5;
-          const int jl = vjl0 + 16 * tt + (lane & 15);
-          const uint32_t* pw = vme.packed + (vt * vme.d + jl) * vP;
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp)
-            if (pp < vP) wds[pp] = pw[pp];
-        }
-#pragma unroll
-        for (int s = 0; s < VT; ++s) {
-          if (s < vme.ntypes) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp)
-              if ((vme.mask[s] >> pp) & 1) word ^= wds[pp];
-            vacc[tt][s] = mfma_fp8_fp4(aw, expand_pm1(word), vacc[tt][s]);
-          }
-        }
+      switch (vme.B) {
+        case 1: value_step<1, VT>(vacc, aw, vc.w[ks]); break;
+        case 2: value_step<2, VT>(vacc, aw, vc.w[ks]); break;
+        case 3: if constexpr (VT >= 4) value_step<3, VT>(vacc, aw, vc.w[ks]); break;
+        default: if constexpr (VT >= 8) value_step<4, VT>(vacc, aw, vc.w[ks]); break;
       }
     }
+    if (more) kc = kn;
   }
 
   // ---------------- partial results of this split
@@ -480,18 +599,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   __syncthreads();
   if (hl < nh) {
     float* part = a.partial + (((int64_t)b * a.Hq + h0 + hl) * a.splits + split) * (kD + 2);
-    int efin = 0;
-#pragma unroll
-    for (int gv = 0; gv < kMaxVG; ++gv)
-      if (gv == vgi) efin = e_run[gv];
-    const float unscale = ldexpf(1.f, efin - 7);
+    const float unscale = ldexpf(1.f, (vgi ? e_run[1] : e_run[0]) - 7);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       float v = 0.f;
 #pragma unroll
       for (int s = 0; s < VT; ++s)
-        if (s < vme.ntypes)
-          v = fmaf(vme.alpha[s], vacc[tt][s][0] + vacc[tt][s][1] + vacc[tt][s][2] + vacc[tt][s][3], v);
+        if (s < vme.ntypes) v = fmaf(vme.alpha[s], vacc[tt][s][0] + vacc[tt][s][1] + vacc[tt][s][2] + vacc[tt][s][3], v);
       part[2 + 32 * w + 16 * tt + tl] = v * unscale;
     }
     if (w == 0 && tl == 0) {
@@ -503,47 +617,72 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
 
 // ------------------------------------------------------------------ combine
 // One workgroup per (batch, query head): merge the split partials (log2
-// domain) and rotate the value accumulator back with R_v^T.
-__global__ __launch_bounds__(kThreads) void combine_kernel(Args a) {
-  __shared__ float acc[kD];
-  __shared__ float tot, mmax;
-  const int bh = blockIdx.x, tid = threadIdx.x;
+// domain) and rotate the value accumulator back with R_v^T. The split weights
+// 2^(m_s - M) are tabulated once; each column sum then streams independent
+// loads, eight splits at a time.
+constexpr int kMaxCombineSplits = 4096;
+constexpr int kCombThreads = 320;  // 2 x (kD + 1) column sums plus spare lanes
+
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
+  __shared__ float wsp[kMaxCombineSplits];
+  __shared__ float acc[2][kD + 1];
+  __shared__ float wred[kCombThreads / 64];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float* part = a.partial + (int64_t)bh * a.splits * (kD + 2);
-  if (tid == 0) {
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, part[(int64_t)s * (kD + 2)]);
-    mmax = M;
+  const int S = a.splits;
+  float mx = -INFINITY;
+  for (int s = tid; s < S; s += kCombThreads) mx = fmaxf(mx, part[(int64_t)s * (kD + 2)]);
+  mx = tqd::wave_max(mx);
+  if (lane == 0) wred[wv] = mx;
+  __syncthreads();
+  float M = wred[0];
+  for (int i = 1; i < kCombThreads / 64; ++i) M = fmaxf(M, wred[i]);
+  for (int s = tid; s < S; s += kCombThreads) {
+    const float ms = part[(int64_t)s * (kD + 2)];
+    wsp[s] = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
   }
   __syncthreads();
-  const float M = mmax;
-  if (tid <= kD) {
-    float v = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < a.splits; ++s) {
-        const float ms = part[(int64_t)s * (kD + 2)];
-        if (ms == -INFINITY) continue;
-        v = fmaf(exp2f(ms - M), part[(int64_t)s * (kD + 2) + 1 + tid], v);
+  // (half, column) pairs: column 0 is the softmax sum, 1.. the accumulator
+  if (tid < 2 * (kD + 1)) {
+    const int col = tid % (kD + 1), half = tid / (kD + 1);
+    const int sbeg = half ? S / 2 : 0, send = half ? S : S / 2;
+    float v0 = 0.f, v1 = 0.f;
+    int s = sbeg;
+    for (; s + 8 <= send; s += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = part[(int64_t)(s + u) * (kD + 2) + 1 + col];
+#pragma unroll
+      for (int u = 0; u < 8; u += 2) {
+        v0 = fmaf(wsp[s + u], x[u], v0);
+        v1 = fmaf(wsp[s + u + 1], x[u + 1], v1);
       }
     }
-    if (tid == 0)
-      tot = v;
-    else
-      acc[tid - 1] = v;
+    for (; s < send; ++s) v0 = fmaf(wsp[s], part[(int64_t)s * (kD + 2) + 1 + col], v0);
+    acc[half][col] = v0 + v1;
   }
   __syncthreads();
+  const float tot = acc[0][0] + acc[1][0];
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
   for (int gv = 0; gv < a.nv; ++gv) {
     const VGroup& vg = a.v[gv];
-    for (int i = tid; i < vg.d; i += kThreads) {
-      float s = 0.f;
-      for (int j = 0; j < vg.d; ++j) s = fmaf(vg.R[(int64_t)j * vg.d + i], acc[vg.ch + j], s);
-      a.out[(int64_t)bh * kD + vg.ch + i] = s * inv;
+    for (int i = tid; i < vg.d; i += kCombThreads) {
+      float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const float* Rc = vg.R + i;
+      for (int j = 0; j < vg.d; j += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          s8[u] = fmaf(Rc[(int64_t)(j + u) * vg.d], acc[0][1 + vg.ch + j + u] + acc[1][1 + vg.ch + j + u], s8[u]);
+      }
+      a.out[(int64_t)bh * kD + vg.ch + i] =
+          (((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]))) * inv;
     }
   }
 }
 
 // Walsh coefficients of a mirror-symmetric codebook: c[idx] =
-// sum_{|S| odd} alpha_S prod_{p in S} (2 bit_p(idx) - 1).
+// sum_{|S| odd} alpha_S prod_{p in S} (2 bit_p(idx) - 1), subsets S in
+// ascending bitmask order.
 int odd_walsh(const tq_quantizer& q, int* masks, float* alphas) {
   const int B = q.mse_bits, L = 1 << B;
   int n = 0;
@@ -563,28 +702,47 @@ int odd_walsh(const tq_quantizer& q, int* masks, float* alphas) {
   return n;
 }
 
-template <int NS, int VT, int NKG>
-void launch_kernel(const Args& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<NS, VT, NKG>), grid, dim3(kThreads), 0, s, a);
+using KernelFn = void (*)(Args);
+
+struct Spec {
+  int kb0, kp0, kb1, kp1, vt;
+  KernelFn fn;
+};
+
+#define TQ_SPEC(a, b, c, d, e) Spec{a, b, c, d, e, decode_kernel<a, b, c, d, e>}
+// Key group layouts compiled for the matrix-core decode: one group of 1-4
+// bits with or without QJL, and the 2.5 / 3.5 bit outlier splits.
+const Spec kSpecs[] = {
+    TQ_SPEC(1, 1, 0, 0, 4), TQ_SPEC(2, 1, 0, 0, 4), TQ_SPEC(3, 1, 0, 0, 4), TQ_SPEC(4, 1, 0, 0, 4),
+    TQ_SPEC(1, 0, 0, 0, 4), TQ_SPEC(2, 0, 0, 0, 4), TQ_SPEC(3, 0, 0, 0, 4), TQ_SPEC(4, 0, 0, 0, 4),
+    TQ_SPEC(3, 1, 0, 0, 8), TQ_SPEC(4, 1, 0, 0, 8), TQ_SPEC(3, 0, 0, 0, 8), TQ_SPEC(4, 0, 0, 0, 8),
+    TQ_SPEC(2, 1, 1, 1, 4), TQ_SPEC(3, 1, 2, 1, 4),
+};
+#undef TQ_SPEC
+
+const Spec* find_spec(const tq_kv_desc& k, const tq_kv_desc& v) {
+  int vt = 0, Dv = 0, D = 0;
+  for (int i = 0; i < v.n_groups; ++i) {
+    const int t = n_odd(v.g[i].q.mse_bits);
+    vt = vt > t ? vt : t;
+    Dv += v.g[i].q.d;
+  }
+  for (int i = 0; i < k.n_groups; ++i) D += k.g[i].q.d;
+  if (D != kD || Dv != kD || k.n_groups > kMaxKG || v.n_groups > kMaxVG2) return nullptr;
+  const int need_vt = vt <= 4 ? 4 : 8;
+  const int kb0 = k.g[0].q.mse_bits, kp0 = k.g[0].q.variant == TQ_PROD;
+  const int kb1 = k.n_groups > 1 ? k.g[1].q.mse_bits : 0;
+  const int kp1 = k.n_groups > 1 ? (k.g[1].q.variant == TQ_PROD) : 0;
+  for (const Spec& sp : kSpecs)
+    if (sp.kb0 == kb0 && sp.kp0 == kp0 && sp.kb1 == kb1 && sp.kp1 == kp1 && sp.vt == need_vt) return &sp;
+  return nullptr;
 }
 
 }  // namespace
 
 namespace tqk {
 
-bool mfma_decode_supported(const tq_kv_desc& k, const tq_kv_desc& v) {
-  int D = 0, Dv = 0, slots = 0, vt = 0;
-  for (int i = 0; i < k.n_groups; ++i) {
-    D += k.g[i].q.d;
-    slots += (1 << (k.g[i].q.mse_bits - 1)) + (k.g[i].q.variant == TQ_PROD ? 1 : 0);
-  }
-  for (int i = 0; i < v.n_groups; ++i) {
-    Dv += v.g[i].q.d;
-    vt = vt > (1 << (v.g[i].q.mse_bits - 1)) ? vt : (1 << (v.g[i].q.mse_bits - 1));
-  }
-  return D == kD && Dv == kD && k.n_groups <= kMaxKG && v.n_groups <= kMaxVG && slots <= kMaxSlots &&
-         vt <= kMaxVTypes;
-}
+bool mfma_decode_supported(const tq_kv_desc& k, const tq_kv_desc& v) { return find_spec(k, v) != nullptr; }
 
 DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int Hq, int Hkv, int T_max) {
   DecodePlan p{};
@@ -594,8 +752,10 @@ DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int
   for (int i = 0; i < k.n_groups; ++i)
     slots += (1 << (k.g[i].q.mse_bits - 1)) + (k.g[i].q.variant == TQ_PROD ? 1 : 0);
   const int64_t wgs_per_split = (int64_t)B * Hkv * HT;
-  int64_t splits = (1024 + wgs_per_split - 1) / wgs_per_split;
+  int64_t splits = (512 + wgs_per_split - 1) / wgs_per_split;
   int64_t sl = (T_max + splits - 1) / splits;
+  const int64_t min_sl = (T_max + kMaxCombineSplits - 1) / kMaxCombineSplits;  // the combine's split table
+  if (sl < min_sl) sl = min_sl;
   sl = (sl + kChunk - 1) / kChunk * kChunk;
   p.split_len = (int)sl;
   p.splits = (int)((T_max + sl - 1) / sl);
@@ -668,23 +828,12 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
   a.ascale = reinterpret_cast<float*>(a.aops + keys * ns * 64 * 8);
   a.partial = static_cast<float*>(ws) + plan.qprep_floats;
   a.out = out;
-  hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)keys), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)keys), dim3(kPrepThreads), 0, s, a);
   const dim3 grid(plan.splits, a.HT, B * Hkv);
-  const bool two = a.nk > 1;
-  if (ns <= 6) {
-    if (vtmax <= 4) {
-      if (two) launch_kernel<6, 4, 2>(a, grid, s); else launch_kernel<6, 4, 1>(a, grid, s);
-    } else {
-      if (two) launch_kernel<6, 8, 2>(a, grid, s); else launch_kernel<6, 8, 1>(a, grid, s);
-    }
-  } else {
-    if (vtmax <= 4) {
-      if (two) launch_kernel<12, 4, 2>(a, grid, s); else launch_kernel<12, 4, 1>(a, grid, s);
-    } else {
-      if (two) launch_kernel<12, 8, 2>(a, grid, s); else launch_kernel<12, 8, 1>(a, grid, s);
-    }
-  }
-  hipLaunchKernelGGL(combine_kernel, dim3(B * Hq), dim3(kThreads), 0, s, a);
+  const Spec* sp = find_spec(k, v);
+  if (!sp) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sp->fn, grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(B * Hq), dim3(kCombThreads), 0, s, a);
   return hipGetLastError();
 }
 
