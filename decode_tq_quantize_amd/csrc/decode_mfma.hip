@@ -318,60 +318,75 @@ __global__ __launch_bounds__(kPrepThreads) void qprep_kernel(Args a) {
   for (int e = tid; e < 512; e += kPrepThreads) dst[e] = src[e];
 }
 
+// P consecutive 32-bit words with one vector load (P = 1..5).
+template <int P>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* out) {
+  if constexpr (P == 1) {
+    out[0] = p[0];
+  } else if constexpr (P == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    out[0] = v.x; out[1] = v.y;
+  } else if constexpr (P == 3) {
+    const uint3 v = *reinterpret_cast<const uint3*>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z;
+  } else if constexpr (P == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  } else {
+    // 5-word records are only 4-byte aligned
+    typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+    const u32x4a v = *reinterpret_cast<const u32x4a*>(p);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3]; out[4] = p[4];
+  }
+}
+
 // Per-lane data of one chunk for the score phase: the key plane words of the
 // lane's coordinate word for its 4 tokens, the key norms and the value norms.
+// Norms are held one per lane (lane l holds token 64 w + l of the chunk) and
+// handed to the score lanes with a cross-lane read.
 template <int NK, int NV>
 struct KChunk {
   uint32_t w[4][5];
-  float n[NK][4], r[NK][4];
-  float nv[NV][4];
+  float n[NK], r[NK];
+  float nv[NV];
 };
 
-template <int NK, int NV, int P>
-__device__ __forceinline__ void load_k(KChunk<NK, NV>& kc, const Args& a, int c0, int te, int bg, int w, int tl,
-                                       const uint32_t* kbase, int64_t kstep, int kP) {
-  // kbase points at this lane's words of token tl of the sequence's first
-  // 16-token tile; tiles are kstep words apart.
+template <int NK, int NV, int P0, int P1>
+__device__ __forceinline__ void load_k(KChunk<NK, NV>& kc, const Args& a, int c0, int te, int bg, int w, int lane,
+                                       int kgi, const uint32_t* kbase, int64_t kstep) {
+  // kbase points at this lane's words of token lane % 16 of the sequence's
+  // first 16-token tile; tiles are kstep words apart.
+  const int tl = lane & 15;
   const int64_t tile0 = (c0 >> 4) + 4 * w;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tok = c0 + 64 * w + 16 * i + tl;
-    const bool valid = tok < te;
 #pragma unroll
     for (int pp = 0; pp < 5; ++pp) kc.w[i][pp] = 0u;
-    if (valid) {
+    if (tok < te) {
       const uint32_t* p = kbase + (tile0 + i) * kstep;
-      if constexpr (P == 4) {
-        const uint4 q4 = *reinterpret_cast<const uint4*>(p);
-        kc.w[i][0] = q4.x;
-        kc.w[i][1] = q4.y;
-        kc.w[i][2] = q4.z;
-        kc.w[i][3] = q4.w;
-      } else if constexpr (P == 2) {
-        const uint2 q2 = *reinterpret_cast<const uint2*>(p);
-        kc.w[i][0] = q2.x;
-        kc.w[i][1] = q2.y;
-      } else {
-#pragma unroll
-        for (int pp = 0; pp < 5; ++pp)
-          if (pp < kP) kc.w[i][pp] = p[pp];
-      }
+      if (NK == 1 || kgi == 0)
+        load_words<P0>(p, kc.w[i]);
+      else
+        load_words<P1>(p, kc.w[i]);
     }
-#pragma unroll
-    for (int gi = 0; gi < NK; ++gi) {
-      float n = 0.f, r = 0.f;
-      if (valid) {
-        const int64_t vi = (int64_t)bg * a.k[gi].seq_stride + tok;
-        n = tqd::half_bits_to_f32(a.k[gi].norm[vi]);
-        if (a.k[gi].prod) r = tqd::half_bits_to_f32(a.k[gi].rnorm[vi]);
-      }
-      kc.n[gi][i] = n;
-      kc.r[gi][i] = r;
-    }
-#pragma unroll
-    for (int gv = 0; gv < NV; ++gv)
-      kc.nv[gv][i] = valid ? tqd::half_bits_to_f32(a.v[gv].norm[(int64_t)bg * a.v[gv].seq_stride + tok]) : 0.f;
   }
+  const int tok = c0 + 64 * w + lane;
+  const bool valid = tok < te;
+#pragma unroll
+  for (int gi = 0; gi < NK; ++gi) {
+    float n = 0.f, r = 0.f;
+    if (valid) {
+      const int64_t vi = (int64_t)bg * a.k[gi].seq_stride + tok;
+      n = tqd::half_bits_to_f32(a.k[gi].norm[vi]);
+      if (a.k[gi].prod) r = tqd::half_bits_to_f32(a.k[gi].rnorm[vi]);
+    }
+    kc.n[gi] = n;
+    kc.r[gi] = r;
+  }
+#pragma unroll
+  for (int gv = 0; gv < NV; ++gv)
+    kc.nv[gv] = valid ? tqd::half_bits_to_f32(a.v[gv].norm[(int64_t)bg * a.v[gv].seq_stride + tok]) : 0.f;
 }
 
 // Value plane words of this wave's 32 coordinates for a chunk's two 128-token steps.
@@ -392,9 +407,12 @@ __device__ __forceinline__ void load_v(VChunk& vc, const VGroup& vme, int c0, in
         const int64_t vt = ((int64_t)bg * vme.seq_stride + tblk) >> 5;
         const int jl = vjl0 + 16 * tt + (lane & 15);
         const uint32_t* pw = vme.packed + (vt * vme.d + jl) * vme.B;
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp)
-          if (pp < vme.B) vc.w[ks][tt][pp] = pw[pp];
+        switch (vme.B) {
+          case 1: load_words<1>(pw, vc.w[ks][tt]); break;
+          case 2: load_words<2>(pw, vc.w[ks][tt]); break;
+          case 3: load_words<3>(pw, vc.w[ks][tt]); break;
+          default: load_words<4>(pw, vc.w[ks][tt]); break;
+        }
       }
     }
   }
@@ -427,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
   __shared__ int red_e[4][NV];
   __shared__ float fin_l[4][kHT];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 4, tl = lane & 15;
   const int split = blockIdx.x, ht = blockIdx.y, bg = blockIdx.z;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -455,10 +473,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
   KChunk<NK, NV> kc;
   VChunk vc;
   if (ts < te) {
-    if constexpr (NK == 1)
-      load_k<NK, NV, KB0 + KP0>(kc, a, ts, te, bg, w, tl, kbase, kstep, kP);
-    else
-      load_k<NK, NV, 0>(kc, a, ts, te, bg, w, tl, kbase, kstep, kP);
+    load_k<NK, NV, KB0 + KP0, KB1 + KP1>(kc, a, ts, te, bg, w, lane, kgi, kbase, kstep);
     load_v(vc, vme, ts, te, bg, lane, vjl0);
   }
   const int key = (b * a.Hkv + g) * a.HT + ht;
@@ -508,12 +523,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
   for (int c0 = ts; c0 < te; c0 += kChunk, buf ^= 1) {
     const bool more = c0 + kChunk < te;
     KChunk<NK, NV> kn;
-    if (more) {
-      if constexpr (NK == 1)
-        load_k<NK, NV, KB0 + KP0>(kn, a, c0 + kChunk, te, bg, w, tl, kbase, kstep, kP);
-      else
-        load_k<NK, NV, 0>(kn, a, c0 + kChunk, te, bg, w, tl, kbase, kstep, kP);
-    }
+    if (more) load_k<NK, NV, KB0 + KP0, KB1 + KP1>(kn, a, c0 + kChunk, te, bg, w, lane, kgi, kbase, kstep);
 
     // ---------------- scores for this wave's 64 tokens
     float lg[4];
@@ -551,9 +561,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
         float part = (sum4(dm[gi]) - cm[gi]) * inv_mse[gi];
         if ((gi == 0 && KP0) || (gi == 1 && KP1)) {
           const float qjl = (sum4(dq[gi]) - cq[gi]) * inv_qjl[gi];
-          part = fmaf(gam[gi] * kc.r[gi][i], qjl, part);
+          part = fmaf(gam[gi] * __shfl(kc.r[gi], 16 * i + tl, 64), qjl, part);
         }
-        sc = fmaf(kc.n[gi][i], part, sc);
+        sc = fmaf(__shfl(kc.n[gi], 16 * i + tl, 64), part, sc);
       }
       const int tok = c0 + 64 * w + 16 * i + tl;
       const bool valid = tok < te && hl < nh;
@@ -566,8 +576,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
     if (tl == 0) red_m[w][hl] = mx;
 #pragma unroll
     for (int gv = 0; gv < NV; ++gv) {
-      float vm = fmaxf(fmaxf(kc.nv[gv][0], kc.nv[gv][1]), fmaxf(kc.nv[gv][2], kc.nv[gv][3]));
-      vm = tqd::wave_max(vm);
+      const float vm = tqd::wave_max(kc.nv[gv]);
       if (lane == 0) red_e[w][gv] = exponent_of(vm);
     }
     __syncthreads();
@@ -605,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
         const int tau = 64 * w + 16 * i + tl;
         const int ks = tau >> 7, tp = tau & 127;
         const int kappa = 32 * (tp >> 5) + 8 * (tp & 3) + ((tp & 31) >> 2);
-        float r = p[i] * kc.nv[gv][i] * sv;
+        float r = p[i] * __shfl(kc.nv[gv], 16 * i + tl, 64) * sv;
         uint8_t* dst = &wbuf[buf][gv][ks][4 * hl][kappa];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
