@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--only", default="", help="comma list of extras to run: quantize,longctx,search")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="first run one 256 MiB device-to-device copy (the known-size reference for the "
+                        "FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -151,6 +154,29 @@ def decode_single_layer(args):
     res = dict(per_call_ms=per_call_ms, wall_ms=tm.wall * 1e3 / args.steps, gbs=gbs, bytes=bytes_per_call)
     res["oracle_inputs"] = (K, V, qry, Rk, Sk, Rv)
     return res
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed counter summary.
+
+    profiles/decode_traffic.json records FETCH_SIZE and WRITE_SIZE of the
+    decode kernels (rocprofv3 --pmc, one counter per run), each scaled by what
+    the same counter reads for a 256 MiB device copy, together with the
+    SHA-256 of the kernel source they were taken on. Returns None when the
+    source has changed since (the counters no longer describe this kernel).
+    """
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    src = os.path.join(ROOT, "decode_tq_quantize_amd", "csrc", "decode_mfma.hip")
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != digest:
+        return None
+    return rec.get("bytes_per_call")
 
 
 def cpu_baseline_decode(inputs, bytes_per_call):
@@ -352,6 +378,12 @@ def main():
         sys.exit(2)
     tq.lib()
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     main_res = decode_single_layer(args)
     extras = {}
     only = set(x for x in args.only.split(",") if x)
@@ -388,7 +420,7 @@ def main():
                    "keys": "TurboQuant_prod 4-bit (3 Lloyd-Max + 1 QJL)", "values": "TurboQuant_mse 3-bit",
                    "kv_copies_rotated": args.copies, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "tq_decode_attn call (qprep + decode + combine kernels), HIP events per call",
                      "bytes_per_call": main_res["bytes"], "us_per_call": round(main_res["per_call_ms"] * 1e3, 3)},
         "cpu_baseline": cpu,

@@ -289,8 +289,9 @@ def decode_scores(qry, kgroups, Hkv):
             for grp in kgroups:
                 y = qry[b, h, grp.lo:grp.lo + grp.q.d][None, :]
                 c = grp.codes
-                sub = Codes(c.idx[b, g], None if c.z is None else c.z[b, g], c.n[b, g], c.rho[b, g],
-                            c.n16[b, g], c.rho16[b, g], c.urot[b, g] if c.urot is not None else None, None)
+                # the estimator reads only the stored fields: codes, signs, halves
+                sub = Codes(c.idx[b, g], None if c.z is None else c.z[b, g], None, None,
+                            c.n16[b, g], c.rho16[b, g], None, None)
                 s[b, h] += estimate_ip(y, sub, grp.q)[0]
     return s
 
@@ -348,8 +349,8 @@ def search_topk(queries, codes: Codes, q: Quantizer, k: int, chunk: int = 65536)
     best_i = np.zeros((Q, 0), dtype=np.int64)
     for lo in range(0, N, chunk):
         hi = min(N, lo + chunk)
-        sub = Codes(codes.idx[lo:hi], None if codes.z is None else codes.z[lo:hi], codes.n[lo:hi],
-                    codes.rho[lo:hi], codes.n16[lo:hi], codes.rho16[lo:hi], None, None)
+        sub = Codes(codes.idx[lo:hi], None if codes.z is None else codes.z[lo:hi], None, None,
+                    codes.n16[lo:hi], codes.rho16[lo:hi], None, None)
         s = estimate_ip(queries, sub, q)
         cand_s = np.concatenate([best_s, s], axis=1)
         cand_i = np.concatenate([best_i, np.broadcast_to(np.arange(lo, hi), (Q, hi - lo))], axis=1)
