@@ -144,7 +144,7 @@ const char* tq_status_string(int status);
  * A zero vector stores n = 0, rho = 0, codes 2^B / 2 and signs 1.
  * Outputs (device): `packed` (tq_packed_bytes bytes, layout as above; it must
  * start at a tile boundary of the cache it belongs to), `norm` [n] half,
- * `rnorm` [n] half (PROD only; NULL for MSE). TQ_LAYOUT_VALUES needs d <= 512.
+ * `rnorm` [n] half (PROD only; NULL for MSE). TQ_LAYOUT_VALUES needs d <= 256.
  * Contractions accumulate in fp32. */
 int tq_quantize_kv(const tq_quantizer* q, tq_layout layout, tq_dtype in_dtype,
                    const void* x, int64_t n, int64_t x_stride_elems, void* packed,
