@@ -62,6 +62,9 @@ constexpr int kMaxKG = 2;
 constexpr int kMaxVG = 2;
 constexpr int kMaxCombineSplits = 4096;
 constexpr int kCombThreads = 256;
+constexpr int kJSlice = 16;                // value channels per combine workgroup
+constexpr int kJSlices = kD / kJSlice;
+constexpr int kRowSlice = 16;              // query-transform rows per workgroup
 
 struct KGroup {
   const uint32_t* packed;
@@ -72,6 +75,7 @@ struct KGroup {
   int64_t seq_stride;
   int ch, d, B, prod;
   float gamma;
+  float amax;  // largest |Walsh coefficient| of the codebook
 };
 
 struct VGroup {
@@ -102,9 +106,9 @@ struct Args {
   float scale_log2;
   int splits, split_len;
   float* scores_out;
-  uint32_t* aops;    // [keys][nslots][64 lanes][8 dwords] query operands
-  float* ascale;     // [keys][4 heads][kMaxKG][2] inverse operand scales
-  float* partial;    // [B * Hq][splits][kD + 2]
+  float* qt;         // [keys][4 heads][kD] q~ = R q per key group
+  float* qh;         // [keys][4 heads][kD] q^ = S q~ (PROD groups, else 0)
+  float* partial;    // [B * Hq][splits][kD + 2] (max, sum, rotated accumulator)
   float* out;
 };
 
@@ -175,147 +179,97 @@ __host__ __device__ constexpr int odd_mask(int B, int t) {
   return 0;
 }
 
-// ------------------------------------------------------------------ qprep
-// One workgroup per (batch, KV head, head tile, slot). Every workgroup of a
-// tile recomputes q~ = R q and q^ = S q~ for the tile's 4 heads (both
-// matrices are read in one round of loads, before the query is needed) and
-// writes the fp8 digit operand of its own slot; slot 0 also writes the
-// inverse scales. Lane (row lane/4, quarter lane%4) of wave w owns rows
-// 16 w + lane/4 and 64 + 16 w + lane/4 of a 128 x 128 matrix (d <= 128).
-constexpr int kPrepThreads = 256;
+// ------------------------------------------------------------------ query transforms
+// q~ = R q (rotate) and q^ = S q~ (project) of every (batch, KV head, head
+// tile), one workgroup per 16 rows of the stacked key groups so that the
+// matrices are read by many compute units at once. Thread t handles row
+// t / 16 of the slice and columns 8 (t % 16) .. 8 (t % 16) + 7 of it for the
+// tile's 4 heads; the 16 partial sums of a row meet by lane exchanges.
+constexpr int kQtThreads = 256;
 
-__device__ __forceinline__ void load_rows(const float* __restrict__ M, int d, float4 (&reg)[2][8]) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int rr = lane >> 2, qtr = lane & 3, span = d >> 2;
-#pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
-    const int i = 64 * ps + 16 * wv + rr;
-#pragma unroll
-    for (int j4 = 0; j4 < 8; ++j4) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i < d && 4 * j4 < span) v = reinterpret_cast<const float4*>(M + (int64_t)i * d + qtr * span)[j4];
-      reg[ps][j4] = v;
-    }
-  }
-}
-
-__device__ __forceinline__ void matvec_regs(const float4 (&reg)[2][8], int d, int ch, const float (*in)[kD],
-                                            float (*out)[kD]) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int rr = lane >> 2, qtr = lane & 3, span = d >> 2;
-#pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
-    const int i = 64 * ps + 16 * wv + rr;
-    float acc[kHT] = {0.f, 0.f, 0.f, 0.f};
-    const int j0 = ch + qtr * span;
-#pragma unroll
-    for (int j4 = 0; j4 < 8; ++j4) {
-      if (4 * j4 < span) {
-        const float4 m4 = reg[ps][j4];
-#pragma unroll
-        for (int h = 0; h < kHT; ++h) {
-          const float4 x = *reinterpret_cast<const float4*>(&in[h][j0 + 4 * j4]);
-          acc[h] = fmaf(m4.x, x.x, acc[h]);
-          acc[h] = fmaf(m4.y, x.y, acc[h]);
-          acc[h] = fmaf(m4.z, x.z, acc[h]);
-          acc[h] = fmaf(m4.w, x.w, acc[h]);
-        }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < kHT; ++h) {
-      acc[h] += __shfl_xor(acc[h], 1, 64);
-      acc[h] += __shfl_xor(acc[h], 2, 64);
-    }
-    if (i < d && qtr == 0) {
-#pragma unroll
-      for (int h = 0; h < kHT; ++h) out[h][ch + i] = acc[h];
-    }
-  }
-}
-
-__global__ __launch_bounds__(kPrepThreads) void qprep_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) float qin[kHT][kD];
-  __shared__ __attribute__((aligned(16))) float qt[kHT][kD];
-  __shared__ __attribute__((aligned(16))) float qh[kHT][kD];
-  __shared__ float smse[kHT][kMaxKG], sqjl[kHT][kMaxKG];
-  __shared__ __attribute__((aligned(16))) uint8_t opb[64][32];
-  const int key = blockIdx.x, slot = blockIdx.y;
+template <bool PROJECT>
+__global__ __launch_bounds__(kQtThreads) void qtransform_kernel(Args a) {
+  const int key = blockIdx.x, slice = blockIdx.y;
   const int b = key / (a.Hkv * a.HT);
   const int g = (key / a.HT) % a.Hkv;
   const int ht = key % a.HT;
   const int h0 = g * a.G + ht * kHT;
   const int nh = min(kHT, a.G - ht * kHT);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  float4 regR[kMaxKG][2][8], regS[kMaxKG][2][8];
-#pragma unroll
-  for (int gi = 0; gi < kMaxKG; ++gi) {
-    if (gi < a.nk) {
-      load_rows(a.k[gi].R, a.k[gi].d, regR[gi]);
-      if (a.k[gi].prod) load_rows(a.k[gi].S, a.k[gi].d, regS[gi]);
-    }
+  const int tid = threadIdx.x, cb = tid & 15;
+  const int i = slice * kRowSlice + (tid >> 4);  // output channel (stacked row)
+  // the slice lies in one key group (group sizes are multiples of 32)
+  const bool g1 = a.nk > 1 && slice * kRowSlice >= a.k[1].ch;
+  const int d = g1 ? a.k[1].d : a.k[0].d, ch = g1 ? a.k[1].ch : a.k[0].ch;
+  const int prod = g1 ? a.k[1].prod : a.k[0].prod;
+  const float* M = PROJECT ? (g1 ? a.k[1].S : a.k[0].S) : (g1 ? a.k[1].R : a.k[0].R);
+  const bool on = 8 * cb < d;
+  const int col = ch + min(8 * cb, d - 8);  // clamped so that every load is in range
+  const int r = i - ch;
+
+  if (PROJECT && !prod) {  // no sign sketch in this group: q^ is not used
+    if (cb < kHT) a.qh[((int64_t)key * kHT + cb) * kD + i] = 0.f;
+    return;
   }
-  for (int e = tid; e < kHT * kD; e += kPrepThreads) {
-    const int h = e / kD, c = e % kD;
-    qin[h][c] = h < nh ? tqd::load_elem(a.q, ((int64_t)b * a.Hq + h0 + h) * kD + c, a.qbf16) : 0.f;
-    qh[h][c] = 0.f;
-  }
-  __syncthreads();
+  const float4* mr = reinterpret_cast<const float4*>(M + (int64_t)r * d + (col - ch));
+  const float4 m0 = mr[0], m1 = mr[1];
+  float x[kHT][8];
+  if (PROJECT) {
 #pragma unroll
-  for (int gi = 0; gi < kMaxKG; ++gi)
-    if (gi < a.nk) matvec_regs(regR[gi], a.k[gi].d, a.k[gi].ch, qin, qt);
-  __syncthreads();
-#pragma unroll
-  for (int gi = 0; gi < kMaxKG; ++gi)
-    if (gi < a.nk && a.k[gi].prod) matvec_regs(regS[gi], a.k[gi].d, a.k[gi].ch, qt, qh);
-  __syncthreads();
-  // power-of-two scales bringing each (head, group) operand below 32 (the
-  // fp4 encoding multiplies it by up to 4); wave w handles head w
-  for (int gi = 0; gi < a.nk; ++gi) {
-    float amax = 0.f;
-    for (int s = 0; s < a.nslots; ++s)
-      if (a.slot[s].group == gi && !a.slot[s].qjl) amax = fmaxf(amax, fabsf(a.slot[s].alpha));
-    float mt = 0.f, mh = 0.f;
-    for (int c = a.k[gi].ch + lane; c < a.k[gi].ch + a.k[gi].d; c += 64) {
-      mt = fmaxf(mt, fabsf(qt[wv][c]));
-      mh = fmaxf(mh, fabsf(qh[wv][c]));
+    for (int h = 0; h < kHT; ++h) {
+      const float4* xr = reinterpret_cast<const float4*>(a.qt + ((int64_t)key * kHT + h) * kD + col);
+      const float4 u = xr[0], v = xr[1];
+      x[h][0] = u.x; x[h][1] = u.y; x[h][2] = u.z; x[h][3] = u.w;
+      x[h][4] = v.x; x[h][5] = v.y; x[h][6] = v.z; x[h][7] = v.w;
     }
-    mt = tqd::wave_max(mt) * amax;
-    mh = tqd::wave_max(mh);
-    if (lane == 0) {
-      const float sm = mt > 0.f ? ldexpf(1.f, 5 - exponent_of(mt)) : 1.f;
-      const float sq = mh > 0.f ? ldexpf(1.f, 5 - exponent_of(mh)) : 1.f;
-      smse[wv][gi] = sm;
-      sqjl[wv][gi] = sq;
-      if (slot == 0) {
-        a.ascale[(((int64_t)key * kHT + wv) * kMaxKG + gi) * 2 + 0] = 1.f / sm;
-        a.ascale[(((int64_t)key * kHT + wv) * kMaxKG + gi) * 2 + 1] = 1.f / sq;
+  } else if (a.qbf16) {
+#pragma unroll
+    for (int h = 0; h < kHT; ++h) {
+      const int hr = min(h, nh - 1);
+      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
+                                                      ((int64_t)b * a.Hq + h0 + hr) * kD + col);
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[h][2 * k] = __uint_as_float(wd[k] << 16);
+        x[h][2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
       }
     }
-  }
-  __syncthreads();
-  // this slot's digits: one value per (head, coordinate), scattered to its operand bytes
-  const Slot sl = a.slot[slot];
-  const KGroup& kg = a.k[sl.group];
-  for (int e = tid; e < kHT * kD; e += kPrepThreads) {
-    const int h = e / kD, c = e % kD;
-    float v = 0.f;
-    if (h < nh && c >= kg.ch && c < kg.ch + kg.d)
-      v = (sl.qjl ? qh[h][c] * sqjl[h][sl.group] : sl.alpha * qt[h][c] * smse[h][sl.group]) * inv_v(c & 3);
-    const int cg = c >> 5, cw = c & 31;
-    const int kappa = 32 * cg + 8 * (cw & 3) + (cw >> 2);
-    const int gp = (kappa & 63) >> 4, byte = (kappa & 15) + 16 * (kappa >> 6);
+  } else {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t d8 = fp8_of(v);
-      v -= f32_of_fp8(d8);
-      opb[16 * gp + 4 * h + m][byte] = (uint8_t)d8;
+    for (int h = 0; h < kHT; ++h) {
+      const int hr = min(h, nh - 1);
+      const float4* xr =
+          reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + ((int64_t)b * a.Hq + h0 + hr) * kD + col);
+      const float4 u = xr[0], v = xr[1];
+      x[h][0] = u.x; x[h][1] = u.y; x[h][2] = u.z; x[h][3] = u.w;
+      x[h][4] = v.x; x[h][5] = v.y; x[h][6] = v.z; x[h][7] = v.w;
     }
   }
-  __syncthreads();
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(&opb[0][0]);
-  uint32_t* dst = a.aops + ((int64_t)key * a.nslots + slot) * 512;
-  for (int e = tid; e < 512; e += kPrepThreads) dst[e] = src[e];
+  float acc[kHT];
+#pragma unroll
+  for (int h = 0; h < kHT; ++h) {
+    float s0 = m0.x * x[h][0], s1 = m0.y * x[h][1];
+    s0 = fmaf(m0.z, x[h][2], s0);
+    s1 = fmaf(m0.w, x[h][3], s1);
+    s0 = fmaf(m1.x, x[h][4], s0);
+    s1 = fmaf(m1.y, x[h][5], s1);
+    s0 = fmaf(m1.z, x[h][6], s0);
+    s1 = fmaf(m1.w, x[h][7], s1);
+    float v = on && h < nh ? s0 + s1 : 0.f;
+    v += __shfl_xor(v, 8, 16);
+    v += __shfl_xor(v, 4, 16);
+    v += __shfl_xor(v, 2, 16);
+    v += __shfl_xor(v, 1, 16);
+    acc[h] = v;
+  }
+  if (cb < kHT) {
+    float v = acc[0];
+#pragma unroll
+    for (int h = 1; h < kHT; ++h)
+      if (cb == h) v = acc[h];
+    float* dst = PROJECT ? a.qh : a.qt;
+    dst[((int64_t)key * kHT + cb) * kD + i] = v;
+  }
 }
 
 // P consecutive 32-bit words with one vector load (P = 1..5).
@@ -344,75 +298,81 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* out) {
 // lane's coordinate word for its 4 tokens, the key norms and the value norms.
 // Norms are held one per lane (lane l holds token 64 w + l of the chunk) and
 // handed to the score lanes with a cross-lane read.
+//
+// Every load below is unconditional and of one fixed shape: tokens past the
+// split's end re-read its last valid tile or token and are masked where they
+// are used (their logits are -inf, so their softmax weights are 0). A load
+// under a per-lane or data-dependent condition would make the compiler wait
+// for it at the join, serialising the prefetch.
 template <int NK, int NV>
 struct KChunk {
   uint32_t w[4][5];
-  float n[NK], r[NK];
-  float nv[NV];
+  uint32_t n[NK], r[NK];  // IEEE half bits, converted where used
+  uint32_t nv[NV];
 };
 
-template <int NK, int NV, int P0, int P1>
+__device__ __forceinline__ float hbits(uint32_t h) { return tqd::half_bits_to_f32((uint16_t)h); }
+
+template <int NK, int NV, int P0, int P1, int KP0, int KP1>
 __device__ __forceinline__ void load_k(KChunk<NK, NV>& kc, const Args& a, int c0, int te, int bg, int w, int lane,
-                                       int kgi, const uint32_t* kbase, int64_t kstep) {
+                                       int kP, const uint32_t* kbase, int64_t kstep) {
   // kbase points at this lane's words of token lane % 16 of the sequence's
   // first 16-token tile; tiles are kstep words apart.
-  const int tl = lane & 15;
-  const int64_t tile0 = (c0 >> 4) + 4 * w;
+  const int last_tile = (te - 1) >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int tok = c0 + 64 * w + 16 * i + tl;
+    const int tile = min((c0 >> 4) + 4 * w + i, last_tile);
+    const uint32_t* p = kbase + tile * kstep;
+    if constexpr (NK == 1) {
+      load_words<P0>(p, kc.w[i]);
+    } else {
+      // lanes of the two groups hold P0 or P1 words; the extra words of the
+      // smaller group are never weighted (its query digits are zero there)
+      constexpr int PM = P0 > P1 ? P0 : P1;
 #pragma unroll
-    for (int pp = 0; pp < 5; ++pp) kc.w[i][pp] = 0u;
-    if (tok < te) {
-      const uint32_t* p = kbase + (tile0 + i) * kstep;
-      if (NK == 1 || kgi == 0)
-        load_words<P0>(p, kc.w[i]);
-      else
-        load_words<P1>(p, kc.w[i]);
+      for (int pp = 0; pp < 5; ++pp) kc.w[i][pp] = pp < PM ? p[min(pp, kP - 1)] : 0u;
     }
   }
-  const int tok = c0 + 64 * w + lane;
-  const bool valid = tok < te;
+  const int tok = min(c0 + 64 * w + lane, te - 1);
 #pragma unroll
   for (int gi = 0; gi < NK; ++gi) {
-    float n = 0.f, r = 0.f;
-    if (valid) {
-      const int64_t vi = (int64_t)bg * a.k[gi].seq_stride + tok;
-      n = tqd::half_bits_to_f32(a.k[gi].norm[vi]);
-      if (a.k[gi].prod) r = tqd::half_bits_to_f32(a.k[gi].rnorm[vi]);
-    }
-    kc.n[gi] = n;
-    kc.r[gi] = r;
+    const int64_t vi = (int64_t)bg * a.k[gi].seq_stride + tok;
+    kc.n[gi] = a.k[gi].norm[vi];
+    kc.r[gi] = ((gi == 0 && KP0) || (gi == 1 && KP1)) ? (uint32_t)a.k[gi].rnorm[vi] : 0u;
   }
 #pragma unroll
-  for (int gv = 0; gv < NV; ++gv)
-    kc.nv[gv] = valid ? tqd::half_bits_to_f32(a.v[gv].norm[(int64_t)bg * a.v[gv].seq_stride + tok]) : 0.f;
+  for (int gv = 0; gv < NV; ++gv) kc.nv[gv] = a.v[gv].norm[(int64_t)bg * a.v[gv].seq_stride + tok];
 }
 
-// Value plane words of this wave's 32 coordinates for a chunk's two 128-token steps.
+// Value plane words of this wave's 32 coordinates for a chunk's two 128-token
+// steps (steps wholly past the split's end are skipped where they are used).
 struct VChunk {
   uint32_t w[2][2][4];
 };
 
-__device__ __forceinline__ void load_v(VChunk& vc, const VGroup& vme, int c0, int te, int bg, int lane, int vjl0) {
+template <int NV, int VB0, int VB1>
+__device__ __forceinline__ void load_v(VChunk& vc, const uint32_t* vpk, int64_t vrow0, int vd, int vB, int c0, int te,
+                                       int lane, int vjl0) {
+  // vpk: this wave's value group's planes; vrow0 = first 32-token tile of
+  // the sequence; vd, vB: that group's channels and bits
   const int gp = lane >> 4;
+  const int last_blk = (te - 1) & ~31;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const int tblk = c0 + 128 * ks + 32 * gp;
+    const int tblk = min(c0 + 128 * ks + 32 * gp, last_blk);
+    const int64_t vt = vrow0 + (tblk >> 5);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
+      const int jl = vjl0 + 16 * tt + (lane & 15);
+      const uint32_t* pw = vpk + (vt * vd + jl) * vB;
+      if constexpr (NV == 1) {
+        load_words<VB0>(pw, vc.w[ks][tt]);
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) vc.w[ks][tt][pp] = 0u;
-      if (tblk < te) {
-        const int64_t vt = ((int64_t)bg * vme.seq_stride + tblk) >> 5;
-        const int jl = vjl0 + 16 * tt + (lane & 15);
-        const uint32_t* pw = vme.packed + (vt * vme.d + jl) * vme.B;
-        switch (vme.B) {
-          case 1: load_words<1>(pw, vc.w[ks][tt]); break;
-          case 2: load_words<2>(pw, vc.w[ks][tt]); break;
-          case 3: load_words<3>(pw, vc.w[ks][tt]); break;
-          default: load_words<4>(pw, vc.w[ks][tt]); break;
-        }
+        for (int pp = VB0; pp < 4; ++pp) vc.w[ks][tt][pp] = 0u;
+      } else {
+        constexpr int PM = VB0 > VB1 ? VB0 : VB1;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) vc.w[ks][tt][pp] = pp < PM ? pw[min(pp, vB - 1)] : 0u;
       }
     }
   }
@@ -435,15 +395,20 @@ __device__ __forceinline__ void value_step(v4f (&vacc)[2][VT], const v8i& aw, co
   }
 }
 
-template <int KB0, int KP0, int KB1, int KP1, int VT, int NV>
+template <int KB0, int KP0, int KB1, int KP1, int VB0, int VB1>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
   constexpr int NK = KB1 > 0 ? 2 : 1;
+  constexpr int NV = VB1 > 0 ? 2 : 1;
+  constexpr int VT = n_odd(VB0) > n_odd(VB1) ? n_odd(VB0) : n_odd(VB1);
   constexpr int NS0 = n_odd(KB0) + KP0;
   constexpr int NS = NS0 + (KB1 > 0 ? n_odd(KB1) + KP1 : 0);
   __shared__ __attribute__((aligned(16))) uint8_t wbuf[2][NV][2][16][128];  // [buf][vgroup][step][row][kappa]
   __shared__ float red_m[4][kHT];
   __shared__ int red_e[4][NV];
   __shared__ float fin_l[4][kHT];
+  __shared__ __attribute__((aligned(16))) float qsh[2][kHT][kD];           // q~, q^ of this key
+  __shared__ float qscale[kHT][kMaxKG][2];
+  __shared__ __attribute__((aligned(16))) uint8_t opb[NS][64][32];         // A operands per slot
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 4, tl = lane & 15;
@@ -456,32 +421,83 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
   const int te = min(ts + a.split_len, len);
 
   // this lane's coordinate word of the key layout (score-phase B operand)
+  // (group fields are selected from uniform values, never indexed per lane)
   const int W = lane >> 4;
-  const int kgi = (NK == 2 && 32 * W >= a.k[NK - 1].ch) ? 1 : 0;
-  const KGroup& kme = a.k[kgi];
-  const int kP = kgi ? (KB1 + KP1) : (KB0 + KP0);
-  const int kGw = kme.d >> 5;
-  const int64_t kstep = (int64_t)kGw * 16 * kP;  // words per 16-token tile
-  const uint32_t* kbase = kme.packed + (((int64_t)bg * kme.seq_stride) >> 4) * kstep +
-                          ((W - (kme.ch >> 5)) * 16 + tl) * kP;
+  const bool kg1 = NK == 2 && 32 * W >= a.k[NK - 1].ch;
+  const int kP = kg1 ? (KB1 + KP1) : (KB0 + KP0);
+  const int kd = kg1 ? a.k[NK - 1].d : a.k[0].d, kch = kg1 ? a.k[NK - 1].ch : a.k[0].ch;
+  const int64_t kss = kg1 ? a.k[NK - 1].seq_stride : a.k[0].seq_stride;
+  const uint32_t* kpk = kg1 ? a.k[NK - 1].packed : a.k[0].packed;
+  const int64_t kstep = (int64_t)(kd >> 5) * 16 * kP;  // words per 16-token tile
+  const uint32_t* kbase = kpk + (((int64_t)bg * kss) >> 4) * kstep + ((W - (kch >> 5)) * 16 + tl) * kP;
   // this wave's value coordinates 32 w .. 32 w + 31 belong to one value group
   const int vgi = (NV > 1 && 32 * w >= a.v[NV - 1].ch) ? 1 : 0;
   const VGroup& vme = a.v[vgi];
   const int vjl0 = 32 * w - vme.ch;
+  const int64_t vrow0 = ((int64_t)bg * vme.seq_stride) >> 5;
 
-  // ---- issue the first chunk's loads, then build the query operands
+  // ---- load q~ and q^ of this key first (loads complete in issue order),
+  // then issue the first chunk's loads
+  const int key = (b * a.Hkv + g) * a.HT + ht;
+  const float4 qv4 = *reinterpret_cast<const float4*>(
+      tid < kHT * kD / 4 ? a.qt + (int64_t)key * kHT * kD + 4 * tid
+                         : a.qh + (int64_t)key * kHT * kD + 4 * (tid - kHT * kD / 4));
   KChunk<NK, NV> kc;
   VChunk vc;
   if (ts < te) {
-    load_k<NK, NV, KB0 + KP0, KB1 + KP1>(kc, a, ts, te, bg, w, lane, kgi, kbase, kstep);
-    load_v(vc, vme, ts, te, bg, lane, vjl0);
+    load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kc, a, ts, te, bg, w, lane, kP, kbase, kstep);
+    load_v<NV, VB0, VB1>(vc, vme.packed, vrow0, vme.d, vme.B, ts, te, lane, vjl0);
   }
-  const int key = (b * a.Hkv + g) * a.HT + ht;
+  // ---- query operands: one power-of-two scale per (head, group, part)
+  // bringing the operand below 32 (the fp4 encoding multiplies it by up to
+  // 4) -> four fp8 digits per value, laid out in LDS as the A operand of
+  // every slot
+  reinterpret_cast<float4*>(&qsh[0][0][0])[tid] = qv4;
+  __syncthreads();
+#pragma unroll
+  for (int gi = 0; gi < NK; ++gi) {
+    const int gch = a.k[gi].ch, gd = a.k[gi].d;
+    float mt = 0.f, mh = 0.f;
+    for (int c = gch + lane; c < gch + gd; c += 64) {
+      mt = fmaxf(mt, fabsf(qsh[0][w][c]));
+      mh = fmaxf(mh, fabsf(qsh[1][w][c]));
+    }
+    mt = tqd::wave_max(mt) * a.k[gi].amax;
+    mh = tqd::wave_max(mh);
+    if (lane == 0) {
+      qscale[w][gi][0] = mt > 0.f ? ldexpf(1.f, 5 - exponent_of(mt)) : 1.f;
+      qscale[w][gi][1] = mh > 0.f ? ldexpf(1.f, 5 - exponent_of(mh)) : 1.f;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const Slot sl = a.slot[s];
+    const int gch = sl.group ? a.k[NK - 1].ch : a.k[0].ch, gd = sl.group ? a.k[NK - 1].d : a.k[0].d;
+#pragma unroll
+    for (int u = 0; u < kHT * kD / kThreads; ++u) {
+      const int e = tid + kThreads * u, h = e / kD, c = e % kD;
+      float v = 0.f;
+      if (c >= gch && c < gch + gd)
+        v = (sl.qjl ? qsh[1][h][c] * qscale[h][sl.group][1] : sl.alpha * qsh[0][h][c] * qscale[h][sl.group][0]) *
+            inv_v(c & 3);
+      const int cg = c >> 5, cw = c & 31;
+      const int kappa = 32 * cg + 8 * (cw & 3) + (cw >> 2);
+      const int gp = (kappa & 63) >> 4, byte = (kappa & 15) + 16 * (kappa >> 6);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t d8 = fp8_of(v);
+        v -= f32_of_fp8(d8);
+        opb[s][16 * gp + 4 * h + m][byte] = (uint8_t)d8;
+      }
+    }
+  }
+  __syncthreads();
   v8i aop[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const v4i* src = reinterpret_cast<const v4i*>(a.aops + (((int64_t)key * NS + s) * 64 + lane) * 8);
-    const v4i lo = src[0], hi = src[1];
+    const v4i lo = *reinterpret_cast<const v4i*>(&opb[s][lane][0]);
+    const v4i hi = *reinterpret_cast<const v4i*>(&opb[s][lane][16]);
     aop[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   // constant parts of the fp4 encoding, per (group, class); scales of this lane's head
@@ -491,8 +507,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
 #pragma unroll
     for (int gi = 0; gi < NK; ++gi) {
       cm[gi] = cq[gi] = 0.f;
-      inv_mse[gi] = a.ascale[(((int64_t)key * kHT + hl) * kMaxKG + gi) * 2 + 0];
-      inv_qjl[gi] = a.ascale[(((int64_t)key * kHT + hl) * kMaxKG + gi) * 2 + 1];
+      inv_mse[gi] = 1.f / qscale[hl][gi][0];
+      inv_qjl[gi] = 1.f / qscale[hl][gi][1];
       gam[gi] = a.k[gi].gamma;
     }
 #pragma unroll
@@ -521,9 +537,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
 
   int buf = 0;
   for (int c0 = ts; c0 < te; c0 += kChunk, buf ^= 1) {
-    const bool more = c0 + kChunk < te;
+    // prefetch the next chunk; the last chunk re-reads its own (cached)
+    // addresses so that the loads stay unconditional
+    const int cn = c0 + kChunk < te ? c0 + kChunk : c0;
     KChunk<NK, NV> kn;
-    if (more) load_k<NK, NV, KB0 + KP0, KB1 + KP1>(kn, a, c0 + kChunk, te, bg, w, lane, kgi, kbase, kstep);
+    VChunk vn;
+    load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kn, a, cn, te, bg, w, lane, kP, kbase, kstep);
+    load_v<NV, VB0, VB1>(vn, vme.packed, vrow0, vme.d, vme.B, cn, te, lane, vjl0);
 
     // ---------------- scores for this wave's 64 tokens
     float lg[4];
@@ -561,9 +581,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
         float part = (sum4(dm[gi]) - cm[gi]) * inv_mse[gi];
         if ((gi == 0 && KP0) || (gi == 1 && KP1)) {
           const float qjl = (sum4(dq[gi]) - cq[gi]) * inv_qjl[gi];
-          part = fmaf(gam[gi] * __shfl(kc.r[gi], 16 * i + tl, 64), qjl, part);
+          part = fmaf(gam[gi] * hbits(__shfl(kc.r[gi], 16 * i + tl, 64)), qjl, part);
         }
-        sc = fmaf(__shfl(kc.n[gi], 16 * i + tl, 64), part, sc);
+        sc = fmaf(hbits(__shfl(kc.n[gi], 16 * i + tl, 64)), part, sc);
       }
       const int tok = c0 + 64 * w + 16 * i + tl;
       const bool valid = tok < te && hl < nh;
@@ -576,7 +596,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
     if (tl == 0) red_m[w][hl] = mx;
 #pragma unroll
     for (int gv = 0; gv < NV; ++gv) {
-      const float vm = tqd::wave_max(kc.nv[gv]);
+      const float vm = tqd::wave_max(hbits(kc.nv[gv]));
       if (lane == 0) red_e[w][gv] = exponent_of(vm);
     }
     __syncthreads();
@@ -614,7 +634,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
         const int tau = 64 * w + 16 * i + tl;
         const int ks = tau >> 7, tp = tau & 127;
         const int kappa = 32 * (tp >> 5) + 8 * (tp & 3) + ((tp & 31) >> 2);
-        float r = p[i] * __shfl(kc.nv[gv], 16 * i + tl, 64) * sv;
+        float r = p[i] * hbits(__shfl(kc.nv[gv], 16 * i + tl, 64)) * sv;
         uint8_t* dst = &wbuf[buf][gv][ks][4 * hl][kappa];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -637,17 +657,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
       const v4i hi = *reinterpret_cast<const v4i*>(wrow + 64 + 16 * gp);
       const v8i aw = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       vcon = mfma_fp8_fp4(aw, cop, vcon);
-      switch (vme.B) {
-        case 1: value_step<1, VT>(vacc, aw, vc.w[ks]); break;
-        case 2: value_step<2, VT>(vacc, aw, vc.w[ks]); break;
-        case 3: if constexpr (VT >= 4) value_step<3, VT>(vacc, aw, vc.w[ks]); break;
-        default: if constexpr (VT >= 8) value_step<4, VT>(vacc, aw, vc.w[ks]); break;
-      }
+      if (NV == 1 || vgi == 0)
+        value_step<VB0, VT>(vacc, aw, vc.w[ks]);
+      else
+        value_step<(VB1 > 0 ? VB1 : 1), VT>(vacc, aw, vc.w[ks]);
     }
-    if (more) {
-      kc = kn;
-      load_v(vc, vme, c0 + kChunk, te, bg, lane, vjl0);
-    }
+    kc = kn;
+    vc = vn;
   }
 
   // ---------------- partial results of this split
@@ -675,77 +691,117 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
 }
 
 // ------------------------------------------------------------------ combine
-// One workgroup per (batch, query head): merge the split partials (log2
-// domain) and rotate the value accumulator back with R_v^T. The split weights
-// 2^(m_s - M) are tabulated once; each (column, half of the splits) sum
-// streams independent loads sixteen at a time; R_v^T splits its rows over the
-// two halves of the workgroup.
+// Merge the split partials (log2 domain) and rotate back with R_v^T. One
+// workgroup per (batch, query head, slice of 16 output channels): it merges
+// the whole rotated accumulator over the splits (the partials are re-read
+// by the head's 8 workgroups, from L2) and multiplies it by the 16 columns
+// of R_v it owns. All loads of the common case (up to 64 splits) are issued
+// before the first result is used; indices are clamped in range and masked
+// where used, so nothing waits between them.
+constexpr int kCombCols = kD / 4;                    // float4 columns of a partial row
+constexpr int kCombRows = kCombThreads / kCombCols;  // split rows per round of loads (8)
+constexpr int kCombBatch = 8;                        // rounds held at once (64 splits)
+
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
   __shared__ float wsp[kMaxCombineSplits];
-  __shared__ float acc[kD + 1];
-  __shared__ float part2[2][kD + 1];
-  __shared__ float osum[2][kD];
-  __shared__ float wred[kCombThreads / 64];
-  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ __attribute__((aligned(16))) float accp[kCombRows][kD];
+  __shared__ __attribute__((aligned(16))) float acc[kD];
+  __shared__ float opart[kCombThreads / kJSlice][kJSlice];
+  __shared__ float wred[kCombThreads / 64], lred[kCombThreads / 64];
+  const int bh = blockIdx.x, is = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float* part = a.partial + (int64_t)bh * a.splits * (kD + 2);
   const int S = a.splits;
-  float mx = -INFINITY;
-  for (int s = tid; s < S; s += kCombThreads) mx = fmaxf(mx, part[(int64_t)s * (kD + 2)]);
+  const int i0 = is * kJSlice;
+  // the output slice lies in one value group (group sizes are multiples of 32)
+  const bool g1 = a.nv > 1 && i0 >= a.v[1].ch;
+  const float* Rv = g1 ? a.v[1].R : a.v[0].R;
+  const int vd = g1 ? a.v[1].d : a.v[0].d, vch = g1 ? a.v[1].ch : a.v[0].ch;
+
+  // R_v rows j (of the group) at this slice's 16 columns: thread t takes row
+  // t / 16 + 16 k (k < vd / 16) and column t % 16
+  const int ic = tid & (kJSlice - 1), jr = tid >> 4;
+  float rcol[kD / 16];
+#pragma unroll
+  for (int k = 0; k < kD / 16; ++k)
+    rcol[k] = Rv[(int64_t)min(jr + 16 * k, vd - 1) * vd + (i0 - vch) + ic];
+  // split maxima and sums
+  const int sm = min(tid, S - 1);
+  const float ms0 = part[(int64_t)sm * (kD + 2)], ls0 = part[(int64_t)sm * (kD + 2) + 1];
+  // accumulator rows: thread t takes float4 column t % 32 of split rows t / 32 + 8 k
+  const int c4 = tid & (kCombCols - 1), sr = tid / kCombCols;
+  float4 x[kCombBatch];
+#pragma unroll
+  for (int k = 0; k < kCombBatch; ++k) {
+    const float* row = part + (int64_t)min(sr + kCombRows * k, S - 1) * (kD + 2) + 2;
+    // rows are kD + 2 floats apart, so only 8-byte aligned: two 8-byte loads
+    const float2 lo = *reinterpret_cast<const float2*>(row + 4 * c4);
+    const float2 hi = *reinterpret_cast<const float2*>(row + 4 * c4 + 2);
+    x[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
+  }
+
+  float mx = tid < S ? ms0 : -INFINITY;
+  for (int s2 = tid + kCombThreads; s2 < S; s2 += kCombThreads) mx = fmaxf(mx, part[(int64_t)s2 * (kD + 2)]);
   mx = tqd::wave_max(mx);
   if (lane == 0) wred[wv] = mx;
   __syncthreads();
   float M = wred[0];
 #pragma unroll
-  for (int i = 1; i < kCombThreads / 64; ++i) M = fmaxf(M, wred[i]);
-  for (int s = tid; s < S; s += kCombThreads) {
-    const float ms = part[(int64_t)s * (kD + 2)];
-    wsp[s] = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+  for (int k = 1; k < kCombThreads / 64; ++k) M = fmaxf(M, wred[k]);
+  float lsum = 0.f;
+  for (int s2 = tid; s2 < S; s2 += kCombThreads) {
+    const float m = s2 == tid ? ms0 : part[(int64_t)s2 * (kD + 2)];
+    const float l = s2 == tid ? ls0 : part[(int64_t)s2 * (kD + 2) + 1];
+    const float wgt = (M == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - M);
+    wsp[s2] = wgt;
+    lsum = fmaf(wgt, l, lsum);
   }
+  lsum = tqd::wave_sum(lsum);
+  if (lane == 0) lred[wv] = lsum;
   __syncthreads();
-  // columns 0..kD (0 = softmax sum) times two halves of the splits
-  for (int job = tid; job < 2 * (kD + 1); job += kCombThreads) {
-    const int col = job % (kD + 1), half = job / (kD + 1);
-    const int sbeg = half ? S / 2 : 0, send = half ? S : S / 2;
-    const float* pc = part + 1 + col;
-    float v0 = 0.f, v1 = 0.f;
-    int s = sbeg;
-    for (; s + 16 <= send; s += 16) {
-      float x[16];
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0;; s0 += kCombRows * kCombBatch) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) x[u] = pc[(int64_t)(s + u) * (kD + 2)];
-#pragma unroll
-      for (int u = 0; u < 16; u += 2) {
-        v0 = fmaf(wsp[s + u], x[u], v0);
-        v1 = fmaf(wsp[s + u + 1], x[u + 1], v1);
-      }
+    for (int k = 0; k < kCombBatch; ++k) {
+      const int sk = s0 + sr + kCombRows * k;
+      const float wk = sk < S ? wsp[sk] : 0.f;
+      v.x = fmaf(wk, x[k].x, v.x);
+      v.y = fmaf(wk, x[k].y, v.y);
+      v.z = fmaf(wk, x[k].z, v.z);
+      v.w = fmaf(wk, x[k].w, v.w);
     }
-    for (; s < send; ++s) v0 = fmaf(wsp[s], pc[(int64_t)s * (kD + 2)], v0);
-    part2[half][col] = v0 + v1;
-  }
-  __syncthreads();
-  if (tid <= kD) acc[tid] = part2[0][tid] + part2[1][tid];
-  __syncthreads();
-  const float tot = acc[0];
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  const int half = tid >> 7, i = tid & 127;
-  for (int gv = 0; gv < a.nv; ++gv) {
-    const VGroup& vg = a.v[gv];
-    if (i < vg.d) {
-      const int jb = half ? vg.d / 2 : 0, je = half ? vg.d : vg.d / 2;  // multiples of 16
-      float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      const float* Rc = vg.R + i;
-      for (int j = jb; j < je; j += 8) {
-        float r8[8];
+    const int nxt = s0 + kCombRows * kCombBatch;
+    if (nxt >= S) break;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) r8[u] = Rc[(int64_t)(j + u) * vg.d];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) s8[u] = fmaf(r8[u], acc[1 + vg.ch + j + u], s8[u]);
-      }
-      osum[half][vg.ch + i] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+    for (int k = 0; k < kCombBatch; ++k) {
+      const float* row = part + (int64_t)min(nxt + sr + kCombRows * k, S - 1) * (kD + 2) + 2;
+      const float2 lo = *reinterpret_cast<const float2*>(row + 4 * c4);
+      const float2 hi = *reinterpret_cast<const float2*>(row + 4 * c4 + 2);
+      x[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
     }
   }
+  *reinterpret_cast<float4*>(&accp[sr][4 * c4]) = v;
   __syncthreads();
-  if (tid < kD) a.out[(int64_t)bh * kD + tid] = (osum[0][tid] + osum[1][tid]) * inv;
+  if (tid < kD) {
+    float t = 0.f;
+#pragma unroll
+    for (int r = 0; r < kCombRows; ++r) t += accp[r][tid];
+    acc[tid] = t;
+  }
+  __syncthreads();
+  // out[i0 + ic] = sum_j R_v[j][i0 + ic - vch] acc[vch + j]
+  float o = 0.f;
+#pragma unroll
+  for (int k = 0; k < kD / 16; ++k)
+    if (jr + 16 * k < vd) o = fmaf(rcol[k], acc[vch + jr + 16 * k], o);
+  opart[jr][ic] = o;
+  __syncthreads();
+  if (tid < kJSlice) {
+    float t = 0.f;
+#pragma unroll
+    for (int r = 0; r < kCombThreads / kJSlice; ++r) t += opart[r][tid];
+    const float tot = (lred[0] + lred[1]) + (lred[2] + lred[3]);
+    a.out[(int64_t)bh * kD + i0 + tid] = tot > 0.f ? t / tot : 0.f;
+  }
 }
 
 // Walsh coefficients of a mirror-symmetric codebook: c[idx] =
@@ -771,38 +827,39 @@ int odd_walsh(const tq_quantizer& q, float* alphas) {
 using KernelFn = void (*)(Args);
 
 struct Spec {
-  int kb0, kp0, kb1, kp1, vt, nv;
+  int kb0, kp0, kb1, kp1, vb0, vb1;
   KernelFn fn;
 };
 
 #define TQ_SPEC(a, b, c, d, e, f) Spec{a, b, c, d, e, f, decode_kernel<a, b, c, d, e, f>}
-// Key group layouts compiled for the matrix-core decode: one group of 1-4
-// bits with or without QJL (values in one group), and the 2.5 / 3.5 bit
-// outlier splits (two key and two value groups).
+// Layouts compiled for the matrix-core decode: keys in one group of 1-4 bits
+// with or without QJL and values of 2-4 bits, plus the outlier-channel splits
+// (32 + 96 channels) of 2.5 and 3.5 bits. Other layouts of 128-channel heads
+// run on the general kernel.
 const Spec kSpecs[] = {
-    TQ_SPEC(1, 1, 0, 0, 4, 1), TQ_SPEC(2, 1, 0, 0, 4, 1), TQ_SPEC(3, 1, 0, 0, 4, 1), TQ_SPEC(4, 1, 0, 0, 4, 1),
-    TQ_SPEC(1, 0, 0, 0, 4, 1), TQ_SPEC(2, 0, 0, 0, 4, 1), TQ_SPEC(3, 0, 0, 0, 4, 1), TQ_SPEC(4, 0, 0, 0, 4, 1),
-    TQ_SPEC(3, 1, 0, 0, 8, 1), TQ_SPEC(4, 1, 0, 0, 8, 1), TQ_SPEC(3, 0, 0, 0, 8, 1), TQ_SPEC(4, 0, 0, 0, 8, 1),
-    TQ_SPEC(2, 1, 1, 1, 4, 2), TQ_SPEC(3, 1, 2, 1, 4, 2),
+    TQ_SPEC(1, 1, 0, 0, 1, 0), TQ_SPEC(1, 1, 0, 0, 2, 0), TQ_SPEC(2, 1, 0, 0, 2, 0), TQ_SPEC(3, 1, 0, 0, 2, 0),
+    TQ_SPEC(1, 1, 0, 0, 3, 0), TQ_SPEC(2, 1, 0, 0, 3, 0), TQ_SPEC(3, 1, 0, 0, 3, 0),
+    TQ_SPEC(1, 1, 0, 0, 4, 0), TQ_SPEC(2, 1, 0, 0, 4, 0), TQ_SPEC(3, 1, 0, 0, 4, 0),
+    TQ_SPEC(4, 1, 0, 0, 4, 0), TQ_SPEC(4, 0, 0, 0, 4, 0), TQ_SPEC(3, 0, 0, 0, 3, 0),
+    TQ_SPEC(2, 0, 0, 0, 2, 0), TQ_SPEC(3, 0, 0, 0, 2, 0), TQ_SPEC(4, 0, 0, 0, 2, 0),
+    TQ_SPEC(2, 1, 1, 1, 3, 2),
 };
 #undef TQ_SPEC
 
 const Spec* find_spec(const tq_kv_desc& k, const tq_kv_desc& v) {
-  int vt = 0, Dv = 0, D = 0;
-  for (int i = 0; i < v.n_groups; ++i) {
-    const int t = n_odd(v.g[i].q.mse_bits);
-    vt = vt > t ? vt : t;
-    Dv += v.g[i].q.d;
-  }
+  int Dv = 0, D = 0;
+  for (int i = 0; i < v.n_groups; ++i) Dv += v.g[i].q.d;
   for (int i = 0; i < k.n_groups; ++i) D += k.g[i].q.d;
   if (D != kD || Dv != kD || k.n_groups > kMaxKG || v.n_groups > kMaxVG) return nullptr;
-  const int need_vt = vt <= 4 ? 4 : 8;
+  // a wave's 32 value coordinates must lie in one value group
+  for (int i = 0; i < v.n_groups; ++i)
+    if (v.g[i].q.d % 32) return nullptr;
   const int kb0 = k.g[0].q.mse_bits, kp0 = k.g[0].q.variant == TQ_PROD;
   const int kb1 = k.n_groups > 1 ? k.g[1].q.mse_bits : 0;
   const int kp1 = k.n_groups > 1 ? (k.g[1].q.variant == TQ_PROD) : 0;
+  const int vb0 = v.g[0].q.mse_bits, vb1 = v.n_groups > 1 ? v.g[1].q.mse_bits : 0;
   for (const Spec& sp : kSpecs)
-    if (sp.kb0 == kb0 && sp.kp0 == kp0 && sp.kb1 == kb1 && sp.kp1 == kp1 && sp.vt == need_vt &&
-        sp.nv == v.n_groups)
+    if (sp.kb0 == kb0 && sp.kp0 == kp0 && sp.kb1 == kb1 && sp.kp1 == kp1 && sp.vb0 == vb0 && sp.vb1 == vb1)
       return &sp;
   return nullptr;
 }
@@ -832,8 +889,10 @@ DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int
   p.Dv = kD;
   int slots = 0;
   for (int i = 0; i < k.n_groups; ++i) slots += n_odd(k.g[i].q.mse_bits) + (k.g[i].q.variant == TQ_PROD ? 1 : 0);
+  (void)slots;
   const size_t keys = (size_t)B * Hkv * HT;
-  p.qprep_floats = keys * slots * 512 + keys * kHT * kMaxKG * 2;
+  // q~, q^ [keys][4][kD], then the split partials
+  p.qprep_floats = 2 * keys * kHT * kD;
   p.partial_floats = (size_t)B * Hq * p.splits * (kD + 2);
   return p;
 }
@@ -863,7 +922,11 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
     o.gamma = (float)(sqrt(M_PI / 2.0) / g.q.d);
     float alphas[kMaxVTypes];
     const int nt = odd_walsh(g.q, alphas);
-    for (int t = 0; t < nt; ++t) a.slot[ns++] = Slot{gi, 0, alphas[t]};
+    o.amax = 0.f;
+    for (int t = 0; t < nt; ++t) {
+      a.slot[ns++] = Slot{gi, 0, alphas[t]};
+      o.amax = fmaxf(o.amax, fabsf(alphas[t]));
+    }
     if (o.prod) a.slot[ns++] = Slot{gi, 1, 1.f};
   }
   a.nslots = ns;
@@ -895,14 +958,17 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
   a.split_len = plan.split_len;
   a.scores_out = scores_out;
   const size_t keys = (size_t)B * Hkv * a.HT;
-  a.aops = static_cast<uint32_t*>(ws);
-  a.ascale = reinterpret_cast<float*>(a.aops + keys * ns * 512);
-  a.partial = static_cast<float*>(ws) + plan.qprep_floats;
+  float* wsf = static_cast<float*>(ws);
+  a.qt = wsf;
+  a.qh = a.qt + keys * kHT * kD;
+  a.partial = wsf + plan.qprep_floats;
   a.out = out;
-  hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)keys, ns), dim3(kPrepThreads), 0, s, a);
+  const dim3 qgrid((unsigned)keys, kD / kRowSlice);
+  hipLaunchKernelGGL(qtransform_kernel<false>, qgrid, dim3(kQtThreads), 0, s, a);
+  hipLaunchKernelGGL(qtransform_kernel<true>, qgrid, dim3(kQtThreads), 0, s, a);
   const dim3 grid(plan.splits, a.HT, B * Hkv);
   hipLaunchKernelGGL(sp->fn, grid, dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(combine_kernel, dim3(B * Hq), dim3(kCombThreads), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(B * Hq, kJSlices), dim3(kCombThreads), 0, s, a);
   return hipGetLastError();
 }
 
