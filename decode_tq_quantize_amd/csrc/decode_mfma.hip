@@ -140,19 +140,35 @@ __device__ __forceinline__ v4f mfma_fp8_fp4(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 0, 0, 0);
 }
 
+// Reductions over the 16 lanes of a DPP row by row rotations (every lane
+// of the row ends with the result); no LDS traffic.
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 8, 64));
-  v = fmaxf(v, __shfl_xor(v, 4, 64));
-  v = fmaxf(v, __shfl_xor(v, 2, 64));
-  v = fmaxf(v, __shfl_xor(v, 1, 64));
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  v = fmaxf(v, row_ror<1>(v));
   return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
-  v += __shfl_xor(v, 8, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 1, 64);
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
   return v;
+}
+// Maximum over the wave: row maxima, then the four rows' values read as
+// uniform values.
+__device__ __forceinline__ float wave_max64(float v) {
+  v = row16_max(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ int exponent_of(float x) {
@@ -307,72 +323,127 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* out) {
 template <int NK, int NV>
 struct KChunk {
   uint32_t w[4][5];
-  uint32_t n[NK], r[NK];  // IEEE half bits, converted where used
-  uint32_t nv[NV];
+  uint32_t n[NK][4], r[NK][4];  // IEEE half bits of token 16 i + lane % 16, converted where used
+  uint32_t nv[NV][4];
 };
 
 __device__ __forceinline__ float hbits(uint32_t h) { return tqd::half_bits_to_f32((uint16_t)h); }
 
+// Load at a 32-bit unsigned byte offset from a base pointer.
+template <class T>
+__device__ __forceinline__ const T* at_bytes(const T* base, uint32_t byte_off) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+// Raw buffer resource over [base, base + bytes): loads use a per-lane byte
+// offset (vector register, fixed for the kernel) plus a wave-uniform byte
+// offset (scalar register, advanced per chunk), and read 0 past `bytes`.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <int P>
+__device__ __forceinline__ void buf_words(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* out) {
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u3 __attribute__((ext_vector_type(3)));
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  if constexpr (P == 1) {
+    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  } else if constexpr (P == 2) {
+    const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    out[0] = v[0]; out[1] = v[1];
+  } else if constexpr (P == 3) {
+    const u3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2];
+  } else {
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+    if constexpr (P == 5) out[4] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 16u, soff, 0);
+  }
+}
+__device__ __forceinline__ uint32_t buf_half(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// Addressing of one wave's loads. One key group: buffer resources over the
+// sequence's key planes and norms. Two key groups (lanes of different
+// groups read different arrays): plain per-lane pointers.
+struct KAddr {
+  rsrc_t res;           // key planes of the sequence (one key group)
+  const uint32_t* seq;  // per-lane base for two key groups
+  uint32_t step;        // bytes per 16-token tile
+  uint32_t lane_off;    // this lane's byte offset within a tile
+  int kP;               // planes of this lane's group
+};
+struct NAddr {
+  rsrc_t n[kMaxKG], r[kMaxKG], nv[kMaxVG];  // norms of the sequence
+};
+struct VAddr {
+  rsrc_t res;           // value planes of the sequence (this wave's value group)
+  uint32_t tile_bytes;  // bytes per 32-token tile
+  uint32_t lane_off;    // this lane's byte offset (its 32-token block and first coordinate)
+  int vB;
+};
+
 template <int NK, int NV, int P0, int P1, int KP0, int KP1>
-__device__ __forceinline__ void load_k(KChunk<NK, NV>& kc, const Args& a, int c0, int te, int bg, int w, int lane,
-                                       int kP, const uint32_t* kbase, int64_t kstep) {
-  // kbase points at this lane's words of token lane % 16 of the sequence's
-  // first 16-token tile; tiles are kstep words apart.
-  const int last_tile = (te - 1) >> 4;
+__device__ __forceinline__ void load_k(KChunk<NK, NV>& kc, const KAddr& ka, const NAddr& na, int c0, int tlast,
+                                       int w, int lane) {
+  // tiles past the split's end re-read its last tile (their tokens are
+  // masked where used; the tile lies inside the sequence's stride)
+  const int last_tile = tlast >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int tile = min((c0 >> 4) + 4 * w + i, last_tile);
-    const uint32_t* p = kbase + tile * kstep;
+    const uint32_t tile = (uint32_t)min((c0 >> 4) + 4 * w + i, last_tile);
     if constexpr (NK == 1) {
-      load_words<P0>(p, kc.w[i]);
+      buf_words<P0>(ka.res, ka.lane_off, tile * ka.step, kc.w[i]);
     } else {
       // lanes of the two groups hold P0 or P1 words; the extra words of the
       // smaller group are never weighted (its query digits are zero there)
       constexpr int PM = P0 > P1 ? P0 : P1;
+      const uint32_t* p = at_bytes(ka.seq, tile * ka.step + ka.lane_off);
 #pragma unroll
-      for (int pp = 0; pp < 5; ++pp) kc.w[i][pp] = pp < PM ? p[min(pp, kP - 1)] : 0u;
+      for (int pp = 0; pp < 5; ++pp) kc.w[i][pp] = pp < PM ? p[min(pp, ka.kP - 1)] : 0u;
     }
   }
-  const int tok = min(c0 + 64 * w + lane, te - 1);
+  const uint32_t tl2 = 2u * (lane & 15);
 #pragma unroll
-  for (int gi = 0; gi < NK; ++gi) {
-    const int64_t vi = (int64_t)bg * a.k[gi].seq_stride + tok;
-    kc.n[gi] = a.k[gi].norm[vi];
-    kc.r[gi] = ((gi == 0 && KP0) || (gi == 1 && KP1)) ? (uint32_t)a.k[gi].rnorm[vi] : 0u;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t tok0 = 16u * (uint32_t)min((c0 >> 4) + 4 * w + i, last_tile);
+#pragma unroll
+    for (int gi = 0; gi < NK; ++gi) {
+      kc.n[gi][i] = buf_half(na.n[gi], tl2, 2u * tok0);
+      kc.r[gi][i] = ((gi == 0 && KP0) || (gi == 1 && KP1)) ? buf_half(na.r[gi], tl2, 2u * tok0) : 0u;
+    }
+#pragma unroll
+    for (int gv = 0; gv < NV; ++gv) kc.nv[gv][i] = buf_half(na.nv[gv], tl2, 2u * tok0);
   }
-#pragma unroll
-  for (int gv = 0; gv < NV; ++gv) kc.nv[gv] = a.v[gv].norm[(int64_t)bg * a.v[gv].seq_stride + tok];
 }
 
 // Value plane words of this wave's 32 coordinates for a chunk's two 128-token
-// steps (steps wholly past the split's end are skipped where they are used).
+// steps (steps wholly past the split's end are skipped where they are used;
+// blocks past the sequence read 0).
 struct VChunk {
   uint32_t w[2][2][4];
 };
 
 template <int NV, int VB0, int VB1>
-__device__ __forceinline__ void load_v(VChunk& vc, const uint32_t* vpk, int64_t vrow0, int vd, int vB, int c0, int te,
-                                       int lane, int vjl0) {
-  // vpk: this wave's value group's planes; vrow0 = first 32-token tile of
-  // the sequence; vd, vB: that group's channels and bits
-  const int gp = lane >> 4;
-  const int last_blk = (te - 1) & ~31;
+__device__ __forceinline__ void load_v(VChunk& vc, const VAddr& va, int c0, int lane) {
+  (void)lane;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const int tblk = min(c0 + 128 * ks + 32 * gp, last_blk);
-    const int64_t vt = vrow0 + (tblk >> 5);
+    const uint32_t soff = (uint32_t)((c0 >> 5) + 4 * ks) * va.tile_bytes;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int jl = vjl0 + 16 * tt + (lane & 15);
-      const uint32_t* pw = vpk + (vt * vd + jl) * vB;
+      const uint32_t voff = va.lane_off + 64u * tt * va.vB;
       if constexpr (NV == 1) {
-        load_words<VB0>(pw, vc.w[ks][tt]);
+        buf_words<VB0>(va.res, voff, soff, vc.w[ks][tt]);
 #pragma unroll
         for (int pp = VB0; pp < 4; ++pp) vc.w[ks][tt][pp] = 0u;
       } else {
         constexpr int PM = VB0 > VB1 ? VB0 : VB1;
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) vc.w[ks][tt][pp] = pp < PM ? pw[min(pp, vB - 1)] : 0u;
+        for (int pp = 0; pp < 4; ++pp)
+          vc.w[ks][tt][pp] = pp < PM ? __builtin_amdgcn_raw_buffer_load_b32(va.res, voff + 4u * min(pp, va.vB - 1), soff, 0) : 0u;
       }
     }
   }
@@ -428,13 +499,34 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
   const int kd = kg1 ? a.k[NK - 1].d : a.k[0].d, kch = kg1 ? a.k[NK - 1].ch : a.k[0].ch;
   const int64_t kss = kg1 ? a.k[NK - 1].seq_stride : a.k[0].seq_stride;
   const uint32_t* kpk = kg1 ? a.k[NK - 1].packed : a.k[0].packed;
-  const int64_t kstep = (int64_t)(kd >> 5) * 16 * kP;  // words per 16-token tile
-  const uint32_t* kbase = kpk + (((int64_t)bg * kss) >> 4) * kstep + ((W - (kch >> 5)) * 16 + tl) * kP;
+  KAddr ka;
+  ka.step = (uint32_t)((kd >> 5) * 16 * kP * 4);
+  ka.seq = kpk + (((int64_t)bg * kss) >> 4) * ((kd >> 5) * 16 * kP);
+  ka.res = make_rsrc(ka.seq, (uint32_t)(kss >> 4) * ka.step);
+  ka.lane_off = (uint32_t)(((W - (kch >> 5)) * 16 + tl) * kP * 4);
+  ka.kP = kP;
+  NAddr na;
+#pragma unroll
+  for (int gi = 0; gi < NK; ++gi) {
+    const uint32_t nb = (uint32_t)(2 * a.k[gi].seq_stride);
+    na.n[gi] = make_rsrc(a.k[gi].norm + (int64_t)bg * a.k[gi].seq_stride, nb);
+    na.r[gi] = make_rsrc(((gi == 0 && KP0) || (gi == 1 && KP1)) ? a.k[gi].rnorm + (int64_t)bg * a.k[gi].seq_stride
+                                                                 : a.k[gi].norm,
+                         ((gi == 0 && KP0) || (gi == 1 && KP1)) ? nb : 0u);
+  }
+#pragma unroll
+  for (int gv = 0; gv < NV; ++gv)
+    na.nv[gv] = make_rsrc(a.v[gv].norm + (int64_t)bg * a.v[gv].seq_stride, (uint32_t)(2 * a.v[gv].seq_stride));
   // this wave's value coordinates 32 w .. 32 w + 31 belong to one value group
   const int vgi = (NV > 1 && 32 * w >= a.v[NV - 1].ch) ? 1 : 0;
   const VGroup& vme = a.v[vgi];
   const int vjl0 = 32 * w - vme.ch;
-  const int64_t vrow0 = ((int64_t)bg * vme.seq_stride) >> 5;
+  VAddr va;
+  va.vB = vme.B;
+  va.tile_bytes = (uint32_t)(vme.d * vme.B * 4);
+  va.res = make_rsrc(vme.packed + (((int64_t)bg * vme.seq_stride) >> 5) * (vme.d * vme.B),
+                     (uint32_t)(vme.seq_stride >> 5) * va.tile_bytes);
+  va.lane_off = (uint32_t)((lane >> 4) * va.tile_bytes + (vjl0 + (lane & 15)) * vme.B * 4);
 
   // ---- load q~ and q^ of this key first (loads complete in issue order),
   // then issue the first chunk's loads
@@ -442,12 +534,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
   const float4 qv4 = *reinterpret_cast<const float4*>(
       tid < kHT * kD / 4 ? a.qt + (int64_t)key * kHT * kD + 4 * tid
                          : a.qh + (int64_t)key * kHT * kD + 4 * (tid - kHT * kD / 4));
-  KChunk<NK, NV> kc;
-  VChunk vc;
-  if (ts < te) {
-    load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kc, a, ts, te, bg, w, lane, kP, kbase, kstep);
-    load_v<NV, VB0, VB1>(vc, vme.packed, vrow0, vme.d, vme.B, ts, te, lane, vjl0);
-  }
+  // (unconditional: an empty split reads token 0 of its sequence, unused)
+  const int tlast = max(te, 1) - 1;
+  KChunk<NK, NV> kA, kB;
+  VChunk vA, vB;
+  load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kA, ka, na, min(ts, tlast), tlast, w, lane);
+  load_v<NV, VB0, VB1>(vA, va, min(ts, tlast), lane);
   // ---- query operands: one power-of-two scale per (head, group, part)
   // bringing the operand below 32 (the fp4 encoding multiplies it by up to
   // 4) -> four fp8 digits per value, laid out in LDS as the A operand of
@@ -470,27 +562,40 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
     }
   }
   __syncthreads();
+  // digits: unit (slot, head, q4) writes one dword (4 consecutive operand
+  // bytes, i.e. coordinates 32 cg + r + 16 t + 4 u, u = 0..3) of each of
+  // the head's 4 digit rows
+  // (two slots per pass; the slot descriptors are read as uniform values and
+  // selected per half of the workgroup, never indexed per lane)
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const Slot sl = a.slot[s];
+  for (int s0 = 0; s0 < NS; s0 += 2) {
+    const int s = s0 + (tid >> 7);
+    if (s >= NS) break;
+    const int h = (tid >> 5) & 3, q4 = tid & 31;
+    const Slot sA = a.slot[s0], sB = a.slot[s0 + 1 < NS ? s0 + 1 : s0];
+    const Slot sl = (tid >> 7) ? sB : sA;
     const int gch = sl.group ? a.k[NK - 1].ch : a.k[0].ch, gd = sl.group ? a.k[NK - 1].d : a.k[0].d;
+    // q4 = kappa / 4: kappa = 32 cg + 8 r + (cw >> 2), cw >> 2 = 4 t + u
+    const int cg = q4 >> 3, r = (q4 >> 1) & 3, t = q4 & 1;
+    const int kappa0 = 4 * q4;
+    const int gp = (kappa0 & 63) >> 4, byte0 = (kappa0 & 15) + 16 * (kappa0 >> 6);
+    const float sc = sl.qjl ? qscale[h][sl.group][1] : sl.alpha * qscale[h][sl.group][0];
+    const float* src = sl.qjl ? &qsh[1][h][0] : &qsh[0][h][0];
+    uint32_t dw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < kHT * kD / kThreads; ++u) {
-      const int e = tid + kThreads * u, h = e / kD, c = e % kD;
-      float v = 0.f;
-      if (c >= gch && c < gch + gd)
-        v = (sl.qjl ? qsh[1][h][c] * qscale[h][sl.group][1] : sl.alpha * qsh[0][h][c] * qscale[h][sl.group][0]) *
-            inv_v(c & 3);
-      const int cg = c >> 5, cw = c & 31;
-      const int kappa = 32 * cg + 8 * (cw & 3) + (cw >> 2);
-      const int gp = (kappa & 63) >> 4, byte = (kappa & 15) + 16 * (kappa >> 6);
+    for (int u = 0; u < 4; ++u) {
+      const int c = 32 * cg + r + 4 * (4 * t + u);
+      float v = (c >= gch && c < gch + gd) ? src[c] * sc * inv_v(r) : 0.f;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const uint32_t d8 = fp8_of(v);
         v -= f32_of_fp8(d8);
-        opb[s][16 * gp + 4 * h + m][byte] = (uint8_t)d8;
+        dw[m] |= d8 << (8 * u);
       }
     }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<uint32_t*>(&opb[s][16 * gp + 4 * h + m][byte0]) = dw[m];
   }
   __syncthreads();
   v8i aop[NS];
@@ -536,14 +641,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
   for (int gv = 0; gv < NV; ++gv) e_run[gv] = -60;
 
   int buf = 0;
-  for (int c0 = ts; c0 < te; c0 += kChunk, buf ^= 1) {
-    // prefetch the next chunk; the last chunk re-reads its own (cached)
-    // addresses so that the loads stay unconditional
+  // one 256-token chunk: kc, vc hold its data; the next chunk is prefetched
+  // into kn, vn (the last chunk re-reads its own, cached, addresses so that
+  // the loads stay unconditional). Called with the two buffers swapped on
+  // alternate chunks, so nothing is copied.
+  auto chunk = [&](const int c0, const KChunk<NK, NV>& kc, const VChunk& vc, KChunk<NK, NV>& kn, VChunk& vn) {
     const int cn = c0 + kChunk < te ? c0 + kChunk : c0;
-    KChunk<NK, NV> kn;
-    VChunk vn;
-    load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kn, a, cn, te, bg, w, lane, kP, kbase, kstep);
-    load_v<NV, VB0, VB1>(vn, vme.packed, vrow0, vme.d, vme.B, cn, te, lane, vjl0);
+    load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kn, ka, na, cn, tlast, w, lane);
+    load_v<NV, VB0, VB1>(vn, va, cn, lane);
 
     // ---------------- scores for this wave's 64 tokens
     float lg[4];
@@ -581,9 +686,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
         float part = (sum4(dm[gi]) - cm[gi]) * inv_mse[gi];
         if ((gi == 0 && KP0) || (gi == 1 && KP1)) {
           const float qjl = (sum4(dq[gi]) - cq[gi]) * inv_qjl[gi];
-          part = fmaf(gam[gi] * hbits(__shfl(kc.r[gi], 16 * i + tl, 64)), qjl, part);
+          part = fmaf(gam[gi] * hbits(kc.r[gi][i]), qjl, part);
         }
-        sc = fmaf(hbits(__shfl(kc.n[gi], 16 * i + tl, 64)), part, sc);
+        sc = fmaf(hbits(kc.n[gi][i]), part, sc);
       }
       const int tok = c0 + 64 * w + 16 * i + tl;
       const bool valid = tok < te && hl < nh;
@@ -596,7 +701,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
     if (tl == 0) red_m[w][hl] = mx;
 #pragma unroll
     for (int gv = 0; gv < NV; ++gv) {
-      const float vm = tqd::wave_max(hbits(kc.nv[gv]));
+      const float vm = wave_max64(fmaxf(fmaxf(hbits(kc.nv[gv][0]), hbits(kc.nv[gv][1])),
+                                        fmaxf(hbits(kc.nv[gv][2]), hbits(kc.nv[gv][3]))));
       if (lane == 0) red_e[w][gv] = exponent_of(vm);
     }
     __syncthreads();
@@ -634,7 +740,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
         const int tau = 64 * w + 16 * i + tl;
         const int ks = tau >> 7, tp = tau & 127;
         const int kappa = 32 * (tp >> 5) + 8 * (tp & 3) + ((tp & 31) >> 2);
-        float r = p[i] * hbits(__shfl(kc.nv[gv], 16 * i + tl, 64)) * sv;
+        float r = p[i] * hbits(kc.nv[gv][i]) * sv;
         uint8_t* dst = &wbuf[buf][gv][ks][4 * hl][kappa];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -662,8 +768,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
       else
         value_step<(VB1 > 0 ? VB1 : 1), VT>(vacc, aw, vc.w[ks]);
     }
-    kc = kn;
-    vc = vn;
+  };
+  for (int c0 = ts; c0 < te;) {
+    chunk(c0, kA, vA, kB, vB);
+    c0 += kChunk;
+    buf ^= 1;
+    if (c0 >= te) break;
+    chunk(c0, kB, vB, kA, vA);
+    c0 += kChunk;
+    buf ^= 1;
   }
 
   // ---------------- partial results of this split
