@@ -110,6 +110,8 @@ def decode_single_layer(args):
     Rv = synth.haar_orthogonal(d, 2, synth.STREAM_R_V)
     Rk_t, Sk_t, Rv_t = dev(Rk), dev(Sk), dev(Rv)
     qk = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, Rk_t, Sk_t)
+    SRk = torch.empty(tq.tq_fold_bytes(d) // 4, dtype=torch.float32, device="cuda")
+    tq.tq_quantizer_fold(qk, SRk)  # S R once per quantiser (setup, untimed)
     qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
     kp = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, n) // 4, dtype=torch.int32, device="cuda")
     vp = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, n) // 4, dtype=torch.int32, device="cuda")
@@ -280,6 +282,10 @@ def longctx_decode(steps=5):
             R_t = dev(synth.haar_orthogonal(gd, 40 + gi + 10 * stream))
             S_t = dev(synth.gaussian_matrix(gd, gd, 40 + gi + 10 * stream)) if var == tq.TQ_PROD else None
             q = tq.tq_quantizer_init(gd, bits, var, R_t, S_t)
+            if var == tq.TQ_PROD:
+                SR_t = torch.empty(tq.tq_fold_bytes(gd) // 4, dtype=torch.float32, device="cuda")
+                tq.tq_quantizer_fold(q, SR_t)
+                keep.append(SR_t)
             pk = torch.empty(tq.tq_packed_bytes(gd, bits, var, layout, n) // 4, dtype=torch.int32, device="cuda")
             nr = torch.empty(n, dtype=torch.int16, device="cuda")
             rr = torch.empty(n, dtype=torch.int16, device="cuda") if var == tq.TQ_PROD else None

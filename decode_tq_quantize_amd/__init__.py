@@ -33,14 +33,14 @@ TQ_MAX_GROUPS = 4
 EXPORTS = [
     "tq_build_codebook", "tq_quantizer_init", "tq_packed_bytes", "tq_status_string",
     "tq_quantize_kv", "tq_decode_workspace_bytes", "tq_decode_attn",
-    "tq_search_workspace_bytes", "tq_search_topk",
+    "tq_search_workspace_bytes", "tq_search_topk", "tq_fold_bytes", "tq_fold_qjl",
 ]
 
 
 class tq_quantizer(ctypes.Structure):
     _fields_ = [
         ("d", c_int), ("mse_bits", c_int), ("variant", c_int),
-        ("R", c_void_p), ("S", c_void_p),
+        ("R", c_void_p), ("S", c_void_p), ("SR", c_void_p),
         ("centroids", c_float * TQ_MAX_LEVELS), ("thresholds", c_float * (TQ_MAX_LEVELS - 1)),
     ]
 
@@ -94,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.tq_search_topk.argtypes = [POINTER(tq_group), c_int64, c_void_p, c_int, c_int, c_void_p, c_void_p,
                                      c_void_p, c_size_t, c_void_p]
         L.tq_search_topk.restype = c_int
+        L.tq_fold_bytes.argtypes = [c_int]
+        L.tq_fold_bytes.restype = c_size_t
+        L.tq_fold_qjl.argtypes = [POINTER(tq_quantizer), c_void_p, c_void_p]
+        L.tq_fold_qjl.restype = c_int
         _lib = L
     return _lib
 
@@ -139,6 +143,23 @@ def tq_build_codebook(d: int, mse_bits: int, max_iter: int = 0):
 def tq_quantizer_init(d: int, mse_bits: int, variant: int, R, S=None) -> tq_quantizer:
     q = tq_quantizer()
     _check(lib().tq_quantizer_init(ctypes.byref(q), d, mse_bits, variant, _ptr(R), _ptr(S)), "tq_quantizer_init")
+    return q
+
+
+def tq_fold_bytes(d: int) -> int:
+    return int(lib().tq_fold_bytes(d))
+
+
+def tq_fold_qjl(q: tq_quantizer, SR, stream=None) -> None:
+    """Fill SR (tq_fold_bytes(q.d) bytes) with S R and its largest row norm;
+    assign q.SR = SR's address to use it (see tq_quantizer_fold)."""
+    _check(lib().tq_fold_qjl(ctypes.byref(q), _ptr(SR), _stream(stream)), "tq_fold_qjl")
+
+
+def tq_quantizer_fold(q: tq_quantizer, SR, stream=None) -> tq_quantizer:
+    """tq_fold_qjl into SR, then return q with q.SR pointing at it."""
+    tq_fold_qjl(q, SR, stream)
+    q.SR = _ptr(SR)
     return q
 
 

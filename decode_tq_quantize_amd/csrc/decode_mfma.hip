@@ -21,9 +21,11 @@
 //    constant part sum a u_r is removed exactly with one more MFMA against
 //    the constant operand 4 u_r;
 //  * the real operand (query coefficients, softmax weights) is split into
-//    four fp8 e4m3 digits v = d0 + d1 + d2 + d3 (each digit the fp8 rounding
-//    of what the previous ones left), carried as four MFMA rows, and summed
-//    after the product: about 16 significant bits, fp32 accumulation.
+//    four fp8 e4m3 digits v = d0 + d1/16 + d2/256 + d3/4096 (each digit the
+//    fp8 rounding of what the previous ones left, scaled up by 16 so that it
+//    stays a normal fp8 number), carried as four MFMA rows and recombined
+//    with those weights after the product: about 16 significant bits, fp32
+//    accumulation.
 // Rows of every MFMA are (query head, digit) = 4 x 4; columns are 16 tokens
 // (scores) or 16 value coordinates (value sums).
 //
@@ -72,6 +74,7 @@ struct KGroup {
   const uint16_t* rnorm;
   const float* R;
   const float* S;
+  const float* SR;  // S R followed by its largest row norm, or null
   int64_t seq_stride;
   int ch, d, B, prod;
   float gamma;
@@ -98,7 +101,9 @@ struct Args {
   int nk, nv, nslots;
   KGroup k[kMaxKG];
   VGroup v[kMaxVG];
-  Slot slot[kMaxSlots];
+  int slot_group;             // bit s: slot s belongs to key group 1
+  int slot_qjl;               // bit s: slot s is the QJL part of its group
+  float slot_alpha[kMaxSlots];  // Walsh coefficient of codebook slot s (1 for QJL)
   const void* q;
   int qbf16;
   int B, Hq, Hkv, G, HT, T_max;
@@ -108,14 +113,28 @@ struct Args {
   float* scores_out;
   float* qt;         // [keys][4 heads][kD] q~ = R q per key group
   float* qh;         // [keys][4 heads][kD] q^ = S q~ (PROD groups, else 0)
+  float* srow;       // [kD / kRowSlice] largest row norm of S in each row slice
+  float* ascale;     // [keys][4 heads][kMaxKG][2] inverse operand scales (codebook, QJL)
+  uint32_t* aops;    // [keys][nslots][64 lanes][8 dwords] query operands of every slot
   float* partial;    // [B * Hq][splits][kD + 2] (max, sum, rotated accumulator)
   float* out;
 };
+
+// Slot s of the operand table for a per-lane s: the coefficients are read
+// as uniform values and selected, so no per-lane access to the argument
+// memory is made.
+__device__ __forceinline__ Slot slot_of(const Args& a, int s) {
+  float al = a.slot_alpha[0];
+#pragma unroll
+  for (int t = 1; t < kMaxSlots; ++t) al = s == t ? a.slot_alpha[t] : al;
+  return Slot{(a.slot_group >> s) & 1, (a.slot_qjl >> s) & 1, al};
+}
 
 __device__ __forceinline__ uint32_t fp8_of(float v) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false) & 0xffu;
 }
 __device__ __forceinline__ float f32_of_fp8(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+
 
 // 32 plane bits -> fp4 operand; register r, nibble i <- bit 4 i + r.
 __device__ __forceinline__ v8i expand_bits(uint32_t w) {
@@ -177,7 +196,15 @@ __device__ __forceinline__ int exponent_of(float x) {
   return x > 0.f ? e : -60;
 }
 
-__device__ __forceinline__ float sum4(v4f x) { return (x[0] + x[1]) + (x[2] + x[3]); }
+// Digits of a real operand: v = d0 + d1 / 16 + d2 / 256 + d3 / 4096, each
+// d_m the fp8 e4m3 rounding of the residual left by the previous digits,
+// scaled by 16 per digit so that every digit stays in the normal fp8 range
+// (relative precision about 2^-16; no absolute floor). The four digits are
+// four rows of the MFMA; wsum4 recombines them.
+constexpr float kDigitStep = 16.f;
+__device__ __forceinline__ float wsum4(v4f x) {
+  return (x[0] + x[1] * (1.f / 16.f)) + (x[2] * (1.f / 256.f) + x[3] * (1.f / 4096.f));
+}
 
 // Odd subsets of B code planes, in ascending bitmask order (the host orders
 // the Walsh coefficients the same way).
@@ -203,46 +230,220 @@ __host__ __device__ constexpr int odd_mask(int B, int t) {
 // tile's 4 heads; the 16 partial sums of a row meet by lane exchanges.
 constexpr int kQtThreads = 256;
 
-template <bool PROJECT>
-__global__ __launch_bounds__(kQtThreads) void qtransform_kernel(Args a) {
+// Both transforms in one pass when S R is available: workgroup (key, 16-row
+// slice) forms rows of q~ = R q and q^ = (S R) q and writes the fp8 digit
+// operands of every slot for those coordinates. Operand scales come from
+// bounds that need no other slice: |q~_c| <= |R_c| |q| = |q| (R orthogonal)
+// and |q^_c| <= max_c |(S R)_c| |q|, each with 0.1 % room for rounding.
+__global__ __launch_bounds__(kQtThreads) void qfused_kernel(Args a) {
+  __shared__ float qts[kHT][kRowSlice], qhs[kHT][kRowSlice];
+  __shared__ float sc_mse[kHT], sc_qjl[kHT];
+  const int nk = a.nk, Hkv = a.Hkv, HT = a.HT, G = a.G, Hq = a.Hq, qbf16 = a.qbf16, nslots = a.nslots;
+  const int k1ch = a.k[1].ch, k0d = a.k[0].d, k1d = a.k[1].d, k0p = a.k[0].prod, k1p = a.k[1].prod;
+  const float* R0 = a.k[0].R;
+  const float* R1 = a.k[1].R;
+  const float* F0 = a.k[0].SR;
+  const float* F1 = a.k[1].SR;
+  const float amax0 = a.k[0].amax, amax1 = a.k[1].amax;
   const int key = blockIdx.x, slice = blockIdx.y;
-  const int b = key / (a.Hkv * a.HT);
-  const int g = (key / a.HT) % a.Hkv;
-  const int ht = key % a.HT;
-  const int h0 = g * a.G + ht * kHT;
-  const int nh = min(kHT, a.G - ht * kHT);
+  const int b = key / (Hkv * HT);
+  const int g = (key / HT) % Hkv;
+  const int ht = key % HT;
+  const int h0 = g * G + ht * kHT;
+  const int nh = min(kHT, G - ht * kHT);
   const int tid = threadIdx.x, cb = tid & 15;
-  const int i = slice * kRowSlice + (tid >> 4);  // output channel (stacked row)
-  // the slice lies in one key group (group sizes are multiples of 32)
-  const bool g1 = a.nk > 1 && slice * kRowSlice >= a.k[1].ch;
-  const int d = g1 ? a.k[1].d : a.k[0].d, ch = g1 ? a.k[1].ch : a.k[0].ch;
-  const int prod = g1 ? a.k[1].prod : a.k[0].prod;
-  const float* M = PROJECT ? (g1 ? a.k[1].S : a.k[0].S) : (g1 ? a.k[1].R : a.k[0].R);
+  const int i = slice * kRowSlice + (tid >> 4);
+  const int gsl = ((nk > 1) & (slice * kRowSlice >= k1ch)) ? 1 : 0;
+  const bool g1 = gsl == 1;
+  const int d = g1 ? k1d : k0d, ch = g1 ? k1ch : 0;
+  const int prod = g1 ? k1p : k0p;
+  const float* Rm = g1 ? R1 : R0;
+  const float* Fm = g1 ? F1 : F0;
   const bool on = 8 * cb < d;
-  const int col = ch + min(8 * cb, d - 8);  // clamped so that every load is in range
+  const int col = ch + min(8 * cb, d - 8);
   const int r = i - ch;
 
-  if (PROJECT && !prod) {  // no sign sketch in this group: q^ is not used
-    if (cb < kHT) a.qh[((int64_t)key * kHT + cb) * kD + i] = 0.f;
-    return;
-  }
-  const float4* mr = reinterpret_cast<const float4*>(M + (int64_t)r * d + (col - ch));
-  const float4 m0 = mr[0], m1 = mr[1];
+  // every load unconditional and of one shape (a group without a sketch
+  // reads R in place of S R and ignores it), so that none waits on another
+  const float* Fsrc = prod ? Fm : Rm;
+  const float4* rr = reinterpret_cast<const float4*>(Rm + (int64_t)r * d + (col - ch));
+  const float4* fr = reinterpret_cast<const float4*>(Fsrc + (int64_t)r * d + (col - ch));
+  const float4 m0 = rr[0], m1 = rr[1];
+  float4 f0 = fr[0], f1 = fr[1];
+  float fmax = Fsrc[prod ? (int64_t)d * d : 0];
   float x[kHT][8];
-  if (PROJECT) {
+  if (qbf16) {
 #pragma unroll
     for (int h = 0; h < kHT; ++h) {
-      const float4* xr = reinterpret_cast<const float4*>(a.qt + ((int64_t)key * kHT + h) * kD + col);
+      const int64_t qo = ((int64_t)b * Hq + h0 + min(h, nh - 1)) * kD + col;
+      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qo);
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[h][2 * k] = __uint_as_float(wd[k] << 16);
+        x[h][2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < kHT; ++h) {
+      const int64_t qo = ((int64_t)b * Hq + h0 + min(h, nh - 1)) * kD + col;
+      const float4* xr = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qo);
       const float4 u = xr[0], v = xr[1];
       x[h][0] = u.x; x[h][1] = u.y; x[h][2] = u.z; x[h][3] = u.w;
       x[h][4] = v.x; x[h][5] = v.y; x[h][6] = v.z; x[h][7] = v.w;
     }
-  } else if (a.qbf16) {
+  }
+  if (!prod) {
+    f0 = f1 = make_float4(0.f, 0.f, 0.f, 0.f);
+    fmax = 0.f;
+  }
+  float ot = 0.f, oh = 0.f, on2 = 0.f;
+#pragma unroll
+  for (int h = 0; h < kHT; ++h) {
+    const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    const float fv[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+    float t = 0.f, u = 0.f, n2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      t = fmaf(mv[k], x[h][k], t);
+      u = fmaf(fv[k], x[h][k], u);
+      n2 = fmaf(x[h][k], x[h][k], n2);
+    }
+    const bool use = on && h < nh;
+    t = use ? t : 0.f;
+    u = use ? u : 0.f;
+    n2 = use ? n2 : 0.f;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      t += __shfl_xor(t, o, 16);
+      u += __shfl_xor(u, o, 16);
+      n2 += __shfl_xor(n2, o, 16);
+    }
+    if (cb == h) {
+      ot = t;
+      oh = u;
+      on2 = n2;
+    }
+  }
+  if (cb < kHT) {
+    a.qt[((int64_t)key * kHT + cb) * kD + i] = ot;
+    a.qh[((int64_t)key * kHT + cb) * kD + i] = oh;
+    qts[cb][tid >> 4] = ot;
+    qhs[cb][tid >> 4] = oh;
+    if ((tid >> 4) == 0) {  // |q| of head cb over the group's channels -> the two scales
+      const float qn = sqrtf(on2) * 1.001f;
+      const float mt = qn * (g1 ? amax1 : amax0), mh = qn * fmax;
+      const float sm = mt > 0.f ? ldexpf(1.f, 6 - exponent_of(mt)) : 1.f;
+      const float sq = mh > 0.f ? ldexpf(1.f, 6 - exponent_of(mh)) : 1.f;
+      sc_mse[cb] = sm;
+      sc_qjl[cb] = sq;
+      if (slice == ch / kRowSlice) {
+        a.ascale[(((int64_t)key * kHT + cb) * kMaxKG + gsl) * 2 + 0] = 1.f / sm;
+        a.ascale[(((int64_t)key * kHT + cb) * kMaxKG + gsl) * 2 + 1] = 1.f / sq;
+      }
+    }
+  }
+  __syncthreads();
+  // unit (slot, head, r): coordinates c = 16 slice + r + 4 u, u = 0..3 (4
+  // consecutive operand bytes kappa0 + u of the head's 4 digit rows); slots
+  // of the other key group get zeros here
+  const int cg = slice >> 1;
+  for (int unit = tid; unit < nslots * kHT * 4; unit += kQtThreads) {
+    const int s2 = unit >> 4, h = (unit >> 2) & 3, rq = unit & 3;
+    const Slot sl = slot_of(a, s2);
+    const int kappa0 = 32 * cg + 8 * rq + 4 * (slice & 1);
+    const int gp = (kappa0 & 63) >> 4, byte0 = (kappa0 & 15) + 16 * (kappa0 >> 6);
+    const float sc = (sl.qjl ? sc_qjl[h] : sl.alpha * sc_mse[h]) * inv_v(rq);
+    uint32_t dw[4] = {0u, 0u, 0u, 0u};
+    if (sl.group == gsl) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float v = (sl.qjl ? qhs[h][rq + 4 * u] : qts[h][rq + 4 * u]) * sc;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t d8 = fp8_of(v);
+          v = (v - f32_of_fp8(d8)) * kDigitStep;
+          dw[m] |= d8 << (8 * u);
+        }
+      }
+    }
+    uint32_t* dst = a.aops + ((int64_t)key * nslots + s2) * 512;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dst[(16 * gp + 4 * h + m) * 8 + byte0 / 4] = dw[m];
+  }
+}
+
+template <bool PROJECT>
+__global__ __launch_bounds__(kQtThreads) void qtransform_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) float qts[kHT][kD];  // q~ of the slice's key group (project)
+  __shared__ float sc_mse[kHT], sc_qjl[kHT];
+  __shared__ float qhs[kHT][kRowSlice];
+  __shared__ float wred[kQtThreads / 64];
+  // every argument field this kernel needs is read up front and
+  // unconditionally (both groups), so the reads overlap instead of chaining
+  const int nk = a.nk, Hkv = a.Hkv, HT = a.HT, G = a.G, Hq = a.Hq, qbf16 = a.qbf16;
+  const int k1ch = a.k[1].ch, k0d = a.k[0].d, k1d = a.k[1].d;
+  const int k0p = a.k[0].prod, k1p = a.k[1].prod;
+  const float* R0 = a.k[0].R;
+  const float* R1 = a.k[1].R;
+  const float* S0 = a.k[0].S;
+  const float* S1 = a.k[1].S;
+  const void* qsrc = a.q;
+  float* qt = a.qt;
+  float* qh = a.qh;
+  float* srow = a.srow;
+  float* ascale = a.ascale;
+  uint32_t* aops = a.aops;
+  const int nslots = a.nslots;
+  const float amax0 = a.k[0].amax, amax1 = a.k[1].amax;
+  const int key = blockIdx.x, slice = blockIdx.y;
+  const int b = key / (Hkv * HT);
+  const int g = (key / HT) % Hkv;
+  const int ht = key % HT;
+  const int h0 = g * G + ht * kHT;
+  const int nh = min(kHT, G - ht * kHT);
+  const int tid = threadIdx.x, cb = tid & 15, lane = tid & 63, wv = tid >> 6;
+  const int i = slice * kRowSlice + (tid >> 4);  // output channel (stacked row)
+  // the slice lies in one key group (group sizes are multiples of 32)
+  const int gsl = ((nk > 1) & (slice * kRowSlice >= k1ch)) ? 1 : 0;
+  const bool g1 = gsl == 1;
+  const int d = g1 ? k1d : k0d, ch = g1 ? k1ch : 0;
+  const int prod = g1 ? k1p : k0p;
+  const float* Rm = g1 ? R1 : R0;
+  const float* Sm = g1 ? S1 : S0;
+  const bool on = 8 * cb < d;
+  const int col = ch + min(8 * cb, d - 8);  // clamped so that every load is in range
+  const int r = i - ch;
+
+  // this thread's 8 entries of row r of R (rotate) or S (project); the
+  // rotate launch also reads S to bound |S q~| by its row norms
+  float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0, s0v = m0, s1v = m0;
+  if (!PROJECT || prod) {
+    const float4* mr = reinterpret_cast<const float4*>((PROJECT ? Sm : Rm) + (int64_t)r * d + (col - ch));
+    m0 = mr[0];
+    m1 = mr[1];
+  }
+  if (!PROJECT && prod && key == 0) {
+    const float4* sr = reinterpret_cast<const float4*>(Sm + (int64_t)r * d + (col - ch));
+    s0v = sr[0];
+    s1v = sr[1];
+  }
+  float x[kHT][8];
+  if (PROJECT) {
+#pragma unroll
+    for (int h = 0; h < kHT; ++h) {
+      const float4* xr = reinterpret_cast<const float4*>(qt + ((int64_t)key * kHT + h) * kD + col);
+      const float4 u = xr[0], v = xr[1];
+      x[h][0] = u.x; x[h][1] = u.y; x[h][2] = u.z; x[h][3] = u.w;
+      x[h][4] = v.x; x[h][5] = v.y; x[h][6] = v.z; x[h][7] = v.w;
+    }
+  } else if (qbf16) {
 #pragma unroll
     for (int h = 0; h < kHT; ++h) {
       const int hr = min(h, nh - 1);
-      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
-                                                      ((int64_t)b * a.Hq + h0 + hr) * kD + col);
+      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(qsrc) +
+                                                      ((int64_t)b * Hq + h0 + hr) * kD + col);
       const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -255,11 +456,18 @@ __global__ __launch_bounds__(kQtThreads) void qtransform_kernel(Args a) {
     for (int h = 0; h < kHT; ++h) {
       const int hr = min(h, nh - 1);
       const float4* xr =
-          reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + ((int64_t)b * a.Hq + h0 + hr) * kD + col);
+          reinterpret_cast<const float4*>(static_cast<const float*>(qsrc) + ((int64_t)b * Hq + h0 + hr) * kD + col);
       const float4 u = xr[0], v = xr[1];
       x[h][0] = u.x; x[h][1] = u.y; x[h][2] = u.z; x[h][3] = u.w;
       x[h][4] = v.x; x[h][5] = v.y; x[h][6] = v.z; x[h][7] = v.w;
     }
+  }
+  // (project) the slot table, read one entry per thread, and the S row-norm
+  // maxima of the group's slices, both in flight with the loads above
+  float srow_v = 0.f;
+  if (PROJECT) {
+    const int q = min(ch / kRowSlice + (tid & 7), (ch + d) / kRowSlice - 1);
+    srow_v = srow[q];
   }
   float acc[kHT];
 #pragma unroll
@@ -278,13 +486,100 @@ __global__ __launch_bounds__(kQtThreads) void qtransform_kernel(Args a) {
     v += __shfl_xor(v, 1, 16);
     acc[h] = v;
   }
-  if (cb < kHT) {
-    float v = acc[0];
+  float out = acc[0];
 #pragma unroll
-    for (int h = 1; h < kHT; ++h)
-      if (cb == h) v = acc[h];
-    float* dst = PROJECT ? a.qh : a.qt;
-    dst[((int64_t)key * kHT + cb) * kD + i] = v;
+  for (int h = 1; h < kHT; ++h)
+    if (cb == h) out = acc[h];
+  if (!PROJECT) {
+    if (cb < kHT) qt[((int64_t)key * kHT + cb) * kD + i] = out;
+    if (key == 0) {  // row norms of S in this slice (the same for every key)
+      float n2 = 0.f;
+      if (on && prod) {
+        n2 = s0v.x * s0v.x + s0v.y * s0v.y + s0v.z * s0v.z + s0v.w * s0v.w + s1v.x * s1v.x + s1v.y * s1v.y +
+             s1v.z * s1v.z + s1v.w * s1v.w;
+      }
+      n2 += __shfl_xor(n2, 8, 16);
+      n2 += __shfl_xor(n2, 4, 16);
+      n2 += __shfl_xor(n2, 2, 16);
+      n2 += __shfl_xor(n2, 1, 16);
+      const float mx = tqd::wave_max(n2);
+      if (lane == 0) wred[wv] = mx;
+      __syncthreads();
+      if (tid == 0) srow[slice] = sqrtf(fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3])));
+    }
+    return;
+  }
+
+  // ---- project only: q^ rows and the operands (fp8 digits) of every slot
+  // for this slice's coordinates. Codebook slots: scale from the largest
+  // |q~| of the group times the largest |Walsh coefficient|. QJL slot: scale
+  // from the bound |(S q~)_c| <= |S_c| |q~| with the largest row norm of S.
+  if (cb < kHT) {
+    qh[((int64_t)key * kHT + cb) * kD + i] = prod ? out : 0.f;
+    qhs[cb][tid >> 4] = prod ? out : 0.f;
+  }
+  if ((tid >> 4) == 0 && on) {
+#pragma unroll
+    for (int h = 0; h < kHT; ++h)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qts[h][col + k] = x[h][k];
+  }
+  // lanes 0..7 of each wave hold the (clamped) slices of the group
+  float smax = srow_v;
+  smax = fmaxf(smax, __shfl_xor(smax, 4, 8));
+  smax = fmaxf(smax, __shfl_xor(smax, 2, 8));
+  smax = fmaxf(smax, __shfl_xor(smax, 1, 8));
+  __syncthreads();
+  {
+    // wave w: head w; max and norm over the group's channels
+    float mt = 0.f, n2 = 0.f;
+    for (int c = ch + lane; c < ch + d; c += 64) {
+      const float v = qts[wv][c];
+      mt = fmaxf(mt, fabsf(v));
+      n2 = fmaf(v, v, n2);
+    }
+    mt = tqd::wave_max(mt) * (g1 ? amax1 : amax0);
+    n2 = tqd::wave_sum(n2);
+    if (lane == 0) {
+      const float mq = sqrtf(n2) * smax * 1.0001f;  // the bound, with room for rounding
+      const float sm = mt > 0.f ? ldexpf(1.f, 5 - exponent_of(mt)) : 1.f;
+      const float sq = mq > 0.f ? ldexpf(1.f, 5 - exponent_of(mq)) : 1.f;
+      sc_mse[wv] = sm;
+      sc_qjl[wv] = sq;
+      if (slice == ch / kRowSlice) {
+        ascale[(((int64_t)key * kHT + wv) * kMaxKG + gsl) * 2 + 0] = 1.f / sm;
+        ascale[(((int64_t)key * kHT + wv) * kMaxKG + gsl) * 2 + 1] = 1.f / sq;
+      }
+    }
+  }
+  __syncthreads();
+  // unit (slot, head, r): coordinates c = 32 cg + r + 16 (slice & 1) + 4 u,
+  // u = 0..3, i.e. 4 consecutive operand bytes kappa0 + u of the head's 4
+  // digit rows; slots of the other key group get zeros here
+  const int cg = slice >> 1;
+  for (int unit = tid; unit < nslots * kHT * 4; unit += kQtThreads) {
+    const int s2 = unit >> 4, h = (unit >> 2) & 3, rr = unit & 3;
+    const Slot sl = slot_of(a, s2);
+    const int kappa0 = 32 * cg + 8 * rr + 4 * (slice & 1);
+    const int gp = (kappa0 & 63) >> 4, byte0 = (kappa0 & 15) + 16 * (kappa0 >> 6);
+    const float sc = (sl.qjl ? sc_qjl[h] : sl.alpha * sc_mse[h]) * inv_v(rr);
+    uint32_t dw[4] = {0u, 0u, 0u, 0u};
+    if (sl.group == gsl) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = 32 * cg + rr + 16 * (slice & 1) + 4 * u;
+        float v = (sl.qjl ? qhs[h][c - slice * kRowSlice] : qts[h][c]) * sc;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t d8 = fp8_of(v);
+          v = (v - f32_of_fp8(d8)) * kDigitStep;
+          dw[m] |= d8 << (8 * u);
+        }
+      }
+    }
+    uint32_t* dst = aops + ((int64_t)key * nslots + s2) * 512;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dst[(16 * gp + 4 * h + m) * 8 + byte0 / 4] = dw[m];
   }
 }
 
@@ -477,9 +772,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
   __shared__ float red_m[4][kHT];
   __shared__ int red_e[4][NV];
   __shared__ float fin_l[4][kHT];
-  __shared__ __attribute__((aligned(16))) float qsh[2][kHT][kD];           // q~, q^ of this key
-  __shared__ float qscale[kHT][kMaxKG][2];
-  __shared__ __attribute__((aligned(16))) uint8_t opb[NS][64][32];         // A operands per slot
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 4, tl = lane & 15;
@@ -528,97 +820,43 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
                      (uint32_t)(vme.seq_stride >> 5) * va.tile_bytes);
   va.lane_off = (uint32_t)((lane >> 4) * va.tile_bytes + (vjl0 + (lane & 15)) * vme.B * 4);
 
-  // ---- load q~ and q^ of this key first (loads complete in issue order),
-  // then issue the first chunk's loads
+  // ---- query operands of every slot and their inverse scales (built by the
+  // query-transform kernels); issued before the first chunk's loads, so
+  // they complete first
   const int key = (b * a.Hkv + g) * a.HT + ht;
-  const float4 qv4 = *reinterpret_cast<const float4*>(
-      tid < kHT * kD / 4 ? a.qt + (int64_t)key * kHT * kD + 4 * tid
-                         : a.qh + (int64_t)key * kHT * kD + 4 * (tid - kHT * kD / 4));
-  // (unconditional: an empty split reads token 0 of its sequence, unused)
+  v8i aop[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const v4i* src = reinterpret_cast<const v4i*>(a.aops + (((int64_t)key * NS + s) * 64 + lane) * 8);
+    const v4i lo = src[0], hi = src[1];
+    aop[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  float inv_mse[NK], inv_qjl[NK];
+#pragma unroll
+  for (int gi = 0; gi < NK; ++gi) {
+    const float2 sc = *reinterpret_cast<const float2*>(a.ascale + (((int64_t)key * kHT + hl) * kMaxKG + gi) * 2);
+    inv_mse[gi] = sc.x;
+    inv_qjl[gi] = sc.y;
+  }
+  // ---- the first chunk's loads (unconditional: an empty split reads token
+  // 0 of its sequence, unused)
   const int tlast = max(te, 1) - 1;
   KChunk<NK, NV> kA, kB;
   VChunk vA, vB;
   load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kA, ka, na, min(ts, tlast), tlast, w, lane);
   load_v<NV, VB0, VB1>(vA, va, min(ts, tlast), lane);
-  // ---- query operands: one power-of-two scale per (head, group, part)
-  // bringing the operand below 32 (the fp4 encoding multiplies it by up to
-  // 4) -> four fp8 digits per value, laid out in LDS as the A operand of
-  // every slot
-  reinterpret_cast<float4*>(&qsh[0][0][0])[tid] = qv4;
-  __syncthreads();
-#pragma unroll
-  for (int gi = 0; gi < NK; ++gi) {
-    const int gch = a.k[gi].ch, gd = a.k[gi].d;
-    float mt = 0.f, mh = 0.f;
-    for (int c = gch + lane; c < gch + gd; c += 64) {
-      mt = fmaxf(mt, fabsf(qsh[0][w][c]));
-      mh = fmaxf(mh, fabsf(qsh[1][w][c]));
-    }
-    mt = tqd::wave_max(mt) * a.k[gi].amax;
-    mh = tqd::wave_max(mh);
-    if (lane == 0) {
-      qscale[w][gi][0] = mt > 0.f ? ldexpf(1.f, 5 - exponent_of(mt)) : 1.f;
-      qscale[w][gi][1] = mh > 0.f ? ldexpf(1.f, 5 - exponent_of(mh)) : 1.f;
-    }
-  }
-  __syncthreads();
-  // digits: unit (slot, head, q4) writes one dword (4 consecutive operand
-  // bytes, i.e. coordinates 32 cg + r + 16 t + 4 u, u = 0..3) of each of
-  // the head's 4 digit rows
-  // (two slots per pass; the slot descriptors are read as uniform values and
-  // selected per half of the workgroup, never indexed per lane)
-#pragma unroll
-  for (int s0 = 0; s0 < NS; s0 += 2) {
-    const int s = s0 + (tid >> 7);
-    if (s >= NS) break;
-    const int h = (tid >> 5) & 3, q4 = tid & 31;
-    const Slot sA = a.slot[s0], sB = a.slot[s0 + 1 < NS ? s0 + 1 : s0];
-    const Slot sl = (tid >> 7) ? sB : sA;
-    const int gch = sl.group ? a.k[NK - 1].ch : a.k[0].ch, gd = sl.group ? a.k[NK - 1].d : a.k[0].d;
-    // q4 = kappa / 4: kappa = 32 cg + 8 r + (cw >> 2), cw >> 2 = 4 t + u
-    const int cg = q4 >> 3, r = (q4 >> 1) & 3, t = q4 & 1;
-    const int kappa0 = 4 * q4;
-    const int gp = (kappa0 & 63) >> 4, byte0 = (kappa0 & 15) + 16 * (kappa0 >> 6);
-    const float sc = sl.qjl ? qscale[h][sl.group][1] : sl.alpha * qscale[h][sl.group][0];
-    const float* src = sl.qjl ? &qsh[1][h][0] : &qsh[0][h][0];
-    uint32_t dw[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = 32 * cg + r + 4 * (4 * t + u);
-      float v = (c >= gch && c < gch + gd) ? src[c] * sc * inv_v(r) : 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t d8 = fp8_of(v);
-        v -= f32_of_fp8(d8);
-        dw[m] |= d8 << (8 * u);
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      *reinterpret_cast<uint32_t*>(&opb[s][16 * gp + 4 * h + m][byte0]) = dw[m];
-  }
-  __syncthreads();
-  v8i aop[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const v4i lo = *reinterpret_cast<const v4i*>(&opb[s][lane][0]);
-    const v4i hi = *reinterpret_cast<const v4i*>(&opb[s][lane][16]);
-    aop[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
   // constant parts of the fp4 encoding, per (group, class); scales of this lane's head
-  float cm[NK], cq[NK], inv_mse[NK], inv_qjl[NK], gam[NK];
+  float cm[NK], cq[NK], gam[NK];
   {
     const v8i cop = const_operand();
 #pragma unroll
     for (int gi = 0; gi < NK; ++gi) {
       cm[gi] = cq[gi] = 0.f;
-      inv_mse[gi] = 1.f / qscale[hl][gi][0];
-      inv_qjl[gi] = 1.f / qscale[hl][gi][1];
       gam[gi] = a.k[gi].gamma;
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const float c4 = 0.25f * sum4(mfma_fp8_fp4(aop[s], cop, v4f{0.f, 0.f, 0.f, 0.f}));
+      const float c4 = 0.25f * wsum4(mfma_fp8_fp4(aop[s], cop, v4f{0.f, 0.f, 0.f, 0.f}));
       const int gi = s < NS0 ? 0 : 1;
       const bool q = (gi == 0) ? (KP0 && s == NS0 - 1) : (KP1 && s == NS - 1);
       if (q)
@@ -683,9 +921,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
       float sc = 0.f;
 #pragma unroll
       for (int gi = 0; gi < NK; ++gi) {
-        float part = (sum4(dm[gi]) - cm[gi]) * inv_mse[gi];
+        float part = (wsum4(dm[gi]) - cm[gi]) * inv_mse[gi];
         if ((gi == 0 && KP0) || (gi == 1 && KP1)) {
-          const float qjl = (sum4(dq[gi]) - cq[gi]) * inv_qjl[gi];
+          const float qjl = (wsum4(dq[gi]) - cq[gi]) * inv_qjl[gi];
           part = fmaf(gam[gi] * hbits(kc.r[gi][i]), qjl, part);
         }
         sc = fmaf(hbits(kc.n[gi][i]), part, sc);
@@ -745,7 +983,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const uint32_t d = fp8_of(r);
-          r -= f32_of_fp8(d);
+          r = (r - f32_of_fp8(d)) * kDigitStep;
           dst[128 * m] = (uint8_t)d;
         }
       }
@@ -787,13 +1025,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
     float* part = a.partial + (((int64_t)b * a.Hq + h0 + hl) * a.splits + split) * (kD + 2);
     const int ef = (NV > 1 && vgi) ? e_run[NV - 1] : e_run[0];
     const float unscale = ldexpf(1.f, ef - 5);
-    const float csub = 0.25f * sum4(vcon) * vme.alpha_sum;
+    const float csub = 0.25f * wsum4(vcon) * vme.alpha_sum;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       float v = -csub;
 #pragma unroll
       for (int s = 0; s < VT; ++s)
-        if (s < vme.ntypes) v = fmaf(vme.alpha[s], sum4(vacc[tt][s]), v);
+        if (s < vme.ntypes) v = fmaf(vme.alpha[s], wsum4(vacc[tt][s]), v);
       part[2 + 32 * w + 16 * tt + tl] = v * unscale;
     }
     if (w == 0 && tl == 0) {
@@ -1002,10 +1240,12 @@ DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int
   p.Dv = kD;
   int slots = 0;
   for (int i = 0; i < k.n_groups; ++i) slots += n_odd(k.g[i].q.mse_bits) + (k.g[i].q.variant == TQ_PROD ? 1 : 0);
-  (void)slots;
   const size_t keys = (size_t)B * Hkv * HT;
-  // q~, q^ [keys][4][kD], then the split partials
-  p.qprep_floats = 2 * keys * kHT * kD;
+  // q~, q^ [keys][4][kD]; S row-norm maxima [kD / 16]; inverse scales
+  // [keys][4][kMaxKG][2]; operands [keys][slots][512]; then the split
+  // partials
+  p.qprep_floats = 2 * keys * kHT * kD + kD / kRowSlice + keys * kHT * kMaxKG * 2 + keys * slots * 512;
+  p.qprep_floats = (p.qprep_floats + 3) / 4 * 4;
   p.partial_floats = (size_t)B * Hq * p.splits * (kD + 2);
   return p;
 }
@@ -1016,6 +1256,7 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
   const Spec* sp = find_spec(k, v);
   if (!sp) return hipErrorInvalidValue;
   Args a{};
+  bool folded = true;  // every PROD key group carries S R: one query-transform pass
   a.nk = k.n_groups;
   a.nv = v.n_groups;
   int ns = 0;
@@ -1027,20 +1268,27 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
     o.rnorm = g.rnorm;
     o.R = g.q.R;
     o.S = g.q.S;
+    o.SR = g.q.SR;
     o.seq_stride = g.seq_stride;
     o.ch = g.ch_offset;
     o.d = g.q.d;
     o.B = g.q.mse_bits;
     o.prod = g.q.variant == TQ_PROD;
+    if (o.prod && !o.SR) folded = false;
     o.gamma = (float)(sqrt(M_PI / 2.0) / g.q.d);
     float alphas[kMaxVTypes];
     const int nt = odd_walsh(g.q, alphas);
     o.amax = 0.f;
     for (int t = 0; t < nt; ++t) {
-      a.slot[ns++] = Slot{gi, 0, alphas[t]};
+      a.slot_group |= gi << ns;
+      a.slot_alpha[ns++] = alphas[t];
       o.amax = fmaxf(o.amax, fabsf(alphas[t]));
     }
-    if (o.prod) a.slot[ns++] = Slot{gi, 1, 1.f};
+    if (o.prod) {
+      a.slot_group |= gi << ns;
+      a.slot_qjl |= 1 << ns;
+      a.slot_alpha[ns++] = 1.f;
+    }
   }
   a.nslots = ns;
   for (int gi = 0; gi < a.nv; ++gi) {
@@ -1074,11 +1322,18 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
   float* wsf = static_cast<float*>(ws);
   a.qt = wsf;
   a.qh = a.qt + keys * kHT * kD;
+  a.srow = a.qh + keys * kHT * kD;
+  a.ascale = a.srow + kD / kRowSlice;
+  a.aops = reinterpret_cast<uint32_t*>(a.ascale + keys * kHT * kMaxKG * 2);
   a.partial = wsf + plan.qprep_floats;
   a.out = out;
   const dim3 qgrid((unsigned)keys, kD / kRowSlice);
-  hipLaunchKernelGGL(qtransform_kernel<false>, qgrid, dim3(kQtThreads), 0, s, a);
-  hipLaunchKernelGGL(qtransform_kernel<true>, qgrid, dim3(kQtThreads), 0, s, a);
+  if (folded) {
+    hipLaunchKernelGGL(qfused_kernel, qgrid, dim3(kQtThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(qtransform_kernel<false>, qgrid, dim3(kQtThreads), 0, s, a);
+    hipLaunchKernelGGL(qtransform_kernel<true>, qgrid, dim3(kQtThreads), 0, s, a);
+  }
   const dim3 grid(plan.splits, a.HT, B * Hkv);
   hipLaunchKernelGGL(sp->fn, grid, dim3(kThreads), 0, s, a);
   hipLaunchKernelGGL(combine_kernel, dim3(B * Hq, kJSlices), dim3(kCombThreads), 0, s, a);

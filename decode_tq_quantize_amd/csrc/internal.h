@@ -40,6 +40,9 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
                               int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out,
                               float* scores_out, void* ws, const DecodePlan& plan, hipStream_t s);
 
+// S R and its largest row norm (fold.hip).
+hipError_t launch_fold(const tq_quantizer& q, float* SR, hipStream_t s);
+
 // Search.
 size_t search_workspace_bytes(const tq_group& db, int64_t N, int Q, int k);
 hipError_t launch_search(const tq_group& db, int64_t N, const float* queries, int Q, int k, int64_t* out_idx,

@@ -19,7 +19,8 @@ int check_quantizer(const tq_quantizer* q) {
   if (q->mse_bits < 1 || q->mse_bits > TQ_MAX_MSE_BITS) return TQ_ERR_UNSUPPORTED;
   if (q->variant != TQ_MSE && q->variant != TQ_PROD) return TQ_ERR_INVALID_ARG;
   if (!q->R || (q->variant == TQ_PROD && !q->S)) return TQ_ERR_INVALID_ARG;
-  if (!aligned16(q->R) || (q->S && !aligned16(q->S))) return TQ_ERR_MISALIGNED;
+  if (!aligned16(q->R) || (q->S && !aligned16(q->S)) || (q->SR && !aligned16(q->SR))) return TQ_ERR_MISALIGNED;
+  if (q->SR && q->variant != TQ_PROD) return TQ_ERR_INVALID_ARG;
   const int L = 1 << q->mse_bits;
   for (int i = 0; i < L; ++i) {
     if (!std::isfinite(q->centroids[i])) return TQ_ERR_INVALID_ARG;
@@ -95,6 +96,19 @@ extern "C" const char* tq_status_string(int status) {
     case TQ_ERR_WORKSPACE: return "workspace missing or too small";
     default: return "unknown status";
   }
+}
+
+extern "C" size_t tq_fold_bytes(int d) {
+  if (d < 32 || d > TQ_MAX_DIM || (d % 32) != 0) return 0;
+  return ((size_t)d * d + 4) * sizeof(float);
+}
+
+extern "C" int tq_fold_qjl(const tq_quantizer* q, float* SR, void* stream) {
+  int rc = check_quantizer(q);
+  if (rc != TQ_OK) return rc;
+  if (q->variant != TQ_PROD || !SR) return TQ_ERR_INVALID_ARG;
+  if (!aligned16(SR)) return TQ_ERR_MISALIGNED;
+  return hip_status(tqk::launch_fold(*q, SR, static_cast<hipStream_t>(stream)));
 }
 
 extern "C" size_t tq_packed_bytes(int d, int mse_bits, tq_variant variant, tq_layout layout, int64_t n) {

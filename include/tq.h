@@ -73,14 +73,17 @@ typedef enum { TQ_LAYOUT_KEYS = 0, TQ_LAYOUT_VALUES = 1 } tq_layout;
  * (ascending, 2^mse_bits centroids and 2^mse_bits - 1 thresholds; entries past
  * those are ignored); R and S are device pointers to d x d row-major fp32
  * matrices owned by the caller (R orthogonal, S i.i.d. N(0,1); S is NULL for
- * TQ_MSE). The decode and search kernels require the mirror-symmetric
- * codebook tq_quantizer_init produces (c_i = -c_{L-1-i}). */
+ * TQ_MSE). SR is optional (NULL from tq_quantizer_init): a device buffer
+ * filled by tq_fold_qjl, with which decode forms S R q in one product. The
+ * decode and search kernels require the mirror-symmetric codebook
+ * tq_quantizer_init produces (c_i = -c_{L-1-i}). */
 typedef struct {
   int d;             /* vector dimension: multiple of 32, 32..2048 */
   int mse_bits;      /* B: Lloyd-Max bits per coordinate, 1..4 */
   tq_variant variant;
   const float* R;
   const float* S;
+  const float* SR;   /* optional: tq_fold_qjl output for this R and S */
   float centroids[TQ_MAX_LEVELS];
   float thresholds[TQ_MAX_LEVELS - 1];
 } tq_quantizer;
@@ -134,6 +137,21 @@ size_t tq_packed_bytes(int d, int mse_bits, tq_variant variant, tq_layout layout
 
 /* Human-readable text for a tq_status value. */
 const char* tq_status_string(int status);
+
+/* Bytes of the buffer tq_fold_qjl fills for dimension d: (d * d + 4) floats
+ * (0 on a bad d). */
+size_t tq_fold_bytes(int d);
+
+/* Precompute the query side of the QJL term (riverfrot section 4.3: the
+ * query enters the sign estimator as S R q, q~ = R q being the rotated
+ * query): SR[0 .. d*d) = S R (d x d row-major fp32) and SR[d*d] = the largest
+ * Euclidean row norm of S R; SR[d*d+1 .. d*d+3] are zero. R and S are read on
+ * `stream`, SR (tq_fold_bytes(d) bytes, device, caller-owned, 16-byte
+ * aligned) is written on it. Store SR in tq_quantizer.SR: decode then forms
+ * R q and S R q in one pass, bounding both operand ranges by the row norms
+ * instead of by a second pass over the products. Errors: INVALID_ARG (not a
+ * PROD quantiser, null pointers), UNSUPPORTED, MISALIGNED, HIP. */
+int tq_fold_qjl(const tq_quantizer* q, float* SR, void* stream);
 
 /* ------------------------------------------------------------ device calls */
 

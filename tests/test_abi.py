@@ -46,17 +46,19 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "tq.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(tq_quantizer), offsetof(tq_quantizer, R),
-         offsetof(tq_quantizer, centroids), offsetof(tq_quantizer, thresholds), sizeof(tq_group),
-         offsetof(tq_group, packed), offsetof(tq_group, seq_stride), sizeof(tq_kv_desc), offsetof(tq_kv_desc, g));
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(tq_quantizer), offsetof(tq_quantizer, R),
+         offsetof(tq_quantizer, SR), offsetof(tq_quantizer, centroids), offsetof(tq_quantizer, thresholds),
+         sizeof(tq_group), offsetof(tq_group, packed), offsetof(tq_group, seq_stride), sizeof(tq_kv_desc),
+         offsetof(tq_kv_desc, g));
   return 0;
 }
 ''')
     exe = tmp_path / "probe"
     subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(probe), "-o", str(exe)], check=True)
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
-    want = [ctypes.sizeof(tq.tq_quantizer), tq.tq_quantizer.R.offset, tq.tq_quantizer.centroids.offset,
-            tq.tq_quantizer.thresholds.offset, ctypes.sizeof(tq.tq_group), tq.tq_group.packed.offset,
+    want = [ctypes.sizeof(tq.tq_quantizer), tq.tq_quantizer.R.offset, tq.tq_quantizer.SR.offset,
+            tq.tq_quantizer.centroids.offset, tq.tq_quantizer.thresholds.offset, ctypes.sizeof(tq.tq_group),
+            tq.tq_group.packed.offset,
             tq.tq_group.seq_stride.offset, ctypes.sizeof(tq.tq_kv_desc), tq.tq_kv_desc.g.offset]
     assert got == want
 
@@ -203,3 +205,25 @@ def test_search_validation_paths():
     assert call(wsb=ws - 8) == tq.TQ_ERR_WORKSPACE
     assert call(qp=None) == tq.TQ_ERR_INVALID_ARG
     assert tq.tq_search_workspace_bytes(db, 1000, 4, 0) == 0
+
+
+def test_fold_validation_paths():
+    L = tq.lib()
+    assert tq.tq_fold_bytes(128) == (128 * 128 + 4) * 4
+    assert tq.tq_fold_bytes(100) == 0
+    qp = _q(128, 3, tq.TQ_PROD)
+    qm = _q(128, 3, tq.TQ_MSE)
+    assert L.tq_fold_qjl(ctypes.byref(qm), FAKE, None) == tq.TQ_ERR_INVALID_ARG   # no sketch to fold
+    assert L.tq_fold_qjl(ctypes.byref(qp), None, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_fold_qjl(ctypes.byref(qp), FAKE + 4, None) == tq.TQ_ERR_MISALIGNED
+    # a quantiser carrying SR must be PROD and SR aligned
+    bad = _q(128, 3, tq.TQ_MSE)
+    bad.SR = FAKE
+    g = tq.make_group(bad, 0, FAKE, FAKE, None, 64)
+    assert L.tq_quantize_kv(ctypes.byref(bad), tq.TQ_LAYOUT_VALUES, tq.TQ_F32, FAKE, 4, 128, FAKE, FAKE, None,
+                            None) == tq.TQ_ERR_INVALID_ARG
+    mis = _q(128, 3, tq.TQ_PROD)
+    mis.SR = FAKE + 8
+    assert L.tq_quantize_kv(ctypes.byref(mis), tq.TQ_LAYOUT_KEYS, tq.TQ_F32, FAKE, 4, 128, FAKE, FAKE, FAKE,
+                            None) == tq.TQ_ERR_MISALIGNED
+    del g

@@ -30,12 +30,16 @@ def _variant(prod):
 class GpuQuantizer:
     """Device copies of R and S plus the library quantiser that points at them."""
 
-    def __init__(self, d, B, prod, seed, r_stream=synth.STREAM_R, s_stream=synth.STREAM_S):
+    def __init__(self, d, B, prod, seed, r_stream=synth.STREAM_R, s_stream=synth.STREAM_S, fold=False):
         self.R32 = synth.haar_orthogonal(d, seed, r_stream)
         self.S32 = synth.gaussian_matrix(d, d, seed, s_stream) if prod else None
         self.Rt = torch_dev(self.R32)
         self.St = torch_dev(self.S32) if prod else None
         self.q = tq.tq_quantizer_init(d, B, _variant(prod), self.Rt, self.St)
+        self.SRt = None
+        if fold and prod:  # S R precomputed: decode takes the one-pass query transform
+            self.SRt = torch.empty(tq.tq_fold_bytes(d) // 4, dtype=torch.float32, device="cuda")
+            tq.tq_quantizer_fold(self.q, self.SRt)
         self.d, self.B, self.prod = d, B, prod
         self.oq = otq.make_quantizer(d, B, prod, self.R32, self.S32)
 
@@ -202,10 +206,11 @@ DECODE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fold", [False, True])
 @pytest.mark.parametrize("B,Hq,Hkv,T,T_cap,seq_lens,kB,vB,qdt", DECODE_CASES)
-def test_decode_matches_oracle_on_oracle_packed_cache(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt):
-    print(f"decode B={B} Hq={Hq} Hkv={Hkv} T={T} lens={seq_lens}", flush=True)
-    _decode_case(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt, 128)
+def test_decode_matches_oracle_on_oracle_packed_cache(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt, fold):
+    print(f"decode B={B} Hq={Hq} Hkv={Hkv} T={T} lens={seq_lens} fold={fold}", flush=True)
+    _decode_case(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt, 128, fold)
 
 
 @pytest.mark.parametrize("d,Hq,Hkv,kB,vB", [(64, 8, 2, 3, 2), (256, 4, 2, 2, 3), (128, 16, 2, 4, 4), (128, 6, 2, 1, 1)])
@@ -216,9 +221,9 @@ def test_decode_other_head_sizes_and_tiles(d, Hq, Hkv, kB, vB):
     _decode_case(2, Hq, Hkv, 700, 736, [700, 333], kB, vB, "bf16", d)
 
 
-def _decode_case(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt, d):
+def _decode_case(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt, d, fold=False):
     K, V = make_kv(B, Hkv, T, d, seed=T)
-    gk = GpuQuantizer(d, kB, True, seed=1)
+    gk = GpuQuantizer(d, kB, True, seed=1, fold=fold)
     gv = GpuQuantizer(d, vB, False, seed=2, r_stream=synth.STREAM_R_V)
     ck, cv = otq.quantize(K, gk.oq), otq.quantize(V, gv.oq)
     qry = synth.rng(T, 30).standard_normal((B, Hq, d)).astype(np.float32)
@@ -247,12 +252,13 @@ def test_score_matrix_tiny_workload(b_total):
     check_decode(out, sc, [otq.Group(0, gk.oq, ck)], [otq.Group(0, gv.oq, cv)], qry[None], 1, None)
 
 
-def test_decode_two_channel_groups():
+@pytest.mark.parametrize("fold", [False, True])
+def test_decode_two_channel_groups(fold):
     # 2.5 bits per channel: 32 outlier channels (keys 2+1 bits, values 3 bits)
     # and 96 others (keys 1+1, values 2), each group with its own norms.
     B, Hq, Hkv, T, T_cap = 2, 8, 2, 200, 224
     K, V = make_kv(B, Hkv, T, 128, seed=4)
-    ka, kb = GpuQuantizer(32, 2, True, 1), GpuQuantizer(96, 1, True, 2)
+    ka, kb = GpuQuantizer(32, 2, True, 1, fold=fold), GpuQuantizer(96, 1, True, 2, fold=fold)
     va, vb = GpuQuantizer(32, 3, False, 3), GpuQuantizer(96, 2, False, 4)
     cka, ckb = otq.quantize(K[..., :32], ka.oq), otq.quantize(K[..., 32:], kb.oq)
     cva, cvb = otq.quantize(V[..., :32], va.oq), otq.quantize(V[..., 32:], vb.oq)
@@ -264,13 +270,14 @@ def test_decode_two_channel_groups():
                  [otq.Group(0, va.oq, cva), otq.Group(32, vb.oq, cvb)], qry, Hkv, [200, 150])
 
 
-def test_decode_on_gpu_quantized_cache():
+@pytest.mark.parametrize("fold", [False, True])
+def test_decode_on_gpu_quantized_cache(fold):
     # stage isolation: the GPU quantiser writes the cache, the oracle decodes
     # the GPU's own codes, and the GPU decode must agree with that.
     B, Hq, Hkv, T = 1, 8, 2, 512
     d = 128
     K, V = make_kv(B, Hkv, T, d, seed=8)
-    gk = GpuQuantizer(d, 3, True, seed=1)
+    gk = GpuQuantizer(d, 3, True, seed=1, fold=fold)
     gv = GpuQuantizer(d, 3, False, seed=2, r_stream=synth.STREAM_R_V)
     n = B * Hkv * T
     kp, kn, kr = gpu_quantize(gk, torch_dev(K.reshape(n, d), torch.bfloat16), n, d, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16)
@@ -307,6 +314,21 @@ def test_decode_is_deterministic():
     a = run_decode([kc], [vc], qry, Hkv, T, None, "f32")
     b = run_decode([kc], [vc], qry, Hkv, T, None, "f32")
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("d", [32, 96, 128, 1536])
+def test_fold_matches_matrix_product(d):
+    # S R and its largest row norm against a float64 product of the same
+    # fp32 matrices; the norm must bound every row (it is rounded up).
+    print(f"fold d={d}", flush=True)
+    gq = GpuQuantizer(d, 2, True, seed=d, fold=True)
+    sr = gq.SRt.cpu().numpy()
+    want = gq.S32.astype(np.float64) @ gq.R32.astype(np.float64)
+    got = sr[:d * d].reshape(d, d)
+    assert np.max(np.abs(got - want)) <= 2e-5 * np.max(np.abs(want))
+    rn = np.sqrt((got.astype(np.float64) ** 2).sum(axis=1))
+    assert sr[d * d] >= rn.max() and sr[d * d] <= rn.max() * (1 + 1e-5)
+    assert np.all(sr[d * d + 1:d * d + 4] == 0)
 
 
 # --------------------------------------------------------------------------
