@@ -17,6 +17,12 @@ inline int planes_of(const tq_quantizer& q) { return q.mse_bits + (q.variant == 
 hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
                            int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s);
 
+// Matrix-core quantiser for 128-channel vectors (quantize_mfma.hip): rows
+// 16-byte aligned.
+bool quantize_mfma_supported(const tq_quantizer& q, tq_dtype dt, const void* x, int64_t stride);
+hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
+                                int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s);
+
 // Decode: workspace sizing and launch. Shapes are validated by the caller.
 struct DecodePlan {
   int head_chunk;   // query heads per workgroup

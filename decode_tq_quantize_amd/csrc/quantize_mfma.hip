@@ -1,0 +1,380 @@
+// Online TurboQuant compression of 128-channel KV vectors on the gfx950
+// matrix cores (riverfrot "TurboQuant" post, section 4.1: x~ = R x / |x|;
+// section 4.2: Lloyd-Max interval index per coordinate; section 4.3: the
+// residual r~ = x~ - c[idx] projected with S, signs kept, plus |r~|).
+//
+// Both d x d products run on v_mfma_f32_16x16x4_f32 (fp32 operands, fp32
+// accumulation): a persistent workgroup of 4 waves keeps rows 32 w .. 32 w +
+// 31 of R and of S (wave w, one 32-coordinate group each) in registers as
+// MFMA A operands and streams tiles of 32 vectors through them. The
+// contraction index is permuted so that each lane reads 32 consecutive
+// coordinates: in MFMA step kk, lane group q (lanes 16 q .. 16 q + 15)
+// carries coordinate 32 q + kk. The rotated vector comes out with lane l
+// holding coordinates 32 w + 16 m + 4 (l / 16) + r (m = 0, 1; r = 0..3) of
+// vector l % 16; codes, residuals and signs are formed there, the residual
+// goes through LDS to the operand layout of the second product, and the
+// codes are packed with wave ballots into the library's bit-plane layouts.
+#include "device_common.h"
+#include "internal.h"
+
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kThreads = 256;
+constexpr int kTile = 32;  // vectors per iteration (one values tile, two keys tiles)
+
+struct QmArgs {
+  const void* x;
+  int64_t n;
+  int64_t stride;
+  int bf16;
+  const float* R;
+  const float* S;
+  int B;
+  int prod;
+  int layout;
+  int64_t ntiles;
+  float cent[TQ_MAX_LEVELS];
+  float thr[TQ_MAX_LEVELS - 1];
+  uint32_t* packed;
+  uint16_t* norm;
+  uint16_t* rnorm;
+};
+
+__device__ __forceinline__ v4f mfma_f32(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v4f mfma_bf16(bf16x8 a, bf16x8 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// bf16 rounding (nearest even) of a finite float, as raw bits.
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Rows 32 w + 16 m + (lane % 16), columns 32 (lane / 16) .. + 31 of M.
+__device__ __forceinline__ void load_rows(const float* __restrict__ M, int w, int lane, float (&A)[2][32]) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const float4* p = reinterpret_cast<const float4*>(M + (int64_t)(32 * w + 16 * m + (lane & 15)) * kD +
+                                                      32 * (lane >> 4));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 v = p[k];
+      A[m][4 * k] = v.x;
+      A[m][4 * k + 1] = v.y;
+      A[m][4 * k + 2] = v.z;
+      A[m][4 * k + 3] = v.w;
+    }
+  }
+}
+
+// 32 consecutive input coordinates 32 q .. 32 q + 31 of vector row `v`
+// (clamped to a valid row; the caller masks rows past n).
+__device__ __forceinline__ void load_x(const QmArgs& a, int64_t v, int q, float (&x)[32]) {
+  if (a.bf16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + v * a.stride + 32 * q);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 u = p[k];
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * k + 2 * e] = __uint_as_float(wd[e] << 16);
+        x[8 * k + 2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + v * a.stride + 32 * q);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 u = p[k];
+      x[4 * k] = u.x;
+      x[4 * k + 1] = u.y;
+      x[4 * k + 2] = u.z;
+      x[4 * k + 3] = u.w;
+    }
+  }
+}
+
+// Sum over the 4 lanes that hold the same vector (lanes l, l ^ 16, l ^ 32, l ^ 48).
+__device__ __forceinline__ float sum_q(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+template <bool BF16IN, int B, bool PROD>
+__global__ __launch_bounds__(kThreads, PROD ? 1 : 2) void quantize_mfma_kernel(QmArgs a) {
+  __shared__ __attribute__((aligned(16))) float rt[16][kD + 4];  // residual, [vector][coordinate]
+  __shared__ uint8_t codes[kTile][kD];                           // idx | z << 4, [vector][coordinate]
+  __shared__ float rho_part[4][kTile];
+  __shared__ float cent[TQ_MAX_LEVELS], thr[TQ_MAX_LEVELS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, nl = lane & 15;
+  constexpr int L = 1 << B;
+  constexpr int P = B + (PROD ? 1 : 0);
+  // thresholds as uniform values (the compares below are unrolled)
+  float th[L - 1];
+#pragma unroll
+  for (int t = 0; t < L - 1; ++t) th[t] = a.thr[t];
+
+  // R as A operands: fp32 (fp32 input), or bf16 high and low parts (bf16
+  // input, which is exact in bf16: R x = R_hi x + R_lo x, |R - R_hi - R_lo|
+  // <= 2^-18 |R| elementwise)
+  float AR[2][32], AS[2][32];
+  bf16x8 RH[2][4], RL[2][4];
+  load_rows(a.R, w, lane, AR);
+  if constexpr (BF16IN) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float r = AR[m][8 * kk + e];
+          const uint32_t hb = bf16_bits(r);
+          const float hf = __uint_as_float(hb << 16);
+          RH[m][kk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb);
+          RL[m][kk][e] = __builtin_bit_cast(__bf16, (uint16_t)bf16_bits(r - hf));
+        }
+  }
+  if (PROD) load_rows(a.S, w, lane, AS);
+  if (tid < TQ_MAX_LEVELS) {
+    cent[tid] = a.cent[tid];
+    thr[tid] = tid < TQ_MAX_LEVELS - 1 ? a.thr[tid] : 0.f;
+  }
+  __syncthreads();
+
+  for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int64_t v0 = tile * kTile;
+    float nrm_sub[2];
+#pragma unroll 1
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t v = v0 + 16 * nt + nl;
+      const bool valid = v < a.n;
+      const int64_t vr = valid ? v : a.n - 1;
+      float s2 = 0.f;
+      v4f acc[2];
+      if constexpr (BF16IN) {
+        const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + vr * a.stride + 32 * q);
+        uint4 xw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xw[k] = xp[k];
+        v4f ah[2][2], al[2][2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) ah[m][c] = al[m][c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 xb = __builtin_bit_cast(bf16x8, xw[kk]);
+          const uint32_t wd[4] = {xw[kk].x, xw[kk].y, xw[kk].z, xw[kk].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float lo = __uint_as_float(wd[e] << 16), hi = __uint_as_float(wd[e] & 0xffff0000u);
+            s2 = fmaf(lo, lo, s2);
+            s2 = fmaf(hi, hi, s2);
+          }
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            ah[m][kk & 1] = mfma_bf16(RH[m][kk], xb, ah[m][kk & 1]);
+            al[m][kk & 1] = mfma_bf16(RL[m][kk], xb, al[m][kk & 1]);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) acc[m] = (ah[m][0] + ah[m][1]) + (al[m][0] + al[m][1]);
+      } else {
+        float x[32];
+        load_x(a, vr, q, x);
+#pragma unroll
+        for (int k = 0; k < 32; ++k) s2 = fmaf(x[k], x[k], s2);
+        v4f ac[2][4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) ac[m][c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk) {
+          ac[0][kk & 3] = mfma_f32(AR[0][kk], x[kk], ac[0][kk & 3]);
+          ac[1][kk & 3] = mfma_f32(AR[1][kk], x[kk], ac[1][kk & 3]);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) acc[m] = (ac[m][0] + ac[m][1]) + (ac[m][2] + ac[m][3]);
+      }
+      const float nrm = sqrtf(sum_q(s2));
+      // codes and residual of coordinates 32 w + 16 m + 4 q + r of vector nl
+      const bool live = valid && nrm > 0.f;
+      const float inv = live ? 1.f / nrm : 0.f;
+      uint32_t cb[2][4];
+      float res[2][4];
+      float r2 = 0.f;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float u = acc[m][r] * inv;
+          int idx = 0;
+#pragma unroll
+          for (int t = 0; t < L - 1; ++t) idx += u >= th[t] ? 1 : 0;
+          if (!live) idx = L / 2;
+          const float rr = live ? u - cent[idx] : 0.f;
+          cb[m][r] = (uint32_t)idx;
+          res[m][r] = rr;
+          r2 = fmaf(rr, rr, r2);
+        }
+      if (PROD) {
+        r2 = sum_q(r2);
+        if (q == 0) rho_part[w][16 * nt + nl] = r2;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) rt[nl][32 * w + 16 * m + 4 * q + r] = res[m][r];
+        __syncthreads();
+        float y[32];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float4 u = *reinterpret_cast<const float4*>(&rt[nl][32 * q + 4 * k]);
+          y[4 * k] = u.x;
+          y[4 * k + 1] = u.y;
+          y[4 * k + 2] = u.z;
+          y[4 * k + 3] = u.w;
+        }
+        v4f pc[2][4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) pc[m][c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk) {
+          pc[0][kk & 3] = mfma_f32(AS[0][kk], y[kk], pc[0][kk & 3]);
+          pc[1][kk & 3] = mfma_f32(AS[1][kk], y[kk], pc[1][kk & 3]);
+        }
+        v4f pj[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) pj[m] = (pc[m][0] + pc[m][1]) + (pc[m][2] + pc[m][3]);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (pj[m][r] >= 0.f || !live) cb[m][r] |= 16u;
+      }
+      // padding vectors keep all-zero bits
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          codes[16 * nt + nl][32 * w + 16 * m + 4 * q + r] = valid ? (uint8_t)cb[m][r] : (uint8_t)0;
+      nrm_sub[nt] = nrm;
+      if (PROD) __syncthreads();  // rt is rewritten by the next sub-tile
+    }
+    __syncthreads();
+    // norms (one lane per vector)
+    if (w == 0 && q < 2) {
+      const int vt = 16 * q + nl;
+      const int64_t v = v0 + vt;
+      if (v < a.n) {
+        a.norm[v] = tqd::f32_to_half_bits(q == 0 ? nrm_sub[0] : nrm_sub[1]);
+        if (PROD) {
+          const float rho = sqrtf((rho_part[0][vt] + rho_part[1][vt]) + (rho_part[2][vt] + rho_part[3][vt]));
+          a.rnorm[v] = tqd::f32_to_half_bits(rho);
+        }
+      }
+    }
+    // pack: wave w packs coordinate group w; one ballot covers 2 x 32 bits
+    const int hi = lane >> 5, l32 = lane & 31;
+    if (a.layout == TQ_LAYOUT_KEYS) {
+      // words (vector, group w, planes 0..P-1): bit i = coordinate 32 w + i;
+      // lane 0 (32) stores the P words of the even (odd) vector at once
+      const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
+      for (int vp = 0; vp < kTile; vp += 2) {
+        const int vt = vp + hi;
+        const uint32_t c = codes[vt][32 * w + l32];
+        uint32_t wd[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const uint64_t m = __ballot((c >> (p < B ? p : 4)) & 1u);
+          wd[p] = hi ? (uint32_t)(m >> 32) : (uint32_t)m;
+        }
+        const int64_t v = v0 + vt;
+        if (l32 == 0 && v < nround) {
+          const int64_t kt = v / tqk::kKeysTile;
+          const int t = (int)(v % tqk::kKeysTile);
+          uint32_t* dst = a.packed + ((kt * (kD / 32) + w) * tqk::kKeysTile + t) * P;
+#pragma unroll
+          for (int p = 0; p < P; ++p) dst[p] = wd[p];
+        }
+      }
+    } else {
+      // word (coordinate j, plane p): bit i = vector v0 + i
+      for (int jp = 0; jp < 32; jp += 2) {
+        const int j = 32 * w + jp + hi;
+        const uint32_t c = codes[l32][j];
+        uint32_t wd[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const uint64_t m = __ballot((c >> (p < B ? p : 4)) & 1u);
+          wd[p] = hi ? (uint32_t)(m >> 32) : (uint32_t)m;
+        }
+        if (l32 == 0) {
+          uint32_t* dst = a.packed + (tile * kD + j) * P;
+#pragma unroll
+          for (int p = 0; p < P; ++p) dst[p] = wd[p];
+        }
+      }
+    }
+    __syncthreads();  // codes / rho_part are rewritten by the next tile
+  }
+}
+
+}  // namespace
+
+namespace tqk {
+
+bool quantize_mfma_supported(const tq_quantizer& q, tq_dtype dt, const void* x, int64_t stride) {
+  const int64_t esz = dt == TQ_BF16 ? 2 : 4;
+  return q.d == kD && ((stride * esz) % 16) == 0 && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+}
+
+hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
+                                int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s) {
+  QmArgs a{};
+  a.x = x;
+  a.n = n;
+  a.stride = stride;
+  a.bf16 = dt == TQ_BF16;
+  a.R = q.R;
+  a.S = q.S;
+  a.B = q.mse_bits;
+  a.prod = q.variant == TQ_PROD;
+  a.layout = layout;
+  a.ntiles = (n + kTile - 1) / kTile;
+  for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = q.centroids[i];
+  for (int i = 0; i < TQ_MAX_LEVELS - 1; ++i) a.thr[i] = q.thresholds[i];
+  a.packed = static_cast<uint32_t*>(packed);
+  a.norm = norm;
+  a.rnorm = rnorm;
+  const int64_t grid = a.ntiles < 512 ? a.ntiles : 512;
+  using Fn = void (*)(QmArgs);
+  // [bf16 input][mse bits - 1][prod]
+  static const Fn fns[2][4][2] = {
+      {{quantize_mfma_kernel<false, 1, false>, quantize_mfma_kernel<false, 1, true>},
+       {quantize_mfma_kernel<false, 2, false>, quantize_mfma_kernel<false, 2, true>},
+       {quantize_mfma_kernel<false, 3, false>, quantize_mfma_kernel<false, 3, true>},
+       {quantize_mfma_kernel<false, 4, false>, quantize_mfma_kernel<false, 4, true>}},
+      {{quantize_mfma_kernel<true, 1, false>, quantize_mfma_kernel<true, 1, true>},
+       {quantize_mfma_kernel<true, 2, false>, quantize_mfma_kernel<true, 2, true>},
+       {quantize_mfma_kernel<true, 3, false>, quantize_mfma_kernel<true, 3, true>},
+       {quantize_mfma_kernel<true, 4, false>, quantize_mfma_kernel<true, 4, true>}}};
+  hipLaunchKernelGGL(fns[a.bf16 ? 1 : 0][a.B - 1][a.prod ? 1 : 0], dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tqk
