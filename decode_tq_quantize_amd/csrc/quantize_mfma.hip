@@ -111,7 +111,10 @@ __device__ __forceinline__ float sum_q(float v) {
 }
 
 template <bool BF16IN, int B, bool PROD>
-__global__ __launch_bounds__(kThreads, PROD ? 1 : 2) void quantize_mfma_kernel(QmArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
+  // S (PROD) stays in LDS, read as MFMA A operands per use, so that two
+  // workgroups fit a compute unit
+  __shared__ __attribute__((aligned(16))) float Ss[PROD ? kD : 1][kD + 4];
   __shared__ __attribute__((aligned(16))) float rt[16][kD + 4];  // residual, [vector][coordinate]
   __shared__ uint8_t codes[kTile][kD];                           // idx | z << 4, [vector][coordinate]
   __shared__ float rho_part[4][kTile];
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(kThreads, PROD ? 1 : 2) void quantize_mfma_kernel(Q
   // R as A operands: fp32 (fp32 input), or bf16 high and low parts (bf16
   // input, which is exact in bf16: R x = R_hi x + R_lo x, |R - R_hi - R_lo|
   // <= 2^-18 |R| elementwise)
-  float AR[2][32], AS[2][32];
+  float AR[2][32];
   bf16x8 RH[2][4], RL[2][4];
   load_rows(a.R, w, lane, AR);
   if constexpr (BF16IN) {
@@ -146,7 +149,12 @@ __global__ __launch_bounds__(kThreads, PROD ? 1 : 2) void quantize_mfma_kernel(Q
           RL[m][kk][e] = __builtin_bit_cast(__bf16, (uint16_t)bf16_bits(r - hf));
         }
   }
-  if (PROD) load_rows(a.S, w, lane, AS);
+  if constexpr (PROD) {
+    for (int e = tid; e < kD * kD / 4; e += kThreads) {
+      const int row = e / (kD / 4), c4 = e % (kD / 4);
+      *reinterpret_cast<float4*>(&Ss[row][4 * c4]) = reinterpret_cast<const float4*>(a.S)[e];
+    }
+  }
   if (tid < TQ_MAX_LEVELS) {
     cent[tid] = a.cent[tid];
     thr[tid] = tid < TQ_MAX_LEVELS - 1 ? a.thr[tid] : 0.f;
@@ -253,9 +261,17 @@ __global__ __launch_bounds__(kThreads, PROD ? 1 : 2) void quantize_mfma_kernel(Q
 #pragma unroll
           for (int c = 0; c < 4; ++c) pc[m][c] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 32; ++kk) {
-          pc[0][kk & 3] = mfma_f32(AS[0][kk], y[kk], pc[0][kk & 3]);
-          pc[1][kk & 3] = mfma_f32(AS[1][kk], y[kk], pc[1][kk & 3]);
+        for (int k4 = 0; k4 < 8; ++k4) {
+          float4 s4[2];
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            s4[m] = *reinterpret_cast<const float4*>(&Ss[PROD ? 32 * w + 16 * m + nl : 0][32 * q + 4 * k4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kk = 4 * k4 + e;
+            pc[0][e] = mfma_f32(s4[0][e], y[kk], pc[0][e]);
+            pc[1][e] = mfma_f32(s4[1][e], y[kk], pc[1][e]);
+          }
         }
         v4f pj[2];
 #pragma unroll
