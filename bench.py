@@ -358,7 +358,11 @@ def vector_search(steps=2):
     exact = (qs[:sample].double() @ db.double().T)
     top = torch.topk(exact, k, dim=1).indices.cpu().numpy()
     rec = otq.recall_at_k(oi[:sample].cpu().numpy(), top)
+    # scan work: both sums of the estimator, 2 d multiply-adds per (query, vector)
+    flops = 2.0 * Q * N * 2 * d
     res = {"qps": round(Q / sec, 1), "ms_per_batch": round(sec * 1e3, 3), "recall_at_10": round(rec, 4),
+           "achieved_tflops": round(flops / sec / 1e12, 2),
+           "mfma_fp32_roofline_frac": round(flops / sec / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
            "db_quantize_ms": round(tq_build.ms, 3),
            "streamed_db_bytes": N * (4 * 1536 // 8 + 4),
            "workload": "1M x 1536 fp32 256-component Gaussian mixture, unit-normalised; 1024 queries; "

@@ -51,6 +51,11 @@ hipError_t launch_fold(const tq_quantizer& q, float* SR, hipStream_t s);
 
 // Search.
 size_t search_workspace_bytes(const tq_group& db, int64_t N, int Q, int k);
+// Matrix-core scores (search_mfma.hip): y~ = R y, y^ = S y~ into qt, qh
+// ([Q][d] each) and the score matrix [Q][N].
+bool search_mfma_supported(const tq_group& db);
+hipError_t launch_search_mfma_scores(const tq_group& db, int64_t N, const float* queries, int Q, float* qt,
+                                     float* qh, float* scores, hipStream_t s);
 hipError_t launch_search(const tq_group& db, int64_t N, const float* queries, int Q, int k, int64_t* out_idx,
                          float* out_score, void* ws, hipStream_t s);
 

@@ -206,12 +206,18 @@ hipError_t launch_search(const tq_group& db, int64_t N, const float* queries, in
   a.out_idx = out_idx;
   a.out_score = out_score;
   hipError_t e;
-  hipLaunchKernelGGL(sprep_kernel, dim3(Q), dim3(kThreads), 2 * a.d * sizeof(float), s, a);
-  const size_t lds_sc = (size_t)kQ * 2 * a.d * sizeof(float);
-  e = hipFuncSetAttribute((const void*)scores_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_sc);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scores_kernel, dim3((unsigned)((N + kThreads - 1) / kThreads), (Q + kQ - 1) / kQ),
-                     dim3(kThreads), lds_sc, s, a);
+  if (search_mfma_supported(db)) {
+    // matrix-core scores: y~ [Q][d], y^ [Q][d], then the score matrix
+    e = launch_search_mfma_scores(db, N, queries, Q, a.qprep, a.qprep + (size_t)Q * a.d, a.scores, s);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL(sprep_kernel, dim3(Q), dim3(kThreads), 2 * a.d * sizeof(float), s, a);
+    const size_t lds_sc = (size_t)kQ * 2 * a.d * sizeof(float);
+    e = hipFuncSetAttribute((const void*)scores_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_sc);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scores_kernel, dim3((unsigned)((N + kThreads - 1) / kThreads), (Q + kQ - 1) / kQ),
+                       dim3(kThreads), lds_sc, s, a);
+  }
   const int nt = topk_threads(k);
   const size_t lds_tk = (size_t)nt * k * (sizeof(float) + sizeof(int64_t));
   e = hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_tk);
