@@ -22,6 +22,12 @@ OBJDIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["codebook.cpp", "tq_api.cpp", "quantize.hip", "decode.hip", "decode_mfma.hip", "search.hip", "fold.hip", "quantize_mfma.hip", "search_mfma.hip"]
 
+# Per-source additions. The decode kernels form no NaN on any path they use
+# (masked logits are -inf and every difference of two maxima is guarded), so
+# they are built without NaN semantics: maxima of loaded or lane-exchanged
+# values then need no quieting instructions.
+EXTRA = {"decode_mfma.hip": ["-fno-honor-nans"]}
+
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -33,7 +39,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -134,6 +134,15 @@ __device__ __forceinline__ uint32_t fp8_of(float v) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false) & 0xffu;
 }
 __device__ __forceinline__ float f32_of_fp8(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+// The leading four significant bits of x (truncated toward zero): a value
+// that e4m3 holds exactly whenever it lies in e4m3's normal range, and
+// x - head4(x) is exact.
+__device__ __forceinline__ float head4(float x) { return __uint_as_float(__float_as_uint(x) & 0xfff00000u); }
+// e4m3 byte (in bits 0..7) of a value with at most four significant bits;
+// the register's other bytes are left undefined.
+__device__ __forceinline__ uint32_t fp8_exact(float x) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, x, (int)__float_as_uint(x), false);
+}
 
 
 // 32 plane bits -> fp4 operand; register r, nibble i <- bit 4 i + r.
@@ -158,6 +167,14 @@ __device__ __forceinline__ float inv_v(int r) { return r == 0 ? 4.f : (r == 1 ? 
 __device__ __forceinline__ v4f mfma_fp8_fp4(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 0, 0, 0);
 }
+// The same with a per-lane E8M0 scale (2^(sa - 127)) on the A operand: the
+// scale of lane l multiplies the A data that lane l holds (row l % 16, its
+// 32 values of K); B is unscaled (127).
+__device__ __forceinline__ v4f mfma_fp8_fp4_sa(v8i a, v8i b, v4f c, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, 127);
+}
+// Sum of the four digit rows of a result already weighted by the scales.
+__device__ __forceinline__ float sum4(v4f x) { return (x[0] + x[1]) + (x[2] + x[3]); }
 
 // Reductions over the 16 lanes of a DPP row by row rotations (every lane
 // of the row ends with the result); no LDS traffic.
@@ -179,15 +196,23 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += row_ror<1>(v);
   return v;
 }
-// Maximum over the wave: row maxima, then the four rows' values read as
-// uniform values.
-__device__ __forceinline__ float wave_max64(float v) {
-  v = row16_max(v);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+// Largest of unsigned values over the wave: row maxima by row rotations,
+// then the four rows' values read as uniform values. (Raw bits of
+// non-negative IEEE halves order like the values they encode.)
+template <int N>
+__device__ __forceinline__ uint32_t row_ror_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 + N, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_max64_u(uint32_t v) {
+  v = max(v, row_ror_u<8>(v));
+  v = max(v, row_ror_u<4>(v));
+  v = max(v, row_ror_u<2>(v));
+  v = max(v, row_ror_u<1>(v));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
 
 __device__ __forceinline__ int exponent_of(float x) {
@@ -200,7 +225,10 @@ __device__ __forceinline__ int exponent_of(float x) {
 // d_m the fp8 e4m3 rounding of the residual left by the previous digits,
 // scaled by 16 per digit so that every digit stays in the normal fp8 range
 // (relative precision about 2^-16; no absolute floor). The four digits are
-// four rows of the MFMA; wsum4 recombines them.
+// four rows of the MFMA; wsum4 recombines them. The softmax weights take
+// their digits by truncation instead (d_m the leading four significant bits
+// of the residual, cut by a mask): each digit then still carries at least
+// four new bits (relative precision about 2^-15) for fewer instructions.
 constexpr float kDigitStep = 16.f;
 __device__ __forceinline__ float wsum4(v4f x) {
   return (x[0] + x[1] * (1.f / 16.f)) + (x[2] * (1.f / 256.f) + x[3] * (1.f / 4096.f));
@@ -762,7 +790,7 @@ __device__ __forceinline__ void value_step(v4f (&vacc)[2][VT], const v8i& aw, co
 }
 
 template <int KB0, int KP0, int KB1, int KP1, int VB0, int VB1>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
+__global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void decode_kernel(Args a) {
   constexpr int NK = KB1 > 0 ? 2 : 1;
   constexpr int NV = VB1 > 0 ? 2 : 1;
   constexpr int VT = n_odd(VB0) > n_odd(VB1) ? n_odd(VB0) : n_odd(VB1);
@@ -776,12 +804,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 4, tl = lane & 15;
   const int split = blockIdx.x, ht = blockIdx.y, bg = blockIdx.z;
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  // the argument fields that the first loads depend on, fetched in one batch
+  // (left to itself the compiler fetches them in several dependent rounds)
+  asm volatile("" ::"s"(a.Hkv), "s"(a.HT), "s"(a.split_len), "s"(a.T_max), "s"(a.aops), "s"(a.ascale),
+               "s"(a.k[0].packed), "s"(a.k[0].norm), "s"(a.k[0].rnorm), "s"(a.k[0].seq_stride), "s"(a.k[0].d),
+               "s"(a.k[0].ch), "s"(a.v[0].packed), "s"(a.v[0].norm), "s"(a.v[0].seq_stride), "s"(a.v[0].d),
+               "s"(a.v[0].B), "s"(a.v[0].ch), "s"(a.seq_lens), "s"(a.B), "s"(a.G));
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int h0 = g * a.G + ht * kHT;
   const int nh = min(kHT, a.G - ht * kHT);
-  const int len = a.seq_lens ? min(max(a.seq_lens[b], 0), a.T_max) : a.T_max;
   const int ts = split * a.split_len;
-  const int te = min(ts + a.split_len, len);
 
   // this lane's coordinate word of the key layout (score-phase B operand)
   // (group fields are selected from uniform values, never indexed per lane)
@@ -823,7 +855,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
   // ---- query operands of every slot and their inverse scales (built by the
   // query-transform kernels); issued before the first chunk's loads, so
   // they complete first
-  const int key = (b * a.Hkv + g) * a.HT + ht;
+  const int key = bg * a.HT + ht;
   v8i aop[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -831,20 +863,35 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
     const v4i lo = src[0], hi = src[1];
     aop[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
-  float inv_mse[NK], inv_qjl[NK];
-#pragma unroll
-  for (int gi = 0; gi < NK; ++gi) {
-    const float2 sc = *reinterpret_cast<const float2*>(a.ascale + (((int64_t)key * kHT + hl) * kMaxKG + gi) * 2);
-    inv_mse[gi] = sc.x;
-    inv_qjl[gi] = sc.y;
-  }
-  // ---- the first chunk's loads (unconditional: an empty split reads token
-  // 0 of its sequence, unused)
-  const int tlast = max(te, 1) - 1;
+  // ---- the first chunk's loads: clamped to the cache's extent (T_max) rather
+  // than to the sequence's length, so that they need no value read from
+  // memory; tokens at or past the length are masked where they are used
   KChunk<NK, NV> kA, kB;
   VChunk vA, vB;
-  load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kA, ka, na, min(ts, tlast), tlast, w, lane);
-  load_v<NV, VB0, VB1>(vA, va, min(ts, tlast), lane);
+  load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kA, ka, na, ts, a.T_max - 1, w, lane);
+  load_v<NV, VB0, VB1>(vA, va, ts, lane);
+  // E8M0 scales of this lane's query-operand rows (row lane % 16 = 4 head +
+  // digit): the digit's weight 16^-digit times the head's inverse operand
+  // scale, a power of two (the query transforms choose it so), per (group,
+  // class); the score MFMAs then return the estimate's terms directly.
+  int esc_mse[NK], esc_qjl[NK];
+#pragma unroll
+  for (int gi = 0; gi < NK; ++gi) {
+    const int hr = (lane & 15) >> 2, dg = lane & 3;
+    const float2 sc = *reinterpret_cast<const float2*>(a.ascale + (((int64_t)key * kHT + hr) * kMaxKG + gi) * 2);
+    esc_mse[gi] = max((int)(__float_as_uint(sc.x) >> 23) - 4 * dg, 0);
+    esc_qjl[gi] = max((int)(__float_as_uint(sc.y) >> 23) - 4 * dg, 0);
+  }
+  // the sequence length, read through a buffer resource that is empty when
+  // no lengths are given (the read then returns 0 without touching memory),
+  // so that no branch holds the loads above behind it
+  const uint32_t lraw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(a.seq_lens, a.seq_lens ? (uint32_t)(4 * a.B) : 0u), 4u * (uint32_t)b, 0u, 0);
+  // nothing below is moved above the loads
+  __builtin_amdgcn_sched_barrier(0);
+  const int len = max(min(max(__builtin_amdgcn_readfirstlane((int)lraw), 0), a.T_max), a.seq_lens ? 0 : a.T_max);
+  const int te = min(ts + a.split_len, len);
+  const int tlast = max(te, 1) - 1;
   // constant parts of the fp4 encoding, per (group, class); scales of this lane's head
   float cm[NK], cq[NK], gam[NK];
   {
@@ -856,9 +903,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const float c4 = 0.25f * wsum4(mfma_fp8_fp4(aop[s], cop, v4f{0.f, 0.f, 0.f, 0.f}));
       const int gi = s < NS0 ? 0 : 1;
       const bool q = (gi == 0) ? (KP0 && s == NS0 - 1) : (KP1 && s == NS - 1);
+      const float c4 = 0.25f * sum4(mfma_fp8_fp4_sa(aop[s], cop, v4f{0.f, 0.f, 0.f, 0.f}, q ? esc_qjl[gi] : esc_mse[gi]));
       if (q)
         cq[gi] += c4;
       else
@@ -889,7 +936,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
     load_v<NV, VB0, VB1>(vn, va, cn, lane);
 
     // ---------------- scores for this wave's 64 tokens
-    float lg[4];
+    float lg[4], raw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t(&wd)[5] = kc.w[i];
@@ -903,9 +950,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
 #pragma unroll
         for (int p = 0; p < 5; ++p)
           if ((m >> p) & 1) word ^= wd[p];
-        dm[0] = mfma_fp8_fp4(aop[t], expand_bits(word), dm[0]);
+        dm[0] = mfma_fp8_fp4_sa(aop[t], expand_bits(word), dm[0], esc_mse[0]);
       }
-      if constexpr (KP0) dq[0] = mfma_fp8_fp4(aop[NS0 - 1], expand_bits(wd[KB0]), dq[0]);
+      if constexpr (KP0) dq[0] = mfma_fp8_fp4_sa(aop[NS0 - 1], expand_bits(wd[KB0]), dq[0], esc_qjl[0]);
       if constexpr (KB1 > 0) {
 #pragma unroll
         for (int t = 0; t < n_odd(KB1); ++t) {
@@ -914,24 +961,31 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
 #pragma unroll
           for (int p = 0; p < 5; ++p)
             if ((m >> p) & 1) word ^= wd[p];
-          dm[NK - 1] = mfma_fp8_fp4(aop[NS0 + t], expand_bits(word), dm[NK - 1]);
+          dm[NK - 1] = mfma_fp8_fp4_sa(aop[NS0 + t], expand_bits(word), dm[NK - 1], esc_mse[NK - 1]);
         }
-        if constexpr (KP1) dq[NK - 1] = mfma_fp8_fp4(aop[NS - 1], expand_bits(wd[KB1]), dq[NK - 1]);
+        if constexpr (KP1) dq[NK - 1] = mfma_fp8_fp4_sa(aop[NS - 1], expand_bits(wd[KB1]), dq[NK - 1], esc_qjl[NK - 1]);
       }
       float sc = 0.f;
 #pragma unroll
       for (int gi = 0; gi < NK; ++gi) {
-        float part = (wsum4(dm[gi]) - cm[gi]) * inv_mse[gi];
+        float part = sum4(dm[gi]) - cm[gi];
         if ((gi == 0 && KP0) || (gi == 1 && KP1)) {
-          const float qjl = (wsum4(dq[gi]) - cq[gi]) * inv_qjl[gi];
+          const float qjl = sum4(dq[gi]) - cq[gi];
           part = fmaf(gam[gi] * hbits(kc.r[gi][i]), qjl, part);
         }
         sc = fmaf(hbits(kc.n[gi][i]), part, sc);
       }
       const int tok = c0 + 64 * w + 16 * i + tl;
       const bool valid = tok < te && hl < nh;
-      if (valid && a.scores_out) a.scores_out[((int64_t)b * a.Hq + h0 + hl) * a.T_max + tok] = sc;
+      raw[i] = sc;
       lg[i] = valid ? sc * a.scale_log2 : -INFINITY;
+    }
+    if (a.scores_out) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = c0 + 64 * w + 16 * i + tl;
+        if (tok < te && hl < nh) a.scores_out[((int64_t)b * a.Hq + h0 + hl) * a.T_max + tok] = raw[i];
+      }
     }
     // ---------------- chunk statistics shared by the four waves
     float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
@@ -939,22 +993,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
     if (tl == 0) red_m[w][hl] = mx;
 #pragma unroll
     for (int gv = 0; gv < NV; ++gv) {
-      const float vm = wave_max64(fmaxf(fmaxf(hbits(kc.nv[gv][0]), hbits(kc.nv[gv][1])),
-                                        fmaxf(hbits(kc.nv[gv][2]), hbits(kc.nv[gv][3]))));
-      if (lane == 0) red_e[w][gv] = exponent_of(vm);
+      const uint32_t vm = wave_max64_u(max(max(kc.nv[gv][0], kc.nv[gv][1]), max(kc.nv[gv][2], kc.nv[gv][3])));
+      if (lane == 0) red_e[w][gv] = exponent_of(hbits(vm));
     }
     __syncthreads();
     const float cmax = fmaxf(fmaxf(red_m[0][hl], red_m[1][hl]), fmaxf(red_m[2][hl], red_m[3][hl]));
     const float m_new = fmaxf(m_run, cmax);
     const bool live = m_new != -INFINITY;
-    const float corr = (live && m_run != -INFINITY) ? exp2f(m_run - m_new) : (live ? 0.f : 1.f);
+    // (v_exp_f32 directly: arguments here are at most 0, and results below
+    // the normal range are negligible beside the chunk's largest weight 1)
+    const float corr = (live && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : (live ? 0.f : 1.f);
     int e_new[NV];
 #pragma unroll
     for (int gv = 0; gv < NV; ++gv)
       e_new[gv] = max(max(max(red_e[0][gv], red_e[1][gv]), max(red_e[2][gv], red_e[3][gv])), e_run[gv]);
     const int eshift = (NV > 1 && vgi) ? e_run[NV - 1] - e_new[NV - 1] : e_run[0] - e_new[0];
     const float vcorr = corr * ldexpf(1.f, eshift);
-    if (vcorr != 1.f) {
+    // (the first chunk of a split has nothing to rescale)
+    if (c0 != ts && vcorr != 1.f) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -966,7 +1022,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = live ? exp2f(lg[i] - m_new) : 0.f;
+      p[i] = live ? __builtin_amdgcn_exp2f(lg[i] - m_new) : 0.f;
       l_run += p[i];
     }
     // weights -> fp8 digits in LDS (pre-multiplied by 1 / v_r of their fp4 register)
@@ -982,9 +1038,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
         uint8_t* dst = &wbuf[buf][gv][ks][4 * hl][kappa];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const uint32_t d = fp8_of(r);
-          r = (r - f32_of_fp8(d)) * kDigitStep;
-          dst[128 * m] = (uint8_t)d;
+          const float hi = head4(r);
+          dst[128 * m] = (uint8_t)fp8_exact(hi);
+          r = (r - hi) * kDigitStep;
         }
       }
       e_run[gv] = e_new[gv];
@@ -1007,7 +1063,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
         value_step<(VB1 > 0 ? VB1 : 1), VT>(vacc, aw, vc.w[ks]);
     }
   };
-  for (int c0 = ts; c0 < te;) {
+  // The first chunk always runs (an empty split runs it fully masked: no
+  // weight, no change to the running state), so that its loads and the
+  // query-operand loads above are issued together, ahead of any branch.
+  int c0 = ts;
+  do {
     chunk(c0, kA, vA, kB, vB);
     c0 += kChunk;
     buf ^= 1;
@@ -1015,7 +1075,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(Args a) {
     chunk(c0, kB, vB, kA, vA);
     c0 += kChunk;
     buf ^= 1;
-  }
+  } while (c0 < te);
 
   // ---------------- partial results of this split
   float lsum = row16_sum(l_run);
