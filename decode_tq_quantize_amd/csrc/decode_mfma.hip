@@ -234,6 +234,11 @@ __device__ __forceinline__ float wsum4(v4f x) {
   return (x[0] + x[1] * (1.f / 16.f)) + (x[2] * (1.f / 256.f) + x[3] * (1.f / 4096.f));
 }
 
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 // Odd subsets of B code planes, in ascending bitmask order (the host orders
 // the Walsh coefficients the same way).
 __host__ __device__ constexpr int n_odd(int B) { return B > 0 ? 1 << (B - 1) : 0; }
@@ -646,11 +651,17 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* out) {
 template <int NK, int NV>
 struct KChunk {
   uint32_t w[4][5];
-  uint32_t n[NK][4], r[NK][4];  // IEEE half bits of token 16 i + lane % 16, converted where used
-  uint32_t nv[NV][4];
+  // IEEE half bits, two to a register, converted where used: key norm (low
+  // half) and residual norm (high half) of token 16 i + lane % 16; value
+  // norms of tokens 32 j + lane % 16 (low) and 32 j + 16 + lane % 16 (high)
+  uint32_t nr[NK][4];
+  uint32_t nv[NV][2];
 };
 
 __device__ __forceinline__ float hbits(uint32_t h) { return tqd::half_bits_to_f32((uint16_t)h); }
+__device__ __forceinline__ float hbits_hi(uint32_t h) { return tqd::half_bits_to_f32((uint16_t)(h >> 16)); }
+// Half i (0: low, 1: high) of a register of two halves.
+__device__ __forceinline__ float hbits_at(uint32_t h, int i) { return i ? hbits_hi(h) : hbits(h); }
 
 // Load at a 32-bit unsigned byte offset from a base pointer.
 template <class T>
@@ -691,12 +702,15 @@ __device__ __forceinline__ uint32_t buf_half(rsrc_t r, uint32_t voff, uint32_t s
 // Addressing of one wave's loads. One key group: buffer resources over the
 // sequence's key planes and norms. Two key groups (lanes of different
 // groups read different arrays): plain per-lane pointers.
+// Key planes: one resource per key group over the sequence's planes. A lane
+// reads its own group's planes at its offset in a tile; its offset into the
+// other group's resource lies outside that resource, so the same load reads
+// 0 there without touching memory, and the two results are merged by OR.
+constexpr uint32_t kOutside = 0x80000000u;
 struct KAddr {
-  rsrc_t res;           // key planes of the sequence (one key group)
-  const uint32_t* seq;  // per-lane base for two key groups
-  uint32_t step;        // bytes per 16-token tile
-  uint32_t lane_off;    // this lane's byte offset within a tile
-  int kP;               // planes of this lane's group
+  rsrc_t res[kMaxKG];     // key planes of the sequence, per group
+  uint32_t step[kMaxKG];  // bytes per 16-token tile, per group
+  uint32_t voff[kMaxKG];  // this lane's byte offset within a tile, per group
 };
 struct NAddr {
   rsrc_t n[kMaxKG], r[kMaxKG], nv[kMaxVG];  // norms of the sequence
@@ -718,14 +732,15 @@ __device__ __forceinline__ void load_k(KChunk<NK, NV>& kc, const KAddr& ka, cons
   for (int i = 0; i < 4; ++i) {
     const uint32_t tile = (uint32_t)min((c0 >> 4) + 4 * w + i, last_tile);
     if constexpr (NK == 1) {
-      buf_words<P0>(ka.res, ka.lane_off, tile * ka.step, kc.w[i]);
+      buf_words<P0>(ka.res[0], ka.voff[0], tile * ka.step[0], kc.w[i]);
     } else {
       // lanes of the two groups hold P0 or P1 words; the extra words of the
-      // smaller group are never weighted (its query digits are zero there)
-      constexpr int PM = P0 > P1 ? P0 : P1;
-      const uint32_t* p = at_bytes(ka.seq, tile * ka.step + ka.lane_off);
+      // smaller group are 0 and never weighted (its query digits are zero)
+      uint32_t w0[5] = {0u, 0u, 0u, 0u, 0u}, w1[5] = {0u, 0u, 0u, 0u, 0u};
+      buf_words<P0>(ka.res[0], ka.voff[0], tile * ka.step[0], w0);
+      buf_words<P1>(ka.res[1], ka.voff[1], tile * ka.step[1], w1);
 #pragma unroll
-      for (int pp = 0; pp < 5; ++pp) kc.w[i][pp] = pp < PM ? p[min(pp, ka.kP - 1)] : 0u;
+      for (int pp = 0; pp < 5; ++pp) kc.w[i][pp] = w0[pp] | w1[pp];
     }
   }
   const uint32_t tl2 = 2u * (lane & 15);
@@ -734,11 +749,15 @@ __device__ __forceinline__ void load_k(KChunk<NK, NV>& kc, const KAddr& ka, cons
     const uint32_t tok0 = 16u * (uint32_t)min((c0 >> 4) + 4 * w + i, last_tile);
 #pragma unroll
     for (int gi = 0; gi < NK; ++gi) {
-      kc.n[gi][i] = buf_half(na.n[gi], tl2, 2u * tok0);
-      kc.r[gi][i] = ((gi == 0 && KP0) || (gi == 1 && KP1)) ? buf_half(na.r[gi], tl2, 2u * tok0) : 0u;
+      const uint32_t nn = buf_half(na.n[gi], tl2, 2u * tok0);
+      const uint32_t rn = ((gi == 0 && KP0) || (gi == 1 && KP1)) ? buf_half(na.r[gi], tl2, 2u * tok0) : 0u;
+      kc.nr[gi][i] = nn | (rn << 16);
     }
 #pragma unroll
-    for (int gv = 0; gv < NV; ++gv) kc.nv[gv][i] = buf_half(na.nv[gv], tl2, 2u * tok0);
+    for (int gv = 0; gv < NV; ++gv) {
+      const uint32_t h = buf_half(na.nv[gv], tl2, 2u * tok0);
+      kc.nv[gv][i >> 1] = (i & 1) ? (kc.nv[gv][i >> 1] | (h << 16)) : h;
+    }
   }
 }
 
@@ -796,6 +815,9 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   constexpr int VT = n_odd(VB0) > n_odd(VB1) ? n_odd(VB0) : n_odd(VB1);
   constexpr int NS0 = n_odd(KB0) + KP0;
   constexpr int NS = NS0 + (KB1 > 0 ? n_odd(KB1) + KP1 : 0);
+  // two key groups hold more per-lane state: their keys are single-buffered
+  // (refilled once a chunk's weights are formed) to stay within 2 waves/SIMD
+  constexpr bool kOneK = NK == 2;
   __shared__ __attribute__((aligned(16))) uint8_t wbuf[2][NV][2][16][128];  // [buf][vgroup][step][row][kappa]
   __shared__ float red_m[4][kHT];
   __shared__ int red_e[4][NV];
@@ -819,16 +841,18 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   // (group fields are selected from uniform values, never indexed per lane)
   const int W = lane >> 4;
   const bool kg1 = NK == 2 && 32 * W >= a.k[NK - 1].ch;
-  const int kP = kg1 ? (KB1 + KP1) : (KB0 + KP0);
-  const int kd = kg1 ? a.k[NK - 1].d : a.k[0].d, kch = kg1 ? a.k[NK - 1].ch : a.k[0].ch;
-  const int64_t kss = kg1 ? a.k[NK - 1].seq_stride : a.k[0].seq_stride;
-  const uint32_t* kpk = kg1 ? a.k[NK - 1].packed : a.k[0].packed;
   KAddr ka;
-  ka.step = (uint32_t)((kd >> 5) * 16 * kP * 4);
-  ka.seq = kpk + (((int64_t)bg * kss) >> 4) * ((kd >> 5) * 16 * kP);
-  ka.res = make_rsrc(ka.seq, (uint32_t)(kss >> 4) * ka.step);
-  ka.lane_off = (uint32_t)(((W - (kch >> 5)) * 16 + tl) * kP * 4);
-  ka.kP = kP;
+#pragma unroll
+  for (int gi = 0; gi < NK; ++gi) {
+    const int P = gi ? (KB1 + KP1) : (KB0 + KP0);
+    const int kd = a.k[gi].d, kch = a.k[gi].ch;
+    const int64_t kss = a.k[gi].seq_stride;
+    ka.step[gi] = (uint32_t)((kd >> 5) * 16 * P * 4);
+    const uint32_t* seq = a.k[gi].packed + (((int64_t)bg * kss) >> 4) * ((kd >> 5) * 16 * P);
+    ka.res[gi] = make_rsrc(seq, (uint32_t)(kss >> 4) * ka.step[gi]);
+    const bool own = NK == 1 || (gi == 1) == kg1;
+    ka.voff[gi] = own ? (uint32_t)(((W - (kch >> 5)) * 16 + tl) * P * 4) : kOutside;
+  }
   NAddr na;
 #pragma unroll
   for (int gi = 0; gi < NK; ++gi) {
@@ -867,9 +891,9 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   // than to the sequence's length, so that they need no value read from
   // memory; tokens at or past the length are masked where they are used
   KChunk<NK, NV> kA, kB;
-  VChunk vA, vB;
+  VChunk vv;
   load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kA, ka, na, ts, a.T_max - 1, w, lane);
-  load_v<NV, VB0, VB1>(vA, va, ts, lane);
+  load_v<NV, VB0, VB1>(vv, va, ts, lane);
   // E8M0 scales of this lane's query-operand rows (row lane % 16 = 4 head +
   // digit): the digit's weight 16^-digit times the head's inverse operand
   // scale, a power of two (the query transforms choose it so), per (group,
@@ -930,10 +954,11 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   // into kn, vn (the last chunk re-reads its own, cached, addresses so that
   // the loads stay unconditional). Called with the two buffers swapped on
   // alternate chunks, so nothing is copied.
-  auto chunk = [&](const int c0, const KChunk<NK, NV>& kc, const VChunk& vc, KChunk<NK, NV>& kn, VChunk& vn) {
+  auto chunk = [&](auto vbt, const int c0, KChunk<NK, NV>& kc, KChunk<NK, NV>& kn, VChunk& vc)
+                   __attribute__((always_inline)) {
+    constexpr int VB = decltype(vbt)::value;  // value bits of this wave's coordinates
     const int cn = c0 + kChunk < te ? c0 + kChunk : c0;
-    load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kn, ka, na, cn, tlast, w, lane);
-    load_v<NV, VB0, VB1>(vn, va, cn, lane);
+    if constexpr (!kOneK) load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kn, ka, na, cn, tlast, w, lane);
 
     // ---------------- scores for this wave's 64 tokens
     float lg[4], raw[4];
@@ -971,9 +996,9 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
         float part = sum4(dm[gi]) - cm[gi];
         if ((gi == 0 && KP0) || (gi == 1 && KP1)) {
           const float qjl = sum4(dq[gi]) - cq[gi];
-          part = fmaf(gam[gi] * hbits(kc.r[gi][i]), qjl, part);
+          part = fmaf(gam[gi] * hbits_hi(kc.nr[gi][i]), qjl, part);
         }
-        sc = fmaf(hbits(kc.n[gi][i]), part, sc);
+        sc = fmaf(hbits(kc.nr[gi][i]), part, sc);
       }
       const int tok = c0 + 64 * w + 16 * i + tl;
       const bool valid = tok < te && hl < nh;
@@ -993,7 +1018,8 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
     if (tl == 0) red_m[w][hl] = mx;
 #pragma unroll
     for (int gv = 0; gv < NV; ++gv) {
-      const uint32_t vm = wave_max64_u(max(max(kc.nv[gv][0], kc.nv[gv][1]), max(kc.nv[gv][2], kc.nv[gv][3])));
+      const uint32_t m2 = max(kc.nv[gv][0] & 0xffffu, kc.nv[gv][1] & 0xffffu);
+      const uint32_t vm = wave_max64_u(max(m2, max(kc.nv[gv][0] >> 16, kc.nv[gv][1] >> 16)));
       if (lane == 0) red_e[w][gv] = exponent_of(hbits(vm));
     }
     __syncthreads();
@@ -1034,7 +1060,7 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
         const int tau = 64 * w + 16 * i + tl;
         const int ks = tau >> 7, tp = tau & 127;
         const int kappa = 32 * (tp >> 5) + 8 * (tp & 3) + ((tp & 31) >> 2);
-        float r = p[i] * hbits(kc.nv[gv][i]) * sv;
+        float r = p[i] * hbits_at(kc.nv[gv][i >> 1], i & 1) * sv;
         uint8_t* dst = &wbuf[buf][gv][ks][4 * hl][kappa];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -1045,37 +1071,50 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
       }
       e_run[gv] = e_new[gv];
     }
+    // (one key buffer: it is used up; refill it with the next chunk's keys)
+    if constexpr (kOneK) load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kc, ka, na, cn, tlast, w, lane);
     __syncthreads();
     // ---------------- values: this wave's 32 coordinates over the 256 tokens
+    // (a step past the split's end has all weights 0 and adds nothing)
     const v8i cop = const_operand();
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      if (c0 + 128 * ks >= te) break;
       const uint8_t* wrow = &wbuf[buf][vgi][ks][lane & 15][0];
       const int gp = lane >> 4;
       const v4i lo = *reinterpret_cast<const v4i*>(wrow + 16 * gp);
       const v4i hi = *reinterpret_cast<const v4i*>(wrow + 64 + 16 * gp);
       const v8i aw = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       vcon = mfma_fp8_fp4(aw, cop, vcon);
-      if (NV == 1 || vgi == 0)
-        value_step<VB0, VT>(vacc, aw, vc.w[ks]);
-      else
-        value_step<(VB1 > 0 ? VB1 : 1), VT>(vacc, aw, vc.w[ks]);
+      value_step<VB, VT>(vacc, aw, vc.w[ks]);
     }
+    // the value words are used: refill them with the next chunk's (they
+    // arrive while its scores and weights are formed)
+    load_v<NV, VB0, VB1>(vc, va, cn, lane);
   };
   // The first chunk always runs (an empty split runs it fully masked: no
   // weight, no change to the running state), so that its loads and the
   // query-operand loads above are issued together, ahead of any branch.
-  int c0 = ts;
-  do {
-    chunk(c0, kA, vA, kB, vB);
-    c0 += kChunk;
-    buf ^= 1;
-    if (c0 >= te) break;
-    chunk(c0, kB, vB, kA, vA);
-    c0 += kChunk;
-    buf ^= 1;
-  } while (c0 < te);
+  // The loop is instantiated once per value width and chosen per wave, so
+  // that no branch inside it touches the value accumulators.
+  auto run = [&](auto vbt) __attribute__((always_inline)) {
+    int c0 = ts;
+    do {
+      chunk(vbt, c0, kA, kB, vv);
+      c0 += kChunk;
+      buf ^= 1;
+      if (c0 >= te) break;
+      if constexpr (kOneK)
+        chunk(vbt, c0, kA, kA, vv);
+      else
+        chunk(vbt, c0, kB, kA, vv);
+      c0 += kChunk;
+      buf ^= 1;
+    } while (c0 < te);
+  };
+  if (NV == 1 || vgi == 0)
+    run(IntC<VB0>{});
+  else
+    run(IntC<(VB1 > 0 ? VB1 : 1)>{});
 
   // ---------------- partial results of this split
   float lsum = row16_sum(l_run);
