@@ -347,12 +347,10 @@ __global__ __launch_bounds__(kQtThreads) void qfused_kernel(Args a) {
     t = use ? t : 0.f;
     u = use ? u : 0.f;
     n2 = use ? n2 : 0.f;
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
-      t += __shfl_xor(t, o, 16);
-      u += __shfl_xor(u, o, 16);
-      n2 += __shfl_xor(n2, o, 16);
-    }
+    // the 16 lanes of a row hold the 16 column blocks: row rotations sum them
+    t = row16_sum(t);
+    u = row16_sum(u);
+    n2 = row16_sum(n2);
     if (cb == h) {
       ot = t;
       oh = u;
@@ -360,8 +358,6 @@ __global__ __launch_bounds__(kQtThreads) void qfused_kernel(Args a) {
     }
   }
   if (cb < kHT) {
-    a.qt[((int64_t)key * kHT + cb) * kD + i] = ot;
-    a.qh[((int64_t)key * kHT + cb) * kD + i] = oh;
     qts[cb][tid >> 4] = ot;
     qhs[cb][tid >> 4] = oh;
     if ((tid >> 4) == 0) {  // |q| of head cb over the group's channels -> the two scales
