@@ -116,7 +116,9 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
   // workgroups fit a compute unit
   __shared__ __attribute__((aligned(16))) float Ss[PROD ? kD : 1][kD + 4];
   __shared__ __attribute__((aligned(16))) float rt[16][kD + 4];  // residual, [vector][coordinate]
-  __shared__ uint8_t codes[kTile][kD];                           // idx | z << 4, [vector][coordinate]
+  // rows padded by one dword: the value layout reads a column (one vector
+  // per lane), which would otherwise fall into one LDS bank
+  __shared__ uint8_t codes[kTile][kD + 4];  // idx | z << 4, [vector][coordinate]
   __shared__ float rho_part[4][kTile];
   __shared__ float cent[TQ_MAX_LEVELS], thr[TQ_MAX_LEVELS];
   const int tid = threadIdx.x, lane = tid & 63;
