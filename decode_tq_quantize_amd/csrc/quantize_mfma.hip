@@ -43,6 +43,22 @@ struct QmArgs {
   uint16_t* rnorm;
 };
 
+// The two 32-bit halves of a wave ballot `m` go to lane l0 of `a` and lane
+// l1 of `b` (v_writelane; l0 and l1 fold to constants in the unrolled loops
+// that call this). A VALU write of an SGPR is not visible to v_writelane's
+// data operand one instruction later (measured: the value read is stale),
+// so the writes wait first.
+__device__ __forceinline__ void ballot_to_lanes(uint32_t& a, uint32_t& b, uint64_t m, int l0, int l1) {
+  asm("s_nop 4\n\tv_writelane_b32 %0, %2, %4\n\tv_writelane_b32 %1, %3, %5"
+      : "+v"(a), "+v"(b)
+      : "s"((uint32_t)m), "s"((uint32_t)(m >> 32)), "i"(l0), "i"(l1));
+}
+__device__ __forceinline__ void ballot_to_lanes(uint32_t& a, uint64_t m, int l0, int l1) {
+  asm("s_nop 4\n\tv_writelane_b32 %0, %1, %3\n\tv_writelane_b32 %0, %2, %4"
+      : "+v"(a)
+      : "s"((uint32_t)m), "s"((uint32_t)(m >> 32)), "i"(l0), "i"(l1));
+}
+
 __device__ __forceinline__ v4f mfma_f32(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -165,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
 
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int64_t v0 = tile * kTile;
-    float nrm_sub[2];
+    float nrm0 = 0.f, nrm1 = 0.f;  // norms of sub-tiles 0 and 1 (registers, not an indexed array)
 #pragma unroll 1
     for (int nt = 0; nt < 2; ++nt) {
       const int64_t v = v0 + 16 * nt + nl;
@@ -290,7 +306,10 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           codes[16 * nt + nl][32 * w + 16 * m + 4 * q + r] = valid ? (uint8_t)cb[m][r] : (uint8_t)0;
-      nrm_sub[nt] = nrm;
+      if (nt == 0)
+        nrm0 = nrm;
+      else
+        nrm1 = nrm;
       if (PROD) __syncthreads();  // rt is rewritten by the next sub-tile
     }
     __syncthreads();
@@ -299,54 +318,75 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
       const int vt = 16 * q + nl;
       const int64_t v = v0 + vt;
       if (v < a.n) {
-        a.norm[v] = tqd::f32_to_half_bits(q == 0 ? nrm_sub[0] : nrm_sub[1]);
+        a.norm[v] = tqd::f32_to_half_bits(q == 0 ? nrm0 : nrm1);
         if (PROD) {
           const float rho = sqrtf((rho_part[0][vt] + rho_part[1][vt]) + (rho_part[2][vt] + rho_part[3][vt]));
           a.rnorm[v] = tqd::f32_to_half_bits(rho);
         }
       }
     }
-    // pack: wave w packs coordinate group w; one ballot covers 2 x 32 bits
+    // pack: wave w packs coordinate group w. One ballot covers 2 x 32 bits
+    // (lanes 0..31 and 32..63 read two different rows); its two halves are
+    // uniform values, placed with v_writelane into the lanes of a word
+    // buffer whose lane l holds the l-th word of the wave's contiguous output
+    // run, which is then stored coalesced.
     const int hi = lane >> 5, l32 = lane & 31;
     if (a.layout == TQ_LAYOUT_KEYS) {
-      // words (vector, group w, planes 0..P-1): bit i = coordinate 32 w + i;
-      // lane 0 (32) stores the P words of the even (odd) vector at once
-      const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
+      // words (vector t of key tile kb, group w, plane p): bit i = coordinate
+      // 32 w + i; the wave's words of key tile kb are 16 P contiguous words
+      constexpr int NW = (16 * P + 63) / 64;
+      uint32_t ow[2][NW];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < NW; ++r) ow[kb][r] = 0u;
+#pragma unroll
       for (int vp = 0; vp < kTile; vp += 2) {
-        const int vt = vp + hi;
-        const uint32_t c = codes[vt][32 * w + l32];
-        uint32_t wd[P];
+        const uint32_t c = codes[vp + hi][32 * w + l32];
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-          const uint64_t m = __ballot((c >> (p < B ? p : 4)) & 1u);
-          wd[p] = hi ? (uint32_t)(m >> 32) : (uint32_t)m;
+        for (int pp = 0; pp < P; ++pp) {
+          const uint64_t m = __ballot((c >> (pp < B ? pp : 4)) & 1u);
+          const int kb = vp >> 4, i0 = (vp & 15) * P + pp, i1 = i0 + P;
+          if ((i0 >> 6) == (i1 >> 6))
+            ballot_to_lanes(ow[kb][i0 >> 6], m, i0 & 63, i1 & 63);
+          else
+            ballot_to_lanes(ow[kb][i0 >> 6], ow[kb][i1 >> 6], m, i0 & 63, i1 & 63);
         }
-        const int64_t v = v0 + vt;
-        if (l32 == 0 && v < nround) {
-          const int64_t kt = v / tqk::kKeysTile;
-          const int t = (int)(v % tqk::kKeysTile);
-          uint32_t* dst = a.packed + ((kt * (kD / 32) + w) * tqk::kKeysTile + t) * P;
+      }
+      const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
 #pragma unroll
-          for (int p = 0; p < P; ++p) dst[p] = wd[p];
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        if (v0 + 16 * kb >= nround) break;
+        const int64_t kt = (v0 >> 4) + kb;
+        uint32_t* dst = a.packed + (kt * (kD / 32) + w) * tqk::kKeysTile * P;
+#pragma unroll
+        for (int r = 0; r < NW; ++r)
+          if (64 * r + lane < 16 * P) dst[64 * r + lane] = ow[kb][r];
       }
     } else {
-      // word (coordinate j, plane p): bit i = vector v0 + i
+      // word (coordinate j, plane p): bit i = vector v0 + i; the wave's
+      // coordinates 32 w .. 32 w + 31 are 32 P contiguous words
+      constexpr int NW = (32 * P + 63) / 64;
+      uint32_t ow[NW];
+#pragma unroll
+      for (int r = 0; r < NW; ++r) ow[r] = 0u;
+#pragma unroll
       for (int jp = 0; jp < 32; jp += 2) {
-        const int j = 32 * w + jp + hi;
-        const uint32_t c = codes[l32][j];
-        uint32_t wd[P];
+        const uint32_t c = codes[l32][32 * w + jp + hi];
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-          const uint64_t m = __ballot((c >> (p < B ? p : 4)) & 1u);
-          wd[p] = hi ? (uint32_t)(m >> 32) : (uint32_t)m;
-        }
-        if (l32 == 0) {
-          uint32_t* dst = a.packed + (tile * kD + j) * P;
-#pragma unroll
-          for (int p = 0; p < P; ++p) dst[p] = wd[p];
+        for (int pp = 0; pp < P; ++pp) {
+          const uint64_t m = __ballot((c >> (pp < B ? pp : 4)) & 1u);
+          const int i0 = jp * P + pp, i1 = i0 + P;
+          if ((i0 >> 6) == (i1 >> 6))
+            ballot_to_lanes(ow[i0 >> 6], m, i0 & 63, i1 & 63);
+          else
+            ballot_to_lanes(ow[i0 >> 6], ow[i1 >> 6], m, i0 & 63, i1 & 63);
         }
       }
+      uint32_t* dst = a.packed + (tile * kD + 32 * w) * P;
+#pragma unroll
+      for (int r = 0; r < NW; ++r)
+        if (64 * r + lane < 32 * P) dst[64 * r + lane] = ow[r];
     }
     __syncthreads();  // codes / rho_part are rewritten by the next tile
   }
@@ -379,7 +419,6 @@ hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtyp
   a.packed = static_cast<uint32_t*>(packed);
   a.norm = norm;
   a.rnorm = rnorm;
-  const int64_t grid = a.ntiles < 512 ? a.ntiles : 512;
   using Fn = void (*)(QmArgs);
   // [bf16 input][mse bits - 1][prod]
   static const Fn fns[2][4][2] = {
@@ -391,7 +430,16 @@ hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtyp
        {quantize_mfma_kernel<true, 2, false>, quantize_mfma_kernel<true, 2, true>},
        {quantize_mfma_kernel<true, 3, false>, quantize_mfma_kernel<true, 3, true>},
        {quantize_mfma_kernel<true, 4, false>, quantize_mfma_kernel<true, 4, true>}}};
-  hipLaunchKernelGGL(fns[a.bf16 ? 1 : 0][a.B - 1][a.prod ? 1 : 0], dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  const Fn fn = fns[a.bf16 ? 1 : 0][a.B - 1][a.prod ? 1 : 0];
+  // persistent grid: as many workgroups as the device holds at once (the
+  // rotation-only kernels need far fewer registers and no S in LDS)
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, 0) != hipSuccess)
+    return hipErrorInvalidValue;
+  const int64_t slots = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+  const int64_t grid = a.ntiles < slots ? a.ntiles : slots;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
