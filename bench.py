@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 METRIC = "compressed-KV decode attn HBM GB/s (% of peak); quantize tokens/s"
 
 
@@ -252,6 +253,10 @@ def quantize_prefill(steps=2):
     res = {"tokens_per_s": round(tokens / sec, 1), "ms_per_step": round(sec * 1e3, 3),
            "workload": "16 seq x 8192 tok x 32 layers x 8 KV heads, d=128, bf16; K 3-bit prod, V 3-bit MSE",
            "achieved_tflops": round(flops / sec / 1e12, 2), "hbm_gbs": round(bytes_ / sec / 1e9, 1),
+           # the products run on the bf16 matrix cores (operands split into bf16
+           # high and low parts), so their own peak is the bf16 one; the fp32
+           # figure is what a plain fp32 implementation would be held to
+           "flops_roofline_frac_bf16_mfma": round(flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
            "flops_roofline_frac_fp32_vector": round(flops / sec / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
            "hbm_roofline_frac": round(bytes_ / sec / 1e9 / HBM_PEAK_GBS, 4)}
     del X

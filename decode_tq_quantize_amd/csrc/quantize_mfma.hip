@@ -74,6 +74,16 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// bf16 high and low parts (round to nearest even, v_cvt_pk_bf16_f32) of
+// two floats, packed two to a register: x = hi + lo + O(2^-17 |x|).
+__device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x0, x1}, bf16x2));
+  const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, bf16x2));
+}
+
 // Rows 32 w + 16 m + (lane % 16), columns 32 (lane / 16) .. + 31 of M.
 __device__ __forceinline__ void load_rows(const float* __restrict__ M, int w, int lane, float (&A)[2][32]) {
 #pragma unroll
@@ -128,10 +138,15 @@ __device__ __forceinline__ float sum_q(float v) {
 
 template <bool BF16IN, int B, bool PROD>
 __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
-  // S (PROD) stays in LDS, read as MFMA A operands per use, so that two
-  // workgroups fit a compute unit
-  __shared__ __attribute__((aligned(16))) float Ss[PROD ? kD : 1][kD + 4];
-  __shared__ __attribute__((aligned(16))) float rt[16][kD + 4];  // residual, [vector][coordinate]
+  // The QJL projection S r~ runs on the bf16 matrix cores with both operands
+  // split into bf16 high and low parts: S r~ = S_hi r_hi + S_hi r_lo +
+  // S_lo r_hi up to about 2^-17 |S| |r~| per term. S (PROD) stays in LDS as
+  // the two parts (two workgroups fit a compute unit); so does the residual
+  // of the current 16 vectors. Rows are 16 chunks of 8 values; chunk c of
+  // row r is stored at c ^ (r % 16), so that the 16 rows read at once hit
+  // different banks.
+  __shared__ uint4 Sq[2][PROD ? kD : 1][kD / 8];
+  __shared__ uint4 rq[2][16][kD / 8];
   // rows padded by one dword: the value layout reads a column (one vector
   // per lane), which would otherwise fall into one LDS bank
   __shared__ uint8_t codes[kTile][kD + 4];  // idx | z << 4, [vector][coordinate]
@@ -168,9 +183,17 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         }
   }
   if constexpr (PROD) {
-    for (int e = tid; e < kD * kD / 4; e += kThreads) {
-      const int row = e / (kD / 4), c4 = e % (kD / 4);
-      *reinterpret_cast<float4*>(&Ss[row][4 * c4]) = reinterpret_cast<const float4*>(a.S)[e];
+    for (int e = tid; e < kD * kD / 8; e += kThreads) {
+      const int row = e / (kD / 8), c = e % (kD / 8);
+      const float4 u0 = reinterpret_cast<const float4*>(a.S)[2 * e];
+      const float4 u1 = reinterpret_cast<const float4*>(a.S)[2 * e + 1];
+      uint32_t h[4], l[4];
+      split_bf16(u0.x, u0.y, h[0], l[0]);
+      split_bf16(u0.z, u0.w, h[1], l[1]);
+      split_bf16(u1.x, u1.y, h[2], l[2]);
+      split_bf16(u1.z, u1.w, h[3], l[3]);
+      Sq[0][row][c ^ (row & 15)] = make_uint4(h[0], h[1], h[2], h[3]);
+      Sq[1][row][c ^ (row & 15)] = make_uint4(l[0], l[1], l[2], l[3]);
     }
   }
   if (tid < TQ_MAX_LEVELS) {
@@ -259,41 +282,43 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
       if (PROD) {
         r2 = sum_q(r2);
         if (q == 0) rho_part[w][16 * nt + nl] = r2;
+        // residual coordinates 32 w + 16 m + 4 q .. + 3 of vector nl: half of
+        // chunk (4 w + 2 m + q / 2) of the vector's row
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) rt[nl][32 * w + 16 * m + 4 * q + r] = res[m][r];
-        __syncthreads();
-        float y[32];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float4 u = *reinterpret_cast<const float4*>(&rt[nl][32 * q + 4 * k]);
-          y[4 * k] = u.x;
-          y[4 * k + 1] = u.y;
-          y[4 * k + 2] = u.z;
-          y[4 * k + 3] = u.w;
+        for (int m = 0; m < 2; ++m) {
+          uint32_t h0, l0, h1, l1;
+          split_bf16(res[m][0], res[m][1], h0, l0);
+          split_bf16(res[m][2], res[m][3], h1, l1);
+          const int c = (4 * w + 2 * m + (q >> 1)) ^ nl, half = q & 1;
+          reinterpret_cast<uint2*>(&rq[0][nl][c])[half] = make_uint2(h0, h1);
+          reinterpret_cast<uint2*>(&rq[1][nl][c])[half] = make_uint2(l0, l1);
         }
-        v4f pc[2][4];
+        __syncthreads();
+        // step kk contracts coordinates 32 q' + 8 kk .. + 7 from lane group q'
+        // (chunk 4 q' + kk), the same assignment on both operands
+        v4f pc[2][3];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) pc[m][c] = v4f{0.f, 0.f, 0.f, 0.f};
+          for (int c = 0; c < 3; ++c) pc[m][c] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k4 = 0; k4 < 8; ++k4) {
-          float4 s4[2];
+        for (int kk = 0; kk < 4; ++kk) {
+          const int ph = (4 * q + kk) ^ nl;
+          const bf16x8 rh = __builtin_bit_cast(bf16x8, rq[0][nl][ph]);
+          const bf16x8 rl = __builtin_bit_cast(bf16x8, rq[1][nl][ph]);
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
-            s4[m] = *reinterpret_cast<const float4*>(&Ss[PROD ? 32 * w + 16 * m + nl : 0][32 * q + 4 * k4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int kk = 4 * k4 + e;
-            pc[0][e] = mfma_f32(s4[0][e], y[kk], pc[0][e]);
-            pc[1][e] = mfma_f32(s4[1][e], y[kk], pc[1][e]);
+          for (int m = 0; m < 2; ++m) {
+            const int row = PROD ? 32 * w + 16 * m + nl : 0;  // row % 16 == nl
+            const bf16x8 sh = __builtin_bit_cast(bf16x8, Sq[0][row][ph]);
+            const bf16x8 sl = __builtin_bit_cast(bf16x8, Sq[1][row][ph]);
+            pc[m][0] = mfma_bf16(sh, rh, pc[m][0]);
+            pc[m][1] = mfma_bf16(sh, rl, pc[m][1]);
+            pc[m][2] = mfma_bf16(sl, rh, pc[m][2]);
           }
         }
         v4f pj[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) pj[m] = (pc[m][0] + pc[m][1]) + (pc[m][2] + pc[m][3]);
+        for (int m = 0; m < 2; ++m) pj[m] = pc[m][0] + (pc[m][1] + pc[m][2]);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
