@@ -277,11 +277,13 @@ def longctx_decode(steps=5):
     groups_v = [(0, 32, 3, tq.TQ_MSE), (32, 96, 2, tq.TQ_MSE)]
     keep = []
     descs = {}
+    sample = {}  # the bf16 K and V of (batch 0, KV head 0), for the quality check
     for name, groups, layout, stream in (("k", groups_k, tq.TQ_LAYOUT_KEYS, 11), ("v", groups_v, tq.TQ_LAYOUT_VALUES, 12)):
         log(f"longctx: generating {name} ({n * d * 2 / 1e9:.1f} GB bf16), outlier channels first")
         X = sdev.kv_with_outliers(B, Hkv, T, d, 0, 1.0, seed=4, stream=stream)
         X[..., :32] *= 10  # the 32 outlier channels, already permuted to the front
         X = X.view(n, d)
+        sample[name] = X[:T].float().cpu().double().numpy()  # rows (b, g, t) -> b = 0, g = 0
         gl = []
         for gi, (ch, gd, bits, var) in enumerate(groups):
             R_t = dev(synth.haar_orthogonal(gd, 40 + gi + 10 * stream))
@@ -315,12 +317,41 @@ def longctx_decode(steps=5):
         for _ in range(steps):
             call()
     ms = tm.ms / steps
+    # quality (not parity): query heads 0..3 (KV head 0, batch 0) against exact
+    # fp64 attention on the bf16 K and V. One more (untimed) call returns the
+    # raw score estimates. With i.i.d. keys and 131072 tokens the softmax is
+    # nearly flat, so the exact output is an average near the noise floor;
+    # the output error is therefore also given relative to the rms value norm.
+    import numpy as np
+    scores = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    tq.tq_decode_attn(descs["k"], descs["v"], q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, 1 / math.sqrt(d), out,
+                      scores, ws, wsb)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    qs = q_t[0, :G].float().cpu().double().numpy()
+    o_gpu = out[0, :G].cpu().double().numpy()
+    s_gpu = scores[0, :G].cpu().double().numpy().T  # [T, G]
+    del scores
+    s_ex = sample["k"] @ qs.T  # [T, G] exact inner products
+    lg = s_ex / math.sqrt(d)
+    pw = np.exp(lg - lg.max(axis=0))
+    o_ex = (pw.T @ sample["v"]) / pw.sum(axis=0)[:, None]
+    rel = np.linalg.norm(o_gpu - o_ex, axis=1) / np.linalg.norm(o_ex, axis=1)
+    vrms = math.sqrt(float((sample["v"] ** 2).sum(axis=1).mean()))
+    rel_v = np.linalg.norm(o_gpu - o_ex, axis=1) / vrms
+    s_rel = np.linalg.norm(s_gpu - s_ex, axis=0) / np.linalg.norm(s_ex, axis=0)
+    s_cos = (s_gpu * s_ex).sum(axis=0) / (np.linalg.norm(s_gpu, axis=0) * np.linalg.norm(s_ex, axis=0))
     bytes_ = n * 84 + B * Hq * d * 6
     bf16_bytes = n * d * 2 * 2
     res = {"ms_per_call": round(ms, 4), "gbs": round(bytes_ / ms / 1e6, 1),
            "hbm_roofline_frac": round(bytes_ / ms / 1e6 / HBM_PEAK_GBS, 4),
            "bf16_attention_roofline_ms": round(bf16_bytes / HBM_PEAK_GBS / 1e6, 4),
            "speedup_vs_bf16_roofline": round(bf16_bytes / HBM_PEAK_GBS / 1e6 / ms, 3),
+           "quality_vs_exact_bf16_attention": {
+               "sample": "batch 0, query heads 0-3 (KV head 0), 131072 tokens",
+               "score_rel_error": round(float(s_rel.mean()), 4), "score_cosine": round(float(s_cos.mean()), 4),
+               "output_rel_error": round(float(rel.mean()), 4),
+               "output_error_over_rms_value_norm": round(float(rel_v.mean()), 6)},
            "workload": "batch 64 x 131072 tokens, 32 q / 8 KV heads, d=128; keys: 32 outlier channels 2+1 bits, "
                        "96 channels 1+1 bits; values 3 / 2 bits MSE; 84 B per token-head"}
     del keep, descs
