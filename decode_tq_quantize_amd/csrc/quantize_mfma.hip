@@ -101,32 +101,26 @@ __device__ __forceinline__ void load_rows(const float* __restrict__ M, int w, in
   }
 }
 
-// 32 consecutive input coordinates 32 q .. 32 q + 31 of vector row `v`
-// (clamped to a valid row; the caller masks rows past n).
-__device__ __forceinline__ void load_x(const QmArgs& a, int64_t v, int q, float (&x)[32]) {
-  if (a.bf16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + v * a.stride + 32 * q);
+// Raw input of one lane: coordinates 32 q .. 32 q + 31 of one vector row.
+template <bool BF16IN>
+struct XIn;
+template <>
+struct XIn<true> {
+  uint4 w[4];
+};
+template <>
+struct XIn<false> {
+  float4 f[8];
+};
+__device__ __forceinline__ void load_in(XIn<true>& r, const QmArgs& a, int64_t v, int q) {
+  const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + v * a.stride + 32 * q);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint4 u = p[k];
-      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+  for (int k = 0; k < 4; ++k) r.w[k] = p[k];
+}
+__device__ __forceinline__ void load_in(XIn<false>& r, const QmArgs& a, int64_t v, int q) {
+  const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + v * a.stride + 32 * q);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[8 * k + 2 * e] = __uint_as_float(wd[e] << 16);
-        x[8 * k + 2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
-      }
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + v * a.stride + 32 * q);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float4 u = p[k];
-      x[4 * k] = u.x;
-      x[4 * k + 1] = u.y;
-      x[4 * k + 2] = u.z;
-      x[4 * k + 3] = u.w;
-    }
-  }
+  for (int k = 0; k < 8; ++k) r.f[k] = p[k];
 }
 
 // Sum over the 4 lanes that hold the same vector (lanes l, l ^ 16, l ^ 32, l ^ 48).
@@ -202,6 +196,10 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
   }
   __syncthreads();
 
+  // the input of the next sub-tile is always in flight while one is
+  // processed (rows past n re-read row n - 1 and are masked)
+  XIn<BF16IN> xin;
+  load_in(xin, a, min((int64_t)blockIdx.x * kTile + nl, a.n - 1), q);
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int64_t v0 = tile * kTile;
     float nrm0 = 0.f, nrm1 = 0.f;  // norms of sub-tiles 0 and 1 (registers, not an indexed array)
@@ -209,14 +207,15 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
     for (int nt = 0; nt < 2; ++nt) {
       const int64_t v = v0 + 16 * nt + nl;
       const bool valid = v < a.n;
-      const int64_t vr = valid ? v : a.n - 1;
+      const XIn<BF16IN> cur = xin;
+      {
+        const int64_t vn = (nt == 0 ? v0 + 16 : v0 + (int64_t)gridDim.x * kTile) + nl;
+        load_in(xin, a, min(vn, a.n - 1), q);
+      }
       float s2 = 0.f;
       v4f acc[2];
       if constexpr (BF16IN) {
-        const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + vr * a.stride + 32 * q);
-        uint4 xw[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) xw[k] = xp[k];
+        const uint4(&xw)[4] = cur.w;
         v4f ah[2][2], al[2][2];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -242,7 +241,13 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         for (int m = 0; m < 2; ++m) acc[m] = (ah[m][0] + ah[m][1]) + (al[m][0] + al[m][1]);
       } else {
         float x[32];
-        load_x(a, vr, q, x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          x[4 * k] = cur.f[k].x;
+          x[4 * k + 1] = cur.f[k].y;
+          x[4 * k + 2] = cur.f[k].z;
+          x[4 * k + 3] = cur.f[k].w;
+        }
 #pragma unroll
         for (int k = 0; k < 32; ++k) s2 = fmaf(x[k], x[k], s2);
         v4f ac[2][4];
