@@ -54,8 +54,10 @@ size_t search_workspace_bytes(const tq_group& db, int64_t N, int Q, int k);
 // Matrix-core scores (search_mfma.hip): y~ = R y, y^ = S y~ into qt, qh
 // ([Q][d] each) and the score matrix [Q][N].
 bool search_mfma_supported(const tq_group& db);
+// Bytes of workspace the matrix-core scan needs beyond y~, y^ and the scores.
+size_t search_mfma_extra_bytes(const tq_group& db, int Q);
 hipError_t launch_search_mfma_scores(const tq_group& db, int64_t N, const float* queries, int Q, float* qt,
-                                     float* qh, float* scores, hipStream_t s);
+                                     float* qh, float* scores, void* extra, hipStream_t s);
 hipError_t launch_search(const tq_group& db, int64_t N, const float* queries, int Q, int k, int64_t* out_idx,
                          float* out_score, void* ws, hipStream_t s);
 

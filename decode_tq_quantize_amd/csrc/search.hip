@@ -181,7 +181,8 @@ namespace tqk {
 
 size_t search_workspace_bytes(const tq_group& db, int64_t N, int Q, int k) {
   (void)k;
-  return ((size_t)Q * 2 * db.q.d + (size_t)Q * N) * sizeof(float);
+  return ((((size_t)Q * 2 * db.q.d + (size_t)Q * N) * sizeof(float) + 15) & ~(size_t)15) +
+         search_mfma_extra_bytes(db, Q);
 }
 
 hipError_t launch_search(const tq_group& db, int64_t N, const float* queries, int Q, int k, int64_t* out_idx,
@@ -208,7 +209,8 @@ hipError_t launch_search(const tq_group& db, int64_t N, const float* queries, in
   hipError_t e;
   if (search_mfma_supported(db)) {
     // matrix-core scores: y~ [Q][d], y^ [Q][d], then the score matrix
-    e = launch_search_mfma_scores(db, N, queries, Q, a.qprep, a.qprep + (size_t)Q * a.d, a.scores, s);
+    char* extra = static_cast<char*>(ws) + ((((size_t)Q * 2 * a.d + (size_t)Q * N) * sizeof(float) + 15) & ~(size_t)15);
+    e = launch_search_mfma_scores(db, N, queries, Q, a.qprep, a.qprep + (size_t)Q * a.d, a.scores, extra, s);
     if (e != hipSuccess) return e;
   } else {
     hipLaunchKernelGGL(sprep_kernel, dim3(Q), dim3(kThreads), 2 * a.d * sizeof(float), s, a);

@@ -17,6 +17,18 @@
 //        4 w .. 4 w + 3 of the block for all 4 query tiles (16 accumulators).
 //        Scores (times n) go to the score matrix, which the top-k kernel of
 //        search.hip reduces.
+// scan2 (bf16 matrix cores; used for 3 code bits with QJL): the
+//        codebook is mirror-symmetric, so c[idx] = sum_{|S| odd} alpha_S
+//        prod_{p in S} (2 b_p - 1), and each product of signs is 2 (xor of
+//        planes) - 1. The query side carries 2 alpha_S y~ per term and
+//        gamma y^ for the QJL term, split into bf16 high and low parts
+//        (qsplit_kernel); the database side is the xor-ed plane bits as bf16
+//        {0, 1} ({0, 2 rho}, split the same way, for the QJL term), so every
+//        product is exact up to the splits (about 2^-17 relative per term,
+//        fp32 accumulation). The constant parts sum_S alpha_S sum y~ and
+//        rho gamma sum y^ are removed per (query, vector) at the end.
+//        v_mfma_f32_16x16x32_bf16 contracts 32 coordinates at once: lane
+//        group kq carries coordinates 32 g + 8 kq .. + 7 on both operands.
 #include <math.h>
 
 #include "device_common.h"
@@ -173,14 +185,280 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a) {
     }
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v4f mfma_bf16(bf16x8 a, bf16x8 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// bf16 high and low parts (round to nearest even) of two floats, two to a
+// register; s0, s1 return hi + lo as floats (the values the products use).
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo, float& s0, float& s1) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x0, x1}, bf16x2));
+  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x0 - h0, x1 - h1}, bf16x2));
+  s0 = h0 + __uint_as_float(lo << 16);
+  s1 = h1 + __uint_as_float(lo & 0xffff0000u);
+}
+
+constexpr int kMaxTerms = 9;  // up to 8 odd subsets + the QJL term
+
+struct QsArgs {
+  const float* qt;  // [Q][d]
+  const float* qh;  // [Q][d]
+  uint16_t* ops;    // [Q][terms][2][d] bf16 bits (high, low)
+  float* cq;        // [Q][2]: sum_S alpha_S sum_c y~_c, gamma sum_c y^_c (as split)
+  int Q, d;
+  float gamma;
+  float alpha[kMaxTerms];
+};
+
+// Per query: the bf16 operand planes of every term and the constant parts.
+template <int B, bool PROD>
+__global__ __launch_bounds__(kThreads) void qsplit_kernel(QsArgs a) {
+  constexpr int TW = 1 << (B - 1), T = TW + (PROD ? 1 : 0);
+  __shared__ float red[2][kThreads / 64];
+  const int qi = blockIdx.x, tid = threadIdx.x;
+  const float* yt = a.qt + (int64_t)qi * a.d;
+  const float* yh = a.qh + (int64_t)qi * a.d;
+  uint32_t* ops = reinterpret_cast<uint32_t*>(a.ops + (int64_t)qi * T * 2 * a.d);
+  float c1 = 0.f, c2 = 0.f;
+  for (int c = 2 * tid; c < a.d; c += 2 * kThreads) {
+    const float t0 = yt[c], t1 = yt[c + 1];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      uint32_t hi, lo;
+      float s0, s1;
+      split2(2.f * a.alpha[t] * t0, 2.f * a.alpha[t] * t1, hi, lo, s0, s1);
+      ops[((t * 2 + 0) * a.d + c) >> 1] = hi;
+      ops[((t * 2 + 1) * a.d + c) >> 1] = lo;
+      c1 += 0.5f * (s0 + s1);
+    }
+    if (PROD) {
+      uint32_t hi, lo;
+      float s0, s1;
+      split2(a.gamma * yh[c], a.gamma * yh[c + 1], hi, lo, s0, s1);
+      ops[(((T - 1) * 2 + 0) * a.d + c) >> 1] = hi;
+      ops[(((T - 1) * 2 + 1) * a.d + c) >> 1] = lo;
+      c2 += s0 + s1;
+    }
+  }
+  c1 = tqd::wave_sum(c1);
+  c2 = tqd::wave_sum(c2);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = c1;
+    red[1][tid >> 6] = c2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float s1 = 0.f, s2 = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      s1 += red[0][w];
+      s2 += red[1][w];
+    }
+    a.cq[2 * qi] = s1;
+    a.cq[2 * qi + 1] = s2;
+  }
+}
+
+struct Scan2Args {
+  const uint32_t* packed;
+  const uint16_t* norm;
+  const uint16_t* rnorm;
+  const uint16_t* ops;  // [Q][terms][2][d]
+  const float* cq;      // [Q][2]
+  float* scores;        // [Q][N]
+  int64_t N;
+  int Q, d;
+};
+
+// Odd subsets of B planes in ascending bitmask order (the order of the
+// coefficients the host passes).
+__host__ __device__ constexpr int odd_subset(int B, int t) {
+  int n = 0;
+  for (int S = 1; S < (1 << B); ++S) {
+    int pc = 0;
+    for (int x = S; x; x >>= 1) pc += x & 1;
+    if (pc & 1) {
+      if (n == t) return S;
+      ++n;
+    }
+  }
+  return 0;
+}
+
+// Eight bits t (bit e = coordinate e) as eight bf16 values mag * bit, two to
+// a register (register j: coordinate 2 j in the low half, 2 j + 1 in the
+// high half). mag is a bf16 bit pattern.
+__device__ __forceinline__ bf16x8 bits_to_bf16(uint32_t t, uint32_t mag) {
+  uint32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = ((((t >> (2 * j)) & 3u) * 0x8001u) & 0x10001u) * mag;
+  return __builtin_bit_cast(bf16x8, make_uint4(r[0], r[1], r[2], r[3]));
+}
+
+// Workgroup: 64 queries x 256 database vectors, 4 waves; wave w takes query
+// tiles 2 (w % 2) and 2 (w % 2) + 1 and database tiles 8 (w / 2) .. + 7.
+template <int B, bool PROD>
+__global__ __launch_bounds__(kThreads, 2) void scan2_kernel(Scan2Args a) {
+  constexpr int TW = 1 << (B - 1), T = TW + (PROD ? 1 : 0), P = B + (PROD ? 1 : 0);
+  // query operands of one 32-coordinate group: [term][plane][query][chunk of
+  // 8 coordinates]; chunk c of query row r is stored at c ^ ((r / 2) % 4)
+  __shared__ uint4 aq[T][2][kQB][4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kq = lane >> 4, nl = lane & 15;
+  const int64_t vb = (int64_t)blockIdx.x * kNB;
+  const int q0 = blockIdx.y * kQB;
+  const int G = a.d / 32;
+  const int64_t last_tile = (a.N - 1) / tqk::kKeysTile;
+  const int qt0 = 2 * (w & 1), dt0 = 8 * (w >> 1);
+  int64_t tile[8];
+  uint32_t r2h[8], r2l[8];  // bf16 bits of 2 rho, high and low parts
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    tile[j] = min((vb >> 4) + dt0 + j, last_tile);
+    const int64_t v = vb + 16 * (dt0 + j) + nl;
+    const int64_t vr = v < a.N ? v : a.N - 1;
+    if (PROD) {
+      const float rho2 = 2.f * tqd::half_bits_to_f32(a.rnorm[vr]);
+      const uint32_t hb = __builtin_bit_cast(uint16_t, (__bf16)rho2);
+      r2h[j] = hb;
+      r2l[j] = __builtin_bit_cast(uint16_t, (__bf16)(rho2 - __uint_as_float(hb << 16)));
+    } else {
+      r2h[j] = r2l[j] = 0u;
+    }
+  }
+  v4f acc[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // this lane's plane words of its 8 database tiles, one coordinate group
+  // ahead (group g + 1 is loaded while group g is processed)
+  uint32_t wn[8][P];
+  auto load_words = [&](int g) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t* p = a.packed + ((tile[j] * G + g) * tqk::kKeysTile + nl) * P;
+#pragma unroll
+      for (int pp = 0; pp < P; ++pp) wn[j][pp] = p[pp];
+    }
+  };
+  load_words(0);
+  for (int g = 0; g < G; ++g) {
+    // stage the query operands of coordinates 32 g .. 32 g + 31: element
+    // e = tid + 256 it is (term * 2 + plane = it, row = tid / 4, chunk =
+    // tid % 4); loads in batches of T, all issued before their LDS writes
+    {
+      const int c = tid & 3, row = tid >> 2;
+      const int qr = min(q0 + row, a.Q - 1);
+      const uint4* src = reinterpret_cast<const uint4*>(a.ops + (int64_t)qr * T * 2 * a.d + 32 * g) + c;
+#pragma unroll
+      for (int b0 = 0; b0 < 2 * T; b0 += T) {
+        uint4 u[T];
+#pragma unroll
+        for (int it = 0; it < T; ++it) u[it] = src[(int64_t)(b0 + it) * a.d / 8];
+#pragma unroll
+        for (int it = 0; it < T; ++it) {
+          const int tp = b0 + it;
+          aq[tp >> 1][tp & 1][row][c ^ ((row >> 1) & 3)] = u[it];
+        }
+      }
+    }
+    // this lane's bits (coordinates 32 g + 8 kq .. + 7) of every plane
+    uint32_t wd[8][P];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int pp = 0; pp < P; ++pp) wd[j][pp] = wn[j][pp] >> (8 * kq);
+    load_words(g + 1 < G ? g + 1 : g);
+    __syncthreads();
+    // query operands of the wave's two query tiles (row 16 qt + nl, chunk kq)
+    bf16x8 A[2][T][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 16 * (qt0 + i) + nl;
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) A[i][t][pl] = __builtin_bit_cast(bf16x8, aq[t][pl][row][kq ^ ((row >> 1) & 3)]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bf16x8 Bw[TW];
+#pragma unroll
+      for (int t = 0; t < TW; ++t) {
+        const int S = odd_subset(B, t);
+        uint32_t x = 0u;
+#pragma unroll
+        for (int pp = 0; pp < B; ++pp)
+          if ((S >> pp) & 1) x ^= wd[j][pp];
+        Bw[t] = bits_to_bf16(x & 0xffu, 0x3f80u);  // bf16 1.0
+      }
+      bf16x8 Bh = Bw[0], Bl = Bw[0];
+      if (PROD) {
+        Bh = bits_to_bf16(wd[j][P - 1] & 0xffu, r2h[j]);
+        Bl = bits_to_bf16(wd[j][P - 1] & 0xffu, r2l[j]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+          acc[i][j] = mfma_bf16(A[i][t][0], Bw[t], acc[i][j]);
+          acc[i][j] = mfma_bf16(A[i][t][1], Bw[t], acc[i][j]);
+        }
+        if (PROD) {
+          acc[i][j] = mfma_bf16(A[i][T - 1][0], Bh, acc[i][j]);
+          acc[i][j] = mfma_bf16(A[i][T - 1][0], Bl, acc[i][j]);
+          acc[i][j] = mfma_bf16(A[i][T - 1][1], Bh, acc[i][j]);
+        }
+      }
+    }
+    __syncthreads();  // aq is rewritten for the next group
+  }
+  // scores of queries q0 + 16 qt + 4 kq + r and vectors vb + 16 (dt0 + j) + nl:
+  // n (acc - C1 - rho C2)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qi = q0 + 16 * (qt0 + i) + 4 * kq + r;
+      if (qi < a.Q) {
+        const float c1 = a.cq[2 * qi], c2 = a.cq[2 * qi + 1];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int64_t v = vb + 16 * (dt0 + j) + nl;
+          if (v < a.N) {
+            const float n = tqd::half_bits_to_f32(a.norm[v]);
+            const float rho = PROD ? tqd::half_bits_to_f32(a.rnorm[v]) : 0.f;
+            a.scores[(int64_t)qi * a.N + v] = n * (acc[i][j][r] - c1 - rho * c2);
+          }
+        }
+      }
+    }
+}
+
 }  // namespace
 
 namespace tqk {
 
 bool search_mfma_supported(const tq_group& db) { return db.q.d % 32 == 0 && db.q.d >= 32; }
 
+// The bf16 scan serves codes of 3 bits with the QJL sign (4-bit search
+// codes); other widths take the fp32 scan.
+static bool scan2_supported(const tq_group& db) { return db.q.variant == TQ_PROD && db.q.mse_bits == 3; }
+
+size_t search_mfma_extra_bytes(const tq_group& db, int Q) {
+  if (!search_mfma_supported(db) || !scan2_supported(db)) return 0;
+  const int T = (1 << (db.q.mse_bits - 1)) + 1;
+  return (size_t)Q * T * 2 * db.q.d * sizeof(uint16_t) + (size_t)Q * 2 * sizeof(float);
+}
+
 hipError_t launch_search_mfma_scores(const tq_group& db, int64_t N, const float* queries, int Q, float* qt,
-                                     float* qh, float* scores, hipStream_t s) {
+                                     float* qh, float* scores, void* extra, hipStream_t s) {
   const int d = db.q.d;
   const dim3 gg(d / kGT, (Q + kGT - 1) / kGT);
   hipLaunchKernelGGL(qgemm_kernel, gg, dim3(kGT * kGT), 0, s, queries, Q, db.q.R, d, qt);
@@ -199,6 +477,45 @@ hipError_t launch_search_mfma_scores(const tq_group& db, int64_t N, const float*
   a.prod = db.q.variant == TQ_PROD;
   a.gamma = (float)(sqrt(M_PI / 2.0) / d);
   for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = db.q.centroids[i];
+  if (scan2_supported(db)) {
+    const int B = db.q.mse_bits, T = (1 << (B - 1)) + 1;
+    QsArgs qa{};
+    qa.qt = qt;
+    qa.qh = qh;
+    qa.ops = static_cast<uint16_t*>(extra);
+    qa.cq = reinterpret_cast<float*>(qa.ops + (size_t)Q * T * 2 * d);
+    qa.Q = Q;
+    qa.d = d;
+    qa.gamma = (float)(sqrt(M_PI / 2.0) / d);
+    // Walsh coefficients of the mirror-symmetric codebook, odd subsets in
+    // ascending bitmask order: alpha_S = mean over idx of c[idx] prod_{p in S} (2 b_p - 1)
+    int nt = 0;
+    for (int S = 1; S < (1 << B); ++S) {
+      if (!(__builtin_popcount(S) & 1)) continue;
+      double acc = 0.0;
+      for (int idx = 0; idx < (1 << B); ++idx) {
+        double chi = 1.0;
+        for (int p = 0; p < B; ++p)
+          if ((S >> p) & 1) chi *= ((idx >> p) & 1) ? 1.0 : -1.0;
+        acc += chi * (double)db.q.centroids[idx];
+      }
+      qa.alpha[nt++] = (float)(acc / (1 << B));
+    }
+    Scan2Args sa{};
+    sa.packed = static_cast<const uint32_t*>(db.packed);
+    sa.norm = db.norm;
+    sa.rnorm = db.rnorm;
+    sa.ops = qa.ops;
+    sa.cq = qa.cq;
+    sa.scores = scores;
+    sa.N = N;
+    sa.Q = Q;
+    sa.d = d;
+    const dim3 grid2((unsigned)((N + kNB - 1) / kNB), (Q + kQB - 1) / kQB);
+    hipLaunchKernelGGL((qsplit_kernel<3, true>), dim3(Q), dim3(kThreads), 0, s, qa);
+    hipLaunchKernelGGL((scan2_kernel<3, true>), grid2, dim3(kThreads), 0, s, sa);
+    return hipGetLastError();
+  }
   using Fn = void (*)(ScanArgs);
   static const Fn fns[4][2] = {{scan_kernel<1, false>, scan_kernel<1, true>},
                                {scan_kernel<2, false>, scan_kernel<2, true>},
