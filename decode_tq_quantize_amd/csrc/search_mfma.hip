@@ -264,6 +264,7 @@ __global__ __launch_bounds__(kThreads) void qsplit_kernel(QsArgs a) {
 
 struct Scan2Args {
   const uint32_t* packed;
+  int64_t packed_bytes;
   const uint16_t* norm;
   const uint16_t* rnorm;
   const uint16_t* ops;  // [Q][terms][2][d]
@@ -303,9 +304,13 @@ __device__ __forceinline__ bf16x8 bits_to_bf16(uint32_t t, uint32_t mag) {
 template <int B, bool PROD>
 __global__ __launch_bounds__(kThreads, 2) void scan2_kernel(Scan2Args a) {
   constexpr int TW = 1 << (B - 1), T = TW + (PROD ? 1 : 0), P = B + (PROD ? 1 : 0);
-  // query operands of one 32-coordinate group: [term][plane][query][chunk of
-  // 8 coordinates]; chunk c of query row r is stored at c ^ ((r / 2) % 4)
-  __shared__ uint4 aq[T][2][kQB][4];
+  static_assert(P == 4, "one byte per plane in a register");
+  // query operands of a 32-coordinate group, two groups in flight:
+  // [buffer][term][plane][query][chunk of 8 coordinates]; chunk c of query
+  // row r is stored at c ^ ((r / 2) % 4). Filled by direct global-to-LDS
+  // loads (lane L of a load lands 16 L bytes past the instruction's base),
+  // so the next group's operands arrive while this group is multiplied.
+  __shared__ uint4 aq[2][T][2][kQB][4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kq = lane >> 4, nl = lane & 15;
@@ -339,43 +344,63 @@ __global__ __launch_bounds__(kThreads, 2) void scan2_kernel(Scan2Args a) {
   // this lane's plane words of its 8 database tiles, one coordinate group
   // ahead (group g + 1 is loaded while group g is processed)
   uint32_t wn[8][P];
+  // (through a buffer resource: uniform byte offset per tile and group, one
+  // lane offset; the database is below 4 GB, which the host checks)
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(a.packed), (short)0, (int)(uint32_t)min(a.packed_bytes, (int64_t)0xffffffff), 0x00020000);
+  const uint32_t word_off = (uint32_t)(nl * P * 4);
   auto load_words = [&](int g) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t* p = a.packed + ((tile[j] * G + g) * tqk::kKeysTile + nl) * P;
-#pragma unroll
-      for (int pp = 0; pp < P; ++pp) wn[j][pp] = p[pp];
+      const uint32_t soff = (uint32_t)((tile[j] * G + g) * (tqk::kKeysTile * P * 4));
+      const u4 u = __builtin_amdgcn_raw_buffer_load_b128(wres, word_off, soff, 0);
+      wn[j][0] = u[0];
+      wn[j][1] = u[1];
+      wn[j][2] = u[2];
+      wn[j][3] = u[3];
     }
   };
+  // staging of group g into buffer bf: plane tp (= term * 2 + plane) of rows
+  // 16 w .. 16 w + 15 is one wave-wide load per plane; lane L carries row
+  // 16 w + L / 4, physical chunk L % 4 (logical chunk (L % 4) ^ ((row / 2) % 4)).
+  // The per-lane byte offset is the same for every plane and group; the
+  // plane and group enter through the uniform base.
+  uint32_t stage_off;
+  {
+    const int row = 16 * w + (lane >> 2);
+    const int qr = min(q0 + row, a.Q - 1);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    stage_off = (uint32_t)(((int64_t)qr * T * 2 * a.d + 8 * c) * sizeof(uint16_t));
+  }
+  const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.ops), (short)0, (int)((int64_t)a.Q * T * 2 * a.d * 2), 0x00020000);
+  auto stage = [&](int g, int bf) {
+#pragma unroll
+    for (int tp = 0; tp < 2 * T; ++tp)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ores, (__attribute__((address_space(3))) void*)&aq[bf][tp >> 1][tp & 1][16 * w][0],
+                                               16, stage_off, (uint32_t)((tp * a.d + 32 * g) * 2), 0, 0);
+  };
   load_words(0);
+  stage(0, 0);
   for (int g = 0; g < G; ++g) {
-    // stage the query operands of coordinates 32 g .. 32 g + 31: element
-    // e = tid + 256 it is (term * 2 + plane = it, row = tid / 4, chunk =
-    // tid % 4); loads in batches of T, all issued before their LDS writes
+    const int bf = g & 1;
+    // this group's staged operands and words have arrived (own loads), and
+    // every wave's (barrier)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // this lane's bits (coordinates 32 g + 8 kq .. + 7) of the P = 4 planes
+    // of each database tile, one byte per plane
+    uint32_t wc[8];
     {
-      const int c = tid & 3, row = tid >> 2;
-      const int qr = min(q0 + row, a.Q - 1);
-      const uint4* src = reinterpret_cast<const uint4*>(a.ops + (int64_t)qr * T * 2 * a.d + 32 * g) + c;
+      const uint32_t sel = (uint32_t)kq | ((4u + kq) << 8) | 0x0c0c0000u;
 #pragma unroll
-      for (int b0 = 0; b0 < 2 * T; b0 += T) {
-        uint4 u[T];
-#pragma unroll
-        for (int it = 0; it < T; ++it) u[it] = src[(int64_t)(b0 + it) * a.d / 8];
-#pragma unroll
-        for (int it = 0; it < T; ++it) {
-          const int tp = b0 + it;
-          aq[tp >> 1][tp & 1][row][c ^ ((row >> 1) & 3)] = u[it];
-        }
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t lo = __builtin_amdgcn_perm(wn[j][1], wn[j][0], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(wn[j][3], wn[j][2], sel);
+        wc[j] = lo | (hi << 16);
       }
     }
-    // this lane's bits (coordinates 32 g + 8 kq .. + 7) of every plane
-    uint32_t wd[8][P];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int pp = 0; pp < P; ++pp) wd[j][pp] = wn[j][pp] >> (8 * kq);
-    load_words(g + 1 < G ? g + 1 : g);
-    __syncthreads();
     // query operands of the wave's two query tiles (row 16 qt + nl, chunk kq)
     bf16x8 A[2][T][2];
 #pragma unroll
@@ -384,7 +409,14 @@ __global__ __launch_bounds__(kThreads, 2) void scan2_kernel(Scan2Args a) {
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl) A[i][t][pl] = __builtin_bit_cast(bf16x8, aq[t][pl][row][kq ^ ((row >> 1) & 3)]);
+        for (int pl = 0; pl < 2; ++pl)
+          A[i][t][pl] = __builtin_bit_cast(bf16x8, aq[bf][t][pl][row][kq ^ ((row >> 1) & 3)]);
+    }
+    // the next group's operands and words (buffer bf ^ 1 was last read in
+    // group g - 1, which every wave finished before the barrier above)
+    if (g + 1 < G) {
+      stage(g + 1, bf ^ 1);
+      load_words(g + 1);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -395,13 +427,13 @@ __global__ __launch_bounds__(kThreads, 2) void scan2_kernel(Scan2Args a) {
         uint32_t x = 0u;
 #pragma unroll
         for (int pp = 0; pp < B; ++pp)
-          if ((S >> pp) & 1) x ^= wd[j][pp];
+          if ((S >> pp) & 1) x ^= wc[j] >> (8 * pp);
         Bw[t] = bits_to_bf16(x & 0xffu, 0x3f80u);  // bf16 1.0
       }
       bf16x8 Bh = Bw[0], Bl = Bw[0];
       if (PROD) {
-        Bh = bits_to_bf16(wd[j][P - 1] & 0xffu, r2h[j]);
-        Bl = bits_to_bf16(wd[j][P - 1] & 0xffu, r2l[j]);
+        Bh = bits_to_bf16((wc[j] >> (8 * (P - 1))) & 0xffu, r2h[j]);
+        Bl = bits_to_bf16((wc[j] >> (8 * (P - 1))) & 0xffu, r2l[j]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -417,7 +449,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan2_kernel(Scan2Args a) {
         }
       }
     }
-    __syncthreads();  // aq is rewritten for the next group
   }
   // scores of queries q0 + 16 qt + 4 kq + r and vectors vb + 16 (dt0 + j) + nl:
   // n (acc - C1 - rho C2)
@@ -449,10 +480,15 @@ bool search_mfma_supported(const tq_group& db) { return db.q.d % 32 == 0 && db.q
 
 // The bf16 scan serves codes of 3 bits with the QJL sign (4-bit search
 // codes); other widths take the fp32 scan.
-static bool scan2_supported(const tq_group& db) { return db.q.variant == TQ_PROD && db.q.mse_bits == 3; }
+static bool scan2_supported(const tq_group& db, int64_t N, int Q) {
+  // (buffer offsets into the database and the query operands are 32-bit)
+  const int64_t bytes = (N + kKeysTile - 1) / kKeysTile * kKeysTile * (db.q.d / 32) * 4 * 4;
+  const int64_t qbytes = (int64_t)Q * 5 * 2 * db.q.d * 2;
+  return db.q.variant == TQ_PROD && db.q.mse_bits == 3 && bytes < ((int64_t)1 << 32) && qbytes < ((int64_t)1 << 31);
+}
 
 size_t search_mfma_extra_bytes(const tq_group& db, int Q) {
-  if (!search_mfma_supported(db) || !scan2_supported(db)) return 0;
+  if (!search_mfma_supported(db) || !scan2_supported(db, 0, Q)) return 0;
   const int T = (1 << (db.q.mse_bits - 1)) + 1;
   return (size_t)Q * T * 2 * db.q.d * sizeof(uint16_t) + (size_t)Q * 2 * sizeof(float);
 }
@@ -477,7 +513,7 @@ hipError_t launch_search_mfma_scores(const tq_group& db, int64_t N, const float*
   a.prod = db.q.variant == TQ_PROD;
   a.gamma = (float)(sqrt(M_PI / 2.0) / d);
   for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = db.q.centroids[i];
-  if (scan2_supported(db)) {
+  if (extra && scan2_supported(db, N, Q)) {
     const int B = db.q.mse_bits, T = (1 << (B - 1)) + 1;
     QsArgs qa{};
     qa.qt = qt;
@@ -503,6 +539,7 @@ hipError_t launch_search_mfma_scores(const tq_group& db, int64_t N, const float*
     }
     Scan2Args sa{};
     sa.packed = static_cast<const uint32_t*>(db.packed);
+    sa.packed_bytes = (int64_t)((N + kKeysTile - 1) / kKeysTile) * kKeysTile * (d / 32) * 4 * 4;
     sa.norm = db.norm;
     sa.rnorm = db.rnorm;
     sa.ops = qa.ops;
