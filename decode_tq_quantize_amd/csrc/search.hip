@@ -10,10 +10,8 @@
 //  sprep   y~ = R y and y^ = S y~ for every query (fp32)
 //  scores  one workgroup per (256 database vectors, 8 queries): thread =
 //          database vector, the queries' y~ / y^ staged in LDS
-//  topk    one workgroup per query: every thread keeps a sorted top-k of its
-//          strided share of the scores; the candidates are then ranked by
-//          counting, for each, the candidates that beat it (higher score, or
-//          equal score and lower index), and rank < k is written out.
+//  topk2   one workgroup per query: a threshold filter over the score row
+//          with per-wave candidate lists, re-ranked by counting (below)
 #include <math.h>
 
 #include "device_common.h"
@@ -115,64 +113,132 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(SArgs a) {
 }
 
 // (s1, i1) ranks before (s2, i2)
-__device__ __forceinline__ bool beats(float s1, int64_t i1, float s2, int64_t i2) {
+// Top-k of one score row by threshold filtering. One workgroup of 8 waves per query; wave w reads chunks
+// w, w + 8, ... of 1024 scores (64 lanes x 16, four 16-byte loads per lane,
+// the next chunk in flight while one is examined). Each wave keeps its best k
+// in LDS, sorted, and its k-th best score as a threshold: a score below the
+// threshold cannot enter, so in the common case a chunk costs 16 compares per
+// lane. Scores at or above it are appended to a per-wave candidate list
+// (ballot + prefix count); when 64 or more have gathered, the list and the
+// current best k are re-ranked by counting, for each entry, the entries that
+// beat it (higher score, or equal score and lower index). The 8 waves' lists
+// are merged the same way at the end. Rows start at any 4-byte boundary: the
+// buffer resource starts at the 16-byte boundary below the row and elements
+// outside [0, N) are never candidates.
+constexpr int kTk2Waves = 8;
+constexpr int kTk2Cap = 64 + 128;  // best k (<= 64) + candidates (< 128)
+
+__device__ __forceinline__ bool beats32(float s1, int i1, float s2, int i2) {
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(SArgs a, int nthreads) {
-  extern __shared__ unsigned char raw[];
-  float* ls = reinterpret_cast<float*>(raw);                      // nthreads * k scores
-  int64_t* li = reinterpret_cast<int64_t*>(ls + nthreads * a.k);  // nthreads * k indices
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(64 * kTk2Waves) void topk2_kernel(const float* scores, int64_t N, int k,
+                                                           int64_t* out_idx, float* out_score) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  // per wave: entries [0, k) are its best k in rank order, [k, k + count) the
+  // candidates gathered since the last re-ranking; .x = score bits, .y = index
+  __shared__ uint2 E[kTk2Waves][kTk2Cap];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qi = blockIdx.x;
-  const int k = a.k;
-  const float* sc = a.scores + (int64_t)qi * a.N;
-  if (tid < nthreads) {
-    float* ms = ls + tid * k;
-    int64_t* mi = li + tid * k;
-    int cnt = 0;
-    for (int64_t i = tid; i < a.N; i += nthreads) {
-      const float s = sc[i];
-      if (cnt == k && !beats(s, i, ms[k - 1], mi[k - 1])) continue;
-      int pos = cnt < k ? cnt : k - 1;
-      while (pos > 0 && beats(s, i, ms[pos - 1], mi[pos - 1])) {
-        ms[pos] = ms[pos - 1];
-        mi[pos] = mi[pos - 1];
-        --pos;
-      }
-      ms[pos] = s;
-      mi[pos] = i;
-      if (cnt < k) ++cnt;
-    }
-    for (int c = cnt; c < k; ++c) {
-      ms[c] = -INFINITY;
-      mi[c] = -1;
-    }
-  }
-  __syncthreads();
-  const int ncand = nthreads * k;
-  for (int c = tid; c < ncand; c += kThreads) {
-    const int64_t ic = li[c];
-    if (ic < 0) continue;
-    const float s = ls[c];
-    int rank = 0;
-    for (int o = 0; o < ncand && rank < k; ++o) {
-      const int64_t io = li[o];
-      if (io >= 0 && beats(ls[o], io, s, ic)) ++rank;
-    }
-    if (rank < k) {
-      a.out_idx[(int64_t)qi * k + rank] = ic;
-      a.out_score[(int64_t)qi * k + rank] = s;
-    }
-  }
-}
+  const uintptr_t ra = reinterpret_cast<uintptr_t>(scores + (int64_t)qi * N);
+  const int off0 = (int)((ra & 15) >> 2);
+  const int nel = (int)N + off0;
+  const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(ra & ~(uintptr_t)15), (short)0, (int)(4 * nel), 0x00020000);
+  const int nch = (nel + 1023) >> 10;
+  // distinct placeholders that every real entry beats (-inf, indices above
+  // any row index), in rank order
+  E[w][lane] = make_uint2(__float_as_uint(-INFINITY), 0x7fff0000u + (uint32_t)(w * 64 + lane));
+  float tau = -INFINITY;  // score of the wave's k-th best entry
+  int count = 0;
 
-int topk_threads(int k) {
-  int t = 8192 / k;  // LDS: t * k * 12 bytes <= 96 KB
-  t = t / 64 * 64;
-  if (t > kThreads) t = kThreads;
-  if (t < 64) t = 64;
-  return t;
+  auto rerank = [&]() __attribute__((always_inline)) {
+    const int n = k + count;
+    float sv[3];
+    int iv[3], rk[3] = {0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const int e = lane + 64 * t;
+      const uint2 x = E[w][e < n ? e : 0];
+      sv[t] = __uint_as_float(x.x);
+      iv[t] = e < n ? (int)x.y : 0x7fffffff;
+    }
+    for (int o = 0; o < n; ++o) {
+      const uint2 x = E[w][o];
+      const float so = __uint_as_float(x.x);
+      const int io = (int)x.y;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) rk[t] += beats32(so, io, sv[t], iv[t]) ? 1 : 0;
+    }
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      if (lane + 64 * t < n && rk[t] < k) E[w][rk[t]] = make_uint2(__float_as_uint(sv[t]), (uint32_t)iv[t]);
+    tau = __uint_as_float(__builtin_amdgcn_readfirstlane(E[w][k - 1].x));
+    count = 0;
+  };
+
+  // examine one chunk held in registers
+  auto examine = [&](const u4 (&x)[4], int c) __attribute__((always_inline)) {
+    bool any = false;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) any |= __uint_as_float(x[sl][e]) >= tau;
+    if (__builtin_amdgcn_ballot_w64(any) == 0) return;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = __uint_as_float(x[sl][e]);
+        const int i = c * 1024 + sl * 256 + lane * 4 + e - off0;
+        const bool cand = v >= tau && i >= 0 && i < (int)N;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(cand);
+        if (m != 0) {
+          if (cand) {
+            const int pos = k + count + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            E[w][pos] = make_uint2(__float_as_uint(v), (uint32_t)i);
+          }
+          count += __builtin_popcountll(m);
+          if (count >= 64) rerank();
+        }
+      }
+  };
+  // chunk c of the row at lane offset voff (loads past the row's end return
+  // zeros, and their elements are never candidates)
+  auto load = [&](u4 (&x)[4], int c) __attribute__((always_inline)) {
+    const uint32_t voff = (uint32_t)(lane * 16) + (uint32_t)c * 4096u;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) x[sl] = __builtin_amdgcn_raw_buffer_load_b128(res, voff + 1024 * sl, 0, 0);
+  };
+  // two chunks per iteration, each loaded one chunk ahead
+  u4 xa[4], xb[4];
+  load(xa, w);
+  for (int c = w; c < nch; c += 2 * kTk2Waves) {
+    load(xb, c + kTk2Waves);
+    examine(xa, c);
+    load(xa, c + 2 * kTk2Waves);
+    examine(xb, c + kTk2Waves);
+  }
+  if (count > 0) rerank();
+  __syncthreads();
+  // merge: the 8 k entries of all waves, ranked by counting
+  const int n = kTk2Waves * k;
+  if (tid < n) {
+    const uint2 x = E[tid / k][tid % k];
+    const float sv = __uint_as_float(x.x);
+    const int iv = (int)x.y;
+    int rk = 0;
+    for (int o = 0; o < n; ++o) {
+      const uint2 y = E[o / k][o % k];
+      rk += beats32(__uint_as_float(y.x), (int)y.y, sv, iv) ? 1 : 0;
+    }
+    if (rk < k) {
+      out_idx[(int64_t)qi * k + rk] = iv;
+      out_score[(int64_t)qi * k + rk] = sv;
+    }
+  }
 }
 
 }  // namespace
@@ -220,11 +286,7 @@ hipError_t launch_search(const tq_group& db, int64_t N, const float* queries, in
     hipLaunchKernelGGL(scores_kernel, dim3((unsigned)((N + kThreads - 1) / kThreads), (Q + kQ - 1) / kQ),
                        dim3(kThreads), lds_sc, s, a);
   }
-  const int nt = topk_threads(k);
-  const size_t lds_tk = (size_t)nt * k * (sizeof(float) + sizeof(int64_t));
-  e = hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_tk);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel, dim3(Q), dim3(kThreads), lds_tk, s, a, nt);
+  hipLaunchKernelGGL(topk2_kernel, dim3(Q), dim3(64 * kTk2Waves), 0, s, a.scores, N, k, out_idx, out_score);
   return hipGetLastError();
 }
 

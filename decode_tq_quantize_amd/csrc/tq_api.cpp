@@ -171,7 +171,8 @@ extern "C" int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const vo
 }
 
 extern "C" size_t tq_search_workspace_bytes(const tq_group* db, int64_t N, int Q, int k) {
-  if (!db || check_quantizer(&db->q) != TQ_OK || N < 1 || Q < 1 || k < 1 || k > 64 || k > N) return 0;
+  if (!db || check_quantizer(&db->q) != TQ_OK || N < 1 || N >= ((int64_t)1 << 29) || Q < 1 || k < 1 || k > 64 || k > N)
+    return 0;
   return tqk::search_workspace_bytes(*db, N, Q, k);
 }
 
@@ -181,7 +182,7 @@ extern "C" int tq_search_topk(const tq_group* db, int64_t N, const float* querie
   int rc = check_quantizer(&db->q);
   if (rc != TQ_OK) return rc;
   if (!symmetric(db->q)) return TQ_ERR_INVALID_ARG;
-  if (N < 1 || Q < 1 || k < 1 || k > 64 || k > N) return TQ_ERR_INVALID_ARG;
+  if (N < 1 || N >= ((int64_t)1 << 29) || Q < 1 || k < 1 || k > 64 || k > N) return TQ_ERR_INVALID_ARG;
   if (!db->packed || !db->norm || (db->q.variant == TQ_PROD && !db->rnorm) || !queries || !out_idx || !out_score)
     return TQ_ERR_INVALID_ARG;
   if (!aligned16(db->packed) || !aligned16(db->norm) || (db->rnorm && !aligned16(db->rnorm)) ||

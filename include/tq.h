@@ -195,7 +195,8 @@ size_t tq_search_workspace_bytes(const tq_group* db, int64_t N, int Q, int k);
 
 /* Top-k database vectors by estimated inner product with each query
  * (uiyeonassociation post: TurboQuant codes used for vector search).
- *   db        one group, TQ_LAYOUT_KEYS, seq_stride ignored (vectors 0..N-1)
+ *   db        one group, TQ_LAYOUT_KEYS, seq_stride ignored (vectors
+ *             0..N-1, 1 <= N < 2^29)
  *   queries   [Q, d] fp32 device
  *   out_idx   [Q, k] int64, out_score [Q, k] fp32: descending score, equal
  *             scores in ascending index order. 1 <= k <= 64, k <= N.

@@ -202,6 +202,8 @@ def test_search_validation_paths():
     assert call(k=0) == tq.TQ_ERR_INVALID_ARG
     assert call(k=65) == tq.TQ_ERR_INVALID_ARG
     assert call(N=5) == tq.TQ_ERR_INVALID_ARG
+    assert call(N=1 << 29) == tq.TQ_ERR_INVALID_ARG
+    assert tq.tq_search_workspace_bytes(db, 1 << 29, 4, 10) == 0
     assert call(wsb=ws - 8) == tq.TQ_ERR_WORKSPACE
     assert call(qp=None) == tq.TQ_ERR_INVALID_ARG
     assert tq.tq_search_workspace_bytes(db, 1000, 4, 0) == 0

@@ -335,7 +335,7 @@ def test_fold_matches_matrix_product(d):
 # search
 # --------------------------------------------------------------------------
 
-def run_search(gq, packed, norm, rnorm, N, queries, k):
+def run_search(gq, packed, norm, rnorm, N, queries, k, want_ws=False):
     db = tq.make_group(gq.q, 0, packed, norm, rnorm, 0)
     Q = queries.shape[0]
     ws_bytes = tq.tq_search_workspace_bytes(db, N, Q, k)
@@ -344,6 +344,8 @@ def run_search(gq, packed, norm, rnorm, N, queries, k):
     osc = torch.empty((Q, k), dtype=torch.float32, device="cuda")
     tq.tq_search_topk(db, N, torch_dev(queries.astype(np.float32)), Q, k, oi, osc, ws, ws_bytes)
     torch.cuda.synchronize()
+    if want_ws:
+        return oi.cpu().numpy(), osc.cpu().numpy(), ws.cpu().numpy()
     return oi.cpu().numpy(), osc.cpu().numpy()
 
 
@@ -375,3 +377,32 @@ def test_search_on_gpu_quantized_db_d1536():
     # recall against exact inner products is reported, not pinned
     truth, _ = otq.exact_topk(qs, db, k)
     print("recall@10", otq.recall_at_k(gi, truth))
+
+
+@pytest.mark.parametrize("k", [1, 10, 64])
+def test_search_topk_selects_exactly_from_the_score_rows(k):
+    # The selection is exact on the fp32 scores the scan produced (the
+    # workspace holds them as [Q, N] after the [Q, 2 d] query transforms):
+    # the same indices in the same order, equal scores by ascending index.
+    # Every database vector appears about ten times, so the rows are full of
+    # exact ties; N = 50001 leaves rows that start off a 16-byte boundary and
+    # gives each wave of the selection several chunks.
+    d, B, N, Q = 128, 3, 50001, 7
+    print(f"topk selection k={k} N={N}", flush=True)
+    gq = GpuQuantizer(d, B, True, seed=11)
+    base, means = synth.gaussian_mixture(5000, d, 16, seed=11)
+    pick = synth.rng(11, synth.STREAM_QUERY + 7).integers(0, 5000, size=N)
+    db = base[pick]
+    qs, _ = synth.gaussian_mixture(Q, d, 16, seed=12, stream=synth.STREAM_QUERY, means=means)
+    packed, norm, rnorm = gpu_quantize(gq, torch_dev(db), N, d, tq.TQ_LAYOUT_KEYS, tq.TQ_F32)
+    torch.cuda.synchronize()
+    gi, gs, ws = run_search(gq, packed, norm, rnorm, N, qs, k, want_ws=True)
+    sc = ws[Q * 2 * d:Q * 2 * d + Q * N].reshape(Q, N)
+    ties = 0
+    for i in range(Q):
+        order = np.lexsort((np.arange(N), -sc[i].astype(np.float64)))[:k]
+        assert np.array_equal(gi[i], order), (i, gi[i], order)
+        assert np.array_equal(gs[i], sc[i][order])
+        ties += int(np.sum(sc[i][order][1:] == sc[i][order][:-1]))
+    if k > 1:
+        assert ties > 0  # the case the index order decides was exercised
