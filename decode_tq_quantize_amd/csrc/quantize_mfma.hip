@@ -46,16 +46,20 @@ struct QmArgs {
 // The two 32-bit halves of a wave ballot `m` go to lane l0 of `a` and lane
 // l1 of `b` (v_writelane; l0 and l1 fold to constants in the unrolled loops
 // that call this). A VALU write of an SGPR is not visible to v_writelane's
-// data operand one instruction later (measured: the value read is stale),
-// so the writes wait first.
+// data operand one instruction later (measured: the value read is stale).
+// The halves are first copied by scalar moves (a scalar read of a
+// VALU-written SGPR waits in hardware), so the lane writes read values
+// written by the scalar unit.
 __device__ __forceinline__ void ballot_to_lanes(uint32_t& a, uint32_t& b, uint64_t m, int l0, int l1) {
-  asm("s_nop 4\n\tv_writelane_b32 %0, %2, %4\n\tv_writelane_b32 %1, %3, %5"
-      : "+v"(a), "+v"(b)
+  uint32_t t0, t1;
+  asm("s_mov_b32 %2, %4\n\ts_mov_b32 %3, %5\n\tv_writelane_b32 %0, %2, %6\n\tv_writelane_b32 %1, %3, %7"
+      : "+v"(a), "+v"(b), "=&s"(t0), "=&s"(t1)
       : "s"((uint32_t)m), "s"((uint32_t)(m >> 32)), "i"(l0), "i"(l1));
 }
 __device__ __forceinline__ void ballot_to_lanes(uint32_t& a, uint64_t m, int l0, int l1) {
-  asm("s_nop 4\n\tv_writelane_b32 %0, %1, %3\n\tv_writelane_b32 %0, %2, %4"
-      : "+v"(a)
+  uint32_t t0, t1;
+  asm("s_mov_b32 %1, %3\n\ts_mov_b32 %2, %4\n\tv_writelane_b32 %0, %1, %5\n\tv_writelane_b32 %0, %2, %6"
+      : "+v"(a), "=&s"(t0), "=&s"(t1)
       : "s"((uint32_t)m), "s"((uint32_t)(m >> 32)), "i"(l0), "i"(l1));
 }
 
@@ -130,6 +134,41 @@ __device__ __forceinline__ float sum_q(float v) {
   return v;
 }
 
+// Threshold th[LO + k STRIDE], k = 0 .. N - 1, chosen by the bits found so
+// far (bits[0] the most significant): a tree of N - 1 selects over values
+// (constant indices only, so the thresholds stay in registers).
+template <int N, int LO, int STRIDE, int NT>
+__device__ __forceinline__ float pick(const float (&th)[NT], const bool* bits) {
+  if constexpr (N == 1) {
+    return th[LO];
+  } else {
+    const float hi = pick<N / 2, LO + (N / 2) * STRIDE, STRIDE>(th, bits + 1);
+    const float lo = pick<N / 2, LO, STRIDE>(th, bits + 1);
+    return bits[0] ? hi : lo;
+  }
+}
+
+// Bit j of the interval index and the bits below it: the compare against
+// the middle threshold th[k 2^(j+1) + 2^j - 1] of the interval k that the
+// higher bits (bits[0 .. B-2-j]) leave.
+template <int B, int J>
+__device__ __forceinline__ void interval_bits(float u, const float (&th)[(1 << B) - 1], bool (&bits)[B]) {
+  bits[B - 1 - J] = u >= pick<(1 << (B - 1 - J)), (1 << J) - 1, (2 << J)>(th, bits);
+  if constexpr (J > 0) interval_bits<B, J - 1>(u, th, bits);
+}
+
+// Interval index #{t : u >= th[t]} of the sorted thresholds by binary
+// search (B compares instead of 2^B - 1).
+template <int B>
+__device__ __forceinline__ int interval(float u, const float (&th)[(1 << B) - 1]) {
+  bool bits[B];
+  interval_bits<B, B - 1>(u, th, bits);
+  int idx = 0;
+#pragma unroll
+  for (int j = 0; j < B; ++j) idx |= bits[j] ? (1 << (B - 1 - j)) : 0;
+  return idx;
+}
+
 template <bool BF16IN, int B, bool PROD>
 __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
   // The QJL projection S r~ runs on the bf16 matrix cores with both operands
@@ -154,7 +193,10 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
   // thresholds as uniform values (the compares below are unrolled)
   float th[L - 1];
 #pragma unroll
-  for (int t = 0; t < L - 1; ++t) th[t] = a.thr[t];
+  for (int t = 0; t < L - 1; ++t) {
+    th[t] = a.thr[t];
+    asm volatile("" : "+v"(th[t]));  // held in a VGPR: the selects below take one SGPR operand at most
+  }
 
   // R as A operands: fp32 (fp32 input), or bf16 high and low parts (bf16
   // input, which is exact in bf16: R x = R_hi x + R_lo x, |R - R_hi - R_lo|
@@ -212,34 +254,34 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         const int64_t vn = (nt == 0 ? v0 + 16 : v0 + (int64_t)gridDim.x * kTile) + nl;
         load_in(xin, a, min(vn, a.n - 1), q);
       }
-      float s2 = 0.f;
+      float nrm;
       v4f acc[2];
       if constexpr (BF16IN) {
         const uint4(&xw)[4] = cur.w;
-        v4f ah[2][2], al[2][2];
+        v4f ah[2], al[2], gram = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int c = 0; c < 2; ++c) ah[m][c] = al[m][c] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 2; ++m) ah[m] = al[m] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const bf16x8 xb = __builtin_bit_cast(bf16x8, xw[kk]);
-          const uint32_t wd[4] = {xw[kk].x, xw[kk].y, xw[kk].z, xw[kk].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float lo = __uint_as_float(wd[e] << 16), hi = __uint_as_float(wd[e] & 0xffff0000u);
-            s2 = fmaf(lo, lo, s2);
-            s2 = fmaf(hi, hi, s2);
-          }
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            ah[m][kk & 1] = mfma_bf16(RH[m][kk], xb, ah[m][kk & 1]);
-            al[m][kk & 1] = mfma_bf16(RL[m][kk], xb, al[m][kk & 1]);
+            ah[m] = mfma_bf16(RH[m][kk], xb, ah[m]);
+            al[m] = mfma_bf16(RL[m][kk], xb, al[m]);
           }
+          // the 16 vectors' Gram matrix: the same register is the A operand
+          // (row = vector) and the B operand (column = vector); products of
+          // bf16 values are exact in the fp32 accumulation
+          gram = mfma_bf16(xb, xb, gram);
         }
 #pragma unroll
-        for (int m = 0; m < 2; ++m) acc[m] = (ah[m][0] + ah[m][1]) + (al[m][0] + al[m][1]);
+        for (int m = 0; m < 2; ++m) acc[m] = ah[m] + al[m];
+        // |x|^2 of vector nl is the diagonal entry (nl, nl), held by lane
+        // 16 (nl / 4) + nl as its element nl % 4
+        const float dsel = (nl & 2) ? ((nl & 1) ? gram[3] : gram[2]) : ((nl & 1) ? gram[1] : gram[0]);
+        nrm = sqrtf(__shfl(dsel, 16 * (nl >> 2) + nl, 64));
       } else {
+        float s2 = 0.f;
         float x[32];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -262,8 +304,8 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) acc[m] = (ac[m][0] + ac[m][1]) + (ac[m][2] + ac[m][3]);
+        nrm = sqrtf(sum_q(s2));
       }
-      const float nrm = sqrtf(sum_q(s2));
       // codes and residual of coordinates 32 w + 16 m + 4 q + r of vector nl
       const bool live = valid && nrm > 0.f;
       const float inv = live ? 1.f / nrm : 0.f;
@@ -275,9 +317,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float u = acc[m][r] * inv;
-          int idx = 0;
-#pragma unroll
-          for (int t = 0; t < L - 1; ++t) idx += u >= th[t] ? 1 : 0;
+          int idx = interval<B>(u, th);
           if (!live) idx = L / 2;
           const float rr = live ? u - cent[idx] : 0.f;
           cb[m][r] = (uint32_t)idx;
