@@ -43,24 +43,21 @@ struct QmArgs {
   uint16_t* rnorm;
 };
 
-// The two 32-bit halves of a wave ballot `m` go to lane l0 of `a` and lane
-// l1 of `b` (v_writelane; l0 and l1 fold to constants in the unrolled loops
-// that call this). A VALU write of an SGPR is not visible to v_writelane's
-// data operand one instruction later (measured: the value read is stale).
-// The halves are first copied by scalar moves (a scalar read of a
-// VALU-written SGPR waits in hardware), so the lane writes read values
-// written by the scalar unit.
-__device__ __forceinline__ void ballot_to_lanes(uint32_t& a, uint32_t& b, uint64_t m, int l0, int l1) {
+// Words of two 16-bit halves to lanes: lane l0 of `a` gets the low halves
+// of x (low) and y (high), lane l1 of `b` their high halves. The packs run
+// on the scalar unit, whose reads of VALU-written SGPRs wait in hardware.
+__device__ __forceinline__ void halves_to_lanes(uint32_t& a, uint32_t& b, uint32_t x, uint32_t y, int l0, int l1) {
   uint32_t t0, t1;
-  asm("s_mov_b32 %2, %4\n\ts_mov_b32 %3, %5\n\tv_writelane_b32 %0, %2, %6\n\tv_writelane_b32 %1, %3, %7"
+  asm("s_pack_ll_b32_b16 %2, %4, %5\n\ts_pack_hh_b32_b16 %3, %4, %5\n\tv_writelane_b32 %0, %2, %6\n\tv_writelane_b32 %1, %3, %7"
       : "+v"(a), "+v"(b), "=&s"(t0), "=&s"(t1)
-      : "s"((uint32_t)m), "s"((uint32_t)(m >> 32)), "i"(l0), "i"(l1));
+      : "s"(x), "s"(y), "i"(l0), "i"(l1));
 }
-__device__ __forceinline__ void ballot_to_lanes(uint32_t& a, uint64_t m, int l0, int l1) {
+// The same with both lanes in one register.
+__device__ __forceinline__ void halves_to_lanes(uint32_t& a, uint32_t x, uint32_t y, int l0, int l1) {
   uint32_t t0, t1;
-  asm("s_mov_b32 %1, %3\n\ts_mov_b32 %2, %4\n\tv_writelane_b32 %0, %1, %5\n\tv_writelane_b32 %0, %2, %6"
+  asm("s_pack_ll_b32_b16 %1, %3, %4\n\ts_pack_hh_b32_b16 %2, %3, %4\n\tv_writelane_b32 %0, %1, %5\n\tv_writelane_b32 %0, %2, %6"
       : "+v"(a), "=&s"(t0), "=&s"(t1)
-      : "s"((uint32_t)m), "s"((uint32_t)(m >> 32)), "i"(l0), "i"(l1));
+      : "s"(x), "s"(y), "i"(l0), "i"(l1));
 }
 
 __device__ __forceinline__ v4f mfma_f32(float a, float b, v4f c) {
@@ -169,7 +166,7 @@ __device__ __forceinline__ int interval(float u, const float (&th)[(1 << B) - 1]
   return idx;
 }
 
-template <bool BF16IN, int B, bool PROD>
+template <bool BF16IN, int B, bool PROD, bool KEYS>
 __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
   // The QJL projection S r~ runs on the bf16 matrix cores with both operands
   // split into bf16 high and low parts: S r~ = S_hi r_hi + S_hi r_lo +
@@ -179,12 +176,8 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
   // row r is stored at c ^ (r % 16), so that the 16 rows read at once hit
   // different banks.
   __shared__ uint4 Sq[2][PROD ? kD : 1][kD / 8];
-  __shared__ uint4 rq[2][16][kD / 8];
-  // rows padded by one dword: the value layout reads a column (one vector
-  // per lane), which would otherwise fall into one LDS bank
-  __shared__ uint8_t codes[kTile][kD + 4];  // idx | z << 4, [vector][coordinate]
+  __shared__ uint4 rq[2][PROD ? 16 : 1][kD / 8];
   __shared__ float rho_part[4][kTile];
-  __shared__ float cent[TQ_MAX_LEVELS], thr[TQ_MAX_LEVELS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, nl = lane & 15;
@@ -232,32 +225,36 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
       Sq[1][row][c ^ (row & 15)] = make_uint4(l[0], l[1], l[2], l[3]);
     }
   }
-  if (tid < TQ_MAX_LEVELS) {
-    cent[tid] = a.cent[tid];
-    thr[tid] = tid < TQ_MAX_LEVELS - 1 ? a.thr[tid] : 0.f;
+  // centroids as values (the residual picks one by the index bits)
+  float cv[L];
+#pragma unroll
+  for (int t = 0; t < L; ++t) {
+    cv[t] = a.cent[t];
+    asm volatile("" : "+v"(cv[t]));
   }
   __syncthreads();
 
-  // the input of the next sub-tile is always in flight while one is
-  // processed (rows past n re-read row n - 1 and are masked)
-  XIn<BF16IN> xin;
-  load_in(xin, a, min((int64_t)blockIdx.x * kTile + nl, a.n - 1), q);
+  // the inputs of the next tile are in flight while one is processed (rows
+  // past n re-read row n - 1 and are masked)
+  XIn<BF16IN> xin[2];
+  auto load_tile = [&](int64_t t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) load_in(xin[nt], a, min(t * kTile + 16 * nt + nl, a.n - 1), q);
+  };
+  load_tile(blockIdx.x);
+  const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int64_t v0 = tile * kTile;
-    float nrm0 = 0.f, nrm1 = 0.f;  // norms of sub-tiles 0 and 1 (registers, not an indexed array)
-#pragma unroll 1
+    XIn<BF16IN> cur[2] = {xin[0], xin[1]};
+    load_tile(tile + gridDim.x);
+    // 1. rotated coordinates 32 w + 16 m + 4 q + r of vector 16 nt + nl, and
+    // the vector norms
+    v4f acc[2][2];
+    float nrm[2];
+#pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int64_t v = v0 + 16 * nt + nl;
-      const bool valid = v < a.n;
-      const XIn<BF16IN> cur = xin;
-      {
-        const int64_t vn = (nt == 0 ? v0 + 16 : v0 + (int64_t)gridDim.x * kTile) + nl;
-        load_in(xin, a, min(vn, a.n - 1), q);
-      }
-      float nrm;
-      v4f acc[2];
       if constexpr (BF16IN) {
-        const uint4(&xw)[4] = cur.w;
+        const uint4(&xw)[4] = cur[nt].w;
         v4f ah[2], al[2], gram = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 2; ++m) ah[m] = al[m] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -275,20 +272,20 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
           gram = mfma_bf16(xb, xb, gram);
         }
 #pragma unroll
-        for (int m = 0; m < 2; ++m) acc[m] = ah[m] + al[m];
+        for (int m = 0; m < 2; ++m) acc[nt][m] = ah[m] + al[m];
         // |x|^2 of vector nl is the diagonal entry (nl, nl), held by lane
         // 16 (nl / 4) + nl as its element nl % 4
         const float dsel = (nl & 2) ? ((nl & 1) ? gram[3] : gram[2]) : ((nl & 1) ? gram[1] : gram[0]);
-        nrm = sqrtf(__shfl(dsel, 16 * (nl >> 2) + nl, 64));
+        nrm[nt] = sqrtf(__shfl(dsel, 16 * (nl >> 2) + nl, 64));
       } else {
         float s2 = 0.f;
         float x[32];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          x[4 * k] = cur.f[k].x;
-          x[4 * k + 1] = cur.f[k].y;
-          x[4 * k + 2] = cur.f[k].z;
-          x[4 * k + 3] = cur.f[k].w;
+          x[4 * k] = cur[nt].f[k].x;
+          x[4 * k + 1] = cur[nt].f[k].y;
+          x[4 * k + 2] = cur[nt].f[k].z;
+          x[4 * k + 3] = cur[nt].f[k].w;
         }
 #pragma unroll
         for (int k = 0; k < 32; ++k) s2 = fmaf(x[k], x[k], s2);
@@ -303,37 +300,123 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
           ac[1][kk & 3] = mfma_f32(AR[1][kk], x[kk], ac[1][kk & 3]);
         }
 #pragma unroll
-        for (int m = 0; m < 2; ++m) acc[m] = (ac[m][0] + ac[m][1]) + (ac[m][2] + ac[m][3]);
-        nrm = sqrtf(sum_q(s2));
+        for (int m = 0; m < 2; ++m) acc[nt][m] = (ac[m][0] + ac[m][1]) + (ac[m][2] + ac[m][3]);
+        nrm[nt] = sqrtf(sum_q(s2));
       }
-      // codes and residual of coordinates 32 w + 16 m + 4 q + r of vector nl
-      const bool live = valid && nrm > 0.f;
-      const float inv = live ? 1.f / nrm : 0.f;
-      uint32_t cb[2][4];
-      float res[2][4];
-      float r2 = 0.f;
+    }
+    // 2. code bits (index bits by binary search, most significant first),
+    // residuals and their norms. A vector of norm 0 gets index L / 2 and
+    // residual 0; padding vectors keep all-zero bits. Wave ballots of the
+    // bits have bit 16 q + nl = coordinate 32 w + 16 m + 4 q + r of vector
+    // 16 nt + nl.
+    bool valid[2], live[2];
+    float inv[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      valid[nt] = v0 + 16 * nt + nl < a.n;
+      live[nt] = valid[nt] && nrm[nt] > 0.f;
+      inv[nt] = live[nt] ? 1.f / nrm[nt] : 0.f;
+      if (w == 0 && q == 0 && valid[nt]) a.norm[v0 + 16 * nt + nl] = tqd::f32_to_half_bits(nrm[nt]);
+    }
+    float res[2][2][4];
+    float r2[2] = {0.f, 0.f};
+    // index plane p (bit B - 1 - p of the search order) of one coordinate
+    auto code = [&](int nt, int m, int r, bool (&pl)[B]) __attribute__((always_inline)) {
+      const float u = acc[nt][m][r] * inv[nt];
+      bool bt[B];
+      interval_bits<B, B - 1>(u, th, bt);
+      if constexpr (PROD) {
+        const float rr = live[nt] ? u - pick<L, 0, 1>(cv, bt) : 0.f;
+        res[nt][m][r] = rr;
+        r2[nt] = fmaf(rr, rr, r2[nt]);
+      }
+#pragma unroll
+      for (int p = 0; p < B; ++p) pl[p] = valid[nt] && (live[nt] ? bt[B - 1 - p] : p == B - 1);
+    };
+    // word (vector t of key tile nt, group w, plane p) of the key layout:
+    // bit i = coordinate 32 w + i. Each lane sets the bits of its 8
+    // coordinates and the 4 lanes of a vector combine theirs.
+    uint32_t kw[2][P];
+    auto key_word = [&](const bool (&b)[2][4]) __attribute__((always_inline)) -> uint32_t {
+      uint32_t nib[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        nib[m] = 0u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) nib[m] |= b[m][r] ? (1u << r) : 0u;
+      }
+      uint32_t wp = (nib[0] | (nib[1] << 16)) << (4 * q);
+      wp |= __shfl_xor(wp, 16, 64);
+      wp |= __shfl_xor(wp, 32, 64);
+      return wp;
+    };
+    // words (coordinate j, plane p) of the value layout: bit i = vector
+    // v0 + i; the wave's coordinates are 32 P contiguous words, word
+    // (j - 32 w) P + p, held by lane (word % 64) of ow[word / 64]. Bits
+    // 16 q .. 16 q + 15 of the two halves' ballots are the low and high
+    // halves of the word of coordinate 32 w + 16 m + 4 q + r.
+    constexpr int NW = (32 * P + 63) / 64;
+    uint32_t ow[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) ow[i] = 0u;
+    auto value_words = [&](int m, int r, int p, bool b0, bool b1) __attribute__((always_inline)) {
+      const uint64_t m0 = __builtin_amdgcn_ballot_w64(b0), m1 = __builtin_amdgcn_ballot_w64(b1);
+      const int i = (16 * m + r) * P + p;  // + 4 q P for lane group q
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // lane groups 2 h and 2 h + 1
+        const int i0 = i + 8 * h * P, i1 = i0 + 4 * P;
+        const uint32_t x = (uint32_t)(m0 >> (32 * h)), y = (uint32_t)(m1 >> (32 * h));
+        if ((i0 >> 6) == (i1 >> 6))
+          halves_to_lanes(ow[i0 >> 6], x, y, i0 & 63, i1 & 63);
+        else
+          halves_to_lanes(ow[i0 >> 6], ow[i1 >> 6], x, y, i0 & 63, i1 & 63);
+      }
+    };
+    if constexpr (KEYS) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        bool pb[B][2][4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            bool pl[B];
+            code(nt, m, r, pl);
+#pragma unroll
+            for (int p = 0; p < B; ++p) pb[p][m][r] = pl[p];
+          }
+#pragma unroll
+        for (int p = 0; p < B; ++p) kw[nt][p] = key_word(pb[p]);
+      }
+    } else {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float u = acc[m][r] * inv;
-          int idx = interval<B>(u, th);
-          if (!live) idx = L / 2;
-          const float rr = live ? u - cent[idx] : 0.f;
-          cb[m][r] = (uint32_t)idx;
-          res[m][r] = rr;
-          r2 = fmaf(rr, rr, r2);
+          bool pl0[B], pl1[B];
+          code(0, m, r, pl0);
+          code(1, m, r, pl1);
+#pragma unroll
+          for (int p = 0; p < B; ++p) value_words(m, r, p, pl0[p], pl1[p]);
         }
-      if (PROD) {
-        r2 = sum_q(r2);
-        if (q == 0) rho_part[w][16 * nt + nl] = r2;
+    }
+    // 3. QJL signs: S r~ on the matrix cores, one 16-vector half at a time
+    if constexpr (PROD) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float rs = sum_q(r2[nt]);
+        if (q == 0) rho_part[w][16 * nt + nl] = rs;
+      }
+      bool zb[2][2][4];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
         // residual coordinates 32 w + 16 m + 4 q .. + 3 of vector nl: half of
         // chunk (4 w + 2 m + q / 2) of the vector's row
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           uint32_t h0, l0, h1, l1;
-          split_bf16(res[m][0], res[m][1], h0, l0);
-          split_bf16(res[m][2], res[m][3], h1, l1);
+          split_bf16(res[nt][m][0], res[nt][m][1], h0, l0);
+          split_bf16(res[nt][m][2], res[nt][m][3], h1, l1);
           const int c = (4 * w + 2 * m + (q >> 1)) ^ nl, half = q & 1;
           reinterpret_cast<uint2*>(&rq[0][nl][c])[half] = make_uint2(h0, h1);
           reinterpret_cast<uint2*>(&rq[1][nl][c])[half] = make_uint2(l0, l1);
@@ -353,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
           const bf16x8 rl = __builtin_bit_cast(bf16x8, rq[1][nl][ph]);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            const int row = PROD ? 32 * w + 16 * m + nl : 0;  // row % 16 == nl
+            const int row = 32 * w + 16 * m + nl;  // row % 16 == nl
             const bf16x8 sh = __builtin_bit_cast(bf16x8, Sq[0][row][ph]);
             const bf16x8 sl = __builtin_bit_cast(bf16x8, Sq[1][row][ph]);
             pc[m][0] = mfma_bf16(sh, rh, pc[m][0]);
@@ -361,104 +444,56 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
             pc[m][2] = mfma_bf16(sl, rh, pc[m][2]);
           }
         }
-        v4f pj[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) pj[m] = pc[m][0] + (pc[m][1] + pc[m][2]);
+        for (int m = 0; m < 2; ++m) {
+          const v4f pj = pc[m][0] + (pc[m][1] + pc[m][2]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) zb[nt][m][r] = valid[nt] && (pj[r] >= 0.f || !live[nt]);
+        }
+        if constexpr (KEYS) kw[nt][B] = key_word(zb[nt]);
+        __syncthreads();  // rq is rewritten by the next half
+      }
+      if constexpr (!KEYS) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (pj[m][r] >= 0.f || !live) cb[m][r] |= 16u;
+          for (int r = 0; r < 4; ++r) value_words(m, r, B, zb[0][m][r], zb[1][m][r]);
       }
-      // padding vectors keep all-zero bits
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          codes[16 * nt + nl][32 * w + 16 * m + 4 * q + r] = valid ? (uint8_t)cb[m][r] : (uint8_t)0;
-      if (nt == 0)
-        nrm0 = nrm;
-      else
-        nrm1 = nrm;
-      if (PROD) __syncthreads();  // rt is rewritten by the next sub-tile
-    }
-    __syncthreads();
-    // norms (one lane per vector)
-    if (w == 0 && q < 2) {
-      const int vt = 16 * q + nl;
-      const int64_t v = v0 + vt;
-      if (v < a.n) {
-        a.norm[v] = tqd::f32_to_half_bits(q == 0 ? nrm0 : nrm1);
-        if (PROD) {
+      // residual norms (one lane per vector)
+      if (w == 0 && q < 2) {
+        const int vt = 16 * q + nl;
+        if (v0 + vt < a.n) {
           const float rho = sqrtf((rho_part[0][vt] + rho_part[1][vt]) + (rho_part[2][vt] + rho_part[3][vt]));
-          a.rnorm[v] = tqd::f32_to_half_bits(rho);
+          a.rnorm[v0 + vt] = tqd::f32_to_half_bits(rho);
         }
       }
     }
-    // pack: wave w packs coordinate group w. One ballot covers 2 x 32 bits
-    // (lanes 0..31 and 32..63 read two different rows); its two halves are
-    // uniform values, placed with v_writelane into the lanes of a word
-    // buffer whose lane l holds the l-th word of the wave's contiguous output
-    // run, which is then stored coalesced.
-    const int hi = lane >> 5, l32 = lane & 31;
-    if (a.layout == TQ_LAYOUT_KEYS) {
-      // words (vector t of key tile kb, group w, plane p): bit i = coordinate
-      // 32 w + i; the wave's words of key tile kb are 16 P contiguous words
-      constexpr int NW = (16 * P + 63) / 64;
-      uint32_t ow[2][NW];
+    // 4. stores
+    if constexpr (KEYS) {
+      // lane (q, nl) stores plane q (and q + 4) of vector nl; the wave's
+      // words of a key tile are 16 P contiguous words, word nl P + p
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int nt = 0; nt < 2; ++nt) {
+        if (v0 + 16 * nt < nround) {
+          const int64_t kt = (v0 >> 4) + nt;
+          uint32_t* dst = a.packed + (kt * (kD / 32) + w) * tqk::kKeysTile * P;
 #pragma unroll
-        for (int r = 0; r < NW; ++r) ow[kb][r] = 0u;
+          for (int pass = 0; pass < (P + 3) / 4; ++pass) {
+            const int p = 4 * pass + q;
+            uint32_t wv = kw[nt][4 * pass];
 #pragma unroll
-      for (int vp = 0; vp < kTile; vp += 2) {
-        const uint32_t c = codes[vp + hi][32 * w + l32];
-#pragma unroll
-        for (int pp = 0; pp < P; ++pp) {
-          const uint64_t m = __ballot((c >> (pp < B ? pp : 4)) & 1u);
-          const int kb = vp >> 4, i0 = (vp & 15) * P + pp, i1 = i0 + P;
-          if ((i0 >> 6) == (i1 >> 6))
-            ballot_to_lanes(ow[kb][i0 >> 6], m, i0 & 63, i1 & 63);
-          else
-            ballot_to_lanes(ow[kb][i0 >> 6], ow[kb][i1 >> 6], m, i0 & 63, i1 & 63);
+            for (int pp = 4 * pass + 1; pp < P && pp < 4 * pass + 4; ++pp) wv = (p == pp) ? kw[nt][pp] : wv;
+            if (p < P) dst[nl * P + p] = wv;
+          }
         }
-      }
-      const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (v0 + 16 * kb >= nround) break;
-        const int64_t kt = (v0 >> 4) + kb;
-        uint32_t* dst = a.packed + (kt * (kD / 32) + w) * tqk::kKeysTile * P;
-#pragma unroll
-        for (int r = 0; r < NW; ++r)
-          if (64 * r + lane < 16 * P) dst[64 * r + lane] = ow[kb][r];
       }
     } else {
-      // word (coordinate j, plane p): bit i = vector v0 + i; the wave's
-      // coordinates 32 w .. 32 w + 31 are 32 P contiguous words
-      constexpr int NW = (32 * P + 63) / 64;
-      uint32_t ow[NW];
-#pragma unroll
-      for (int r = 0; r < NW; ++r) ow[r] = 0u;
-#pragma unroll
-      for (int jp = 0; jp < 32; jp += 2) {
-        const uint32_t c = codes[l32][32 * w + jp + hi];
-#pragma unroll
-        for (int pp = 0; pp < P; ++pp) {
-          const uint64_t m = __ballot((c >> (pp < B ? pp : 4)) & 1u);
-          const int i0 = jp * P + pp, i1 = i0 + P;
-          if ((i0 >> 6) == (i1 >> 6))
-            ballot_to_lanes(ow[i0 >> 6], m, i0 & 63, i1 & 63);
-          else
-            ballot_to_lanes(ow[i0 >> 6], ow[i1 >> 6], m, i0 & 63, i1 & 63);
-        }
-      }
       uint32_t* dst = a.packed + (tile * kD + 32 * w) * P;
 #pragma unroll
-      for (int r = 0; r < NW; ++r)
-        if (64 * r + lane < 32 * P) dst[64 * r + lane] = ow[r];
+      for (int i = 0; i < NW; ++i)
+        if (64 * i + lane < 32 * P) dst[64 * i + lane] = ow[i];
     }
-    __syncthreads();  // codes / rho_part are rewritten by the next tile
+    if constexpr (PROD) __syncthreads();  // rho_part is rewritten by the next tile
   }
 }
 
@@ -490,17 +525,13 @@ hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtyp
   a.norm = norm;
   a.rnorm = rnorm;
   using Fn = void (*)(QmArgs);
-  // [bf16 input][mse bits - 1][prod]
-  static const Fn fns[2][4][2] = {
-      {{quantize_mfma_kernel<false, 1, false>, quantize_mfma_kernel<false, 1, true>},
-       {quantize_mfma_kernel<false, 2, false>, quantize_mfma_kernel<false, 2, true>},
-       {quantize_mfma_kernel<false, 3, false>, quantize_mfma_kernel<false, 3, true>},
-       {quantize_mfma_kernel<false, 4, false>, quantize_mfma_kernel<false, 4, true>}},
-      {{quantize_mfma_kernel<true, 1, false>, quantize_mfma_kernel<true, 1, true>},
-       {quantize_mfma_kernel<true, 2, false>, quantize_mfma_kernel<true, 2, true>},
-       {quantize_mfma_kernel<true, 3, false>, quantize_mfma_kernel<true, 3, true>},
-       {quantize_mfma_kernel<true, 4, false>, quantize_mfma_kernel<true, 4, true>}}};
-  const Fn fn = fns[a.bf16 ? 1 : 0][a.B - 1][a.prod ? 1 : 0];
+  // [bf16 input][mse bits - 1][prod][keys layout]
+#define TQ_QM(BF, B) {{quantize_mfma_kernel<BF, B, false, false>, quantize_mfma_kernel<BF, B, false, true>}, \
+                      {quantize_mfma_kernel<BF, B, true, false>, quantize_mfma_kernel<BF, B, true, true>}}
+  static const Fn fns[2][4][2][2] = {{TQ_QM(false, 1), TQ_QM(false, 2), TQ_QM(false, 3), TQ_QM(false, 4)},
+                                     {TQ_QM(true, 1), TQ_QM(true, 2), TQ_QM(true, 3), TQ_QM(true, 4)}};
+#undef TQ_QM
+  const Fn fn = fns[a.bf16 ? 1 : 0][a.B - 1][a.prod ? 1 : 0][layout == TQ_LAYOUT_KEYS ? 1 : 0];
   // persistent grid: as many workgroups as the device holds at once (the
   // rotation-only kernels need far fewer registers and no S in LDS)
   int dev = 0, cus = 0, per_cu = 0;

@@ -73,6 +73,11 @@ QUANT_CASES = [
     (128, 3, True, "keys", 1000, "bf16"),
     (128, 2, True, "keys", 37, "f32"),
     (128, 3, False, "values", 1000, "bf16"),
+    (128, 4, True, "keys", 333, "bf16"),
+    (128, 2, True, "values", 100, "bf16"),
+    (128, 1, True, "values", 70, "f32"),
+    (128, 4, False, "values", 129, "f32"),
+    (128, 1, False, "keys", 45, "bf16"),
     (32, 2, True, "keys", 100, "f32"),
     (96, 1, True, "keys", 100, "bf16"),
     (96, 2, False, "values", 77, "f32"),
