@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         // |x|^2 of vector nl is the diagonal entry (nl, nl), held by lane
         // 16 (nl / 4) + nl as its element nl % 4
         const float dsel = (nl & 2) ? ((nl & 1) ? gram[3] : gram[2]) : ((nl & 1) ? gram[1] : gram[0]);
-        nrm[nt] = sqrtf(__shfl(dsel, 16 * (nl >> 2) + nl, 64));
+        nrm[nt] = __builtin_amdgcn_sqrtf(__shfl(dsel, 16 * (nl >> 2) + nl, 64));
       } else {
         float s2 = 0.f;
         float x[32];
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) acc[nt][m] = (ac[m][0] + ac[m][1]) + (ac[m][2] + ac[m][3]);
-        nrm[nt] = sqrtf(sum_q(s2));
+        nrm[nt] = __builtin_amdgcn_sqrtf(sum_q(s2));
       }
     }
     // 2. code bits (index bits by binary search, most significant first),
@@ -314,8 +314,8 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       valid[nt] = v0 + 16 * nt + nl < a.n;
-      live[nt] = valid[nt] && nrm[nt] > 0.f;
-      inv[nt] = live[nt] ? 1.f / nrm[nt] : 0.f;
+      live[nt] = valid[nt] & (nrm[nt] > 0.f);
+      inv[nt] = live[nt] ? __builtin_amdgcn_rcpf(nrm[nt]) : 0.f;
       if (w == 0 && q == 0 && valid[nt]) a.norm[v0 + 16 * nt + nl] = tqd::f32_to_half_bits(nrm[nt]);
     }
     float res[2][2][4];
@@ -325,13 +325,15 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
       const float u = acc[nt][m][r] * inv[nt];
       bool bt[B];
       interval_bits<B, B - 1>(u, th, bt);
+      // (bitwise forms, not selects: the compiler would otherwise branch
+      // around the search for lanes that do not need it)
       if constexpr (PROD) {
-        const float rr = live[nt] ? u - pick<L, 0, 1>(cv, bt) : 0.f;
+        const float rr = (u - pick<L, 0, 1>(cv, bt)) * (float)live[nt];
         res[nt][m][r] = rr;
         r2[nt] = fmaf(rr, rr, r2[nt]);
       }
 #pragma unroll
-      for (int p = 0; p < B; ++p) pl[p] = valid[nt] && (live[nt] ? bt[B - 1 - p] : p == B - 1);
+      for (int p = 0; p < B; ++p) pl[p] = valid[nt] & ((live[nt] & bt[B - 1 - p]) | (!live[nt] & (p == B - 1)));
     };
     // word (vector t of key tile nt, group w, plane p) of the key layout:
     // bit i = coordinate 32 w + i. Each lane sets the bits of its 8
@@ -448,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         for (int m = 0; m < 2; ++m) {
           const v4f pj = pc[m][0] + (pc[m][1] + pc[m][2]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) zb[nt][m][r] = valid[nt] && (pj[r] >= 0.f || !live[nt]);
+          for (int r = 0; r < 4; ++r) zb[nt][m][r] = valid[nt] & ((pj[r] >= 0.f) | !live[nt]);
         }
         if constexpr (KEYS) kw[nt][B] = key_word(zb[nt]);
         __syncthreads();  // rq is rewritten by the next half
@@ -463,7 +465,8 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
       if (w == 0 && q < 2) {
         const int vt = 16 * q + nl;
         if (v0 + vt < a.n) {
-          const float rho = sqrtf((rho_part[0][vt] + rho_part[1][vt]) + (rho_part[2][vt] + rho_part[3][vt]));
+          const float rho =
+              __builtin_amdgcn_sqrtf((rho_part[0][vt] + rho_part[1][vt]) + (rho_part[2][vt] + rho_part[3][vt]));
           a.rnorm[v0 + vt] = tqd::f32_to_half_bits(rho);
         }
       }
