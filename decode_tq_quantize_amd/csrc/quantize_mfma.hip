@@ -320,10 +320,10 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
     }
     float res[2][2][4];
     float r2[2] = {0.f, 0.f};
-    // index plane p (bit B - 1 - p of the search order) of one coordinate
-    auto code = [&](int nt, int m, int r, bool (&pl)[B]) __attribute__((always_inline)) {
+    // the search bits of one coordinate (most significant first), and the
+    // residual
+    auto code_bits = [&](int nt, int m, int r, bool (&bt)[B]) __attribute__((always_inline)) {
       const float u = acc[nt][m][r] * inv[nt];
-      bool bt[B];
       interval_bits<B, B - 1>(u, th, bt);
       // (bitwise forms, not selects: the compiler would otherwise branch
       // around the search for lanes that do not need it)
@@ -332,6 +332,11 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         res[nt][m][r] = rr;
         r2[nt] = fmaf(rr, rr, r2[nt]);
       }
+    };
+    // index plane p of one coordinate, zero and padding vectors applied
+    auto code = [&](int nt, int m, int r, bool (&pl)[B]) __attribute__((always_inline)) {
+      bool bt[B];
+      code_bits(nt, m, r, bt);
 #pragma unroll
       for (int p = 0; p < B; ++p) pl[p] = valid[nt] & ((live[nt] & bt[B - 1 - p]) | (!live[nt] & (p == B - 1)));
     };
@@ -361,8 +366,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
     uint32_t ow[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) ow[i] = 0u;
-    auto value_words = [&](int m, int r, int p, bool b0, bool b1) __attribute__((always_inline)) {
-      const uint64_t m0 = __builtin_amdgcn_ballot_w64(b0), m1 = __builtin_amdgcn_ballot_w64(b1);
+    auto value_words = [&](int m, int r, int p, uint64_t m0, uint64_t m1) __attribute__((always_inline)) {
       const int i = (16 * m + r) * P + p;  // + 4 q P for lane group q
 #pragma unroll
       for (int h = 0; h < 2; ++h) {  // lane groups 2 h and 2 h + 1
@@ -391,15 +395,32 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         for (int p = 0; p < B; ++p) kw[nt][p] = key_word(pb[p]);
       }
     } else {
+      // ballots of the compares themselves (a ballot of a combined flag
+      // would make the compiler round-trip it through a vector register);
+      // zero and padding vectors are applied to the masks
+      uint64_t vm[2], lm[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        vm[nt] = __builtin_amdgcn_ballot_w64(valid[nt]);
+        lm[nt] = __builtin_amdgcn_ballot_w64(live[nt]);
+      }
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          bool pl0[B], pl1[B];
-          code(0, m, r, pl0);
-          code(1, m, r, pl1);
+          uint64_t pm[2][B];
 #pragma unroll
-          for (int p = 0; p < B; ++p) value_words(m, r, p, pl0[p], pl1[p]);
+          for (int nt = 0; nt < 2; ++nt) {
+            bool bt[B];
+            code_bits(nt, m, r, bt);
+#pragma unroll
+            for (int p = 0; p < B; ++p) {
+              const uint64_t c = __builtin_amdgcn_ballot_w64(bt[B - 1 - p]);
+              pm[nt][p] = (c & lm[nt]) | (p == B - 1 ? (vm[nt] & ~lm[nt]) : 0ull);
+            }
+          }
+#pragma unroll
+          for (int p = 0; p < B; ++p) value_words(m, r, p, pm[0][p], pm[1][p]);
         }
     }
     // 3. QJL signs: S r~ on the matrix cores, one 16-vector half at a time
@@ -459,7 +480,8 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) value_words(m, r, B, zb[0][m][r], zb[1][m][r]);
+          for (int r = 0; r < 4; ++r)
+            value_words(m, r, B, __builtin_amdgcn_ballot_w64(zb[0][m][r]), __builtin_amdgcn_ballot_w64(zb[1][m][r]));
       }
       // residual norms (one lane per vector)
       if (w == 0 && q < 2) {
