@@ -255,16 +255,18 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
     for (int nt = 0; nt < 2; ++nt) {
       if constexpr (BF16IN) {
         const uint4(&xw)[4] = cur[nt].w;
-        v4f ah[2], al[2], gram = v4f{0.f, 0.f, 0.f, 0.f};
+        // one accumulator per 16 rows: the matrix cores accumulate in place
+        // back to back, so the hi and lo products need no separate sums
+        v4f ah[2], gram = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 2; ++m) ah[m] = al[m] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 2; ++m) ah[m] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const bf16x8 xb = __builtin_bit_cast(bf16x8, xw[kk]);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             ah[m] = mfma_bf16(RH[m][kk], xb, ah[m]);
-            al[m] = mfma_bf16(RL[m][kk], xb, al[m]);
+            ah[m] = mfma_bf16(RL[m][kk], xb, ah[m]);
           }
           // the 16 vectors' Gram matrix: the same register is the A operand
           // (row = vector) and the B operand (column = vector); products of
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
           gram = mfma_bf16(xb, xb, gram);
         }
 #pragma unroll
-        for (int m = 0; m < 2; ++m) acc[nt][m] = ah[m] + al[m];
+        for (int m = 0; m < 2; ++m) acc[nt][m] = ah[m];
         // |x|^2 of vector nl is the diagonal entry (nl, nl), held by lane
         // 16 (nl / 4) + nl as its element nl % 4
         const float dsel = (nl & 2) ? ((nl & 1) ? gram[3] : gram[2]) : ((nl & 1) ? gram[1] : gram[0]);
@@ -447,11 +449,9 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         __syncthreads();
         // step kk contracts coordinates 32 q' + 8 kk .. + 7 from lane group q'
         // (chunk 4 q' + kk), the same assignment on both operands
-        v4f pc[2][3];
+        v4f pc[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int c = 0; c < 3; ++c) pc[m][c] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 2; ++m) pc[m] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const int ph = (4 * q + kk) ^ nl;
@@ -462,14 +462,14 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
             const int row = 32 * w + 16 * m + nl;  // row % 16 == nl
             const bf16x8 sh = __builtin_bit_cast(bf16x8, Sq[0][row][ph]);
             const bf16x8 sl = __builtin_bit_cast(bf16x8, Sq[1][row][ph]);
-            pc[m][0] = mfma_bf16(sh, rh, pc[m][0]);
-            pc[m][1] = mfma_bf16(sh, rl, pc[m][1]);
-            pc[m][2] = mfma_bf16(sl, rh, pc[m][2]);
+            pc[m] = mfma_bf16(sh, rh, pc[m]);
+            pc[m] = mfma_bf16(sh, rl, pc[m]);
+            pc[m] = mfma_bf16(sl, rh, pc[m]);
           }
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const v4f pj = pc[m][0] + (pc[m][1] + pc[m][2]);
+          const v4f pj = pc[m];
 #pragma unroll
           for (int r = 0; r < 4; ++r) zb[nt][m][r] = valid[nt] & ((pj[r] >= 0.f) | !live[nt]);
         }
