@@ -43,6 +43,15 @@ struct QmArgs {
   uint16_t* rnorm;
 };
 
+// 2 x + (this lane's bit of the wave mask): one add with the mask as the
+// carry in. The masks passed here are formed by the scalar unit.
+__device__ __forceinline__ uint32_t shift_in(uint32_t x, uint64_t mask) {
+  uint32_t r;
+  uint64_t co;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=&s"(co) : "v"(x), "s"(mask));
+  return r;
+}
+
 // Words of two 16-bit halves to lanes: lane l0 of `a` gets the low halves
 // of x (low) and y (high), lane l1 of `b` their high halves. The packs run
 // on the scalar unit, whose reads of VALU-written SGPRs wait in hardware.
@@ -335,26 +344,14 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         r2[nt] = fmaf(rr, rr, r2[nt]);
       }
     };
-    // index plane p of one coordinate, zero and padding vectors applied
-    auto code = [&](int nt, int m, int r, bool (&pl)[B]) __attribute__((always_inline)) {
-      bool bt[B];
-      code_bits(nt, m, r, bt);
-#pragma unroll
-      for (int p = 0; p < B; ++p) pl[p] = valid[nt] & ((live[nt] & bt[B - 1 - p]) | (!live[nt] & (p == B - 1)));
-    };
     // word (vector t of key tile nt, group w, plane p) of the key layout:
-    // bit i = coordinate 32 w + i. Each lane sets the bits of its 8
-    // coordinates and the 4 lanes of a vector combine theirs.
+    // bit i = coordinate 32 w + i. Each lane shifts its 8 bits of the plane
+    // into an accumulator straight from the plane's ballots (coordinates
+    // (m, r) in descending order, one add-with-carry per bit), spreads them
+    // to bits 16 m + 4 q + r, and the 4 lanes of a vector combine theirs.
     uint32_t kw[2][P];
-    auto key_word = [&](const bool (&b)[2][4]) __attribute__((always_inline)) -> uint32_t {
-      uint32_t nib[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        nib[m] = 0u;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) nib[m] |= b[m][r] ? (1u << r) : 0u;
-      }
-      uint32_t wp = (nib[0] | (nib[1] << 16)) << (4 * q);
+    auto key_word = [&](uint32_t acc8) __attribute__((always_inline)) -> uint32_t {
+      uint32_t wp = ((acc8 & 0xfu) | ((acc8 & 0xf0u) << 12)) << (4 * q);
       wp |= __shfl_xor(wp, 16, 64);
       wp |= __shfl_xor(wp, 32, 64);
       return wp;
@@ -380,32 +377,37 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
           halves_to_lanes(ow[i0 >> 6], ow[i1 >> 6], x, y, i0 & 63, i1 & 63);
       }
     };
+    // ballots of the compares themselves (a ballot of a combined flag, or a
+    // per-lane combination, makes the compiler round-trip it through a
+    // vector register); zero and padding vectors are applied to the masks
+    uint64_t vm[2], lm[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      vm[nt] = __builtin_amdgcn_ballot_w64(valid[nt]);
+      lm[nt] = __builtin_amdgcn_ballot_w64(live[nt]);
+    }
     if constexpr (KEYS) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        bool pb[B][2][4];
+        uint32_t acc8[B];
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int p = 0; p < B; ++p) acc8[p] = 0u;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            bool pl[B];
-            code(nt, m, r, pl);
+        for (int m = 1; m >= 0; --m)
 #pragma unroll
-            for (int p = 0; p < B; ++p) pb[p][m][r] = pl[p];
+          for (int r = 3; r >= 0; --r) {
+            bool bt[B];
+            code_bits(nt, m, r, bt);
+#pragma unroll
+            for (int p = 0; p < B; ++p) {
+              const uint64_t c = __builtin_amdgcn_ballot_w64(bt[B - 1 - p]);
+              acc8[p] = shift_in(acc8[p], (c & lm[nt]) | (p == B - 1 ? (vm[nt] & ~lm[nt]) : 0ull));
+            }
           }
 #pragma unroll
-        for (int p = 0; p < B; ++p) kw[nt][p] = key_word(pb[p]);
+        for (int p = 0; p < B; ++p) kw[nt][p] = key_word(acc8[p]);
       }
     } else {
-      // ballots of the compares themselves (a ballot of a combined flag
-      // would make the compiler round-trip it through a vector register);
-      // zero and padding vectors are applied to the masks
-      uint64_t vm[2], lm[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        vm[nt] = __builtin_amdgcn_ballot_w64(valid[nt]);
-        lm[nt] = __builtin_amdgcn_ballot_w64(live[nt]);
-      }
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         const float rs = sum_q(r2[nt]);
         if (q == 0) rho_part[w][16 * nt + nl] = rs;
       }
-      bool zb[2][2][4];
+      uint64_t zm[2][2][4];  // sign-plane masks
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         // residual coordinates 32 w + 16 m + 4 q .. + 3 of vector nl: half of
@@ -471,9 +473,16 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         for (int m = 0; m < 2; ++m) {
           const v4f pj = pc[m];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) zb[nt][m][r] = valid[nt] & ((pj[r] >= 0.f) | !live[nt]);
+          for (int r = 0; r < 4; ++r) zm[nt][m][r] = (__builtin_amdgcn_ballot_w64(pj[r] >= 0.f) | ~lm[nt]) & vm[nt];
         }
-        if constexpr (KEYS) kw[nt][B] = key_word(zb[nt]);
+        if constexpr (KEYS) {
+          uint32_t acc8 = 0u;
+#pragma unroll
+          for (int m = 1; m >= 0; --m)
+#pragma unroll
+            for (int r = 3; r >= 0; --r) acc8 = shift_in(acc8, zm[nt][m][r]);
+          kw[nt][B] = key_word(acc8);
+        }
         __syncthreads();  // rq is rewritten by the next half
       }
       if constexpr (!KEYS) {
@@ -481,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         for (int m = 0; m < 2; ++m)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            value_words(m, r, B, __builtin_amdgcn_ballot_w64(zb[0][m][r]), __builtin_amdgcn_ballot_w64(zb[1][m][r]));
+            value_words(m, r, B, zm[0][m][r], zm[1][m][r]);
       }
       // residual norms (one lane per vector)
       if (w == 0 && q < 2) {
