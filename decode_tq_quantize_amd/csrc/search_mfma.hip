@@ -343,13 +343,13 @@ __global__ __launch_bounds__(kThreads, 2) void scan2_kernel(Scan2Args a) {
 
   // this lane's plane words of its 8 database tiles, one coordinate group
   // ahead (group g + 1 is loaded while group g is processed)
-  uint32_t wn[8][P];
+  uint32_t wA[8][P], wB[8][P];
   // (through a buffer resource: uniform byte offset per tile and group, one
   // lane offset; the database is below 4 GB, which the host checks)
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(a.packed), (short)0, (int)(uint32_t)min(a.packed_bytes, (int64_t)0xffffffff), 0x00020000);
   const uint32_t word_off = (uint32_t)(nl * P * 4);
-  auto load_words = [&](int g) {
+  auto load_words = [&](int g, uint32_t (&wn)[8][P]) __attribute__((always_inline)) {
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -381,9 +381,11 @@ __global__ __launch_bounds__(kThreads, 2) void scan2_kernel(Scan2Args a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ores, (__attribute__((address_space(3))) void*)&aq[bf][tp >> 1][tp & 1][16 * w][0],
                                                16, stage_off, (uint32_t)((tp * a.d + 32 * g) * 2), 0, 0);
   };
-  load_words(0);
+  load_words(0, wA);
   stage(0, 0);
-  for (int g = 0; g < G; ++g) {
+  // one group; its words are in wn, the next group's go to wnext (the loop
+  // below alternates two arrays, so no words are copied)
+  auto group = [&](int g, const uint32_t (&wn)[8][P], uint32_t (&wnext)[8][P]) __attribute__((always_inline)) {
     const int bf = g & 1;
     // this group's staged operands and words have arrived (own loads), and
     // every wave's (barrier)
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan2_kernel(Scan2Args a) {
     // group g - 1, which every wave finished before the barrier above)
     if (g + 1 < G) {
       stage(g + 1, bf ^ 1);
-      load_words(g + 1);
+      load_words(g + 1, wnext);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -449,6 +451,10 @@ __global__ __launch_bounds__(kThreads, 2) void scan2_kernel(Scan2Args a) {
         }
       }
     }
+  };
+  for (int g = 0; g < G; g += 2) {
+    group(g, wA, wB);
+    if (g + 1 < G) group(g + 1, wB, wA);
   }
   // scores of queries q0 + 16 qt + 4 kq + r and vectors vb + 16 (dt0 + j) + nl:
   // n (acc - C1 - rho C2)
