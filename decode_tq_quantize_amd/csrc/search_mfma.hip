@@ -230,10 +230,11 @@ __global__ __launch_bounds__(kThreads) void qsplit_kernel(QsArgs a) {
     for (int t = 0; t < TW; ++t) {
       uint32_t hi, lo;
       float s0, s1;
-      split2(2.f * a.alpha[t] * t0, 2.f * a.alpha[t] * t1, hi, lo, s0, s1);
+      // (the scan's B operand for these terms is 2 b, so A is alpha_S y~)
+      split2(a.alpha[t] * t0, a.alpha[t] * t1, hi, lo, s0, s1);
       ops[((t * 2 + 0) * a.d + c) >> 1] = hi;
       ops[((t * 2 + 1) * a.d + c) >> 1] = lo;
-      c1 += 0.5f * (s0 + s1);
+      c1 += s0 + s1;
     }
     if (PROD) {
       uint32_t hi, lo;
@@ -289,14 +290,41 @@ __host__ __device__ constexpr int odd_subset(int B, int t) {
   return 0;
 }
 
-// Eight bits t (bit e = coordinate e) as eight bf16 values mag * bit, two to
-// a register (register j: coordinate 2 j in the low half, 2 j + 1 in the
-// high half). mag is a bf16 bit pattern.
-__device__ __forceinline__ bf16x8 bits_to_bf16(uint32_t t, uint32_t mag) {
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Byte k of w in both 16-bit halves (one byte permute).
+__device__ __forceinline__ uint32_t byte_twice(uint32_t w, int k) {
+  return __builtin_amdgcn_perm(w, w, (uint32_t)k | (0x0cu << 8) | ((uint32_t)k << 16) | (0x0cu << 24));
+}
+
+// Eight bits (a byte held in both halves of tt; bit e = coordinate e) as
+// eight bf16 values 2 * bit, two to a register (register j: coordinate 2 j
+// in the low half, 2 j + 1 in the high half). bf16 2.0 is the single bit
+// 0x4000, so each half is the byte shifted to put its bit on bit 14 (one
+// packed 16-bit shift), then masked.
+__device__ __forceinline__ bf16x8 bits_to_bf16_two(uint32_t tt) {
   uint32_t r[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) r[j] = ((((t >> (2 * j)) & 3u) * 0x8001u) & 0x10001u) * mag;
+  for (int j = 0; j < 4; ++j) {
+    const u16x2 sh = {(unsigned short)(14 - 2 * j), (unsigned short)(13 - 2 * j)};
+    r[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, tt) << sh) & 0x40004000u;
+  }
   return __builtin_bit_cast(bf16x8, make_uint4(r[0], r[1], r[2], r[3]));
+}
+
+// The same bits as bf16 values magh * bit and magl * bit (bf16 bit patterns
+// below 2^16): bits moved to bit 0 of each half, then one 24-bit multiply.
+__device__ __forceinline__ void bits_to_bf16_mag(uint32_t tt, uint32_t magh, uint32_t magl, bf16x8& bh, bf16x8& bl) {
+  uint32_t rh[4], rl[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u16x2 sh = {(unsigned short)(2 * j), (unsigned short)(2 * j + 1)};
+    const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, tt) >> sh) & 0x00010001u;
+    rh[j] = b * magh;
+    rl[j] = b * magl;
+  }
+  bh = __builtin_bit_cast(bf16x8, make_uint4(rh[0], rh[1], rh[2], rh[3]));
+  bl = __builtin_bit_cast(bf16x8, make_uint4(rl[0], rl[1], rl[2], rl[3]));
 }
 
 // Workgroup: 64 queries x 256 database vectors, 4 waves; wave w takes query
@@ -430,13 +458,10 @@ __global__ __launch_bounds__(kThreads, 2) void scan2_kernel(Scan2Args a) {
 #pragma unroll
         for (int pp = 0; pp < B; ++pp)
           if ((S >> pp) & 1) x ^= wc[j] >> (8 * pp);
-        Bw[t] = bits_to_bf16(x & 0xffu, 0x3f80u);  // bf16 1.0
+        Bw[t] = bits_to_bf16_two(byte_twice(x, 0));  // bf16 2.0 per set bit
       }
       bf16x8 Bh = Bw[0], Bl = Bw[0];
-      if (PROD) {
-        Bh = bits_to_bf16((wc[j] >> (8 * (P - 1))) & 0xffu, r2h[j]);
-        Bl = bits_to_bf16((wc[j] >> (8 * (P - 1))) & 0xffu, r2l[j]);
-      }
+      if (PROD) bits_to_bf16_mag(byte_twice(wc[j], P - 1), r2h[j], r2l[j], Bh, Bl);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
