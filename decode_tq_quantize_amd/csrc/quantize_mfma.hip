@@ -3,17 +3,19 @@
 // section 4.2: Lloyd-Max interval index per coordinate; section 4.3: the
 // residual r~ = x~ - c[idx] projected with S, signs kept, plus |r~|).
 //
-// Both d x d products run on v_mfma_f32_16x16x4_f32 (fp32 operands, fp32
-// accumulation): a persistent workgroup of 4 waves keeps rows 32 w .. 32 w +
-// 31 of R and of S (wave w, one 32-coordinate group each) in registers as
-// MFMA A operands and streams tiles of 32 vectors through them. The
-// contraction index is permuted so that each lane reads 32 consecutive
-// coordinates: in MFMA step kk, lane group q (lanes 16 q .. 16 q + 15)
-// carries coordinate 32 q + kk. The rotated vector comes out with lane l
-// holding coordinates 32 w + 16 m + 4 (l / 16) + r (m = 0, 1; r = 0..3) of
-// vector l % 16; codes, residuals and signs are formed there, the residual
-// goes through LDS to the operand layout of the second product, and the
-// codes are packed with wave ballots into the library's bit-plane layouts.
+// A persistent workgroup of 4 waves streams tiles of 32 vectors; wave w owns
+// output coordinates 32 w .. 32 w + 31. bf16 inputs are exact in bf16, so R
+// is held in registers as bf16 high and low parts (MFMA A operands) and R x
+// runs on v_mfma_f32_16x16x32_bf16 with both products accumulated in place;
+// one more MFMA with the input as both operands gives the vectors' Gram
+// matrix, whose diagonal is |x|^2. fp32 inputs use v_mfma_f32_16x16x4_f32
+// with R in fp32. The rotated vector comes out with lane l holding
+// coordinates 32 w + 16 m + 4 (l / 16) + r (m = 0, 1; r = 0..3) of vector
+// l % 16 of a 16-vector half; the interval index is found there by binary
+// search over the thresholds, the residual's bf16 parts go through LDS to
+// the operand layout of S r~ (bf16 matrix cores, S in LDS), and the code
+// and sign bits are packed straight from wave ballots of the compares into
+// the library's bit-plane layouts.
 #include "device_common.h"
 #include "internal.h"
 

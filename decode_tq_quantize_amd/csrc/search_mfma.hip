@@ -20,10 +20,11 @@
 // scan2 (bf16 matrix cores; used for 3 code bits with QJL): the
 //        codebook is mirror-symmetric, so c[idx] = sum_{|S| odd} alpha_S
 //        prod_{p in S} (2 b_p - 1), and each product of signs is 2 (xor of
-//        planes) - 1. The query side carries 2 alpha_S y~ per term and
+//        planes) - 1. The query side carries alpha_S y~ per term and
 //        gamma y^ for the QJL term, split into bf16 high and low parts
-//        (qsplit_kernel); the database side is the xor-ed plane bits as bf16
-//        {0, 1} ({0, 2 rho}, split the same way, for the QJL term), so every
+//        (qsplit_kernel); the database side is the xor-ed plane bits as bf16 {0, 2} (2.0 is
+//        a single bit, so a packed 16-bit shift and a mask place it), or
+//        {0, 2 rho} split the same way for the QJL term, so every
 //        product is exact up to the splits (about 2^-17 relative per term,
 //        fp32 accumulation). The constant parts sum_S alpha_S sum y~ and
 //        rho gamma sum y^ are removed per (query, vector) at the end.
