@@ -187,8 +187,11 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
   // row r is stored at c ^ (r % 16), so that the 16 rows read at once hit
   // different banks.
   __shared__ uint4 Sq[2][PROD ? kD : 1][kD / 8];
-  __shared__ uint4 rq[2][PROD ? 16 : 1][kD / 8];
-  __shared__ float rho_part[4][kTile];
+  // residual parts of both 16-vector halves ([half][hi / lo][vector][chunk]);
+  // once the projection has read them, the same space takes the residual
+  // norms' partial sums (S and this fill the 160 KB of two workgroups)
+  __shared__ uint4 rq[PROD ? 2 : 1][2][PROD ? 16 : 1][kD / 8];
+  float(&rho_part)[4][kTile] = *reinterpret_cast<float(*)[4][kTile]>(&rq[0][0][0][0]);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, nl = lane & 15;
@@ -429,54 +432,60 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
           for (int p = 0; p < B; ++p) value_words(m, r, p, pm[0][p], pm[1][p]);
         }
     }
-    // 3. QJL signs: S r~ on the matrix cores, one 16-vector half at a time
+    // 3. QJL signs: S r~ on the matrix cores, both 16-vector halves per S
+    // operand read
     if constexpr (PROD) {
+      // residual coordinates 32 w + 16 m + 4 q .. + 3 of vector nl: half of
+      // chunk (4 w + 2 m + q / 2) of the vector's row
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float rs = sum_q(r2[nt]);
-        if (q == 0) rho_part[w][16 * nt + nl] = rs;
-      }
-      uint64_t zm[2][2][4];  // sign-plane masks
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        // residual coordinates 32 w + 16 m + 4 q .. + 3 of vector nl: half of
-        // chunk (4 w + 2 m + q / 2) of the vector's row
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           uint32_t h0, l0, h1, l1;
           split_bf16(res[nt][m][0], res[nt][m][1], h0, l0);
           split_bf16(res[nt][m][2], res[nt][m][3], h1, l1);
           const int c = (4 * w + 2 * m + (q >> 1)) ^ nl, half = q & 1;
-          reinterpret_cast<uint2*>(&rq[0][nl][c])[half] = make_uint2(h0, h1);
-          reinterpret_cast<uint2*>(&rq[1][nl][c])[half] = make_uint2(l0, l1);
+          reinterpret_cast<uint2*>(&rq[nt][0][nl][c])[half] = make_uint2(h0, h1);
+          reinterpret_cast<uint2*>(&rq[nt][1][nl][c])[half] = make_uint2(l0, l1);
         }
-        __syncthreads();
-        // step kk contracts coordinates 32 q' + 8 kk .. + 7 from lane group q'
-        // (chunk 4 q' + kk), the same assignment on both operands
-        v4f pc[2];
+      __syncthreads();
+      // step kk contracts coordinates 32 q' + 8 kk .. + 7 from lane group q'
+      // (chunk 4 q' + kk), the same assignment on both operands
+      v4f pc[2][2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) pc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int ph = (4 * q + kk) ^ nl;
-          const bf16x8 rh = __builtin_bit_cast(bf16x8, rq[0][nl][ph]);
-          const bf16x8 rl = __builtin_bit_cast(bf16x8, rq[1][nl][ph]);
+        for (int m = 0; m < 2; ++m) pc[nt][m] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const int row = 32 * w + 16 * m + nl;  // row % 16 == nl
-            const bf16x8 sh = __builtin_bit_cast(bf16x8, Sq[0][row][ph]);
-            const bf16x8 sl = __builtin_bit_cast(bf16x8, Sq[1][row][ph]);
-            pc[m] = mfma_bf16(sh, rh, pc[m]);
-            pc[m] = mfma_bf16(sh, rl, pc[m]);
-            pc[m] = mfma_bf16(sl, rh, pc[m]);
-          }
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ph = (4 * q + kk) ^ nl;
+        bf16x8 rh[2], rl[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          rh[nt] = __builtin_bit_cast(bf16x8, rq[nt][0][nl][ph]);
+          rl[nt] = __builtin_bit_cast(bf16x8, rq[nt][1][nl][ph]);
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const v4f pj = pc[m];
+          const int row = 32 * w + 16 * m + nl;  // row % 16 == nl
+          const bf16x8 sh = __builtin_bit_cast(bf16x8, Sq[0][row][ph]);
+          const bf16x8 sl = __builtin_bit_cast(bf16x8, Sq[1][row][ph]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) zm[nt][m][r] = (__builtin_amdgcn_ballot_w64(pj[r] >= 0.f) | ~lm[nt]) & vm[nt];
+          for (int nt = 0; nt < 2; ++nt) {
+            pc[nt][m] = mfma_bf16(sh, rh[nt], pc[nt][m]);
+            pc[nt][m] = mfma_bf16(sh, rl[nt], pc[nt][m]);
+            pc[nt][m] = mfma_bf16(sl, rh[nt], pc[nt][m]);
+          }
         }
+      }
+      uint64_t zm[2][2][4];  // sign-plane masks
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            zm[nt][m][r] = (__builtin_amdgcn_ballot_w64(pc[nt][m][r] >= 0.f) | ~lm[nt]) & vm[nt];
         if constexpr (KEYS) {
           uint32_t acc8 = 0u;
 #pragma unroll
@@ -485,15 +494,20 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
             for (int r = 3; r >= 0; --r) acc8 = shift_in(acc8, zm[nt][m][r]);
           kw[nt][B] = key_word(acc8);
         }
-        __syncthreads();  // rq is rewritten by the next half
       }
       if constexpr (!KEYS) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            value_words(m, r, B, zm[0][m][r], zm[1][m][r]);
+          for (int r = 0; r < 4; ++r) value_words(m, r, B, zm[0][m][r], zm[1][m][r]);
       }
+      __syncthreads();  // every wave has read rq: its space takes the norms' partials
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float rs = sum_q(r2[nt]);
+        if (q == 0) rho_part[w][16 * nt + nl] = rs;
+      }
+      __syncthreads();
       // residual norms (one lane per vector)
       if (w == 0 && q < 2) {
         const int vt = 16 * q + nl;
@@ -529,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
       for (int i = 0; i < NW; ++i)
         if (64 * i + lane < 32 * P) dst[64 * i + lane] = ow[i];
     }
-    if constexpr (PROD) __syncthreads();  // rho_part is rewritten by the next tile
+    if constexpr (PROD) __syncthreads();  // rq (and rho_part in it) is rewritten by the next tile
   }
 }
 
