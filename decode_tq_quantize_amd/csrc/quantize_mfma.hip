@@ -248,19 +248,16 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
   }
   __syncthreads();
 
-  // the inputs of the next tile are in flight while one is processed (rows
-  // past n re-read row n - 1 and are masked)
-  XIn<BF16IN> xin[2];
-  auto load_tile = [&](int64_t t) __attribute__((always_inline)) {
+  // a tile's inputs (rows past n re-read row n - 1 and are masked)
+  auto load_tile = [&](XIn<BF16IN>(&dst)[2], int64_t t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) load_in(xin[nt], a, min(t * kTile + 16 * nt + nl, a.n - 1), q);
+    for (int nt = 0; nt < 2; ++nt) load_in(dst[nt], a, min(t * kTile + 16 * nt + nl, a.n - 1), q);
   };
-  load_tile(blockIdx.x);
   const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
-  for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+  // one tile, whose inputs are in cur; once the rotation has read them, cur
+  // takes the inputs of tile tnext
+  auto body = [&](int64_t tile, XIn<BF16IN>(&cur)[2], int64_t tnext) __attribute__((always_inline)) {
     const int64_t v0 = tile * kTile;
-    XIn<BF16IN> cur[2] = {xin[0], xin[1]};
-    load_tile(tile + gridDim.x);
     // 1. rotated coordinates 32 w + 16 m + 4 q + r of vector 16 nt + nl, and
     // the vector norms
     v4f acc[2][2];
@@ -320,6 +317,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         nrm[nt] = __builtin_amdgcn_sqrtf(sum_q(s2));
       }
     }
+    load_tile(cur, tnext);
     // 2. code bits (index bits by binary search, most significant first),
     // residuals and their norms. A vector of norm 0 gets index L / 2 and
     // residual 0; padding vectors keep all-zero bits. Wave ballots of the
@@ -544,6 +542,18 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         if (64 * i + lane < 32 * P) dst[64 * i + lane] = ow[i];
     }
     if constexpr (PROD) __syncthreads();  // rq (and rho_part in it) is rewritten by the next tile
+  };
+  XIn<BF16IN> xa[2], xb[2];
+  load_tile(xa, blockIdx.x);
+  if constexpr (BF16IN) {
+    // two tiles' inputs in flight (the two buffers alternate, nothing is copied)
+    load_tile(xb, (int64_t)blockIdx.x + gridDim.x);
+    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += 2 * (int64_t)gridDim.x) {
+      body(tile, xa, tile + 2 * (int64_t)gridDim.x);
+      if (tile + gridDim.x < a.ntiles) body(tile + gridDim.x, xb, tile + 3 * (int64_t)gridDim.x);
+    }
+  } else {
+    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) body(tile, xa, tile + gridDim.x);
   }
 }
 
