@@ -135,11 +135,21 @@ __device__ __forceinline__ void load_in(XIn<false>& r, const QmArgs& a, int64_t 
   for (int k = 0; k < 8; ++k) r.f[k] = p[k];
 }
 
+// Lane exchanges with lane l ^ 16 and l ^ 32 (v_permlane16/32_swap: with
+// both operands the same value, the two results are this lane's value and
+// its partner's, in some order), so combining them is symmetric.
+__device__ __forceinline__ uint32_t or_q(uint32_t v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = a[0] | a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return b[0] | b[1];
+}
 // Sum over the 4 lanes that hold the same vector (lanes l, l ^ 16, l ^ 32, l ^ 48).
 __device__ __forceinline__ float sum_q(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Threshold th[LO + k STRIDE], k = 0 .. N - 1, chosen by the bits found so
@@ -354,10 +364,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
     // to bits 16 m + 4 q + r, and the 4 lanes of a vector combine theirs.
     uint32_t kw[2][P];
     auto key_word = [&](uint32_t acc8) __attribute__((always_inline)) -> uint32_t {
-      uint32_t wp = ((acc8 & 0xfu) | ((acc8 & 0xf0u) << 12)) << (4 * q);
-      wp |= __shfl_xor(wp, 16, 64);
-      wp |= __shfl_xor(wp, 32, 64);
-      return wp;
+      return or_q(((acc8 & 0xfu) | ((acc8 & 0xf0u) << 12)) << (4 * q));
     };
     // words (coordinate j, plane p) of the value layout: bit i = vector
     // v0 + i; the wave's coordinates are 32 P contiguous words, word
