@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--copies", type=int, default=24)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--only", default="", help="comma list of extras to run: quantize,longctx,search")
+    p.add_argument("--only", default="", help="comma list of extras to run: quantize,longctx,search,bits")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one 256 MiB device-to-device copy (the known-size reference for the "
                         "FETCH_SIZE / WRITE_SIZE counters)")
@@ -163,6 +163,129 @@ def decode_single_layer(args):
                dk_ms=dk_ms, dk_bytes=dk_bytes)
     res["oracle_inputs"] = (K, V, qry, Rk, Sk, Rv)
     return res
+
+
+def graph_ms(call, steps, warmup=5):
+    """Mean time per call of `steps` calls captured into one HIP graph (HIP events around one replay)."""
+    import torch
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(steps):
+                call(i)
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()  # one untimed replay
+    with Timer() as tm:
+        graph.replay()
+    return tm.ms / steps, side
+
+
+# key / value bit allocations at the single-layer shape: (name, key MSE bits,
+# key has the QJL sketch, value bits)
+ALLOCATIONS = [
+    ("keys 3+1 prod, values 3 (headline)", 3, True, 3),
+    ("keys 4 MSE-only, values 3", 4, False, 3),
+    ("keys 3 MSE-only, values 3", 3, False, 3),
+    ("keys 3+1 prod, values 2", 3, True, 2),
+    ("keys 2+1 prod, values 2", 2, True, 2),
+]
+
+
+def bit_allocations(inputs, steps=100, copies=12):
+    """Decode rate and attention quality of several key/value bit allocations.
+
+    Same single-layer shape and inputs as the headline (batch 1, 32 q / 8 KV
+    heads, head_dim 128, 32768 tokens, bf16 K and V with outlier channels).
+    Each allocation quantises K and V with libtq (untimed), rotates `copies`
+    copies of its cache inside one captured graph, and reports per-call and
+    decode-kernel rates against its own algorithmic bytes; quality compares
+    KV head 0's four query heads with exact fp64 attention on the bf16 K and V.
+    """
+    import numpy as np
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+
+    K, V, qry, Rk, Sk, Rv = inputs
+    B, Hq, Hkv, T, d = 1, 32, 8, 32768, 128
+    n = B * Hkv * T
+    Kt = dev(K.reshape(n, d), torch.bfloat16)
+    Vt = dev(V.reshape(n, d), torch.bfloat16)
+    Kb = Kt[:T].double().cpu().numpy()  # (b 0, KV head 0) rows of the bf16 inputs
+    Vb = Vt[:T].double().cpu().numpy()
+    q_t = dev(qry, torch.bfloat16)
+    G = Hq // Hkv
+    qs = q_t[0, :G].double().cpu().numpy()
+    s_ex = Kb @ qs.T  # [T, G]
+    lg = s_ex / math.sqrt(d)
+    pw = np.exp(lg - lg.max(axis=0))
+    o_ex = (pw.T @ Vb) / pw.sum(axis=0)[:, None]
+    Rk_t, Sk_t, Rv_t = dev(Rk), dev(Sk), dev(Rv)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    res = []
+    for name, kb, kprod, vb in ALLOCATIONS:
+        kvar = tq.TQ_PROD if kprod else tq.TQ_MSE
+        qk = tq.tq_quantizer_init(d, kb, kvar, Rk_t, Sk_t if kprod else None)
+        SRk = None
+        if kprod:
+            SRk = torch.empty(tq.tq_fold_bytes(d) // 4, dtype=torch.float32, device="cuda")
+            tq.tq_quantizer_fold(qk, SRk)
+        qv = tq.tq_quantizer_init(d, vb, tq.TQ_MSE, Rv_t)
+        kp = torch.empty(tq.tq_packed_bytes(d, kb, kvar, tq.TQ_LAYOUT_KEYS, n) // 4, dtype=torch.int32, device="cuda")
+        vp = torch.empty(tq.tq_packed_bytes(d, vb, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, n) // 4, dtype=torch.int32,
+                         device="cuda")
+        kn, vn = (torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(2))
+        kr = torch.empty(n, dtype=torch.int16, device="cuda") if kprod else None
+        tq.tq_quantize_kv(qk, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, Kt, n, d, kp, kn, kr)
+        tq.tq_quantize_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, Vt, n, d, vp, vn)
+        cps = []
+        for c in range(copies):
+            bufs = [x.clone() if x is not None else None for x in (kp, kn, kr, vp, vn)]
+            kd = tq.make_desc([tq.make_group(qk, 0, bufs[0], bufs[1], bufs[2], T)])
+            vd = tq.make_desc([tq.make_group(qv, 0, bufs[3], bufs[4], None, T)])
+            cps.append((bufs, kd, vd))
+        wsb = tq.tq_decode_workspace_bytes(cps[0][1], cps[0][2], B, Hq, Hkv, T)
+        ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+
+        def call(i):
+            _, kd, vd = cps[i % len(cps)]
+            tq.tq_decode_attn(kd, vd, q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, scale, out, None, ws, wsb)
+
+        ms, side = graph_ms(call, steps)
+        dk_ms = kernel_only_ms(call, steps, side)
+        kv_bytes = n * ((kb + kprod) * (d // 8) + 2 + 2 * kprod + vb * (d // 8) + 2)
+        call_bytes = kv_bytes + B * Hq * d * (2 + 4)
+        scores = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+        _, kd, vd = cps[0]
+        tq.tq_decode_attn(kd, vd, q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, scale, out, scores, ws, wsb)
+        torch.cuda.synchronize()
+        s_gpu = scores[0, :G].double().cpu().numpy().T
+        o_gpu = out[0, :G].double().cpu().numpy()
+        s_rel = np.linalg.norm(s_gpu - s_ex, axis=0) / np.linalg.norm(s_ex, axis=0)
+        o_rel = np.linalg.norm(o_gpu - o_ex, axis=1) / np.linalg.norm(o_ex, axis=1)
+        top1 = float(np.mean(np.argmax(s_gpu, axis=0) == np.argmax(s_ex, axis=0)))
+        res.append({"allocation": name, "bytes_per_token_head": kv_bytes // n,
+                    "bits_per_channel": round(8 * (kv_bytes // n) / (2 * d), 3),
+                    "us_per_call": round(ms * 1e3, 3), "call_gbs": round(call_bytes / ms / 1e6, 1),
+                    "decode_kernel_us": round(dk_ms * 1e3, 3), "decode_kernel_gbs": round(kv_bytes / dk_ms / 1e6, 1),
+                    "decode_kernel_hbm_frac": round(kv_bytes / dk_ms / 1e6 / HBM_PEAK_GBS, 4),
+                    "score_rel_error": round(float(s_rel.mean()), 4),
+                    "output_rel_error": round(float(o_rel.mean()), 4),
+                    "top1_token_agreement": top1})
+        log(f"bit allocation {res[-1]}")
+        del cps, ws, scores, kp, vp, kn, vn, kr, SRk
+        torch.cuda.empty_cache()
+    return {"workload": "single-layer decode shape (batch 1, 32 q / 8 KV heads, d=128, 32768 tokens), same bf16 "
+                        "inputs as the headline; quality on KV head 0's 4 query heads against exact fp64 attention",
+            "allocations": res}
 
 
 def _hip_runtime():
@@ -537,6 +660,11 @@ def main():
             except Exception as e:  # an extra that fails is reported, not hidden
                 extras[name] = {"error": repr(e)}
             log(f"{name}: {extras[name]}")
+        if not only or "bits" in only:
+            try:
+                extras["bit_allocations"] = bit_allocations(main_res["oracle_inputs"])
+            except Exception as e:
+                extras["bit_allocations"] = {"error": repr(e)}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline_decode(main_res["oracle_inputs"], main_res["bytes"])

@@ -1279,14 +1279,15 @@ struct Spec {
 
 #define TQ_SPEC(a, b, c, d, e, f) Spec{a, b, c, d, e, f, decode_kernel<a, b, c, d, e, f>}
 // Layouts compiled for the matrix-core decode: keys in one group of 1-4 bits
-// with or without QJL and values of 2-4 bits, plus the outlier-channel splits
-// (32 + 96 channels) of 2.5 and 3.5 bits. Other layouts of 128-channel heads
-// run on the general kernel.
+// with or without QJL and values of 2-4 bits (including MSE-only keys at 2-4
+// bits and asymmetric key/value widths), plus the 2.5-bit outlier-channel
+// split (32 + 96 channels). Other layouts of 128-channel heads run on the
+// general kernel.
 const Spec kSpecs[] = {
     TQ_SPEC(1, 1, 0, 0, 1, 0), TQ_SPEC(1, 1, 0, 0, 2, 0), TQ_SPEC(2, 1, 0, 0, 2, 0), TQ_SPEC(3, 1, 0, 0, 2, 0),
     TQ_SPEC(1, 1, 0, 0, 3, 0), TQ_SPEC(2, 1, 0, 0, 3, 0), TQ_SPEC(3, 1, 0, 0, 3, 0),
     TQ_SPEC(1, 1, 0, 0, 4, 0), TQ_SPEC(2, 1, 0, 0, 4, 0), TQ_SPEC(3, 1, 0, 0, 4, 0),
-    TQ_SPEC(4, 1, 0, 0, 4, 0), TQ_SPEC(4, 0, 0, 0, 4, 0), TQ_SPEC(3, 0, 0, 0, 3, 0),
+    TQ_SPEC(4, 1, 0, 0, 4, 0), TQ_SPEC(4, 0, 0, 0, 4, 0), TQ_SPEC(4, 0, 0, 0, 3, 0), TQ_SPEC(3, 0, 0, 0, 3, 0),
     TQ_SPEC(2, 0, 0, 0, 2, 0), TQ_SPEC(3, 0, 0, 0, 2, 0), TQ_SPEC(4, 0, 0, 0, 2, 0),
     TQ_SPEC(2, 1, 1, 1, 3, 2),
 };

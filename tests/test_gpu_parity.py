@@ -226,9 +226,9 @@ def test_decode_other_head_sizes_and_tiles(d, Hq, Hkv, kB, vB):
     _decode_case(2, Hq, Hkv, 700, 736, [700, 333], kB, vB, "bf16", d)
 
 
-def _decode_case(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt, d, fold=False):
+def _decode_case(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt, d, fold=False, kprod=True):
     K, V = make_kv(B, Hkv, T, d, seed=T)
-    gk = GpuQuantizer(d, kB, True, seed=1, fold=fold)
+    gk = GpuQuantizer(d, kB, kprod, seed=1, fold=fold)
     gv = GpuQuantizer(d, vB, False, seed=2, r_stream=synth.STREAM_R_V)
     ck, cv = otq.quantize(K, gk.oq), otq.quantize(V, gv.oq)
     qry = synth.rng(T, 30).standard_normal((B, Hq, d)).astype(np.float32)
@@ -238,6 +238,18 @@ def _decode_case(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt, d, fold=False):
     vc = Cache(gv, 0, cv, T_cap, "values")
     out, sc = run_decode([kc], [vc], qry, Hkv, T_cap, seq_lens, qdt)
     check_decode(out, sc, [otq.Group(0, gk.oq, ck)], [otq.Group(0, gv.oq, cv)], qry, Hkv, seq_lens)
+
+
+@pytest.mark.parametrize("d,kB,kprod,vB", [
+    (128, 4, False, 3), (128, 3, False, 3), (128, 2, False, 2), (128, 4, False, 2),  # MSE-only keys
+    (128, 3, True, 2), (128, 1, True, 4),  # asymmetric key / value widths
+    (64, 3, False, 2),  # MSE-only keys on the general kernel
+])
+def test_decode_key_value_bit_allocations(d, kB, kprod, vB):
+    # keys without the QJL sketch (TurboQuant_mse: no sign plane, no residual
+    # norm, no S R q) and keys and values at different widths
+    print(f"decode d={d} keys {kB}{'+1' if kprod else ''} values {vB}", flush=True)
+    _decode_case(2, 8, 2, 600, 640, [600, 257], kB, vB, "bf16", d, fold=kprod, kprod=kprod)
 
 
 @pytest.mark.parametrize("b_total", [2, 3, 4])
