@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--copies", type=int, default=24)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--only", default="", help="comma list of extras to run: quantize,longctx,search,bits")
+    p.add_argument("--only", default="", help="comma list of extras to run: quantize,longctx,search,bits,niah")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one 256 MiB device-to-device copy (the known-size reference for the "
                         "FETCH_SIZE / WRITE_SIZE counters)")
@@ -286,6 +286,93 @@ def bit_allocations(inputs, steps=100, copies=12):
     return {"workload": "single-layer decode shape (batch 1, 32 q / 8 KV heads, d=128, 32768 tokens), same bf16 "
                         "inputs as the headline; quality on KV head 0's 4 query heads against exact fp64 attention",
             "allocations": res}
+
+
+NIAH_KEYS = [("3+1 prod", 3, True), ("4 MSE-only", 4, False), ("2+1 prod", 2, True), ("3 MSE-only", 3, False),
+             ("1+1 prod", 1, True)]
+
+
+def niah_proxy(lengths=(1024, 4096, 16384), cosines=(0.4, 0.5), B=8):
+    """Needle-in-a-haystack proxy: is the needle still the top-scoring token?
+
+    Per (sequence, KV head) one needle key is planted at a seeded position
+    among keys of the headline law (bf16 N(0, 1), 4 channels x10): its
+    direction has cosine `c` with the group's first query head (the rest a
+    random direction orthogonal to it) and its norm is the median key norm of
+    that head. The needle's parameters are unstated in the pages, so this
+    reproduces the trend only. Reported per (length, cosine, key allocation):
+    the fraction of (sequence, KV head) trials whose exact fp64 score argmax
+    is the needle, and the fraction whose libtq score estimate argmax is.
+    """
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+    from synth import device as sdev
+
+    Hq, Hkv, d = 32, 8, 128
+    G = Hq // Hkv
+    Rk_t = dev(synth.haar_orthogonal(d, 7))
+    Sk_t = dev(synth.gaussian_matrix(d, d, 7))
+    Rv_t = dev(synth.haar_orthogonal(d, 7, synth.STREAM_R_V))
+    qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
+    quants = []
+    for name, kb, kprod in NIAH_KEYS:
+        q = tq.tq_quantizer_init(d, kb, tq.TQ_PROD if kprod else tq.TQ_MSE, Rk_t, Sk_t if kprod else None)
+        SR = None
+        if kprod:
+            SR = torch.empty(tq.tq_fold_bytes(d) // 4, dtype=torch.float32, device="cuda")
+            tq.tq_quantizer_fold(q, SR)
+        quants.append((name, kb, kprod, q, SR))
+    rows = []
+    for L in lengths:
+        n = B * Hkv * L
+        V = sdev.kv_with_outliers(B, Hkv, L, d, 4, 10.0, seed=L, stream=21)
+        vp = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, n) // 4, dtype=torch.int32,
+                         device="cuda")
+        vn = torch.empty(n, dtype=torch.int16, device="cuda")
+        tq.tq_quantize_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, V.view(n, d), n, d, vp, vn)
+        vd = tq.make_desc([tq.make_group(qv, 0, vp, vn, None, L)])
+        gen = sdev.generator(L, 22)
+        qry = torch.randn((B, Hq, d), generator=gen, device="cuda").to(torch.bfloat16)
+        for c in cosines:
+            K = sdev.kv_with_outliers(B, Hkv, L, d, 4, 10.0, seed=L, stream=20)
+            pos = torch.randint(0, L, (B, Hkv), generator=gen, device="cuda")
+            qh = qry[:, ::G].float()  # [B, Hkv, d]: each group's first query head
+            qhat = qh / qh.norm(dim=-1, keepdim=True)
+            rnd = torch.randn((B, Hkv, d), generator=gen, device="cuda")
+            rnd -= (rnd * qhat).sum(-1, keepdim=True) * qhat
+            rnd /= rnd.norm(dim=-1, keepdim=True)
+            knorm = K.float().norm(dim=-1).median(dim=-1).values  # [B, Hkv]
+            needle = (c * qhat + math.sqrt(1 - c * c) * rnd) * knorm[..., None]
+            bi = torch.arange(B, device="cuda")[:, None].expand(B, Hkv)
+            gi = torch.arange(Hkv, device="cuda")[None, :].expand(B, Hkv)
+            K[bi, gi, pos] = needle.to(torch.bfloat16)
+            ex = torch.matmul(K.double(), qh.double()[..., None])[..., 0]  # [B, Hkv, L] exact scores
+            exact_hit = (ex.argmax(dim=-1) == pos).float().mean().item()
+            for name, kb, kprod, q, _ in quants:
+                kp = torch.empty(tq.tq_packed_bytes(d, kb, tq.TQ_PROD if kprod else tq.TQ_MSE, tq.TQ_LAYOUT_KEYS, n)
+                                 // 4, dtype=torch.int32, device="cuda")
+                kn = torch.empty(n, dtype=torch.int16, device="cuda")
+                kr = torch.empty(n, dtype=torch.int16, device="cuda") if kprod else None
+                tq.tq_quantize_kv(q, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, K.view(n, d), n, d, kp, kn, kr)
+                kd = tq.make_desc([tq.make_group(q, 0, kp, kn, kr, L)])
+                wsb = tq.tq_decode_workspace_bytes(kd, vd, B, Hq, Hkv, L)
+                ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+                out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+                sc = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+                tq.tq_decode_attn(kd, vd, qry, tq.TQ_BF16, B, Hq, Hkv, L, None, 1 / math.sqrt(d), out, sc, ws, wsb)
+                torch.cuda.synchronize()
+                hit = (sc[:, ::G].argmax(dim=-1) == pos).float().mean().item()
+                rows.append({"seq_len": L, "needle_cosine": c, "keys": name, "exact_top1": round(exact_hit, 4),
+                             "libtq_top1": round(hit, 4)})
+                log(f"niah proxy {rows[-1]}")
+            del K, ex
+        del V, vp, vn
+        torch.cuda.empty_cache()
+    return {"workload": f"{B} sequences x 8 KV heads per length, 32 q heads, d=128, values 3-bit MSE; one needle "
+                        "per (sequence, KV head) at a seeded position, scored against the group's first query head",
+            "rows": rows}
 
 
 def _hip_runtime():
@@ -660,6 +747,11 @@ def main():
             except Exception as e:  # an extra that fails is reported, not hidden
                 extras[name] = {"error": repr(e)}
             log(f"{name}: {extras[name]}")
+        if not only or "niah" in only:
+            try:
+                extras["niah_proxy"] = niah_proxy()
+            except Exception as e:
+                extras["niah_proxy"] = {"error": repr(e)}
         if not only or "bits" in only:
             try:
                 extras["bit_allocations"] = bit_allocations(main_res["oracle_inputs"])
