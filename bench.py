@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--copies", type=int, default=24)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--only", default="", help="comma list of extras to run: quantize,longctx,search,bits,niah")
+    p.add_argument("--only", default="", help="comma list of extras to run: quantize,longctx,search,bits,niah,append")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one 256 MiB device-to-device copy (the known-size reference for the "
                         "FETCH_SIZE / WRITE_SIZE counters)")
@@ -286,6 +286,49 @@ def bit_allocations(inputs, steps=100, copies=12):
     return {"workload": "single-layer decode shape (batch 1, 32 q / 8 KV heads, d=128, 32768 tokens), same bf16 "
                         "inputs as the headline; quality on KV head 0's 4 query heads against exact fp64 attention",
             "allocations": res}
+
+
+def append_step(steps=200):
+    """Latency of appending one decoded token per (sequence, KV head) to the cache.
+
+    Batch 64 x 8 KV heads, d = 128 (the long-context decode's sequences, one
+    new token each): K as 3+1-bit prod and V as 3-bit MSE, each one
+    tq_append_kv call writing 512 rows of a 4096-token-per-head cache; the
+    two calls of a step are captured into one graph with the step's rows
+    advancing by one token per step.
+    """
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+    from synth import device as sdev
+
+    B, Hkv, d, T = 64, 8, 128, 4096
+    Rk_t, Sk_t = dev(synth.haar_orthogonal(d, 5)), dev(synth.gaussian_matrix(d, d, 5))
+    Rv_t = dev(synth.haar_orthogonal(d, 5, synth.STREAM_R_V))
+    qk = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, Rk_t, Sk_t)
+    qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
+    C = B * Hkv * T
+    kp = torch.zeros(tq.tq_packed_bytes(d, 3, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, C) // 4, dtype=torch.int32, device="cuda")
+    vp = torch.zeros(tq.tq_packed_bytes(d, 3, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, C) // 4, dtype=torch.int32,
+                     device="cuda")
+    kn, kr, vn = (torch.zeros(C, dtype=torch.int16, device="cuda") for _ in range(3))
+    xk = sdev.kv_with_outliers(1, Hkv, B, d, 4, 10.0, seed=5, stream=31).view(B * Hkv, d)
+    xv = sdev.kv_with_outliers(1, Hkv, B, d, 4, 10.0, seed=5, stream=32).view(B * Hkv, d)
+    base = torch.arange(B * Hkv, device="cuda", dtype=torch.int64) * T
+    rows = [base + (1000 + i) for i in range(steps)]  # token 1000 + i of every (sequence, head)
+    n = B * Hkv
+
+    def call(i):
+        r = rows[i % len(rows)]
+        tq.tq_append_kv(qk, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, xk, n, d, r, C, kp, kn, kr)
+        tq.tq_append_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, xv, n, d, r, C, vp, vn)
+
+    ms, _ = graph_ms(call, steps)
+    return {"us_per_step": round(ms * 1e3, 3), "vectors_per_step": 2 * n,
+            "vectors_per_s": round(2 * n / ms * 1e3, 1),
+            "workload": "one new token per (sequence, KV head): batch 64 x 8 KV heads, d=128, K 3+1-bit prod and "
+                        "V 3-bit MSE appended into a 4096-token-per-head cache (two tq_append_kv calls per step)"}
 
 
 NIAH_KEYS = [("3+1 prod", 3, True), ("4 MSE-only", 4, False), ("2+1 prod", 2, True), ("3 MSE-only", 3, False),
@@ -747,6 +790,12 @@ def main():
             except Exception as e:  # an extra that fails is reported, not hidden
                 extras[name] = {"error": repr(e)}
             log(f"{name}: {extras[name]}")
+        if not only or "append" in only:
+            try:
+                extras["append_step"] = append_step()
+            except Exception as e:
+                extras["append_step"] = {"error": repr(e)}
+            log(f"append_step: {extras['append_step']}")
         if not only or "niah" in only:
             try:
                 extras["niah_proxy"] = niah_proxy()

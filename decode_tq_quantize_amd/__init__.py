@@ -32,7 +32,7 @@ TQ_MAX_GROUPS = 4
 
 EXPORTS = [
     "tq_build_codebook", "tq_quantizer_init", "tq_packed_bytes", "tq_status_string",
-    "tq_quantize_kv", "tq_decode_workspace_bytes", "tq_decode_attn",
+    "tq_quantize_kv", "tq_append_kv", "tq_decode_workspace_bytes", "tq_decode_attn",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_fold_bytes", "tq_fold_qjl",
 ]
 
@@ -84,6 +84,9 @@ def lib() -> ctypes.CDLL:
         L.tq_quantize_kv.argtypes = [POINTER(tq_quantizer), c_int, c_int, c_void_p, c_int64, c_int64,
                                      c_void_p, c_void_p, c_void_p, c_void_p]
         L.tq_quantize_kv.restype = c_int
+        L.tq_append_kv.argtypes = [POINTER(tq_quantizer), c_int, c_int, c_void_p, c_int64, c_int64, c_void_p,
+                                   c_int64, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.tq_append_kv.restype = c_int
         L.tq_decode_workspace_bytes.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_int, c_int, c_int, c_int]
         L.tq_decode_workspace_bytes.restype = c_size_t
         L.tq_decode_attn.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_void_p, c_int, c_int, c_int, c_int,
@@ -171,6 +174,12 @@ def tq_quantize_kv(q: tq_quantizer, layout: int, in_dtype: int, x, n: int, x_str
                    packed, norm, rnorm=None, stream=None) -> None:
     _check(lib().tq_quantize_kv(ctypes.byref(q), layout, in_dtype, _ptr(x), n, x_stride_elems, _ptr(packed),
                                 _ptr(norm), _ptr(rnorm), _stream(stream)), "tq_quantize_kv")
+
+
+def tq_append_kv(q: tq_quantizer, layout: int, in_dtype: int, x, n: int, x_stride_elems: int, rows,
+                 cache_rows: int, packed, norm, rnorm=None, stream=None) -> None:
+    _check(lib().tq_append_kv(ctypes.byref(q), layout, in_dtype, _ptr(x), n, x_stride_elems, _ptr(rows),
+                              cache_rows, _ptr(packed), _ptr(norm), _ptr(rnorm), _stream(stream)), "tq_append_kv")
 
 
 def make_group(q: tq_quantizer, ch_offset: int, packed, norm, rnorm, seq_stride: int) -> tq_group:

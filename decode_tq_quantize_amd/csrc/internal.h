@@ -15,7 +15,8 @@ constexpr int kValuesTile = 32;
 inline int planes_of(const tq_quantizer& q) { return q.mse_bits + (q.variant == TQ_PROD ? 1 : 0); }
 
 hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
-                           int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s);
+                           int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s,
+                           const int64_t* rows = nullptr, int64_t cache_rows = 0);
 
 // Matrix-core quantiser for 128-channel vectors (quantize_mfma.hip): rows
 // 16-byte aligned.

@@ -10,7 +10,10 @@
 // coordinate-major; each d x d product is computed as a tile GEMM in fp32
 // FMA (fp32 accumulation, fixed summation order j = 0..d-1) with the matrix
 // streamed through LDS in 128 x 32 chunks. Codes, signs and norms are then
-// packed into the requested layout with one word per thread.
+// packed into the requested layout with one word per thread. The same kernel
+// serves appends: each vector is then written to a caller-given cache row
+// (one token per sequence and head during decoding, or the rows of a paged
+// block), keys as whole words, values as one bit per tile word.
 #include "device_common.h"
 #include "internal.h"
 
@@ -18,8 +21,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kIC = 128;       // output coordinates per chunk (one per thread column)
-constexpr int kJC = 32;        // input coordinates per chunk
 constexpr int kMtStride = kIC + 1;
+// Input coordinates per chunk of the matrix staged in LDS: small tiles (few
+// vectors, latency-bound) stage 128 columns per round, large tiles 32.
+template <int TV>
+constexpr int jc_of() { return TV <= 4 ? 128 : 32; }
 
 struct QArgs {
   const void* x;
@@ -37,6 +43,8 @@ struct QArgs {
   uint32_t* packed;
   uint16_t* norm;
   uint16_t* rnorm;
+  const int64_t* rows;  // append: cache row of each vector (null: vector i is row i)
+  int64_t cache_rows;
 };
 
 // Out[j][v] = sum_k M[j][k] In[k][v] for the TV vectors of the tile (arrays
@@ -44,6 +52,7 @@ struct QArgs {
 // i0 + ii of vectors vh*TV/2 .. vh*TV/2 + TV/2 - 1.
 template <int TV>
 __device__ void matvec_tile(const float* __restrict__ M, int d, const float* In, float* Out, float* Mt) {
+  constexpr int kJC = jc_of<TV>();
   const int tid = threadIdx.x;
   const int ii = tid % kIC;
   const int vh = tid / kIC;
@@ -54,14 +63,33 @@ __device__ void matvec_tile(const float* __restrict__ M, int d, const float* In,
     for (int k = 0; k < VH; ++k) acc[k] = 0.f;
     for (int j0 = 0; j0 < d; j0 += kJC) {
       __syncthreads();
-      for (int e = tid; e < kIC * kJC; e += kThreads) {
-        const int r = e / kJC, jj = e % kJC;
-        const int i = i0 + r;
-        Mt[jj * kMtStride + r] = (i < d) ? M[(int64_t)i * d + j0 + jj] : 0.f;
+      // (d is a multiple of 32: a 128-column chunk may run past d, a 32-column
+      // one never does)
+      const int jn = min(kJC, d - j0);
+      // four columns per load, every load of the chunk issued before any
+      // store (addresses clamped into the matrix, out-of-range values zeroed)
+      constexpr int kLoads = kIC * kJC / 4 / kThreads;
+      float4 mv[kLoads];
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) {
+        const int e4 = tid + u * kThreads;
+        const int r = e4 / (kJC / 4), c = 4 * (e4 % (kJC / 4));
+        const int i = min(i0 + r, d - 1), cc = min(c, jn - 4);
+        mv[u] = *reinterpret_cast<const float4*>(M + (int64_t)i * d + j0 + cc);
+      }
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) {
+        const int e4 = tid + u * kThreads;
+        const int r = e4 / (kJC / 4), c = 4 * (e4 % (kJC / 4));
+        const bool ok = i0 + r < d && c < jn;
+        Mt[(c + 0) * kMtStride + r] = ok ? mv[u].x : 0.f;
+        Mt[(c + 1) * kMtStride + r] = ok ? mv[u].y : 0.f;
+        Mt[(c + 2) * kMtStride + r] = ok ? mv[u].z : 0.f;
+        Mt[(c + 3) * kMtStride + r] = ok ? mv[u].w : 0.f;
       }
       __syncthreads();
       if (i0 + ii < d) {
-        for (int jj = 0; jj < kJC; ++jj) {
+        for (int jj = 0; jj < jn; ++jj) {
           const float m = Mt[jj * kMtStride + ii];
           const float* in = In + (j0 + jj) * TV + vh * VH;
 #pragma unroll
@@ -84,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QArgs a) {
   __shared__ float cent[TQ_MAX_LEVELS], thr[TQ_MAX_LEVELS];
   const int d = a.d;
   float* Mt = smem;
-  float* In = Mt + kJC * kMtStride;
+  float* In = Mt + jc_of<TV>() * kMtStride;
   float* Out = In + d * TV;
   uint8_t* C = reinterpret_cast<uint8_t*>(Out + d * TV);
   const int tid = threadIdx.x, lane = tid % tqd::kWave, wv = tid / tqd::kWave;
@@ -141,6 +169,52 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QArgs a) {
   }
   // 6. pack
   const int P = a.B + a.prod;
+  if (a.rows) {
+    // append: every vector goes to its own cache row. A key row owns its
+    // words; a value row owns one bit of each of its tile's words, set or
+    // cleared atomically (rows of one call are distinct, so the updates of a
+    // word commute). Rows outside the cache are skipped.
+    if (a.layout == TQ_LAYOUT_KEYS) {
+      const int G = d / 32;
+      for (int e = tid; e < TV * G * P; e += kThreads) {
+        const int p = e % P, g = (e / P) % G, v = e / (P * G);
+        const int64_t gv = v0 + v;
+        if (gv >= a.n) continue;
+        const int64_t row = a.rows[gv];
+        if (row < 0 || row >= a.cache_rows) continue;
+        const int sh = p < a.B ? p : 4;
+        uint32_t w = 0;
+        for (int i = 0; i < 32; ++i) w |= (uint32_t)((C[(32 * g + i) * TV + v] >> sh) & 1) << i;
+        const int64_t tile = row / tqk::kKeysTile;
+        const int t = (int)(row % tqk::kKeysTile);
+        a.packed[((tile * G + g) * tqk::kKeysTile + t) * P + p] = w;
+      }
+    } else {
+      for (int e = tid; e < TV * d * P; e += kThreads) {
+        const int p = e % P, j = (e / P) % d, v = e / (P * d);
+        const int64_t gv = v0 + v;
+        if (gv >= a.n) continue;
+        const int64_t row = a.rows[gv];
+        if (row < 0 || row >= a.cache_rows) continue;
+        const int sh = p < a.B ? p : 4;
+        const uint32_t bit = 1u << (uint32_t)(row % tqk::kValuesTile);
+        uint32_t* wp = a.packed + ((row / tqk::kValuesTile) * d + j) * P + p;
+        if ((C[j * TV + v] >> sh) & 1)
+          atomicOr(wp, bit);
+        else
+          atomicAnd(wp, ~bit);
+      }
+    }
+    for (int v = tid; v < TV; v += kThreads) {
+      const int64_t gv = v0 + v;
+      if (gv >= a.n) continue;
+      const int64_t row = a.rows[gv];
+      if (row < 0 || row >= a.cache_rows) continue;
+      a.norm[row] = tqd::f32_to_half_bits(nrm[v]);
+      if (a.prod) a.rnorm[row] = tqd::f32_to_half_bits(rho[v]);
+    }
+    return;
+  }
   if (a.layout == TQ_LAYOUT_KEYS) {
     const int G = d / 32;
     const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
@@ -179,7 +253,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QArgs a) {
   }
 }
 
-size_t lds_bytes(int d, int TV) { return (size_t)(kJC * kMtStride + 2 * d * TV) * 4 + (size_t)d * TV; }
+size_t lds_bytes(int d, int TV) {
+  const int jc = TV <= 4 ? 128 : 32;  // jc_of<TV>()
+  return (size_t)(jc * kMtStride + 2 * d * TV) * 4 + (size_t)d * TV;
+}
 
 template <int TV>
 hipError_t launch_tv(const QArgs& a, int64_t nround, hipStream_t s) {
@@ -197,8 +274,11 @@ hipError_t launch_tv(const QArgs& a, int64_t nround, hipStream_t s) {
 namespace tqk {
 
 hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
-                           int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s) {
+                           int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s,
+                           const int64_t* rows, int64_t cache_rows) {
   QArgs a{};
+  a.rows = rows;
+  a.cache_rows = cache_rows;
   a.x = x;
   a.n = n;
   a.stride = stride;
@@ -214,9 +294,20 @@ hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt,
   a.packed = static_cast<uint32_t*>(packed);
   a.norm = norm;
   a.rnorm = rnorm;
-  const int tile = layout == TQ_LAYOUT_KEYS ? kKeysTile : kValuesTile;
+  // (an append writes rows one by one: no tile of the output to round to)
+  const int tile = rows ? 1 : (layout == TQ_LAYOUT_KEYS ? kKeysTile : kValuesTile);
   const int64_t nround = (n + tile - 1) / tile * tile;
   const size_t limit = 150 * 1024;
+  if (rows) {
+    // an append is a few vectors per sequence: small tiles, so that the
+    // vectors spread over the compute units (about 256 workgroups or more)
+    auto fits = [&](int tv) { return n >= 256 * (int64_t)tv && lds_bytes(q.d, tv) <= limit; };
+    if (fits(32)) return launch_tv<32>(a, nround, s);
+    if (fits(16)) return launch_tv<16>(a, nround, s);
+    if (fits(8)) return launch_tv<8>(a, nround, s);
+    if (fits(4)) return launch_tv<4>(a, nround, s);
+    return launch_tv<2>(a, nround, s);
+  }
   if (layout == TQ_LAYOUT_VALUES || lds_bytes(q.d, 32) <= limit) return launch_tv<32>(a, nround, s);
   if (lds_bytes(q.d, 16) <= limit) return launch_tv<16>(a, nround, s);
   if (lds_bytes(q.d, 8) <= limit) return launch_tv<8>(a, nround, s);

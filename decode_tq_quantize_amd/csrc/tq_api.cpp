@@ -141,6 +141,25 @@ extern "C" int tq_quantize_kv(const tq_quantizer* q, tq_layout layout, tq_dtype 
                                          static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int tq_append_kv(const tq_quantizer* q, tq_layout layout, tq_dtype in_dtype, const void* x, int64_t n,
+                            int64_t x_stride_elems, const int64_t* rows, int64_t cache_rows, void* packed,
+                            uint16_t* norm, uint16_t* rnorm, void* stream) {
+  int rc = check_quantizer(q);
+  if (rc != TQ_OK) return rc;
+  if (layout != TQ_LAYOUT_KEYS && layout != TQ_LAYOUT_VALUES) return TQ_ERR_INVALID_ARG;
+  if (in_dtype != TQ_F32 && in_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (n < 0 || x_stride_elems < q->d || cache_rows <= 0) return TQ_ERR_INVALID_ARG;
+  if (layout == TQ_LAYOUT_VALUES && q->d > 256) return TQ_ERR_UNSUPPORTED;
+  if (n == 0) return TQ_OK;
+  if (!x || !rows || !packed || !norm || (q->variant == TQ_PROD && !rnorm)) return TQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(norm) || (rnorm && !aligned16(rnorm)) ||
+      reinterpret_cast<uintptr_t>(rows) % alignof(int64_t) != 0)
+    return TQ_ERR_MISALIGNED;
+  uint16_t* rn = q->variant == TQ_PROD ? rnorm : nullptr;
+  return hip_status(tqk::launch_quantize(*q, layout, in_dtype, x, n, x_stride_elems, packed, norm, rn,
+                                         static_cast<hipStream_t>(stream), rows, cache_rows));
+}
+
 extern "C" size_t tq_decode_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq, int Hkv,
                                             int T_max) {
   int D = 0, Dv = 0;

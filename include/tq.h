@@ -168,6 +168,26 @@ int tq_quantize_kv(const tq_quantizer* q, tq_layout layout, tq_dtype in_dtype,
                    const void* x, int64_t n, int64_t x_stride_elems, void* packed,
                    uint16_t* norm, uint16_t* rnorm, void* stream);
 
+/* Append: quantise n vectors exactly as tq_quantize_kv does (riverfrot
+ * sections 4.1-4.3; the pages quantise each generated token online, section
+ * 2.4) and write vector i into row rows[i] of an existing cache instead of
+ * row i: one new token per (sequence, KV head) during decoding, or the rows
+ * of a paged block. `rows` (device, int64 [n], 8-byte aligned) holds
+ * distinct rows in [0, cache_rows); a row outside that range is skipped, and
+ * two equal rows leave either vector's bits. `packed`, `norm` and `rnorm`
+ * are the cache's own arrays over its cache_rows rows (packed holds
+ * tq_packed_bytes(d, bits, variant, layout, cache_rows) bytes and starts at
+ * a tile boundary). A key row owns its words and is overwritten whole; a
+ * value row owns one bit of each word of its 32-row tile, and only those
+ * bits change (set or cleared atomically), so appends into rows that share a
+ * tile may run in one call. Other rows are left as they are. Errors as for
+ * tq_quantize_kv, plus INVALID_ARG for cache_rows <= 0 or a null `rows`
+ * with n > 0. */
+int tq_append_kv(const tq_quantizer* q, tq_layout layout, tq_dtype in_dtype,
+                 const void* x, int64_t n, int64_t x_stride_elems, const int64_t* rows,
+                 int64_t cache_rows, void* packed, uint16_t* norm, uint16_t* rnorm,
+                 void* stream);
+
 /* Workspace bytes tq_decode_attn needs for these shapes (0 on bad arguments). */
 size_t tq_decode_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq,
                                  int Hkv, int T_max);

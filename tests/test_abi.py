@@ -148,6 +148,29 @@ def test_quantize_validation_paths():
     assert call(big, layout=tq.TQ_LAYOUT_VALUES, stride=512) == tq.TQ_ERR_UNSUPPORTED
 
 
+def test_append_validation_paths():
+    L = tq.lib()
+
+    def call(q, layout=tq.TQ_LAYOUT_KEYS, dt=tq.TQ_F32, x=FAKE, n=10, stride=128, rows=FAKE, cache_rows=64,
+             p=FAKE, nrm=FAKE, rn=FAKE):
+        return L.tq_append_kv(ctypes.byref(q), layout, dt, x, n, stride, rows, cache_rows, p, nrm, rn, None)
+
+    q = _q()
+    assert call(q, rows=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(q, x=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(q, rn=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(q, cache_rows=0) == tq.TQ_ERR_INVALID_ARG
+    assert call(q, n=-1) == tq.TQ_ERR_INVALID_ARG
+    assert call(q, stride=64) == tq.TQ_ERR_INVALID_ARG
+    assert call(q, rows=FAKE + 4) == tq.TQ_ERR_MISALIGNED
+    assert call(q, p=FAKE + 4) == tq.TQ_ERR_MISALIGNED
+    assert call(q, layout=5) == tq.TQ_ERR_INVALID_ARG
+    assert call(q, dt=7) == tq.TQ_ERR_INVALID_ARG
+    assert call(q, n=0) == tq.TQ_OK  # nothing to do, nothing launched
+    big = _q(d=512, B=2, variant=tq.TQ_MSE)
+    assert call(big, layout=tq.TQ_LAYOUT_VALUES, stride=512, rn=None) == tq.TQ_ERR_UNSUPPORTED
+
+
 def _desc(groups):
     return tq.make_desc(groups)
 

@@ -111,6 +111,68 @@ def test_quantize_matches_oracle(d, B, prod, lay, N, dt):
     assert not pidx[N:].any() and (pz is None or not pz[N:].any())
 
 
+APPEND_CASES = [
+    (128, 3, True, "keys", "bf16"),
+    (128, 3, False, "values", "bf16"),
+    (128, 2, True, "values", "f32"),
+    (96, 1, True, "keys", "f32"),
+    (32, 2, False, "values", "bf16"),
+    (256, 4, True, "keys", "f32"),
+]
+
+
+@pytest.mark.parametrize("d,B,prod,lay,dt", APPEND_CASES)
+def test_append_writes_only_its_rows(d, B, prod, lay, dt):
+    # vectors appended into rows of an existing cache (unsorted, not tile
+    # aligned, sharing tiles, the first and last row, two rows outside the
+    # cache): the appended rows decode to the oracle's codes, every other
+    # bit and norm of the cache is unchanged
+    print(f"append d={d} B={B} prod={prod} {lay} {dt}", flush=True)
+    C, n_in = 203, 61
+    gq = GpuQuantizer(d, B, prod, seed=d + 3 * B)
+    layout = tq.TQ_LAYOUT_KEYS if lay == "keys" else tq.TQ_LAYOUT_VALUES
+    g = synth.rng(d + B, 9)
+    rows = np.concatenate([[C - 1, 0], g.choice(np.arange(1, C - 1), n_in - 2, replace=False)]).astype(np.int64)
+    g.shuffle(rows)
+    rows_all = np.concatenate([rows[:30], [-1], rows[30:], [C]]).astype(np.int64)  # two rows outside the cache
+    n = rows_all.size
+    x = synth.unit_gaussian(n, d, 21) * g.lognormal(0, 0.5, (n, 1)).astype(np.float32)
+    x[5] = 0.0
+    if dt == "bf16":
+        x = synth.bf16_bits_to_f32(synth.to_bf16_bits(x))
+    nbytes = tq.tq_packed_bytes(d, B, _variant(prod), layout, C)
+    w0 = g.integers(0, 2**32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    n0 = g.integers(0, 2**16, C, dtype=np.uint64).astype(np.uint16)
+    r0 = g.integers(0, 2**16, C, dtype=np.uint64).astype(np.uint16)
+    packed = torch_dev(w0.view(np.int32))
+    norm = torch_dev(n0.view(np.int16))
+    rnorm = torch_dev(r0.view(np.int16)) if prod else None
+    x_t = torch_dev(x, torch.bfloat16 if dt == "bf16" else torch.float32)
+    tq.tq_append_kv(gq.q, layout, tq.TQ_BF16 if dt == "bf16" else tq.TQ_F32, x_t, n, d, torch_dev(rows_all), C,
+                    packed, norm, rnorm)
+    torch.cuda.synchronize()
+    tile = otq.KEYS_TILE if lay == "keys" else otq.VALUES_TILE
+    n_round = -(-C // tile) * tile
+    w1 = to_np_u32(packed)
+    idx0, z0 = otq.unpack(w0, n_round, d, B, prod, lay)
+    idx1, z1 = otq.unpack(w1, n_round, d, B, prod, lay)
+    other = np.ones(n_round, bool)
+    other[rows] = False
+    assert np.array_equal(idx1[other], idx0[other])
+    if prod:
+        assert np.array_equal(z1[other], z0[other])
+    n1 = to_np_f16(norm).view(np.uint16)
+    assert np.array_equal(n1[other[:C]], n0[other[:C]])
+    r1 = to_np_f16(rnorm).view(np.uint16) if prod else None
+    if prod:
+        assert np.array_equal(r1[other[:C]], r0[other[:C]])
+    keep = (rows_all >= 0) & (rows_all < C)
+    codes = otq.quantize(x[keep].astype(np.float64), gq.oq)
+    rk = rows_all[keep]
+    assert_codes_match(idx1[rk], None if not prod else z1[rk], n1[rk].view(np.float16),
+                       None if not prod else r1[rk].view(np.float16), codes, gq.oq)
+
+
 def test_quantize_strided_channel_group():
     # quantise channels 32..127 of 128-channel rows (a channel group)
     N, D = 200, 128
