@@ -105,6 +105,17 @@ __device__ void matvec_tile(const float* __restrict__ M, int d, const float* In,
   __syncthreads();
 }
 
+// Key-layout word of vector v, coordinate word g, code bit sh (4: the sign)
+// for the half-wave this lane is in: lane i of the half takes coordinate
+// 32 g + i, a ballot gathers the 32 bits, and the half's word is returned to
+// all its lanes. Every lane of the wave must call it (a wave-wide ballot).
+__device__ __forceinline__ uint32_t key_word(const uint8_t* C, int TV, int v, int g, int sh, int lane) {
+  const int i = lane & 31;
+  const bool bit = (C[(32 * g + i) * TV + v] >> sh) & 1;
+  const uint64_t m = __ballot(bit);
+  return (uint32_t)(m >> (32 * (lane >> 5)));
+}
+
 template <int TV>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QArgs a) {
   extern __shared__ float smem[];
@@ -176,15 +187,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QArgs a) {
     // word commute). Rows outside the cache are skipped.
     if (a.layout == TQ_LAYOUT_KEYS) {
       const int G = d / 32;
-      for (int e = tid; e < TV * G * P; e += kThreads) {
+      for (int w0 = 2 * wv; w0 < TV * G * P; w0 += 2 * (kThreads / tqd::kWave)) {
+        const int e = w0 + (lane >> 5);
         const int p = e % P, g = (e / P) % G, v = e / (P * G);
         const int64_t gv = v0 + v;
-        if (gv >= a.n) continue;
+        const uint32_t w = key_word(C, TV, v, g, p < a.B ? p : 4, lane);
+        if ((lane & 31) || gv >= a.n) continue;
         const int64_t row = a.rows[gv];
         if (row < 0 || row >= a.cache_rows) continue;
-        const int sh = p < a.B ? p : 4;
-        uint32_t w = 0;
-        for (int i = 0; i < 32; ++i) w |= (uint32_t)((C[(32 * g + i) * TV + v] >> sh) & 1) << i;
         const int64_t tile = row / tqk::kKeysTile;
         const int t = (int)(row % tqk::kKeysTile);
         a.packed[((tile * G + g) * tqk::kKeysTile + t) * P + p] = w;
@@ -218,15 +228,15 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QArgs a) {
   if (a.layout == TQ_LAYOUT_KEYS) {
     const int G = d / 32;
     const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
-    for (int e = tid; e < TV * G * P; e += kThreads) {
+    for (int w0 = 2 * wv; w0 < TV * G * P; w0 += 2 * (kThreads / tqd::kWave)) {
+      const int e = w0 + (lane >> 5);
       const int p = e % P, g = (e / P) % G, v = e / (P * G);
       const int64_t gv = v0 + v;
-      if (gv >= nround) continue;
-      uint32_t w = 0;
-      if (gv < a.n) {
-        const int sh = p < a.B ? p : 4;
-        for (int i = 0; i < 32; ++i) w |= (uint32_t)((C[(32 * g + i) * TV + v] >> sh) & 1) << i;
-      }
+      // (padding vectors of the last tile pack to zero words; the ballot
+      // itself runs on every lane)
+      uint32_t w = key_word(C, TV, v, g, p < a.B ? p : 4, lane);
+      if (gv >= a.n) w = 0u;
+      if ((lane & 31) || gv >= nround) continue;
       const int64_t tile = gv / tqk::kKeysTile;
       const int t = (int)(gv % tqk::kKeysTile);
       a.packed[((tile * G + g) * tqk::kKeysTile + t) * P + p] = w;
