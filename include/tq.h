@@ -174,7 +174,8 @@ int tq_quantize_kv(const tq_quantizer* q, tq_layout layout, tq_dtype in_dtype,
  * row i: one new token per (sequence, KV head) during decoding, or the rows
  * of a paged block. `rows` (device, int64 [n], 8-byte aligned) holds
  * distinct rows in [0, cache_rows); a row outside that range is skipped, and
- * two equal rows leave either vector's bits. `packed`, `norm` and `rnorm`
+ * two equal rows leave that row with an unspecified mix of the two vectors'
+ * bits and norms. `packed`, `norm` and `rnorm`
  * are the cache's own arrays over its cache_rows rows (packed holds
  * tq_packed_bytes(d, bits, variant, layout, cache_rows) bytes and starts at
  * a tile boundary). A key row owns its words and is overwritten whole; a
