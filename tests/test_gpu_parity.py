@@ -112,29 +112,33 @@ def test_quantize_matches_oracle(d, B, prod, lay, N, dt):
 
 
 APPEND_CASES = [
-    (128, 3, True, "keys", "bf16"),
-    (128, 3, False, "values", "bf16"),
-    (128, 2, True, "values", "f32"),
-    (96, 1, True, "keys", "f32"),
-    (32, 2, False, "values", "bf16"),
-    (256, 4, True, "keys", "f32"),
+    # d, B, prod, layout, dtype, cache rows, appended rows (the count picks the
+    # kernel's tile: 2 vectors per workgroup below 1024, up to 32 from 8192)
+    (128, 3, True, "keys", "bf16", 203, 61),
+    (128, 3, False, "values", "bf16", 203, 61),
+    (128, 2, True, "values", "f32", 203, 61),
+    (96, 1, True, "keys", "f32", 203, 61),
+    (32, 2, False, "values", "bf16", 203, 61),
+    (256, 4, True, "keys", "f32", 203, 61),
+    (128, 3, True, "keys", "bf16", 6000, 4300),
+    (128, 3, False, "values", "f32", 12000, 9000),
+    (1536, 3, True, "keys", "f32", 700, 300),
 ]
 
 
-@pytest.mark.parametrize("d,B,prod,lay,dt", APPEND_CASES)
-def test_append_writes_only_its_rows(d, B, prod, lay, dt):
+@pytest.mark.parametrize("d,B,prod,lay,dt,C,n_in", APPEND_CASES)
+def test_append_writes_only_its_rows(d, B, prod, lay, dt, C, n_in):
     # vectors appended into rows of an existing cache (unsorted, not tile
     # aligned, sharing tiles, the first and last row, two rows outside the
     # cache): the appended rows decode to the oracle's codes, every other
     # bit and norm of the cache is unchanged
-    print(f"append d={d} B={B} prod={prod} {lay} {dt}", flush=True)
-    C, n_in = 203, 61
+    print(f"append d={d} B={B} prod={prod} {lay} {dt} C={C} n={n_in}", flush=True)
     gq = GpuQuantizer(d, B, prod, seed=d + 3 * B)
     layout = tq.TQ_LAYOUT_KEYS if lay == "keys" else tq.TQ_LAYOUT_VALUES
     g = synth.rng(d + B, 9)
     rows = np.concatenate([[C - 1, 0], g.choice(np.arange(1, C - 1), n_in - 2, replace=False)]).astype(np.int64)
     g.shuffle(rows)
-    rows_all = np.concatenate([rows[:30], [-1], rows[30:], [C]]).astype(np.int64)  # two rows outside the cache
+    rows_all = np.concatenate([rows[:n_in // 2], [-1], rows[n_in // 2:], [C]]).astype(np.int64)  # two outside
     n = rows_all.size
     x = synth.unit_gaussian(n, d, 21) * g.lognormal(0, 0.5, (n, 1)).astype(np.float32)
     x[5] = 0.0
