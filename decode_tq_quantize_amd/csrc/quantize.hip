@@ -53,53 +53,63 @@ struct QArgs {
 template <int TV>
 __device__ void matvec_tile(const float* __restrict__ M, int d, const float* In, float* Out, float* Mt) {
   constexpr int kJC = jc_of<TV>();
+  constexpr int kLoads = kIC * kJC / 4 / kThreads;  // 16-byte loads per thread per chunk
   const int tid = threadIdx.x;
   const int ii = tid % kIC;
   const int vh = tid / kIC;
   constexpr int VH = TV / 2;
-  for (int i0 = 0; i0 < d; i0 += kIC) {
-    float acc[VH];
+  // chunks (output rows i0 .. i0 + 127) x (input columns j0 .. j0 + kJC - 1),
+  // walked row block by row block; the next chunk's loads are issued before
+  // the current chunk is multiplied, so they arrive meanwhile. (d is a
+  // multiple of 32: a 128-column chunk may run past d, a 32-column one never
+  // does; addresses are clamped into the matrix and values outside it zeroed.)
+  const int nJ = (d + kJC - 1) / kJC;
+  const int nQ = ((d + kIC - 1) / kIC) * nJ;
+  float4 mv[kLoads];
+  auto load = [&](int q) __attribute__((always_inline)) {
+    const int i0 = (q / nJ) * kIC, j0 = (q % nJ) * kJC, jn = min(kJC, d - j0);
 #pragma unroll
-    for (int k = 0; k < VH; ++k) acc[k] = 0.f;
-    for (int j0 = 0; j0 < d; j0 += kJC) {
-      __syncthreads();
-      // (d is a multiple of 32: a 128-column chunk may run past d, a 32-column
-      // one never does)
-      const int jn = min(kJC, d - j0);
-      // four columns per load, every load of the chunk issued before any
-      // store (addresses clamped into the matrix, out-of-range values zeroed)
-      constexpr int kLoads = kIC * kJC / 4 / kThreads;
-      float4 mv[kLoads];
+    for (int u = 0; u < kLoads; ++u) {
+      const int e4 = tid + u * kThreads;
+      const int r = e4 / (kJC / 4), c = 4 * (e4 % (kJC / 4));
+      const int i = min(i0 + r, d - 1), cc = min(c, jn - 4);
+      mv[u] = *reinterpret_cast<const float4*>(M + (int64_t)i * d + j0 + cc);
+    }
+  };
+  load(0);
+  float acc[VH];
 #pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        const int e4 = tid + u * kThreads;
-        const int r = e4 / (kJC / 4), c = 4 * (e4 % (kJC / 4));
-        const int i = min(i0 + r, d - 1), cc = min(c, jn - 4);
-        mv[u] = *reinterpret_cast<const float4*>(M + (int64_t)i * d + j0 + cc);
-      }
+  for (int k = 0; k < VH; ++k) acc[k] = 0.f;
+  for (int q = 0; q < nQ; ++q) {
+    const int i0 = (q / nJ) * kIC, j0 = (q % nJ) * kJC, jn = min(kJC, d - j0);
+    __syncthreads();  // the previous chunk's products are done with Mt
 #pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        const int e4 = tid + u * kThreads;
-        const int r = e4 / (kJC / 4), c = 4 * (e4 % (kJC / 4));
-        const bool ok = i0 + r < d && c < jn;
-        Mt[(c + 0) * kMtStride + r] = ok ? mv[u].x : 0.f;
-        Mt[(c + 1) * kMtStride + r] = ok ? mv[u].y : 0.f;
-        Mt[(c + 2) * kMtStride + r] = ok ? mv[u].z : 0.f;
-        Mt[(c + 3) * kMtStride + r] = ok ? mv[u].w : 0.f;
-      }
-      __syncthreads();
-      if (i0 + ii < d) {
-        for (int jj = 0; jj < jn; ++jj) {
-          const float m = Mt[jj * kMtStride + ii];
-          const float* in = In + (j0 + jj) * TV + vh * VH;
+    for (int u = 0; u < kLoads; ++u) {
+      const int e4 = tid + u * kThreads;
+      const int r = e4 / (kJC / 4), c = 4 * (e4 % (kJC / 4));
+      const bool ok = i0 + r < d && c < jn;
+      Mt[(c + 0) * kMtStride + r] = ok ? mv[u].x : 0.f;
+      Mt[(c + 1) * kMtStride + r] = ok ? mv[u].y : 0.f;
+      Mt[(c + 2) * kMtStride + r] = ok ? mv[u].z : 0.f;
+      Mt[(c + 3) * kMtStride + r] = ok ? mv[u].w : 0.f;
+    }
+    __syncthreads();
+    load(min(q + 1, nQ - 1));  // (the last chunk re-reads itself)
+    if (i0 + ii < d) {
+      for (int jj = 0; jj < jn; ++jj) {
+        const float m = Mt[jj * kMtStride + ii];
+        const float* in = In + (j0 + jj) * TV + vh * VH;
 #pragma unroll
-          for (int k = 0; k < VH; ++k) acc[k] = fmaf(m, in[k], acc[k]);
-        }
+        for (int k = 0; k < VH; ++k) acc[k] = fmaf(m, in[k], acc[k]);
       }
     }
-    if (i0 + ii < d) {
+    if (q % nJ == nJ - 1) {  // row block done
+      if (i0 + ii < d) {
 #pragma unroll
-      for (int k = 0; k < VH; ++k) Out[(i0 + ii) * TV + vh * VH + k] = acc[k];
+        for (int k = 0; k < VH; ++k) Out[(i0 + ii) * TV + vh * VH + k] = acc[k];
+      }
+#pragma unroll
+      for (int k = 0; k < VH; ++k) acc[k] = 0.f;
     }
   }
   __syncthreads();
