@@ -283,9 +283,16 @@ def bit_allocations(inputs, steps=100, copies=12):
         log(f"bit allocation {res[-1]}")
         del cps, ws, scores, kp, vp, kn, vn, kr, SRk
         torch.cuda.empty_cache()
+    # the section 4.5 rule applied to these inputs' median key and value norms
+    kn_med = float(np.median(np.linalg.norm(Kb, axis=1)))
+    vn_med = float(np.median(np.linalg.norm(Vb, axis=1)))
+    cls, kbits, vbits = tq.tq_kv_bit_allocation(kn_med, vn_med)
+    policy = {"median_key_norm": round(kn_med, 3), "median_value_norm": round(vn_med, 3),
+              "ratio": round(kn_med / vn_med, 3), "class": ["uniform", "asymmetric", "mixed"][cls],
+              "key_bits": kbits, "value_bits": vbits}
     return {"workload": "single-layer decode shape (batch 1, 32 q / 8 KV heads, d=128, 32768 tokens), same bf16 "
                         "inputs as the headline; quality on KV head 0's 4 query heads against exact fp64 attention",
-            "allocations": res}
+            "norm_ratio_policy": policy, "allocations": res}
 
 
 def append_step(steps=200):

@@ -27,12 +27,13 @@ TQ_ERR_WORKSPACE = -6
 TQ_MSE, TQ_PROD = 0, 1
 TQ_F32, TQ_BF16 = 0, 1
 TQ_LAYOUT_KEYS, TQ_LAYOUT_VALUES = 0, 1
+TQ_KV_UNIFORM, TQ_KV_ASYMMETRIC, TQ_KV_MIXED = 0, 1, 2
 TQ_MAX_LEVELS = 16
 TQ_MAX_GROUPS = 4
 
 EXPORTS = [
     "tq_build_codebook", "tq_quantizer_init", "tq_packed_bytes", "tq_status_string",
-    "tq_quantize_kv", "tq_append_kv", "tq_decode_workspace_bytes", "tq_decode_attn",
+    "tq_quantize_kv", "tq_append_kv", "tq_decode_workspace_bytes", "tq_decode_attn", "tq_kv_bit_allocation",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_fold_bytes", "tq_fold_qjl",
 ]
 
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.tq_append_kv.argtypes = [POINTER(tq_quantizer), c_int, c_int, c_void_p, c_int64, c_int64, c_void_p,
                                    c_int64, c_void_p, c_void_p, c_void_p, c_void_p]
         L.tq_append_kv.restype = c_int
+        L.tq_kv_bit_allocation.argtypes = [c_double, c_double, POINTER(c_int), POINTER(c_int)]
+        L.tq_kv_bit_allocation.restype = c_int
         L.tq_decode_workspace_bytes.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_int, c_int, c_int, c_int]
         L.tq_decode_workspace_bytes.restype = c_size_t
         L.tq_decode_attn.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_void_p, c_int, c_int, c_int, c_int,
@@ -180,6 +183,14 @@ def tq_append_kv(q: tq_quantizer, layout: int, in_dtype: int, x, n: int, x_strid
                  cache_rows: int, packed, norm, rnorm=None, stream=None) -> None:
     _check(lib().tq_append_kv(ctypes.byref(q), layout, in_dtype, _ptr(x), n, x_stride_elems, _ptr(rows),
                               cache_rows, _ptr(packed), _ptr(norm), _ptr(rnorm), _stream(stream)), "tq_append_kv")
+
+
+def tq_kv_bit_allocation(key_norm: float, value_norm: float) -> tuple[int, int, int]:
+    """(class, key_bits, value_bits) for typical key and value norms."""
+    kb, vb = c_int(0), c_int(0)
+    rc = lib().tq_kv_bit_allocation(float(key_norm), float(value_norm), ctypes.byref(kb), ctypes.byref(vb))
+    _check(min(rc, 0), "tq_kv_bit_allocation")
+    return rc, kb.value, vb.value
 
 
 def make_group(q: tq_quantizer, ch_offset: int, packed, norm, rnorm, seq_stride: int) -> tq_group:

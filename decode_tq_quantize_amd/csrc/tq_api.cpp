@@ -121,6 +121,21 @@ extern "C" size_t tq_packed_bytes(int d, int mse_bits, tq_variant variant, tq_la
   return (size_t)nr * (size_t)P * (size_t)d / 8;
 }
 
+extern "C" int tq_kv_bit_allocation(double key_norm, double value_norm, int* key_bits, int* value_bits) {
+  if (!key_bits || !value_bits) return TQ_ERR_INVALID_ARG;
+  if (!std::isfinite(key_norm) || !std::isfinite(value_norm) || !(key_norm > 0.0) || !(value_norm > 0.0))
+    return TQ_ERR_INVALID_ARG;
+  const double r = key_norm / value_norm;
+  if (r < 10.0) {
+    *key_bits = 3;
+    *value_bits = 3;
+    return TQ_KV_UNIFORM;
+  }
+  *key_bits = 4;
+  *value_bits = 2;
+  return r <= 100.0 ? TQ_KV_ASYMMETRIC : TQ_KV_MIXED;
+}
+
 extern "C" int tq_quantize_kv(const tq_quantizer* q, tq_layout layout, tq_dtype in_dtype, const void* x, int64_t n,
                               int64_t x_stride_elems, void* packed, uint16_t* norm, uint16_t* rnorm, void* stream) {
   int rc = check_quantizer(q);

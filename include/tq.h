@@ -63,6 +63,8 @@ typedef enum {
 typedef enum { TQ_MSE = 0, TQ_PROD = 1 } tq_variant;
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 typedef enum { TQ_LAYOUT_KEYS = 0, TQ_LAYOUT_VALUES = 1 } tq_layout;
+/* Classes of tq_kv_bit_allocation. */
+typedef enum { TQ_KV_UNIFORM = 0, TQ_KV_ASYMMETRIC = 1, TQ_KV_MIXED = 2 } tq_kv_alloc;
 
 #define TQ_MAX_MSE_BITS 4
 #define TQ_MAX_LEVELS 16
@@ -134,6 +136,19 @@ int tq_quantizer_init(tq_quantizer* q, int d, int mse_bits, tq_variant variant,
 /* Bytes of the packed codes of n vectors in `layout`, including the padding
  * of the last tile: ceil(n / tile) * tile * P * d / 8. 0 on bad arguments. */
 size_t tq_packed_bytes(int d, int mse_bits, tq_variant variant, tq_layout layout, int64_t n);
+
+/* Key/value bit widths from the ratio r = key_norm / value_norm of typical
+ * key and value norms (riverfrot section 4.5: a quantised vector's error
+ * scales with its squared norm, so keys with much larger norms need more
+ * bits). Host only. The section's rule: r < 10 -> TQ_KV_UNIFORM, 3-bit keys
+ * and values; 10 <= r <= 60 -> TQ_KV_ASYMMETRIC, 4-bit keys and 2-bit
+ * values; r > 100 -> TQ_KV_MIXED (per channel group, e.g. the outlier
+ * split of tq_kv_desc groups), with 4 and 2 as the base widths. The section
+ * leaves 60 < r <= 100 open; it is read as asymmetric. Widths are total bits
+ * per channel (a 4-bit TurboQuant_prod key is 3 codebook bits + 1 sign).
+ * Returns the class, or INVALID_ARG for a norm that is not finite and
+ * positive or a null output (nothing is written then). */
+int tq_kv_bit_allocation(double key_norm, double value_norm, int* key_bits, int* value_bits);
 
 /* Human-readable text for a tq_status value. */
 const char* tq_status_string(int status);

@@ -389,3 +389,37 @@ def compressed_kv_bytes(layers, kv_heads, seq_len, k_groups, v_groups):
     for (d, B, prod) in list(k_groups) + list(v_groups):
         per_tok += (B + (1 if prod else 0)) * d // 8 + (4 if prod else 2)
     return layers * kv_heads * seq_len * per_tok
+
+
+# ----------------------------------------------------------------------------
+# Key/value bit allocation from the norm ratio (riverfrot post, section 4.5)
+# ----------------------------------------------------------------------------
+
+KV_UNIFORM, KV_ASYMMETRIC, KV_MIXED = 0, 1, 2
+
+
+def kv_norm_sensitivity(key_norm, value_norm):
+    """How much more the keys' quantisation error weighs than the values':
+    the error of a quantised vector scales with its squared norm, so the
+    ratio is (key_norm / value_norm)^2 (section 4.5's "~37,000x" for key
+    norms up to 778 against value norms of 4)."""
+    return (float(key_norm) / float(value_norm)) ** 2
+
+
+def kv_bit_allocation(key_norm, value_norm):
+    """Section 4.5's rule for the K/V norm ratio r = key_norm / value_norm:
+    r < 10 -> uniform 3-bit keys and values; 10 <= r <= 60 -> asymmetric,
+    4-bit keys and 2-bit values; r > 100 -> mixed precision (per channel
+    group). The section leaves 60 < r <= 100 open: read as asymmetric (the
+    next stated threshold is 100). Returns (class, key_bits, value_bits); a
+    mixed allocation keeps 4/2 as the base widths of its channel groups.
+    Parity: the section's own table (pinned in the tests at each band)."""
+    k, v = float(key_norm), float(value_norm)
+    if not (np.isfinite(k) and np.isfinite(v) and k > 0 and v > 0):
+        raise ValueError("norms must be finite and positive")
+    r = k / v
+    if r < 10.0:
+        return KV_UNIFORM, 3, 3
+    if r <= 100.0:
+        return KV_ASYMMETRIC, 4, 2
+    return KV_MIXED, 4, 2

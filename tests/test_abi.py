@@ -171,6 +171,18 @@ def test_append_validation_paths():
     assert call(big, layout=tq.TQ_LAYOUT_VALUES, stride=512, rn=None) == tq.TQ_ERR_UNSUPPORTED
 
 
+def test_kv_bit_allocation_matches_oracle():
+    for r in np.concatenate([np.geomspace(0.01, 1e4, 400), [9.999, 10.0, 60.0, 60.001, 100.0, 100.001]]):
+        for v in (0.5, 3.0, 1000.0):
+            assert tq.tq_kv_bit_allocation(r * v, v) == otq.kv_bit_allocation(r * v, v), (r, v)
+    L = tq.lib()
+    kb, vb = ctypes.c_int(-7), ctypes.c_int(-7)
+    for k, v in [(0.0, 1.0), (1.0, 0.0), (-2.0, 1.0), (float("inf"), 1.0), (1.0, float("nan"))]:
+        assert L.tq_kv_bit_allocation(k, v, ctypes.byref(kb), ctypes.byref(vb)) == tq.TQ_ERR_INVALID_ARG
+    assert (kb.value, vb.value) == (-7, -7)  # nothing written on error
+    assert L.tq_kv_bit_allocation(1.0, 1.0, None, ctypes.byref(vb)) == tq.TQ_ERR_INVALID_ARG
+
+
 def _desc(groups):
     return tq.make_desc(groups)
 

@@ -357,3 +357,29 @@ def test_compressed_size_of_the_long_context_workload():
     assert per == 84
     # ratio to bf16 K and V (2 x 128 x 2 bytes)
     assert 512 / per > 6.0
+
+
+# --------------------------------------------------------------------------
+# key/value bit allocation (riverfrot section 4.5)
+# --------------------------------------------------------------------------
+
+def test_kv_bit_allocation_follows_the_norm_ratio_table():
+    # the section's bands: below 10x uniform 3-bit, 10-60x asymmetric
+    # 4-bit keys / 2-bit values, above 100x mixed precision
+    assert tq.kv_bit_allocation(5.0, 1.0) == (tq.KV_UNIFORM, 3, 3)
+    assert tq.kv_bit_allocation(9.99, 1.0)[0] == tq.KV_UNIFORM
+    assert tq.kv_bit_allocation(10.0, 1.0) == (tq.KV_ASYMMETRIC, 4, 2)
+    assert tq.kv_bit_allocation(37.0, 1.0) == (tq.KV_ASYMMETRIC, 4, 2)
+    assert tq.kv_bit_allocation(60.0, 1.0)[0] == tq.KV_ASYMMETRIC
+    assert tq.kv_bit_allocation(80.0, 1.0)[0] == tq.KV_ASYMMETRIC  # the open band, read as asymmetric
+    assert tq.kv_bit_allocation(100.5, 1.0)[0] == tq.KV_MIXED
+    # the section's Qwen measurement: key norms 172-778 against value norms
+    # 2-4 put the typical ratio (~160x at the middles) in the mixed band
+    assert tq.kv_bit_allocation((172 + 778) / 2, (2 + 4) / 2)[0] == tq.KV_MIXED
+    # and its "~37,000x" sensitivity is the squared ratio 778 / 4
+    assert abs(tq.kv_norm_sensitivity(778, 4) - 37000) / 37000 < 0.03
+    # the ratio is what matters, not the scale
+    assert tq.kv_bit_allocation(500.0, 50.0) == tq.kv_bit_allocation(10.0, 1.0)
+    for bad in [(0.0, 1.0), (1.0, 0.0), (-1.0, 1.0), (float("inf"), 1.0), (float("nan"), 1.0)]:
+        with pytest.raises(ValueError):
+            tq.kv_bit_allocation(*bad)
