@@ -34,6 +34,7 @@ TQ_MAX_GROUPS = 4
 EXPORTS = [
     "tq_build_codebook", "tq_quantizer_init", "tq_packed_bytes", "tq_status_string",
     "tq_quantize_kv", "tq_append_kv", "tq_decode_workspace_bytes", "tq_decode_attn", "tq_kv_bit_allocation",
+    "tq_decode_paged_workspace_bytes", "tq_decode_attn_paged",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_fold_bytes", "tq_fold_qjl",
 ]
 
@@ -90,6 +91,13 @@ def lib() -> ctypes.CDLL:
         L.tq_append_kv.restype = c_int
         L.tq_kv_bit_allocation.argtypes = [c_double, c_double, POINTER(c_int), POINTER(c_int)]
         L.tq_kv_bit_allocation.restype = c_int
+        L.tq_decode_paged_workspace_bytes.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_int, c_int, c_int,
+                                                      c_int, c_int]
+        L.tq_decode_paged_workspace_bytes.restype = c_size_t
+        L.tq_decode_attn_paged.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_void_p, c_int, c_int, c_int,
+                                           c_int, c_int, c_void_p, c_void_p, c_int, c_int, c_int64, c_float,
+                                           c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.tq_decode_attn_paged.restype = c_int
         L.tq_decode_workspace_bytes.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_int, c_int, c_int, c_int]
         L.tq_decode_workspace_bytes.restype = c_size_t
         L.tq_decode_attn.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_void_p, c_int, c_int, c_int, c_int,
@@ -221,6 +229,21 @@ def tq_decode_attn(k: tq_kv_desc, v: tq_kv_desc, q, q_dtype: int, B: int, Hq: in
     _check(lib().tq_decode_attn(ctypes.byref(k), ctypes.byref(v), _ptr(q), q_dtype, B, Hq, Hkv, T_max,
                                 _ptr(seq_lens), scale, _ptr(out), _ptr(scores_out), _ptr(ws), ws_bytes,
                                 _stream(stream)), "tq_decode_attn")
+
+
+def tq_decode_paged_workspace_bytes(k: tq_kv_desc, v: tq_kv_desc, B: int, Hq: int, Hkv: int, T_max: int,
+                                    block_tokens: int) -> int:
+    return int(lib().tq_decode_paged_workspace_bytes(ctypes.byref(k), ctypes.byref(v), B, Hq, Hkv, T_max,
+                                                     block_tokens))
+
+
+def tq_decode_attn_paged(k: tq_kv_desc, v: tq_kv_desc, q, q_dtype: int, B: int, Hq: int, Hkv: int, T_max: int,
+                         seq_lens, block_table, max_blocks: int, block_tokens: int, num_blocks: int, scale: float,
+                         out, scores_out, ws, ws_bytes: int, stream=None) -> None:
+    _check(lib().tq_decode_attn_paged(ctypes.byref(k), ctypes.byref(v), _ptr(q), q_dtype, B, Hq, Hkv, T_max,
+                                      _ptr(seq_lens), _ptr(block_table), max_blocks, block_tokens, num_blocks,
+                                      scale, _ptr(out), _ptr(scores_out), _ptr(ws), ws_bytes, _stream(stream)),
+           "tq_decode_attn_paged")
 
 
 def tq_search_workspace_bytes(db: tq_group, N: int, Q: int, k: int) -> int:

@@ -45,6 +45,8 @@
 // workspace; combine merges the splits and applies R_v^T.
 #include <math.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -118,6 +120,12 @@ struct Args {
   uint32_t* aops;    // [keys][nslots][64 lanes][8 dwords] query operands of every slot
   float* partial;    // [B * Hq][splits][kD + 2] (max, sum, rotated accumulator)
   float* out;
+  // paged cache (null table: contiguous sequences): row of (sequence b, KV
+  // head g, token t) = (block_table[b][t / block_tokens] * Hkv + g) *
+  // block_tokens + t % block_tokens
+  const int32_t* block_table;
+  int max_blocks, block_tokens;
+  int64_t num_blocks;
 };
 
 // Slot s of the operand table for a per-lane s: the coefficients are read
@@ -832,6 +840,22 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   const int h0 = g * a.G + ht * kHT;
   const int nh = min(kHT, a.G - ht * kHT);
   const int ts = split * a.split_len;
+  // A paged cache: the split lies in one block of the sequence's block
+  // table; that block's rows stand where a contiguous sequence's would
+  // (pbg), token offsets count from the block's first token (tok_base), and
+  // a block id outside the pool reads as empty (zero-sized resources).
+  int64_t pbg = bg;
+  int tok_base = 0, rel_first_last = a.T_max - 1;
+  uint32_t live = 1u;
+  if (a.block_table) {
+    const int bi = ts / a.block_tokens;
+    const int blk = a.block_table[(int64_t)b * a.max_blocks + bi];
+    const bool ok = blk >= 0 && blk < a.num_blocks;
+    pbg = (int64_t)(ok ? blk : 0) * a.Hkv + g;
+    tok_base = bi * a.block_tokens;
+    rel_first_last = a.block_tokens - 1;
+    live = ok ? 1u : 0u;
+  }
 
   // this lane's coordinate word of the key layout (score-phase B operand)
   // (group fields are selected from uniform values, never indexed per lane)
@@ -844,23 +868,23 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
     const int kd = a.k[gi].d, kch = a.k[gi].ch;
     const int64_t kss = a.k[gi].seq_stride;
     ka.step[gi] = (uint32_t)((kd >> 5) * 16 * P * 4);
-    const uint32_t* seq = a.k[gi].packed + (((int64_t)bg * kss) >> 4) * ((kd >> 5) * 16 * P);
-    ka.res[gi] = make_rsrc(seq, (uint32_t)(kss >> 4) * ka.step[gi]);
+    const uint32_t* seq = a.k[gi].packed + ((pbg * kss) >> 4) * ((kd >> 5) * 16 * P);
+    ka.res[gi] = make_rsrc(seq, (uint32_t)(kss >> 4) * ka.step[gi] * live);
     const bool own = NK == 1 || (gi == 1) == kg1;
     ka.voff[gi] = own ? (uint32_t)(((W - (kch >> 5)) * 16 + tl) * P * 4) : kOutside;
   }
   NAddr na;
 #pragma unroll
   for (int gi = 0; gi < NK; ++gi) {
-    const uint32_t nb = (uint32_t)(2 * a.k[gi].seq_stride);
-    na.n[gi] = make_rsrc(a.k[gi].norm + (int64_t)bg * a.k[gi].seq_stride, nb);
-    na.r[gi] = make_rsrc(((gi == 0 && KP0) || (gi == 1 && KP1)) ? a.k[gi].rnorm + (int64_t)bg * a.k[gi].seq_stride
+    const uint32_t nb = (uint32_t)(2 * a.k[gi].seq_stride) * live;
+    na.n[gi] = make_rsrc(a.k[gi].norm + pbg * a.k[gi].seq_stride, nb);
+    na.r[gi] = make_rsrc(((gi == 0 && KP0) || (gi == 1 && KP1)) ? a.k[gi].rnorm + pbg * a.k[gi].seq_stride
                                                                  : a.k[gi].norm,
                          ((gi == 0 && KP0) || (gi == 1 && KP1)) ? nb : 0u);
   }
 #pragma unroll
   for (int gv = 0; gv < NV; ++gv)
-    na.nv[gv] = make_rsrc(a.v[gv].norm + (int64_t)bg * a.v[gv].seq_stride, (uint32_t)(2 * a.v[gv].seq_stride));
+    na.nv[gv] = make_rsrc(a.v[gv].norm + pbg * a.v[gv].seq_stride, (uint32_t)(2 * a.v[gv].seq_stride) * live);
   // this wave's value coordinates 32 w .. 32 w + 31 belong to one value group
   const int vgi = (NV > 1 && 32 * w >= a.v[NV - 1].ch) ? 1 : 0;
   const VGroup& vme = a.v[vgi];
@@ -868,8 +892,8 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   VAddr va;
   va.vB = vme.B;
   va.tile_bytes = (uint32_t)(vme.d * vme.B * 4);
-  va.res = make_rsrc(vme.packed + (((int64_t)bg * vme.seq_stride) >> 5) * (vme.d * vme.B),
-                     (uint32_t)(vme.seq_stride >> 5) * va.tile_bytes);
+  va.res = make_rsrc(vme.packed + ((pbg * vme.seq_stride) >> 5) * (vme.d * vme.B),
+                     (uint32_t)(vme.seq_stride >> 5) * va.tile_bytes * live);
   va.lane_off = (uint32_t)((lane >> 4) * va.tile_bytes + (vjl0 + (lane & 15)) * vme.B * 4);
 
   // ---- query operands of every slot and their inverse scales (built by the
@@ -888,8 +912,8 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   // memory; tokens at or past the length are masked where they are used
   KChunk<NK, NV> kA, kB;
   VChunk vv;
-  load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kA, ka, na, ts, a.T_max - 1, w, lane);
-  load_v<NV, VB0, VB1>(vv, va, ts, lane);
+  load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kA, ka, na, ts - tok_base, rel_first_last, w, lane);
+  load_v<NV, VB0, VB1>(vv, va, ts - tok_base, lane);
   // E8M0 scales of this lane's query-operand rows (row lane % 16 = 4 head +
   // digit): the digit's weight 16^-digit times the head's inverse operand
   // scale, a power of two (the query transforms choose it so), per (group,
@@ -912,6 +936,8 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   const int len = max(min(max(__builtin_amdgcn_readfirstlane((int)lraw), 0), a.T_max), a.seq_lens ? 0 : a.T_max);
   const int te = min(ts + a.split_len, len);
   const int tlast = max(te, 1) - 1;
+  // (loads take token offsets within the block of a paged cache)
+  const int rel_last = max(tlast - tok_base, 0);
   // constant parts of the fp4 encoding, per (group, class); scales of this lane's head
   float cm[NK], cq[NK], gam[NK];
   {
@@ -954,7 +980,7 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
                    __attribute__((always_inline)) {
     constexpr int VB = decltype(vbt)::value;  // value bits of this wave's coordinates
     const int cn = c0 + kChunk < te ? c0 + kChunk : c0;
-    if constexpr (!kOneK) load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kn, ka, na, cn, tlast, w, lane);
+    if constexpr (!kOneK) load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kn, ka, na, cn - tok_base, rel_last, w, lane);
 
     // ---------------- scores for this wave's 64 tokens
     float lg[4], raw[4];
@@ -1068,7 +1094,7 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
       e_run[gv] = e_new[gv];
     }
     // (one key buffer: it is used up; refill it with the next chunk's keys)
-    if constexpr (kOneK) load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kc, ka, na, cn, tlast, w, lane);
+    if constexpr (kOneK) load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kc, ka, na, cn - tok_base, rel_last, w, lane);
     __syncthreads();
     // ---------------- values: this wave's 32 coordinates over the 256 tokens
     // (a step past the split's end has all weights 0 and adds nothing)
@@ -1085,7 +1111,7 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
     }
     // the value words are used: refill them with the next chunk's (they
     // arrive while its scores and weights are formed)
-    load_v<NV, VB0, VB1>(vc, va, cn, lane);
+    load_v<NV, VB0, VB1>(vc, va, cn - tok_base, lane);
   };
   // The first chunk always runs (an empty split runs it fully masked: no
   // weight, no change to the running state), so that its loads and the
@@ -1317,7 +1343,10 @@ namespace tqk {
 
 bool mfma_decode_supported(const tq_kv_desc& k, const tq_kv_desc& v) { return find_spec(k, v) != nullptr; }
 
-DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int Hq, int Hkv, int T_max) {
+int mfma_decode_max_splits() { return kMaxCombineSplits; }
+
+DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int Hq, int Hkv, int T_max,
+                            int block_tokens) {
   (void)v;
   DecodePlan p{};
   const int G = Hq / Hkv;
@@ -1328,6 +1357,10 @@ DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int
   const int64_t min_sl = (T_max + kMaxCombineSplits - 1) / kMaxCombineSplits;  // the combine's split table
   if (sl < min_sl) sl = min_sl;
   sl = (sl + kChunk - 1) / kChunk * kChunk;
+  if (block_tokens > 0) {  // a split must not leave its block: a divisor of it
+    sl = std::min<int64_t>(sl, block_tokens);
+    while (block_tokens % sl) sl -= kChunk;
+  }
   p.split_len = (int)sl;
   p.splits = (int)((T_max + sl - 1) / sl);
   p.head_chunk = kHT;
@@ -1348,10 +1381,17 @@ DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int
 
 hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const void* q, tq_dtype qdt, int B, int Hq,
                               int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out,
-                              float* scores_out, void* ws, const DecodePlan& plan, hipStream_t s) {
+                              float* scores_out, void* ws, const DecodePlan& plan, hipStream_t s,
+                              const PageTable* pages) {
   const Spec* sp = find_spec(k, v);
   if (!sp) return hipErrorInvalidValue;
   Args a{};
+  if (pages) {
+    a.block_table = pages->table;
+    a.max_blocks = pages->max_blocks;
+    a.block_tokens = pages->block_tokens;
+    a.num_blocks = pages->num_blocks;
+  }
   bool folded = true;  // every PROD key group carries S R: one query-transform pass
   a.nk = k.n_groups;
   a.nv = v.n_groups;

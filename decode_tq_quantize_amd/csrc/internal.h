@@ -40,12 +40,26 @@ hipError_t launch_decode(const tq_kv_desc& k, const tq_kv_desc& v, const void* q
                          int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out, float* scores_out,
                          void* ws, const DecodePlan& plan, hipStream_t s);
 
-// Matrix-core decode for 128-channel heads (decode_mfma.hip).
+// Block table of a paged cache: the rows of (sequence b, KV head g) are
+// block_tokens-row blocks of a pool of num_blocks blocks per head.
+struct PageTable {
+  const int32_t* table;  // device [B, max_blocks]
+  int max_blocks;
+  int block_tokens;      // a multiple of 256
+  int64_t num_blocks;
+};
+
+// Matrix-core decode for 128-channel heads (decode_mfma.hip). With a block
+// size, the split length divides it (a split never leaves its block).
 bool mfma_decode_supported(const tq_kv_desc& k, const tq_kv_desc& v);
-DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int Hq, int Hkv, int T_max);
+DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int Hq, int Hkv, int T_max,
+                            int block_tokens = 0);
 hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const void* q, tq_dtype qdt, int B, int Hq,
                               int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out,
-                              float* scores_out, void* ws, const DecodePlan& plan, hipStream_t s);
+                              float* scores_out, void* ws, const DecodePlan& plan, hipStream_t s,
+                              const PageTable* pages = nullptr);
+// Largest number of splits per sequence the combine handles.
+int mfma_decode_max_splits();
 
 // S R and its largest row norm (fold.hip).
 hipError_t launch_fold(const tq_quantizer& q, float* SR, hipStream_t s);

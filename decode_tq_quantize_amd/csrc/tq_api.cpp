@@ -76,6 +76,28 @@ int check_decode(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq, int Hk
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
 
+// Shapes of a paged decode: the matrix-core layouts only, blocks of a
+// multiple of 256 rows, every group's rows per (block, KV head) equal to the
+// block size, and no more splits than the combine takes.
+int check_paged_shape(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq, int Hkv, int T_max,
+                      int block_tokens, int* D, int* Dv) {
+  int rc = check_desc(k, false, D);
+  if (rc != TQ_OK) return rc;
+  rc = check_desc(v, true, Dv);
+  if (rc != TQ_OK) return rc;
+  if (*D > 256 || *Dv > 256) return TQ_ERR_UNSUPPORTED;
+  if (B < 1 || Hq < 1 || Hkv < 1 || (Hq % Hkv) != 0 || T_max < 1) return TQ_ERR_INVALID_ARG;
+  if (block_tokens < 256 || block_tokens % 256) return TQ_ERR_UNSUPPORTED;
+  for (int i = 0; i < k->n_groups; ++i)
+    if (k->g[i].seq_stride != block_tokens) return TQ_ERR_INVALID_ARG;
+  for (int i = 0; i < v->n_groups; ++i)
+    if (v->g[i].seq_stride != block_tokens) return TQ_ERR_INVALID_ARG;
+  if (!tqk::mfma_decode_supported(*k, *v)) return TQ_ERR_UNSUPPORTED;
+  const tqk::DecodePlan p = tqk::plan_decode_mfma(*k, *v, B, Hq, Hkv, T_max, block_tokens);
+  if (p.splits > tqk::mfma_decode_max_splits()) return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
+
 // 128-channel heads run on the matrix cores; other head sizes on the
 // general kernel of decode.hip.
 tqk::DecodePlan decode_plan(const tq_kv_desc& k, const tq_kv_desc& v, int B, int Hq, int Hkv, int T_max) {
@@ -202,6 +224,36 @@ extern "C" int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const vo
                                               scores_out, ws, p, static_cast<hipStream_t>(stream)));
   return hip_status(tqk::launch_decode(*k, *v, q, q_dtype, B, Hq, Hkv, T_max, seq_lens, scale, out, scores_out,
                                        ws, p, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" size_t tq_decode_paged_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq, int Hkv,
+                                                  int T_max, int block_tokens) {
+  int D = 0, Dv = 0;
+  if (check_paged_shape(k, v, B, Hq, Hkv, T_max, block_tokens, &D, &Dv) != TQ_OK) return 0;
+  const tqk::DecodePlan p = tqk::plan_decode_mfma(*k, *v, B, Hq, Hkv, T_max, block_tokens);
+  return (p.qprep_floats + p.partial_floats) * sizeof(float);
+}
+
+extern "C" int tq_decode_attn_paged(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype, int B,
+                                    int Hq, int Hkv, int T_max, const int32_t* seq_lens, const int32_t* block_table,
+                                    int max_blocks, int block_tokens, int64_t num_blocks, float scale, float* out,
+                                    float* scores_out, void* ws, size_t ws_bytes, void* stream) {
+  int D = 0, Dv = 0;
+  int rc = check_paged_shape(k, v, B, Hq, Hkv, T_max, block_tokens, &D, &Dv);
+  if (rc != TQ_OK) return rc;
+  if (!q || !out || !block_table || max_blocks < 1 || num_blocks < 1) return TQ_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks * block_tokens < T_max) return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || (scores_out && !aligned16(scores_out)) ||
+      (seq_lens && !aligned16(seq_lens)) || (ws && !aligned16(ws)) ||
+      reinterpret_cast<uintptr_t>(block_table) % alignof(int32_t) != 0)
+    return TQ_ERR_MISALIGNED;
+  const tqk::DecodePlan p = tqk::plan_decode_mfma(*k, *v, B, Hq, Hkv, T_max, block_tokens);
+  if (!ws || ws_bytes < (p.qprep_floats + p.partial_floats) * sizeof(float)) return TQ_ERR_WORKSPACE;
+  const tqk::PageTable pages{block_table, max_blocks, block_tokens, num_blocks};
+  return hip_status(tqk::launch_decode_mfma(*k, *v, q, q_dtype, B, Hq, Hkv, T_max, seq_lens, scale, out, scores_out,
+                                            ws, p, static_cast<hipStream_t>(stream), &pages));
 }
 
 extern "C" size_t tq_search_workspace_bytes(const tq_group* db, int64_t N, int Q, int k) {

@@ -226,6 +226,30 @@ int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_d
                    int B, int Hq, int Hkv, int T_max, const int32_t* seq_lens, float scale,
                    float* out, float* scores_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes tq_decode_attn_paged needs (0 on bad arguments). */
+size_t tq_decode_paged_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq,
+                                       int Hkv, int T_max, int block_tokens);
+
+/* tq_decode_attn over a paged cache (the same attention, riverfrot sections
+ * 2.2-2.3 and 4.3): the cache of every group is a pool of num_blocks blocks
+ * of block_tokens rows per KV head, and token t of sequence b, KV head g is
+ * row (block_table[b * max_blocks + t / block_tokens] * Hkv + g) *
+ * block_tokens + t % block_tokens of the group's packed, norm and rnorm
+ * arrays (each group's seq_stride must equal block_tokens). block_table:
+ * device int32 [B, max_blocks], with max_blocks * block_tokens >= T_max;
+ * entries past a sequence's last block are not read for its scores, and a
+ * block id outside [0, num_blocks) reads as an empty block (no fault; its
+ * tokens are then not the cache's). block_tokens: a multiple of 256 (the
+ * decode kernel's chunk), so that each workgroup's split lies in one block.
+ * Head size 128 in the layouts the matrix-core decode compiles (otherwise
+ * UNSUPPORTED). Other arguments and errors as for tq_decode_attn, with the
+ * workspace sized by tq_decode_paged_workspace_bytes. */
+int tq_decode_attn_paged(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype,
+                         int B, int Hq, int Hkv, int T_max, const int32_t* seq_lens,
+                         const int32_t* block_table, int max_blocks, int block_tokens,
+                         int64_t num_blocks, float scale, float* out, float* scores_out, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* Workspace bytes tq_search_topk needs. */
 size_t tq_search_workspace_bytes(const tq_group* db, int64_t N, int Q, int k);
 

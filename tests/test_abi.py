@@ -225,6 +225,32 @@ def test_decode_validation_paths():
     assert tq.tq_decode_workspace_bytes(k, v, 1, 30, 8, 1024) == 0
 
 
+def test_paged_decode_validation_paths():
+    L = tq.lib()
+    bt = 512
+    k, v = _kv(T=bt)  # every group's rows per (block, KV head) = the block size
+    ws = tq.tq_decode_paged_workspace_bytes(k, v, 2, 32, 8, 4000, bt)
+    assert ws > 0
+    assert tq.tq_decode_paged_workspace_bytes(k, v, 2, 32, 8, 4000, 300) == 0   # not a multiple of 256
+    assert tq.tq_decode_paged_workspace_bytes(k, v, 2, 32, 8, 4000, 1024) == 0  # seq_stride != block size
+
+    def call(k=k, v=v, table=FAKE, max_blocks=8, bt=bt, nblk=64, T=4000, out=FAKE, wsp=FAKE, wsb=ws):
+        return L.tq_decode_attn_paged(ctypes.byref(k), ctypes.byref(v), FAKE, tq.TQ_BF16, 2, 32, 8, T, None, table,
+                                      max_blocks, bt, nblk, 0.088, out, None, wsp, wsb, None)
+
+    assert call(table=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(max_blocks=7) == tq.TQ_ERR_INVALID_ARG      # 7 x 512 < 4000 tokens
+    assert call(nblk=0) == tq.TQ_ERR_INVALID_ARG
+    assert call(bt=384) == tq.TQ_ERR_UNSUPPORTED            # not a multiple of 256
+    assert call(table=FAKE + 2) == tq.TQ_ERR_MISALIGNED
+    assert call(wsb=ws - 1) == tq.TQ_ERR_WORKSPACE
+    assert call(out=None) == tq.TQ_ERR_INVALID_ARG
+    k2, v2 = _kv(T=1024)
+    assert call(k=k2, v=v2) == tq.TQ_ERR_INVALID_ARG        # rows per block differ from the block size
+    kp, vp = _kv(T=bt, kd=64, vd=64)
+    assert call(k=kp, v=vp) == tq.TQ_ERR_UNSUPPORTED        # head size without the matrix-core decode
+
+
 def test_search_validation_paths():
     L = tq.lib()
     db = tq.make_group(_q(1536, 3, tq.TQ_PROD), 0, FAKE, FAKE, FAKE, 0)

@@ -353,6 +353,80 @@ def test_decode_two_channel_groups(fold):
                  [otq.Group(0, va.oq, cva), otq.Group(32, vb.oq, cvb)], qry, Hkv, [200, 150])
 
 
+def paged_group(gq: GpuQuantizer, ch, codes: otq.Codes, table, bt, num_blocks, layout, rng):
+    """One channel group of a paged cache: a pool of num_blocks blocks of bt
+    rows per KV head holding every (sequence, head, token) at row
+    (table[b, t // bt] * H + g) * bt + t % bt; the other rows hold random
+    codes and finite random norms (never to be read as the cache's)."""
+    B, H, T, d = codes.idx.shape
+    rows = num_blocks * H * bt
+    idx = rng.integers(0, 1 << gq.B, (rows, d)).astype(np.uint8)
+    z = (rng.random((rows, d)) < 0.5) if gq.prod else None
+    n16 = np.abs(rng.standard_normal(rows)).astype(np.float16)
+    r16 = np.abs(rng.standard_normal(rows)).astype(np.float16)
+    for b in range(B):
+        for g in range(H):
+            for t0 in range(0, T, bt):
+                r0 = (int(table[b, t0 // bt]) * H + g) * bt
+                nt = min(bt, T - t0)
+                idx[r0:r0 + nt] = codes.idx[b, g, t0:t0 + nt]
+                if gq.prod:
+                    z[r0:r0 + nt] = codes.z[b, g, t0:t0 + nt]
+                    r16[r0:r0 + nt] = codes.rho16[b, g, t0:t0 + nt]
+                n16[r0:r0 + nt] = codes.n16[b, g, t0:t0 + nt]
+    words = otq.pack(idx, z, gq.B, layout)
+    c = Cache.__new__(Cache)
+    c.packed = torch_dev(words.view(np.int32))
+    c.norm = torch_dev(n16.view(np.int16))
+    c.rnorm = torch_dev(r16.view(np.int16)) if gq.prod else None
+    c.group = tq.make_group(gq.q, ch, c.packed, c.norm, c.rnorm, bt)
+    c.gq = gq  # keeps R, S and S R (which the group points at) alive
+    return c
+
+
+@pytest.mark.parametrize("bt,split", [(256, False), (1024, False), (512, True)])
+def test_decode_paged_cache(bt, split):
+    # the cache in a shuffled pool of blocks with spare (garbage) blocks; one
+    # or two channel groups; sequences ending inside a block
+    print(f"paged decode block={bt} groups={2 if split else 1}", flush=True)
+    B, Hq, Hkv, T, d = 2, 8, 2, 1500, 128
+    lens = [1500, 700]
+    K, V = make_kv(B, Hkv, T, d, seed=bt)
+    rng = synth.rng(bt, 5)
+    nbs = -(-T // bt)
+    max_blocks = nbs + 1
+    num_blocks = B * nbs + 3
+    table = np.full((B, max_blocks), -1, np.int32)
+    table[:, :nbs] = rng.permutation(num_blocks)[:B * nbs].reshape(B, nbs)
+    if split:
+        specs_k = [(0, 32, 2, True, 1), (32, 96, 1, True, 2)]
+        specs_v = [(0, 32, 3, False, 3), (32, 96, 2, False, 4)]
+    else:
+        specs_k = [(0, 128, 3, True, 1)]
+        specs_v = [(0, 128, 3, False, 2)]
+    kcs, vcs, kgs, vgs = [], [], [], []
+    for specs, X, caches, ogs, lay in ((specs_k, K, kcs, kgs, "keys"), (specs_v, V, vcs, vgs, "values")):
+        for ch, gd, bits, prod, seed in specs:
+            gq = GpuQuantizer(gd, bits, prod, seed, fold=prod,
+                              r_stream=synth.STREAM_R if lay == "keys" else synth.STREAM_R_V)
+            codes = otq.quantize(X[..., ch:ch + gd], gq.oq)
+            caches.append(paged_group(gq, ch, codes, table, bt, num_blocks, lay, rng))
+            ogs.append(otq.Group(ch, gq.oq, codes))
+    qry = synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.rng(bt, 31).standard_normal((B, Hq, d)).astype(np.float32)))
+    kd = tq.make_desc([c.group for c in kcs])
+    vd = tq.make_desc([c.group for c in vcs])
+    wsb = tq.tq_decode_paged_workspace_bytes(kd, vd, B, Hq, Hkv, T, bt)
+    assert wsb > 0
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    sc = torch.full((B, Hq, T), float("nan"), dtype=torch.float32, device="cuda")
+    tq.tq_decode_attn_paged(kd, vd, torch_dev(qry, torch.bfloat16), tq.TQ_BF16, B, Hq, Hkv, T,
+                            torch_dev(np.asarray(lens, np.int32)), torch_dev(table), max_blocks, bt, num_blocks,
+                            1.0 / math.sqrt(d), out, sc, ws, wsb)
+    torch.cuda.synchronize()
+    check_decode(out.cpu().numpy(), sc.cpu().numpy(), kgs, vgs, qry, Hkv, lens)
+
+
 @pytest.mark.parametrize("fold", [False, True])
 def test_decode_on_gpu_quantized_cache(fold):
     # stage isolation: the GPU quantiser writes the cache, the oracle decodes
