@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--copies", type=int, default=24)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--only", default="", help="comma list of extras to run: quantize,longctx,search,bits,niah,append")
+    p.add_argument("--only", default="", help="comma list of extras to run: quantize,longctx,search,bits,niah,append,paged")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one 256 MiB device-to-device copy (the known-size reference for the "
                         "FETCH_SIZE / WRITE_SIZE counters)")
@@ -336,6 +336,86 @@ def append_step(steps=200):
             "vectors_per_s": round(2 * n / ms * 1e3, 1),
             "workload": "one new token per (sequence, KV head): batch 64 x 8 KV heads, d=128, K 3+1-bit prod and "
                         "V 3-bit MSE appended into a 4096-token-per-head cache (two tq_append_kv calls per step)"}
+
+
+def paged_decode(steps=20):
+    """Decode from a paged cache against the same cache stored contiguously.
+
+    Batch 16 x 32768 tokens, 32 q / 8 KV heads, d = 128, K 3+1-bit prod and
+    V 3-bit MSE (the single-layer law); the paged copy holds every (sequence,
+    KV head) in 4096-token blocks scattered over a shuffled pool.
+    """
+    import numpy as np
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+    from synth import device as sdev
+
+    B, Hq, Hkv, T, d, bt = 16, 32, 8, 32768, 128, 4096
+    n = B * Hkv * T
+    nbs = T // bt
+    Rk_t, Sk_t = dev(synth.haar_orthogonal(d, 6)), dev(synth.gaussian_matrix(d, d, 6))
+    Rv_t = dev(synth.haar_orthogonal(d, 6, synth.STREAM_R_V))
+    qk = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, Rk_t, Sk_t)
+    SR = torch.empty(tq.tq_fold_bytes(d) // 4, dtype=torch.float32, device="cuda")
+    tq.tq_quantizer_fold(qk, SR)
+    qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
+    perm = torch.from_numpy(synth.rng(6, 7).permutation(B * nbs).astype(np.int64)).cuda()
+    table = perm.view(B, nbs).to(torch.int32).contiguous()
+    # pool row of (b, g, t): (table[b, t / bt] * Hkv + g) * bt + t % bt
+    b_i = torch.arange(B, device="cuda").view(B, 1, 1, 1)
+    g_i = torch.arange(Hkv, device="cuda").view(1, Hkv, 1, 1)
+    blk = torch.arange(nbs, device="cuda").view(1, 1, nbs, 1)
+    t_i = torch.arange(bt, device="cuda").view(1, 1, 1, bt)
+    rows = ((table.long()[b_i, blk] * Hkv + g_i) * bt + t_i).reshape(-1)  # in (b, g, t) order
+    keep = []
+    descs = {}
+    for name, q, lay, var, st in (("k", qk, tq.TQ_LAYOUT_KEYS, tq.TQ_PROD, 1), ("v", qv, tq.TQ_LAYOUT_VALUES, tq.TQ_MSE, 2)):
+        X = sdev.kv_with_outliers(B, Hkv, T, d, 4, 10.0, seed=6, stream=st).view(n, d)
+        bits = 3
+        pk = torch.empty(tq.tq_packed_bytes(d, bits, var, lay, n) // 4, dtype=torch.int32, device="cuda")
+        pp = torch.zeros_like(pk)
+        nr, pn = (torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(2))
+        rr, pr = ((torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(2)) if var == tq.TQ_PROD
+                  else (None, None))
+        tq.tq_quantize_kv(q, lay, tq.TQ_BF16, X, n, d, pk, nr, rr)
+        tq.tq_append_kv(q, lay, tq.TQ_BF16, X, n, d, rows, n, pp, pn, pr)  # the same vectors into the pool
+        torch.cuda.synchronize()
+        del X
+        keep += [pk, pp, nr, pn, rr, pr]
+        descs[name] = (tq.make_desc([tq.make_group(q, 0, pk, nr, rr, T)]), tq.make_desc([tq.make_group(q, 0, pp, pn, pr, bt)]))
+    q_t = torch.randn((B, Hq, d), generator=sdev.generator(6, 8), device="cuda").to(torch.bfloat16)
+    out_c = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    out_p = torch.empty_like(out_c)
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    wsc = tq.tq_decode_workspace_bytes(descs["k"][0], descs["v"][0], B, Hq, Hkv, T)
+    wsp = tq.tq_decode_paged_workspace_bytes(descs["k"][1], descs["v"][1], B, Hq, Hkv, T, bt)
+    ws_c = torch.empty(wsc // 4 + 4, dtype=torch.float32, device="cuda")
+    ws_p = torch.empty(wsp // 4 + 4, dtype=torch.float32, device="cuda")
+
+    def contiguous():
+        tq.tq_decode_attn(descs["k"][0], descs["v"][0], q_t, tq.TQ_BF16, B, Hq, Hkv, T, lens, 1 / math.sqrt(d),
+                          out_c, None, ws_c, wsc)
+
+    def paged():
+        tq.tq_decode_attn_paged(descs["k"][1], descs["v"][1], q_t, tq.TQ_BF16, B, Hq, Hkv, T, lens, table, nbs, bt,
+                                B * nbs, 1 / math.sqrt(d), out_p, None, ws_p, wsp)
+
+    res = {}
+    for name, fn in (("contiguous", contiguous), ("paged", paged)):
+        fn()
+        with Timer() as tm:
+            for _ in range(steps):
+                fn()
+        res[name] = tm.ms / steps
+    diff = float((out_p - out_c).norm() / out_c.norm())
+    bytes_ = n * 118 + B * Hq * d * 6
+    return {"contiguous_ms": round(res["contiguous"], 4), "paged_ms": round(res["paged"], 4),
+            "paged_gbs": round(bytes_ / res["paged"] / 1e6, 1), "paged_hbm_frac": round(bytes_ / res["paged"] / 1e6 / HBM_PEAK_GBS, 4),
+            "paged_vs_contiguous_output_rel_diff": diff,
+            "workload": "batch 16 x 32768 tokens, 32 q / 8 KV heads, d=128, K 3+1-bit prod, V 3-bit MSE; paged copy in "
+                        "4096-token blocks over a shuffled pool (written with tq_append_kv)"}
 
 
 NIAH_KEYS = [("3+1 prod", 3, True), ("4 MSE-only", 4, False), ("2+1 prod", 2, True), ("3 MSE-only", 3, False),
@@ -797,6 +877,12 @@ def main():
             except Exception as e:  # an extra that fails is reported, not hidden
                 extras[name] = {"error": repr(e)}
             log(f"{name}: {extras[name]}")
+        if not only or "paged" in only:
+            try:
+                extras["paged_decode"] = paged_decode()
+            except Exception as e:
+                extras["paged_decode"] = {"error": repr(e)}
+            log(f"paged_decode: {extras['paged_decode']}")
         if not only or "append" in only:
             try:
                 extras["append_step"] = append_step()
