@@ -835,7 +835,7 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   asm volatile("" ::"s"(a.Hkv), "s"(a.HT), "s"(a.split_len), "s"(a.T_max), "s"(a.aops), "s"(a.ascale),
                "s"(a.k[0].packed), "s"(a.k[0].norm), "s"(a.k[0].rnorm), "s"(a.k[0].seq_stride), "s"(a.k[0].d),
                "s"(a.k[0].ch), "s"(a.v[0].packed), "s"(a.v[0].norm), "s"(a.v[0].seq_stride), "s"(a.v[0].d),
-               "s"(a.v[0].B), "s"(a.v[0].ch), "s"(a.seq_lens), "s"(a.B), "s"(a.G));
+               "s"(a.v[0].B), "s"(a.v[0].ch), "s"(a.seq_lens), "s"(a.B), "s"(a.G), "s"(a.block_table));
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int h0 = g * a.G + ht * kHT;
   const int nh = min(kHT, a.G - ht * kHT);
