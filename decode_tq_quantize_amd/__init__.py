@@ -33,7 +33,7 @@ TQ_MAX_GROUPS = 4
 
 EXPORTS = [
     "tq_build_codebook", "tq_quantizer_init", "tq_packed_bytes", "tq_status_string",
-    "tq_quantize_kv", "tq_append_kv", "tq_decode_workspace_bytes", "tq_decode_attn", "tq_kv_bit_allocation",
+    "tq_quantize_kv", "tq_append_kv", "tq_append_kv_pair", "tq_decode_workspace_bytes", "tq_decode_attn", "tq_kv_bit_allocation",
     "tq_decode_paged_workspace_bytes", "tq_decode_attn_paged",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_fold_bytes", "tq_fold_qjl",
 ]
@@ -89,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.tq_append_kv.argtypes = [POINTER(tq_quantizer), c_int, c_int, c_void_p, c_int64, c_int64, c_void_p,
                                    c_int64, c_void_p, c_void_p, c_void_p, c_void_p]
         L.tq_append_kv.restype = c_int
+        L.tq_append_kv_pair.argtypes = [POINTER(tq_quantizer), POINTER(tq_quantizer), c_int, c_void_p, c_void_p,
+                                        c_int64, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_void_p]
+        L.tq_append_kv_pair.restype = c_int
         L.tq_kv_bit_allocation.argtypes = [c_double, c_double, POINTER(c_int), POINTER(c_int)]
         L.tq_kv_bit_allocation.restype = c_int
         L.tq_decode_paged_workspace_bytes.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_int, c_int, c_int,
@@ -191,6 +195,15 @@ def tq_append_kv(q: tq_quantizer, layout: int, in_dtype: int, x, n: int, x_strid
                  cache_rows: int, packed, norm, rnorm=None, stream=None) -> None:
     _check(lib().tq_append_kv(ctypes.byref(q), layout, in_dtype, _ptr(x), n, x_stride_elems, _ptr(rows),
                               cache_rows, _ptr(packed), _ptr(norm), _ptr(rnorm), _stream(stream)), "tq_append_kv")
+
+
+def tq_append_kv_pair(qk: tq_quantizer, qv: tq_quantizer, in_dtype: int, xk, xv, n: int, xk_stride_elems: int,
+                      xv_stride_elems: int, rows, cache_rows: int, kpacked, knorm, krnorm, vpacked, vnorm,
+                      vrnorm=None, stream=None) -> None:
+    _check(lib().tq_append_kv_pair(ctypes.byref(qk), ctypes.byref(qv), in_dtype, _ptr(xk), _ptr(xv), n,
+                                   xk_stride_elems, xv_stride_elems, _ptr(rows), cache_rows, _ptr(kpacked),
+                                   _ptr(knorm), _ptr(krnorm), _ptr(vpacked), _ptr(vnorm), _ptr(vrnorm),
+                                   _stream(stream)), "tq_append_kv_pair")
 
 
 def tq_kv_bit_allocation(key_norm: float, value_norm: float) -> tuple[int, int, int]:

@@ -17,6 +17,12 @@ inline int planes_of(const tq_quantizer& q) { return q.mse_bits + (q.variant == 
 hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
                            int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s,
                            const int64_t* rows = nullptr, int64_t cache_rows = 0);
+// Keys (key layout) and values (value layout) of the same rows appended in one
+// launch.
+hipError_t launch_append_pair(const tq_quantizer& qk, const tq_quantizer& qv, tq_dtype dt, const void* xk,
+                              const void* xv, int64_t n, int64_t k_stride, int64_t v_stride, const int64_t* rows,
+                              int64_t cache_rows, void* kpacked, uint16_t* knorm, uint16_t* krnorm, void* vpacked,
+                              uint16_t* vnorm, uint16_t* vrnorm, hipStream_t s);
 
 // Matrix-core quantiser for 128-channel vectors (quantize_mfma.hip): rows
 // 16-byte aligned.

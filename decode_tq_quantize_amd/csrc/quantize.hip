@@ -14,6 +14,8 @@
 // serves appends: each vector is then written to a caller-given cache row
 // (one token per sequence and head during decoding, or the rows of a paged
 // block), keys as whole words, values as one bit per tile word.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -126,8 +128,15 @@ __device__ __forceinline__ uint32_t key_word(const uint8_t* C, int TV, int v, in
   return (uint32_t)(m >> (32 * (lane >> 5)));
 }
 
+// Up to two tensors per launch (the keys and values of one append): grid
+// row blockIdx.y takes argument set y.
+struct QArgsPair {
+  QArgs a[2];
+};
+
 template <int TV>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QArgs a) {
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QArgsPair pair) {
+  const QArgs& a = pair.a[blockIdx.y];
   extern __shared__ float smem[];
   __shared__ float nrm[TV], rho[TV];
   __shared__ float cent[TQ_MAX_LEVELS], thr[TQ_MAX_LEVELS];
@@ -278,24 +287,23 @@ size_t lds_bytes(int d, int TV) {
   return (size_t)(jc * kMtStride + 2 * d * TV) * 4 + (size_t)d * TV;
 }
 
+// count (1 or 2) argument sets, the first nround vectors of each
 template <int TV>
-hipError_t launch_tv(const QArgs& a, int64_t nround, hipStream_t s) {
-  const size_t lds = lds_bytes(a.d, TV);
+hipError_t launch_tv(const QArgs* as, int count, int64_t nround, hipStream_t s) {
+  QArgsPair pair{};
+  pair.a[0] = as[0];
+  pair.a[1] = as[count > 1 ? 1 : 0];
+  const size_t lds = lds_bytes(std::max(pair.a[0].d, pair.a[1].d), TV);
   hipError_t e = hipFuncSetAttribute((const void*)quantize_kernel<TV>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (nround + TV - 1) / TV;
-  hipLaunchKernelGGL(quantize_kernel<TV>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL(quantize_kernel<TV>, dim3((unsigned)blocks, (unsigned)count), dim3(kThreads), lds, s, pair);
   return hipGetLastError();
 }
 
-}  // namespace
-
-namespace tqk {
-
-hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
-                           int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s,
-                           const int64_t* rows, int64_t cache_rows) {
+QArgs make_args(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n, int64_t stride,
+                void* packed, uint16_t* norm, uint16_t* rnorm, const int64_t* rows, int64_t cache_rows) {
   QArgs a{};
   a.rows = rows;
   a.cache_rows = cache_rows;
@@ -314,24 +322,48 @@ hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt,
   a.packed = static_cast<uint32_t*>(packed);
   a.norm = norm;
   a.rnorm = rnorm;
-  // (an append writes rows one by one: no tile of the output to round to)
-  const int tile = rows ? 1 : (layout == TQ_LAYOUT_KEYS ? kKeysTile : kValuesTile);
+  return a;
+}
+
+constexpr size_t kLdsLimit = 150 * 1024;
+
+// An append is a few vectors per sequence: small tiles, so that the vectors
+// spread over the compute units (about 256 workgroups or more per tensor).
+hipError_t launch_rows(const QArgs* as, int count, int64_t n, hipStream_t s) {
+  const int d = count > 1 ? std::max(as[0].d, as[1].d) : as[0].d;
+  auto fits = [&](int tv) { return n >= 256 * (int64_t)tv && lds_bytes(d, tv) <= kLdsLimit; };
+  if (fits(32)) return launch_tv<32>(as, count, n, s);
+  if (fits(16)) return launch_tv<16>(as, count, n, s);
+  if (fits(8)) return launch_tv<8>(as, count, n, s);
+  if (fits(4)) return launch_tv<4>(as, count, n, s);
+  return launch_tv<2>(as, count, n, s);
+}
+
+}  // namespace
+
+namespace tqk {
+
+hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
+                           int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s,
+                           const int64_t* rows, int64_t cache_rows) {
+  const QArgs a = make_args(q, layout, dt, x, n, stride, packed, norm, rnorm, rows, cache_rows);
+  if (rows) return launch_rows(&a, 1, n, s);  // (rows are written one by one: no output tile to round to)
+  const int tile = layout == TQ_LAYOUT_KEYS ? kKeysTile : kValuesTile;
   const int64_t nround = (n + tile - 1) / tile * tile;
-  const size_t limit = 150 * 1024;
-  if (rows) {
-    // an append is a few vectors per sequence: small tiles, so that the
-    // vectors spread over the compute units (about 256 workgroups or more)
-    auto fits = [&](int tv) { return n >= 256 * (int64_t)tv && lds_bytes(q.d, tv) <= limit; };
-    if (fits(32)) return launch_tv<32>(a, nround, s);
-    if (fits(16)) return launch_tv<16>(a, nround, s);
-    if (fits(8)) return launch_tv<8>(a, nround, s);
-    if (fits(4)) return launch_tv<4>(a, nround, s);
-    return launch_tv<2>(a, nround, s);
-  }
-  if (layout == TQ_LAYOUT_VALUES || lds_bytes(q.d, 32) <= limit) return launch_tv<32>(a, nround, s);
-  if (lds_bytes(q.d, 16) <= limit) return launch_tv<16>(a, nround, s);
-  if (lds_bytes(q.d, 8) <= limit) return launch_tv<8>(a, nround, s);
-  return launch_tv<4>(a, nround, s);
+  if (layout == TQ_LAYOUT_VALUES || lds_bytes(q.d, 32) <= kLdsLimit) return launch_tv<32>(&a, 1, nround, s);
+  if (lds_bytes(q.d, 16) <= kLdsLimit) return launch_tv<16>(&a, 1, nround, s);
+  if (lds_bytes(q.d, 8) <= kLdsLimit) return launch_tv<8>(&a, 1, nround, s);
+  return launch_tv<4>(&a, 1, nround, s);
+}
+
+hipError_t launch_append_pair(const tq_quantizer& qk, const tq_quantizer& qv, tq_dtype dt, const void* xk,
+                              const void* xv, int64_t n, int64_t k_stride, int64_t v_stride, const int64_t* rows,
+                              int64_t cache_rows, void* kpacked, uint16_t* knorm, uint16_t* krnorm, void* vpacked,
+                              uint16_t* vnorm, uint16_t* vrnorm, hipStream_t s) {
+  const QArgs as[2] = {
+      make_args(qk, TQ_LAYOUT_KEYS, dt, xk, n, k_stride, kpacked, knorm, krnorm, rows, cache_rows),
+      make_args(qv, TQ_LAYOUT_VALUES, dt, xv, n, v_stride, vpacked, vnorm, vrnorm, rows, cache_rows)};
+  return launch_rows(as, 2, n, s);
 }
 
 }  // namespace tqk

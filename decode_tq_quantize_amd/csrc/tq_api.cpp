@@ -143,6 +143,31 @@ extern "C" size_t tq_packed_bytes(int d, int mse_bits, tq_variant variant, tq_la
   return (size_t)nr * (size_t)P * (size_t)d / 8;
 }
 
+extern "C" int tq_append_kv_pair(const tq_quantizer* qk, const tq_quantizer* qv, tq_dtype in_dtype, const void* xk,
+                                 const void* xv, int64_t n, int64_t xk_stride_elems, int64_t xv_stride_elems,
+                                 const int64_t* rows, int64_t cache_rows, void* kpacked, uint16_t* knorm,
+                                 uint16_t* krnorm, void* vpacked, uint16_t* vnorm, uint16_t* vrnorm, void* stream) {
+  int rc = check_quantizer(qk);
+  if (rc != TQ_OK) return rc;
+  rc = check_quantizer(qv);
+  if (rc != TQ_OK) return rc;
+  if (in_dtype != TQ_F32 && in_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (n < 0 || xk_stride_elems < qk->d || xv_stride_elems < qv->d || cache_rows <= 0) return TQ_ERR_INVALID_ARG;
+  if (qv->d > 256) return TQ_ERR_UNSUPPORTED;
+  if (n == 0) return TQ_OK;
+  if (!xk || !xv || !rows || !kpacked || !knorm || (qk->variant == TQ_PROD && !krnorm) || !vpacked || !vnorm ||
+      (qv->variant == TQ_PROD && !vrnorm))
+    return TQ_ERR_INVALID_ARG;
+  if (!aligned16(xk) || !aligned16(xv) || !aligned16(kpacked) || !aligned16(knorm) || (krnorm && !aligned16(krnorm)) ||
+      !aligned16(vpacked) || !aligned16(vnorm) || (vrnorm && !aligned16(vrnorm)) ||
+      reinterpret_cast<uintptr_t>(rows) % alignof(int64_t) != 0)
+    return TQ_ERR_MISALIGNED;
+  return hip_status(tqk::launch_append_pair(*qk, *qv, in_dtype, xk, xv, n, xk_stride_elems, xv_stride_elems, rows,
+                                            cache_rows, kpacked, knorm, qk->variant == TQ_PROD ? krnorm : nullptr,
+                                            vpacked, vnorm, qv->variant == TQ_PROD ? vrnorm : nullptr,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int tq_kv_bit_allocation(double key_norm, double value_norm, int* key_bits, int* value_bits) {
   if (!key_bits || !value_bits) return TQ_ERR_INVALID_ARG;
   if (!std::isfinite(key_norm) || !std::isfinite(value_norm) || !(key_norm > 0.0) || !(value_norm > 0.0))

@@ -204,6 +204,18 @@ int tq_append_kv(const tq_quantizer* q, tq_layout layout, tq_dtype in_dtype,
                  int64_t cache_rows, void* packed, uint16_t* norm, uint16_t* rnorm,
                  void* stream);
 
+/* tq_append_kv for a key cache (TQ_LAYOUT_KEYS) and a value cache
+ * (TQ_LAYOUT_VALUES) in one launch: row rows[i] of both caches receives
+ * key xk[i] and value xv[i] (each quantised by its own quantiser, exactly as
+ * tq_append_kv would). For a decoding step that appends one token per
+ * (sequence, KV head) to both caches; the two caches share `rows` and
+ * cache_rows. Errors as for tq_append_kv, for either half. */
+int tq_append_kv_pair(const tq_quantizer* qk, const tq_quantizer* qv, tq_dtype in_dtype,
+                      const void* xk, const void* xv, int64_t n, int64_t xk_stride_elems,
+                      int64_t xv_stride_elems, const int64_t* rows, int64_t cache_rows,
+                      void* kpacked, uint16_t* knorm, uint16_t* krnorm, void* vpacked,
+                      uint16_t* vnorm, uint16_t* vrnorm, void* stream);
+
 /* Workspace bytes tq_decode_attn needs for these shapes (0 on bad arguments). */
 size_t tq_decode_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq,
                                  int Hkv, int T_max);

@@ -183,6 +183,24 @@ def test_kv_bit_allocation_matches_oracle():
     assert L.tq_kv_bit_allocation(1.0, 1.0, None, ctypes.byref(vb)) == tq.TQ_ERR_INVALID_ARG
 
 
+def test_append_pair_validation_paths():
+    L = tq.lib()
+
+    def call(qk, qv, xk=FAKE, xv=FAKE, n=10, rows=FAKE, cache_rows=64, kr=FAKE, vr=None, sk=128, sv=128):
+        return L.tq_append_kv_pair(ctypes.byref(qk), ctypes.byref(qv), tq.TQ_F32, xk, xv, n, sk, sv, rows,
+                                   cache_rows, FAKE, FAKE, kr, FAKE, FAKE, vr, None)
+
+    qk, qv = _q(), _q(128, 3, tq.TQ_MSE)
+    assert call(qk, qv, rows=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(qk, qv, xv=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(qk, qv, kr=None) == tq.TQ_ERR_INVALID_ARG   # PROD keys need their residual norms
+    assert call(qk, qv, cache_rows=0) == tq.TQ_ERR_INVALID_ARG
+    assert call(qk, qv, sv=64) == tq.TQ_ERR_INVALID_ARG
+    assert call(qk, qv, xk=FAKE + 4) == tq.TQ_ERR_MISALIGNED
+    assert call(qk, qv, n=0) == tq.TQ_OK
+    assert call(qk, _q(512, 2, tq.TQ_MSE), sv=512) == tq.TQ_ERR_UNSUPPORTED  # values layout needs d <= 256
+
+
 def _desc(groups):
     return tq.make_desc(groups)
 

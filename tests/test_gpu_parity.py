@@ -177,6 +177,37 @@ def test_append_writes_only_its_rows(d, B, prod, lay, dt, C, n_in):
                        None if not prod else r1[rk].view(np.float16), codes, gq.oq)
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64)])
+def test_append_pair_equals_two_appends(dk, dv):
+    # one launch for keys and values writes exactly what two appends write
+    print(f"append pair dk={dk} dv={dv}", flush=True)
+    C, n = 4096, 700
+    gk = GpuQuantizer(dk, 3, True, seed=7, fold=True)
+    gv = GpuQuantizer(dv, 3, False, seed=8, r_stream=synth.STREAM_R_V)
+    g = synth.rng(dk + dv, 10)
+    rows = torch_dev(g.choice(C, n, replace=False).astype(np.int64))
+    xk = torch_dev(synth.unit_gaussian(n, dk, 1) * 3, torch.bfloat16)
+    xv = torch_dev(synth.unit_gaussian(n, dv, 2) * 2, torch.bfloat16)
+
+    def cache(gq, lay):
+        nbytes = tq.tq_packed_bytes(gq.d, 3, _variant(gq.prod), lay, C)
+        w = torch_dev(g.integers(0, 2**32, nbytes // 4, dtype=np.uint64).astype(np.uint32).view(np.int32))
+        nrm = torch_dev(g.integers(0, 2**16, C, dtype=np.uint64).astype(np.uint16).view(np.int16))
+        rn = torch_dev(g.integers(0, 2**16, C, dtype=np.uint64).astype(np.uint16).view(np.int16)) if gq.prod else None
+        return w, nrm, rn
+
+    kA, vA = cache(gk, tq.TQ_LAYOUT_KEYS), cache(gv, tq.TQ_LAYOUT_VALUES)
+    kB = tuple(None if t is None else t.clone() for t in kA)
+    vB = tuple(None if t is None else t.clone() for t in vA)
+    tq.tq_append_kv_pair(gk.q, gv.q, tq.TQ_BF16, xk, xv, n, dk, dv, rows, C, kA[0], kA[1], kA[2], vA[0], vA[1])
+    tq.tq_append_kv(gk.q, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, xk, n, dk, rows, C, kB[0], kB[1], kB[2])
+    tq.tq_append_kv(gv.q, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, xv, n, dv, rows, C, vB[0], vB[1])
+    torch.cuda.synchronize()
+    for a_, b_ in zip(kA + vA, kB + vB):
+        if a_ is not None:
+            assert torch.equal(a_, b_)
+
+
 def test_quantize_strided_channel_group():
     # quantise channels 32..127 of 128-channel rows (a channel group)
     N, D = 200, 128
