@@ -21,11 +21,11 @@
 //    constant part sum a u_r is removed exactly with one more MFMA against
 //    the constant operand 4 u_r;
 //  * the real operand (query coefficients, softmax weights) is split into
-//    four fp8 e4m3 digits v = d0 + d1/16 + d2/256 + d3/4096 (each digit the
-//    fp8 rounding of what the previous ones left, scaled up by 16 so that it
-//    stays a normal fp8 number), carried as four MFMA rows and recombined
-//    with those weights after the product: about 16 significant bits, fp32
-//    accumulation.
+//    fp8 e4m3 digits v = d0 + d1/16 + d2/256 (+ d3/4096 for the queries;
+//    each digit the fp8 rounding of what the previous ones left, scaled up
+//    by 16 so that it stays a normal fp8 number), carried as MFMA rows and
+//    recombined with those weights after the product: about 16 significant
+//    bits for the queries, 12 for the weights, fp32 accumulation.
 // Rows of every MFMA are (query head, digit) = 4 x 4; columns are 16 tokens
 // (scores) or 16 value coordinates (value sums).
 //
@@ -234,9 +234,10 @@ __device__ __forceinline__ int exponent_of(float x) {
 // scaled by 16 per digit so that every digit stays in the normal fp8 range
 // (relative precision about 2^-16; no absolute floor). The four digits are
 // four rows of the MFMA; wsum4 recombines them. The softmax weights take
-// their digits by truncation instead (d_m the leading four significant bits
-// of the residual, cut by a mask): each digit then still carries at least
-// four new bits (relative precision about 2^-15) for fewer instructions.
+// three digits: the first two by truncation (d_m the leading four
+// significant bits of the residual, cut by a mask, so each carries at least
+// four new bits), the third rounded to nearest, relative precision about
+// 2^-12 with no bias; their fourth row is zero.
 constexpr float kDigitStep = 16.f;
 __device__ __forceinline__ float wsum4(v4f x) {
   return (x[0] + x[1] * (1.f / 16.f)) + (x[2] * (1.f / 256.f) + x[3] * (1.f / 4096.f));
@@ -972,6 +973,12 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   for (int gv = 0; gv < NV; ++gv) e_run[gv] = -60;
 
   int buf = 0;
+  // the weights' fourth digit rows stay zero (three digits are written)
+  for (int e = tid; e < 2 * NV * 2 * 4 * 8; e += kThreads) {
+    const int q16 = e & 7, rowq = (e >> 3) & 3, bsg = e >> 5;  // 16-byte piece, head, (buffer, group, step)
+    *reinterpret_cast<uint4*>(&wbuf[0][0][0][0][0] + (size_t)bsg * 16 * 128 + (4 * rowq + 3) * 128 + 16 * q16) =
+        make_uint4(0u, 0u, 0u, 0u);
+  }
   // one 256-token chunk: kc, vc hold its data; the next chunk is prefetched
   // into kn, vn (the last chunk re-reads its own, cached, addresses so that
   // the loads stay unconditional). Called with the two buffers swapped on
@@ -1085,11 +1092,12 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
         float r = p[i] * hbits_at(kc.nv[gv][i >> 1], i & 1) * sv;
         uint8_t* dst = &wbuf[buf][gv][ks][4 * hl][kappa];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < 2; ++m) {
           const float hi = head4(r);
           dst[128 * m] = (uint8_t)fp8_exact(hi);
           r = (r - hi) * kDigitStep;
         }
+        dst[256] = (uint8_t)fp8_of(r);  // the third and last digit, rounded to nearest
       }
       e_run[gv] = e_new[gv];
     }
