@@ -9,11 +9,14 @@
 // One workgroup quantises a tile of TV vectors. The tile is staged in LDS
 // coordinate-major; each d x d product is computed as a tile GEMM in fp32
 // FMA (fp32 accumulation, fixed summation order j = 0..d-1) with the matrix
-// streamed through LDS in 128 x 32 chunks. Codes, signs and norms are then
-// packed into the requested layout with one word per thread. The same kernel
-// serves appends: each vector is then written to a caller-given cache row
-// (one token per sequence and head during decoding, or the rows of a paged
-// block), keys as whole words, values as one bit per tile word.
+// streamed through LDS in chunks of 128 rows x 32 columns (128 columns for
+// tiles of 2-4 vectors), the next chunk's loads in flight while one is
+// multiplied. Codes, signs and norms are then packed into the requested
+// layout (key words gathered by wave ballots). The same kernel serves
+// appends: each vector is then written to a caller-given cache row (one
+// token per sequence and head during decoding, or the rows of a paged
+// block), keys as whole words, values as one bit per tile word; one launch
+// can carry a key cache and a value cache (grid row 0 and 1).
 #include <algorithm>
 
 #include "device_common.h"
