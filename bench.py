@@ -852,8 +852,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the hot path on a single MI355X and launches no "
-              "multi-GPU job; the sharding plan is written up in DESIGN.md.", file=sys.stderr)
+        print("bench.py measures one GPU: the hot path runs on a single MI355X and no multi-GPU job is launched; "
+              "pass --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
 
