@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import decode_tq_quantize_amd as tq
-    tq.lib()  # fail loudly if the library is missing on a GPU machine
+    tq.lib()  # fail loudly if the library is missing
 
 
 def _variant(prod):
