@@ -727,7 +727,7 @@ struct VAddr {
   int vB;
 };
 
-template <int NK, int NV, int P0, int P1, int KP0, int KP1>
+template <int NK, int NV, int P0, int P1, int KP0, int KP1, int PART = 3>
 __device__ __forceinline__ void load_k(KChunk<NK, NV>& kc, const KAddr& ka, const NAddr& na, int c0, int tlast,
                                        int w, int lane) {
   // tiles past the split's end re-read its last tile (their tokens are
@@ -735,6 +735,7 @@ __device__ __forceinline__ void load_k(KChunk<NK, NV>& kc, const KAddr& ka, cons
   const int last_tile = tlast >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    if constexpr (!(PART & 1)) break;
     const uint32_t tile = (uint32_t)min((c0 >> 4) + 4 * w + i, last_tile);
     if constexpr (NK == 1) {
       buf_words<P0>(ka.res[0], ka.voff[0], tile * ka.step[0], kc.w[i]);
@@ -754,12 +755,14 @@ __device__ __forceinline__ void load_k(KChunk<NK, NV>& kc, const KAddr& ka, cons
     const uint32_t tok0 = 16u * (uint32_t)min((c0 >> 4) + 4 * w + i, last_tile);
 #pragma unroll
     for (int gi = 0; gi < NK; ++gi) {
+      if constexpr (!(PART & 1)) break;
       const uint32_t nn = buf_half(na.n[gi], tl2, 2u * tok0);
       const uint32_t rn = ((gi == 0 && KP0) || (gi == 1 && KP1)) ? buf_half(na.r[gi], tl2, 2u * tok0) : 0u;
       kc.nr[gi][i] = nn | (rn << 16);
     }
 #pragma unroll
     for (int gv = 0; gv < NV; ++gv) {
+      if constexpr (!(PART & 2)) break;
       const uint32_t h = buf_half(na.nv[gv], tl2, 2u * tok0);
       kc.nv[gv][i >> 1] = (i & 1) ? (kc.nv[gv][i >> 1] | (h << 16)) : h;
     }
@@ -1041,6 +1044,8 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
         if (tok < te && hl < nh) a.scores_out[((int64_t)b * a.Hq + h0 + hl) * a.T_max + tok] = raw[i];
       }
     }
+    // (one key buffer: its plane words and key norms are used up; refill them)
+    if constexpr (kOneK) load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1, 1>(kc, ka, na, cn - tok_base, rel_last, w, lane);
     // ---------------- chunk statistics shared by the four waves
     float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
     mx = row16_max(mx);
@@ -1102,7 +1107,7 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
       e_run[gv] = e_new[gv];
     }
     // (one key buffer: it is used up; refill it with the next chunk's keys)
-    if constexpr (kOneK) load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kc, ka, na, cn - tok_base, rel_last, w, lane);
+    if constexpr (kOneK) load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1, 2>(kc, ka, na, cn - tok_base, rel_last, w, lane);
     __syncthreads();
     // ---------------- values: this wave's 32 coordinates over the 256 tokens
     // (a step past the split's end has all weights 0 and adds nothing)
