@@ -113,13 +113,16 @@ def test_quantize_matches_oracle(d, B, prod, lay, N, dt):
 
 APPEND_CASES = [
     # d, B, prod, layout, dtype, cache rows, appended rows (the count picks the
-    # kernel's tile: 2 vectors per workgroup below 1024, up to 32 from 8192)
+    # kernel's tile: 2 vectors per workgroup below 1024, 4 below 2048, 8
+    # below 4096, 16 below 8192, 32 from 8192)
     (128, 3, True, "keys", "bf16", 203, 61),
     (128, 3, False, "values", "bf16", 203, 61),
     (128, 2, True, "values", "f32", 203, 61),
     (96, 1, True, "keys", "f32", 203, 61),
     (32, 2, False, "values", "bf16", 203, 61),
     (256, 4, True, "keys", "f32", 203, 61),
+    (128, 3, True, "keys", "bf16", 4000, 1500),
+    (128, 3, False, "values", "bf16", 6000, 2500),
     (128, 3, True, "keys", "bf16", 6000, 4300),
     (128, 3, False, "values", "f32", 12000, 9000),
     (1536, 3, True, "keys", "f32", 700, 300),
