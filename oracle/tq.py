@@ -207,9 +207,9 @@ def _bits_to_words(bits):  # [..., 32] bool -> [...] uint32
     return w.astype(np.uint32)
 
 
-def _words_to_bits(w):  # [...] uint32 -> [..., 32] bool
-    w = w.astype(np.uint64)
-    return np.stack([((w >> np.uint64(i)) & np.uint64(1)).astype(bool) for i in range(32)], axis=-1)
+def _words_to_bits(w):  # [...] uint32 -> [..., 32] bool, bit i of the word at position i
+    b = np.ascontiguousarray(w, dtype="<u4").view(np.uint8).reshape(w.shape + (4,))
+    return np.unpackbits(b, axis=-1, bitorder="little").reshape(w.shape + (32,)).astype(bool)
 
 
 def packed_words(d, mse_bits, prod, n, layout):
