@@ -14,7 +14,9 @@ import os
 from ctypes import POINTER, c_double, c_float, c_int, c_int64, c_size_t, c_void_p
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtq.so")
+# TQ_LIBRARY names another build of the same library (the tests run the C ABI
+# checks against a host-sanitized build this way); the default is the in-tree one
+LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(_HERE, "libtq.so")
 
 TQ_OK = 0
 TQ_ERR_INVALID_ARG = -1

@@ -22,10 +22,12 @@ OBJDIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["codebook.cpp", "tq_api.cpp", "quantize.hip", "decode.hip", "decode_mfma.hip", "search.hip", "fold.hip", "quantize_mfma.hip", "search_mfma.hip"]
 
-# Per-source additions. The decode kernels form no NaN on any path they use
-# (masked logits are -inf and every difference of two maxima is guarded), so
-# they are built without NaN semantics: maxima of loaded or lane-exchanged
-# values then need no quieting instructions.
+# Per-source additions. The matrix-core decode forms no NaN from valid inputs:
+# masked logits are -inf by selection, every difference of two maxima is
+# guarded, and the value norms of rows at or past a sequence's length (which
+# its unconditional loads may read, whatever they hold) are cleared by a bit
+# mask before any arithmetic. It is therefore built without NaN semantics:
+# maxima of loaded or lane-exchanged values then need no quieting instructions.
 EXTRA = {"decode_mfma.hip": ["-fno-honor-nans"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

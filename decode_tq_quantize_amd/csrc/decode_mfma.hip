@@ -44,6 +44,7 @@
 // the current chunk. Partials (max, sum, rotated accumulator) go to the
 // workspace; combine merges the splits and applies R_v^T.
 #include <math.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -1046,6 +1047,19 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
     }
     // (one key buffer: its plane words and key norms are used up; refill them)
     if constexpr (kOneK) load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1, 1>(kc, ka, na, cn - tok_base, rel_last, w, lane);
+    // value norms of tokens at or past the split's end (rows the loads
+    // re-read or the cache never wrote) are cleared before they are used:
+    // token c0 + 64 w + 16 i + tl is in range iff 16 i < rem
+    {
+      const int rem = te - (c0 + 64 * w + tl);
+      const uint32_t mk0 = (rem > 0 ? 0xffffu : 0u) | (rem > 16 ? 0xffff0000u : 0u);
+      const uint32_t mk1 = (rem > 32 ? 0xffffu : 0u) | (rem > 48 ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int gv = 0; gv < NV; ++gv) {
+        kc.nv[gv][0] &= mk0;
+        kc.nv[gv][1] &= mk1;
+      }
+    }
     // ---------------- chunk statistics shared by the four waves
     float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
     mx = row16_max(mx);
@@ -1098,9 +1112,12 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
         uint8_t* dst = &wbuf[buf][gv][ks][4 * hl][kappa];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const float hi = head4(r);
-          dst[128 * m] = (uint8_t)fp8_exact(hi);
-          r = (r - hi) * kDigitStep;
+          // the residual is taken from the digit as stored: below e4m3's
+          // normal range the conversion rounds the leading bits, and that
+          // rounding must pass on to the next digit
+          const uint32_t d8 = fp8_exact(head4(r)) & 0xffu;
+          dst[128 * m] = (uint8_t)d8;
+          r = (r - f32_of_fp8(d8)) * kDigitStep;
         }
         dst[256] = (uint8_t)fp8_of(r);  // the third and last digit, rounded to nearest
       }
@@ -1166,7 +1183,8 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
 #pragma unroll
       for (int s = 0; s < VT; ++s)
         if (s < vme.ntypes) v = fmaf(vme.alpha[s], wsum4(vacc[tt][s]), v);
-      part[2 + 32 * w + 16 * tt + tl] = v * unscale;
+      // a split with no token in range leaves zeros (its weight in the merge is 0)
+      part[2 + 32 * w + 16 * tt + tl] = m_run == -INFINITY ? 0.f : v * unscale;
     }
     if (w == 0 && tl == 0) {
       part[0] = m_run;
@@ -1365,8 +1383,19 @@ DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int
   const int G = Hq / Hkv;
   const int HT = (G + kHT - 1) / kHT;
   const int64_t wgs_per_split = (int64_t)B * Hkv * HT;
-  int64_t splits = (512 + wgs_per_split - 1) / wgs_per_split;
+  // enough splits that every compute unit holds two workgroups (the kernel's
+  // launch bounds) at once
+  const int64_t target = 2 * (int64_t)device_cus();
+  int64_t splits = (target + wgs_per_split - 1) / wgs_per_split;
   int64_t sl = (T_max + splits - 1) / splits;
+  // test hook: TQ_DECODE_SPLIT_TOKENS (a positive multiple of 256) fixes the
+  // split length instead, so that tests can compare results across split
+  // counts; read at every plan, so a size query and the decode it sizes
+  // agree as long as the variable does not change between them
+  if (const char* ev = getenv("TQ_DECODE_SPLIT_TOKENS")) {
+    const long v = strtol(ev, nullptr, 10);
+    if (v > 0 && v % kChunk == 0) sl = v;
+  }
   const int64_t min_sl = (T_max + kMaxCombineSplits - 1) / kMaxCombineSplits;  // the combine's split table
   if (sl < min_sl) sl = min_sl;
   sl = (sl + kChunk - 1) / kChunk * kChunk;

@@ -14,6 +14,13 @@ constexpr int kValuesTile = 32;
 
 inline int planes_of(const tq_quantizer& q) { return q.mse_bits + (q.variant == TQ_PROD ? 1 : 0); }
 
+// Compute units of the current device, queried once per device and kept
+// (256, the MI355X count, when no device answers: host-only size queries).
+int device_cus();
+// Workgroups of `fn` (threads per workgroup) one compute unit holds at once,
+// queried once per (device, kernel) and kept; 1 when the query fails.
+int kernel_wgs_per_cu(const void* fn, int threads);
+
 hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
                            int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s,
                            const int64_t* rows = nullptr, int64_t cache_rows = 0);

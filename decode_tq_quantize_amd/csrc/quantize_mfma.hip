@@ -601,11 +601,8 @@ hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtyp
   const Fn fn = fns[a.bf16 ? 1 : 0][a.B - 1][a.prod ? 1 : 0][layout == TQ_LAYOUT_KEYS ? 1 : 0];
   // persistent grid: as many workgroups as the device holds at once (the
   // rotation-only kernels need far fewer registers and no S in LDS)
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, 0) != hipSuccess)
-    return hipErrorInvalidValue;
-  const int64_t slots = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+  // (both queried once per device and kernel, not per call)
+  const int64_t slots = (int64_t)device_cus() * kernel_wgs_per_cu(reinterpret_cast<const void*>(fn), kThreads);
   const int64_t grid = a.ntiles < slots ? a.ntiles : slots;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();

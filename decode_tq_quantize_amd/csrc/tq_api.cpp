@@ -2,11 +2,52 @@
 // Every check runs before the first device call; on error nothing is written.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "internal.h"
 #include "tq.h"
+
+namespace tqk {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // 0 = not yet queried
+std::mutex g_occ_mu;
+struct OccEntry {
+  int dev;
+  const void* fn;
+  int threads, per_cu;
+};
+OccEntry g_occ[256];
+int g_occ_n = 0;
+}  // namespace
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int c = g_cus[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) return 256;
+  g_cus[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+int kernel_wgs_per_cu(const void* fn, int threads) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  std::lock_guard<std::mutex> lk(g_occ_mu);
+  for (int i = 0; i < g_occ_n; ++i)
+    if (g_occ[i].dev == dev && g_occ[i].fn == fn && g_occ[i].threads == threads) return g_occ[i].per_cu;
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, threads, 0) != hipSuccess || per < 1) per = 1;
+  if (g_occ_n < (int)(sizeof(g_occ) / sizeof(g_occ[0]))) g_occ[g_occ_n++] = OccEntry{dev, fn, threads, per};
+  return per;
+}
+
+}  // namespace tqk
 
 namespace {
 

@@ -115,3 +115,27 @@ def gaussian_mixture(n: int, d: int, n_comp: int, seed: int, stream: int = STREA
     x = means[comp] + g.standard_normal((n, d))
     x /= np.linalg.norm(x, axis=1, keepdims=True)
     return np.ascontiguousarray(x.astype(np.float32)), means
+
+
+def plant_needles(K: np.ndarray, qdir: np.ndarray, cosine: float, seed: int, stream: int = STREAM_QUERY):
+    """Needle-in-a-haystack keys: one planted key per (sequence, KV head).
+
+    K [B, H, T, d] (modified in place and returned with the positions [B, H]);
+    qdir [B, H, d] the query each needle is aimed at. The needle has cosine
+    ``cosine`` with qdir (the rest a random direction orthogonal to it) and
+    the median key norm of its (sequence, head); bf16-valued like K.
+    """
+    B, H, T, d = K.shape
+    g = rng(seed, stream)
+    pos = g.integers(0, T, size=(B, H))
+    qh = qdir / np.linalg.norm(qdir, axis=-1, keepdims=True)
+    rnd = g.standard_normal((B, H, d))
+    rnd -= np.sum(rnd * qh, axis=-1, keepdims=True) * qh
+    rnd /= np.linalg.norm(rnd, axis=-1, keepdims=True)
+    knorm = np.median(np.linalg.norm(K.astype(np.float64), axis=-1), axis=-1)
+    needle = (cosine * qh + np.sqrt(1.0 - cosine * cosine) * rnd) * knorm[..., None]
+    needle = bf16_bits_to_f32(to_bf16_bits(needle.astype(np.float32)))
+    for b in range(B):
+        for h in range(H):
+            K[b, h, pos[b, h]] = needle[b, h]
+    return K, pos

@@ -283,16 +283,21 @@ def check_decode(out, sc, kgroups, vgroups, qry, Hkv, seq_lens):
     o_out, o_sc = otq.decode_attention(qry.astype(np.float64), kgroups, vgroups, Hkv, seq_lens,
                                        1.0 / math.sqrt(D))
     lens = seq_lens if seq_lens is not None else [o_sc.shape[2]] * B
+    worst_out = worst_sc = 0.0
     for b in range(B):
         L = int(lens[b])
         if L == 0:
             assert np.all(out[b] == 0)
             continue
         e_out = normwise_rel_err(out[b], o_out[b])
+        worst_out = max(worst_out, e_out)
         assert e_out <= REL_TOL, f"batch {b}: output error {e_out}"
         if sc is not None:
             e_sc = rowmax_rel_err(sc[b, :, :L], o_sc[b, :, :L])
+            worst_sc = max(worst_sc, e_sc)
             assert e_sc <= REL_TOL, f"batch {b}: score error {e_sc}"
+    # the margin against the 2e-3 tolerance, for the record
+    print(f"decode margin: output {worst_out:.2e}, scores {worst_sc:.2e} (tolerance {REL_TOL:.0e})", flush=True)
     return o_out, o_sc
 
 
@@ -387,22 +392,30 @@ def test_decode_two_channel_groups(fold):
                  [otq.Group(0, va.oq, cva), otq.Group(32, vb.oq, cvb)], qry, Hkv, [200, 150])
 
 
-def paged_group(gq: GpuQuantizer, ch, codes: otq.Codes, table, bt, num_blocks, layout, rng):
+def paged_group(gq: GpuQuantizer, ch, codes: otq.Codes, table, bt, num_blocks, layout, rng, lens=None,
+                garbage=None):
     """One channel group of a paged cache: a pool of num_blocks blocks of bt
     rows per KV head holding every (sequence, head, token) at row
     (table[b, t // bt] * H + g) * bt + t % bt; the other rows hold random
-    codes and finite random norms (never to be read as the cache's)."""
+    codes and finite random norms (never to be read as the cache's). With
+    `garbage` (IEEE half bits), every row that is not a token t < lens[b] of
+    its sequence holds those bits as its norms instead."""
     B, H, T, d = codes.idx.shape
     rows = num_blocks * H * bt
     idx = rng.integers(0, 1 << gq.B, (rows, d)).astype(np.uint8)
     z = (rng.random((rows, d)) < 0.5) if gq.prod else None
     n16 = np.abs(rng.standard_normal(rows)).astype(np.float16)
     r16 = np.abs(rng.standard_normal(rows)).astype(np.float16)
+    if garbage is not None:
+        n16[:] = np.uint16(garbage).view(np.float16)
+        r16[:] = np.uint16(garbage).view(np.float16)
     for b in range(B):
         for g in range(H):
             for t0 in range(0, T, bt):
                 r0 = (int(table[b, t0 // bt]) * H + g) * bt
                 nt = min(bt, T - t0)
+                if garbage is not None:
+                    nt = max(0, min(nt, int(lens[b]) - t0))
                 idx[r0:r0 + nt] = codes.idx[b, g, t0:t0 + nt]
                 if gq.prod:
                     z[r0:r0 + nt] = codes.z[b, g, t0:t0 + nt]
@@ -461,6 +474,82 @@ def test_decode_paged_cache(bt, split):
     check_decode(out.cpu().numpy(), sc.cpu().numpy(), kgs, vgs, qry, Hkv, lens)
 
 
+GARBAGE_HALF_BITS = [0x7E00, 0xFC00, 0x8001, 0x7BFF]  # NaN, -inf, a negative subnormal, the largest half
+SPECS_ONE = ([(0, 128, 3, True, 1)], [(0, 128, 3, False, 2)])
+SPECS_SPLIT = ([(0, 32, 2, True, 1), (32, 96, 1, True, 2)], [(0, 32, 3, False, 3), (32, 96, 2, False, 4)])
+
+
+def _groups(specs, X, lay):
+    gqs, codes = [], []
+    for ch, gd, bits, prod, seed in specs:
+        gq = GpuQuantizer(gd, bits, prod, seed, fold=prod,
+                          r_stream=synth.STREAM_R if lay == "keys" else synth.STREAM_R_V)
+        gqs.append(gq)
+        codes.append(otq.quantize(X[..., ch:ch + gd], gq.oq))
+    return gqs, codes
+
+
+@pytest.mark.parametrize("bits", GARBAGE_HALF_BITS)
+@pytest.mark.parametrize("split", [False, True])
+def test_decode_ignores_rows_past_the_length(bits, split):
+    # rows at or past a sequence's length hold norm bits no quantiser writes
+    # (a cache allocated uninitialised and filled by appends): the decode must
+    # not let them into any result; lengths 1 and 300 leave whole splits empty
+    print(f"decode rows past the length: norm bits {bits:#06x}, groups {2 if split else 1}", flush=True)
+    B, Hq, Hkv, T, d = 3, 16, 2, 1024, 128
+    lens = [1000, 1, 300]
+    K, V = make_kv(B, Hkv, T, d, seed=bits & 0xff)
+    specs_k, specs_v = SPECS_SPLIT if split else SPECS_ONE
+    kq, kcodes = _groups(specs_k, K, "keys")
+    vq, vcodes = _groups(specs_v, V, "values")
+    gbits = np.uint16(bits).view(np.float16)
+    for c in kcodes + vcodes:
+        for b, L in enumerate(lens):
+            c.n16[b, :, L:] = gbits
+            c.rho16[b, :, L:] = gbits
+    kcs = [Cache(gq, specs_k[i][0], kcodes[i], T, "keys") for i, gq in enumerate(kq)]
+    vcs = [Cache(gq, specs_v[i][0], vcodes[i], T, "values") for i, gq in enumerate(vq)]
+    qry = synth.rng(bits, 31).standard_normal((B, Hq, d)).astype(np.float32)
+    out, sc = run_decode(kcs, vcs, qry, Hkv, T, lens, "f32")
+    assert np.isfinite(out).all()
+    with np.errstate(invalid="ignore", over="ignore"):
+        check_decode(out, sc, [otq.Group(s[0], gq.oq, c) for s, gq, c in zip(specs_k, kq, kcodes)],
+                     [otq.Group(s[0], gq.oq, c) for s, gq, c in zip(specs_v, vq, vcodes)], qry, Hkv, lens)
+
+
+@pytest.mark.parametrize("bits", [0x7E00, 0x8001])
+def test_paged_decode_ignores_rows_past_the_length(bits):
+    print(f"paged decode rows past the length: norm bits {bits:#06x}", flush=True)
+    B, Hq, Hkv, T, d, bt = 2, 8, 2, 1500, 128, 512
+    lens = [1500, 300]
+    K, V = make_kv(B, Hkv, T, d, seed=7)
+    rng = synth.rng(7, 5)
+    nbs = -(-T // bt)
+    num_blocks = B * nbs + 2
+    table = np.full((B, nbs + 1), -1, np.int32)
+    table[:, :nbs] = rng.permutation(num_blocks)[:B * nbs].reshape(B, nbs)
+    kcs, vcs, kgs, vgs = [], [], [], []
+    for specs, X, caches, ogs, lay in ((SPECS_SPLIT[0], K, kcs, kgs, "keys"), (SPECS_SPLIT[1], V, vcs, vgs, "values")):
+        gqs, codes = _groups(specs, X, lay)
+        for (ch, *_), gq, c in zip(specs, gqs, codes):
+            caches.append(paged_group(gq, ch, c, table, bt, num_blocks, lay, rng, lens, bits))
+            ogs.append(otq.Group(ch, gq.oq, c))
+    qry = synth.rng(3, 31).standard_normal((B, Hq, d)).astype(np.float32)
+    kd = tq.make_desc([c.group for c in kcs])
+    vd = tq.make_desc([c.group for c in vcs])
+    wsb = tq.tq_decode_paged_workspace_bytes(kd, vd, B, Hq, Hkv, T, bt)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    sc = torch.full((B, Hq, T), float("nan"), dtype=torch.float32, device="cuda")
+    tq.tq_decode_attn_paged(kd, vd, torch_dev(qry), tq.TQ_F32, B, Hq, Hkv, T,
+                            torch_dev(np.asarray(lens, np.int32)), torch_dev(table), nbs + 1, bt, num_blocks,
+                            1.0 / math.sqrt(d), out, sc, ws, wsb)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.isfinite(o).all()
+    check_decode(o, sc.cpu().numpy(), kgs, vgs, qry, Hkv, lens)
+
+
 @pytest.mark.parametrize("fold", [False, True])
 def test_decode_on_gpu_quantized_cache(fold):
     # stage isolation: the GPU quantiser writes the cache, the oracle decodes
@@ -505,6 +594,41 @@ def test_decode_is_deterministic():
     a = run_decode([kc], [vc], qry, Hkv, T, None, "f32")
     b = run_decode([kc], [vc], qry, Hkv, T, None, "f32")
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_decode_across_split_counts(monkeypatch):
+    # the same cache decoded with the sequence cut into splits of 256, 1024
+    # and 4096 tokens (and the shape's own choice): each run repeats bit for
+    # bit, each matches the oracle, and the runs agree within the tolerance
+    # (a missing barrier or a split-boundary error shows up as a difference)
+    B, Hq, Hkv, T = 2, 32, 8, 4096
+    lens = [4096, 2500]
+    K, V = make_kv(B, Hkv, T, 128, seed=5)
+    gk = GpuQuantizer(128, 3, True, seed=1, fold=True)
+    gv = GpuQuantizer(128, 3, False, seed=2, r_stream=synth.STREAM_R_V)
+    ck, cv = otq.quantize(K, gk.oq), otq.quantize(V, gv.oq)
+    kc = Cache(gk, 0, ck, T, "keys")
+    vc = Cache(gv, 0, cv, T, "values")
+    qry = synth.rng(5, 0).standard_normal((B, Hq, 128)).astype(np.float32)
+    kd = tq.make_desc([kc.group])
+    vd = tq.make_desc([vc.group])
+    outs, sizes = [], set()
+    for sl in ("256", "1024", "4096", None):
+        if sl is None:
+            monkeypatch.delenv("TQ_DECODE_SPLIT_TOKENS", raising=False)
+        else:
+            monkeypatch.setenv("TQ_DECODE_SPLIT_TOKENS", sl)
+        print(f"decode split tokens {sl}", flush=True)
+        sizes.add(tq.tq_decode_workspace_bytes(kd, vd, B, Hq, Hkv, T))
+        a = run_decode([kc], [vc], qry, Hkv, T, lens, "f32")
+        b = run_decode([kc], [vc], qry, Hkv, T, lens, "f32")
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1], equal_nan=True)
+        check_decode(a[0], a[1], [otq.Group(0, gk.oq, ck)], [otq.Group(0, gv.oq, cv)], qry, Hkv, lens)
+        outs.append(a[0])
+    assert len(sizes) >= 3  # the partials' workspace follows the split count
+    for o in outs[1:]:
+        for bb in range(B):
+            assert normwise_rel_err(o[bb], outs[0][bb].astype(np.float64)) <= REL_TOL
 
 
 @pytest.mark.parametrize("d", [32, 96, 128, 1536])
