@@ -3,23 +3,26 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
 
-One step is one compressed-KV decode-attention call on the Llama-3.1-8B
-single-layer shape (batch 1, 32 query / 8 KV heads, head_dim 128, 32768
-cached tokens; keys 4-bit TurboQuant_prod = 3 Lloyd-Max bits + 1 QJL bit,
-values 3-bit MSE-only). Inputs are resident in HBM; the timed steps rotate
-over 24 copies of the compressed cache (742 MB, larger than the 256 MB
-Infinity Cache) inside one captured HIP graph, so the number is HBM-bound
-streaming rather than cache hits or Python launch overhead.
+One step is one compressed-KV decode-attention call on the long-context
+batched workload: batch 64 x 131072 cached tokens, 32 query / 8 KV heads,
+head_dim 128, one layer, 2.5 bits per channel (keys: 32 outlier channels at
+2 + 1 bits and 96 channels at 1 + 1 bits of TurboQuant_prod; values: 3 / 2
+bits MSE-only; half norms per group): 84 bytes per (token, KV head), 5.64 GB
+per call, resident in HBM. K calls are captured into one HIP graph and timed
+with HIP events on the launch stream.
 
 The printed JSON line also carries:
-  roofline      decode bytes per call / per-call time from HIP events on the
-                launch stream, against 8 TB/s
-  cpu_baseline  the fp64 oracle timed on this host's cores on the same workload
-  extras        prefill quantize tokens/s (16 seq x 8192 tok x 32 layers x 8 KV
-                heads, K 3-bit prod, V 3-bit MSE), long-context batched decode
-                (batch 64 x 131072 tokens, 2.5 bits/channel in two channel
-                groups) and inner-product search QPS (1M x 1536, 1024 queries,
-                top-10, with recall@10 on a query sample)
+  roofline      the decode kernel's algorithmic bytes per launch / its mean
+                launch time (a graph of its launches alone, found by kernel
+                name), against 8 TB/s; HBM traffic from rocprofv3 counters
+  cpu_baseline  the fp64 oracle on one batch element of the same workload,
+                timed on this host's cores, scaled to the whole batch
+  extras        the single-layer decode (batch 1, 32768 tokens; with its own
+                roofline and oracle baseline), the tiny 64 x 4096 score
+                matrix, prefill quantise tokens/s, vector search (batched and
+                one query at a time), key/value bit allocations, the needle
+                proxy, token append and paged decode, each with its oracle
+                baseline where the pages' metric asks for one
 """
 from __future__ import annotations
 
@@ -34,9 +37,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 METRIC = "compressed-KV decode attn HBM GB/s (% of peak); quantize tokens/s"
+# the decode's arithmetic: query and softmax-weight digits in fp8 e4m3 times
+# fp4-encoded code bit-planes on the matrix cores, fp32 accumulation
+DECODE_DTYPE = "fp8e4m3 x fp4 mfma, fp32 accumulate"
 
 
 def log(*a):
@@ -46,12 +51,12 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=400)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--copies", type=int, default=24)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--only", default="", help="comma list of extras to run: quantize,longctx,search,bits,niah,append,paged")
+    p.add_argument("--only", default="",
+                   help="comma list of extras to run: single,tiny,quantize,search,bits,niah,append,paged")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one 256 MiB device-to-device copy (the known-size reference for the "
                         "FETCH_SIZE / WRITE_SIZE counters)")
@@ -89,83 +94,20 @@ def dev(a, dtype=None):
     return (t.to(dtype) if dtype is not None else t).cuda()
 
 
-# --------------------------------------------------------------------------
-# single-layer decode (the headline)
-# --------------------------------------------------------------------------
+def blas_threads():
+    """Threads numpy's BLAS runs the oracle's products on (what the oracle actually uses)."""
+    try:
+        from threadpoolctl import threadpool_info
 
-def decode_single_layer(args):
-    import numpy as np
-    import torch
-
-    import decode_tq_quantize_amd as tq
-    import synth
-
-    B, Hq, Hkv, T, d = 1, 32, 8, 32768, 128
-    n = B * Hkv * T
-    log("decode: generating inputs")
-    K = synth.kv_with_outliers(B, Hkv, T, d, 4, 10.0, 2, synth.STREAM_DATA, synth.STREAM_OUTLIER)
-    V = synth.kv_with_outliers(B, Hkv, T, d, 4, 10.0, 2, synth.STREAM_NORM, synth.STREAM_R_V)
-    qry = synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.rng(2, synth.STREAM_QUERY).standard_normal(
-        (B, Hq, d)).astype(np.float32)))
-    Rk, Sk = synth.haar_orthogonal(d, 2), synth.gaussian_matrix(d, d, 2)
-    Rv = synth.haar_orthogonal(d, 2, synth.STREAM_R_V)
-    Rk_t, Sk_t, Rv_t = dev(Rk), dev(Sk), dev(Rv)
-    qk = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, Rk_t, Sk_t)
-    SRk = torch.empty(tq.tq_fold_bytes(d) // 4, dtype=torch.float32, device="cuda")
-    tq.tq_quantizer_fold(qk, SRk)  # S R once per quantiser (setup, untimed)
-    qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
-    kp = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, n) // 4, dtype=torch.int32, device="cuda")
-    vp = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, n) // 4, dtype=torch.int32, device="cuda")
-    kn, kr, vn = (torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(3))
-    tq.tq_quantize_kv(qk, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, dev(K.reshape(n, d), torch.bfloat16), n, d, kp, kn, kr)
-    tq.tq_quantize_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, dev(V.reshape(n, d), torch.bfloat16), n, d, vp, vn)
-    copies = []
-    for c in range(args.copies):
-        bufs = [x.clone() for x in (kp, kn, kr, vp, vn)]
-        kd = tq.make_desc([tq.make_group(qk, 0, bufs[0], bufs[1], bufs[2], T)])
-        vd = tq.make_desc([tq.make_group(qv, 0, bufs[3], bufs[4], None, T)])
-        copies.append((bufs, kd, vd))
-    q_t = dev(qry, torch.bfloat16)
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
-    ws_bytes = tq.tq_decode_workspace_bytes(copies[0][1], copies[0][2], B, Hq, Hkv, T)
-    ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
-    scale = 1.0 / math.sqrt(d)
-
-    def call(i):
-        _, kd, vd = copies[i % len(copies)]
-        tq.tq_decode_attn(kd, vd, q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, scale, out, None, ws, ws_bytes)
-
-    for i in range(args.warmup):
-        call(i)
-    torch.cuda.synchronize()
-    log(f"decode: capturing {args.steps} calls into one graph")
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(graph, stream=side):
-            for i in range(args.steps):
-                call(i)
-    torch.cuda.current_stream().wait_stream(side)
-    graph.replay()  # one untimed replay
-    with Timer() as tm:
-        graph.replay()
-    per_call_ms = tm.ms / args.steps
-    bytes_per_call = n * (48 + 16 + 4 + 48 + 2) + B * Hq * d * (2 + 4)
-    gbs = bytes_per_call / (per_call_ms * 1e-3) / 1e9
-    log(f"decode: {per_call_ms * 1e3:.2f} us/call, {gbs:.1f} GB/s")
-    # the decode kernel alone: the same calls captured again, every node but
-    # the decode kernel's removed, the decode launches chained in call order
-    dk_ms = kernel_only_ms(call, args.steps, side)
-    dk_bytes = n * (48 + 16 + 4 + 48 + 2)
-    log(f"decode kernel alone: {dk_ms * 1e3:.2f} us/launch, {dk_bytes / (dk_ms * 1e-3) / 1e9:.1f} GB/s")
-    res = dict(per_call_ms=per_call_ms, wall_ms=tm.wall * 1e3 / args.steps, gbs=gbs, bytes=bytes_per_call,
-               dk_ms=dk_ms, dk_bytes=dk_bytes)
-    res["oracle_inputs"] = (K, V, qry, Rk, Sk, Rv)
-    return res
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
 
 
-def graph_ms(call, steps, warmup=5):
+def graph_ms(call, steps, warmup=3):
     """Mean time per call of `steps` calls captured into one HIP graph (HIP events around one replay)."""
     import torch
 
@@ -183,7 +125,579 @@ def graph_ms(call, steps, warmup=5):
     graph.replay()  # one untimed replay
     with Timer() as tm:
         graph.replay()
-    return tm.ms / steps, side
+    res = (tm.ms / steps, side, tm.wall * 1e3 / steps)
+    del graph
+    return res
+
+
+def _hip_runtime():
+    """The HIP runtime this process already uses (the one torch loaded)."""
+    import ctypes
+
+    for line in open("/proc/self/maps"):
+        if "libamdhip64.so" in line:
+            return ctypes.CDLL(line.split()[-1])
+    raise RuntimeError("HIP runtime not loaded")
+
+
+def kernel_only_ms(call, steps, stream, name="decode_kernel"):
+    """Mean time per launch of the kernel called `name` among the launches of `call`.
+
+    The calls are captured on `stream`; each kernel node's function handle is
+    resolved to its kernel name, every node of another kernel is removed and
+    the kept launches are chained one after another, so each starts when the
+    previous one ends (the interval between two graph kernels is included).
+    """
+    import ctypes
+    from ctypes import byref, c_int, c_size_t, c_uint, c_void_p
+
+    import torch
+
+    class KParams(ctypes.Structure):
+        _fields_ = [("bx", c_uint), ("by", c_uint), ("bz", c_uint), ("extra", c_void_p), ("func", c_void_p),
+                    ("gx", c_uint), ("gy", c_uint), ("gz", c_uint), ("kparams", c_void_p), ("shmem", c_uint)]
+
+    hip = _hip_runtime()
+    hip.hipKernelNameRefByPtr.restype = ctypes.c_char_p
+    hip.hipKernelNameRefByPtr.argtypes = [c_void_p, c_void_p]
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed: HIP error {rc}")
+
+    s = c_void_p(stream.cuda_stream)
+    torch.cuda.synchronize()
+    ok(hip.hipStreamBeginCapture(s, c_int(2)), "hipStreamBeginCapture")  # relaxed mode
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            call(i)
+    g = c_void_p()
+    ok(hip.hipStreamEndCapture(s, byref(g)), "hipStreamEndCapture")
+    try:
+        nn = c_size_t(0)
+        ok(hip.hipGraphGetNodes(g, None, byref(nn)), "hipGraphGetNodes")
+        nodes = (c_void_p * nn.value)()
+        ok(hip.hipGraphGetNodes(g, nodes, byref(nn)), "hipGraphGetNodes")
+        keep, drop, names = [], [], {}
+        for nd in nodes:
+            t = c_int(-1)
+            ok(hip.hipGraphNodeGetType(c_void_p(nd), byref(t)), "hipGraphNodeGetType")
+            hit = False
+            if t.value == 0:  # a kernel node: its function handle -> kernel name
+                p = KParams()
+                ok(hip.hipGraphKernelNodeGetParams(c_void_p(nd), byref(p)), "hipGraphKernelNodeGetParams")
+                if p.func not in names:
+                    nm = hip.hipKernelNameRefByPtr(c_void_p(p.func), s)
+                    names[p.func] = nm.decode() if nm else ""
+                hit = name in names[p.func]
+            (keep if hit else drop).append(nd)
+        if len(keep) != steps:
+            raise RuntimeError(f"expected {steps} launches of {name}, found {len(keep)} "
+                               f"(kernels: {sorted(set(names.values()))})")
+        for nd in drop:
+            ok(hip.hipGraphDestroyNode(c_void_p(nd)), "hipGraphDestroyNode")
+        for a, b in zip(keep, keep[1:]):
+            ok(hip.hipGraphAddDependencies(g, byref(c_void_p(a)), byref(c_void_p(b)), c_size_t(1)),
+               "hipGraphAddDependencies")
+        ex = c_void_p()
+        ok(hip.hipGraphInstantiate(byref(ex), g, None, None, c_size_t(0)), "hipGraphInstantiate")
+        try:
+            with torch.cuda.stream(stream):
+                ok(hip.hipGraphLaunch(ex, s), "hipGraphLaunch")  # one untimed replay
+                with Timer() as tm:
+                    ok(hip.hipGraphLaunch(ex, s), "hipGraphLaunch")
+        finally:
+            torch.cuda.synchronize()
+            hip.hipGraphExecDestroy(ex)
+    finally:
+        hip.hipGraphDestroy(g)
+    return tm.ms / steps
+
+
+def measured_traffic(workload):
+    """HBM bytes of the decode kernels from the committed counter summary of `workload`.
+
+    profiles/traffic_<workload>.json records FETCH_SIZE and WRITE_SIZE per
+    dispatch of each kernel (rocprofv3 --pmc, one counter per run), each
+    scaled by what the same counter reads for a 256 MiB device copy,
+    together with the SHA-256 of the kernel sources they were taken on.
+    Returns None when a source has changed since (the counters no longer
+    describe these kernels).
+    """
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        rec = json.load(open(path))
+        for rel, digest in rec["source_sha256"].items():
+            if hashlib.sha256(open(os.path.join(ROOT, rel), "rb").read()).hexdigest() != digest:
+                return None
+    except (OSError, ValueError, KeyError, AttributeError):
+        return None
+    per = [v for k, v in rec.get("per_kernel", {}).items() if k.startswith("decode_kernel")]
+    if len(per) != 1:
+        return None
+    return {"call": rec.get("bytes_per_call"), "decode_kernel": per[0]["fetch_bytes"] + per[0]["write_bytes"]}
+
+
+def roofline_block(kernel_bytes, kernel_ms, call_bytes, call_ms, traffic, kernel_desc):
+    ach = kernel_bytes / (kernel_ms * 1e-3) / 1e9
+    call = call_bytes / (call_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic["decode_kernel"] if traffic else None,
+            "kernel": kernel_desc, "bytes_per_launch": kernel_bytes, "us_per_launch": round(kernel_ms * 1e3, 3),
+            "whole_call": {"kernels": "everything one tq_decode_attn call launches",
+                           "achieved": round(call, 2), "frac": round(call / HBM_PEAK_GBS, 4),
+                           "bytes_per_call": call_bytes, "us_per_call": round(call_ms * 1e3, 3),
+                           "traffic": traffic["call"] if traffic else None}}
+
+
+# --------------------------------------------------------------------------
+# the headline: long-context batched decode
+# --------------------------------------------------------------------------
+
+LC = dict(B=64, Hq=32, Hkv=8, T=131072, d=128)
+LC_GROUPS_K = [(0, 32, 2, True), (32, 96, 1, True)]     # (first channel, channels, MSE bits, QJL sign)
+LC_GROUPS_V = [(0, 32, 3, False), (32, 96, 2, False)]
+LC_BYTES_PER_TOKEN_HEAD = 84
+
+
+def _lc_matrices(gi, gd, prod, stream):
+    import synth
+
+    seed = 40 + gi + 10 * stream
+    R = synth.haar_orthogonal(gd, seed)
+    S = synth.gaussian_matrix(gd, gd, seed) if prod else None
+    return R, S
+
+
+def longctx_decode(args):
+    """Batch 64 x 131072 tokens; returns timings plus what the CPU baseline needs."""
+    import numpy as np
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    from synth import device as sdev
+
+    B, Hq, Hkv, T, d = LC["B"], LC["Hq"], LC["Hkv"], LC["T"], LC["d"]
+    n = B * Hkv * T
+    keep, descs, host = [], {}, {}
+    for name, groups, layout, stream in (("k", LC_GROUPS_K, tq.TQ_LAYOUT_KEYS, 11),
+                                         ("v", LC_GROUPS_V, tq.TQ_LAYOUT_VALUES, 12)):
+        log(f"longctx: generating {name} ({n * d * 2 / 1e9:.1f} GB bf16), outlier channels first")
+        X = sdev.kv_with_outliers(B, Hkv, T, d, 0, 1.0, seed=4, stream=stream)
+        X[..., :32] *= 10  # the 32 outlier channels, already permuted to the front
+        X = X.view(n, d)
+        host[name] = X[:Hkv * T].float().cpu().numpy()  # batch element 0 (rows (0, g, t))
+        gl = []
+        for gi, (ch, gd, bits, prod) in enumerate(groups):
+            R, S = _lc_matrices(gi, gd, prod, stream)
+            R_t, S_t = dev(R), (dev(S) if prod else None)
+            var = tq.TQ_PROD if prod else tq.TQ_MSE
+            q = tq.tq_quantizer_init(gd, bits, var, R_t, S_t)
+            if prod:
+                SR_t = torch.empty(tq.tq_fold_bytes(gd) // 4, dtype=torch.float32, device="cuda")
+                tq.tq_quantizer_fold(q, SR_t)
+                keep.append(SR_t)
+            pk = torch.empty(tq.tq_packed_bytes(gd, bits, var, layout, n) // 4, dtype=torch.int32, device="cuda")
+            nr = torch.empty(n, dtype=torch.int16, device="cuda")
+            rr = torch.empty(n, dtype=torch.int16, device="cuda") if prod else None
+            tq.tq_quantize_kv(q, layout, tq.TQ_BF16, X[:, ch:], n, d, pk, nr, rr)
+            keep += [R_t, S_t, pk, nr, rr]
+            gl.append(tq.make_group(q, ch, pk, nr, rr, T))
+        torch.cuda.synchronize()
+        del X
+        torch.cuda.empty_cache()
+        descs[name] = tq.make_desc(gl)
+    q_t = torch.randn((B, Hq, d), generator=sdev.generator(4, 13), device="cuda").to(torch.bfloat16)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    wsb = tq.tq_decode_workspace_bytes(descs["k"], descs["v"], B, Hq, Hkv, T)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+
+    def call(i):
+        tq.tq_decode_attn(descs["k"], descs["v"], q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, scale, out, None, ws, wsb)
+
+    log(f"longctx: {args.steps} calls in one graph")
+    ms, side, wall_ms = graph_ms(call, args.steps, args.warmup)
+    dk_ms = kernel_only_ms(call, args.steps, side)
+    kv_bytes = n * LC_BYTES_PER_TOKEN_HEAD
+    call_bytes = kv_bytes + B * Hq * d * (2 + 4)
+    log(f"longctx: {ms:.4f} ms/call ({call_bytes / ms / 1e6:.1f} GB/s); decode kernel {dk_ms:.4f} ms "
+        f"({kv_bytes / dk_ms / 1e6:.1f} GB/s)")
+    # quality (not parity): query heads 0..3 (KV head 0, batch 0) against exact
+    # fp64 attention on the bf16 K and V; one more (untimed) call returns the
+    # raw score estimates
+    scores = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    tq.tq_decode_attn(descs["k"], descs["v"], q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, scale, out, scores, ws, wsb)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    qs = q_t[0, :G].float().cpu().double().numpy()
+    o_gpu = out[0, :G].cpu().double().numpy()
+    s_gpu = scores[0, :G].cpu().double().numpy().T  # [T, G]
+    del scores
+    kb, vb = host["k"][:T].astype(np.float64), host["v"][:T].astype(np.float64)
+    s_ex = kb @ qs.T
+    lg = s_ex * scale
+    pw = np.exp(lg - lg.max(axis=0))
+    o_ex = (pw.T @ vb) / pw.sum(axis=0)[:, None]
+    rel = np.linalg.norm(o_gpu - o_ex, axis=1) / np.linalg.norm(o_ex, axis=1)
+    s_rel = np.linalg.norm(s_gpu - s_ex, axis=0) / np.linalg.norm(s_ex, axis=0)
+    s_cos = (s_gpu * s_ex).sum(axis=0) / (np.linalg.norm(s_gpu, axis=0) * np.linalg.norm(s_ex, axis=0))
+    bf16_bytes = n * d * 2 * 2
+    res = {"per_call_ms": ms, "wall_ms": wall_ms, "call_bytes": call_bytes, "dk_ms": dk_ms, "kv_bytes": kv_bytes,
+           "extras": {"bf16_attention_roofline_ms": round(bf16_bytes / HBM_PEAK_GBS / 1e6, 4),
+                      "speedup_vs_bf16_roofline": round(bf16_bytes / HBM_PEAK_GBS / 1e6 / ms, 3),
+                      "quality_vs_exact_bf16_attention": {
+                          "sample": "batch 0, query heads 0-3 (KV head 0), 131072 tokens",
+                          "score_rel_error": round(float(s_rel.mean()), 4),
+                          "score_cosine": round(float(s_cos.mean()), 4),
+                          "output_rel_error": round(float(rel.mean()), 4)}},
+           "oracle": (host, q_t[:1].float().cpu().numpy())}
+    del keep, descs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_longctx(oracle_inputs, call_bytes):
+    """The oracle's decode of batch element 0 (8 KV heads, 32 query heads, 131072 tokens), x 64."""
+    import numpy as np
+
+    from oracle import tq as otq
+
+    host, qry = oracle_inputs
+    Hkv, T, d = LC["Hkv"], LC["T"], LC["d"]
+    log("cpu baseline (long-context): oracle quantisation of batch element 0 (untimed)")
+    groups = {}
+    for name, specs, stream in (("k", LC_GROUPS_K, 11), ("v", LC_GROUPS_V, 12)):
+        X = host[name].astype(np.float64).reshape(1, Hkv, T, d)
+        gl = []
+        for gi, (ch, gd, bits, prod) in enumerate(specs):
+            R, S = _lc_matrices(gi, gd, prod, stream)
+            oq = otq.make_quantizer(gd, bits, prod, R, S)
+            gl.append(otq.Group(ch, oq, otq.quantize(X[..., ch:ch + gd], oq)))
+        groups[name] = gl
+    threads = blas_threads()
+    log(f"cpu baseline (long-context): oracle decode on {threads} threads")
+    t0 = time.perf_counter()
+    otq.decode_attention(qry.astype(np.float64), groups["k"], groups["v"], Hkv)
+    dt = time.perf_counter() - t0
+    per_call = dt * LC["B"]
+    return {"value": round(call_bytes / per_call / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"batch element 0 of 64 (8 KV heads, 32 query heads, 131072 tokens, both channel groups), "
+                      f"{dt:.2f} s, scaled x64 to the whole call; codes from the oracle's own quantiser (untimed)"}
+
+
+# --------------------------------------------------------------------------
+# extras
+# --------------------------------------------------------------------------
+
+def single_layer_decode(steps=200, copies=24, cpu=True):
+    """Batch 1, 32 q / 8 KV heads, d = 128, 32768 tokens; K 3+1-bit prod, V 3-bit MSE."""
+    import numpy as np
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+
+    B, Hq, Hkv, T, d = 1, 32, 8, 32768, 128
+    n = B * Hkv * T
+    log("single-layer decode: generating inputs")
+    K = synth.kv_with_outliers(B, Hkv, T, d, 4, 10.0, 2, synth.STREAM_DATA, synth.STREAM_OUTLIER)
+    V = synth.kv_with_outliers(B, Hkv, T, d, 4, 10.0, 2, synth.STREAM_NORM, synth.STREAM_R_V)
+    qry = synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.rng(2, synth.STREAM_QUERY).standard_normal(
+        (B, Hq, d)).astype(np.float32)))
+    Rk, Sk = synth.haar_orthogonal(d, 2), synth.gaussian_matrix(d, d, 2)
+    Rv = synth.haar_orthogonal(d, 2, synth.STREAM_R_V)
+    Rk_t, Sk_t, Rv_t = dev(Rk), dev(Sk), dev(Rv)
+    qk = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, Rk_t, Sk_t)
+    SRk = torch.empty(tq.tq_fold_bytes(d) // 4, dtype=torch.float32, device="cuda")
+    tq.tq_quantizer_fold(qk, SRk)  # S R once per quantiser (setup, untimed)
+    qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
+    kp = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, n) // 4, dtype=torch.int32, device="cuda")
+    vp = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, n) // 4, dtype=torch.int32, device="cuda")
+    kn, kr, vn = (torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(3))
+    tq.tq_quantize_kv(qk, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, dev(K.reshape(n, d), torch.bfloat16), n, d, kp, kn, kr)
+    tq.tq_quantize_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, dev(V.reshape(n, d), torch.bfloat16), n, d, vp, vn)
+    # copies of the 31 MB cache rotated inside the graph, so that no call
+    # finds its cache in the 256 MB last-level cache
+    cps = []
+    for _ in range(copies):
+        bufs = [x.clone() for x in (kp, kn, kr, vp, vn)]
+        kd = tq.make_desc([tq.make_group(qk, 0, bufs[0], bufs[1], bufs[2], T)])
+        vd = tq.make_desc([tq.make_group(qv, 0, bufs[3], bufs[4], None, T)])
+        cps.append((bufs, kd, vd))
+    q_t = dev(qry, torch.bfloat16)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    wsb = tq.tq_decode_workspace_bytes(cps[0][1], cps[0][2], B, Hq, Hkv, T)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+
+    def call(i):
+        _, kd, vd = cps[i % len(cps)]
+        tq.tq_decode_attn(kd, vd, q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, scale, out, None, ws, wsb)
+
+    ms, side, _ = graph_ms(call, steps)
+    dk_ms = kernel_only_ms(call, steps, side)
+    kv_bytes = n * 118
+    call_bytes = kv_bytes + B * Hq * d * (2 + 4)
+    res = {"workload": "single-layer decode, Llama-3.1-8B shape: batch 1, 32 q / 8 KV heads, d=128, 32768 tokens; "
+                       f"K 3+1-bit prod, V 3-bit MSE; 118 B per token-head; {copies} cache copies rotated",
+           "us_per_call": round(ms * 1e3, 3), "gbs": round(call_bytes / ms / 1e6, 1),
+           "roofline": roofline_block(kv_bytes, dk_ms, call_bytes, ms, measured_traffic("single_layer_decode"),
+                                      "decode_kernel")}
+    log(f"single-layer decode: {res}")
+    if cpu:
+        from oracle import tq as otq
+
+        oqk = otq.make_quantizer(d, 3, True, Rk, Sk)
+        oqv = otq.make_quantizer(d, 3, False, Rv)
+        ck, cv = otq.quantize(K, oqk), otq.quantize(V, oqv)
+        threads = blas_threads()
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            otq.decode_attention(qry.astype(np.float64), [otq.Group(0, oqk, ck)], [otq.Group(0, oqv, cv)], Hkv)
+            reps += 1
+            if time.perf_counter() - t0 > 8.0 and reps >= 2:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": round(call_bytes / dt / 1e9, 5), "unit": "GB/s", "cores": threads,
+                               "kind": "oracle", "sample": f"the full call, {reps} repetition(s), {dt:.2f} s each; "
+                                                           "codes from the oracle's own quantiser (untimed)"}
+    res["oracle_inputs"] = (K, V, qry, Rk, Sk, Rv)
+    del cps, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def tiny_score_matrix(steps=200, cpu=True):
+    """4096 unit keys, d = 128, 64 queries; PROD b = 2, 3, 4; the 64 x 4096 score matrix."""
+    import numpy as np
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+
+    d, N, Q = 128, 4096, 64
+    keys = synth.unit_gaussian(N, d, 0)
+    qry = synth.unit_gaussian(Q, d, 0, synth.STREAM_QUERY)
+    Vx = synth.unit_gaussian(N, d, 0, synth.STREAM_NORM)
+    R, S = synth.haar_orthogonal(d, 0), synth.gaussian_matrix(d, d, 0)
+    Rv = synth.haar_orthogonal(d, 0, synth.STREAM_R_V)
+    R_t, S_t, Rv_t = dev(R), dev(S), dev(Rv)
+    rows = []
+    for b in (2, 3, 4):
+        qk = tq.tq_quantizer_init(d, b - 1, tq.TQ_PROD, R_t, S_t)
+        SR = torch.empty(tq.tq_fold_bytes(d) // 4, dtype=torch.float32, device="cuda")
+        tq.tq_quantizer_fold(qk, SR)
+        qv = tq.tq_quantizer_init(d, 2, tq.TQ_MSE, Rv_t)
+        kp = torch.empty(tq.tq_packed_bytes(d, b - 1, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, N) // 4, dtype=torch.int32,
+                         device="cuda")
+        vp = torch.empty(tq.tq_packed_bytes(d, 2, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, N) // 4, dtype=torch.int32,
+                         device="cuda")
+        kn, kr, vn = (torch.empty(N, dtype=torch.int16, device="cuda") for _ in range(3))
+        tq.tq_quantize_kv(qk, tq.TQ_LAYOUT_KEYS, tq.TQ_F32, dev(keys), N, d, kp, kn, kr)
+        tq.tq_quantize_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_F32, dev(Vx), N, d, vp, vn)
+        kd = tq.make_desc([tq.make_group(qk, 0, kp, kn, kr, N)])
+        vd = tq.make_desc([tq.make_group(qv, 0, vp, vn, None, N)])
+        q_t = dev(qry.reshape(1, Q, d))
+        out = torch.empty((1, Q, d), dtype=torch.float32, device="cuda")
+        sc = torch.empty((1, Q, N), dtype=torch.float32, device="cuda")
+        wsb = tq.tq_decode_workspace_bytes(kd, vd, 1, Q, 1, N)
+        ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+
+        def call(i):
+            tq.tq_decode_attn(kd, vd, q_t, tq.TQ_F32, 1, Q, 1, N, None, 1 / math.sqrt(d), out, sc, ws, wsb)
+
+        ms, _, _ = graph_ms(call, steps)
+        row = {"bits": b, "us_per_call": round(ms * 1e3, 3), "scores_per_s": round(Q * N / ms * 1e3, 1)}
+        if cpu:
+            from threadpoolctl import threadpool_limits
+
+            from oracle import tq as otq
+
+            oq = otq.make_quantizer(d, b - 1, True, R, S)
+            codes = otq.quantize(keys.astype(np.float64), oq)
+            for label, lim in (("oracle_1_core", 1), ("oracle_all_cores", None)):
+                with threadpool_limits(limits=lim):
+                    threads = blas_threads()
+                    t0 = time.perf_counter()
+                    reps = 0
+                    while time.perf_counter() - t0 < 1.0 or reps < 3:
+                        otq.estimate_ip(qry.astype(np.float64), codes, oq)
+                        reps += 1
+                    dt = (time.perf_counter() - t0) / reps
+                row[label] = {"seconds": round(dt, 5), "scores_per_s": round(Q * N / dt, 1), "cores": threads}
+        rows.append(row)
+        log(f"tiny score matrix: {row}")
+    return {"workload": "4096 keys d=128 and 64 queries, N(0,I) unit-normalised, TurboQuant_prod b=2,3,4; the 64 x "
+                        "4096 score matrix through tq_decode_attn's score output (Hkv=1, Hq=64); launch-bound, "
+                        "parity only (no roofline)", "rows": rows}
+
+
+def quantize_prefill(steps=2, cpu=True):
+    import numpy as np
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+    from synth import device as sdev
+
+    L, S, Tq, H, d = 32, 16, 8192, 8, 128
+    n = S * Tq * H
+    log("quantize: generating 17.2 GB of bf16 K/V on the device")
+    X = torch.empty((L, 2, n, d), dtype=torch.bfloat16, device="cuda")
+    for l in range(L):
+        for t in range(2):
+            sdev.lognormal_norm_vectors(n, d, seed=1000 + 2 * l + t, out=X[l, t])
+    Rk, Sk = synth.haar_orthogonal(d, 3), synth.gaussian_matrix(d, d, 3)
+    Rv = synth.haar_orthogonal(d, 3, synth.STREAM_R_V)
+    Rk_t, Sk_t, Rv_t = dev(Rk), dev(Sk), dev(Rv)
+    qk = tq.tq_quantizer_init(d, 2, tq.TQ_PROD, Rk_t, Sk_t)
+    qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
+    kb = tq.tq_packed_bytes(d, 2, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, n)
+    vb = tq.tq_packed_bytes(d, 3, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, n)
+    kp = torch.empty((L, kb // 4), dtype=torch.int32, device="cuda")
+    vp = torch.empty((L, vb // 4), dtype=torch.int32, device="cuda")
+    kn = torch.empty((L, n), dtype=torch.int16, device="cuda")
+    kr = torch.empty((L, n), dtype=torch.int16, device="cuda")
+    vn = torch.empty((L, n), dtype=torch.int16, device="cuda")
+
+    def step():
+        for l in range(L):
+            tq.tq_quantize_kv(qk, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, X[l, 0], n, d, kp[l], kn[l], kr[l])
+            tq.tq_quantize_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, X[l, 1], n, d, vp[l], vn[l])
+
+    step()
+    with Timer() as tm:
+        for _ in range(steps):
+            step()
+    sec = tm.ms * 1e-3 / steps
+    tokens = S * Tq
+    flops = tokens * L * H * (2 * 2 * d * d + 2 * d * d)
+    bytes_ = tokens * L * H * (2 * d * 2 + (3 * 16 + 4) + (3 * 16 + 2))
+    res = {"tokens_per_s": round(tokens / sec, 1), "ms_per_step": round(sec * 1e3, 3),
+           "workload": "16 seq x 8192 tok x 32 layers x 8 KV heads, d=128, bf16; K 3-bit prod, V 3-bit MSE",
+           "achieved_tflops": round(flops / sec / 1e12, 2), "hbm_gbs": round(bytes_ / sec / 1e9, 1),
+           # the products run on the bf16 matrix cores (operands split into
+           # bf16 high and low parts), so their peak is the bf16 one
+           "flops_roofline_frac_bf16_mfma": round(flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+           "hbm_roofline_frac": round(bytes_ / sec / 1e9 / HBM_PEAK_GBS, 4)}
+    if cpu:
+        from oracle import tq as otq
+
+        # one (layer, KV head) slice: the 131072 vectors of layer 0's first KV
+        # head per tensor (vector (s, t, h) is row (s * 8192 + t) * 8 + h)
+        xs = [X[0, t].view(S * Tq, H, d)[:, 0].float().cpu().numpy().astype(np.float64) for t in (0, 1)]
+        oqk = otq.make_quantizer(d, 2, True, Rk, Sk)
+        oqv = otq.make_quantizer(d, 3, False, Rv)
+        threads = blas_threads()
+        t0 = time.perf_counter()
+        ck = otq.quantize(xs[0], oqk)
+        otq.pack(ck.idx, ck.z, 2, "keys")
+        cv = otq.quantize(xs[1], oqv)
+        otq.pack(cv.idx, None, 3, "values")
+        dt = time.perf_counter() - t0
+        del ck, cv
+        res["cpu_baseline"] = {"value": round(tokens / (dt * L * H), 2), "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"1 layer x 1 KV head (131072 key and 131072 value vectors), {dt:.2f} s, "
+                                         f"scaled x256 to 32 layers x 8 KV heads"}
+    del X
+    torch.cuda.empty_cache()
+    return res
+
+
+def vector_search(steps=2, stream_steps=50, cpu=True):
+    import numpy as np
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+    from synth import device as sdev
+
+    N, d, Q, k = 1 << 20, 1536, 1024, 10
+    log("search: generating the 1M x 1536 database")
+    db, means = sdev.gaussian_mixture(N, d, 256, seed=5, stream=0)
+    qs, _ = sdev.gaussian_mixture(Q, d, 256, seed=5, stream=1, means=means)
+    R, S = synth.haar_orthogonal(d, 5), synth.gaussian_matrix(d, d, 5)
+    R_t, S_t = dev(R), dev(S)
+    q = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, R_t, S_t)
+    pk = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, N) // 4, dtype=torch.int32, device="cuda")
+    nr = torch.empty(N, dtype=torch.int16, device="cuda")
+    rr = torch.empty(N, dtype=torch.int16, device="cuda")
+    tq.tq_quantize_kv(q, tq.TQ_LAYOUT_KEYS, tq.TQ_F32, db, N, d, pk, nr, rr)
+    with Timer() as tq_build:
+        tq.tq_quantize_kv(q, tq.TQ_LAYOUT_KEYS, tq.TQ_F32, db, N, d, pk, nr, rr)
+    g = tq.make_group(q, 0, pk, nr, rr, 0)
+    wsb = tq.tq_search_workspace_bytes(g, N, Q, k)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+    oi = torch.empty((Q, k), dtype=torch.int64, device="cuda")
+    osc = torch.empty((Q, k), dtype=torch.float32, device="cuda")
+    tq.tq_search_topk(g, N, qs, Q, k, oi, osc, ws, wsb)
+    with Timer() as tm:
+        for _ in range(steps):
+            tq.tq_search_topk(g, N, qs, Q, k, oi, osc, ws, wsb)
+    sec = tm.ms * 1e-3 / steps
+    # one query at a time (streaming): the whole database is read per query
+    wsb1 = tq.tq_search_workspace_bytes(g, N, 1, k)
+    ws1 = torch.empty(wsb1 // 4 + 4, dtype=torch.float32, device="cuda")
+    oi1 = torch.empty((1, k), dtype=torch.int64, device="cuda")
+    os1 = torch.empty((1, k), dtype=torch.float32, device="cuda")
+
+    def one(i):
+        tq.tq_search_topk(g, N, qs[i % Q:i % Q + 1], 1, k, oi1, os1, ws1, wsb1)
+
+    ms1, _, _ = graph_ms(one, stream_steps)
+    db_bytes = N * (4 * d // 8 + 4)
+    # recall@10 against exact fp64 inner products on a 64-query sample
+    sample = 64
+    exact = (qs[:sample].double() @ db.double().T)
+    top = torch.topk(exact, k, dim=1).indices.cpu().numpy()
+    got = oi[:sample].cpu().numpy()
+    rec = float(np.mean([len(set(got[i].tolist()) & set(top[i].tolist())) / k for i in range(sample)]))
+    del exact
+    # estimator work: both sums, 2 d multiply-adds per (query, vector)
+    flops = 2.0 * Q * N * 2 * d
+    # what the bf16 matrix cores execute: per coordinate 4 Walsh terms x 2
+    # operand halves + 3 QJL products = 11 multiply-adds per (query, vector)
+    mfma_flops = 2.0 * 11 * Q * N * d
+    res = {"qps": round(Q / sec, 1), "ms_per_batch": round(sec * 1e3, 3), "recall_at_10": round(rec, 4),
+           "estimator_tflops": round(flops / sec / 1e12, 2),
+           "mfma_bf16_tflops_executed": round(mfma_flops / sec / 1e12, 2),
+           "mfma_bf16_roofline_frac": round(mfma_flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+           "streaming": {"qps": round(1e3 / ms1, 1), "us_per_query": round(ms1 * 1e3, 2),
+                         "db_bytes_per_query": db_bytes,
+                         "hbm_gbs": round(db_bytes / ms1 / 1e6, 1),
+                         "hbm_roofline_frac": round(db_bytes / ms1 / 1e6 / HBM_PEAK_GBS, 4),
+                         "how": f"{stream_steps} single-query calls in one graph"},
+           "db_quantize_ms": round(tq_build.ms, 3),
+           "workload": "1M x 1536 fp32 256-component Gaussian mixture, unit-normalised; 1024 queries; "
+                       "4-bit prod (3+1) codes; top-10"}
+    log(f"search: {res}")
+    if cpu:
+        from oracle import tq as otq
+
+        # the oracle searches the GPU's own codes (unpacked on the host, untimed)
+        words = pk.cpu().numpy().view(np.uint32)
+        idx, z = otq.unpack(words, N, d, 3, True, "keys")
+        codes = otq.Codes(idx, z, None, None, nr.cpu().numpy().view(np.float16), rr.cpu().numpy().view(np.float16),
+                          None, None)
+        del words
+        oq = otq.make_quantizer(d, 3, True, R, S)
+        yq = qs[:64].cpu().numpy().astype(np.float64)
+        threads = blas_threads()
+        t0 = time.perf_counter()
+        otq.search_topk(yq, codes, oq, k)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(Q / (dt * 16), 3), "unit": "QPS", "cores": threads, "kind": "oracle",
+                               "sample": f"64 of the 1024 queries against the whole database, {dt:.2f} s, "
+                                         f"scaled x16; the GPU's codes unpacked on the host (untimed)"}
+        del idx, z, codes
+    del db, pk, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 # key / value bit allocations at the single-layer shape: (name, key MSE bits,
@@ -259,7 +773,7 @@ def bit_allocations(inputs, steps=100, copies=12):
             _, kd, vd = cps[i % len(cps)]
             tq.tq_decode_attn(kd, vd, q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, scale, out, None, ws, wsb)
 
-        ms, side = graph_ms(call, steps)
+        ms, side, _ = graph_ms(call, steps)
         dk_ms = kernel_only_ms(call, steps, side)
         kv_bytes = n * ((kb + kprod) * (d // 8) + 2 + 2 * kprod + vb * (d // 8) + 2)
         call_bytes = kv_bytes + B * Hq * d * (2 + 4)
@@ -331,98 +845,18 @@ def append_step(steps=200):
         tq.tq_append_kv(qk, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, xk, n, d, r, C, kp, kn, kr)
         tq.tq_append_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, xv, n, d, r, C, vp, vn)
 
-    ms, _ = graph_ms(call, steps)
+    ms, _, _ = graph_ms(call, steps)
 
     def call_pair(i):
         r = rows[i % len(rows)]
         tq.tq_append_kv_pair(qk, qv, tq.TQ_BF16, xk, xv, n, d, d, r, C, kp, kn, kr, vp, vn)
 
-    ms_pair, _ = graph_ms(call_pair, steps)
+    ms_pair, _, _ = graph_ms(call_pair, steps)
     return {"us_per_step": round(ms_pair * 1e3, 3), "us_per_step_two_calls": round(ms * 1e3, 3),
             "vectors_per_step": 2 * n, "vectors_per_s": round(2 * n / ms_pair * 1e3, 1),
             "workload": "one new token per (sequence, KV head): batch 64 x 8 KV heads, d=128, K 3+1-bit prod and "
                         "V 3-bit MSE appended into a 4096-token-per-head cache (one tq_append_kv_pair call per step; "
                         "two tq_append_kv calls beside it)"}
-
-
-def paged_decode(steps=20):
-    """Decode from a paged cache against the same cache stored contiguously.
-
-    Batch 16 x 32768 tokens, 32 q / 8 KV heads, d = 128, K 3+1-bit prod and
-    V 3-bit MSE (the single-layer law); the paged copy holds every (sequence,
-    KV head) in 4096-token blocks scattered over a shuffled pool.
-    """
-    import numpy as np
-    import torch
-
-    import decode_tq_quantize_amd as tq
-    import synth
-    from synth import device as sdev
-
-    B, Hq, Hkv, T, d, bt = 16, 32, 8, 32768, 128, 4096
-    n = B * Hkv * T
-    nbs = T // bt
-    Rk_t, Sk_t = dev(synth.haar_orthogonal(d, 6)), dev(synth.gaussian_matrix(d, d, 6))
-    Rv_t = dev(synth.haar_orthogonal(d, 6, synth.STREAM_R_V))
-    qk = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, Rk_t, Sk_t)
-    SR = torch.empty(tq.tq_fold_bytes(d) // 4, dtype=torch.float32, device="cuda")
-    tq.tq_quantizer_fold(qk, SR)
-    qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
-    perm = torch.from_numpy(synth.rng(6, 7).permutation(B * nbs).astype(np.int64)).cuda()
-    table = perm.view(B, nbs).to(torch.int32).contiguous()
-    # pool row of (b, g, t): (table[b, t / bt] * Hkv + g) * bt + t % bt
-    b_i = torch.arange(B, device="cuda").view(B, 1, 1, 1)
-    g_i = torch.arange(Hkv, device="cuda").view(1, Hkv, 1, 1)
-    blk = torch.arange(nbs, device="cuda").view(1, 1, nbs, 1)
-    t_i = torch.arange(bt, device="cuda").view(1, 1, 1, bt)
-    rows = ((table.long()[b_i, blk] * Hkv + g_i) * bt + t_i).reshape(-1)  # in (b, g, t) order
-    keep = []
-    descs = {}
-    for name, q, lay, var, st in (("k", qk, tq.TQ_LAYOUT_KEYS, tq.TQ_PROD, 1), ("v", qv, tq.TQ_LAYOUT_VALUES, tq.TQ_MSE, 2)):
-        X = sdev.kv_with_outliers(B, Hkv, T, d, 4, 10.0, seed=6, stream=st).view(n, d)
-        bits = 3
-        pk = torch.empty(tq.tq_packed_bytes(d, bits, var, lay, n) // 4, dtype=torch.int32, device="cuda")
-        pp = torch.zeros_like(pk)
-        nr, pn = (torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(2))
-        rr, pr = ((torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(2)) if var == tq.TQ_PROD
-                  else (None, None))
-        tq.tq_quantize_kv(q, lay, tq.TQ_BF16, X, n, d, pk, nr, rr)
-        tq.tq_append_kv(q, lay, tq.TQ_BF16, X, n, d, rows, n, pp, pn, pr)  # the same vectors into the pool
-        torch.cuda.synchronize()
-        del X
-        keep += [pk, pp, nr, pn, rr, pr]
-        descs[name] = (tq.make_desc([tq.make_group(q, 0, pk, nr, rr, T)]), tq.make_desc([tq.make_group(q, 0, pp, pn, pr, bt)]))
-    q_t = torch.randn((B, Hq, d), generator=sdev.generator(6, 8), device="cuda").to(torch.bfloat16)
-    out_c = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
-    out_p = torch.empty_like(out_c)
-    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
-    wsc = tq.tq_decode_workspace_bytes(descs["k"][0], descs["v"][0], B, Hq, Hkv, T)
-    wsp = tq.tq_decode_paged_workspace_bytes(descs["k"][1], descs["v"][1], B, Hq, Hkv, T, bt)
-    ws_c = torch.empty(wsc // 4 + 4, dtype=torch.float32, device="cuda")
-    ws_p = torch.empty(wsp // 4 + 4, dtype=torch.float32, device="cuda")
-
-    def contiguous():
-        tq.tq_decode_attn(descs["k"][0], descs["v"][0], q_t, tq.TQ_BF16, B, Hq, Hkv, T, lens, 1 / math.sqrt(d),
-                          out_c, None, ws_c, wsc)
-
-    def paged():
-        tq.tq_decode_attn_paged(descs["k"][1], descs["v"][1], q_t, tq.TQ_BF16, B, Hq, Hkv, T, lens, table, nbs, bt,
-                                B * nbs, 1 / math.sqrt(d), out_p, None, ws_p, wsp)
-
-    res = {}
-    for name, fn in (("contiguous", contiguous), ("paged", paged)):
-        fn()
-        with Timer() as tm:
-            for _ in range(steps):
-                fn()
-        res[name] = tm.ms / steps
-    diff = float((out_p - out_c).norm() / out_c.norm())
-    bytes_ = n * 118 + B * Hq * d * 6
-    return {"contiguous_ms": round(res["contiguous"], 4), "paged_ms": round(res["paged"], 4),
-            "paged_gbs": round(bytes_ / res["paged"] / 1e6, 1), "paged_hbm_frac": round(bytes_ / res["paged"] / 1e6 / HBM_PEAK_GBS, 4),
-            "paged_vs_contiguous_output_rel_diff": diff,
-            "workload": "batch 16 x 32768 tokens, 32 q / 8 KV heads, d=128, K 3+1-bit prod, V 3-bit MSE; paged copy in "
-                        "4096-token blocks over a shuffled pool (written with tq_append_kv)"}
 
 
 NIAH_KEYS = [("3+1 prod", 3, True), ("4 MSE-only", 4, False), ("2+1 prod", 2, True), ("3 MSE-only", 3, False),
@@ -512,340 +946,114 @@ def niah_proxy(lengths=(1024, 4096, 16384), cosines=(0.4, 0.5), B=8):
             "rows": rows}
 
 
-def _hip_runtime():
-    """The HIP runtime this process already uses (the one torch loaded)."""
-    import ctypes
+def paged_decode(steps=20):
+    """Decode from a paged cache against the same cache stored contiguously.
 
-    for line in open("/proc/self/maps"):
-        if "libamdhip64.so" in line:
-            return ctypes.CDLL(line.split()[-1])
-    raise RuntimeError("HIP runtime not loaded")
-
-
-def kernel_only_ms(call, steps, stream):
-    """Mean time per launch of the largest-grid kernel of `call`, in a graph.
-
-    The calls are captured on `stream`; every other node is removed and the
-    kept launches are chained one after another, so each starts when the
-    previous one ends (the interval between two graph kernels is included).
+    Batch 16 x 32768 tokens, 32 q / 8 KV heads, d = 128, K 3+1-bit prod and
+    V 3-bit MSE (the single-layer law). The pool's 4096-token blocks are
+    copies of the contiguous cache's block slices scattered over a shuffled
+    pool, so the two decodes read the same codes and differ only in
+    addressing and split lengths. Separately, the same vectors are quantised
+    by the append path (the general kernel) to report how often it decides a
+    code bit differently from the bulk matrix-core quantiser.
     """
-    import ctypes
-    from ctypes import byref, c_int, c_size_t, c_uint, c_void_p
-
-    import torch
-
-    class KParams(ctypes.Structure):
-        _fields_ = [("bx", c_uint), ("by", c_uint), ("bz", c_uint), ("extra", c_void_p), ("func", c_void_p),
-                    ("gx", c_uint), ("gy", c_uint), ("gz", c_uint), ("kparams", c_void_p), ("shmem", c_uint)]
-
-    hip = _hip_runtime()
-
-    def ok(rc, what):
-        if rc != 0:
-            raise RuntimeError(f"{what} failed: HIP error {rc}")
-
-    s = c_void_p(stream.cuda_stream)
-    torch.cuda.synchronize()
-    ok(hip.hipStreamBeginCapture(s, c_int(2)), "hipStreamBeginCapture")  # relaxed mode
-    with torch.cuda.stream(stream):
-        for i in range(steps):
-            call(i)
-    g = c_void_p()
-    ok(hip.hipStreamEndCapture(s, byref(g)), "hipStreamEndCapture")
-    try:
-        nn = c_size_t(0)
-        ok(hip.hipGraphGetNodes(g, None, byref(nn)), "hipGraphGetNodes")
-        nodes = (c_void_p * nn.value)()
-        ok(hip.hipGraphGetNodes(g, nodes, byref(nn)), "hipGraphGetNodes")
-        size = []
-        for nd in nodes:
-            t = c_int(-1)
-            ok(hip.hipGraphNodeGetType(c_void_p(nd), byref(t)), "hipGraphNodeGetType")
-            if t.value != 0:  # not a kernel node
-                size.append(-1)
-                continue
-            p = KParams()
-            ok(hip.hipGraphKernelNodeGetParams(c_void_p(nd), byref(p)), "hipGraphKernelNodeGetParams")
-            size.append(p.gx * p.gy * p.gz)
-        big = max(size)
-        keep = [nd for nd, z in zip(nodes, size) if z == big]
-        if len(keep) != steps:
-            raise RuntimeError(f"expected {steps} launches of the largest kernel, found {len(keep)}")
-        for nd, z in zip(nodes, size):
-            if z != big:
-                ok(hip.hipGraphDestroyNode(c_void_p(nd)), "hipGraphDestroyNode")
-        for a, b in zip(keep, keep[1:]):
-            ok(hip.hipGraphAddDependencies(g, byref(c_void_p(a)), byref(c_void_p(b)), c_size_t(1)),
-               "hipGraphAddDependencies")
-        ex = c_void_p()
-        ok(hip.hipGraphInstantiate(byref(ex), g, None, None, c_size_t(0)), "hipGraphInstantiate")
-        try:
-            with torch.cuda.stream(stream):
-                ok(hip.hipGraphLaunch(ex, s), "hipGraphLaunch")  # one untimed replay
-                with Timer() as tm:
-                    ok(hip.hipGraphLaunch(ex, s), "hipGraphLaunch")
-        finally:
-            torch.cuda.synchronize()
-            hip.hipGraphExecDestroy(ex)
-    finally:
-        hip.hipGraphDestroy(g)
-    return tm.ms / steps
-
-
-def measured_traffic():
-    """HBM bytes per decode call from the committed counter summary.
-
-    profiles/decode_traffic.json records FETCH_SIZE and WRITE_SIZE of the
-    decode kernels (rocprofv3 --pmc, one counter per run), each scaled by what
-    the same counter reads for a 256 MiB device copy, together with the
-    SHA-256 of the kernel source they were taken on. Returns None when the
-    source has changed since (the counters no longer describe this kernel).
-    """
-    import hashlib
-
-    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
-    src = os.path.join(ROOT, "decode_tq_quantize_amd", "csrc", "decode_mfma.hip")
-    try:
-        rec = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    except (OSError, ValueError):
-        return None
-    if rec.get("source_sha256") != digest:
-        return None
-    per = [v for k, v in rec.get("per_kernel", {}).items() if k.startswith("decode_kernel")]
-    if len(per) != 1:
-        return None
-    return {"call": rec.get("bytes_per_call"), "decode_kernel": per[0]["fetch_bytes"] + per[0]["write_bytes"]}
-
-
-def cpu_baseline_decode(inputs, bytes_per_call):
     import numpy as np
-
-    import synth  # noqa: F401
-    from oracle import tq as otq
-
-    K, V, qry, Rk, Sk, Rv = inputs
-    cores = len(os.sched_getaffinity(0))
-    log(f"cpu baseline: oracle decode on {cores} cores")
-    oqk = otq.make_quantizer(128, 3, True, Rk, Sk)
-    oqv = otq.make_quantizer(128, 3, False, Rv)
-    ck, cv = otq.quantize(K, oqk), otq.quantize(V, oqv)
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        otq.decode_attention(qry.astype(np.float64), [otq.Group(0, oqk, ck)], [otq.Group(0, oqv, cv)], 8)
-        reps += 1
-        if time.perf_counter() - t0 > 10.0 and reps >= 3:  # about 10 s of CPU work, 3 repetitions at least
-            break
-    dt = (time.perf_counter() - t0) / reps
-    return {"value": round(bytes_per_call / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"the full single-layer decode step (32 heads x 32768 tokens), {reps} repetition(s), "
-                      f"{dt:.2f} s each; codes from the oracle's own quantiser (untimed)"}
-
-
-# --------------------------------------------------------------------------
-# extras
-# --------------------------------------------------------------------------
-
-def quantize_prefill(steps=2):
     import torch
 
     import decode_tq_quantize_amd as tq
     import synth
     from synth import device as sdev
 
-    L, S, Tq, H, d = 32, 16, 8192, 8, 128
-    n = S * Tq * H
-    log("quantize: generating 17.2 GB of bf16 K/V on the device")
-    X = torch.empty((L, 2, n, d), dtype=torch.bfloat16, device="cuda")
-    for l in range(L):
-        for t in range(2):
-            sdev.lognormal_norm_vectors(n, d, seed=1000 + 2 * l + t, out=X[l, t])
-    Rk_t, Sk_t = dev(synth.haar_orthogonal(d, 3)), dev(synth.gaussian_matrix(d, d, 3))
-    Rv_t = dev(synth.haar_orthogonal(d, 3, synth.STREAM_R_V))
-    qk = tq.tq_quantizer_init(d, 2, tq.TQ_PROD, Rk_t, Sk_t)
-    qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
-    kb = tq.tq_packed_bytes(d, 2, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, n)
-    vb = tq.tq_packed_bytes(d, 3, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, n)
-    kp = torch.empty((L, kb // 4), dtype=torch.int32, device="cuda")
-    vp = torch.empty((L, vb // 4), dtype=torch.int32, device="cuda")
-    kn = torch.empty((L, n), dtype=torch.int16, device="cuda")
-    kr = torch.empty((L, n), dtype=torch.int16, device="cuda")
-    vn = torch.empty((L, n), dtype=torch.int16, device="cuda")
-
-    def step():
-        for l in range(L):
-            tq.tq_quantize_kv(qk, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, X[l, 0], n, d, kp[l], kn[l], kr[l])
-            tq.tq_quantize_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, X[l, 1], n, d, vp[l], vn[l])
-
-    step()
-    with Timer() as tm:
-        for _ in range(steps):
-            step()
-    sec = tm.ms * 1e-3 / steps
-    tokens = S * Tq
-    flops = tokens * L * H * (2 * 2 * d * d + 2 * d * d)
-    bytes_ = tokens * L * H * (2 * d * 2 + (3 * 16 + 4) + (3 * 16 + 2))
-    res = {"tokens_per_s": round(tokens / sec, 1), "ms_per_step": round(sec * 1e3, 3),
-           "workload": "16 seq x 8192 tok x 32 layers x 8 KV heads, d=128, bf16; K 3-bit prod, V 3-bit MSE",
-           "achieved_tflops": round(flops / sec / 1e12, 2), "hbm_gbs": round(bytes_ / sec / 1e9, 1),
-           # the products run on the bf16 matrix cores (operands split into bf16
-           # high and low parts), so their own peak is the bf16 one; the fp32
-           # figure is what a plain fp32 implementation would be held to
-           "flops_roofline_frac_bf16_mfma": round(flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-           "flops_roofline_frac_fp32_vector": round(flops / sec / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
-           "hbm_roofline_frac": round(bytes_ / sec / 1e9 / HBM_PEAK_GBS, 4)}
-    del X
-    torch.cuda.empty_cache()
-    return res
-
-
-def longctx_decode(steps=5):
-    import torch
-
-    import decode_tq_quantize_amd as tq
-    import synth
-    from synth import device as sdev
-
-    B, Hq, Hkv, T, d = 64, 32, 8, 131072, 128
+    B, Hq, Hkv, T, d, bt = 16, 32, 8, 32768, 128, 4096
     n = B * Hkv * T
-    groups_k = [(0, 32, 2, tq.TQ_PROD), (32, 96, 1, tq.TQ_PROD)]
-    groups_v = [(0, 32, 3, tq.TQ_MSE), (32, 96, 2, tq.TQ_MSE)]
-    keep = []
-    descs = {}
-    sample = {}  # the bf16 K and V of (batch 0, KV head 0), for the quality check
-    for name, groups, layout, stream in (("k", groups_k, tq.TQ_LAYOUT_KEYS, 11), ("v", groups_v, tq.TQ_LAYOUT_VALUES, 12)):
-        log(f"longctx: generating {name} ({n * d * 2 / 1e9:.1f} GB bf16), outlier channels first")
-        X = sdev.kv_with_outliers(B, Hkv, T, d, 0, 1.0, seed=4, stream=stream)
-        X[..., :32] *= 10  # the 32 outlier channels, already permuted to the front
-        X = X.view(n, d)
-        sample[name] = X[:T].float().cpu().double().numpy()  # rows (b, g, t) -> b = 0, g = 0
-        gl = []
-        for gi, (ch, gd, bits, var) in enumerate(groups):
-            R_t = dev(synth.haar_orthogonal(gd, 40 + gi + 10 * stream))
-            S_t = dev(synth.gaussian_matrix(gd, gd, 40 + gi + 10 * stream)) if var == tq.TQ_PROD else None
-            q = tq.tq_quantizer_init(gd, bits, var, R_t, S_t)
-            if var == tq.TQ_PROD:
-                SR_t = torch.empty(tq.tq_fold_bytes(gd) // 4, dtype=torch.float32, device="cuda")
-                tq.tq_quantizer_fold(q, SR_t)
-                keep.append(SR_t)
-            pk = torch.empty(tq.tq_packed_bytes(gd, bits, var, layout, n) // 4, dtype=torch.int32, device="cuda")
-            nr = torch.empty(n, dtype=torch.int16, device="cuda")
-            rr = torch.empty(n, dtype=torch.int16, device="cuda") if var == tq.TQ_PROD else None
-            tq.tq_quantize_kv(q, layout, tq.TQ_BF16, X[:, ch:], n, d, pk, nr, rr)
-            keep += [R_t, S_t, pk, nr, rr]
-            gl.append(tq.make_group(q, ch, pk, nr, rr, T))
+    nbs = T // bt
+    Rk_t, Sk_t = dev(synth.haar_orthogonal(d, 6)), dev(synth.gaussian_matrix(d, d, 6))
+    Rv_t = dev(synth.haar_orthogonal(d, 6, synth.STREAM_R_V))
+    qk = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, Rk_t, Sk_t)
+    SR = torch.empty(tq.tq_fold_bytes(d) // 4, dtype=torch.float32, device="cuda")
+    tq.tq_quantizer_fold(qk, SR)
+    qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
+    perm = torch.from_numpy(synth.rng(6, 7).permutation(B * nbs).astype(np.int64)).cuda()
+    table = perm.view(B, nbs).to(torch.int32).contiguous()
+    # block (b, g, j) of the contiguous cache -> pool block table[b, j] * Hkv + g
+    src_blk = torch.arange(B * Hkv * nbs, device="cuda")
+    b_i = src_blk // (Hkv * nbs)
+    g_i = (src_blk // nbs) % Hkv
+    j_i = src_blk % nbs
+    dst_blk = table.long()[b_i, j_i] * Hkv + g_i
+    keep, descs, flips = [], {}, {}
+    identity = torch.arange(n, device="cuda", dtype=torch.int64)
+    for name, q, lay, var, st in (("k", qk, tq.TQ_LAYOUT_KEYS, tq.TQ_PROD, 1),
+                                  ("v", qv, tq.TQ_LAYOUT_VALUES, tq.TQ_MSE, 2)):
+        X = sdev.kv_with_outliers(B, Hkv, T, d, 4, 10.0, seed=6, stream=st).view(n, d)
+        nb = tq.tq_packed_bytes(d, 3, var, lay, n)
+        pk = torch.empty(nb // 4, dtype=torch.int32, device="cuda")
+        nr = torch.empty(n, dtype=torch.int16, device="cuda")
+        rr = torch.empty(n, dtype=torch.int16, device="cuda") if var == tq.TQ_PROD else None
+        tq.tq_quantize_kv(q, lay, tq.TQ_BF16, X, n, d, pk, nr, rr)
+        # the pool: each block slice copied to its shuffled place (blocks are
+        # whole tiles of both layouts, so a block is one contiguous range)
+        pp = torch.zeros_like(pk)
+        pp.view(B * Hkv * nbs, -1)[dst_blk] = pk.view(B * Hkv * nbs, -1)[src_blk]
+        pn = torch.zeros_like(nr)
+        pn.view(B * Hkv * nbs, bt)[dst_blk] = nr.view(B * Hkv * nbs, bt)[src_blk]
+        pr = None
+        if rr is not None:
+            pr = torch.zeros_like(rr)
+            pr.view(B * Hkv * nbs, bt)[dst_blk] = rr.view(B * Hkv * nbs, bt)[src_blk]
+        # the append path's codes for the same vectors, row for row
+        ap = torch.zeros_like(pk)
+        an = torch.zeros_like(nr)
+        ar = torch.zeros_like(rr) if rr is not None else None
+        tq.tq_append_kv(q, lay, tq.TQ_BF16, X, n, d, identity, n, ap, an, ar)
         torch.cuda.synchronize()
-        del X
-        torch.cuda.empty_cache()
-        descs[name] = tq.make_desc(gl)
-    q_t = torch.randn((B, Hq, d), generator=sdev.generator(4, 13), device="cuda").to(torch.bfloat16)
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
-    wsb = tq.tq_decode_workspace_bytes(descs["k"], descs["v"], B, Hq, Hkv, T)
-    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+        xor = torch.bitwise_xor(ap, pk)
+        bits_diff = int(sum(int(((xor >> s) & 1).sum()) for s in range(32)))
+        flips[name] = {"code_and_sign_bits_differing": bits_diff, "bits": nb * 8,
+                       "rate": bits_diff / (nb * 8),
+                       "norms_differing": int((an != nr).sum()),
+                       "residual_norms_differing": int((ar != rr).sum()) if rr is not None else 0}
+        del X, ap, an, ar, xor
+        keep += [pk, pp, nr, pn, rr, pr]
+        descs[name] = (tq.make_desc([tq.make_group(q, 0, pk, nr, rr, T)]),
+                       tq.make_desc([tq.make_group(q, 0, pp, pn, pr, bt)]))
+    q_t = torch.randn((B, Hq, d), generator=sdev.generator(6, 8), device="cuda").to(torch.bfloat16)
+    out_c = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    out_p = torch.empty_like(out_c)
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    wsc = tq.tq_decode_workspace_bytes(descs["k"][0], descs["v"][0], B, Hq, Hkv, T)
+    wsp = tq.tq_decode_paged_workspace_bytes(descs["k"][1], descs["v"][1], B, Hq, Hkv, T, bt)
+    ws_c = torch.empty(wsc // 4 + 4, dtype=torch.float32, device="cuda")
+    ws_p = torch.empty(wsp // 4 + 4, dtype=torch.float32, device="cuda")
 
-    def call():
-        tq.tq_decode_attn(descs["k"], descs["v"], q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, 1 / math.sqrt(d), out,
-                          None, ws, wsb)
+    def contiguous(i=0):
+        tq.tq_decode_attn(descs["k"][0], descs["v"][0], q_t, tq.TQ_BF16, B, Hq, Hkv, T, lens, 1 / math.sqrt(d),
+                          out_c, None, ws_c, wsc)
 
-    call()
-    with Timer() as tm:
-        for _ in range(steps):
-            call()
-    ms = tm.ms / steps
-    # quality (not parity): query heads 0..3 (KV head 0, batch 0) against exact
-    # fp64 attention on the bf16 K and V. One more (untimed) call returns the
-    # raw score estimates. With i.i.d. keys and 131072 tokens the softmax is
-    # nearly flat, so the exact output is an average near the noise floor;
-    # the output error is therefore also given relative to the rms value norm.
-    import numpy as np
-    scores = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
-    tq.tq_decode_attn(descs["k"], descs["v"], q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, 1 / math.sqrt(d), out,
-                      scores, ws, wsb)
-    torch.cuda.synchronize()
-    G = Hq // Hkv
-    qs = q_t[0, :G].float().cpu().double().numpy()
-    o_gpu = out[0, :G].cpu().double().numpy()
-    s_gpu = scores[0, :G].cpu().double().numpy().T  # [T, G]
-    del scores
-    s_ex = sample["k"] @ qs.T  # [T, G] exact inner products
-    lg = s_ex / math.sqrt(d)
-    pw = np.exp(lg - lg.max(axis=0))
-    o_ex = (pw.T @ sample["v"]) / pw.sum(axis=0)[:, None]
-    rel = np.linalg.norm(o_gpu - o_ex, axis=1) / np.linalg.norm(o_ex, axis=1)
-    vrms = math.sqrt(float((sample["v"] ** 2).sum(axis=1).mean()))
-    rel_v = np.linalg.norm(o_gpu - o_ex, axis=1) / vrms
-    s_rel = np.linalg.norm(s_gpu - s_ex, axis=0) / np.linalg.norm(s_ex, axis=0)
-    s_cos = (s_gpu * s_ex).sum(axis=0) / (np.linalg.norm(s_gpu, axis=0) * np.linalg.norm(s_ex, axis=0))
-    bytes_ = n * 84 + B * Hq * d * 6
-    bf16_bytes = n * d * 2 * 2
-    res = {"ms_per_call": round(ms, 4), "gbs": round(bytes_ / ms / 1e6, 1),
-           "hbm_roofline_frac": round(bytes_ / ms / 1e6 / HBM_PEAK_GBS, 4),
-           "bf16_attention_roofline_ms": round(bf16_bytes / HBM_PEAK_GBS / 1e6, 4),
-           "speedup_vs_bf16_roofline": round(bf16_bytes / HBM_PEAK_GBS / 1e6 / ms, 3),
-           "quality_vs_exact_bf16_attention": {
-               "sample": "batch 0, query heads 0-3 (KV head 0), 131072 tokens",
-               "score_rel_error": round(float(s_rel.mean()), 4), "score_cosine": round(float(s_cos.mean()), 4),
-               "output_rel_error": round(float(rel.mean()), 4),
-               "output_error_over_rms_value_norm": round(float(rel_v.mean()), 6)},
-           "workload": "batch 64 x 131072 tokens, 32 q / 8 KV heads, d=128; keys: 32 outlier channels 2+1 bits, "
-                       "96 channels 1+1 bits; values 3 / 2 bits MSE; 84 B per token-head"}
-    del keep, descs
-    torch.cuda.empty_cache()
-    return res
+    def paged(i=0):
+        tq.tq_decode_attn_paged(descs["k"][1], descs["v"][1], q_t, tq.TQ_BF16, B, Hq, Hkv, T, lens, table, nbs, bt,
+                                B * nbs, 1 / math.sqrt(d), out_p, None, ws_p, wsp)
+
+    res = {}
+    for name, fn in (("contiguous", contiguous), ("paged", paged)):
+        res[name], _, _ = graph_ms(fn, steps)
+    diff = (out_p - out_c).double().norm(dim=-1) / out_c.double().norm(dim=-1)
+    bytes_ = n * 118 + B * Hq * d * 6
+    return {"contiguous_ms": round(res["contiguous"], 4), "paged_ms": round(res["paged"], 4),
+            "paged_gbs": round(bytes_ / res["paged"] / 1e6, 1),
+            "paged_hbm_frac": round(bytes_ / res["paged"] / 1e6 / HBM_PEAK_GBS, 4),
+            "paged_vs_contiguous_output_rel_diff_max": float(diff.max()),
+            "append_vs_bulk_quantiser": flips,
+            "workload": "batch 16 x 32768 tokens, 32 q / 8 KV heads, d=128, K 3+1-bit prod, V 3-bit MSE; the paged "
+                        "copy is the contiguous cache's 4096-token blocks over a shuffled pool"}
 
 
-def vector_search(steps=2):
-    import numpy as np
-    import torch
-
-    import decode_tq_quantize_amd as tq
-    import synth
-    from synth import device as sdev
-
-    N, d, Q, k = 1 << 20, 1536, 1024, 10
-    log("search: generating the 1M x 1536 database")
-    db, means = sdev.gaussian_mixture(N, d, 256, seed=5, stream=0)
-    qs, _ = sdev.gaussian_mixture(Q, d, 256, seed=5, stream=1, means=means)
-    R_t, S_t = dev(synth.haar_orthogonal(d, 5)), dev(synth.gaussian_matrix(d, d, 5))
-    q = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, R_t, S_t)
-    pk = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, N) // 4, dtype=torch.int32, device="cuda")
-    nr = torch.empty(N, dtype=torch.int16, device="cuda")
-    rr = torch.empty(N, dtype=torch.int16, device="cuda")
-    with Timer() as tq_build:
-        tq.tq_quantize_kv(q, tq.TQ_LAYOUT_KEYS, tq.TQ_F32, db, N, d, pk, nr, rr)
-    g = tq.make_group(q, 0, pk, nr, rr, 0)
-    wsb = tq.tq_search_workspace_bytes(g, N, Q, k)
-    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
-    oi = torch.empty((Q, k), dtype=torch.int64, device="cuda")
-    osc = torch.empty((Q, k), dtype=torch.float32, device="cuda")
-    tq.tq_search_topk(g, N, qs, Q, k, oi, osc, ws, wsb)
-    with Timer() as tm:
-        for _ in range(steps):
-            tq.tq_search_topk(g, N, qs, Q, k, oi, osc, ws, wsb)
-    sec = tm.ms * 1e-3 / steps
-    # recall@10 against exact fp64 inner products on a 64-query sample
-    sample = 64
-    exact = (qs[:sample].double() @ db.double().T)
-    top = torch.topk(exact, k, dim=1).indices.cpu().numpy()
-    got = oi[:sample].cpu().numpy()
-    rec = float(np.mean([len(set(got[i].tolist()) & set(top[i].tolist())) / k for i in range(sample)]))
-    # estimator work: both sums, 2 d multiply-adds per (query, vector)
-    flops = 2.0 * Q * N * 2 * d
-    # what the bf16 matrix cores execute: per coordinate 4 Walsh terms x 2
-    # operand halves + 3 QJL products = 11 multiply-adds per (query, vector)
-    mfma_flops = 2.0 * 11 * Q * N * d
-    res = {"qps": round(Q / sec, 1), "ms_per_batch": round(sec * 1e3, 3), "recall_at_10": round(rec, 4),
-           "estimator_tflops": round(flops / sec / 1e12, 2),
-           "mfma_bf16_tflops_executed": round(mfma_flops / sec / 1e12, 2),
-           "mfma_bf16_roofline_frac": round(mfma_flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-           "db_quantize_ms": round(tq_build.ms, 3),
-           "streamed_db_bytes": N * (4 * 1536 // 8 + 4),
-           "workload": "1M x 1536 fp32 256-component Gaussian mixture, unit-normalised; 1024 queries; "
-                       "4-bit prod (3+1) codes; top-10"}
-    del db, pk, ws
-    torch.cuda.empty_cache()
-    return res
+def run_extra(extras, name, fn):
+    try:
+        extras[name] = fn()
+    except Exception as e:  # an extra that fails is reported, not hidden
+        extras[name] = {"error": repr(e)}
+    log(f"{name}: {extras[name]}")
 
 
 def main():
@@ -870,76 +1078,60 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    main_res = decode_single_layer(args)
-    extras = {}
-    only = set(x for x in args.only.split(",") if x)
-    if not args.no_extras:
-        for name, fn in (("quantize_prefill", quantize_prefill), ("longctx_decode", longctx_decode),
-                         ("vector_search", vector_search)):
-            key = name.split("_")[0]
-            if only and key not in only and name not in only:
-                continue
-            try:
-                extras[name] = fn()
-            except Exception as e:  # an extra that fails is reported, not hidden
-                extras[name] = {"error": repr(e)}
-            log(f"{name}: {extras[name]}")
-        if not only or "paged" in only:
-            try:
-                extras["paged_decode"] = paged_decode()
-            except Exception as e:
-                extras["paged_decode"] = {"error": repr(e)}
-            log(f"paged_decode: {extras['paged_decode']}")
-        if not only or "append" in only:
-            try:
-                extras["append_step"] = append_step()
-            except Exception as e:
-                extras["append_step"] = {"error": repr(e)}
-            log(f"append_step: {extras['append_step']}")
-        if not only or "niah" in only:
-            try:
-                extras["niah_proxy"] = niah_proxy()
-            except Exception as e:
-                extras["niah_proxy"] = {"error": repr(e)}
-        if not only or "bits" in only:
-            try:
-                extras["bit_allocations"] = bit_allocations(main_res["oracle_inputs"])
-            except Exception as e:
-                extras["bit_allocations"] = {"error": repr(e)}
+    head = longctx_decode(args)
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline_decode(main_res["oracle_inputs"], main_res["bytes"])
-    gbs = main_res["gbs"]
-    dk_gbs = main_res["dk_bytes"] / (main_res["dk_ms"] * 1e-3) / 1e9
-    traffic = measured_traffic()
+        cpu = cpu_baseline_longctx(head["oracle"], head["call_bytes"])
+        log(f"cpu baseline: {cpu}")
+    extras = {"longctx_decode": head["extras"]}
+    only = set(x for x in args.only.split(",") if x)
+    want = (lambda key: not args.no_extras and (not only or key in only))
+    with_cpu = not args.no_cpu
+    single = None
+    if want("single") or want("bits"):
+        try:
+            single = single_layer_decode(cpu=with_cpu)
+            extras["single_layer_decode"] = {k: v for k, v in single.items() if k != "oracle_inputs"}
+        except Exception as e:
+            extras["single_layer_decode"] = {"error": repr(e)}
+    if want("tiny"):
+        run_extra(extras, "tiny_score_matrix", lambda: tiny_score_matrix(cpu=with_cpu))
+    if want("quantize"):
+        run_extra(extras, "quantize_prefill", lambda: quantize_prefill(cpu=with_cpu))
+    if want("search"):
+        run_extra(extras, "vector_search", lambda: vector_search(cpu=with_cpu))
+    if want("paged"):
+        run_extra(extras, "paged_decode", paged_decode)
+    if want("append"):
+        run_extra(extras, "append_step", append_step)
+    if want("niah"):
+        run_extra(extras, "niah_proxy", niah_proxy)
+    if want("bits") and single is not None and "oracle_inputs" in single:
+        run_extra(extras, "bit_allocations", lambda: bit_allocations(single["oracle_inputs"]))
+    traffic = measured_traffic("longctx_decode")
     line = {
         "metric": METRIC,
-        "value": round(gbs, 2),
+        "value": round(head["call_bytes"] / (head["per_call_ms"] * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(main_res["wall_ms"], 6),
+        "ms_per_step": round(head["per_call_ms"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": DECODE_DTYPE,
         "data": "synthetic",
-        "config": {"workload": "single-layer decode attention from compressed KV, Llama-3.1-8B shape",
-                   "batch": 1, "seq_len": 32768, "q_heads": 32, "kv_heads": 8, "head_dim": 128,
-                   "keys": "TurboQuant_prod 4-bit (3 Lloyd-Max + 1 QJL)", "values": "TurboQuant_mse 3-bit",
-                   "kv_copies_rotated": args.copies, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": round(dk_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dk_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic["decode_kernel"] if traffic else None,
-                     "kernel": "decode_kernel (compressed-cache scores, softmax and value sums; HIP events around "
-                               "a graph of its launches alone, chained)",
-                     "bytes_per_launch": main_res["dk_bytes"], "us_per_launch": round(main_res["dk_ms"] * 1e3, 3),
-                     "whole_call": {"kernels": "query transform + decode + combine (one tq_decode_attn)",
-                                    "achieved": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                    "bytes_per_call": main_res["bytes"],
-                                    "us_per_call": round(main_res["per_call_ms"] * 1e3, 3),
-                                    "traffic": traffic["call"] if traffic else None}},
+        "config": {"workload": "long-context batched decode attention from compressed KV: batch 64 x 131072 tokens, "
+                               "32 q / 8 KV heads, head_dim 128, one layer, 2.5 bits per channel",
+                   "batch": LC["B"], "seq_len": LC["T"], "q_heads": LC["Hq"], "kv_heads": LC["Hkv"],
+                   "head_dim": LC["d"],
+                   "keys": "TurboQuant_prod: 32 outlier channels 2+1 bits, 96 channels 1+1 bits",
+                   "values": "TurboQuant_mse: 32 outlier channels 3 bits, 96 channels 2 bits",
+                   "bytes_per_token_head": LC_BYTES_PER_TOKEN_HEAD, "parallelism": "none (1 GPU)"},
+        "roofline": roofline_block(head["kv_bytes"], head["dk_ms"], head["call_bytes"], head["per_call_ms"], traffic,
+                                   "decode_kernel (compressed-cache scores, softmax and value sums; HIP events around "
+                                   "a graph of its launches alone, chained)"),
         "cpu_baseline": cpu,
         "extras": extras,
     }
