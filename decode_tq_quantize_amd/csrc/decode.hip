@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
           int idx = 0;
 #pragma unroll
           for (int p = 0; p < TQ_MAX_MSE_BITS; ++p)
-            if (p < P) idx |= (int)((w[p] >> i) & 1u) << p;
+            if (p < P) idx |= (int)((w[p] >> tqk::value_bit(i)) & 1u) << p;
           const float val = vcent[gi][idx] * nvbuf[wv][gi][tl];
 #pragma unroll
           for (int h = 0; h < kMaxHC; ++h)

@@ -177,8 +177,10 @@ __device__ __forceinline__ v4f mfma_fp8_fp4(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 0, 0, 0);
 }
 // The same with a per-lane E8M0 scale (2^(sa - 127)) on the A operand: the
-// scale of lane l multiplies the A data that lane l holds (row l % 16, its
-// 32 values of K); B is unscaled (127).
+// scale of lane l multiplies row l % 16 over the 32 consecutive K positions
+// 32 (l / 16) .. + 31 (measured on gfx950: not the bytes lane l holds, which
+// are K 16 (l / 16) + 0..15 and 64 + 16 (l / 16) + 0..15); B is unscaled
+// (127).
 __device__ __forceinline__ v4f mfma_fp8_fp4_sa(v8i a, v8i b, v4f c, int sa) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, 127);
 }
@@ -189,7 +191,7 @@ __device__ __forceinline__ float sum4(v4f x) { return (x[0] + x[1]) + (x[2] + x[
 // of the row ends with the result); no LDS traffic.
 template <int N>
 __device__ __forceinline__ float row_ror(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, true));
 }
 __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, row_ror<8>(v));
@@ -210,7 +212,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 // non-negative IEEE halves order like the values they encode.)
 template <int N>
 __device__ __forceinline__ uint32_t row_ror_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 + N, 0xf, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 + N, 0xf, 0xf, true);
 }
 __device__ __forceinline__ uint32_t wave_max64_u(uint32_t v) {
   v = max(v, row_ror_u<8>(v));
@@ -963,7 +965,10 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
         cm[gi] += c4;
     }
   }
-  const float tinv = inv_v(tl & 3);  // fp4 register of this lane's tokens in the value step
+  // fp4 register of this lane's tokens in the value step: token 16 i + tl of
+  // a 32-token word sits at bit 4 (u mod 8) + u / 8, u = 16 (i mod 2) + tl,
+  // i.e. in register u / 8 = 2 (i mod 2) + tl / 8
+  const float tinv_e = inv_v(tl >> 3), tinv_o = inv_v(2 + (tl >> 3));
 
   v4f vacc[2][VT], vcon;
 #pragma unroll
@@ -1102,12 +1107,15 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
     // weights -> fp8 digits in LDS (pre-multiplied by 1 / v_r of their fp4 register)
 #pragma unroll
     for (int gv = 0; gv < NV; ++gv) {
-      const float sv = ldexpf(tinv, 5 - e_new[gv]);
+      const float sv_e = ldexpf(tinv_e, 5 - e_new[gv]), sv_o = ldexpf(tinv_o, 5 - e_new[gv]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        const float sv = (i & 1) ? sv_o : sv_e;
         const int tau = 64 * w + 16 * i + tl;
         const int ks = tau >> 7, tp = tau & 127;
-        const int kappa = 32 * (tp >> 5) + 8 * (tp & 3) + ((tp & 31) >> 2);
+        // operand position of the token: value words hold vector u at bit
+        // 4 (u mod 8) + u / 8, which the fp4 expansion puts at K position u
+        const int kappa = tp;
         float r = p[i] * hbits_at(kc.nv[gv][i >> 1], i & 1) * sv;
         uint8_t* dst = &wbuf[buf][gv][ks][4 * hl][kappa];
 #pragma unroll
@@ -1307,6 +1315,601 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
   }
 }
 
+// ------------------------------------------------------------------ two-wave decode
+// A workgroup of two waves walks 128-token chunks of its split. Per chunk:
+//  * wave w scores 4 of the chunk's 8 key tiles (16 tokens each) on the
+//    fp8 x fp4 matrix cores as above: tiles 2w, 2w + 1, 2w + 4, 2w + 5, the
+//    tokens of the value operand's K blocks w and w + 2 (32 tokens each, the
+//    unit of its per-lane scale); lane (h, c) = (lane / 16, lane % 16) ends
+//    with token c's score for head h;
+//  * each wave turns its softmax weights times the value norm into three
+//    fp8 digits per token (each the rounding of 16 times what the previous
+//    ones left) and a 4 x 4 byte transpose inside each lane quad (two DPP
+//    moves, two byte permutes) into one digit row's 4 consecutive operand
+//    bytes, stored with one 32-bit LDS write: the value words hold token u
+//    of a 32-token word at bit 4 (u mod 8) + u / 8, so the fp4 expansion
+//    puts token t of the chunk at operand position t and a quad's 4 tokens
+//    are 4 consecutive bytes;
+//  * one barrier; each wave reads the whole weight operand (two 16-byte LDS
+//    reads per value group) and accumulates the value sums of its 64 value
+//    coordinates (4 tiles of 16) over the chunk's 128 tokens.
+// Each wave keeps its own weight reference per head: its running maximum of
+// the logits (log2 domain) rounded up to an integer, and per value group the
+// running maximum exponent of the value norms. The value accumulators keep
+// the references both waves reported at the first chunk; a wave's later
+// weights enter the matrix cores with the difference as a power-of-two
+// (E8M0) operand scale per lane, so the accumulators are never rescaled in
+// the loop (only if a reference ran more than kMaxShift above them).
+constexpr int kPChunk = 128;
+constexpr int kPThreads = 128;
+constexpr int kWRow = 144;    // bytes per digit row of the weight operand in LDS (conflict-free, 16-byte aligned)
+constexpr int kWScale = 6;    // weight (<= 1) x value norm x 2^(kWScale - its exponent) x fp4 pre-scale (<= 4) < 256
+constexpr int kMaxShift = 60;  // largest reference difference carried by the operand scale
+
+// 4 x 4 byte transpose inside each lane quad: lane b of a quad returns byte b
+// of each quad lane's x (the byte from quad lane b' at position b').
+__device__ __forceinline__ uint32_t quad_transpose(uint32_t x, uint32_t sel1, uint32_t sel2) {
+  const uint32_t p = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xf, 0xf, false);  // quad lane b ^ 1
+  const uint32_t z = __builtin_amdgcn_perm(p, x, sel1);
+  const uint32_t q = (uint32_t)__builtin_amdgcn_mov_dpp((int)z, 0x4E, 0xf, 0xf, false);  // quad lane b ^ 2
+  return __builtin_amdgcn_perm(q, z, sel2);
+}
+
+// Three fp8 digits of two non-negative values a, b: dwords [a0, a1, a2, 0]
+// and [b0, b1, b2, 0], digit m the e4m3 rounding (to nearest) of 16^m times
+// what the digits before it left.
+__device__ __forceinline__ void digits3(float a, float b, uint32_t& xa, uint32_t& xb) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  int r01 = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);  // digit 0 in the low half
+  f2 f = __builtin_amdgcn_cvt_pk_f32_fp8(r01, false);
+  a = (a - f[0]) * kDigitStep;
+  b = (b - f[1]) * kDigitStep;
+  r01 = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, r01, true);  // digit 1 in the high half
+  f = __builtin_amdgcn_cvt_pk_f32_fp8(r01, true);
+  a = (a - f[0]) * kDigitStep;
+  b = (b - f[1]) * kDigitStep;
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);  // (high half stays 0)
+  // bytes (r01: 0 a0, 1 b0, 2 a1, 3 b1; r2: 4 a2, 5 b2; 0x0c: zero)
+  xa = __builtin_amdgcn_perm(r2, (uint32_t)r01, 0x0c040200u);
+  xb = __builtin_amdgcn_perm(r2, (uint32_t)r01, 0x0c050301u);
+}
+
+// Chunk tile j (0..3) of wave w: 2 w + (j % 2) + 4 (j / 2).
+__device__ __forceinline__ int ptile(int w, int j) { return 2 * w + (j & 1) + 4 * (j >> 1); }
+
+template <int NK>
+struct PKeys {
+  uint32_t kw[4][5];  // key plane words of the lane's coordinate word, token c of each of the wave's tiles
+  uint32_t nr[NK][4];  // key norm (low half) | residual norm (high half)
+};
+template <int NV>
+struct PVals {
+  uint32_t nv[NV][2];  // value norms of the wave's tiles 2 j (low) and 2 j + 1 (high), token c
+  uint32_t vw[4][3];  // value plane words of the wave's 4 coordinate tiles
+};
+
+template <int NK, int P0, int P1, int KP0, int KP1>
+__device__ __forceinline__ void pload_keys(PKeys<NK>& dt, const KAddr& ka, const NAddr& na, int c0, int tlast,
+                                           int w, int lane) {
+  const int last_tile = tlast >> 4;
+  const uint32_t tl2 = 2u * (lane & 15);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t tile = (uint32_t)min((c0 >> 4) + ptile(w, j), last_tile);
+    if constexpr (NK == 1) {
+      buf_words<P0>(ka.res[0], ka.voff[0], tile * ka.step[0], dt.kw[j]);
+    } else {
+      uint32_t w0[5] = {0u, 0u, 0u, 0u, 0u}, w1[5] = {0u, 0u, 0u, 0u, 0u};
+      buf_words<P0>(ka.res[0], ka.voff[0], tile * ka.step[0], w0);
+      buf_words<P1>(ka.res[1], ka.voff[1], tile * ka.step[1], w1);
+#pragma unroll
+      for (int pp = 0; pp < 5; ++pp) dt.kw[j][pp] = w0[pp] | w1[pp];
+    }
+#pragma unroll
+    for (int gi = 0; gi < NK; ++gi) {
+      const uint32_t nn = buf_half(na.n[gi], tl2, 32u * tile);
+      const uint32_t rn = ((gi == 0 && KP0) || (gi == 1 && KP1)) ? buf_half(na.r[gi], tl2, 32u * tile) : 0u;
+      dt.nr[gi][j] = __builtin_amdgcn_perm(rn, nn, 0x05040100u);  // (nn low half, rn high half)
+    }
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void pload_vnorms(PVals<NV>& dt, const NAddr& na, int c0, int tlast, int w, int lane) {
+  const int last_tile = tlast >> 4;
+  const uint32_t tl2 = 2u * (lane & 15);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t tile = (uint32_t)min((c0 >> 4) + ptile(w, j), last_tile);
+#pragma unroll
+    for (int gv = 0; gv < NV; ++gv) {
+      const uint32_t h = buf_half(na.nv[gv], tl2, 32u * tile);
+      dt.nv[gv][j >> 1] = (j & 1) ? __builtin_amdgcn_perm(h, dt.nv[gv][j >> 1], 0x05040100u) : h;
+    }
+  }
+}
+
+// Value words of the wave's coordinate tiles (global tiles 4 W + j, value
+// group G[j] with B[j] planes): this lane's coordinate (lane % 16) and
+// 32-token block (lane / 16) of the chunk.
+template <int NV, int W, int G0, int G1, int G2, int G3, int B0, int B1, int B2, int B3>
+__device__ __forceinline__ void pload_values(PVals<NV>& dt, const rsrc_t (&vres)[2], const uint32_t (&vtile_bytes)[2],
+                                             const uint32_t (&voff)[4], int c0) {
+  constexpr int Gs[4] = {G0, G1, G2, G3}, Bs[4] = {B0, B1, B2, B3};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t soff = (uint32_t)(c0 >> 5) * vtile_bytes[Gs[j]];
+    if (Bs[j] == 3) {  // (constant once the loop is unrolled)
+      buf_words<3>(vres[Gs[j]], voff[j], soff, dt.vw[j]);
+    } else if (Bs[j] == 2) {
+      buf_words<2>(vres[Gs[j]], voff[j], soff, dt.vw[j]);
+      dt.vw[j][2] = 0u;
+    } else {
+      buf_words<1>(vres[Gs[j]], voff[j], soff, dt.vw[j]);
+      dt.vw[j][1] = dt.vw[j][2] = 0u;
+    }
+  }
+}
+
+// CT1: first 16-coordinate tile of value group 1 (8 with one value group);
+// two key groups split at a channel that is a multiple of 32.
+template <int KB0, int KP0, int KB1, int KP1, int VB0, int VB1, int CT1>
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void pair_decode_kernel(Args a) {
+  constexpr int NK = KB1 > 0 ? 2 : 1;
+  constexpr int NV = VB1 > 0 ? 2 : 1;
+  constexpr int NS0 = n_odd(KB0) + KP0;
+  constexpr int NS = NS0 + (KB1 > 0 ? n_odd(KB1) + KP1 : 0);
+  constexpr int P0 = KB0 + KP0, P1 = KB1 + KP1;
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf[2][NV][16 * kWRow];
+  __shared__ float xm[2][2][kHT];  // [parity][wave][head] weight references (log2, integer-valued)
+  __shared__ int xe[2][2][2];      // [parity][wave][value group] value-norm exponents
+  __shared__ float xl[2][kHT];     // [wave][head] final sums
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 4, tl = lane & 15;
+  const int split = blockIdx.x, ht = blockIdx.y, bg = blockIdx.z;
+  asm volatile("" ::"s"(a.Hkv), "s"(a.HT), "s"(a.split_len), "s"(a.T_max), "s"(a.aops), "s"(a.ascale),
+               "s"(a.k[0].packed), "s"(a.k[0].norm), "s"(a.k[0].rnorm), "s"(a.k[0].seq_stride), "s"(a.k[0].d),
+               "s"(a.k[0].ch), "s"(a.v[0].packed), "s"(a.v[0].norm), "s"(a.v[0].seq_stride), "s"(a.v[0].d),
+               "s"(a.v[0].B), "s"(a.v[0].ch), "s"(a.seq_lens), "s"(a.B), "s"(a.G), "s"(a.block_table));
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int h0 = g * a.G + ht * kHT;
+  const int nh = min(kHT, a.G - ht * kHT);
+  const int ts = split * a.split_len;
+  int64_t pbg = bg;
+  int tok_base = 0, rel_first_last = a.T_max - 1;
+  uint32_t live_blk = 1u;
+  if (a.block_table) {
+    const int bi = ts / a.block_tokens;
+    const int blk = a.block_table[(int64_t)b * a.max_blocks + bi];
+    const bool ok = blk >= 0 && blk < a.num_blocks;
+    pbg = (int64_t)(ok ? blk : 0) * a.Hkv + g;
+    tok_base = bi * a.block_tokens;
+    rel_first_last = a.block_tokens - 1;
+    live_blk = ok ? 1u : 0u;
+  }
+  // key words: lane group W = lane / 16 reads coordinate word W
+  const int W = lane >> 4;
+  const bool kg1 = NK == 2 && 32 * W >= a.k[NK - 1].ch;
+  KAddr ka;
+#pragma unroll
+  for (int gi = 0; gi < NK; ++gi) {
+    const int P = gi ? P1 : P0;
+    const int kd = a.k[gi].d, kch = a.k[gi].ch;
+    const int64_t kss = a.k[gi].seq_stride;
+    ka.step[gi] = (uint32_t)((kd >> 5) * 16 * P * 4);
+    const uint32_t* seq = a.k[gi].packed + ((pbg * kss) >> 4) * ((kd >> 5) * 16 * P);
+    ka.res[gi] = make_rsrc(seq, (uint32_t)(kss >> 4) * ka.step[gi] * live_blk);
+    const bool own = NK == 1 || (gi == 1) == kg1;
+    ka.voff[gi] = own ? (uint32_t)(((W - (kch >> 5)) * 16 + tl) * P * 4) : kOutside;
+  }
+  NAddr na;
+#pragma unroll
+  for (int gi = 0; gi < NK; ++gi) {
+    const uint32_t nb = (uint32_t)(2 * a.k[gi].seq_stride) * live_blk;
+    na.n[gi] = make_rsrc(a.k[gi].norm + pbg * a.k[gi].seq_stride, nb);
+    const bool pr = (gi == 0 && KP0) || (gi == 1 && KP1);
+    na.r[gi] = make_rsrc(pr ? a.k[gi].rnorm + pbg * a.k[gi].seq_stride : a.k[gi].norm, pr ? nb : 0u);
+  }
+  rsrc_t vres[2];
+  uint32_t vtile_bytes[2];
+#pragma unroll
+  for (int gv = 0; gv < 2; ++gv) {
+    const VGroup& vg = a.v[NV > 1 ? gv : 0];
+    na.nv[gv < NV ? gv : 0] = make_rsrc(vg.norm + pbg * vg.seq_stride, (uint32_t)(2 * vg.seq_stride) * live_blk);
+    vtile_bytes[gv] = (uint32_t)(vg.d * vg.B * 4);
+    vres[gv] = make_rsrc(vg.packed + ((pbg * vg.seq_stride) >> 5) * (vg.d * vg.B),
+                         (uint32_t)(vg.seq_stride >> 5) * vtile_bytes[gv] * live_blk);
+  }
+
+  // query operands of every slot and their scales (from the query transform)
+  const int key = bg * a.HT + ht;
+  v8i aop[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const v4i* src = reinterpret_cast<const v4i*>(a.aops + (((int64_t)key * NS + s) * 64 + lane) * 8);
+    const v4i lo = src[0], hi = src[1];
+    aop[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  PKeys<NK> kA;
+  PVals<NV> vd;
+  pload_keys<NK, P0, P1, KP0, KP1>(kA, ka, na, ts - tok_base, rel_first_last, w, lane);
+  pload_vnorms<NV>(vd, na, ts - tok_base, rel_first_last, w, lane);
+  int esc_mse[NK], esc_qjl[NK];
+#pragma unroll
+  for (int gi = 0; gi < NK; ++gi) {
+    const int hr = (lane & 15) >> 2, dg = lane & 3;
+    const float2 sc = *reinterpret_cast<const float2*>(a.ascale + (((int64_t)key * kHT + hr) * kMaxKG + gi) * 2);
+    esc_mse[gi] = max((int)(__float_as_uint(sc.x) >> 23) - 4 * dg, 0);
+    esc_qjl[gi] = max((int)(__float_as_uint(sc.y) >> 23) - 4 * dg, 0);
+  }
+  const uint32_t lraw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(a.seq_lens, a.seq_lens ? (uint32_t)(4 * a.B) : 0u), 4u * (uint32_t)b, 0u, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  const int len = max(min(max(__builtin_amdgcn_readfirstlane((int)lraw), 0), a.T_max), a.seq_lens ? 0 : a.T_max);
+  const int te = min(ts + a.split_len, len);
+  const int tlast = max(te, 1) - 1;
+  const int rel_last = max(tlast - tok_base, 0);
+
+  // constant part of the fp4 encoding per (group, class), as the initial
+  // value of each score accumulator (its four digit rows sum to -constant)
+  v4f cinit_m[NK], cinit_q[NK];
+  float gam[NK];
+  {
+    const v8i cop = const_operand();
+#pragma unroll
+    for (int gi = 0; gi < NK; ++gi) {
+      cinit_m[gi] = cinit_q[gi] = v4f{0.f, 0.f, 0.f, 0.f};
+      gam[gi] = a.k[gi].gamma;
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int gi = s < NS0 ? 0 : 1;
+      const bool q = (gi == 0) ? (KP0 && s == NS0 - 1) : (KP1 && s == NS - 1);
+      const v4f c = mfma_fp8_fp4_sa(aop[s], cop, v4f{0.f, 0.f, 0.f, 0.f}, q ? esc_qjl[gi] : esc_mse[gi]);
+      if (q)
+        cinit_q[gi] -= 0.25f * c;
+      else
+        cinit_m[gi] -= 0.25f * c;
+    }
+  }
+  // byte-permute selectors of the quad transpose; fp4 register of this
+  // lane's token in the value words (token 16 T + tl of the chunk lies in
+  // register ((16 T + tl) / 8) % 4 = 2 (T % 2) + tl / 8)
+  const uint32_t sel1 = (tl & 1) ? 0x03070105u : 0x06020400u;
+  const uint32_t sel2 = (tl & 2) ? 0x03020706u : 0x05040100u;
+  const float tinv[2] = {inv_v(tl >> 3), inv_v(2 + (tl >> 3))};
+  const int dg_row = lane & 3;             // digit of this lane's row of the weight operand (row lane % 16)
+  const int h_row = (lane & 15) >> 2;      // head of that row
+  // The E8M0 scale a lane gives the A operand covers the 32 consecutive K
+  // positions of block lane / 16 (measured on gfx950), here tokens
+  // 32 (lane / 16) .. + 31 of the chunk, i.e. tiles 2 (lane / 16) and
+  // 2 (lane / 16) + 1: written by wave (lane / 16) % 2
+  const int src_w = (lane >> 4) & 1;
+
+  // ---- the wave's loop, instantiated per wave (its value tiles' groups and
+  // widths are compile-time)
+  auto run = [&](auto wt) __attribute__((always_inline)) {
+    constexpr int WW = decltype(wt)::value;
+    constexpr int G0 = (NV > 1 && 4 * WW + 0 >= CT1) ? 1 : 0, G1 = (NV > 1 && 4 * WW + 1 >= CT1) ? 1 : 0;
+    constexpr int G2 = (NV > 1 && 4 * WW + 2 >= CT1) ? 1 : 0, G3 = (NV > 1 && 4 * WW + 3 >= CT1) ? 1 : 0;
+    constexpr int Gs[4] = {G0, G1, G2, G3};
+    constexpr int B0 = G0 ? VB1 : VB0, B1 = G1 ? VB1 : VB0, B2 = G2 ? VB1 : VB0, B3 = G3 ? VB1 : VB0;
+    constexpr int Bs[4] = {B0, B1, B2, B3};
+    constexpr int T0 = n_odd(B0), T1 = n_odd(B1), T2 = n_odd(B2), T3 = n_odd(B3);
+    constexpr int Ts[4] = {T0, T1, T2, T3};
+    constexpr int TM = n_odd(VB0 > VB1 ? VB0 : VB1);
+    uint32_t voff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const VGroup& vg = a.v[Gs[j]];
+      voff[j] = (uint32_t)((lane >> 4) * vtile_bytes[Gs[j]] + (16 * (4 * WW + j) - vg.ch + (lane & 15)) * Bs[j] * 4);
+    }
+    pload_values<NV, WW, G0, G1, G2, G3, B0, B1, B2, B3>(vd, vres, vtile_bytes, voff, ts - tok_base);
+    // value accumulators [tile][Walsh term]: rows (head, digit), columns the
+    // tile's 16 coordinates; constant parts per value group
+    v4f vacc[4][TM], vcon[NV];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int t = 0; t < TM; ++t) vacc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int gv = 0; gv < NV; ++gv) vcon[gv] = v4f{0.f, 0.f, 0.f, 0.f};
+    // this wave's weight references (per lane: head hl), sum of its weights
+    float m_w = -INFINITY, l_w = 0.f;
+    int e_w[NV];
+#pragma unroll
+    for (int gv = 0; gv < NV; ++gv) e_w[gv] = -60;
+    // the accumulators' references (the same in both waves): per head, and
+    // per value group
+    float m_acc[kHT] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    int e_acc[NV];
+#pragma unroll
+    for (int gv = 0; gv < NV; ++gv) e_acc[gv] = -60;
+    int par = 0;
+
+    auto chunk = [&](const int c0, PKeys<NK>& dc) __attribute__((always_inline)) {
+      // (wave-uniform) the chunk holds tokens at or past the split's end, or
+      // the group has fewer than kHT heads: only then is anything masked
+      const bool tail = c0 + kPChunk > te || nh < kHT;
+      const int cn = c0 + kPChunk < te ? c0 + kPChunk : c0;
+      // ---------------- scores of the wave's 4 tiles
+      float lg[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t(&wd)[5] = dc.kw[j];
+        v4f dm[NK], dq[NK];
+#pragma unroll
+        for (int gi = 0; gi < NK; ++gi) {
+          dm[gi] = cinit_m[gi];
+          dq[gi] = cinit_q[gi];
+        }
+#pragma unroll
+        for (int t = 0; t < n_odd(KB0); ++t) {
+          uint32_t word = 0;
+          const int m = odd_mask(KB0, t);
+#pragma unroll
+          for (int p = 0; p < 5; ++p)
+            if ((m >> p) & 1) word ^= wd[p];
+          dm[0] = mfma_fp8_fp4_sa(aop[t], expand_bits(word), dm[0], esc_mse[0]);
+        }
+        if constexpr (KP0) dq[0] = mfma_fp8_fp4_sa(aop[NS0 - 1], expand_bits(wd[KB0]), dq[0], esc_qjl[0]);
+        if constexpr (KB1 > 0) {
+#pragma unroll
+          for (int t = 0; t < n_odd(KB1); ++t) {
+            uint32_t word = 0;
+            const int m = odd_mask(KB1, t);
+#pragma unroll
+            for (int p = 0; p < 5; ++p)
+              if ((m >> p) & 1) word ^= wd[p];
+            dm[NK - 1] = mfma_fp8_fp4_sa(aop[NS0 + t], expand_bits(word), dm[NK - 1], esc_mse[NK - 1]);
+          }
+          if constexpr (KP1)
+            dq[NK - 1] = mfma_fp8_fp4_sa(aop[NS - 1], expand_bits(wd[KB1]), dq[NK - 1], esc_qjl[NK - 1]);
+        }
+        float sc = 0.f;
+#pragma unroll
+        for (int gi = 0; gi < NK; ++gi) {
+          float part = sum4(dm[gi]);
+          if ((gi == 0 && KP0) || (gi == 1 && KP1)) part = fmaf(gam[gi] * hbits_hi(dc.nr[gi][j]), sum4(dq[gi]), part);
+          sc = fmaf(hbits(dc.nr[gi][j]), part, sc);
+        }
+        lg[j] = sc;
+      }
+      if (a.scores_out) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tok = c0 + 16 * ptile(WW, j) + tl;
+          if (tok < te && hl < nh) a.scores_out[((int64_t)b * a.Hq + h0 + hl) * a.T_max + tok] = lg[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lg[j] *= a.scale_log2;
+      if (tail) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tok = c0 + 16 * ptile(WW, j) + tl;
+          if (!(tok < te && hl < nh)) lg[j] = -INFINITY;
+        }
+      }
+      // the key words and norms are used up: the next chunk's go to the same
+      // registers, arriving while this chunk's weights and value sums run
+      pload_keys<NK, P0, P1, KP0, KP1>(dc, ka, na, cn - tok_base, rel_last, WW, lane);
+      // value norms of tokens at or past the split's end are cleared
+      if (tail) {
+        const int rem = te - (c0 + tl);  // token c0 + 16 T + tl is in range iff 16 T < rem
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int Ta = ptile(WW, 2 * jj), Tb = ptile(WW, 2 * jj + 1);
+          const uint32_t mk = (rem > 16 * Ta ? 0xffffu : 0u) | (rem > 16 * Tb ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int gv = 0; gv < NV; ++gv) vd.nv[gv][jj] &= mk;
+        }
+      }
+      // ---------------- this wave's references: running maximum (rounded up
+      // to an integer) and value-norm exponents
+      float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+      mx = row16_max(mx);
+      if (mx > m_w) {
+        const float mn = ceilf(mx);
+        l_w = m_w == -INFINITY ? 0.f : l_w * __builtin_amdgcn_exp2f(m_w - mn);
+        m_w = mn;
+      }
+#pragma unroll
+      for (int gv = 0; gv < NV; ++gv) {
+        // (every 16-lane row holds the same 16 tokens of each tile: a row
+        // maximum is the wave's)
+        uint32_t vm = max(max(vd.nv[gv][0] & 0xffffu, vd.nv[gv][0] >> 16), max(vd.nv[gv][1] & 0xffffu, vd.nv[gv][1] >> 16));
+        vm = max(vm, row_ror_u<8>(vm));
+        vm = max(vm, row_ror_u<4>(vm));
+        vm = max(vm, row_ror_u<2>(vm));
+        vm = max(vm, row_ror_u<1>(vm));
+        e_w[gv] = max(e_w[gv], exponent_of(hbits(vm)));
+      }
+      const bool live = m_w != -INFINITY;
+      // value-norm scale times the fp4 pre-scale, per group and tile parity
+      float st[NV][2];
+#pragma unroll
+      for (int gv = 0; gv < NV; ++gv) {
+        const float s = ldexpf(1.f, kWScale - e_w[gv]);
+        st[gv][0] = s * tinv[0];
+        st[gv][1] = s * tinv[1];
+      }
+      // ---------------- weights -> fp8 digits -> the operand rows in LDS
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        float p[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          p[u] = live ? __builtin_amdgcn_exp2f(lg[2 * jj + u] - m_w) : 0.f;
+          l_w += p[u];
+        }
+        uint32_t x[NV][2];
+        if constexpr (NV == 1) {
+          digits3((p[0] * st[0][0]) * hbits(vd.nv[0][jj]), (p[1] * st[0][1]) * hbits_hi(vd.nv[0][jj]), x[0][0],
+                  x[0][1]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            digits3((p[u] * st[0][u]) * hbits_at(vd.nv[0][jj], u), (p[u] * st[1][u]) * hbits_at(vd.nv[1][jj], u),
+                    x[0][u], x[1][u]);
+        }
+#pragma unroll
+        for (int gv = 0; gv < NV; ++gv)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const uint32_t y = quad_transpose(x[gv][u], sel1, sel2);
+            // row (head, digit tl % 4), operand bytes 16 T + 4 (tl / 4) .. + 3
+            *reinterpret_cast<uint32_t*>(
+                &wbuf[par][gv][(4 * hl + (tl & 3)) * kWRow + 16 * ptile(WW, 2 * jj + u) + 4 * (tl >> 2)]) = y;
+          }
+      }
+      if (tl == 0) xm[par][WW][hl] = m_w;
+      if (lane == 0) {
+#pragma unroll
+        for (int gv = 0; gv < NV; ++gv) xe[par][WW][gv] = e_w[gv];
+      }
+      pload_vnorms<NV>(vd, na, cn - tok_base, rel_last, WW, lane);  // the value norms are used up
+      __syncthreads();
+      // ---------------- the weight operand and its per-lane scales
+      v8i aw[NV];
+#pragma unroll
+      for (int gv = 0; gv < NV; ++gv) {
+        const uint8_t* row = &wbuf[par][gv][(lane & 15) * kWRow];
+        const v4i lo = *reinterpret_cast<const v4i*>(row + 16 * (lane >> 4));
+        const v4i hi = *reinterpret_cast<const v4i*>(row + 64 + 16 * (lane >> 4));
+        aw[gv] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      float ms[2][kHT];
+      int es[2][NV];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int h = 0; h < kHT; ++h) ms[s][h] = xm[par][s][h];
+#pragma unroll
+        for (int gv = 0; gv < NV; ++gv) es[s][gv] = xe[par][s][gv];
+      }
+      // the accumulators' references: set at a head's first reported maximum
+      // (its accumulator rows are still zero then); raised, with a rescale,
+      // only when a wave's reference runs more than kMaxShift above them
+      bool raise = false;
+#pragma unroll
+      for (int h = 0; h < kHT; ++h) {
+        const float mh = fmaxf(ms[0][h], ms[1][h]);
+        if (m_acc[h] == -INFINITY) m_acc[h] = mh;
+        raise |= mh - m_acc[h] > (float)kMaxShift;
+      }
+#pragma unroll
+      for (int gv = 0; gv < NV; ++gv) {
+        const int eh = max(es[0][gv], es[1][gv]);
+        if (e_acc[gv] == -60) e_acc[gv] = eh;
+        raise |= eh - e_acc[gv] > kMaxShift;
+      }
+      if (raise) {  // (wave-uniform) move the references up to the reported ones
+        float f[kHT];
+#pragma unroll
+        for (int h = 0; h < kHT; ++h) {
+          const float mh = fmaxf(ms[0][h], ms[1][h]);
+          f[h] = m_acc[h] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_acc[h] - fmaxf(mh, m_acc[h]));
+          m_acc[h] = fmaxf(mh, m_acc[h]);
+        }
+        const float fl = hl == 0 ? f[0] : (hl == 1 ? f[1] : (hl == 2 ? f[2] : f[3]));
+        float fe[NV];
+#pragma unroll
+        for (int gv = 0; gv < NV; ++gv) {
+          const int eh = max(max(es[0][gv], es[1][gv]), e_acc[gv]);
+          fe[gv] = ldexpf(1.f, e_acc[gv] - eh);
+          e_acc[gv] = eh;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int t = 0; t < TM; ++t)
+            if (t < Ts[j]) vacc[j][t] *= fl * fe[Gs[j]];
+#pragma unroll
+        for (int gv = 0; gv < NV; ++gv) vcon[gv] *= fl * fe[gv];
+      }
+      // this lane's operand scale: digit 16^-dg times 2^(reference shift) of
+      // the wave that wrote its columns
+      int sa[NV];
+      {
+        const float m0 = h_row == 0 ? ms[0][0] : (h_row == 1 ? ms[0][1] : (h_row == 2 ? ms[0][2] : ms[0][3]));
+        const float m1 = h_row == 0 ? ms[1][0] : (h_row == 1 ? ms[1][1] : (h_row == 2 ? ms[1][2] : ms[1][3]));
+        const float msrc = src_w ? m1 : m0;
+        const float macc = h_row == 0 ? m_acc[0] : (h_row == 1 ? m_acc[1] : (h_row == 2 ? m_acc[2] : m_acc[3]));
+        // (a source without any weight yet, or a masked head, has all-zero
+        // digits: any scale will do; one far below the reference has
+        // negligible weights, and its scale is clamped into E8M0's range)
+        const int dm = (msrc == -INFINITY || macc == -INFINITY) ? 0 : (int)(msrc - macc);
+#pragma unroll
+        for (int gv = 0; gv < NV; ++gv)
+          sa[gv] = min(max(127 - 4 * dg_row + dm + (src_w ? es[1][gv] : es[0][gv]) - e_acc[gv], 1), 254);
+      }
+      // ---------------- value sums of the wave's 4 coordinate tiles
+      const v8i cop = const_operand();
+#pragma unroll
+      for (int gv = 0; gv < NV; ++gv) vcon[gv] = mfma_fp8_fp4_sa(aw[gv], cop, vcon[gv], sa[gv]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int t = 0; t < Ts[j]; ++t) {
+          uint32_t word = 0;
+          const int m = odd_mask(Bs[j], t);
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            if ((m >> p) & 1) word ^= vd.vw[j][p];
+          vacc[j][t] = mfma_fp8_fp4_sa(aw[Gs[j]], expand_bits(word), vacc[j][t], sa[Gs[j]]);
+        }
+      }
+      pload_values<NV, WW, G0, G1, G2, G3, B0, B1, B2, B3>(vd, vres, vtile_bytes, voff, cn - tok_base);
+      par ^= 1;
+    };
+    int c0 = ts;
+    do {  // (an empty split still runs one chunk, all of it masked)
+      chunk(c0, kA);
+      c0 += kPChunk;
+    } while (c0 < te);
+
+    // ---------------- this split's partial results: the sum of weights of
+    // both waves relative to the accumulators' reference
+    const float lsum = row16_sum(l_w);
+    if (tl == 0) {
+      xl[WW][hl] = lsum;
+      xm[par][WW][hl] = m_w;
+    }
+    __syncthreads();
+    if (hl < nh) {
+      const float macc = hl == 0 ? m_acc[0] : (hl == 1 ? m_acc[1] : (hl == 2 ? m_acc[2] : m_acc[3]));
+      float* part = a.partial + (((int64_t)b * a.Hq + h0 + hl) * a.splits + split) * (kD + 2);
+      const bool none = macc == -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const VGroup& vg = a.v[Gs[j]];
+        const float csub = 0.25f * sum4(vcon[Gs[j]]) * vg.alpha_sum;
+        float v = -csub;
+#pragma unroll
+        for (int t = 0; t < Ts[j]; ++t) v = fmaf(vg.alpha[t], sum4(vacc[j][t]), v);
+        part[2 + 16 * (4 * WW + j) + tl] = none ? 0.f : v * ldexpf(1.f, e_acc[Gs[j]] - kWScale);
+      }
+      if (WW == 0 && tl == 0) {
+        float l = 0.f;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const float msw = xm[par][s][hl];
+          if (msw != -INFINITY && !none) l += xl[s][hl] * __builtin_amdgcn_exp2f(msw - macc);
+        }
+        part[0] = macc;
+        part[1] = l;
+      }
+    }
+  };
+  if (w == 0)
+    run(IntC<0>{});
+  else
+    run(IntC<1>{});
+}
+
 // Walsh coefficients of a mirror-symmetric codebook: c[idx] =
 // sum_{|S| odd} alpha_S prod_{p in S} (2 bit_p(idx) - 1), subsets S in
 // ascending bitmask order.
@@ -1350,6 +1953,37 @@ const Spec kSpecs[] = {
 };
 #undef TQ_SPEC
 
+// Layouts of the two-wave kernel: value codes of up to 3 bits (each wave's
+// value accumulators, 64 coordinates, then stay within the registers of two
+// waves per SIMD; 4-bit MSE-only keys with 3-bit values would not), one key
+// and one value group, or the 2.5-bit outlier split at channel 32 (CT1 = 2).
+#define TQ_WSPEC(a, b, c, d, e, f, ct) Spec{a, b, c, d, e, f, pair_decode_kernel<a, b, c, d, e, f, ct>}
+const Spec kWSpecs[] = {
+    TQ_WSPEC(1, 1, 0, 0, 1, 0, 8), TQ_WSPEC(1, 1, 0, 0, 2, 0, 8), TQ_WSPEC(2, 1, 0, 0, 2, 0, 8),
+    TQ_WSPEC(3, 1, 0, 0, 2, 0, 8), TQ_WSPEC(1, 1, 0, 0, 3, 0, 8), TQ_WSPEC(2, 1, 0, 0, 3, 0, 8),
+    TQ_WSPEC(3, 1, 0, 0, 3, 0, 8), TQ_WSPEC(3, 0, 0, 0, 3, 0, 8),
+    TQ_WSPEC(2, 0, 0, 0, 2, 0, 8), TQ_WSPEC(3, 0, 0, 0, 2, 0, 8), TQ_WSPEC(4, 0, 0, 0, 2, 0, 8),
+    TQ_WSPEC(2, 1, 1, 1, 3, 2, 2),
+};
+#undef TQ_WSPEC
+
+const Spec* find_wspec(const tq_kv_desc& k, const tq_kv_desc& v) {
+  int Dv = 0, D = 0;
+  for (int i = 0; i < v.n_groups; ++i) Dv += v.g[i].q.d;
+  for (int i = 0; i < k.n_groups; ++i) D += k.g[i].q.d;
+  if (D != kD || Dv != kD || k.n_groups > kMaxKG || v.n_groups > kMaxVG) return nullptr;
+  if (k.n_groups > 1 && k.g[1].ch_offset != 32) return nullptr;
+  if (v.n_groups > 1 && v.g[1].ch_offset != 32) return nullptr;
+  const int kb0 = k.g[0].q.mse_bits, kp0 = k.g[0].q.variant == TQ_PROD;
+  const int kb1 = k.n_groups > 1 ? k.g[1].q.mse_bits : 0;
+  const int kp1 = k.n_groups > 1 ? (k.g[1].q.variant == TQ_PROD) : 0;
+  const int vb0 = v.g[0].q.mse_bits, vb1 = v.n_groups > 1 ? v.g[1].q.mse_bits : 0;
+  for (const Spec& sp : kWSpecs)
+    if (sp.kb0 == kb0 && sp.kp0 == kp0 && sp.kb1 == kb1 && sp.kp1 == kp1 && sp.vb0 == vb0 && sp.vb1 == vb1)
+      return &sp;
+  return nullptr;
+}
+
 const Spec* find_spec(const tq_kv_desc& k, const tq_kv_desc& v) {
   int Dv = 0, D = 0;
   for (int i = 0; i < v.n_groups; ++i) Dv += v.g[i].q.d;
@@ -1372,20 +2006,25 @@ const Spec* find_spec(const tq_kv_desc& k, const tq_kv_desc& v) {
 
 namespace tqk {
 
-bool mfma_decode_supported(const tq_kv_desc& k, const tq_kv_desc& v) { return find_spec(k, v) != nullptr; }
+bool mfma_decode_supported(const tq_kv_desc& k, const tq_kv_desc& v) {
+  return find_wspec(k, v) != nullptr || find_spec(k, v) != nullptr;
+}
 
 int mfma_decode_max_splits() { return kMaxCombineSplits; }
 
 DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int Hq, int Hkv, int T_max,
                             int block_tokens) {
-  (void)v;
   DecodePlan p{};
   const int G = Hq / Hkv;
   const int HT = (G + kHT - 1) / kHT;
   const int64_t wgs_per_split = (int64_t)B * Hkv * HT;
-  // enough splits that every compute unit holds two workgroups (the kernel's
-  // launch bounds) at once
-  const int64_t target = 2 * (int64_t)device_cus();
+  // the two-wave kernel: two waves per SIMD, i.e. four two-wave workgroups
+  // per compute unit, chunks of 128 tokens; otherwise two four-wave
+  // workgroups per compute unit and chunks of 256 tokens (the kernels'
+  // launch bounds)
+  const bool wave = find_wspec(k, v) != nullptr;
+  const int chunk = wave ? kPChunk : kChunk;
+  const int64_t target = (wave ? 4 : 2) * (int64_t)device_cus();
   int64_t splits = (target + wgs_per_split - 1) / wgs_per_split;
   int64_t sl = (T_max + splits - 1) / splits;
   // test hook: TQ_DECODE_SPLIT_TOKENS (a positive multiple of 256) fixes the
@@ -1393,15 +2032,15 @@ DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int
   // counts; read at every plan, so a size query and the decode it sizes
   // agree as long as the variable does not change between them
   if (const char* ev = getenv("TQ_DECODE_SPLIT_TOKENS")) {
-    const long v = strtol(ev, nullptr, 10);
-    if (v > 0 && v % kChunk == 0) sl = v;
+    const long ov = strtol(ev, nullptr, 10);
+    if (ov > 0 && ov % kChunk == 0) sl = ov;
   }
   const int64_t min_sl = (T_max + kMaxCombineSplits - 1) / kMaxCombineSplits;  // the combine's split table
   if (sl < min_sl) sl = min_sl;
-  sl = (sl + kChunk - 1) / kChunk * kChunk;
+  sl = (sl + chunk - 1) / chunk * chunk;
   if (block_tokens > 0) {  // a split must not leave its block: a divisor of it
     sl = std::min<int64_t>(sl, block_tokens);
-    while (block_tokens % sl) sl -= kChunk;
+    while (block_tokens % sl) sl -= chunk;
   }
   p.split_len = (int)sl;
   p.splits = (int)((T_max + sl - 1) / sl);
@@ -1425,7 +2064,8 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
                               int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out,
                               float* scores_out, void* ws, const DecodePlan& plan, hipStream_t s,
                               const PageTable* pages) {
-  const Spec* sp = find_spec(k, v);
+  const Spec* wsp = find_wspec(k, v);
+  const Spec* sp = wsp ? wsp : find_spec(k, v);
   if (!sp) return hipErrorInvalidValue;
   Args a{};
   if (pages) {
@@ -1513,7 +2153,7 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
     hipLaunchKernelGGL(qtransform_kernel<true>, qgrid, dim3(kQtThreads), 0, s, a);
   }
   const dim3 grid(plan.splits, a.HT, B * Hkv);
-  hipLaunchKernelGGL(sp->fn, grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(sp->fn, grid, dim3(wsp ? kPThreads : kThreads), 0, s, a);
   hipLaunchKernelGGL(combine_kernel, dim3(B * Hq, kJSlices), dim3(kCombThreads), 0, s, a);
   return hipGetLastError();
 }

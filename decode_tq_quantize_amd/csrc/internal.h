@@ -12,6 +12,12 @@ namespace tqk {
 constexpr int kKeysTile = 16;
 constexpr int kValuesTile = 32;
 
+// Bit of the value-layout word that holds vector u (0..31) of its tile:
+// 4 (u mod 8) + u / 8, so that each fp4 register the decode's matrix cores
+// expand from a word (bits 4 i + r, i = 0..7, for register r) holds 8
+// consecutive vectors.
+__host__ __device__ constexpr int value_bit(int u) { return 4 * (u & 7) + (u >> 3); }
+
 inline int planes_of(const tq_quantizer& q) { return q.mse_bits + (q.variant == TQ_PROD ? 1 : 0); }
 
 // Compute units of the current device, queried once per device and kept

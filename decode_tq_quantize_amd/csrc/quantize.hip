@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QArgsPair pair) {
         const int64_t row = a.rows[gv];
         if (row < 0 || row >= a.cache_rows) continue;
         const int sh = p < a.B ? p : 4;
-        const uint32_t bit = 1u << (uint32_t)(row % tqk::kValuesTile);
+        const uint32_t bit = 1u << (uint32_t)tqk::value_bit((int)(row % tqk::kValuesTile));
         uint32_t* wp = a.packed + ((row / tqk::kValuesTile) * d + j) * P + p;
         if ((C[j * TV + v] >> sh) & 1)
           atomicOr(wp, bit);
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QArgsPair pair) {
       const int sh = p < a.B ? p : 4;
       uint32_t w = 0;
       for (int v = 0; v < TV; ++v)
-        if (v0 + v < a.n) w |= (uint32_t)((C[j * TV + v] >> sh) & 1) << v;
+        if (v0 + v < a.n) w |= (uint32_t)((C[j * TV + v] >> sh) & 1) << tqk::value_bit(v);
       a.packed[(tile * d + j) * P + p] = w;
     }
   }

@@ -258,10 +258,17 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
   }
   __syncthreads();
 
+  // The vector of a tile that MFMA column nl of half nt carries: for keys
+  // vector 16 nt + nl; for values the vector whose bit in the value words is
+  // 16 nt + nl (bit 4 (u mod 8) + u / 8 holds vector u), so that the halves'
+  // ballots are the words' halves as they stand
+  auto col_vec = [&](int nt, int c) __attribute__((always_inline)) -> int {
+    return KEYS ? 16 * nt + c : 8 * (c & 3) + 4 * nt + (c >> 2);
+  };
   // a tile's inputs (rows past n re-read row n - 1 and are masked)
   auto load_tile = [&](XIn<BF16IN>(&dst)[2], int64_t t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) load_in(dst[nt], a, min(t * kTile + 16 * nt + nl, a.n - 1), q);
+    for (int nt = 0; nt < 2; ++nt) load_in(dst[nt], a, min(t * kTile + col_vec(nt, nl), a.n - 1), q);
   };
   const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
   // one tile, whose inputs are in cur; once the rotation has read them, cur
@@ -337,10 +344,10 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
     float inv[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      valid[nt] = v0 + 16 * nt + nl < a.n;
+      valid[nt] = v0 + col_vec(nt, nl) < a.n;
       live[nt] = valid[nt] & (nrm[nt] > 0.f);
       inv[nt] = live[nt] ? __builtin_amdgcn_rcpf(nrm[nt]) : 0.f;
-      if (w == 0 && q == 0 && valid[nt]) a.norm[v0 + 16 * nt + nl] = tqd::f32_to_half_bits(nrm[nt]);
+      if (w == 0 && q == 0 && valid[nt]) a.norm[v0 + col_vec(nt, nl)] = tqd::f32_to_half_bits(nrm[nt]);
     }
     float res[2][2][4];
     float r2[2] = {0.f, 0.f};
@@ -366,8 +373,9 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
     auto key_word = [&](uint32_t acc8) __attribute__((always_inline)) -> uint32_t {
       return or_q(((acc8 & 0xfu) | ((acc8 & 0xf0u) << 12)) << (4 * q));
     };
-    // words (coordinate j, plane p) of the value layout: bit i = vector
-    // v0 + i; the wave's coordinates are 32 P contiguous words, word
+    // words (coordinate j, plane p) of the value layout: bit i = the vector
+    // of column i % 16 of half i / 16; the wave's coordinates are 32 P
+    // contiguous words, word
     // (j - 32 w) P + p, held by lane (word % 64) of ow[word / 64]. Bits
     // 16 q .. 16 q + 15 of the two halves' ballots are the low and high
     // halves of the word of coordinate 32 w + 16 m + 4 q + r.
@@ -515,11 +523,11 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
       __syncthreads();
       // residual norms (one lane per vector)
       if (w == 0 && q < 2) {
-        const int vt = 16 * q + nl;
-        if (v0 + vt < a.n) {
+        const int vt = 16 * q + nl;  // column nl of half q
+        if (v0 + col_vec(q, nl) < a.n) {
           const float rho =
               __builtin_amdgcn_sqrtf((rho_part[0][vt] + rho_part[1][vt]) + (rho_part[2][vt] + rho_part[3][vt]));
-          a.rnorm[v0 + vt] = tqd::f32_to_half_bits(rho);
+          a.rnorm[v0 + col_vec(q, nl)] = tqd::f32_to_half_bits(rho);
         }
       }
     }

@@ -36,7 +36,8 @@
  *    vector 16 tile + t.
  *  - TQ_LAYOUT_VALUES (token-contiguous; values): tiles of 32 vectors;
  *    word index (tile * d + j) * P + p holds coordinate j of vectors
- *    32 tile .. 32 tile + 31 (bit i = vector 32 tile + i).
+ *    32 tile .. 32 tile + 31, vector 32 tile + u at bit 4 (u mod 8) + u / 8
+ *    (bits 4 i + r, i = 0..7, hold the 8 consecutive vectors 8 r .. 8 r + 7).
  *  Vectors past n in the last tile are all-zero bits. Norms are separate
  *  arrays of IEEE half (uint16 bits), one per vector.
  */

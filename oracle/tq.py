@@ -185,9 +185,18 @@ def estimate_ip(y, c: Codes, q: Quantizer) -> np.ndarray:
 #   p = plane (0..B-1: code bit p, LSB first; B: QJL sign, PROD only);
 #   bit i of the word = coordinate 32 g + i.
 # VALUES (token-contiguous), tiles of 32 vectors, words indexed [tile][j][p],
-#   j = coordinate; bit i of the word = vector 32 tile + i.
+#   j = coordinate; vector 32 tile + u sits at bit 4 (u mod 8) + u // 8 of
+#   the word (a transpose of the 4 x 8 bit matrix; value_bit below).
 # Vectors past N in the last tile are all-zero bits.
 # ----------------------------------------------------------------------------
+
+def value_bit(u):
+    """Bit of a value-layout word that holds vector u (0..31) of its tile."""
+    return 4 * (u % 8) + u // 8
+
+
+_VALUE_ORDER = np.array([[u for u in range(32) if value_bit(u) == b][0] for b in range(32)])  # bit -> vector
+
 
 def _planes(idx, z, mse_bits):
     N, d = idx.shape
@@ -235,8 +244,8 @@ def pack(idx, z, mse_bits, layout):
         w = _bits_to_words(full.reshape(NT * tile, P, G, 32))           # [V, P, G]
         w = w.reshape(NT, tile, P, G).transpose(0, 3, 1, 2)             # [tile, g, t, p]
     elif layout == "values":
-        b = full.reshape(NT, tile, P, d).transpose(0, 3, 2, 1)          # [tile, j, p, i]
-        w = _bits_to_words(b)                                           # [tile, j, p]
+        b = full.reshape(NT, tile, P, d).transpose(0, 3, 2, 1)          # [tile, j, p, u]
+        w = _bits_to_words(b[..., _VALUE_ORDER])                        # [tile, j, p]
     else:
         raise ValueError(layout)
     return np.ascontiguousarray(w).reshape(-1)
@@ -254,7 +263,9 @@ def unpack(words, N, d, mse_bits, prod, layout):
         pl = _words_to_bits(w).reshape(NT * tile, P, d)
     else:
         w = w.reshape(NT, d, P)                                         # [tile, j, p]
-        pl = _words_to_bits(w).transpose(0, 3, 2, 1).reshape(NT * tile, P, d)
+        bits = _words_to_bits(w)                                        # [tile, j, p, bit]
+        bits = bits[..., [value_bit(u) for u in range(32)]]             # [tile, j, p, u]
+        pl = bits.transpose(0, 3, 2, 1).reshape(NT * tile, P, d)
     pl = pl[:N]
     idx = np.zeros((N, d), dtype=np.uint8)
     for p in range(mse_bits):
