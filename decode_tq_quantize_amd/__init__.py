@@ -25,6 +25,8 @@ TQ_ERR_MISALIGNED = -3
 TQ_ERR_NO_CONVERGE = -4
 TQ_ERR_HIP = -5
 TQ_ERR_WORKSPACE = -6
+TQ_ERR_SCRATCH = -7
+TQ_DECODE_SCRATCH_BYTES = 16 << 20
 
 TQ_MSE, TQ_PROD = 0, 1
 TQ_F32, TQ_BF16 = 0, 1
@@ -36,7 +38,7 @@ TQ_MAX_GROUPS = 4
 EXPORTS = [
     "tq_build_codebook", "tq_quantizer_init", "tq_packed_bytes", "tq_status_string",
     "tq_quantize_kv", "tq_append_kv", "tq_append_kv_pair", "tq_decode_workspace_bytes", "tq_decode_attn", "tq_kv_bit_allocation",
-    "tq_decode_paged_workspace_bytes", "tq_decode_attn_paged",
+    "tq_decode_paged_workspace_bytes", "tq_decode_attn_paged", "tq_decode_attn_noalloc",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_fold_bytes", "tq_fold_qjl",
 ]
 
@@ -109,6 +111,9 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attn.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_void_p, c_int, c_int, c_int, c_int,
                                      c_int, c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.tq_decode_attn.restype = c_int
+        L.tq_decode_attn_noalloc.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_void_p, c_int, c_int, c_int,
+                                             c_int, c_int, c_void_p, c_float, c_void_p, c_void_p, c_void_p]
+        L.tq_decode_attn_noalloc.restype = c_int
         L.tq_search_workspace_bytes.argtypes = [POINTER(tq_group), c_int64, c_int, c_int]
         L.tq_search_workspace_bytes.restype = c_size_t
         L.tq_search_topk.argtypes = [POINTER(tq_group), c_int64, c_void_p, c_int, c_int, c_void_p, c_void_p,
@@ -244,6 +249,13 @@ def tq_decode_attn(k: tq_kv_desc, v: tq_kv_desc, q, q_dtype: int, B: int, Hq: in
     _check(lib().tq_decode_attn(ctypes.byref(k), ctypes.byref(v), _ptr(q), q_dtype, B, Hq, Hkv, T_max,
                                 _ptr(seq_lens), scale, _ptr(out), _ptr(scores_out), _ptr(ws), ws_bytes,
                                 _stream(stream)), "tq_decode_attn")
+
+
+def tq_decode_attn_noalloc(k: tq_kv_desc, v: tq_kv_desc, q, q_dtype: int, B: int, Hq: int, Hkv: int, T_max: int,
+                           seq_lens, scale: float, out, scores_out, stream=None) -> None:
+    _check(lib().tq_decode_attn_noalloc(ctypes.byref(k), ctypes.byref(v), _ptr(q), q_dtype, B, Hq, Hkv, T_max,
+                                        _ptr(seq_lens), scale, _ptr(out), _ptr(scores_out), _stream(stream)),
+           "tq_decode_attn_noalloc")
 
 
 def tq_decode_paged_workspace_bytes(k: tq_kv_desc, v: tq_kv_desc, B: int, Hq: int, Hkv: int, T_max: int,

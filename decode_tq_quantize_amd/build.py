@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libtq.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["codebook.cpp", "tq_api.cpp", "quantize.hip", "decode.hip", "decode_mfma.hip", "search.hip", "fold.hip", "quantize_mfma.hip", "search_mfma.hip"]
+SOURCES = ["codebook.cpp", "tq_api.cpp", "quantize.hip", "decode.hip", "decode_mfma.hip", "search.hip", "fold.hip", "quantize_mfma.hip", "search_mfma.hip", "decode_noalloc.hip"]
 
 # Per-source additions. The matrix-core decode forms no NaN from valid inputs:
 # masked logits are -inf by selection, every difference of two maxima is

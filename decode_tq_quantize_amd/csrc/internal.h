@@ -43,6 +43,12 @@ bool quantize_mfma_supported(const tq_quantizer& q, tq_dtype dt, const void* x, 
 hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
                                 int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s);
 
+// Every check of a tq_decode_attn call except those of its workspace, in the
+// same order; on TQ_OK *ws_need holds the workspace bytes the call needs.
+int check_decode_call(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype, int B, int Hq,
+                      int Hkv, int T_max, const int32_t* seq_lens, float scale, const float* out,
+                      const float* scores_out, size_t* ws_need);
+
 // Decode: workspace sizing and launch. Shapes are validated by the caller.
 struct DecodePlan {
   int head_chunk;   // query heads per workgroup

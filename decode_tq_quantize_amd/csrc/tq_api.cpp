@@ -157,6 +157,7 @@ extern "C" const char* tq_status_string(int status) {
     case TQ_ERR_NO_CONVERGE: return "Lloyd-Max iteration did not converge";
     case TQ_ERR_HIP: return "HIP launch failed";
     case TQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case TQ_ERR_SCRATCH: return "needs more workspace than the fixed decode scratch (TQ_DECODE_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -271,9 +272,11 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_kv_desc* k, const tq_kv_des
   return (p.qprep_floats + p.partial_floats) * sizeof(float);
 }
 
-extern "C" int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype, int B,
-                              int Hq, int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out,
-                              float* scores_out, void* ws, size_t ws_bytes, void* stream) {
+namespace tqk {
+
+int check_decode_call(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype, int B, int Hq,
+                      int Hkv, int T_max, const int32_t* seq_lens, float scale, const float* out,
+                      const float* scores_out, size_t* ws_need) {
   int D = 0, Dv = 0;
   int rc = check_decode(k, v, B, Hq, Hkv, T_max, &D, &Dv);
   if (rc != TQ_OK) return rc;
@@ -281,10 +284,24 @@ extern "C" int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const vo
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(out) || (scores_out && !aligned16(scores_out)) ||
-      (seq_lens && !aligned16(seq_lens)) || (ws && !aligned16(ws)))
+      (seq_lens && !aligned16(seq_lens)))
     return TQ_ERR_MISALIGNED;
   const tqk::DecodePlan p = decode_plan(*k, *v, B, Hq, Hkv, T_max);
-  if (!ws || ws_bytes < (p.qprep_floats + p.partial_floats) * sizeof(float)) return TQ_ERR_WORKSPACE;
+  *ws_need = (p.qprep_floats + p.partial_floats) * sizeof(float);
+  return TQ_OK;
+}
+
+}  // namespace tqk
+
+extern "C" int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype, int B,
+                              int Hq, int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out,
+                              float* scores_out, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  const int rc = tqk::check_decode_call(k, v, q, q_dtype, B, Hq, Hkv, T_max, seq_lens, scale, out, scores_out, &need);
+  if (rc != TQ_OK) return rc;
+  if (ws && !aligned16(ws)) return TQ_ERR_MISALIGNED;
+  if (!ws || ws_bytes < need) return TQ_ERR_WORKSPACE;
+  const tqk::DecodePlan p = decode_plan(*k, *v, B, Hq, Hkv, T_max);
   if (tqk::mfma_decode_supported(*k, *v))
     return hip_status(tqk::launch_decode_mfma(*k, *v, q, q_dtype, B, Hq, Hkv, T_max, seq_lens, scale, out,
                                               scores_out, ws, p, static_cast<hipStream_t>(stream)));

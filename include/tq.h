@@ -15,7 +15,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All device buffers are owned by the caller; libtq never allocates device
- *    memory and keeps no mutable global state, so calls are thread-safe.
+ *    memory. Its one piece of mutable device state is the fixed scratch
+ *    array of tq_decode_attn_noalloc (one per GPU); every other call keeps
+ *    no mutable global state and is thread-safe.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
  *    device entry point only enqueues work on it and returns; nothing
  *    synchronises.
@@ -58,7 +60,8 @@ typedef enum {
   TQ_ERR_MISALIGNED = -3,   /* a device base pointer is not 16-byte aligned */
   TQ_ERR_NO_CONVERGE = -4,  /* Lloyd-Max did not converge within max_iter */
   TQ_ERR_HIP = -5,          /* a HIP launch failed */
-  TQ_ERR_WORKSPACE = -6     /* workspace missing or smaller than the size query says */
+  TQ_ERR_WORKSPACE = -6,    /* workspace missing or smaller than the size query says */
+  TQ_ERR_SCRATCH = -7       /* the call needs more workspace than TQ_DECODE_SCRATCH_BYTES */
 } tq_status;
 
 typedef enum { TQ_MSE = 0, TQ_PROD = 1 } tq_variant;
@@ -238,6 +241,29 @@ size_t tq_decode_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B
 int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype,
                    int B, int Hq, int Hkv, int T_max, const int32_t* seq_lens, float scale,
                    float* out, float* scores_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Size of the scratch array tq_decode_attn_noalloc uses as its workspace. */
+#define TQ_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* tq_decode_attn for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same attention, arguments, results and errors, with no workspace
+ * argument. Its workspace is a fixed array of TQ_DECODE_SCRATCH_BYTES in
+ * every GPU's memory, part of the library's code object, held from the load
+ * until the process ends; the call allocates nothing.
+ *   - A call whose tq_decode_workspace_bytes exceeds TQ_DECODE_SCRATCH_BYTES
+ *     returns TQ_ERR_SCRATCH before any device work (use tq_decode_attn).
+ *   - All calls on one GPU share its array. Calls in one stream are ordered;
+ *     calls that may overlap in time on one GPU (other streams, other host
+ *     threads) race on it and must be serialised by the caller.
+ *   - Nothing in the array needs clearing: every call writes each word of
+ *     it that it reads, so leftovers of the last call do not matter.
+ *   - TQ_ERR_HIP if the array's device address cannot be obtained (it is
+ *     looked up once per device, on the first call with that device
+ *     current). */
+int tq_decode_attn_noalloc(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype,
+                           int B, int Hq, int Hkv, int T_max, const int32_t* seq_lens, float scale,
+                           float* out, float* scores_out, void* stream);
 
 /* Workspace bytes tq_decode_attn_paged needs (0 on bad arguments). */
 size_t tq_decode_paged_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq,

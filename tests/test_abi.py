@@ -243,6 +243,29 @@ def test_decode_validation_paths():
     assert tq.tq_decode_workspace_bytes(k, v, 1, 30, 8, 1024) == 0
 
 
+def test_noalloc_decode_validation_paths():
+    # the allocation-free entry point validates like tq_decode_attn and refuses
+    # requests beyond its fixed scratch array, all before any device call
+    L = tq.lib()
+    k, v = _kv()
+
+    def call(k=k, v=v, q=FAKE, B=1, Hq=32, Hkv=8, T=1024, out=FAKE, scale=0.088):
+        return L.tq_decode_attn_noalloc(ctypes.byref(k), ctypes.byref(v), q, tq.TQ_BF16, B, Hq, Hkv, T, None,
+                                        scale, out, None, None)
+
+    assert call(Hq=30) == tq.TQ_ERR_INVALID_ARG
+    assert call(T=2048) == tq.TQ_ERR_INVALID_ARG
+    assert call(out=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(q=FAKE + 2) == tq.TQ_ERR_MISALIGNED
+    assert call(scale=float("nan")) == tq.TQ_ERR_INVALID_ARG
+    kp, vp = _kv(kd=512, vd=512)
+    assert call(k=kp, v=vp) == tq.TQ_ERR_UNSUPPORTED
+    need = tq.tq_decode_workspace_bytes(k, v, 1024, 64, 8, 1024)
+    assert need > tq.TQ_DECODE_SCRATCH_BYTES
+    assert call(B=1024, Hq=64) == tq.TQ_ERR_SCRATCH
+    assert "TQ_DECODE_SCRATCH_BYTES" in L.tq_status_string(tq.TQ_ERR_SCRATCH).decode()
+
+
 def test_paged_decode_validation_paths():
     L = tq.lib()
     bt = 512
