@@ -60,6 +60,9 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one 256 MiB device-to-device copy (the known-size reference for the "
                         "FETCH_SIZE / WRITE_SIZE counters)")
+    p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="write profiles/traffic_longctx_decode.json from two rocprofv3 --pmc runs of "
+                        "'bench.py --no-extras --no-cpu --calibrate-copy' (FETCH_SIZE, then WRITE_SIZE) and exit")
     return p.parse_args()
 
 
@@ -107,13 +110,22 @@ def blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def graph_ms(call, steps, warmup=3):
-    """Mean time per call of `steps` calls captured into one HIP graph (HIP events around one replay)."""
+def graph_ms(call, steps, warmup=3, warm_s=0.0):
+    """Mean time per call of `steps` calls captured into one HIP graph (HIP events around one replay).
+
+    Before capture: `warmup` calls, then more untimed calls until `warm_s`
+    seconds have passed (the first few tens of long calls on a fresh GPU run
+    up to 20% slower while its clocks settle).
+    """
     import torch
 
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        call(0)
+        torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -240,6 +252,82 @@ def measured_traffic(workload):
     return {"call": rec.get("bytes_per_call"), "decode_kernel": per[0]["fetch_bytes"] + per[0]["write_bytes"]}
 
 
+TRAFFIC_SOURCES = ["decode_tq_quantize_amd/csrc/decode_mfma.hip", "decode_tq_quantize_amd/csrc/internal.h"]
+
+
+def traffic_summary(fetch_dir, write_dir):
+    """HBM bytes per dispatch of the long-context decode kernels from two
+    rocprofv3 counter runs (csv output), written to
+    profiles/traffic_longctx_decode.json.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the
+    same counter reads for the 256 MiB device copy --calibrate-copy runs
+    first. The median over a kernel's dispatches is kept (the one quality call
+    that also writes the score matrix is an outlier).
+    """
+    import collections
+    import csv
+    import glob
+    import hashlib
+    import re
+    import statistics
+
+    def load(folder, counter):
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    per[r["Kernel_Name"]][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+        return {k: list(v.values()) for k, v in per.items()}
+
+    F, W = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copy_kib = (256 << 20) / 1024
+    fcopy = max(max(v) for k, v in F.items() if "copy" in k.lower())
+    wcopy = max(max(v) for k, v in W.items() if "copy" in k.lower())
+    ff, wf = copy_kib / fcopy, copy_kib / wcopy
+
+    def short(k):
+        for s in ("qfused_kernel", "qtransform_kernel", "combine_kernel"):
+            if s in k:
+                return s
+        return "decode_kernel" if "decode_kernel<" in k else None
+
+    per = {}
+    for k in F:
+        s = short(k)
+        if s is None or k not in W:
+            continue
+        fk, wk = statistics.median(F[k]), statistics.median(W[k])
+        m = re.search(r"\w+_kernel(<[^>]*>)?", k)
+        per[s] = {"kernel": m.group(0) if m else k, "fetch_kib": round(fk, 2),
+                  "write_kib": round(wk, 2), "fetch_bytes": int(round(fk * 1024 * ff)),
+                  "write_bytes": int(round(wk * 1024 * wf)), "dispatches": len(F[k])}
+    n = LC["B"] * LC["Hkv"] * LC["T"]
+    kv_bytes = n * LC_BYTES_PER_TOKEN_HEAD
+    rec = {"what": "HBM bytes per dispatch of the long-context decode call (batch 64 x 131072 tokens, 32 q / 8 KV "
+                   "heads, head_dim 128, 2.5 bits per channel): rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by "
+                   "its reading for a 256 MiB device copy; median over dispatches",
+           "commands": ["rocprofv3 --output-format csv --pmc FETCH_SIZE -d <fetch_dir> -o fetch -- python3 bench.py "
+                        "--no-extras --no-cpu --steps 6 --warmup 1 --calibrate-copy",
+                        "rocprofv3 --output-format csv --pmc WRITE_SIZE -d <write_dir> -o write -- python3 bench.py "
+                        "--no-extras --no-cpu --steps 6 --warmup 1 --calibrate-copy",
+                        "python3 bench.py --traffic-summary <fetch_dir> <write_dir>"],
+           "calibration": {"copy_bytes": 256 << 20, "fetch_size_kib": round(fcopy, 4), "write_size_kib": round(wcopy, 4),
+                           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "per_kernel": per,
+           "bytes_per_call": sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values()),
+           "algorithmic_bytes_decode_kernel": kv_bytes,
+           "algorithmic_bytes_per_call": kv_bytes + LC["B"] * LC["Hq"] * LC["d"] * (2 + 4),
+           "source_sha256": {rel: hashlib.sha256(open(os.path.join(ROOT, rel), "rb").read()).hexdigest()
+                             for rel in TRAFFIC_SOURCES}}
+    if "decode_kernel" in per:
+        dk = per["decode_kernel"]
+        rec["decode_kernel_traffic_over_algorithmic"] = round((dk["fetch_bytes"] + dk["write_bytes"]) / kv_bytes, 4)
+    out = os.path.join(ROOT, "profiles", "traffic_longctx_decode.json")
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def roofline_block(kernel_bytes, kernel_ms, call_bytes, call_ms, traffic, kernel_desc):
     ach = kernel_bytes / (kernel_ms * 1e-3) / 1e9
     call = call_bytes / (call_ms * 1e-3) / 1e9
@@ -319,7 +407,7 @@ def longctx_decode(args):
         tq.tq_decode_attn(descs["k"], descs["v"], q_t, tq.TQ_BF16, B, Hq, Hkv, T, None, scale, out, None, ws, wsb)
 
     log(f"longctx: {args.steps} calls in one graph")
-    ms, side, wall_ms = graph_ms(call, args.steps, args.warmup)
+    ms, side, wall_ms = graph_ms(call, args.steps, args.warmup, warm_s=0.5)
     dk_ms = kernel_only_ms(call, args.steps, side)
     kv_bytes = n * LC_BYTES_PER_TOKEN_HEAD
     call_bytes = kv_bytes + B * Hq * d * (2 + 4)
@@ -1058,6 +1146,9 @@ def run_extra(extras, name, fn):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the hot path runs on a single MI355X and no multi-GPU job is launched; "

@@ -1466,7 +1466,11 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   __shared__ float xl[2][kHT];     // [wave][head] final sums
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The two roles differ in value work (with the outlier split, role 0 sums
+  // the 3-bit tiles); alternating them between neighbouring workgroups puts
+  // both roles on each SIMD (about 1% faster than a fixed assignment).
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6) ^ (lin & 1);
   const int hl = lane >> 4, tl = lane & 15;
   const int split = blockIdx.x, ht = blockIdx.y, bg = blockIdx.z;
   asm volatile("" ::"s"(a.Hkv), "s"(a.HT), "s"(a.split_len), "s"(a.T_max), "s"(a.aops), "s"(a.ascale),
