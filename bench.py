@@ -370,6 +370,7 @@ def longctx_decode(args):
     B, Hq, Hkv, T, d = LC["B"], LC["Hq"], LC["Hkv"], LC["T"], LC["d"]
     n = B * Hkv * T
     keep, descs, host = [], {}, {}
+    cache_q = []  # the cache's quantisation, one call per channel group (timed once each)
     for name, groups, layout, stream in (("k", LC_GROUPS_K, tq.TQ_LAYOUT_KEYS, 11),
                                          ("v", LC_GROUPS_V, tq.TQ_LAYOUT_VALUES, 12)):
         log(f"longctx: generating {name} ({n * d * 2 / 1e9:.1f} GB bf16), outlier channels first")
@@ -390,7 +391,15 @@ def longctx_decode(args):
             pk = torch.empty(tq.tq_packed_bytes(gd, bits, var, layout, n) // 4, dtype=torch.int32, device="cuda")
             nr = torch.empty(n, dtype=torch.int16, device="cuda")
             rr = torch.empty(n, dtype=torch.int16, device="cuda") if prod else None
-            tq.tq_quantize_kv(q, layout, tq.TQ_BF16, X[:, ch:], n, d, pk, nr, rr)
+            with Timer() as tm:
+                tq.tq_quantize_kv(q, layout, tq.TQ_BF16, X[:, ch:], n, d, pk, nr, rr)
+            # HBM bytes: the group's bf16 channels read, its bit planes and fp16 norms written
+            qbytes = n * gd * 2 + pk.numel() * 4 + n * 2 * (2 if prod else 1)
+            cache_q.append({"group": f"{'K' if name == 'k' else 'V'} channels {ch}..{ch + gd - 1}, {bits}"
+                                     f"{'+1' if prod else ''} bits", "vectors": n, "ms": round(tm.ms, 3),
+                            "vectors_per_s": round(n / (tm.ms * 1e-3), 1),
+                            "hbm_gbs": round(qbytes / (tm.ms * 1e-3) / 1e9, 1),
+                            "hbm_roofline_frac": round(qbytes / (tm.ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
             keep += [R_t, S_t, pk, nr, rr]
             gl.append(tq.make_group(q, ch, pk, nr, rr, T))
         torch.cuda.synchronize()
@@ -434,7 +443,8 @@ def longctx_decode(args):
     s_cos = (s_gpu * s_ex).sum(axis=0) / (np.linalg.norm(s_gpu, axis=0) * np.linalg.norm(s_ex, axis=0))
     bf16_bytes = n * d * 2 * 2
     res = {"per_call_ms": ms, "wall_ms": wall_ms, "call_bytes": call_bytes, "dk_ms": dk_ms, "kv_bytes": kv_bytes,
-           "extras": {"bf16_attention_roofline_ms": round(bf16_bytes / HBM_PEAK_GBS / 1e6, 4),
+           "extras": {"cache_quantize": cache_q,
+                      "bf16_attention_roofline_ms": round(bf16_bytes / HBM_PEAK_GBS / 1e6, 4),
                       "speedup_vs_bf16_roofline": round(bf16_bytes / HBM_PEAK_GBS / 1e6 / ms, 3),
                       "quality_vs_exact_bf16_attention": {
                           "sample": "batch 0, query heads 0-3 (KV head 0), 131072 tokens",

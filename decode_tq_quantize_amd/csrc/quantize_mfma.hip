@@ -1,17 +1,21 @@
-// Online TurboQuant compression of 128-channel KV vectors on the gfx950
-// matrix cores (riverfrot "TurboQuant" post, section 4.1: x~ = R x / |x|;
-// section 4.2: Lloyd-Max interval index per coordinate; section 4.3: the
-// residual r~ = x~ - c[idx] projected with S, signs kept, plus |r~|).
+// Online TurboQuant compression of KV vectors of d = 32, 64, 96 or 128
+// channels on the gfx950 matrix cores (riverfrot "TurboQuant" post, section
+// 4.1: x~ = R x / |x|; section 4.2: Lloyd-Max interval index per coordinate;
+// section 4.3: the residual r~ = x~ - c[idx] projected with S, signs kept,
+// plus |r~|).
 //
-// A persistent workgroup of 4 waves streams tiles of 32 vectors; wave w owns
-// output coordinates 32 w .. 32 w + 31. bf16 inputs are exact in bf16, so R
+// A persistent workgroup of d / 32 waves streams tiles of 32 vectors; wave w
+// owns output coordinates 32 w .. 32 w + 31. bf16 inputs are exact in bf16, so R
 // is held in registers as bf16 high and low parts (MFMA A operands) and R x
 // runs on v_mfma_f32_16x16x32_bf16 with both products accumulated in place;
 // one more MFMA with the input as both operands gives the vectors' Gram
 // matrix, whose diagonal is |x|^2. fp32 inputs use v_mfma_f32_16x16x4_f32
 // with R in fp32. The rotated vector comes out with lane l holding
 // coordinates 32 w + 16 m + 4 (l / 16) + r (m = 0, 1; r = 0..3) of vector
-// l % 16 of a 16-vector half; the interval index is found there by binary
+// l % 16 of a 16-vector half. Every contraction over the d input coordinates
+// runs in d / 32 steps of 32, lane group q (= lane / 16) supplying the d / 4
+// consecutive coordinates d q / 4 .. d q / 4 + d / 4 - 1 (8 per step) on both
+// operands. The interval index is found there by binary
 // search over the thresholds, the residual's bf16 parts go through LDS to
 // the operand layout of S r~ (bf16 matrix cores, S in LDS), and the code
 // and sign bits are packed straight from wave ballots of the compares into
@@ -23,9 +27,20 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kD = 128;
-constexpr int kThreads = 256;
 constexpr int kTile = 32;  // vectors per iteration (one values tile, two keys tiles)
+
+// 16-byte chunks per LDS row of a d-wide bf16 matrix (S, and the residuals):
+// 128-wide rows are swizzled (chunk c of row r at c ^ (r % 16)), narrower
+// rows padded to an odd number of chunks, so the 16 rows that a step reads
+// at once hit 16 different bank groups either way.
+template <int D>
+constexpr int row_chunks() {
+  return D == 128 ? 16 : D / 8 + 1;
+}
+template <int D>
+__device__ __forceinline__ int swz(int row, int c) {
+  return D == 128 ? c ^ (row & 15) : c;
+}
 
 struct QmArgs {
   const void* x;
@@ -96,14 +111,16 @@ __device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uin
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, bf16x2));
 }
 
-// Rows 32 w + 16 m + (lane % 16), columns 32 (lane / 16) .. + 31 of M.
-__device__ __forceinline__ void load_rows(const float* __restrict__ M, int w, int lane, float (&A)[2][32]) {
+// Rows 32 w + 16 m + (lane % 16), columns D (lane / 16) / 4 .. + D / 4 - 1
+// of the D x D matrix M.
+template <int D>
+__device__ __forceinline__ void load_rows(const float* __restrict__ M, int w, int lane, float (&A)[2][D / 4]) {
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const float4* p = reinterpret_cast<const float4*>(M + (int64_t)(32 * w + 16 * m + (lane & 15)) * kD +
-                                                      32 * (lane >> 4));
+    const float4* p = reinterpret_cast<const float4*>(M + (int64_t)(32 * w + 16 * m + (lane & 15)) * D +
+                                                      (D / 4) * (lane >> 4));
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < D / 16; ++k) {
       const float4 v = p[k];
       A[m][4 * k] = v.x;
       A[m][4 * k + 1] = v.y;
@@ -113,26 +130,29 @@ __device__ __forceinline__ void load_rows(const float* __restrict__ M, int w, in
   }
 }
 
-// Raw input of one lane: coordinates 32 q .. 32 q + 31 of one vector row.
-template <bool BF16IN>
+// Raw input of one lane: coordinates D q / 4 .. D q / 4 + D / 4 - 1 of one
+// vector row.
+template <int D, bool BF16IN>
 struct XIn;
-template <>
-struct XIn<true> {
-  uint4 w[4];
+template <int D>
+struct XIn<D, true> {
+  uint4 w[D / 32];
 };
-template <>
-struct XIn<false> {
-  float4 f[8];
+template <int D>
+struct XIn<D, false> {
+  float4 f[D / 16];
 };
-__device__ __forceinline__ void load_in(XIn<true>& r, const QmArgs& a, int64_t v, int q) {
-  const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + v * a.stride + 32 * q);
+template <int D>
+__device__ __forceinline__ void load_in(XIn<D, true>& r, const QmArgs& a, int64_t v, int q) {
+  const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + v * a.stride + (D / 4) * q);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) r.w[k] = p[k];
+  for (int k = 0; k < D / 32; ++k) r.w[k] = p[k];
 }
-__device__ __forceinline__ void load_in(XIn<false>& r, const QmArgs& a, int64_t v, int q) {
-  const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + v * a.stride + 32 * q);
+template <int D>
+__device__ __forceinline__ void load_in(XIn<D, false>& r, const QmArgs& a, int64_t v, int q) {
+  const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + v * a.stride + (D / 4) * q);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) r.f[k] = p[k];
+  for (int k = 0; k < D / 16; ++k) r.f[k] = p[k];
 }
 
 // Lane exchanges with lane l ^ 16 and l ^ 32 (v_permlane16/32_swap: with
@@ -187,21 +207,26 @@ __device__ __forceinline__ int interval(float u, const float (&th)[(1 << B) - 1]
   return idx;
 }
 
-template <bool BF16IN, int B, bool PROD, bool KEYS>
-__global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
+// (registers sized for two waves per SIMD)
+template <int D, bool BF16IN, int B, bool PROD, bool KEYS>
+__global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
+  constexpr int NG = D / 32;  // waves (32-coordinate groups), and 32-coordinate steps of a contraction
+  constexpr int kThreads = 64 * NG;
+  constexpr int RC = row_chunks<D>();
   // The QJL projection S r~ runs on the bf16 matrix cores with both operands
   // split into bf16 high and low parts: S r~ = S_hi r_hi + S_hi r_lo +
   // S_lo r_hi up to about 2^-17 |S| |r~| per term. S (PROD) stays in LDS as
-  // the two parts (two workgroups fit a compute unit); so does the residual
-  // of the current 16 vectors. Rows are 16 chunks of 8 values; chunk c of
-  // row r is stored at c ^ (r % 16), so that the 16 rows read at once hit
-  // different banks.
-  __shared__ uint4 Sq[2][PROD ? kD : 1][kD / 8];
+  // the two parts (for d = 128 two workgroups fit a compute unit); so does
+  // the residual of the current 16 vectors. Rows are d / 8 chunks of 8
+  // values (placed by swz within row_chunks<D>() slots).
+  __shared__ uint4 Sq[2][PROD ? D : 1][RC];
   // residual parts of both 16-vector halves ([half][hi / lo][vector][chunk]);
   // once the projection has read them, the same space takes the residual
-  // norms' partial sums (S and this fill the 160 KB of two workgroups)
-  __shared__ uint4 rq[PROD ? 2 : 1][2][PROD ? 16 : 1][kD / 8];
-  float(&rho_part)[4][kTile] = *reinterpret_cast<float(*)[4][kTile]>(&rq[0][0][0][0]);
+  // norms' partial sums (for d = 128, S and this fill the 160 KB of two
+  // workgroups)
+  __shared__ uint4 rq[PROD ? 2 : 1][2][PROD ? 16 : 1][RC];
+  static_assert(!PROD || sizeof(rq) >= sizeof(float) * NG * kTile, "norm partials must fit the residual space");
+  float(&rho_part)[NG][kTile] = *reinterpret_cast<float(*)[NG][kTile]>(&rq[0][0][0][0]);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, nl = lane & 15;
@@ -218,14 +243,14 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
   // R as A operands: fp32 (fp32 input), or bf16 high and low parts (bf16
   // input, which is exact in bf16: R x = R_hi x + R_lo x, |R - R_hi - R_lo|
   // <= 2^-18 |R| elementwise)
-  float AR[2][32];
-  bf16x8 RH[2][4], RL[2][4];
-  load_rows(a.R, w, lane, AR);
+  float AR[2][D / 4];
+  bf16x8 RH[2][NG], RL[2][NG];
+  load_rows<D>(a.R, w, lane, AR);
   if constexpr (BF16IN) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < NG; ++kk)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float r = AR[m][8 * kk + e];
@@ -236,8 +261,8 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         }
   }
   if constexpr (PROD) {
-    for (int e = tid; e < kD * kD / 8; e += kThreads) {
-      const int row = e / (kD / 8), c = e % (kD / 8);
+    for (int e = tid; e < D * D / 8; e += kThreads) {
+      const int row = e / (D / 8), c = e % (D / 8);
       const float4 u0 = reinterpret_cast<const float4*>(a.S)[2 * e];
       const float4 u1 = reinterpret_cast<const float4*>(a.S)[2 * e + 1];
       uint32_t h[4], l[4];
@@ -245,8 +270,8 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
       split_bf16(u0.z, u0.w, h[1], l[1]);
       split_bf16(u1.x, u1.y, h[2], l[2]);
       split_bf16(u1.z, u1.w, h[3], l[3]);
-      Sq[0][row][c ^ (row & 15)] = make_uint4(h[0], h[1], h[2], h[3]);
-      Sq[1][row][c ^ (row & 15)] = make_uint4(l[0], l[1], l[2], l[3]);
+      Sq[0][row][swz<D>(row, c)] = make_uint4(h[0], h[1], h[2], h[3]);
+      Sq[1][row][swz<D>(row, c)] = make_uint4(l[0], l[1], l[2], l[3]);
     }
   }
   // centroids as values (the residual picks one by the index bits)
@@ -266,14 +291,14 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
     return KEYS ? 16 * nt + c : 8 * (c & 3) + 4 * nt + (c >> 2);
   };
   // a tile's inputs (rows past n re-read row n - 1 and are masked)
-  auto load_tile = [&](XIn<BF16IN>(&dst)[2], int64_t t) __attribute__((always_inline)) {
+  auto load_tile = [&](XIn<D, BF16IN>(&dst)[2], int64_t t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) load_in(dst[nt], a, min(t * kTile + col_vec(nt, nl), a.n - 1), q);
+    for (int nt = 0; nt < 2; ++nt) load_in<D>(dst[nt], a, min(t * kTile + col_vec(nt, nl), a.n - 1), q);
   };
   const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
   // one tile, whose inputs are in cur; once the rotation has read them, cur
   // takes the inputs of tile tnext
-  auto body = [&](int64_t tile, XIn<BF16IN>(&cur)[2], int64_t tnext) __attribute__((always_inline)) {
+  auto body = [&](int64_t tile, XIn<D, BF16IN>(&cur)[2], int64_t tnext) __attribute__((always_inline)) {
     const int64_t v0 = tile * kTile;
     // 1. rotated coordinates 32 w + 16 m + 4 q + r of vector 16 nt + nl, and
     // the vector norms
@@ -282,14 +307,14 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       if constexpr (BF16IN) {
-        const uint4(&xw)[4] = cur[nt].w;
+        const uint4(&xw)[NG] = cur[nt].w;
         // one accumulator per 16 rows: the matrix cores accumulate in place
         // back to back, so the hi and lo products need no separate sums
         v4f ah[2], gram = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 2; ++m) ah[m] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < NG; ++kk) {
           const bf16x8 xb = __builtin_bit_cast(bf16x8, xw[kk]);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
@@ -309,23 +334,23 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         nrm[nt] = __builtin_amdgcn_sqrtf(__shfl(dsel, 16 * (nl >> 2) + nl, 64));
       } else {
         float s2 = 0.f;
-        float x[32];
+        float x[D / 4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < D / 16; ++k) {
           x[4 * k] = cur[nt].f[k].x;
           x[4 * k + 1] = cur[nt].f[k].y;
           x[4 * k + 2] = cur[nt].f[k].z;
           x[4 * k + 3] = cur[nt].f[k].w;
         }
 #pragma unroll
-        for (int k = 0; k < 32; ++k) s2 = fmaf(x[k], x[k], s2);
+        for (int k = 0; k < D / 4; ++k) s2 = fmaf(x[k], x[k], s2);
         v4f ac[2][4];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
           for (int c = 0; c < 4; ++c) ac[m][c] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 32; ++kk) {
+        for (int kk = 0; kk < D / 4; ++kk) {
           ac[0][kk & 3] = mfma_f32(AR[0][kk], x[kk], ac[0][kk & 3]);
           ac[1][kk & 3] = mfma_f32(AR[1][kk], x[kk], ac[1][kk & 3]);
         }
@@ -457,21 +482,21 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
           uint32_t h0, l0, h1, l1;
           split_bf16(res[nt][m][0], res[nt][m][1], h0, l0);
           split_bf16(res[nt][m][2], res[nt][m][3], h1, l1);
-          const int c = (4 * w + 2 * m + (q >> 1)) ^ nl, half = q & 1;
+          const int c = swz<D>(nl, 4 * w + 2 * m + (q >> 1)), half = q & 1;
           reinterpret_cast<uint2*>(&rq[nt][0][nl][c])[half] = make_uint2(h0, h1);
           reinterpret_cast<uint2*>(&rq[nt][1][nl][c])[half] = make_uint2(l0, l1);
         }
       __syncthreads();
-      // step kk contracts coordinates 32 q' + 8 kk .. + 7 from lane group q'
-      // (chunk 4 q' + kk), the same assignment on both operands
+      // step kk contracts coordinates 8 (NG q' + kk) .. + 7 from lane group q'
+      // (chunk NG q' + kk), the same assignment on both operands
       v4f pc[2][2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int m = 0; m < 2; ++m) pc[nt][m] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int ph = (4 * q + kk) ^ nl;
+      for (int kk = 0; kk < NG; ++kk) {
+        const int ph = swz<D>(nl, NG * q + kk);
         bf16x8 rh[2], rl[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
@@ -525,8 +550,15 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
       if (w == 0 && q < 2) {
         const int vt = 16 * q + nl;  // column nl of half q
         if (v0 + col_vec(q, nl) < a.n) {
-          const float rho =
-              __builtin_amdgcn_sqrtf((rho_part[0][vt] + rho_part[1][vt]) + (rho_part[2][vt] + rho_part[3][vt]));
+          float s;
+          if constexpr (NG == 4)
+            s = (rho_part[0][vt] + rho_part[1][vt]) + (rho_part[2][vt] + rho_part[3][vt]);
+          else {
+            s = rho_part[0][vt];
+#pragma unroll
+            for (int i = 1; i < NG; ++i) s += rho_part[i][vt];
+          }
+          const float rho = __builtin_amdgcn_sqrtf(s);
           a.rnorm[v0 + col_vec(q, nl)] = tqd::f32_to_half_bits(rho);
         }
       }
@@ -539,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
       for (int nt = 0; nt < 2; ++nt) {
         if (v0 + 16 * nt < nround) {
           const int64_t kt = (v0 >> 4) + nt;
-          uint32_t* dst = a.packed + (kt * (kD / 32) + w) * tqk::kKeysTile * P;
+          uint32_t* dst = a.packed + (kt * NG + w) * tqk::kKeysTile * P;
 #pragma unroll
           for (int pass = 0; pass < (P + 3) / 4; ++pass) {
             const int p = 4 * pass + q;
@@ -551,14 +583,14 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(QmArgs a) {
         }
       }
     } else {
-      uint32_t* dst = a.packed + (tile * kD + 32 * w) * P;
+      uint32_t* dst = a.packed + (tile * D + 32 * w) * P;
 #pragma unroll
       for (int i = 0; i < NW; ++i)
         if (64 * i + lane < 32 * P) dst[64 * i + lane] = ow[i];
     }
     if constexpr (PROD) __syncthreads();  // rq (and rho_part in it) is rewritten by the next tile
   };
-  XIn<BF16IN> xa[2], xb[2];
+  XIn<D, BF16IN> xa[2], xb[2];
   load_tile(xa, blockIdx.x);
   if constexpr (BF16IN) {
     // two tiles' inputs in flight (the two buffers alternate, nothing is copied)
@@ -578,7 +610,8 @@ namespace tqk {
 
 bool quantize_mfma_supported(const tq_quantizer& q, tq_dtype dt, const void* x, int64_t stride) {
   const int64_t esz = dt == TQ_BF16 ? 2 : 4;
-  return q.d == kD && ((stride * esz) % 16) == 0 && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  return (q.d == 32 || q.d == 64 || q.d == 96 || q.d == 128) && ((stride * esz) % 16) == 0 &&
+         ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
 }
 
 hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
@@ -600,19 +633,22 @@ hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtyp
   a.norm = norm;
   a.rnorm = rnorm;
   using Fn = void (*)(QmArgs);
-  // [bf16 input][mse bits - 1][prod][keys layout]
-#define TQ_QM(BF, B) {{quantize_mfma_kernel<BF, B, false, false>, quantize_mfma_kernel<BF, B, false, true>}, \
-                      {quantize_mfma_kernel<BF, B, true, false>, quantize_mfma_kernel<BF, B, true, true>}}
-  static const Fn fns[2][4][2][2] = {{TQ_QM(false, 1), TQ_QM(false, 2), TQ_QM(false, 3), TQ_QM(false, 4)},
-                                     {TQ_QM(true, 1), TQ_QM(true, 2), TQ_QM(true, 3), TQ_QM(true, 4)}};
+  // [d / 32 - 1][bf16 input][mse bits - 1][prod][keys layout]
+#define TQ_QM(D, BF, B) {{quantize_mfma_kernel<D, BF, B, false, false>, quantize_mfma_kernel<D, BF, B, false, true>}, \
+                         {quantize_mfma_kernel<D, BF, B, true, false>, quantize_mfma_kernel<D, BF, B, true, true>}}
+#define TQ_QD(D) {{TQ_QM(D, false, 1), TQ_QM(D, false, 2), TQ_QM(D, false, 3), TQ_QM(D, false, 4)}, \
+                  {TQ_QM(D, true, 1), TQ_QM(D, true, 2), TQ_QM(D, true, 3), TQ_QM(D, true, 4)}}
+  static const Fn fns[4][2][4][2][2] = {TQ_QD(32), TQ_QD(64), TQ_QD(96), TQ_QD(128)};
+#undef TQ_QD
 #undef TQ_QM
-  const Fn fn = fns[a.bf16 ? 1 : 0][a.B - 1][a.prod ? 1 : 0][layout == TQ_LAYOUT_KEYS ? 1 : 0];
+  const Fn fn = fns[q.d / 32 - 1][a.bf16 ? 1 : 0][a.B - 1][a.prod ? 1 : 0][layout == TQ_LAYOUT_KEYS ? 1 : 0];
+  const int threads = 2 * q.d;
   // persistent grid: as many workgroups as the device holds at once (the
   // rotation-only kernels need far fewer registers and no S in LDS)
   // (both queried once per device and kernel, not per call)
-  const int64_t slots = (int64_t)device_cus() * kernel_wgs_per_cu(reinterpret_cast<const void*>(fn), kThreads);
+  const int64_t slots = (int64_t)device_cus() * kernel_wgs_per_cu(reinterpret_cast<const void*>(fn), threads);
   const int64_t grid = a.ntiles < slots ? a.ntiles : slots;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -42,6 +42,17 @@ def _key_rows(words, rows, d, mse_bits, prod):
     return idx[pos], (z[pos] if z is not None else None)
 
 
+def _value_rows(words, rows, d, mse_bits, prod):
+    """Codes of the given rows of a value-layout array (their whole 32-vector tiles unpacked)."""
+    P = mse_bits + (1 if prod else 0)
+    per_tile = d * P
+    tiles = np.unique(rows // 32)
+    sub = words.reshape(-1, per_tile)[tiles].reshape(-1)
+    idx, z = otq.unpack(sub, len(tiles) * 32, d, mse_bits, prod, "values")
+    pos = np.searchsorted(tiles, rows // 32) * 32 + rows % 32
+    return idx[pos], (z[pos] if z is not None else None)
+
+
 def _slice_words(words, r0, T, d, mse_bits, prod, layout):
     """Packed words of rows r0 .. r0 + T (r0 and T multiples of the layout's tile)."""
     P = mse_bits + (1 if prod else 0)
@@ -115,6 +126,44 @@ def test_prefill_quantize_full_layer(keys):
     want = otq.quantize(xs, gq.oq)
     assert_codes_match(idx[rows], None if z is None else z[rows], to_np_f16(norm)[rows],
                        None if rnorm is None else to_np_f16(rnorm)[rows], want, gq.oq)
+
+
+@pytest.mark.parametrize("keys", [True, False])
+def test_channel_group_quantize_large(keys):
+    # the long-context cache's channel groups (32 outlier channels, 96 others;
+    # keys 2 + 1 and 1 + 1 bits, values 3 and 2 bits) quantised as the
+    # benchmark quantises them, strided out of 128-channel bf16 rows, for 8 of
+    # its 64 sequences: 8 x 8 KV heads x 131072 tokens = 8,388,608 vectors per
+    # call; sampled rows against the oracle
+    n, d = 8 * 8 * 131072, 128
+    stream = 11 if keys else 12
+    print(f"channel-group quantise keys={keys} n={n}", flush=True)
+    X = sdev.kv_with_outliers(8, 8, 131072, d, 0, 1.0, seed=4, stream=stream)
+    X[..., :32] *= 10
+    X = X.view(n, d)
+    rows = np.sort(synth.rng(stream, 7).choice(n, 8192, replace=False))
+    rows = np.unique(np.concatenate([rows, np.arange(n - 40, n), np.arange(31, n, n // 64)]))
+    xs = X[torch_dev(rows.astype(np.int64))].float().cpu().numpy().astype(np.float64)
+    groups = [(0, 32, 2, True), (32, 96, 1, True)] if keys else [(0, 32, 3, False), (32, 96, 2, False)]
+    layout = tq.TQ_LAYOUT_KEYS if keys else tq.TQ_LAYOUT_VALUES
+    for gi, (ch, gd, bits, prod) in enumerate(groups):
+        seed = 40 + gi + 10 * stream
+        R = synth.haar_orthogonal(gd, seed)
+        S = synth.gaussian_matrix(gd, gd, seed) if prod else None
+        R_t, S_t = torch_dev(R), (torch_dev(S) if prod else None)
+        var = tq.TQ_PROD if prod else tq.TQ_MSE
+        q = tq.tq_quantizer_init(gd, bits, var, R_t, S_t)
+        pk = torch.empty(tq.tq_packed_bytes(gd, bits, var, layout, n) // 4, dtype=torch.int32, device="cuda")
+        nr = torch.empty(n, dtype=torch.int16, device="cuda")
+        rr = torch.empty(n, dtype=torch.int16, device="cuda") if prod else None
+        tq.tq_quantize_kv(q, layout, tq.TQ_BF16, X[:, ch:], n, d, pk, nr, rr)
+        torch.cuda.synchronize()
+        words = to_np_u32(pk)
+        idx, z = (_key_rows if keys else _value_rows)(words, rows, gd, bits, prod)
+        oq = otq.make_quantizer(gd, bits, prod, R, S)
+        want = otq.quantize(xs[:, ch:ch + gd], oq)
+        assert_codes_match(idx, z, to_np_f16(nr)[rows], None if rr is None else to_np_f16(rr)[rows], want, oq)
+        del pk, nr, rr
 
 
 def test_long_context_decode_full_size():

@@ -85,6 +85,15 @@ QUANT_CASES = [
     (64, 4, False, "values", 64, "bf16"),
     (1536, 3, True, "keys", 40, "f32"),
     (2048, 1, True, "keys", 5, "f32"),
+    # channel groups on the matrix cores (d = 32, 64, 96): several tiles and a
+    # ragged tail
+    (32, 3, False, "values", 1000, "bf16"),
+    (32, 1, True, "keys", 777, "bf16"),
+    (64, 3, True, "keys", 333, "f32"),
+    (64, 2, True, "values", 513, "bf16"),
+    (96, 2, True, "keys", 1000, "bf16"),
+    (96, 3, False, "values", 999, "bf16"),
+    (96, 4, True, "values", 301, "bf16"),
 ]
 
 
