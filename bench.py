@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--only", default="",
-                   help="comma list of extras to run: single,tiny,quantize,search,bits,niah,append,paged")
+                   help="comma list of extras to run: single,tiny,quantize,search,bits,niah,append,step,paged")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one 256 MiB device-to-device copy (the known-size reference for the "
                         "FETCH_SIZE / WRITE_SIZE counters)")
@@ -957,6 +957,86 @@ def append_step(steps=200):
                         "two tq_append_kv calls beside it)"}
 
 
+def decode_step(steps=100):
+    """One decode step per call: append every (sequence, KV head)'s new key and value, then attend.
+
+    tq_decode_step (the appends inside the decode's query-transform launch)
+    against the two-call sequence (tq_append_kv_pair, then tq_decode_attn)
+    and against the decode alone, each as a graph of `steps` calls whose
+    lengths grow by one token per call. d = 128, K 3+1-bit prod (S R folded),
+    V 3-bit MSE, bf16 rows; the caches stay resident in the last-level cache
+    where they fit (the batch-1 one does), so the launch costs dominate there.
+    """
+    import numpy as np
+    import torch
+
+    import decode_tq_quantize_amd as tq
+    import synth
+    from synth import device as sdev
+
+    res = {}
+    for name, B, Hq, Hkv, T in (("batch 1 x 32768 tokens", 1, 32, 8, 32768),
+                                ("batch 64 x 4096 tokens", 64, 32, 8, 4096)):
+        d = 128
+        n = B * Hkv * T
+        Rk_t, Sk_t = dev(synth.haar_orthogonal(d, 8)), dev(synth.gaussian_matrix(d, d, 8))
+        Rv_t = dev(synth.haar_orthogonal(d, 8, synth.STREAM_R_V))
+        qk = tq.tq_quantizer_init(d, 3, tq.TQ_PROD, Rk_t, Sk_t)
+        SR = torch.empty(tq.tq_fold_bytes(d) // 4, dtype=torch.float32, device="cuda")
+        tq.tq_quantizer_fold(qk, SR)
+        qv = tq.tq_quantizer_init(d, 3, tq.TQ_MSE, Rv_t)
+        kp = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_PROD, tq.TQ_LAYOUT_KEYS, n) // 4, dtype=torch.int32,
+                         device="cuda")
+        vp = torch.empty(tq.tq_packed_bytes(d, 3, tq.TQ_MSE, tq.TQ_LAYOUT_VALUES, n) // 4, dtype=torch.int32,
+                         device="cuda")
+        kn, kr, vn = (torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(3))
+        X = sdev.kv_with_outliers(B, Hkv, T, d, 4, 10.0, seed=8, stream=41).view(n, d)
+        tq.tq_quantize_kv(qk, tq.TQ_LAYOUT_KEYS, tq.TQ_BF16, X, n, d, kp, kn, kr)
+        X = sdev.kv_with_outliers(B, Hkv, T, d, 4, 10.0, seed=8, stream=42).view(n, d)
+        tq.tq_quantize_kv(qv, tq.TQ_LAYOUT_VALUES, tq.TQ_BF16, X, n, d, vp, vn)
+        del X
+        kd = tq.make_desc([tq.make_group(qk, 0, kp, kn, kr, T)])
+        vd = tq.make_desc([tq.make_group(qv, 0, vp, vn, None, T)])
+        gen = sdev.generator(8, 43)
+        k_new = torch.randn((B * Hkv, d), generator=gen, device="cuda").to(torch.bfloat16)
+        v_new = torch.randn((B * Hkv, d), generator=gen, device="cuda").to(torch.bfloat16)
+        q_t = torch.randn((B, Hq, d), generator=gen, device="cuda").to(torch.bfloat16)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        wsb = tq.tq_decode_workspace_bytes(kd, vd, B, Hq, Hkv, T)
+        ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device="cuda")
+        scale = 1.0 / math.sqrt(d)
+        start = T - steps - 1
+        lens = [torch.full((B,), start + 1 + i, dtype=torch.int32, device="cuda") for i in range(steps)]
+        base = torch.arange(B * Hkv, device="cuda", dtype=torch.int64) * T
+        rows = [base + (start + i) for i in range(steps)]
+
+        def fused(i):
+            tq.tq_decode_step(kd, vd, k_new, v_new, tq.TQ_BF16, q_t, tq.TQ_BF16, B, Hq, Hkv, T, lens[i % steps],
+                              scale, out, None, ws, wsb)
+
+        def two_calls(i):
+            tq.tq_append_kv_pair(qk, qv, tq.TQ_BF16, k_new, v_new, B * Hkv, d, d, rows[i % steps], n, kp, kn, kr, vp,
+                                 vn)
+            tq.tq_decode_attn(kd, vd, q_t, tq.TQ_BF16, B, Hq, Hkv, T, lens[i % steps], scale, out, None, ws, wsb)
+
+        def decode_only(i):
+            tq.tq_decode_attn(kd, vd, q_t, tq.TQ_BF16, B, Hq, Hkv, T, lens[i % steps], scale, out, None, ws, wsb)
+
+        r = {}
+        for label, fn in (("tq_decode_step_us", fused), ("append_pair_then_decode_us", two_calls),
+                          ("decode_alone_us", decode_only)):
+            ms, _, _ = graph_ms(fn, steps)
+            r[label] = round(ms * 1e3, 3)
+        r["append_cost_in_step_us"] = round(r["tq_decode_step_us"] - r["decode_alone_us"], 3)
+        r["append_cost_two_calls_us"] = round(r["append_pair_then_decode_us"] - r["decode_alone_us"], 3)
+        res[name] = r
+        del kp, vp, kn, kr, vn
+        torch.cuda.empty_cache()
+    res["workload"] = ("one new token per (sequence, KV head) appended and attended per step, 32 q / 8 KV heads, "
+                       "d=128, K 3+1-bit prod (S R folded), V 3-bit MSE; graphs of 100 steps")
+    return res
+
+
 NIAH_KEYS = [("3+1 prod", 3, True), ("4 MSE-only", 4, False), ("2+1 prod", 2, True), ("3 MSE-only", 3, False),
              ("1+1 prod", 1, True)]
 
@@ -1205,6 +1285,8 @@ def main():
         run_extra(extras, "paged_decode", paged_decode)
     if want("append"):
         run_extra(extras, "append_step", append_step)
+    if want("step"):
+        run_extra(extras, "decode_step", decode_step)
     if want("niah"):
         run_extra(extras, "niah_proxy", niah_proxy)
     if want("bits") and single is not None and "oracle_inputs" in single:

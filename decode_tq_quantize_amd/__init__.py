@@ -38,7 +38,7 @@ TQ_MAX_GROUPS = 4
 EXPORTS = [
     "tq_build_codebook", "tq_quantizer_init", "tq_packed_bytes", "tq_status_string",
     "tq_quantize_kv", "tq_append_kv", "tq_append_kv_pair", "tq_decode_workspace_bytes", "tq_decode_attn", "tq_kv_bit_allocation",
-    "tq_decode_paged_workspace_bytes", "tq_decode_attn_paged", "tq_decode_attn_noalloc",
+    "tq_decode_paged_workspace_bytes", "tq_decode_attn_paged", "tq_decode_attn_noalloc", "tq_decode_step",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_fold_bytes", "tq_fold_qjl",
 ]
 
@@ -114,6 +114,10 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attn_noalloc.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_void_p, c_int, c_int, c_int,
                                              c_int, c_int, c_void_p, c_float, c_void_p, c_void_p, c_void_p]
         L.tq_decode_attn_noalloc.restype = c_int
+        L.tq_decode_step.argtypes = [POINTER(tq_kv_desc), POINTER(tq_kv_desc), c_void_p, c_void_p, c_int, c_void_p,
+                                     c_int, c_int, c_int, c_int, c_int, c_void_p, c_float, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]
+        L.tq_decode_step.restype = c_int
         L.tq_search_workspace_bytes.argtypes = [POINTER(tq_group), c_int64, c_int, c_int]
         L.tq_search_workspace_bytes.restype = c_size_t
         L.tq_search_topk.argtypes = [POINTER(tq_group), c_int64, c_void_p, c_int, c_int, c_void_p, c_void_p,
@@ -256,6 +260,14 @@ def tq_decode_attn_noalloc(k: tq_kv_desc, v: tq_kv_desc, q, q_dtype: int, B: int
     _check(lib().tq_decode_attn_noalloc(ctypes.byref(k), ctypes.byref(v), _ptr(q), q_dtype, B, Hq, Hkv, T_max,
                                         _ptr(seq_lens), scale, _ptr(out), _ptr(scores_out), _stream(stream)),
            "tq_decode_attn_noalloc")
+
+
+def tq_decode_step(k: tq_kv_desc, v: tq_kv_desc, k_new, v_new, kv_dtype: int, q, q_dtype: int, B: int, Hq: int,
+                   Hkv: int, T_max: int, seq_lens, scale: float, out, scores_out, ws, ws_bytes: int,
+                   stream=None) -> None:
+    _check(lib().tq_decode_step(ctypes.byref(k), ctypes.byref(v), _ptr(k_new), _ptr(v_new), kv_dtype, _ptr(q),
+                                q_dtype, B, Hq, Hkv, T_max, _ptr(seq_lens), scale, _ptr(out), _ptr(scores_out),
+                                _ptr(ws), ws_bytes, _stream(stream)), "tq_decode_step")
 
 
 def tq_decode_paged_workspace_bytes(k: tq_kv_desc, v: tq_kv_desc, B: int, Hq: int, Hkv: int, T_max: int,

@@ -50,6 +50,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "quantize_tile.h"
 
 namespace {
 
@@ -280,7 +281,7 @@ constexpr int kQtThreads = 256;
 // operands of every slot for those coordinates. Operand scales come from
 // bounds that need no other slice: |q~_c| <= |R_c| |q| = |q| (R orthogonal)
 // and |q^_c| <= max_c |(S R)_c| |q|, each with 0.1 % room for rounding.
-__global__ __launch_bounds__(kQtThreads) void qfused_kernel(Args a) {
+__device__ __forceinline__ void qfused_body(const Args& a, const int key, const int slice) {
   __shared__ float qts[kHT][kRowSlice], qhs[kHT][kRowSlice];
   __shared__ float sc_mse[kHT], sc_qjl[kHT];
   const int nk = a.nk, Hkv = a.Hkv, HT = a.HT, G = a.G, Hq = a.Hq, qbf16 = a.qbf16, nslots = a.nslots;
@@ -290,7 +291,6 @@ __global__ __launch_bounds__(kQtThreads) void qfused_kernel(Args a) {
   const float* F0 = a.k[0].SR;
   const float* F1 = a.k[1].SR;
   const float amax0 = a.k[0].amax, amax1 = a.k[1].amax;
-  const int key = blockIdx.x, slice = blockIdx.y;
   const int b = key / (Hkv * HT);
   const int g = (key / HT) % Hkv;
   const int ht = key % HT;
@@ -413,6 +413,37 @@ __global__ __launch_bounds__(kQtThreads) void qfused_kernel(Args a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) dst[(16 * gp + 4 * h + m) * 8 + byte0 / 4] = dw[m];
   }
+}
+
+__global__ __launch_bounds__(kQtThreads) void qfused_kernel(Args a) { qfused_body(a, blockIdx.x, blockIdx.y); }
+
+// The appends of a decode step (riverfrot sections 2.2-2.3 and 4.1-4.3: the
+// new token's key and value are compressed into the cache before the query
+// attends to them), carried by the query-transform launch: workgroups past
+// the transform's take 2-vector tiles of one group's appends each.
+struct StepAppend {
+  tqq::QArgs q[2 * TQ_MAX_GROUPS];
+  int n;             // argument sets
+  int tiles;         // 2-vector tiles per set
+  int key_columns;   // transform workgroups along x (the rest are appends)
+};
+// (tiles of 2 vectors, the matrices staged through LDS 32 columns at a time:
+// about 19 KB of LDS, so the transform's workgroups keep their occupancy;
+// staging 128 columns at once measured no faster)
+constexpr int kStepTV = 2, kStepJC = 32;
+static_assert(sizeof(Args) + sizeof(StepAppend) <= 4096, "kernel arguments of the step launch");
+
+__global__ __launch_bounds__(kQtThreads) void qfused_step_kernel(Args a, StepAppend st) {
+  static_assert(kQtThreads == tqq::kQThreads, "the append tiles assume the quantiser's workgroup size");
+  if ((int)blockIdx.x < st.key_columns) {
+    qfused_body(a, blockIdx.x, blockIdx.y);
+    return;
+  }
+  const int t = ((int)blockIdx.x - st.key_columns) * (int)gridDim.y + (int)blockIdx.y;
+  const int e = t / st.tiles;
+  if (e >= st.n) return;
+  extern __shared__ float smem[];
+  tqq::quantize_tile<kStepTV, kStepJC>(st.q[e], t - e * st.tiles, smem);
 }
 
 template <bool PROJECT>
@@ -2067,7 +2098,7 @@ DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int
 hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const void* q, tq_dtype qdt, int B, int Hq,
                               int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out,
                               float* scores_out, void* ws, const DecodePlan& plan, hipStream_t s,
-                              const PageTable* pages) {
+                              const PageTable* pages, const StepRows* step) {
   const Spec* wsp = find_wspec(k, v);
   const Spec* sp = wsp ? wsp : find_spec(k, v);
   if (!sp) return hipErrorInvalidValue;
@@ -2150,7 +2181,24 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
   a.partial = wsf + plan.qprep_floats;
   a.out = out;
   const dim3 qgrid((unsigned)keys, kD / kRowSlice);
-  if (folded) {
+  if (step && !folded) {  // (without S R the appends take launches of their own)
+    const hipError_t e = launch_append_step(k, v, *step, B, Hkv, s);
+    if (e != hipSuccess) return e;
+  }
+  if (step && folded) {
+    StepAppend st{};
+    st.n = tqq::step_args(k, v, *step, B, Hkv, st.q);
+    st.tiles = (B * Hkv + kStepTV - 1) / kStepTV;
+    st.key_columns = (int)keys;
+    int dmax = 32;
+    for (int i = 0; i < st.n; ++i) dmax = std::max(dmax, st.q[i].d);
+    const int extra = (st.n * st.tiles + (int)qgrid.y - 1) / (int)qgrid.y;
+    const size_t lds = tqq::lds_bytes(dmax, kStepTV, kStepJC);
+    const hipError_t e = hipFuncSetAttribute((const void*)qfused_step_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(qfused_step_kernel, dim3(qgrid.x + extra, qgrid.y), dim3(kQtThreads), lds, s, a, st);
+  } else if (folded) {
     hipLaunchKernelGGL(qfused_kernel, qgrid, dim3(kQtThreads), 0, s, a);
   } else {
     hipLaunchKernelGGL(qtransform_kernel<false>, qgrid, dim3(kQtThreads), 0, s, a);

@@ -37,7 +37,20 @@ hipError_t launch_append_pair(const tq_quantizer& qk, const tq_quantizer& qv, tq
                               int64_t cache_rows, void* kpacked, uint16_t* knorm, uint16_t* krnorm, void* vpacked,
                               uint16_t* vnorm, uint16_t* vrnorm, hipStream_t s);
 
-// Matrix-core quantiser for 128-channel vectors (quantize_mfma.hip): rows
+// The new rows of a decode step (tq_decode_step): row b Hkv + g of k_new /
+// v_new is the new token of sequence b, KV head g, and goes to cache row
+// (b Hkv + g) seq_stride + seq_lens[b] - 1 of every channel group.
+struct StepRows {
+  const void* k_new;        // [B][Hkv][D]
+  const void* v_new;        // [B][Hkv][Dv]
+  tq_dtype dt;
+  const int32_t* seq_lens;  // [B] lengths after the append
+};
+// The appends of a decode step as launches of their own (quantize.hip).
+hipError_t launch_append_step(const tq_kv_desc& k, const tq_kv_desc& v, const StepRows& st, int B, int Hkv,
+                              hipStream_t s);
+
+// Matrix-core quantiser for vectors of 32, 64, 96 or 128 channels (quantize_mfma.hip): rows
 // 16-byte aligned.
 bool quantize_mfma_supported(const tq_quantizer& q, tq_dtype dt, const void* x, int64_t stride);
 hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
@@ -82,7 +95,7 @@ DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int
 hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const void* q, tq_dtype qdt, int B, int Hq,
                               int Hkv, int T_max, const int32_t* seq_lens, float scale, float* out,
                               float* scores_out, void* ws, const DecodePlan& plan, hipStream_t s,
-                              const PageTable* pages = nullptr);
+                              const PageTable* pages = nullptr, const StepRows* step = nullptr);
 // Largest number of splits per sequence the combine handles.
 int mfma_decode_max_splits();
 

@@ -309,6 +309,30 @@ extern "C" int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const vo
                                        ws, p, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int tq_decode_step(const tq_kv_desc* k, const tq_kv_desc* v, const void* k_new, const void* v_new,
+                              tq_dtype kv_dtype, const void* q, tq_dtype q_dtype, int B, int Hq, int Hkv, int T_max,
+                              const int32_t* seq_lens, float scale, float* out, float* scores_out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  const int rc = tqk::check_decode_call(k, v, q, q_dtype, B, Hq, Hkv, T_max, seq_lens, scale, out, scores_out, &need);
+  if (rc != TQ_OK) return rc;
+  if (!k_new || !v_new || !seq_lens) return TQ_ERR_INVALID_ARG;
+  if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return TQ_ERR_MISALIGNED;
+  if (ws && !aligned16(ws)) return TQ_ERR_MISALIGNED;
+  if (!ws || ws_bytes < need) return TQ_ERR_WORKSPACE;
+  const tqk::DecodePlan p = decode_plan(*k, *v, B, Hq, Hkv, T_max);
+  const tqk::StepRows st{k_new, v_new, kv_dtype, seq_lens};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (tqk::mfma_decode_supported(*k, *v))
+    return hip_status(tqk::launch_decode_mfma(*k, *v, q, q_dtype, B, Hq, Hkv, T_max, seq_lens, scale, out,
+                                              scores_out, ws, p, s, nullptr, &st));
+  const hipError_t e = tqk::launch_append_step(*k, *v, st, B, Hkv, s);
+  if (e != hipSuccess) return TQ_ERR_HIP;
+  return hip_status(tqk::launch_decode(*k, *v, q, q_dtype, B, Hq, Hkv, T_max, seq_lens, scale, out, scores_out, ws,
+                                       p, s));
+}
+
 extern "C" size_t tq_decode_paged_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B, int Hq, int Hkv,
                                                   int T_max, int block_tokens) {
   int D = 0, Dv = 0;

@@ -242,6 +242,29 @@ int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_d
                    int B, int Hq, int Hkv, int T_max, const int32_t* seq_lens, float scale,
                    float* out, float* scores_out, void* ws, size_t ws_bytes, void* stream);
 
+/* One decode step (riverfrot sections 2.2-2.3: the generated token's key
+ * and value join the cache, compressed online as in sections 4.1-4.3, and
+ * the new query attends to every cached token, this one included): the new
+ * key and value rows of every (sequence, KV head) are quantised into the
+ * cache, then the attention of tq_decode_attn runs over lengths seq_lens.
+ * For head_dim-128 layouts whose PROD key groups carry S R (tq_fold_qjl) the
+ * appends run inside the decode's query-transform launch, so the step takes
+ * the launches of tq_decode_attn alone; otherwise they take launches of
+ * their own before it.
+ *   k_new    [B, Hkv, D] new key rows, v_new [B, Hkv, Dv] new value rows
+ *            (fp32 or bf16 as kv_dtype, contiguous, 16-byte aligned)
+ *   seq_lens [B] int32 device, required: lengths after the append. The new
+ *            row of (b, g) goes to row (b Hkv + g) seq_stride + seq_lens[b] - 1
+ *            of every group (the row tq_append_kv would write); a sequence
+ *            with seq_lens[b] = 0 appends nothing.
+ * The cache the descriptors point at is written (their const pointers are
+ * the decode's view of it). Other arguments, the workspace
+ * (tq_decode_workspace_bytes) and errors as for tq_decode_attn. */
+int tq_decode_step(const tq_kv_desc* k, const tq_kv_desc* v, const void* k_new, const void* v_new,
+                   tq_dtype kv_dtype, const void* q, tq_dtype q_dtype, int B, int Hq, int Hkv, int T_max,
+                   const int32_t* seq_lens, float scale, float* out, float* scores_out, void* ws,
+                   size_t ws_bytes, void* stream);
+
 /* Size of the scratch array tq_decode_attn_noalloc uses as its workspace. */
 #define TQ_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
 

@@ -243,6 +243,26 @@ def test_decode_validation_paths():
     assert tq.tq_decode_workspace_bytes(k, v, 1, 30, 8, 1024) == 0
 
 
+def test_decode_step_validation_paths():
+    L = tq.lib()
+    k, v = _kv()
+    ws = tq.tq_decode_workspace_bytes(k, v, 1, 32, 8, 1024)
+
+    def call(kn=FAKE, vn=FAKE, kvdt=tq.TQ_BF16, sl=FAKE, Hq=32, wsp=FAKE, wsb=ws, out=FAKE):
+        return L.tq_decode_step(ctypes.byref(k), ctypes.byref(v), kn, vn, kvdt, FAKE, tq.TQ_BF16, 1, Hq, 8, 1024, sl,
+                                0.088, out, None, wsp, wsb, None)
+
+    assert call(Hq=30) == tq.TQ_ERR_INVALID_ARG
+    assert call(kn=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(vn=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(sl=None) == tq.TQ_ERR_INVALID_ARG     # the lengths say where the new rows go
+    assert call(kvdt=7) == tq.TQ_ERR_INVALID_ARG
+    assert call(kn=FAKE + 8) == tq.TQ_ERR_MISALIGNED
+    assert call(out=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(wsb=ws - 1) == tq.TQ_ERR_WORKSPACE
+    assert call(wsp=None) == tq.TQ_ERR_WORKSPACE
+
+
 def test_noalloc_decode_validation_paths():
     # the allocation-free entry point validates like tq_decode_attn and refuses
     # requests beyond its fixed scratch array, all before any device call
