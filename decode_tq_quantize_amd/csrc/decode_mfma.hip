@@ -433,6 +433,7 @@ struct StepAppend {
 constexpr int kStepTV = 2, kStepJC = 32;
 static_assert(sizeof(Args) + sizeof(StepAppend) <= 4096, "kernel arguments of the step launch");
 
+template <bool DIRECT>
 __global__ __launch_bounds__(kQtThreads) void qfused_step_kernel(Args a, StepAppend st) {
   static_assert(kQtThreads == tqq::kQThreads, "the append tiles assume the quantiser's workgroup size");
   if ((int)blockIdx.x < st.key_columns) {
@@ -443,7 +444,7 @@ __global__ __launch_bounds__(kQtThreads) void qfused_step_kernel(Args a, StepApp
   const int e = t / st.tiles;
   if (e >= st.n) return;
   extern __shared__ float smem[];
-  tqq::quantize_tile<kStepTV, kStepJC>(st.q[e], t - e * st.tiles, smem);
+  tqq::quantize_tile<kStepTV, kStepJC, DIRECT>(st.q[e], t - e * st.tiles, smem);
 }
 
 template <bool PROJECT>
@@ -2194,10 +2195,18 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
     for (int i = 0; i < st.n; ++i) dmax = std::max(dmax, st.q[i].d);
     const int extra = (st.n * st.tiles + (int)qgrid.y - 1) / (int)qgrid.y;
     const size_t lds = tqq::lds_bytes(dmax, kStepTV, kStepJC);
-    const hipError_t e = hipFuncSetAttribute((const void*)qfused_step_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // direct products for a handful of new rows (latency first); staged ones
+    // otherwise, whose smaller register footprint keeps the transform's
+    // workgroups at full occupancy
+    const bool direct = B * Hkv <= 64;
+    const void* fn = direct ? (const void*)qfused_step_kernel<true> : (const void*)qfused_step_kernel<false>;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(qfused_step_kernel, dim3(qgrid.x + extra, qgrid.y), dim3(kQtThreads), lds, s, a, st);
+    const dim3 sgrid(qgrid.x + extra, qgrid.y);
+    if (direct)
+      hipLaunchKernelGGL(qfused_step_kernel<true>, sgrid, dim3(kQtThreads), lds, s, a, st);
+    else
+      hipLaunchKernelGGL(qfused_step_kernel<false>, sgrid, dim3(kQtThreads), lds, s, a, st);
   } else if (folded) {
     hipLaunchKernelGGL(qfused_kernel, qgrid, dim3(kQtThreads), 0, s, a);
   } else {

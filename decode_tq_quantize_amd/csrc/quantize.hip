@@ -20,32 +20,37 @@ struct QArgsPair {
   QArgs a[2];
 };
 
-template <int TV>
+template <int TV, bool DIRECT = false>
 __global__ __launch_bounds__(tqq::kQThreads) void quantize_kernel(QArgsPair pair) {
   extern __shared__ float smem[];
-  tqq::quantize_tile<TV, tqq::jc_of<TV>()>(pair.a[blockIdx.y], blockIdx.x, smem);
+  tqq::quantize_tile<TV, tqq::jc_of<TV>(), DIRECT>(pair.a[blockIdx.y], blockIdx.x, smem);
 }
 
 size_t lds_bytes(int d, int TV) { return tqq::lds_bytes(d, TV, TV <= 4 ? 128 : 32); }
 
 // count (1 or 2) argument sets, the first nround vectors of each
-template <int TV>
+template <int TV, bool DIRECT = false>
 hipError_t launch_tv(const QArgs* as, int count, int64_t nround, hipStream_t s) {
   QArgsPair pair{};
   pair.a[0] = as[0];
   pair.a[1] = as[count > 1 ? 1 : 0];
   const size_t lds = tqq::lds_bytes(std::max(pair.a[0].d, pair.a[1].d), TV, tqq::jc_of<TV>());
-  hipError_t e = hipFuncSetAttribute((const void*)quantize_kernel<TV>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = hipFuncSetAttribute((const void*)quantize_kernel<TV, DIRECT>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (nround + TV - 1) / TV;
-  hipLaunchKernelGGL(quantize_kernel<TV>, dim3((unsigned)blocks, (unsigned)count), dim3(tqq::kQThreads), lds, s, pair);
+  hipLaunchKernelGGL((quantize_kernel<TV, DIRECT>), dim3((unsigned)blocks, (unsigned)count), dim3(tqq::kQThreads), lds,
+                     s, pair);
   return hipGetLastError();
 }
 
 using tqq::make_args;
 
 constexpr size_t kLdsLimit = 150 * 1024;
+// Appends of at most this many vectors per tensor take the direct products
+// (measured: batch 1 x 8 KV heads faster, batch 64 x 8 slower, its larger
+// register footprint costing more than the latency it saves).
+constexpr int64_t kDirectMaxN = 64;
 
 // An append is a few vectors per sequence: small tiles, so that the vectors
 // spread over the compute units (about 256 workgroups or more per tensor).
@@ -56,6 +61,8 @@ hipError_t launch_rows(const QArgs* as, int count, int64_t n, hipStream_t s) {
   if (fits(16)) return launch_tv<16>(as, count, n, s);
   if (fits(8)) return launch_tv<8>(as, count, n, s);
   if (fits(4)) return launch_tv<4>(as, count, n, s);
+  // a handful of vectors (a decode step at small batch): latency first
+  if (n <= kDirectMaxN && d <= tqq::kDirectMaxD) return launch_tv<2, true>(as, count, n, s);
   return launch_tv<2>(as, count, n, s);
 }
 

@@ -137,6 +137,45 @@ __device__ void matvec_tile(const float* __restrict__ M, int d, const float* In,
   __syncthreads();
 }
 
+// Products of a matrix with tiles of at most 2 vectors of d <= 128
+// coordinates (appends), with no staging: thread t owns output coordinate
+// t / 2 and half t % 2 of its row, whose d / 2 entries it loads straight into
+// registers (all at once, one memory round trip), and the two halves' sums
+// meet by a lane exchange.
+constexpr int kDirectMaxD = 128;
+__device__ __forceinline__ void load_half_row(const float* __restrict__ M, int d, float4 (&m)[kDirectMaxD / 8]) {
+  const int i = min((int)threadIdx.x >> 1, d - 1), h = threadIdx.x & 1;
+  const float4* p = reinterpret_cast<const float4*>(M + (int64_t)i * d + h * (d / 2));
+#pragma unroll
+  for (int k = 0; k < kDirectMaxD / 8; ++k) m[k] = k < d / 8 ? p[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+template <int TV>
+__device__ void matvec_direct(const float4 (&m)[kDirectMaxD / 8], int d, const float* In, float* Out) {
+  static_assert(2 * kDirectMaxD == kQThreads, "two threads per output coordinate");
+  const int i = threadIdx.x >> 1, h = threadIdx.x & 1;
+  const float* in = In + h * (d / 2) * TV;
+  float acc[TV];
+#pragma unroll
+  for (int v = 0; v < TV; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int k = 0; k < kDirectMaxD / 8; ++k) {
+    if (k < d / 8) {
+      const float mv[4] = {m[k].x, m[k].y, m[k].z, m[k].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < TV; ++v) acc[v] = fmaf(mv[c], in[(4 * k + c) * TV + v], acc[v]);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < TV; ++v) acc[v] += __shfl_xor(acc[v], 1, tqd::kWave);
+  if (i < d && h == 0) {
+#pragma unroll
+    for (int v = 0; v < TV; ++v) Out[i * TV + v] = acc[v];
+  }
+  __syncthreads();
+}
+
 // Key-layout word of vector v, coordinate word g, code bit sh (4: the sign)
 // for the half-wave this lane is in: lane i of the half takes coordinate
 // 32 g + i, a ballot gathers the 32 bits, and the half's word is returned to
@@ -150,8 +189,11 @@ __device__ __forceinline__ uint32_t key_word(const uint8_t* C, int TV, int v, in
 
 // Quantise tile blk (vectors blk TV .. blk TV + TV - 1) of a.x with a
 // workgroup of kQThreads threads; smem holds lds_bytes(a.d, TV, JC) bytes.
-template <int TV, int JC>
+// DIRECT (tiles of at most 2 vectors): matrices of d <= 128 go straight to
+// registers (lower latency, about 128 more registers per thread).
+template <int TV, int JC, bool DIRECT = false>
 __device__ void quantize_tile(const QArgs& a, int64_t blk, float* smem) {
+  static_assert(!DIRECT || TV <= 2, "direct products take tiles of at most 2 vectors");
   __shared__ float nrm[TV], rho[TV];
   __shared__ float cent[TQ_MAX_LEVELS], thr[TQ_MAX_LEVELS];
   const int d = a.d;
@@ -162,6 +204,16 @@ __device__ void quantize_tile(const QArgs& a, int64_t blk, float* smem) {
   const int tid = threadIdx.x, lane = tid % tqd::kWave, wv = tid / tqd::kWave;
   const int64_t v0 = blk * TV;
   const int L = 1 << a.B;
+  // tiles of appends (2 vectors, d <= 128): R and S rows straight to
+  // registers, their loads issued before anything else
+  const bool direct = DIRECT && d <= kDirectMaxD;
+  float4 rm[kDirectMaxD / 8], sm[kDirectMaxD / 8];
+  if constexpr (DIRECT) {
+    if (direct) {
+      load_half_row(a.R, d, rm);
+      if (a.prod) load_half_row(a.S, d, sm);
+    }
+  }
 
   if (tid < TQ_MAX_LEVELS) {
     cent[tid] = a.cent[tid];
@@ -182,7 +234,14 @@ __device__ void quantize_tile(const QArgs& a, int64_t blk, float* smem) {
     if (lane == 0) nrm[v] = sqrtf(s);
   }
   // 3. rotation (unnormalised: R x, divided by |x| below)
-  matvec_tile<TV, JC>(a.R, d, In, Out, Mt);
+  if constexpr (DIRECT) {
+    if (direct)
+      matvec_direct<TV>(rm, d, In, Out);
+    else
+      matvec_tile<TV, JC>(a.R, d, In, Out, Mt);
+  } else {
+    matvec_tile<TV, JC>(a.R, d, In, Out, Mt);
+  }
   // 4. codes; the rotated residual replaces the input tile
   for (int e = tid; e < TV * d; e += kQThreads) {
     const int v = e % TV;
@@ -203,7 +262,14 @@ __device__ void quantize_tile(const QArgs& a, int64_t blk, float* smem) {
       if (lane == 0) rho[v] = sqrtf(s);
     }
     // 5. QJL projection of the residual; keep the signs (sign(0) -> +)
-    matvec_tile<TV, JC>(a.S, d, In, Out, Mt);
+    if constexpr (DIRECT) {
+      if (direct)
+        matvec_direct<TV>(sm, d, In, Out);
+      else
+        matvec_tile<TV, JC>(a.S, d, In, Out, Mt);
+    } else {
+      matvec_tile<TV, JC>(a.S, d, In, Out, Mt);
+    }
     for (int e = tid; e < TV * d; e += kQThreads) {
       const int v = e % TV;
       const bool z = (Out[e] >= 0.f) || !(nrm[v] > 0.f);

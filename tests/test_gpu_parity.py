@@ -122,8 +122,11 @@ def test_quantize_matches_oracle(d, B, prod, lay, N, dt):
 
 APPEND_CASES = [
     # d, B, prod, layout, dtype, cache rows, appended rows (the count picks the
-    # kernel's tile: 2 vectors per workgroup below 1024, 4 below 2048, 8
-    # below 4096, 16 below 8192, 32 from 8192)
+    # kernel's tile: 2 vectors per workgroup below 1024 (matrices straight to
+    # registers up to 64 vectors of d <= 128, staged through LDS above), 4
+    # below 2048, 8 below 4096, 16 below 8192, 32 from 8192)
+    (128, 3, True, "keys", "bf16", 2000, 500),
+    (128, 3, False, "values", "bf16", 2000, 65),
     (128, 3, True, "keys", "bf16", 203, 61),
     (128, 3, False, "values", "bf16", 203, 61),
     (128, 2, True, "values", "f32", 203, 61),
