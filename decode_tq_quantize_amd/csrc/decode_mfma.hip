@@ -1347,6 +1347,78 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
   }
 }
 
+// Few splits (large batches): the same merge and rotation with kHeadsPerComb
+// query heads per workgroup, so that R_v is read once per workgroup (into
+// LDS) instead of once per head and channel slice. Thread t of head
+// t / 32 merges channels 4 (t % 32) .. + 3 over the splits, then forms the
+// same 4 output channels from the merged accumulator and R_v's columns.
+constexpr int kHeadsPerComb = kCombThreads / 32;
+constexpr int kFewSplits = 8;
+
+__global__ __launch_bounds__(kCombThreads) void combine_heads_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) float rv[kD * kD];  // the value groups' R_v, one after the other
+  __shared__ __attribute__((aligned(16))) float accs[kHeadsPerComb][kD];
+  __shared__ float tots[kHeadsPerComb];
+  const int tid = threadIdx.x, hh = tid >> 5, c = tid & 31;
+  const int S = a.splits;
+  const int64_t bh = (int64_t)blockIdx.x * kHeadsPerComb + hh;
+  const bool live = bh < (int64_t)a.B * a.Hq;
+  // R_v of every value group into LDS
+  int off[kMaxVG];
+  {
+    int o = 0;
+#pragma unroll
+    for (int g = 0; g < kMaxVG; ++g) {
+      off[g] = o;
+      if (g < a.nv) {
+        const int dg = a.v[g].d;
+        const float4* src = reinterpret_cast<const float4*>(a.v[g].R);
+        for (int e = tid; e < dg * dg / 4; e += kCombThreads) *reinterpret_cast<float4*>(&rv[o + 4 * e]) = src[e];
+        o += dg * dg;
+      }
+    }
+  }
+  // merge this head's splits (channels 4 c .. 4 c + 3)
+  const float* part = a.partial + (live ? bh : 0) * S * (kD + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, part[(int64_t)s * (kD + 2)]);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  float tot = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* row = part + (int64_t)s * (kD + 2);
+    const float m = row[0];
+    const float wgt = (M == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - M);
+    tot = fmaf(wgt, row[1], tot);
+    const float2 lo = *reinterpret_cast<const float2*>(row + 2 + 4 * c);
+    const float2 hi = *reinterpret_cast<const float2*>(row + 4 + 4 * c);
+    v.x = fmaf(wgt, lo.x, v.x);
+    v.y = fmaf(wgt, lo.y, v.y);
+    v.z = fmaf(wgt, hi.x, v.z);
+    v.w = fmaf(wgt, hi.y, v.w);
+  }
+  *reinterpret_cast<float4*>(&accs[hh][4 * c]) = v;
+  if (c == 0) tots[hh] = tot;
+  __syncthreads();
+  // out[i] = sum_j R_v[j][i - ch] acc[ch + j] over i's value group
+  const int i0 = 4 * c;
+  const int g = (a.nv > 1 && i0 >= a.v[1].ch) ? 1 : 0;
+  const int dg = g ? a.v[1].d : a.v[0].d, ch = g ? a.v[1].ch : 0, og = g ? off[1] : off[0];
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < dg; ++j) {
+    const float4 r = *reinterpret_cast<const float4*>(&rv[og + j * dg + (i0 - ch)]);
+    const float x = accs[hh][ch + j];
+    o.x = fmaf(r.x, x, o.x);
+    o.y = fmaf(r.y, x, o.y);
+    o.z = fmaf(r.z, x, o.z);
+    o.w = fmaf(r.w, x, o.w);
+  }
+  const float t = tots[hh];
+  if (live) {
+    const float inv = t > 0.f ? 1.f / t : 0.f;
+    *reinterpret_cast<float4*>(a.out + bh * kD + i0) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  }
+}
+
 // ------------------------------------------------------------------ two-wave decode
 // A workgroup of two waves walks 128-token chunks of its split. Per chunk:
 //  * wave w scores 4 of the chunk's 8 key tiles (16 tokens each) on the
@@ -2215,7 +2287,11 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
   }
   const dim3 grid(plan.splits, a.HT, B * Hkv);
   hipLaunchKernelGGL(sp->fn, grid, dim3(wsp ? kPThreads : kThreads), 0, s, a);
-  hipLaunchKernelGGL(combine_kernel, dim3(B * Hq, kJSlices), dim3(kCombThreads), 0, s, a);
+  if (plan.splits <= kFewSplits)
+    hipLaunchKernelGGL(combine_heads_kernel, dim3((B * Hq + kHeadsPerComb - 1) / kHeadsPerComb), dim3(kCombThreads),
+                       0, s, a);
+  else
+    hipLaunchKernelGGL(combine_kernel, dim3(B * Hq, kJSlices), dim3(kCombThreads), 0, s, a);
   return hipGetLastError();
 }
 
