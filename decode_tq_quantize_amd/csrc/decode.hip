@@ -213,19 +213,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
       const GroupArgs& g = a.v[gi];
       const int jl = j - g.ch;
       const int P = g.B;
-      const int64_t tile0 = ((int64_t)bg * g.seq_stride + c0) / tqk::kValuesTile;
-      for (int half = 0; half < 2 && half * 32 < ntok; ++half) {
+      // the chunk is one 64-vector block of the value layout (chunks start
+      // at multiples of 64): two tiles whose words interleave its tokens
+      const int64_t tile0 = ((int64_t)bg * g.seq_stride + c0) / tqk::kValuesBlock * 2;
+      for (int half = 0; half < 2; ++half) {
         const uint32_t* wp = g.packed + ((tile0 + half) * g.d + jl) * P;
         uint32_t w[TQ_MAX_MSE_BITS];
 #pragma unroll
         for (int p = 0; p < TQ_MAX_MSE_BITS; ++p) w[p] = p < P ? wp[p] : 0u;
-        const int iend = min(32, ntok - half * 32);
-        for (int i = 0; i < iend; ++i) {
-          const int tl = half * 32 + i;
+        for (int i = 0; i < 32; ++i) {
+          const int tl = tqk::value_tok(half, i);
+          if (tl >= ntok) continue;
           int idx = 0;
 #pragma unroll
           for (int p = 0; p < TQ_MAX_MSE_BITS; ++p)
-            if (p < P) idx |= (int)((w[p] >> tqk::value_bit(i)) & 1u) << p;
+            if (p < P) idx |= (int)((w[p] >> i) & 1u) << p;
           const float val = vcent[gi][idx] * nvbuf[wv][gi][tl];
 #pragma unroll
           for (int h = 0; h < kMaxHC; ++h)

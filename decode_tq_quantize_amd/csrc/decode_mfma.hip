@@ -997,10 +997,10 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
         cm[gi] += c4;
     }
   }
-  // fp4 register of this lane's tokens in the value step: token 16 i + tl of
-  // a 32-token word sits at bit 4 (u mod 8) + u / 8, u = 16 (i mod 2) + tl,
-  // i.e. in register u / 8 = 2 (i mod 2) + tl / 8
-  const float tinv_e = inv_v(tl >> 3), tinv_o = inv_v(2 + (tl >> 3));
+  // fp4 register of this lane's tokens in the value step: token t of a
+  // 64-token block sits in register (t mod 8) / 2 of its tile's expansion,
+  // and this lane's tokens 64 w + 16 i + tl all have t mod 8 = tl mod 8
+  const float tinv = inv_v((tl & 7) >> 1);
 
   v4f vacc[2][VT], vcon;
 #pragma unroll
@@ -1139,15 +1139,16 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
     // weights -> fp8 digits in LDS (pre-multiplied by 1 / v_r of their fp4 register)
 #pragma unroll
     for (int gv = 0; gv < NV; ++gv) {
-      const float sv_e = ldexpf(tinv_e, 5 - e_new[gv]), sv_o = ldexpf(tinv_o, 5 - e_new[gv]);
+      const float sv = ldexpf(tinv, 5 - e_new[gv]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float sv = (i & 1) ? sv_o : sv_e;
         const int tau = 64 * w + 16 * i + tl;
         const int ks = tau >> 7, tp = tau & 127;
-        // operand position of the token: value words hold vector u at bit
-        // 4 (u mod 8) + u / 8, which the fp4 expansion puts at K position u
-        const int kappa = tp;
+        // operand position of the token: the fp4 expansion of the words of
+        // value tile s puts token t = 16 q + 8 s + 2 r + e of its block
+        // (e = 0, 1) at K position 32 s + 8 r + q + 4 e of the block's 64,
+        // i.e. token 16 i + tl at 4 tl + i
+        const int kappa = 64 * (tp >> 6) + 4 * (tp & 15) + ((tp >> 4) & 3);
         float r = p[i] * hbits_at(kc.nv[gv][i >> 1], i & 1) * sv;
         uint8_t* dst = &wbuf[buf][gv][ks][4 * hl][kappa];
 #pragma unroll
@@ -1422,18 +1423,18 @@ __global__ __launch_bounds__(kCombThreads) void combine_heads_kernel(Args a) {
 // ------------------------------------------------------------------ two-wave decode
 // A workgroup of two waves walks 128-token chunks of its split. Per chunk:
 //  * wave w scores 4 of the chunk's 8 key tiles (16 tokens each) on the
-//    fp8 x fp4 matrix cores as above: tiles 2w, 2w + 1, 2w + 4, 2w + 5, the
-//    tokens of the value operand's K blocks w and w + 2 (32 tokens each, the
-//    unit of its per-lane scale); lane (h, c) = (lane / 16, lane % 16) ends
-//    with token c's score for head h;
+//    fp8 x fp4 matrix cores as above: tiles 4 w .. 4 w + 3, the 64-token
+//    block w of the chunk, whose tokens fill the value operand's K blocks
+//    2 w and 2 w + 1 (32 positions each, the unit of its per-lane scale);
+//    lane (h, c) = (lane / 16, lane % 16) ends with the scores of tokens
+//    64 w + 16 j + c (j = 0..3) for head h;
 //  * each wave turns its softmax weights times the value norm into three
 //    fp8 digits per token (each the rounding of 16 times what the previous
-//    ones left) and a 4 x 4 byte transpose inside each lane quad (two DPP
-//    moves, two byte permutes) into one digit row's 4 consecutive operand
-//    bytes, stored with one 32-bit LDS write: the value words hold token u
-//    of a 32-token word at bit 4 (u mod 8) + u / 8, so the fp4 expansion
-//    puts token t of the chunk at operand position t and a quad's 4 tokens
-//    are 4 consecutive bytes;
+//    ones left), four tokens per conversion pair: the value layout puts
+//    token 16 j + c of a 64-token block at K position 4 c + j of the
+//    block's 64 (the two tiles of a block interleave its tokens), so a
+//    lane's four tokens are one digit row's 4 consecutive operand bytes,
+//    stored with one 32-bit LDS write per digit;
 //  * one barrier; each wave reads the whole weight operand (two 16-byte LDS
 //    reads per value group) and accumulates the value sums of its 64 value
 //    coordinates (4 tiles of 16) over the chunk's 128 tokens.
@@ -1450,36 +1451,27 @@ constexpr int kWRow = 144;    // bytes per digit row of the weight operand in LD
 constexpr int kWScale = 6;    // weight (<= 1) x value norm x 2^(kWScale - its exponent) x fp4 pre-scale (<= 4) < 256
 constexpr int kMaxShift = 60;  // largest reference difference carried by the operand scale
 
-// 4 x 4 byte transpose inside each lane quad: lane b of a quad returns byte b
-// of each quad lane's x (the byte from quad lane b' at position b').
-__device__ __forceinline__ uint32_t quad_transpose(uint32_t x, uint32_t sel1, uint32_t sel2) {
-  const uint32_t p = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xf, 0xf, false);  // quad lane b ^ 1
-  const uint32_t z = __builtin_amdgcn_perm(p, x, sel1);
-  const uint32_t q = (uint32_t)__builtin_amdgcn_mov_dpp((int)z, 0x4E, 0xf, 0xf, false);  // quad lane b ^ 2
-  return __builtin_amdgcn_perm(q, z, sel2);
-}
-
-// Three fp8 digits of two non-negative values a, b: dwords [a0, a1, a2, 0]
-// and [b0, b1, b2, 0], digit m the e4m3 rounding (to nearest) of 16^m times
-// what the digits before it left.
-__device__ __forceinline__ void digits3(float a, float b, uint32_t& xa, uint32_t& xb) {
+// Three fp8 digits of two non-negative values a, b into half HI of the
+// dwords x[0..2]: digit m of a and b in bytes 2 HI and 2 HI + 1 of x[m],
+// digit m the e4m3 rounding (to nearest) of 16^m times what the digits
+// before it left (taken from the digits as stored). The low half clears
+// the dwords' high half.
+template <bool HI>
+__device__ __forceinline__ void digits3(float a, float b, uint32_t (&x)[3]) {
   typedef float f2 __attribute__((ext_vector_type(2)));
-  int r01 = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);  // digit 0 in the low half
-  f2 f = __builtin_amdgcn_cvt_pk_f32_fp8(r01, false);
-  a = (a - f[0]) * kDigitStep;
-  b = (b - f[1]) * kDigitStep;
-  r01 = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, r01, true);  // digit 1 in the high half
-  f = __builtin_amdgcn_cvt_pk_f32_fp8(r01, true);
-  a = (a - f[0]) * kDigitStep;
-  b = (b - f[1]) * kDigitStep;
-  const uint32_t r2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);  // (high half stays 0)
-  // bytes (r01: 0 a0, 1 b0, 2 a1, 3 b1; r2: 4 a2, 5 b2; 0x0c: zero)
-  xa = __builtin_amdgcn_perm(r2, (uint32_t)r01, 0x0c040200u);
-  xb = __builtin_amdgcn_perm(r2, (uint32_t)r01, 0x0c050301u);
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    x[m] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, HI ? (int)x[m] : 0, HI);
+    if (m < 2) {
+      const f2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[m], HI);
+      a = (a - f[0]) * kDigitStep;
+      b = (b - f[1]) * kDigitStep;
+    }
+  }
 }
 
-// Chunk tile j (0..3) of wave w: 2 w + (j % 2) + 4 (j / 2).
-__device__ __forceinline__ int ptile(int w, int j) { return 2 * w + (j & 1) + 4 * (j >> 1); }
+// Chunk tile j (0..3) of wave w: 4 w + j.
+__device__ __forceinline__ int ptile(int w, int j) { return 4 * w + j; }
 
 template <int NK>
 struct PKeys {
@@ -1682,19 +1674,22 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         cinit_m[gi] -= 0.25f * c;
     }
   }
-  // byte-permute selectors of the quad transpose; fp4 register of this
-  // lane's token in the value words (token 16 T + tl of the chunk lies in
-  // register ((16 T + tl) / 8) % 4 = 2 (T % 2) + tl / 8)
-  const uint32_t sel1 = (tl & 1) ? 0x03070105u : 0x06020400u;
-  const uint32_t sel2 = (tl & 2) ? 0x03020706u : 0x05040100u;
-  const float tinv[2] = {inv_v(tl >> 3), inv_v(2 + (tl >> 3))};
+  // fp4 register of this lane's tokens in the value step: token t of a
+  // 64-token block lies in register (t mod 8) / 2 of its tile's expansion,
+  // and the lane's tokens 16 j + tl all have t mod 8 = tl mod 8
+  const float tinv = inv_v((tl & 7) >> 1);
   const int dg_row = lane & 3;             // digit of this lane's row of the weight operand (row lane % 16)
   const int h_row = (lane & 15) >> 2;      // head of that row
   // The E8M0 scale a lane gives the A operand covers the 32 consecutive K
-  // positions of block lane / 16 (measured on gfx950), here tokens
-  // 32 (lane / 16) .. + 31 of the chunk, i.e. tiles 2 (lane / 16) and
-  // 2 (lane / 16) + 1: written by wave (lane / 16) % 2
-  const int src_w = (lane >> 4) & 1;
+  // positions of block lane / 16 (measured on gfx950), here K blocks of the
+  // chunk's 64-token block lane / 32: written by wave lane / 32
+  const int src_w = (lane >> 5) & 1;
+  // digit row 3 of every head stays zero (three digits per weight)
+  // (thread tid: head tid / 32, dword tid % 32 of the row, in each buffer)
+  static_assert(kPThreads == kHT * kPChunk / 4, "one dword of a zero row per thread");
+#pragma unroll
+  for (int k = 0; k < 2 * NV; ++k)
+    *reinterpret_cast<uint32_t*>(&wbuf[k / NV][k % NV][(4 * (tid >> 5) + 3) * kWRow + 4 * (tid & 31)]) = 0u;
 
   // ---- the wave's loop, instantiated per wave (its value tiles' groups and
   // widths are compile-time)
@@ -1836,42 +1831,25 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         e_w[gv] = max(e_w[gv], exponent_of(hbits(vm)));
       }
       const bool live = m_w != -INFINITY;
-      // value-norm scale times the fp4 pre-scale, per group and tile parity
-      float st[NV][2];
+      // ---------------- weights -> fp8 digits -> the operand rows in LDS
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = live ? __builtin_amdgcn_exp2f(lg[j] - m_w) : 0.f;
+        l_w += p[j];
+      }
 #pragma unroll
       for (int gv = 0; gv < NV; ++gv) {
-        const float s = ldexpf(1.f, kWScale - e_w[gv]);
-        st[gv][0] = s * tinv[0];
-        st[gv][1] = s * tinv[1];
-      }
-      // ---------------- weights -> fp8 digits -> the operand rows in LDS
+        // value-norm scale times the fp4 pre-scale; tokens in pairs, the
+        // second pair's digits into the dwords' high halves
+        const float st = ldexpf(tinv, kWScale - e_w[gv]);
+        uint32_t x[3];
+        digits3<false>((p[0] * st) * hbits(vd.nv[gv][0]), (p[1] * st) * hbits_hi(vd.nv[gv][0]), x);
+        digits3<true>((p[2] * st) * hbits(vd.nv[gv][1]), (p[3] * st) * hbits_hi(vd.nv[gv][1]), x);
+        // rows (head hl, digit m), operand bytes 64 WW + 4 tl .. + 3
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        float p[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          p[u] = live ? __builtin_amdgcn_exp2f(lg[2 * jj + u] - m_w) : 0.f;
-          l_w += p[u];
-        }
-        uint32_t x[NV][2];
-        if constexpr (NV == 1) {
-          digits3((p[0] * st[0][0]) * hbits(vd.nv[0][jj]), (p[1] * st[0][1]) * hbits_hi(vd.nv[0][jj]), x[0][0],
-                  x[0][1]);
-        } else {
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            digits3((p[u] * st[0][u]) * hbits_at(vd.nv[0][jj], u), (p[u] * st[1][u]) * hbits_at(vd.nv[1][jj], u),
-                    x[0][u], x[1][u]);
-        }
-#pragma unroll
-        for (int gv = 0; gv < NV; ++gv)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const uint32_t y = quad_transpose(x[gv][u], sel1, sel2);
-            // row (head, digit tl % 4), operand bytes 16 T + 4 (tl / 4) .. + 3
-            *reinterpret_cast<uint32_t*>(
-                &wbuf[par][gv][(4 * hl + (tl & 3)) * kWRow + 16 * ptile(WW, 2 * jj + u) + 4 * (tl >> 2)]) = y;
-          }
+        for (int m = 0; m < 3; ++m)
+          *reinterpret_cast<uint32_t*>(&wbuf[par][gv][(4 * hl + m) * kWRow + 64 * WW + 4 * tl]) = x[m];
       }
       if (tl == 0) xm[par][WW][hl] = m_w;
       if (lane == 0) {

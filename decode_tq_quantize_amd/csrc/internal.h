@@ -11,12 +11,19 @@ namespace tqk {
 // Tile sizes of the packed layouts (see tq.h).
 constexpr int kKeysTile = 16;
 constexpr int kValuesTile = 32;
+constexpr int kValuesBlock = 64;  // two value tiles whose vectors interleave
 
-// Bit of the value-layout word that holds vector u (0..31) of its tile:
-// 4 (u mod 8) + u / 8, so that each fp4 register the decode's matrix cores
-// expand from a word (bits 4 i + r, i = 0..7, for register r) holds 8
-// consecutive vectors.
-__host__ __device__ constexpr int value_bit(int u) { return 4 * (u & 7) + (u >> 3); }
+// Value layout: vector t (0..63) of a 64-vector block sits in tile
+// value_tile(t) of the block, at bit value_bit(t) of that tile's words;
+// value_tok inverts the pair. Each fp4 register the decode's matrix cores
+// expand from a word (bits 4 i + r, i = 0..7, for register r) then holds the
+// vectors 16 (i mod 4) + 8 s + 2 r + i / 4 of tile s: for r = 0..3 and one
+// i, two pairs of adjacent vectors per tile, so the decode's attention
+// weights for four consecutive vectors land in the bytes one conversion
+// writes.
+__host__ __device__ constexpr int value_tile(int t) { return (t >> 3) & 1; }
+__host__ __device__ constexpr int value_bit(int t) { return 16 * (t & 1) + 4 * (t >> 4) + ((t & 7) >> 1); }
+__host__ __device__ constexpr int value_tok(int s, int b) { return 16 * ((b >> 2) & 3) + 8 * s + 2 * (b & 3) + (b >> 4); }
 
 inline int planes_of(const tq_quantizer& q) { return q.mse_bits + (q.variant == TQ_PROD ? 1 : 0); }
 

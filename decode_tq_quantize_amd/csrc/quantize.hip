@@ -75,7 +75,7 @@ hipError_t launch_quantize(const tq_quantizer& q, tq_layout layout, tq_dtype dt,
                            const int64_t* rows, int64_t cache_rows) {
   const QArgs a = make_args(q, layout, dt, x, n, stride, packed, norm, rnorm, rows, cache_rows);
   if (rows) return launch_rows(&a, 1, n, s);  // (rows are written one by one: no output tile to round to)
-  const int tile = layout == TQ_LAYOUT_KEYS ? kKeysTile : kValuesTile;
+  const int tile = layout == TQ_LAYOUT_KEYS ? kKeysTile : kValuesBlock;
   const int64_t nround = (n + tile - 1) / tile * tile;
   if (layout == TQ_LAYOUT_VALUES || lds_bytes(q.d, 32) <= kLdsLimit) return launch_tv<32>(&a, 1, nround, s);
   if (lds_bytes(q.d, 16) <= kLdsLimit) return launch_tv<16>(&a, 1, nround, s);

@@ -283,17 +283,19 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
   }
   __syncthreads();
 
-  // The vector of a tile that MFMA column nl of half nt carries: for keys
-  // vector 16 nt + nl; for values the vector whose bit in the value words is
-  // 16 nt + nl (bit 4 (u mod 8) + u / 8 holds vector u), so that the halves'
-  // ballots are the words' halves as they stand
-  auto col_vec = [&](int nt, int c) __attribute__((always_inline)) -> int {
-    return KEYS ? 16 * nt + c : 8 * (c & 3) + 4 * nt + (c >> 2);
+  // The vector that MFMA column c of half nt of tile t carries: for keys
+  // vector 32 t + 16 nt + c; for values the vector whose bit in the words of
+  // value tile t is 16 nt + c (the two tiles of a 64-vector block interleave
+  // its vectors), so that the halves' ballots are the words' halves as they
+  // stand
+  auto col_vec = [&](int64_t t, int nt, int c) __attribute__((always_inline)) -> int64_t {
+    return KEYS ? t * kTile + 16 * nt + c
+                : (t >> 1) * tqk::kValuesBlock + tqk::value_tok((int)(t & 1), 16 * nt + c);
   };
   // a tile's inputs (rows past n re-read row n - 1 and are masked)
   auto load_tile = [&](XIn<D, BF16IN>(&dst)[2], int64_t t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) load_in<D>(dst[nt], a, min(t * kTile + col_vec(nt, nl), a.n - 1), q);
+    for (int nt = 0; nt < 2; ++nt) load_in<D>(dst[nt], a, min(col_vec(t, nt, nl), a.n - 1), q);
   };
   const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
   // one tile, whose inputs are in cur; once the rotation has read them, cur
@@ -369,10 +371,10 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
     float inv[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      valid[nt] = v0 + col_vec(nt, nl) < a.n;
+      valid[nt] = col_vec(tile, nt, nl) < a.n;
       live[nt] = valid[nt] & (nrm[nt] > 0.f);
       inv[nt] = live[nt] ? __builtin_amdgcn_rcpf(nrm[nt]) : 0.f;
-      if (w == 0 && q == 0 && valid[nt]) a.norm[v0 + col_vec(nt, nl)] = tqd::f32_to_half_bits(nrm[nt]);
+      if (w == 0 && q == 0 && valid[nt]) a.norm[col_vec(tile, nt, nl)] = tqd::f32_to_half_bits(nrm[nt]);
     }
     float res[2][2][4];
     float r2[2] = {0.f, 0.f};
@@ -549,7 +551,7 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
       // residual norms (one lane per vector)
       if (w == 0 && q < 2) {
         const int vt = 16 * q + nl;  // column nl of half q
-        if (v0 + col_vec(q, nl) < a.n) {
+        if (col_vec(tile, q, nl) < a.n) {
           float s;
           if constexpr (NG == 4)
             s = (rho_part[0][vt] + rho_part[1][vt]) + (rho_part[2][vt] + rho_part[3][vt]);
@@ -559,7 +561,7 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
             for (int i = 1; i < NG; ++i) s += rho_part[i][vt];
           }
           const float rho = __builtin_amdgcn_sqrtf(s);
-          a.rnorm[v0 + col_vec(q, nl)] = tqd::f32_to_half_bits(rho);
+          a.rnorm[col_vec(tile, q, nl)] = tqd::f32_to_half_bits(rho);
         }
       }
     }
@@ -626,7 +628,8 @@ hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtyp
   a.B = q.mse_bits;
   a.prod = q.variant == TQ_PROD;
   a.layout = layout;
-  a.ntiles = (n + kTile - 1) / kTile;
+  // (value tiles: both tiles of the last 64-vector block, whose vectors interleave)
+  a.ntiles = layout == TQ_LAYOUT_KEYS ? (n + kTile - 1) / kTile : (n + kValuesBlock - 1) / kValuesBlock * 2;
   for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = q.centroids[i];
   for (int i = 0; i < TQ_MAX_LEVELS - 1; ++i) a.thr[i] = q.thresholds[i];
   a.packed = static_cast<uint32_t*>(packed);

@@ -69,6 +69,17 @@ __device__ __forceinline__ int64_t dest_row(const QArgs& a, int64_t gv) {
 }
 
 
+// Vector (row of x) that slot v of tile blk quantises. A bulk value-layout
+// tile (32 slots) takes the vectors its memory tile holds, slot v = bit v of
+// the tile's words (the vectors of a 64-vector block interleave over its two
+// tiles); every other tile takes vectors blk TV .. blk TV + TV - 1.
+template <int TV>
+__device__ __forceinline__ int64_t tile_vec(const QArgs& a, int64_t blk, int v) {
+  if (TV == tqk::kValuesTile && a.layout == TQ_LAYOUT_VALUES && !a.rows && !a.step_lens)
+    return (blk >> 1) * tqk::kValuesBlock + tqk::value_tok((int)(blk & 1), v);
+  return blk * TV + v;
+}
+
 // Out[j][v] = sum_k M[j][k] In[k][v] for the TV vectors of the tile (arrays
 // coordinate-major, row stride TV). Thread (ii, vh) owns output coordinate
 // i0 + ii of vectors vh*TV/2 .. vh*TV/2 + TV/2 - 1.
@@ -187,7 +198,7 @@ __device__ __forceinline__ uint32_t key_word(const uint8_t* C, int TV, int v, in
   return (uint32_t)(m >> (32 * (lane >> 5)));
 }
 
-// Quantise tile blk (vectors blk TV .. blk TV + TV - 1) of a.x with a
+// Quantise tile blk (the vectors tile_vec<TV> names) of a.x with a
 // workgroup of kQThreads threads; smem holds lds_bytes(a.d, TV, JC) bytes.
 // DIRECT (tiles of at most 2 vectors): matrices of d <= 128 go straight to
 // registers (lower latency, about 128 more registers per thread).
@@ -222,7 +233,7 @@ __device__ void quantize_tile(const QArgs& a, int64_t blk, float* smem) {
   // 1. load the tile, coordinate-major (vectors past n are zero)
   for (int e = tid; e < TV * d; e += kQThreads) {
     const int v = e / d, j = e % d;
-    const int64_t gv = v0 + v;
+    const int64_t gv = tile_vec<TV>(a, blk, v);
     In[j * TV + v] = gv < a.n ? tqd::load_elem(a.x, gv * a.stride + j, a.bf16) : 0.f;
   }
   __syncthreads();
@@ -306,8 +317,10 @@ __device__ void quantize_tile(const QArgs& a, int64_t blk, float* smem) {
         const int64_t row = dest_row(a, gv);
         if (row < 0 || row >= a.cache_rows) continue;
         const int sh = p < a.B ? p : 4;
-        const uint32_t bit = 1u << (uint32_t)tqk::value_bit((int)(row % tqk::kValuesTile));
-        uint32_t* wp = a.packed + ((row / tqk::kValuesTile) * d + j) * P + p;
+        const int t = (int)(row % tqk::kValuesBlock);
+        const uint32_t bit = 1u << (uint32_t)tqk::value_bit(t);
+        const int64_t tile = row / tqk::kValuesBlock * 2 + tqk::value_tile(t);
+        uint32_t* wp = a.packed + (tile * d + j) * P + p;
         if ((C[j * TV + v] >> sh) & 1)
           atomicOr(wp, bit);
         else
@@ -341,20 +354,19 @@ __device__ void quantize_tile(const QArgs& a, int64_t blk, float* smem) {
       a.packed[((tile * G + g) * tqk::kKeysTile + t) * P + p] = w;
     }
   } else {
-    // TV == 32 == the values tile; v0 is tile aligned
-    const int64_t tile = v0 / tqk::kValuesTile;
+    // TV == 32 == the values tile; slot v is bit v of the tile's words
     for (int e = tid; e < d * P; e += kQThreads) {
       const int p = e % P, j = e / P;
       const int sh = p < a.B ? p : 4;
       uint32_t w = 0;
       for (int v = 0; v < TV; ++v)
-        if (v0 + v < a.n) w |= (uint32_t)((C[j * TV + v] >> sh) & 1) << tqk::value_bit(v);
-      a.packed[(tile * d + j) * P + p] = w;
+        if (tile_vec<TV>(a, blk, v) < a.n) w |= (uint32_t)((C[j * TV + v] >> sh) & 1) << v;
+      a.packed[(blk * d + j) * P + p] = w;
     }
   }
   // 7. norms as IEEE half
   for (int v = tid; v < TV; v += kQThreads) {
-    const int64_t gv = v0 + v;
+    const int64_t gv = tile_vec<TV>(a, blk, v);
     if (gv < a.n) {
       a.norm[gv] = tqd::f32_to_half_bits(nrm[v]);
       if (a.prod) a.rnorm[gv] = tqd::f32_to_half_bits(rho[v]);

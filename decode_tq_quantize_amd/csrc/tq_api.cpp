@@ -94,7 +94,7 @@ int check_desc(const tq_kv_desc* k, bool values, int* total_d) {
     if (values && g.q.variant != TQ_MSE) return TQ_ERR_UNSUPPORTED;
     if (!g.packed || !g.norm || (g.q.variant == TQ_PROD && !g.rnorm)) return TQ_ERR_INVALID_ARG;
     if (!aligned16(g.packed) || !aligned16(g.norm) || (g.rnorm && !aligned16(g.rnorm))) return TQ_ERR_MISALIGNED;
-    if (g.seq_stride <= 0 || (g.seq_stride % tqk::kValuesTile) != 0) return TQ_ERR_INVALID_ARG;
+    if (g.seq_stride <= 0 || (g.seq_stride % tqk::kValuesBlock) != 0) return TQ_ERR_INVALID_ARG;
     ch += g.q.d;
   }
   *total_d = ch;
@@ -180,7 +180,7 @@ extern "C" size_t tq_packed_bytes(int d, int mse_bits, tq_variant variant, tq_la
   if (variant != TQ_MSE && variant != TQ_PROD) return 0;
   if (layout != TQ_LAYOUT_KEYS && layout != TQ_LAYOUT_VALUES) return 0;
   const int P = mse_bits + (variant == TQ_PROD ? 1 : 0);
-  const int64_t tile = layout == TQ_LAYOUT_KEYS ? tqk::kKeysTile : tqk::kValuesTile;
+  const int64_t tile = layout == TQ_LAYOUT_KEYS ? tqk::kKeysTile : tqk::kValuesBlock;
   const int64_t nr = (n + tile - 1) / tile * tile;
   return (size_t)nr * (size_t)P * (size_t)d / 8;
 }

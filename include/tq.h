@@ -36,12 +36,15 @@
  *    tiles of 16 vectors; uint32 word index ((tile * d/32 + g) * 16 + t) * P + p
  *    holds coordinates 32 g .. 32 g + 31 (bit i = coordinate 32 g + i) of
  *    vector 16 tile + t.
- *  - TQ_LAYOUT_VALUES (token-contiguous; values): tiles of 32 vectors;
- *    word index (tile * d + j) * P + p holds coordinate j of vectors
- *    32 tile .. 32 tile + 31, vector 32 tile + u at bit 4 (u mod 8) + u / 8
- *    (bits 4 i + r, i = 0..7, hold the 8 consecutive vectors 8 r .. 8 r + 7).
- *  Vectors past n in the last tile are all-zero bits. Norms are separate
- *  arrays of IEEE half (uint16 bits), one per vector.
+ *  - TQ_LAYOUT_VALUES (token-contiguous; values): tiles of 32 vectors in
+ *    blocks of two (64 vectors); word index (tile * d + j) * P + p holds
+ *    coordinate j of 32 vectors of its block. Vector 64 k + t (t = 0..63)
+ *    lies in tile 2 k + (t / 8) mod 2 at bit 16 (t mod 2) + 4 (t / 16) +
+ *    (t mod 8) / 2: bits 4 i + r (i = 0..7) of tile 2 k + s hold vectors
+ *    64 k + 16 (i mod 4) + 8 s + 2 r + i / 4. The packed size rounds n up to
+ *    a whole block.
+ *  Vectors past n in the last tile (block) are all-zero bits. Norms are
+ *  separate arrays of IEEE half (uint16 bits), one per vector.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -99,7 +102,7 @@ typedef struct {
  * Sequence (b, kv_head) starts at vector (b * Hkv + kv_head) * seq_stride;
  * token t of it is vector (b * Hkv + kv_head) * seq_stride + t in `packed`
  * (layout TQ_LAYOUT_KEYS for keys, TQ_LAYOUT_VALUES for values), `norm` and
- * `rnorm`. seq_stride must be a multiple of 32. */
+ * `rnorm`. seq_stride must be a multiple of 64. */
 typedef struct {
   tq_quantizer q;
   int ch_offset;

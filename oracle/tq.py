@@ -45,7 +45,8 @@ import numpy as np
 from . import codebook as _cb
 
 KEYS_TILE = 16    # vectors per tile of the key (coordinate-contiguous) layout
-VALUES_TILE = 32  # vectors per tile of the value (token-contiguous) layout
+VALUES_TILE = 32  # vectors per tile (word) of the value (token-contiguous) layout
+VALUES_BLOCK = 64  # vectors per block of two value tiles (their tokens interleave)
 
 
 @dataclass
@@ -185,17 +186,22 @@ def estimate_ip(y, c: Codes, q: Quantizer) -> np.ndarray:
 #   p = plane (0..B-1: code bit p, LSB first; B: QJL sign, PROD only);
 #   bit i of the word = coordinate 32 g + i.
 # VALUES (token-contiguous), tiles of 32 vectors, words indexed [tile][j][p],
-#   j = coordinate; vector 32 tile + u sits at bit 4 (u mod 8) + u // 8 of
-#   the word (a transpose of the 4 x 8 bit matrix; value_bit below).
-# Vectors past N in the last tile are all-zero bits.
+#   j = coordinate. Tiles come in blocks of two covering 64 vectors: vector
+#   64 B + t (t = 0..63) sits in tile 2 B + (t // 8) % 2, at bit
+#   16 (t % 2) + 4 (t // 16) + (t % 8) // 2 of its words (value_tile_bit
+#   below), so a tile holds the vectors t = 16 q + 8 s + e (q = 0..3,
+#   e = 0..7) of its block.
+# Vectors past N in the last block are all-zero bits.
 # ----------------------------------------------------------------------------
 
-def value_bit(u):
-    """Bit of a value-layout word that holds vector u (0..31) of its tile."""
-    return 4 * (u % 8) + u // 8
+def value_tile_bit(t):
+    """(tile within the block, bit) of vector t (0..63) of a 64-vector block of the value layout."""
+    return (t // 8) % 2, 16 * (t % 2) + 4 * (t // 16) + (t % 8) // 2
 
 
-_VALUE_ORDER = np.array([[u for u in range(32) if value_bit(u) == b][0] for b in range(32)])  # bit -> vector
+# [block position t] -> position in the block's two tiles' bits (tile * 32 + bit)
+_VALUE_POS = np.array([32 * value_tile_bit(t)[0] + value_tile_bit(t)[1] for t in range(64)])
+_VALUE_ORDER = np.argsort(_VALUE_POS)  # tile * 32 + bit -> block position t
 
 
 def _planes(idx, z, mse_bits):
@@ -223,8 +229,8 @@ def _words_to_bits(w):  # [...] uint32 -> [..., 32] bool, bit i of the word at p
 
 def packed_words(d, mse_bits, prod, n, layout):
     P = mse_bits + (1 if prod else 0)
-    tile = KEYS_TILE if layout == "keys" else VALUES_TILE
-    return -(-n // tile) * tile * d * P // 32
+    unit = KEYS_TILE if layout == "keys" else VALUES_BLOCK
+    return -(-n // unit) * unit * d * P // 32
 
 
 def pack(idx, z, mse_bits, layout):
@@ -235,17 +241,18 @@ def pack(idx, z, mse_bits, layout):
         z = np.asarray(z).reshape(N, d)
     pl = _planes(idx, z, mse_bits)
     P = pl.shape[1]
-    tile = KEYS_TILE if layout == "keys" else VALUES_TILE
-    NT = -(-N // tile)
-    full = np.zeros((NT * tile, P, d), dtype=bool)
+    unit = KEYS_TILE if layout == "keys" else VALUES_BLOCK
+    NT = -(-N // unit)
+    full = np.zeros((NT * unit, P, d), dtype=bool)
     full[:N] = pl
     if layout == "keys":
         G = d // 32
-        w = _bits_to_words(full.reshape(NT * tile, P, G, 32))           # [V, P, G]
-        w = w.reshape(NT, tile, P, G).transpose(0, 3, 1, 2)             # [tile, g, t, p]
+        w = _bits_to_words(full.reshape(NT * unit, P, G, 32))           # [V, P, G]
+        w = w.reshape(NT, unit, P, G).transpose(0, 3, 1, 2)             # [tile, g, t, p]
     elif layout == "values":
-        b = full.reshape(NT, tile, P, d).transpose(0, 3, 2, 1)          # [tile, j, p, u]
-        w = _bits_to_words(b[..., _VALUE_ORDER])                        # [tile, j, p]
+        b = full.reshape(NT, unit, P, d)[:, _VALUE_ORDER]               # [block, tile * 32 + bit, p, j]
+        b = b.reshape(NT, 2, 32, P, d).transpose(0, 1, 4, 3, 2)         # [block, tile, j, p, bit]
+        w = _bits_to_words(b)                                           # [block, tile, j, p]
     else:
         raise ValueError(layout)
     return np.ascontiguousarray(w).reshape(-1)
@@ -254,18 +261,18 @@ def pack(idx, z, mse_bits, layout):
 def unpack(words, N, d, mse_bits, prod, layout):
     """Inverse of ``pack``: returns (idx [N, d] uint8, z [N, d] bool or None)."""
     P = mse_bits + (1 if prod else 0)
-    tile = KEYS_TILE if layout == "keys" else VALUES_TILE
-    NT = -(-N // tile)
+    unit = KEYS_TILE if layout == "keys" else VALUES_BLOCK
+    NT = -(-N // unit)
     w = np.asarray(words, dtype=np.uint32)
     if layout == "keys":
         G = d // 32
-        w = w.reshape(NT, G, tile, P).transpose(0, 2, 3, 1)            # [tile, t, p, g]
-        pl = _words_to_bits(w).reshape(NT * tile, P, d)
+        w = w.reshape(NT, G, unit, P).transpose(0, 2, 3, 1)            # [tile, t, p, g]
+        pl = _words_to_bits(w).reshape(NT * unit, P, d)
     else:
-        w = w.reshape(NT, d, P)                                         # [tile, j, p]
-        bits = _words_to_bits(w)                                        # [tile, j, p, bit]
-        bits = bits[..., [value_bit(u) for u in range(32)]]             # [tile, j, p, u]
-        pl = bits.transpose(0, 3, 2, 1).reshape(NT * tile, P, d)
+        w = w.reshape(NT, 2, d, P)                                      # [block, tile, j, p]
+        bits = _words_to_bits(w)                                        # [block, tile, j, p, bit]
+        bits = bits.transpose(0, 1, 4, 3, 2).reshape(NT, 64, P, d)      # [block, tile * 32 + bit, p, j]
+        pl = bits[:, _VALUE_POS].reshape(NT * unit, P, d)
     pl = pl[:N]
     idx = np.zeros((N, d), dtype=np.uint8)
     for p in range(mse_bits):

@@ -43,22 +43,23 @@ def _key_rows(words, rows, d, mse_bits, prod):
 
 
 def _value_rows(words, rows, d, mse_bits, prod):
-    """Codes of the given rows of a value-layout array (their whole 32-vector tiles unpacked)."""
+    """Codes of the given rows of a value-layout array (their whole 64-vector blocks unpacked)."""
     P = mse_bits + (1 if prod else 0)
-    per_tile = d * P
-    tiles = np.unique(rows // 32)
-    sub = words.reshape(-1, per_tile)[tiles].reshape(-1)
-    idx, z = otq.unpack(sub, len(tiles) * 32, d, mse_bits, prod, "values")
-    pos = np.searchsorted(tiles, rows // 32) * 32 + rows % 32
+    B = otq.VALUES_BLOCK
+    per_block = B * d * P // 32
+    blocks = np.unique(rows // B)
+    sub = words.reshape(-1, per_block)[blocks].reshape(-1)
+    idx, z = otq.unpack(sub, len(blocks) * B, d, mse_bits, prod, "values")
+    pos = np.searchsorted(blocks, rows // B) * B + rows % B
     return idx[pos], (z[pos] if z is not None else None)
 
 
 def _slice_words(words, r0, T, d, mse_bits, prod, layout):
-    """Packed words of rows r0 .. r0 + T (r0 and T multiples of the layout's tile)."""
+    """Packed words of rows r0 .. r0 + T (r0 and T multiples of the layout's packing unit)."""
     P = mse_bits + (1 if prod else 0)
-    tile = 16 if layout == "keys" else 32
-    per_row = d * P // 32  # words per vector, whole tiles
-    return words[r0 // tile * tile * per_row:(r0 + T) // tile * tile * per_row]
+    unit = otq.KEYS_TILE if layout == "keys" else otq.VALUES_BLOCK
+    per_row = d * P // 32  # words per vector, whole units
+    return words[r0 // unit * unit * per_row:(r0 + T) // unit * unit * per_row]
 
 
 def test_single_layer_decode_full_size():

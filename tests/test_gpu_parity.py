@@ -113,8 +113,8 @@ def test_quantize_matches_oracle(d, B, prod, lay, N, dt):
     idx, z = otq.unpack(words, N, d, B, prod, lay)
     codes = otq.quantize(x.astype(np.float64), gq.oq)
     assert_codes_match(idx, z, to_np_f16(norm), to_np_f16(rnorm), codes, gq.oq)
-    # padding vectors of the last tile are zero bits
-    tile = otq.KEYS_TILE if lay == "keys" else otq.VALUES_TILE
+    # padding vectors of the last tile (64-vector block for values) are zero bits
+    tile = otq.KEYS_TILE if lay == "keys" else otq.VALUES_BLOCK
     n_round = -(-N // tile) * tile
     pidx, pz = otq.unpack(words, n_round, d, B, prod, lay)
     assert not pidx[N:].any() and (pz is None or not pz[N:].any())
@@ -170,7 +170,7 @@ def test_append_writes_only_its_rows(d, B, prod, lay, dt, C, n_in):
     tq.tq_append_kv(gq.q, layout, tq.TQ_BF16 if dt == "bf16" else tq.TQ_F32, x_t, n, d, torch_dev(rows_all), C,
                     packed, norm, rnorm)
     torch.cuda.synchronize()
-    tile = otq.KEYS_TILE if lay == "keys" else otq.VALUES_TILE
+    tile = otq.KEYS_TILE if lay == "keys" else otq.VALUES_BLOCK
     n_round = -(-C // tile) * tile
     w1 = to_np_u32(packed)
     idx0, z0 = otq.unpack(w0, n_round, d, B, prod, lay)
@@ -323,7 +323,7 @@ DECODE_CASES = [
     # B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt
     (2, 8, 2, 300, 320, [300, 123], 3, 3, "bf16"),
     (1, 32, 8, 1024, 1024, None, 3, 3, "bf16"),
-    (3, 4, 1, 65, 96, [1, 64, 65], 2, 2, "f32"),
+    (3, 4, 1, 65, 128, [1, 64, 65], 2, 2, "f32"),
     (2, 4, 2, 63, 64, [0, 63], 1, 1, "f32"),
 ]
 
@@ -340,7 +340,7 @@ def test_decode_other_head_sizes_and_tiles(d, Hq, Hkv, kB, vB):
     # head sizes other than 128 (general kernel), GQA groups of 8 (two
     # head tiles), groups of 3 (a partial tile) and 4-bit codebooks
     print(f"decode d={d} Hq={Hq} Hkv={Hkv} kB={kB} vB={vB}", flush=True)
-    _decode_case(2, Hq, Hkv, 700, 736, [700, 333], kB, vB, "bf16", d)
+    _decode_case(2, Hq, Hkv, 700, 768, [700, 333], kB, vB, "bf16", d)
 
 
 def _decode_case(B, Hq, Hkv, T, T_cap, seq_lens, kB, vB, qdt, d, fold=False, kprod=True):
@@ -390,7 +390,7 @@ def test_score_matrix_tiny_workload(b_total):
 def test_decode_two_channel_groups(fold):
     # 2.5 bits per channel: 32 outlier channels (keys 2+1 bits, values 3 bits)
     # and 96 others (keys 1+1, values 2), each group with its own norms.
-    B, Hq, Hkv, T, T_cap = 2, 8, 2, 200, 224
+    B, Hq, Hkv, T, T_cap = 2, 8, 2, 200, 256
     K, V = make_kv(B, Hkv, T, 128, seed=4)
     ka, kb = GpuQuantizer(32, 2, True, 1, fold=fold), GpuQuantizer(96, 1, True, 2, fold=fold)
     va, vb = GpuQuantizer(32, 3, False, 3), GpuQuantizer(96, 2, False, 4)

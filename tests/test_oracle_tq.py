@@ -212,19 +212,27 @@ def test_keys_layout_hand_fixture():
 
 
 def test_values_layout_hand_fixture():
-    # d = 32, B = 2, MSE: word [tile][j][p] holds vector 32 tile + u at bit
-    # 4 (u mod 8) + u // 8: vector 0 -> bit 0, vector 33 (u = 1) -> bit 4,
-    # vector 9 (u = 9) -> bit 5, vector 31 -> bit 31.
-    idx = np.zeros((34, 32), np.uint8)
+    # d = 32, B = 2, MSE: words [tile][j][p]; tiles come in blocks of two
+    # covering 64 vectors, vector 64 B + t in tile 2 B + (t // 8) % 2 at bit
+    # 16 (t % 2) + 4 (t // 16) + (t % 8) // 2:
+    #   vector 0  -> tile 0, bit 0;      vector 9  -> tile 1, bit 16;
+    #   vector 31 -> tile 1, bit 23;     vector 63 -> tile 1, bit 31;
+    #   vector 50 -> tile 0, bit 13;     vector 64 -> tile 2, bit 0 (the next block).
+    idx = np.zeros((65, 32), np.uint8)
     idx[0, 5] = 3          # both planes set at coordinate 5 of vector 0
-    idx[33, 0] = 2         # plane 1 set at coordinate 0 of vector 33 (tile 1, u = 1)
+    idx[64, 0] = 2         # plane 1 set at coordinate 0 of vector 64
     idx[9, 2] = 1          # plane 0 at coordinate 2 of vector 9
     idx[31, 2] = 1         # plane 0 at coordinate 2 of vector 31
-    w = tq.pack(idx, None, 2, "values").reshape(2, 32, 2)
+    idx[63, 2] = 1         # plane 0 at coordinate 2 of vector 63
+    idx[50, 7] = 1         # plane 0 at coordinate 7 of vector 50
+    w = tq.pack(idx, None, 2, "values")
+    assert w.shape == (4 * 32 * 2,)                   # two blocks of two tiles, 32 coordinates, 2 planes
+    w = w.reshape(4, 32, 2)
     assert w[0, 5, 0] == 1 and w[0, 5, 1] == 1
-    assert w[1, 0, 0] == 0 and w[1, 0, 1] == 1 << 4
-    assert w[0, 2, 0] == (1 << 5) | (1 << 31) and w[0, 2, 1] == 0
-    assert int(w.astype(np.uint64).sum()) == 1 + 1 + (1 << 4) + (1 << 5) + (1 << 31)
+    assert w[2, 0, 0] == 0 and w[2, 0, 1] == 1
+    assert w[1, 2, 0] == (1 << 16) | (1 << 23) | (1 << 31) and w[1, 2, 1] == 0
+    assert w[0, 7, 0] == 1 << 13
+    assert int(w.astype(np.uint64).sum()) == 1 + 1 + 1 + (1 << 16) + (1 << 23) + (1 << 31) + (1 << 13)
 
 
 @pytest.mark.parametrize("layout", ["keys", "values"])
