@@ -1838,6 +1838,18 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         p[j] = live ? __builtin_amdgcn_exp2f(lg[j] - m_w) : 0.f;
         l_w += p[j];
       }
+      // this lane's operand bytes in the rows of head hl. With one value
+      // group they are recomputed in every chunk from the lane index: the
+      // compiler otherwise holds the offset through the loop, spills it
+      // (those layouts have the widest key and value codes) and reloads it
+      // behind the loads in flight.
+      int wofs = 4 * hl * kWRow + 4 * tl + 64 * WW;
+      if constexpr (NV == 1) {
+        uint32_t ones = ~0u;
+        asm volatile("" : "+s"(ones));
+        const int wl = (int)__builtin_amdgcn_mbcnt_hi(ones, __builtin_amdgcn_mbcnt_lo(ones, 0u));
+        wofs = (wl >> 4) * (4 * kWRow) + 4 * (wl & 15) + 64 * WW;
+      }
 #pragma unroll
       for (int gv = 0; gv < NV; ++gv) {
         // value-norm scale times the fp4 pre-scale; tokens in pairs, the
@@ -1848,8 +1860,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         digits3<true>((p[2] * st) * hbits(vd.nv[gv][1]), (p[3] * st) * hbits_hi(vd.nv[gv][1]), x);
         // rows (head hl, digit m), operand bytes 64 WW + 4 tl .. + 3
 #pragma unroll
-        for (int m = 0; m < 3; ++m)
-          *reinterpret_cast<uint32_t*>(&wbuf[par][gv][(4 * hl + m) * kWRow + 64 * WW + 4 * tl]) = x[m];
+        for (int m = 0; m < 3; ++m) *reinterpret_cast<uint32_t*>(&wbuf[par][gv][wofs + m * kWRow]) = x[m];
       }
       if (tl == 0) xm[par][WW][hl] = m_w;
       if (lane == 0) {
