@@ -1476,17 +1476,20 @@ __device__ __forceinline__ int ptile(int w, int j) { return 4 * w + j; }
 template <int NK>
 struct PKeys {
   uint32_t kw[4][5];  // key plane words of the lane's coordinate word, token c of each of the wave's tiles
-  uint32_t nr[NK][4];  // key norm (low half) | residual norm (high half)
+  // (norms are kept as loaded, one half per register: packing or widening
+  // them right after the load would wait for the loads in flight)
+  uint16_t nn[NK][4];  // key norm (half bits), token c of each of the wave's tiles
+  uint16_t rn[NK][4];  // residual norm (half bits; groups with the sketch)
 };
 template <int NV>
 struct PVals {
-  uint32_t nv[NV][2];  // value norms of the wave's tiles 2 j (low) and 2 j + 1 (high), token c
+  uint16_t nv[NV][4];  // value norms (half bits), token c of each of the wave's tiles
   uint32_t vw[4][3];  // value plane words of the wave's 4 coordinate tiles
 };
 
 template <int NK, int P0, int P1, int KP0, int KP1>
 __device__ __forceinline__ void pload_keys(PKeys<NK>& dt, const KAddr& ka, const NAddr& na, int c0, int tlast,
-                                           int w, int lane) {
+                                           int w, int lane, bool g1) {
   const int last_tile = tlast >> 4;
   const uint32_t tl2 = 2u * (lane & 15);
 #pragma unroll
@@ -1495,17 +1498,27 @@ __device__ __forceinline__ void pload_keys(PKeys<NK>& dt, const KAddr& ka, const
     if constexpr (NK == 1) {
       buf_words<P0>(ka.res[0], ka.voff[0], tile * ka.step[0], dt.kw[j]);
     } else {
-      uint32_t w0[5] = {0u, 0u, 0u, 0u, 0u}, w1[5] = {0u, 0u, 0u, 0u, 0u};
-      buf_words<P0>(ka.res[0], ka.voff[0], tile * ka.step[0], w0);
-      buf_words<P1>(ka.res[1], ka.voff[1], tile * ka.step[1], w1);
+      // each lane loads its own group's words (two loads under complementary
+      // lane masks into the same registers: nothing merges the groups' words
+      // after the loads)
+      uint32_t wv[5];
+      if (g1) {
+        buf_words<P1>(ka.res[1], ka.voff[1], tile * ka.step[1], wv);
 #pragma unroll
-      for (int pp = 0; pp < 5; ++pp) dt.kw[j][pp] = w0[pp] | w1[pp];
+        for (int pp = P1; pp < 5; ++pp) wv[pp] = 0u;
+      } else {
+        buf_words<P0>(ka.res[0], ka.voff[0], tile * ka.step[0], wv);
+#pragma unroll
+        for (int pp = P0; pp < 5; ++pp) wv[pp] = 0u;
+      }
+#pragma unroll
+      for (int pp = 0; pp < 5; ++pp) dt.kw[j][pp] = wv[pp];
     }
 #pragma unroll
     for (int gi = 0; gi < NK; ++gi) {
-      const uint32_t nn = buf_half(na.n[gi], tl2, 32u * tile);
-      const uint32_t rn = ((gi == 0 && KP0) || (gi == 1 && KP1)) ? buf_half(na.r[gi], tl2, 32u * tile) : 0u;
-      dt.nr[gi][j] = __builtin_amdgcn_perm(rn, nn, 0x05040100u);  // (nn low half, rn high half)
+      dt.nn[gi][j] = __builtin_amdgcn_raw_buffer_load_b16(na.n[gi], tl2, 32u * tile, 0);
+      dt.rn[gi][j] = ((gi == 0 && KP0) || (gi == 1 && KP1)) ? __builtin_amdgcn_raw_buffer_load_b16(na.r[gi], tl2, 32u * tile, 0)
+                                                             : (uint16_t)0;
     }
   }
 }
@@ -1519,8 +1532,7 @@ __device__ __forceinline__ void pload_vnorms(PVals<NV>& dt, const NAddr& na, int
     const uint32_t tile = (uint32_t)min((c0 >> 4) + ptile(w, j), last_tile);
 #pragma unroll
     for (int gv = 0; gv < NV; ++gv) {
-      const uint32_t h = buf_half(na.nv[gv], tl2, 32u * tile);
-      dt.nv[gv][j >> 1] = (j & 1) ? __builtin_amdgcn_perm(h, dt.nv[gv][j >> 1], 0x05040100u) : h;
+      dt.nv[gv][j] = __builtin_amdgcn_raw_buffer_load_b16(na.nv[gv], tl2, 32u * tile, 0);
     }
   }
 }
@@ -1634,7 +1646,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   }
   PKeys<NK> kA;
   PVals<NV> vd;
-  pload_keys<NK, P0, P1, KP0, KP1>(kA, ka, na, ts - tok_base, rel_first_last, w, lane);
+  pload_keys<NK, P0, P1, KP0, KP1>(kA, ka, na, ts - tok_base, rel_first_last, w, lane, kg1);
   pload_vnorms<NV>(vd, na, ts - tok_base, rel_first_last, w, lane);
   int esc_mse[NK], esc_qjl[NK];
 #pragma unroll
@@ -1775,8 +1787,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
         for (int gi = 0; gi < NK; ++gi) {
           float part = sum4(dm[gi]);
-          if ((gi == 0 && KP0) || (gi == 1 && KP1)) part = fmaf(gam[gi] * hbits_hi(dc.nr[gi][j]), sum4(dq[gi]), part);
-          sc = fmaf(hbits(dc.nr[gi][j]), part, sc);
+          if ((gi == 0 && KP0) || (gi == 1 && KP1)) part = fmaf(gam[gi] * hbits(dc.rn[gi][j]), sum4(dq[gi]), part);
+          sc = fmaf(hbits(dc.nn[gi][j]), part, sc);
         }
         lg[j] = sc;
       }
@@ -1798,16 +1810,15 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       }
       // the key words and norms are used up: the next chunk's go to the same
       // registers, arriving while this chunk's weights and value sums run
-      pload_keys<NK, P0, P1, KP0, KP1>(dc, ka, na, cn - tok_base, rel_last, WW, lane);
+      pload_keys<NK, P0, P1, KP0, KP1>(dc, ka, na, cn - tok_base, rel_last, WW, lane, kg1);
       // value norms of tokens at or past the split's end are cleared
       if (tail) {
         const int rem = te - (c0 + tl);  // token c0 + 16 T + tl is in range iff 16 T < rem
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int Ta = ptile(WW, 2 * jj), Tb = ptile(WW, 2 * jj + 1);
-          const uint32_t mk = (rem > 16 * Ta ? 0xffffu : 0u) | (rem > 16 * Tb ? 0xffff0000u : 0u);
+        for (int j = 0; j < 4; ++j) {
+          const bool in = rem > 16 * ptile(WW, j);
 #pragma unroll
-          for (int gv = 0; gv < NV; ++gv) vd.nv[gv][jj] &= mk;
+          for (int gv = 0; gv < NV; ++gv) vd.nv[gv][j] = in ? vd.nv[gv][j] : (uint16_t)0;
         }
       }
       // ---------------- this wave's references: running maximum (rounded up
@@ -1823,7 +1834,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       for (int gv = 0; gv < NV; ++gv) {
         // (every 16-lane row holds the same 16 tokens of each tile: a row
         // maximum is the wave's)
-        uint32_t vm = max(max(vd.nv[gv][0] & 0xffffu, vd.nv[gv][0] >> 16), max(vd.nv[gv][1] & 0xffffu, vd.nv[gv][1] >> 16));
+        uint32_t vm = max(max(vd.nv[gv][0], vd.nv[gv][1]), max(vd.nv[gv][2], vd.nv[gv][3]));  // (16-bit maxima)
         vm = max(vm, row_ror_u<8>(vm));
         vm = max(vm, row_ror_u<4>(vm));
         vm = max(vm, row_ror_u<2>(vm));
@@ -1856,8 +1867,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         // second pair's digits into the dwords' high halves
         const float st = ldexpf(tinv, kWScale - e_w[gv]);
         uint32_t x[3];
-        digits3<false>((p[0] * st) * hbits(vd.nv[gv][0]), (p[1] * st) * hbits_hi(vd.nv[gv][0]), x);
-        digits3<true>((p[2] * st) * hbits(vd.nv[gv][1]), (p[3] * st) * hbits_hi(vd.nv[gv][1]), x);
+        digits3<false>((p[0] * st) * hbits(vd.nv[gv][0]), (p[1] * st) * hbits(vd.nv[gv][1]), x);
+        digits3<true>((p[2] * st) * hbits(vd.nv[gv][2]), (p[3] * st) * hbits(vd.nv[gv][3]), x);
         // rows (head hl, digit m), operand bytes 64 WW + 4 tl .. + 3
 #pragma unroll
         for (int m = 0; m < 3; ++m) *reinterpret_cast<uint32_t*>(&wbuf[par][gv][wofs + m * kWRow]) = x[m];
