@@ -60,6 +60,14 @@ hipError_t launch_append_step(const tq_kv_desc& k, const tq_kv_desc& v, const St
 // Matrix-core quantiser for vectors of 32, 64, 96 or 128 channels (quantize_mfma.hip): rows
 // 16-byte aligned.
 bool quantize_mfma_supported(const tq_quantizer& q, tq_dtype dt, const void* x, int64_t stride);
+// Matrix-core quantiser for vectors of more than 128 channels in the key
+// layout (quantize_mfma.hip): two GEMM-shaped passes over batches of 65536
+// vectors; with the sketch it keeps a device workspace of the batch's
+// residuals (about 4 d bytes per vector), allocated on first use per
+// device and kept until the process ends.
+bool quantize_wide_supported(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t stride);
+hipError_t launch_quantize_wide(const tq_quantizer& q, tq_dtype dt, const void* x, int64_t n, int64_t stride,
+                                void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s);
 hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t n,
                                 int64_t stride, void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s);
 

@@ -20,6 +20,10 @@
 // the operand layout of S r~ (bf16 matrix cores, S in LDS), and the code
 // and sign bits are packed straight from wave ballots of the compares into
 // the library's bit-plane layouts.
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -606,6 +610,328 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
   }
 }
 
+
+// ------------------------------------------------------------------ wide vectors
+// Vectors of more than 128 channels (key layout): the same steps as above,
+// as two GEMM-shaped passes over batches of vectors, because R and S no
+// longer fit a workgroup's registers and LDS (riverfrot section 4.1 for the
+// rotation and the interval index, section 4.3 for the sketch).
+//
+// A workgroup of 4 waves owns a tile of kWC = 128 output coordinates x kWV
+// = 128 vectors; wave w the coordinates 32 w .. 32 w + 31 of the tile (two
+// 16-row MFMA blocks) for all 128 vectors (8 blocks of 16). The contraction
+// over the d inputs runs in steps of 32 on v_mfma_f32_16x16x32_bf16: the
+// wave's matrix rows come straight from global memory (fp32, split into
+// bf16 high and low parts in registers), the tile's inputs through LDS
+// (split once, double-buffered, rows padded to 80 bytes so that the 16
+// rows a read touches fall in different banks); three products hi hi +
+// hi lo + lo hi (two for bf16 inputs, which are exact), fp32 accumulation,
+// so the error is about 2^-17 of the terms' magnitudes as in the narrow
+// kernel.
+// Pass 1 (matrix R): |x|^2 from the staged inputs; u = (R x)_c / |x|; the
+// interval index by binary search, packed from wave ballots into the key
+// words of the tile's 32-coordinate groups; with the sketch, the residual
+// u - c[idx] (fp32) to the batch workspace and its squared sum per vector
+// and 32-coordinate group.
+// Pass 2 (matrix S, on the residuals): the signs of (S r~)_c into the sign
+// plane; the workgroups of coordinate tile 0 write |r~| from the partial
+// sums.
+// Tiles are numbered so that the coordinate tiles of one vector tile run on
+// one XCD, one after another (its inputs stay in that XCD's L2).
+constexpr int kWC = 128;
+constexpr int kWV = 128;
+constexpr int kWThreads = 256;
+constexpr int kWRowB = 80;
+constexpr int64_t kWBatch = 65536;  // vectors per batch (the residual workspace holds one)
+
+struct WArgs {
+  const void* x;   // input rows: pass 1 the call's vectors, pass 2 the residual workspace
+  int64_t stride;  // elements per input row
+  int64_t xrow0;   // input row of the batch's first vector
+  const float* M;  // R (pass 1) or S (pass 2), d x d row-major
+  float* res;      // [kWBatch][d] residuals of the batch (pass 1 writes, pass 2 reads)
+  float* rho2;     // [kWBatch][d / 32] squared residual sums per 32-coordinate group
+  int64_t v0;      // first vector of the batch
+  int64_t nb;      // vectors in the batch
+  int64_t n;       // vectors in the call
+  int d;
+  int B;
+  float cent[TQ_MAX_LEVELS];
+  float thr[TQ_MAX_LEVELS - 1];
+  uint32_t* packed;
+  uint16_t* norm;
+  uint16_t* rnorm;
+};
+
+__device__ __forceinline__ uint32_t key_word_of(uint32_t acc8, int q) {
+  return or_q(((acc8 & 0xfu) | ((acc8 & 0xf0u) << 12)) << (4 * q));
+}
+
+// The GEMM core shared by both passes: acc[m][nt] = rows c0 + 16 m + (4 q
+// .. 4 q + 3) of M times vectors 16 nt + (lane % 16) of the tile. Returns
+// the sum of squares of the inputs this thread staged (thread t: vector t /
+// 2, inputs 16 (t % 2) .. + 15 of every step).
+template <bool F32IN>
+__device__ __forceinline__ float wide_gemm(const WArgs& a, int64_t lv0, int c0, bool wave_on, v4f (&acc)[2][8],
+                                           uint8_t (*xs)[2][kWV][kWRowB]) {
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, nl = lane & 15;
+  const int d = a.d, nks = d / 32;
+  const int sv = tid >> 1, kh = tid & 1;
+  const int64_t srow = a.xrow0 + (lv0 + sv < a.nb ? lv0 + sv : a.nb - 1);  // (padding vectors re-read the last row)
+  float ss = 0.f;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[m][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+  // staged inputs of one step, in registers while the previous step computes
+  float4 xf[4];
+  uint4 xb[2];
+  auto load_x = [&](int ks) __attribute__((always_inline)) {
+    if constexpr (F32IN) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + srow * a.stride + 32 * ks + 16 * kh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xf[i] = p[i];
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + srow * a.stride + 32 * ks + 16 * kh);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) xb[i] = p[i];
+    }
+  };
+  auto stage = [&](int buf) __attribute__((always_inline)) {
+    if constexpr (F32IN) {
+      uint32_t h[8], l[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        split_bf16(xf[i].x, xf[i].y, h[2 * i], l[2 * i]);
+        split_bf16(xf[i].z, xf[i].w, h[2 * i + 1], l[2 * i + 1]);
+        ss = fmaf(xf[i].x, xf[i].x, ss);
+        ss = fmaf(xf[i].y, xf[i].y, ss);
+        ss = fmaf(xf[i].z, xf[i].z, ss);
+        ss = fmaf(xf[i].w, xf[i].w, ss);
+      }
+      uint4* hp = reinterpret_cast<uint4*>(&xs[buf][0][sv][32 * kh]);
+      uint4* lp = reinterpret_cast<uint4*>(&xs[buf][1][sv][32 * kh]);
+      hp[0] = make_uint4(h[0], h[1], h[2], h[3]);
+      hp[1] = make_uint4(h[4], h[5], h[6], h[7]);
+      lp[0] = make_uint4(l[0], l[1], l[2], l[3]);
+      lp[1] = make_uint4(l[4], l[5], l[6], l[7]);
+    } else {
+      const uint32_t wv[8] = {xb[0].x, xb[0].y, xb[0].z, xb[0].w, xb[1].x, xb[1].y, xb[1].z, xb[1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float lo = __uint_as_float(wv[i] << 16), hi = __uint_as_float(wv[i] & 0xffff0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+      uint4* hp = reinterpret_cast<uint4*>(&xs[buf][0][sv][32 * kh]);
+      hp[0] = xb[0];
+      hp[1] = xb[1];
+    }
+  };
+  // the wave's matrix rows c0 + 16 m + (lane % 16), inputs 32 ks + 8 q .. + 7
+  float4 mr[2][2], mn[2][2];
+  auto load_m = [&](int ks, float4 (&dst)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float4* p = reinterpret_cast<const float4*>(a.M + (int64_t)(c0 + 16 * m + nl) * d + 32 * ks + 8 * q);
+      dst[m][0] = p[0];
+      dst[m][1] = p[1];
+    }
+  };
+  load_x(0);
+  if (wave_on) load_m(0, mr);
+  stage(0);
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const int cur = ks & 1;
+    const bool more = ks + 1 < nks;
+    if (more) {
+      load_x(ks + 1);
+      if (wave_on) load_m(ks + 1, mn);
+    }
+    if (wave_on) {
+      bf16x8 ah[2], al[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        uint32_t h[4], l[4];
+        split_bf16(mr[m][0].x, mr[m][0].y, h[0], l[0]);
+        split_bf16(mr[m][0].z, mr[m][0].w, h[1], l[1]);
+        split_bf16(mr[m][1].x, mr[m][1].y, h[2], l[2]);
+        split_bf16(mr[m][1].z, mr[m][1].w, h[3], l[3]);
+        ah[m] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+        al[m] = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&xs[cur][0][16 * nt + nl][16 * q]);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          acc[m][nt] = mfma_bf16(ah[m], bh, acc[m][nt]);
+          acc[m][nt] = mfma_bf16(al[m], bh, acc[m][nt]);
+        }
+        if constexpr (F32IN) {
+          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&xs[cur][1][16 * nt + nl][16 * q]);
+#pragma unroll
+          for (int m = 0; m < 2; ++m) acc[m][nt] = mfma_bf16(ah[m], bl, acc[m][nt]);
+        }
+      }
+    }
+    if (more) stage(cur ^ 1);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      mr[m][0] = mn[m][0];
+      mr[m][1] = mn[m][1];
+    }
+    __syncthreads();
+  }
+  return ss;
+}
+
+// Tile of this workgroup (coordinate tiles of one vector tile on one XCD);
+// false for the grid's padding.
+__device__ __forceinline__ bool wide_tile(const WArgs& a, int& vt, int& ct) {
+  const int nct = (a.d + kWC - 1) / kWC, nvt = (int)((a.nb + kWV - 1) / kWV);
+  const int id = blockIdx.x, k8 = id >> 3;
+  vt = (k8 / nct) * 8 + (id & 7);
+  ct = k8 % nct;
+  return vt < nvt;
+}
+
+template <bool F32IN, int B, bool PROD>
+__global__ __launch_bounds__(kWThreads, 2) void wide_rotate_kernel(WArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][2][kWV][kWRowB];
+  __shared__ float sinv[kWV];
+  int vt, ct;
+  if (!wide_tile(a, vt, ct)) return;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, nl = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int d = a.d, G = d / 32;
+  const int c0 = ct * kWC + 32 * w;
+  const bool wave_on = c0 < d;
+  const int64_t lv0 = (int64_t)vt * kWV;
+  constexpr int L = 1 << B;
+  constexpr int P = B + (PROD ? 1 : 0);
+  float th[L - 1], cv[L];
+#pragma unroll
+  for (int t = 0; t < L - 1; ++t) {
+    th[t] = a.thr[t];
+    asm volatile("" : "+v"(th[t]));  // held in a VGPR: the selects take one SGPR operand at most
+  }
+#pragma unroll
+  for (int t = 0; t < L; ++t) {
+    cv[t] = a.cent[t];
+    asm volatile("" : "+v"(cv[t]));
+  }
+  v4f acc[2][8];
+  float ss = wide_gemm<F32IN>(a, lv0, c0, wave_on, acc, xs);
+  // |x| of the tile's vectors (two staging threads per vector)
+  ss += __shfl_xor(ss, 1);
+  if ((tid & 1) == 0) {
+    const int sv = tid >> 1;
+    const bool valid = lv0 + sv < a.nb;
+    const float nrm = __builtin_amdgcn_sqrtf(ss);
+    sinv[sv] = valid && nrm > 0.f ? __builtin_amdgcn_rcpf(nrm) : 0.f;
+    if (ct == 0 && valid) a.norm[a.v0 + lv0 + sv] = tqd::f32_to_half_bits(nrm);
+  }
+  __syncthreads();
+  if (!wave_on) return;
+  const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const int lvl = 16 * nt + nl;
+    const int64_t lv = lv0 + lvl;
+    const bool valid = lv < a.nb;
+    const float inv = sinv[lvl];
+    const bool live = inv > 0.f;
+    const uint64_t vm = __builtin_amdgcn_ballot_w64(valid), lm = __builtin_amdgcn_ballot_w64(live);
+    uint32_t acc8[B];
+#pragma unroll
+    for (int p = 0; p < B; ++p) acc8[p] = 0u;
+    float rres[2][4];
+    float r2 = 0.f;
+    // (coordinates in descending order: the shift-ins build bit 4 m + r)
+#pragma unroll
+    for (int m = 1; m >= 0; --m)
+#pragma unroll
+      for (int r = 3; r >= 0; --r) {
+        const float u = acc[m][nt][r] * inv;
+        bool bt[B];
+        interval_bits<B, B - 1>(u, th, bt);
+#pragma unroll
+        for (int p = 0; p < B; ++p) {
+          const uint64_t c = __builtin_amdgcn_ballot_w64(bt[B - 1 - p]);
+          acc8[p] = shift_in(acc8[p], (c & lm) | (p == B - 1 ? (vm & ~lm) : 0ull));
+        }
+        if constexpr (PROD) {
+          const float rv = (u - pick<L, 0, 1>(cv, bt)) * (float)live;
+          rres[m][r] = rv;
+          r2 = fmaf(rv, rv, r2);
+        }
+      }
+    uint32_t kw[B];
+#pragma unroll
+    for (int p = 0; p < B; ++p) kw[p] = key_word_of(acc8[p], q);
+    // key tile (16 vectors) of this block; lane (q, nl) stores planes q, q + 4
+    const int64_t vt16 = a.v0 + lv0 + 16 * nt;
+    if (vt16 < nround) {
+      uint32_t* dst = a.packed + ((vt16 / 16) * G + (c0 >> 5)) * 16 * P;
+#pragma unroll
+      for (int pass = 0; pass < (B + 3) / 4; ++pass) {
+        const int p = 4 * pass + q;
+        uint32_t wv = kw[4 * pass];
+#pragma unroll
+        for (int pp = 4 * pass + 1; pp < B && pp < 4 * pass + 4; ++pp) wv = (p == pp) ? kw[pp] : wv;
+        if (p < B) dst[nl * P + p] = wv;
+      }
+    }
+    if constexpr (PROD) {
+      const float s = sum_q(r2);
+      if (valid) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          *reinterpret_cast<float4*>(a.res + lv * d + c0 + 16 * m + 4 * q) =
+              make_float4(rres[m][0], rres[m][1], rres[m][2], rres[m][3]);
+        if (q == 0) a.rho2[lv * G + (c0 >> 5)] = s;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kWThreads, 2) void wide_sketch_kernel(WArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][2][kWV][kWRowB];
+  int vt, ct;
+  if (!wide_tile(a, vt, ct)) return;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, nl = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int d = a.d, G = d / 32, P = a.B + 1;
+  const int c0 = ct * kWC + 32 * w;
+  const bool wave_on = c0 < d;
+  const int64_t lv0 = (int64_t)vt * kWV;
+  // |r~| from pass 1's partial sums (coordinate tile 0)
+  if (ct == 0 && tid < kWV && lv0 + tid < a.nb) {
+    const float* p = a.rho2 + (lv0 + tid) * G;
+    float s = 0.f;
+    for (int g = 0; g < G; ++g) s += p[g];
+    a.rnorm[a.v0 + lv0 + tid] = tqd::f32_to_half_bits(__builtin_amdgcn_sqrtf(s));
+  }
+  v4f acc[2][8];
+  (void)wide_gemm<true>(a, lv0, c0, wave_on, acc, xs);
+  if (!wave_on) return;
+  const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const uint64_t vm = __builtin_amdgcn_ballot_w64(lv0 + 16 * nt + nl < a.nb);
+    uint32_t acc8 = 0u;
+#pragma unroll
+    for (int m = 1; m >= 0; --m)
+#pragma unroll
+      for (int r = 3; r >= 0; --r) acc8 = shift_in(acc8, __builtin_amdgcn_ballot_w64(acc[m][nt][r] >= 0.f) & vm);
+    const uint32_t kw = key_word_of(acc8, q);
+    const int64_t vt16 = a.v0 + lv0 + 16 * nt;
+    if (vt16 < nround && q == 0) a.packed[(((vt16 / 16) * G + (c0 >> 5)) * 16 + nl) * P + a.B] = kw;
+  }
+}
+
 }  // namespace
 
 namespace tqk {
@@ -653,6 +979,94 @@ hipError_t launch_quantize_mfma(const tq_quantizer& q, tq_layout layout, tq_dtyp
   const int64_t grid = a.ntiles < slots ? a.ntiles : slots;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), 0, s, a);
   return hipGetLastError();
+}
+
+
+bool quantize_wide_supported(const tq_quantizer& q, tq_layout layout, tq_dtype dt, const void* x, int64_t stride) {
+  const int64_t esz = dt == TQ_BF16 ? 2 : 4;
+  return layout == TQ_LAYOUT_KEYS && q.d > 128 && (q.d % 32) == 0 && ((stride * esz) % 16) == 0 &&
+         ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+}
+
+// Device workspace of the wide quantiser (the residuals of one batch),
+// allocated on first use per device and kept until the process ends; grown
+// when a call needs more.
+static float* wide_workspace(size_t floats, hipError_t& err) {
+  static std::mutex mu;
+  static std::vector<std::pair<float*, size_t>> per_dev;
+  int dev = 0;
+  err = hipGetDevice(&dev);
+  if (err != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)per_dev.size() <= dev) per_dev.resize(dev + 1, {nullptr, 0});
+  auto& slot = per_dev[dev];
+  if (slot.second < floats) {
+    if (slot.first) {
+      err = hipFree(slot.first);  // (waits for work in flight on the device)
+      if (err != hipSuccess) return nullptr;
+      slot = {nullptr, 0};
+    }
+    void* p = nullptr;
+    err = hipMalloc(&p, floats * sizeof(float));
+    if (err != hipSuccess) return nullptr;
+    slot = {static_cast<float*>(p), floats};
+  }
+  return slot.first;
+}
+
+hipError_t launch_quantize_wide(const tq_quantizer& q, tq_dtype dt, const void* x, int64_t n, int64_t stride,
+                                void* packed, uint16_t* norm, uint16_t* rnorm, hipStream_t s) {
+  WArgs a{};
+  a.x = x;
+  a.stride = stride;
+  a.M = q.R;
+  a.n = n;
+  a.d = q.d;
+  a.B = q.mse_bits;
+  for (int i = 0; i < TQ_MAX_LEVELS; ++i) a.cent[i] = q.centroids[i];
+  for (int i = 0; i < TQ_MAX_LEVELS - 1; ++i) a.thr[i] = q.thresholds[i];
+  a.packed = static_cast<uint32_t*>(packed);
+  a.norm = norm;
+  a.rnorm = rnorm;
+  const bool prod = q.variant == TQ_PROD;
+  if (prod) {
+    hipError_t e;
+    const int64_t batch = n < kWBatch ? n : kWBatch;
+    float* ws = wide_workspace((size_t)batch * q.d + (size_t)batch * (q.d / 32), e);
+    if (!ws) return e;
+    a.res = ws;
+    a.rho2 = ws + (size_t)batch * q.d;
+  }
+  using Fn = void (*)(WArgs);
+#define TQ_WR(F, B) {wide_rotate_kernel<F, B, false>, wide_rotate_kernel<F, B, true>}
+  static const Fn rot[2][4][2] = {{TQ_WR(false, 1), TQ_WR(false, 2), TQ_WR(false, 3), TQ_WR(false, 4)},
+                                  {TQ_WR(true, 1), TQ_WR(true, 2), TQ_WR(true, 3), TQ_WR(true, 4)}};
+#undef TQ_WR
+  const Fn fr = rot[dt == TQ_F32 ? 1 : 0][q.mse_bits - 1][prod ? 1 : 0];
+  const int nct = (q.d + kWC - 1) / kWC;
+  for (int64_t v0 = 0; v0 < n; v0 += kWBatch) {
+    a.v0 = v0;
+    a.nb = n - v0 < kWBatch ? n - v0 : kWBatch;
+    const int64_t nvt = (a.nb + kWV - 1) / kWV;
+    const unsigned grid = (unsigned)((nvt + 7) / 8 * 8 * nct);
+    WArgs a1 = a;
+    a1.x = x;
+    a1.stride = stride;
+    a1.xrow0 = v0;
+    a1.M = q.R;
+    hipLaunchKernelGGL(fr, dim3(grid), dim3(kWThreads), 0, s, a1);
+    if (prod) {
+      WArgs a2 = a;
+      a2.x = a.res;
+      a2.stride = q.d;
+      a2.xrow0 = 0;
+      a2.M = q.S;
+      hipLaunchKernelGGL(wide_sketch_kernel, dim3(grid), dim3(kWThreads), 0, s, a2);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace tqk

@@ -238,6 +238,9 @@ extern "C" int tq_quantize_kv(const tq_quantizer* q, tq_layout layout, tq_dtype 
   if (!aligned16(x) || !aligned16(packed) || !aligned16(norm) || (rnorm && !aligned16(rnorm)))
     return TQ_ERR_MISALIGNED;
   uint16_t* rn = q->variant == TQ_PROD ? rnorm : nullptr;
+  if (tqk::quantize_wide_supported(*q, layout, in_dtype, x, x_stride_elems))
+    return hip_status(tqk::launch_quantize_wide(*q, in_dtype, x, n, x_stride_elems, packed, norm, rn,
+                                                static_cast<hipStream_t>(stream)));
   if (tqk::quantize_mfma_supported(*q, in_dtype, x, x_stride_elems))
     return hip_status(tqk::launch_quantize_mfma(*q, layout, in_dtype, x, n, x_stride_elems, packed, norm, rn,
                                                 static_cast<hipStream_t>(stream)));

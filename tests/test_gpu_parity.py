@@ -94,6 +94,14 @@ QUANT_CASES = [
     (96, 2, True, "keys", 1000, "bf16"),
     (96, 3, False, "values", 999, "bf16"),
     (96, 4, True, "values", 301, "bf16"),
+    # wide vectors (more than 128 channels, key layout) on the GEMM-shaped
+    # matrix-core passes: several 128-vector tiles and a ragged tail,
+    # partial 128-channel tiles (160, 320), both input types
+    (256, 2, True, "keys", 300, "bf16"),
+    (1536, 3, True, "keys", 700, "f32"),
+    (320, 1, False, "keys", 257, "f32"),
+    (160, 4, True, "keys", 130, "bf16"),
+    (384, 3, False, "keys", 129, "bf16"),
 ]
 
 
@@ -118,6 +126,23 @@ def test_quantize_matches_oracle(d, B, prod, lay, N, dt):
     n_round = -(-N // tile) * tile
     pidx, pz = otq.unpack(words, n_round, d, B, prod, lay)
     assert not pidx[N:].any() and (pz is None or not pz[N:].any())
+
+
+def test_quantize_wide_across_batches():
+    # wide vectors are quantised in batches of 65536 (the residual workspace
+    # holds one batch): 65536 + 300 vectors of 256 channels cross a batch
+    # boundary mid-key-tile free (65536 is a multiple of 128); every code,
+    # sign and norm against the oracle
+    d, B, N = 256, 2, 65536 + 300
+    print(f"quantize wide d={d} B={B} N={N} across batches", flush=True)
+    gq = GpuQuantizer(d, B, True, seed=29)
+    x = synth.unit_gaussian(N, d, 31) * synth.rng(32, 0).lognormal(0, 0.5, (N, 1)).astype(np.float32)
+    x[65535] = 0.0  # a zero vector at the end of the first batch
+    packed, norm, rnorm = gpu_quantize(gq, torch_dev(x), N, d, tq.TQ_LAYOUT_KEYS, tq.TQ_F32)
+    torch.cuda.synchronize()
+    idx, z = otq.unpack(to_np_u32(packed), N, d, B, True, "keys")
+    codes = otq.quantize(x.astype(np.float64), gq.oq)
+    assert_codes_match(idx, z, to_np_f16(norm), to_np_f16(rnorm), codes, gq.oq)
 
 
 APPEND_CASES = [
