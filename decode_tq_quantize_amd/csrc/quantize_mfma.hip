@@ -738,52 +738,57 @@ __device__ __forceinline__ float wide_gemm(const WArgs& a, int64_t lv0, int c0, 
       dst[m][1] = p[1];
     }
   };
-  load_x(0);
-  if (wave_on) load_m(0, mr);
-  stage(0);
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const int cur = ks & 1;
+  // one step: this step's products from LDS buffer ks % 2 and the rows in
+  // `cur` while the next step's inputs and rows load (into `nxt`); the loop
+  // runs two steps per iteration so that the two row buffers swap roles
+  // without copies
+  auto step = [&](int ks, float4 (&cur)[2][2], float4 (&nxt)[2][2]) __attribute__((always_inline)) {
+    const int buf = ks & 1;
     const bool more = ks + 1 < nks;
     if (more) {
       load_x(ks + 1);
-      if (wave_on) load_m(ks + 1, mn);
+      if (wave_on) load_m(ks + 1, nxt);
     }
     if (wave_on) {
       bf16x8 ah[2], al[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         uint32_t h[4], l[4];
-        split_bf16(mr[m][0].x, mr[m][0].y, h[0], l[0]);
-        split_bf16(mr[m][0].z, mr[m][0].w, h[1], l[1]);
-        split_bf16(mr[m][1].x, mr[m][1].y, h[2], l[2]);
-        split_bf16(mr[m][1].z, mr[m][1].w, h[3], l[3]);
+        split_bf16(cur[m][0].x, cur[m][0].y, h[0], l[0]);
+        split_bf16(cur[m][0].z, cur[m][0].w, h[1], l[1]);
+        split_bf16(cur[m][1].x, cur[m][1].y, h[2], l[2]);
+        split_bf16(cur[m][1].z, cur[m][1].w, h[3], l[3]);
         ah[m] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
         al[m] = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&xs[cur][0][16 * nt + nl][16 * q]);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&xs[buf][0][16 * nt + nl][16 * q]);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           acc[m][nt] = mfma_bf16(ah[m], bh, acc[m][nt]);
           acc[m][nt] = mfma_bf16(al[m], bh, acc[m][nt]);
         }
         if constexpr (F32IN) {
-          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&xs[cur][1][16 * nt + nl][16 * q]);
+          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&xs[buf][1][16 * nt + nl][16 * q]);
 #pragma unroll
           for (int m = 0; m < 2; ++m) acc[m][nt] = mfma_bf16(ah[m], bl, acc[m][nt]);
         }
       }
     }
-    if (more) stage(cur ^ 1);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      mr[m][0] = mn[m][0];
-      mr[m][1] = mn[m][1];
-    }
+    if (more) stage(buf ^ 1);
     __syncthreads();
+  };
+  load_x(0);
+  if (wave_on) load_m(0, mr);
+  stage(0);
+  __syncthreads();
+  int ks = 0;
+  for (; ks + 1 < nks; ks += 2) {
+    step(ks, mr, mn);
+    step(ks + 1, mn, mr);
   }
+  if (ks < nks) step(ks, mr, mn);
   return ss;
 }
 
