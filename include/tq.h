@@ -185,7 +185,13 @@ int tq_fold_qjl(const tq_quantizer* q, float* SR, void* stream);
  * Outputs (device): `packed` (tq_packed_bytes bytes, layout as above; it must
  * start at a tile boundary of the cache it belongs to), `norm` [n] half,
  * `rnorm` [n] half (PROD only; NULL for MSE). TQ_LAYOUT_VALUES needs d <= 256.
- * Contractions accumulate in fp32. */
+ * Contractions accumulate in fp32 (products of bf16 high/low parts on the
+ * matrix cores, about 2^-17 of the terms' magnitudes). PROD keys of d > 128
+ * run in batches of 65536 vectors through a device workspace of
+ * 65536 * (d + d / 32) floats that the library allocates on a call's first
+ * use on a device (so that call may block and return TQ_ERR_HIP if the
+ * allocation fails) and keeps until the process ends; such calls that
+ * overlap on one device (different streams or threads) race on it. */
 int tq_quantize_kv(const tq_quantizer* q, tq_layout layout, tq_dtype in_dtype,
                    const void* x, int64_t n, int64_t x_stride_elems, void* packed,
                    uint16_t* norm, uint16_t* rnorm, void* stream);
@@ -201,7 +207,7 @@ int tq_quantize_kv(const tq_quantizer* q, tq_layout layout, tq_dtype in_dtype,
  * are the cache's own arrays over its cache_rows rows (packed holds
  * tq_packed_bytes(d, bits, variant, layout, cache_rows) bytes and starts at
  * a tile boundary). A key row owns its words and is overwritten whole; a
- * value row owns one bit of each word of its 32-row tile, and only those
+ * value row owns one bit of each word of its tile, and only those
  * bits change (set or cleared atomically), so appends into rows that share a
  * tile may run in one call. Other rows are left as they are. Errors as for
  * tq_quantize_kv, plus INVALID_ARG for cache_rows <= 0 or a null `rows`
