@@ -601,10 +601,15 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
   if constexpr (BF16IN) {
     // two tiles' inputs in flight (the two buffers alternate, nothing is copied)
     load_tile(xb, (int64_t)blockIdx.x + gridDim.x);
-    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += 2 * (int64_t)gridDim.x) {
+    // (both tiles of an iteration unconditional, the odd last one after the
+    // loop: a conditional second tile makes the loop head wait for every
+    // load in flight, the other buffer's prefetch included)
+    int64_t tile = blockIdx.x;
+    for (; tile + gridDim.x < a.ntiles; tile += 2 * (int64_t)gridDim.x) {
       body(tile, xa, tile + 2 * (int64_t)gridDim.x);
-      if (tile + gridDim.x < a.ntiles) body(tile + gridDim.x, xb, tile + 3 * (int64_t)gridDim.x);
+      body(tile + gridDim.x, xb, tile + 3 * (int64_t)gridDim.x);
     }
+    if (tile < a.ntiles) body(tile, xa, tile + 2 * (int64_t)gridDim.x);
   } else {
     for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) body(tile, xa, tile + gridDim.x);
   }
