@@ -1738,7 +1738,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     for (int gv = 0; gv < NV; ++gv) e_w[gv] = -60;
     // the accumulators' references (the same in both waves): per head, and
     // per value group
-    float m_acc[kHT] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // (per lane: the reference of the head of its operand row, h_row, and of
+    // its accumulator rows, hl)
+    float macc_row = -INFINITY, macc_out = -INFINITY;
     int e_acc[NV];
 #pragma unroll
     for (int gv = 0; gv < NV; ++gv) e_acc[gv] = -60;
@@ -1889,40 +1891,33 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const v4i hi = *reinterpret_cast<const v4i*>(row + 64 + 16 * (lane >> 4));
         aw[gv] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      float ms[2][kHT];
+      // the two waves' references, each lane reading those of its operand
+      // row's head and of its accumulator rows' head (the value-norm
+      // exponents are per group)
+      const float mr0 = xm[par][0][h_row], mr1 = xm[par][1][h_row];
+      const float mo0 = xm[par][0][hl], mo1 = xm[par][1][hl];
       int es[2][NV];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int h = 0; h < kHT; ++h) ms[s][h] = xm[par][s][h];
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int gv = 0; gv < NV; ++gv) es[s][gv] = xe[par][s][gv];
-      }
       // the accumulators' references: set at a head's first reported maximum
       // (its accumulator rows are still zero then); raised, with a rescale,
       // only when a wave's reference runs more than kMaxShift above them
-      bool raise = false;
-#pragma unroll
-      for (int h = 0; h < kHT; ++h) {
-        const float mh = fmaxf(ms[0][h], ms[1][h]);
-        if (m_acc[h] == -INFINITY) m_acc[h] = mh;
-        raise |= mh - m_acc[h] > (float)kMaxShift;
-      }
+      const float mh_row = fmaxf(mr0, mr1), mh_out = fmaxf(mo0, mo1);
+      if (macc_row == -INFINITY) macc_row = mh_row;
+      if (macc_out == -INFINITY) macc_out = mh_out;
+      bool over = mh_row - macc_row > (float)kMaxShift;  // (every head is some lane's operand-row head)
 #pragma unroll
       for (int gv = 0; gv < NV; ++gv) {
         const int eh = max(es[0][gv], es[1][gv]);
         if (e_acc[gv] == -60) e_acc[gv] = eh;
-        raise |= eh - e_acc[gv] > kMaxShift;
+        over |= eh - e_acc[gv] > kMaxShift;
       }
-      if (raise) {  // (wave-uniform) move the references up to the reported ones
-        float f[kHT];
-#pragma unroll
-        for (int h = 0; h < kHT; ++h) {
-          const float mh = fmaxf(ms[0][h], ms[1][h]);
-          f[h] = m_acc[h] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_acc[h] - fmaxf(mh, m_acc[h]));
-          m_acc[h] = fmaxf(mh, m_acc[h]);
-        }
-        const float fl = hl == 0 ? f[0] : (hl == 1 ? f[1] : (hl == 2 ? f[2] : f[3]));
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {  // (wave-uniform) move the references up to the reported ones
+        const float fl = macc_out == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(macc_out - fmaxf(mh_out, macc_out));
+        macc_out = fmaxf(mh_out, macc_out);
+        macc_row = fmaxf(mh_row, macc_row);
         float fe[NV];
 #pragma unroll
         for (int gv = 0; gv < NV; ++gv) {
@@ -1942,14 +1937,11 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       // the wave that wrote its columns
       int sa[NV];
       {
-        const float m0 = h_row == 0 ? ms[0][0] : (h_row == 1 ? ms[0][1] : (h_row == 2 ? ms[0][2] : ms[0][3]));
-        const float m1 = h_row == 0 ? ms[1][0] : (h_row == 1 ? ms[1][1] : (h_row == 2 ? ms[1][2] : ms[1][3]));
-        const float msrc = src_w ? m1 : m0;
-        const float macc = h_row == 0 ? m_acc[0] : (h_row == 1 ? m_acc[1] : (h_row == 2 ? m_acc[2] : m_acc[3]));
+        const float msrc = src_w ? mr1 : mr0;
         // (a source without any weight yet, or a masked head, has all-zero
         // digits: any scale will do; one far below the reference has
         // negligible weights, and its scale is clamped into E8M0's range)
-        const int dm = (msrc == -INFINITY || macc == -INFINITY) ? 0 : (int)(msrc - macc);
+        const int dm = (msrc == -INFINITY || macc_row == -INFINITY) ? 0 : (int)(msrc - macc_row);
 #pragma unroll
         for (int gv = 0; gv < NV; ++gv)
           sa[gv] = min(max(127 - 4 * dg_row + dm + (src_w ? es[1][gv] : es[0][gv]) - e_acc[gv], 1), 254);
@@ -1988,7 +1980,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     }
     __syncthreads();
     if (hl < nh) {
-      const float macc = hl == 0 ? m_acc[0] : (hl == 1 ? m_acc[1] : (hl == 2 ? m_acc[2] : m_acc[3]));
+      const float macc = macc_out;
       float* part = a.partial + (((int64_t)b * a.Hq + h0 + hl) * a.splits + split) * (kD + 2);
       const bool none = macc == -INFINITY;
 #pragma unroll
