@@ -12,10 +12,12 @@
 // matrix, whose diagonal is |x|^2. fp32 inputs use v_mfma_f32_16x16x4_f32
 // with R in fp32. The rotated vector comes out with lane l holding
 // coordinates 32 w + 16 m + 4 (l / 16) + r (m = 0, 1; r = 0..3) of vector
-// l % 16 of a 16-vector half. Every contraction over the d input coordinates
-// runs in d / 32 steps of 32, lane group q (= lane / 16) supplying the d / 4
-// consecutive coordinates d q / 4 .. d q / 4 + d / 4 - 1 (8 per step) on both
-// operands. The interval index is found there by binary
+// l % 16 of a 16-vector half. The rotation's contraction over the d input
+// coordinates runs in d / 32 steps of 32, lane group q (= lane / 16)
+// supplying coordinates 32 k + 8 q .. + 7 at step k on both operands (fp32:
+// steps of 4, coordinate 16 j + 4 q + e at step 4 j + e), so the four lanes
+// of a vector row load one contiguous 64-byte segment per instruction. The
+// interval index is found there by binary
 // search over the thresholds, the residual's bf16 parts go through LDS to
 // the operand layout of S r~ (bf16 matrix cores, S in LDS), and the code
 // and sign bits are packed straight from wave ballots of the compares into
@@ -73,21 +75,12 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t x, uint64_t mask) {
   return r;
 }
 
-// Words of two 16-bit halves to lanes: lane l0 of `a` gets the low halves
-// of x (low) and y (high), lane l1 of `b` their high halves. The packs run
-// on the scalar unit, whose reads of VALU-written SGPRs wait in hardware.
-__device__ __forceinline__ void halves_to_lanes(uint32_t& a, uint32_t& b, uint32_t x, uint32_t y, int l0, int l1) {
-  uint32_t t0, t1;
-  asm("s_pack_ll_b32_b16 %2, %4, %5\n\ts_pack_hh_b32_b16 %3, %4, %5\n\tv_writelane_b32 %0, %2, %6\n\tv_writelane_b32 %1, %3, %7"
-      : "+v"(a), "+v"(b), "=&s"(t0), "=&s"(t1)
-      : "s"(x), "s"(y), "i"(l0), "i"(l1));
-}
-// The same with both lanes in one register.
-__device__ __forceinline__ void halves_to_lanes(uint32_t& a, uint32_t x, uint32_t y, int l0, int l1) {
-  uint32_t t0, t1;
-  asm("s_pack_ll_b32_b16 %1, %3, %4\n\ts_pack_hh_b32_b16 %2, %3, %4\n\tv_writelane_b32 %0, %1, %5\n\tv_writelane_b32 %0, %2, %6"
-      : "+v"(a), "=&s"(t0), "=&s"(t1)
-      : "s"(x), "s"(y), "i"(l0), "i"(l1));
+// v_writelane_b32 as the compiler's own intrinsic (its hazard checks then
+// see the instruction; inline asm would be fenced with wait states)
+extern "C" __device__ int tq_writelane_i32(int x, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+// Lane `l` of v takes the uniform value x.
+__device__ __forceinline__ void write_lane(uint32_t& v, uint32_t x, int l) {
+  v = (uint32_t)tq_writelane_i32((int)x, l, (int)v);
 }
 
 __device__ __forceinline__ v4f mfma_f32(float a, float b, v4f c) {
@@ -115,27 +108,29 @@ __device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uin
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, bf16x2));
 }
 
-// Rows 32 w + 16 m + (lane % 16), columns D (lane / 16) / 4 .. + D / 4 - 1
-// of the D x D matrix M.
-template <int D>
+// Rows 32 w + 16 m + (lane % 16) of the D x D matrix M, at the columns that
+// lane group q = lane / 16 supplies to the contraction: A[m][8 k + e] =
+// column 32 k + 8 q + e (bf16 inputs), A[m][4 j + e] = column 16 j + 4 q + e
+// (fp32 inputs).
+template <int D, bool BF16IN>
 __device__ __forceinline__ void load_rows(const float* __restrict__ M, int w, int lane, float (&A)[2][D / 4]) {
+  const int q = lane >> 4;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const float4* p = reinterpret_cast<const float4*>(M + (int64_t)(32 * w + 16 * m + (lane & 15)) * D +
-                                                      (D / 4) * (lane >> 4));
+    const float4* p = reinterpret_cast<const float4*>(M + (int64_t)(32 * w + 16 * m + (lane & 15)) * D);
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) {
-      const float4 v = p[k];
-      A[m][4 * k] = v.x;
-      A[m][4 * k + 1] = v.y;
-      A[m][4 * k + 2] = v.z;
-      A[m][4 * k + 3] = v.w;
+    for (int i = 0; i < D / 16; ++i) {
+      const float4 v = p[BF16IN ? 8 * (i >> 1) + 2 * q + (i & 1) : 4 * i + q];
+      A[m][4 * i] = v.x;
+      A[m][4 * i + 1] = v.y;
+      A[m][4 * i + 2] = v.z;
+      A[m][4 * i + 3] = v.w;
     }
   }
 }
 
-// Raw input of one lane: coordinates D q / 4 .. D q / 4 + D / 4 - 1 of one
-// vector row.
+// Raw input of one lane, lane group q, from one vector row: coordinates
+// 32 k + 8 q .. + 7 in w[k] (bf16), 16 j + 4 q .. + 3 in f[j] (fp32).
 template <int D, bool BF16IN>
 struct XIn;
 template <int D>
@@ -148,15 +143,15 @@ struct XIn<D, false> {
 };
 template <int D>
 __device__ __forceinline__ void load_in(XIn<D, true>& r, const QmArgs& a, int64_t v, int q) {
-  const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + v * a.stride + (D / 4) * q);
+  const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + v * a.stride) + q;
 #pragma unroll
-  for (int k = 0; k < D / 32; ++k) r.w[k] = p[k];
+  for (int k = 0; k < D / 32; ++k) r.w[k] = p[4 * k];
 }
 template <int D>
 __device__ __forceinline__ void load_in(XIn<D, false>& r, const QmArgs& a, int64_t v, int q) {
-  const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + v * a.stride + (D / 4) * q);
+  const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + v * a.stride) + q;
 #pragma unroll
-  for (int k = 0; k < D / 16; ++k) r.f[k] = p[k];
+  for (int k = 0; k < D / 16; ++k) r.f[k] = p[4 * k];
 }
 
 // Lane exchanges with lane l ^ 16 and l ^ 32 (v_permlane16/32_swap: with
@@ -249,7 +244,7 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
   // <= 2^-18 |R| elementwise)
   float AR[2][D / 4];
   bf16x8 RH[2][NG], RL[2][NG];
-  load_rows<D>(a.R, w, lane, AR);
+  load_rows<D, BF16IN>(a.R, w, lane, AR);
   if constexpr (BF16IN) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -283,7 +278,7 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
 #pragma unroll
   for (int t = 0; t < L; ++t) {
     cv[t] = a.cent[t];
-    asm volatile("" : "+v"(cv[t]));
+    if constexpr (PROD) asm volatile("" : "+v"(cv[t]));
   }
   __syncthreads();
 
@@ -301,6 +296,19 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) load_in<D>(dst[nt], a, min(col_vec(t, nt, nl), a.n - 1), q);
   };
+  // (value layout) word offset of this lane's pair word within the wave's
+  // 32 P words, and the byte selector of the join (sources y, x)
+  int woff[KEYS ? 1 : (16 * P + 31) / 32];
+  uint32_t wsel = 0u;
+  if constexpr (!KEYS) {
+#pragma unroll
+    for (int i = 0; i < (16 * P + 31) / 32; ++i) {
+      const int k = 32 * i + (lane & 31), p = k % P, t = k / P;
+      const int r = t & 3, h = (t >> 2) & 1, m = t >> 3;
+      woff[i] = (16 * m + 4 * (2 * h + (lane >> 5)) + r) * P + p;
+    }
+    wsel = lane < 32 ? 0x05040100u : 0x07060302u;
+  }
   const int64_t nround = (a.n + tqk::kKeysTile - 1) / tqk::kKeysTile * tqk::kKeysTile;
   // one tile, whose inputs are in cur; once the rotation has read them, cur
   // takes the inputs of tile tnext
@@ -372,25 +380,28 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
     // bits have bit 16 q + nl = coordinate 32 w + 16 m + 4 q + r of vector
     // 16 nt + nl.
     bool valid[2], live[2];
-    float inv[2];
+    float inv[2], bias[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       valid[nt] = col_vec(tile, nt, nl) < a.n;
       live[nt] = valid[nt] & (nrm[nt] > 0.f);
       inv[nt] = live[nt] ? __builtin_amdgcn_rcpf(nrm[nt]) : 0.f;
+      bias[nt] = valid[nt] ? (live[nt] ? 0.f : th[L / 2 - 1]) : -INFINITY;
       if (w == 0 && q == 0 && valid[nt]) a.norm[col_vec(tile, nt, nl)] = tqd::f32_to_half_bits(nrm[nt]);
     }
     float res[2][2][4];
     float r2[2] = {0.f, 0.f};
     // the search bits of one coordinate (most significant first), and the
-    // residual
+    // residual. u = acc / |x| + bias: bias 0 for live vectors; for a vector
+    // of norm 0 (inv 0) the threshold below the middle, which lands on
+    // index L / 2; for padding (inv 0) -inf, index 0 (all bits clear). So
+    // the code ballots need no masks; the residuals of those vectors are
+    // not used (their signs are masked, their residual norm written as 0).
     auto code_bits = [&](int nt, int m, int r, bool (&bt)[B]) __attribute__((always_inline)) {
-      const float u = acc[nt][m][r] * inv[nt];
+      const float u = fmaf(acc[nt][m][r], inv[nt], bias[nt]);
       interval_bits<B, B - 1>(u, th, bt);
-      // (bitwise forms, not selects: the compiler would otherwise branch
-      // around the search for lanes that do not need it)
       if constexpr (PROD) {
-        const float rr = (u - pick<L, 0, 1>(cv, bt)) * (float)live[nt];
+        const float rr = u - pick<L, 0, 1>(cv, bt);
         res[nt][m][r] = rr;
         r2[nt] = fmaf(rr, rr, r2[nt]);
       }
@@ -405,25 +416,23 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
       return or_q(((acc8 & 0xfu) | ((acc8 & 0xf0u) << 12)) << (4 * q));
     };
     // words (coordinate j, plane p) of the value layout: bit i = the vector
-    // of column i % 16 of half i / 16; the wave's coordinates are 32 P
-    // contiguous words, word
-    // (j - 32 w) P + p, held by lane (word % 64) of ow[word / 64]. Bits
-    // 16 q .. 16 q + 15 of the two halves' ballots are the low and high
-    // halves of the word of coordinate 32 w + 16 m + 4 q + r.
-    constexpr int NW = (32 * P + 63) / 64;
-    uint32_t ow[NW];
+    // of column i % 16 of half i / 16. Bits 16 q .. 16 q + 15 of the two
+    // halves' ballots are the low and high halves of the word of coordinate
+    // 32 w + 16 m + 4 q + r, so the low (high) 32 bits of a ballot pair give
+    // the words of lane groups 2 h and 2 h + 1 (h = 0 (1)): pair k =
+    // ((2 m + h) 4 + r) P + p puts the first half-ballot in lane k % 32 and
+    // the second in lane k % 32 + 32 of ow[k / 32], as they are; the stores
+    // join them.
+    constexpr int NR = (16 * P + 31) / 32;
+    uint32_t ow[NR];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) ow[i] = 0u;
+    for (int i = 0; i < NR; ++i) ow[i] = 0u;
     auto value_words = [&](int m, int r, int p, uint64_t m0, uint64_t m1) __attribute__((always_inline)) {
-      const int i = (16 * m + r) * P + p;  // + 4 q P for lane group q
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {  // lane groups 2 h and 2 h + 1
-        const int i0 = i + 8 * h * P, i1 = i0 + 4 * P;
-        const uint32_t x = (uint32_t)(m0 >> (32 * h)), y = (uint32_t)(m1 >> (32 * h));
-        if ((i0 >> 6) == (i1 >> 6))
-          halves_to_lanes(ow[i0 >> 6], x, y, i0 & 63, i1 & 63);
-        else
-          halves_to_lanes(ow[i0 >> 6], ow[i1 >> 6], x, y, i0 & 63, i1 & 63);
+      for (int h = 0; h < 2; ++h) {
+        const int k = ((2 * m + h) * 4 + r) * P + p;
+        write_lane(ow[k >> 5], (uint32_t)(m0 >> (32 * h)), k & 31);
+        write_lane(ow[k >> 5], (uint32_t)(m1 >> (32 * h)), (k & 31) + 32);
       }
     };
     // ballots of the compares themselves (a ballot of a combined flag, or a
@@ -448,10 +457,7 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
             bool bt[B];
             code_bits(nt, m, r, bt);
 #pragma unroll
-            for (int p = 0; p < B; ++p) {
-              const uint64_t c = __builtin_amdgcn_ballot_w64(bt[B - 1 - p]);
-              acc8[p] = shift_in(acc8[p], (c & lm[nt]) | (p == B - 1 ? (vm[nt] & ~lm[nt]) : 0ull));
-            }
+            for (int p = 0; p < B; ++p) acc8[p] = shift_in(acc8[p], __builtin_amdgcn_ballot_w64(bt[B - 1 - p]));
           }
 #pragma unroll
         for (int p = 0; p < B; ++p) kw[nt][p] = key_word(acc8[p]);
@@ -467,10 +473,7 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
             bool bt[B];
             code_bits(nt, m, r, bt);
 #pragma unroll
-            for (int p = 0; p < B; ++p) {
-              const uint64_t c = __builtin_amdgcn_ballot_w64(bt[B - 1 - p]);
-              pm[nt][p] = (c & lm[nt]) | (p == B - 1 ? (vm[nt] & ~lm[nt]) : 0ull);
-            }
+            for (int p = 0; p < B; ++p) pm[nt][p] = __builtin_amdgcn_ballot_w64(bt[B - 1 - p]);
           }
 #pragma unroll
           for (int p = 0; p < B; ++p) value_words(m, r, p, pm[0][p], pm[1][p]);
@@ -549,7 +552,7 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const float rs = sum_q(r2[nt]);
-        if (q == 0) rho_part[w][16 * nt + nl] = rs;
+        if (q == 0) rho_part[w][16 * nt + nl] = live[nt] ? rs : 0.f;
       }
       __syncthreads();
       // residual norms (one lane per vector)
@@ -589,10 +592,16 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
         }
       }
     } else {
+      // after the swap every lane of a pair holds its two half-ballots x
+      // (first) and y; the low lane stores x.lo | y.lo << 16, the high one
+      // x.hi | y.hi << 16
       uint32_t* dst = a.packed + (tile * D + 32 * w) * P;
 #pragma unroll
-      for (int i = 0; i < NW; ++i)
-        if (64 * i + lane < 32 * P) dst[64 * i + lane] = ow[i];
+      for (int i = 0; i < NR; ++i) {
+        const auto xy = __builtin_amdgcn_permlane32_swap(ow[i], ow[i], false, false);
+        const uint32_t word = __builtin_amdgcn_perm(xy[1], xy[0], wsel);
+        if (32 * i + (lane & 31) < 16 * P) dst[woff[i]] = word;
+      }
     }
     if constexpr (PROD) __syncthreads();  // rq (and rho_part in it) is rewritten by the next tile
   };
