@@ -128,6 +128,50 @@ def test_quantize_matches_oracle(d, B, prod, lay, N, dt):
     assert not pidx[N:].any() and (pz is None or not pz[N:].any())
 
 
+@pytest.mark.parametrize("d,B,prod,lay,N,dt", [
+    (128, 2, True, "keys", 300, "bf16"),
+    (128, 3, False, "values", 200, "bf16"),
+    (64, 3, True, "keys", 97, "f32"),
+    (256, 2, True, "keys", 150, "bf16"),
+    (256, 3, False, "values", 70, "f32"),
+])
+def test_quantize_asymmetric_codebook(d, B, prod, lay, N, dt):
+    """A codebook whose middle threshold is not 0 (sorted, as the library
+    accepts): zero vectors still get index L / 2 (and rho 0, signs +),
+    padding still all-zero bits, every path (narrow and wide matrix-core
+    kernels, the vector-unit kernel)."""
+    print(f"asymmetric codebook d={d} B={B} prod={prod} {lay} N={N} {dt}", flush=True)
+    gq = GpuQuantizer(d, B, prod, seed=d + 7 * B)
+    L = 1 << B
+    cent = np.array(gq.q.centroids[:L], np.float64) + 0.35 / np.sqrt(d)
+    thr = 0.5 * (cent[:-1] + cent[1:])
+    assert thr[L // 2 - 1] > 0.0  # the middle threshold is off zero
+    cent32, thr32 = cent.astype(np.float32), thr.astype(np.float32)
+    for i in range(L):
+        gq.q.centroids[i] = float(cent32[i])
+    for i in range(L - 1):
+        gq.q.thresholds[i] = float(thr32[i])
+    gq.oq = otq.make_quantizer(d, B, prod, gq.R32, gq.S32, cent32.astype(np.float64), thr32.astype(np.float64))
+    x = synth.unit_gaussian(N, d, 21) * synth.rng(22, 0).lognormal(0, 0.5, (N, 1)).astype(np.float32)
+    for z in (0, 5, 40, N - 1):  # zero vectors in the first tile, later tiles and the ragged tail
+        x[z] = 0.0
+    if dt == "bf16":
+        x = synth.bf16_bits_to_f32(synth.to_bf16_bits(x))
+    layout = tq.TQ_LAYOUT_KEYS if lay == "keys" else tq.TQ_LAYOUT_VALUES
+    x_t = torch_dev(x, torch.bfloat16 if dt == "bf16" else torch.float32)
+    packed, norm, rnorm = gpu_quantize(gq, x_t, N, d, layout, tq.TQ_BF16 if dt == "bf16" else tq.TQ_F32)
+    torch.cuda.synchronize()
+    words = to_np_u32(packed)
+    idx, z = otq.unpack(words, N, d, B, prod, lay)
+    codes = otq.quantize(x.astype(np.float64), gq.oq)
+    assert (codes.idx[[0, 5, 40, N - 1]] == L // 2).all()
+    assert_codes_match(idx, z, to_np_f16(norm), to_np_f16(rnorm), codes, gq.oq)
+    tile = otq.KEYS_TILE if lay == "keys" else otq.VALUES_BLOCK
+    n_round = -(-N // tile) * tile
+    pidx, pz = otq.unpack(words, n_round, d, B, prod, lay)
+    assert not pidx[N:].any() and (pz is None or not pz[N:].any())
+
+
 def test_quantize_wide_across_batches():
     # wide vectors are quantised in batches of 65536 (the residual workspace
     # holds one batch): 65536 + 300 vectors of 256 channels cross a batch
