@@ -437,7 +437,8 @@ __global__ __launch_bounds__(2 * D, 2) void quantize_mfma_kernel(QmArgs a) {
     };
     // ballots of the compares themselves (a ballot of a combined flag, or a
     // per-lane combination, makes the compiler round-trip it through a
-    // vector register); zero and padding vectors are applied to the masks
+    // vector register); the sign plane applies zero and padding vectors to
+    // its masks with these
     uint64_t vm[2], lm[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
