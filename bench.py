@@ -262,8 +262,9 @@ def traffic_summary(fetch_dir, write_dir):
 
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the
     same counter reads for the 256 MiB device copy --calibrate-copy runs
-    first. The median over a kernel's dispatches is kept (the one quality call
-    that also writes the score matrix is an outlier).
+    first (the first copy dispatch of the run: later copies, of other sizes,
+    are the inputs' set-up). The median over a kernel's dispatches is kept
+    (the one quality call that also writes the score matrix is an outlier).
     """
     import collections
     import csv
@@ -278,12 +279,12 @@ def traffic_summary(fetch_dir, write_dir):
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] == counter:
                     per[r["Kernel_Name"]][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
-        return {k: list(v.values()) for k, v in per.items()}
+        # the calibration copy: the run's first copy dispatch
+        copies = [(d, v) for k, dv in per.items() if "copy" in k.lower() for d, v in dv.items()]
+        return {k: list(v.values()) for k, v in per.items()}, min(copies)[1]
 
-    F, W = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    (F, fcopy), (W, wcopy) = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
     copy_kib = (256 << 20) / 1024
-    fcopy = max(max(v) for k, v in F.items() if "copy" in k.lower())
-    wcopy = max(max(v) for k, v in W.items() if "copy" in k.lower())
     ff, wf = copy_kib / fcopy, copy_kib / wcopy
 
     def short(k):
