@@ -12,30 +12,33 @@
 // prod_{p in S} s_p = 2 (xor_{p in S} b_p) - 1. Every score term and every
 // value sum is therefore a dot product of real weights with a +-1 vector
 // whose bits are the packed planes (xor-combined). Those products run on the
-// fp8 x fp4 MFMA (v_mfma_f32_16x16x128_f8f6f4):
+// fp8 / fp6 x fp4 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4):
 //  * a 32-bit plane word w becomes four fp4 registers, register r taking bit
 //    4 i + r of w into nibble i with one bit operation: r = 3 gives +-1
-//    (bit select), r = 2, 1, 0 give {0, 2}, {0, 1}, {0, 1/2} (masks), i.e.
-//    u_r + v_r sigma with (u, v) = (0, 1), (1, 1), (1/2, 1/2), (1/4, 1/4);
-//    the real operand is pre-multiplied by 1 / v_r (a power of two) and the
-//    constant part sum a u_r is removed exactly with one more MFMA against
-//    the constant operand 4 u_r;
-//  * the real operand (query coefficients, softmax weights) is split into
-//    fp8 e4m3 digits v = d0 + d1/16 + d2/256 (+ d3/4096 for the queries;
-//    each digit the fp8 rounding of what the previous ones left, scaled up
-//    by 16 so that it stays a normal fp8 number), carried as MFMA rows and
-//    recombined with those weights after the product: about 16 significant
-//    bits for the queries, 12 for the weights, fp32 accumulation.
+//    (bit select); for the value sums r = 2, 1, 0 give {0, 2}, {0, 1},
+//    {0, 1/2} (masks), i.e. u_r + v_r sigma with (u, v) = (0, 1), (1, 1),
+//    (1/2, 1/2), (1/4, 1/4), and the weights are pre-multiplied by 1 / v_r
+//    (a power of two); for the scores r = 0, 1 also take fixed exponent bits
+//    ({4, 6}, {2, 4}, {0, 2}: every plane bit weighs 2, expand_key_bits);
+//    the constant part is removed exactly with MFMAs against constant
+//    operands;
+//  * the softmax weights are split into fp8 e4m3 digits v = d0 + d1/16 +
+//    d2/256 (each the fp8 rounding of what the previous ones left, scaled up
+//    by 16 so that it stays a normal fp8 number), about 12 significant bits;
+//    the query coefficients into four fp6 e2m3 digits per 32-channel block
+//    with a per-block E8M0 scale (write_block_operands), error at most 2^-20
+//    of the block's largest; digits are MFMA rows, fp32 accumulation.
 // Rows of every MFMA are (query head, digit) = 4 x 4; columns are 16 tokens
 // (scores) or 16 value coordinates (value sums).
 //
-// Operand layouts used (measured on gfx950 for the mixed fp8 x fp4 form):
+// Operand layouts used (measured on gfx950 for the mixed forms):
 // fp4 operand lane l, nibble p (register p/8) -> k = 32 (l/16) + p; fp8
-// operand lane l, byte p -> k = 16 (l/16) + (p % 16) + 64 (p / 16); D lane l
-// register i -> row 4 (l/16) + i, column l % 16.
+// operand lane l, byte p -> k = 16 (l/16) + (p % 16) + 64 (p / 16); fp6
+// operand lane l, bits 6 p .. 6 p + 5 of 6 registers -> k = 32 (l/16) + p;
+// D lane l register i -> row 4 (l/16) + i, column l % 16.
 //
 // Kernels: qprep builds the query operands of every (batch, KV head, head
-// tile) (q~ = R q, q^ = S q~, power-of-two scales, fp8 digits); decode runs
+// tile) (q~ = R q, q^ = S q~, per-block scales, fp6 digits); decode runs
 // one workgroup (4 waves) per (split of the sequence, head tile of 4 query
 // heads, batch x KV head) over 256-token chunks: each wave scores 64 tokens,
 // the chunk maximum is exchanged through LDS, each wave writes the fp8 digits
@@ -70,7 +73,7 @@ constexpr int kMaxCombineSplits = 4096;
 constexpr int kCombThreads = 256;
 constexpr int kJSlice = 16;                // value channels per combine workgroup
 constexpr int kJSlices = kD / kJSlice;
-constexpr int kRowSlice = 16;              // query-transform rows per workgroup
+constexpr int kRowSlice = 32;              // query-transform rows per workgroup (one K block of the score products)
 
 struct KGroup {
   const uint32_t* packed;
@@ -171,6 +174,32 @@ __device__ __forceinline__ v8i const_operand() {
   return v8i{0x22222222, 0x44444444, 0x66666666, 0, 0, 0, 0, 0};
 }
 
+// Key planes for the score products: every plane register carries 2 b plus
+// an offset o_r = 4, 2, 0 (fp4 pairs {4, 6}, {2, 4}, {0, 2}: an OR of fixed
+// exponent bits, no shift), register 3 the sign +-1 as in expand_bits. With
+// the same weight 2 in every register the query operand needs no per-register
+// factor, so the 32 entries of a block share one magnitude range.
+// (w & m) | c in one VALU instruction (the VOP3 form takes one scalar and
+// one vector constant: the compiler otherwise splits it in two)
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(m), "v"(c));
+  return r;
+}
+__device__ __forceinline__ v8i expand_key_bits(uint32_t w) {
+  v8i r;
+  r[0] = (int)and_or(w, 0x11111111u, 0x66666666u);
+  r[1] = (int)and_or(w, 0x22222222u, 0x44444444u);
+  r[2] = (int)(w & 0x44444444u);
+  r[3] = (int)((w & 0x22222222u) | (~w & 0xAAAAAAAAu));
+  r[4] = r[5] = r[6] = r[7] = 0;
+  return r;
+}
+// What expand_key_bits adds beyond 2 b - 1 in registers 0..2, 1 + o_r =
+// 5, 3, 1, as two fp4 operands (4, 2, 1, 0) + (1, 1, 0, 0): 5 has no fp4 code.
+__device__ __forceinline__ v8i key_const_hi() { return v8i{0x66666666, 0x44444444, 0x22222222, 0, 0, 0, 0, 0}; }
+__device__ __forceinline__ v8i key_const_lo() { return v8i{0x22222222, 0x22222222, 0, 0, 0, 0, 0, 0}; }
+
 // 1 / v_r for register r of the fp4 operand.
 __device__ __forceinline__ float inv_v(int r) { return r == 0 ? 4.f : (r == 1 ? 2.f : 1.f); }
 
@@ -184,6 +213,12 @@ __device__ __forceinline__ v4f mfma_fp8_fp4(v8i a, v8i b, v4f c) {
 // (127).
 __device__ __forceinline__ v4f mfma_fp8_fp4_sa(v8i a, v8i b, v4f c, int sa) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, 127);
+}
+// The same with an fp6 e2m3 A operand (six registers: lane l holds K
+// positions 32 (l / 16) + f in bits 6 f .. 6 f + 5, measured on gfx950), at
+// twice the fp8 rate.
+__device__ __forceinline__ v4f mfma_fp6_fp4_sa(v8i a, v8i b, v4f c, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 2, 4, 0, sa, 0, 127);
 }
 // Sum of the four digit rows of a result already weighted by the scales.
 __device__ __forceinline__ float sum4(v4f x) { return (x[0] + x[1]) + (x[2] + x[3]); }
@@ -233,6 +268,21 @@ __device__ __forceinline__ int exponent_of(float x) {
   return x > 0.f ? e : -60;
 }
 
+// fp6 e2m3 (OCP MX: sign, two exponent bits of bias 1, three mantissa bits;
+// magnitudes 0.125 .. 7.5, subnormals below 1) of x, rounded to nearest
+// even, saturating; and the value of such a code.
+__device__ __forceinline__ uint32_t e2m3_of(float x) {
+  const float ax = fabsf(x);
+  const int ep = ax < 2.f ? 1 : (ax < 4.f ? 2 : 3);  // max(exponent field, 1)
+  const int code = min((int)rintf(ldexpf(ax, 4 - ep)) + 8 * (ep - 1), 31);
+  return (uint32_t)code | (x < 0.f ? 32u : 0u);
+}
+__device__ __forceinline__ float e2m3_value(uint32_t c) {
+  const int ef = (int)((c >> 3) & 3), m = (int)(c & 7);
+  const float v = ef == 0 ? 0.125f * (float)m : ldexpf(1.f + 0.125f * (float)m, ef - 1);
+  return (c & 32u) ? -v : v;
+}
+
 // Digits of a real operand: v = d0 + d1 / 16 + d2 / 256 + d3 / 4096, each
 // d_m the fp8 e4m3 rounding of the residual left by the previous digits,
 // scaled by 16 per digit so that every digit stays in the normal fp8 range
@@ -243,6 +293,8 @@ __device__ __forceinline__ int exponent_of(float x) {
 // four new bits), the third rounded to nearest, relative precision about
 // 2^-12 with no bias; their fourth row is zero.
 constexpr float kDigitStep = 16.f;
+// The score operands' fp6 digits step by 32 (write_block_operands).
+constexpr float kScoreDigitStep = 32.f;
 __device__ __forceinline__ float wsum4(v4f x) {
   return (x[0] + x[1] * (1.f / 16.f)) + (x[2] * (1.f / 256.f) + x[3] * (1.f / 4096.f));
 }
@@ -276,28 +328,89 @@ __host__ __device__ constexpr int odd_mask(int B, int t) {
 // tile's 4 heads; the 16 partial sums of a row meet by lane exchanges.
 constexpr int kQtThreads = 256;
 
-// Both transforms in one pass when S R is available: workgroup (key, 16-row
-// slice) forms rows of q~ = R q and q^ = (S R) q and writes the fp8 digit
-// operands of every slot for those coordinates. Operand scales come from
-// bounds that need no other slice: |q~_c| <= |R_c| |q| = |q| (R orthogonal)
-// and |q^_c| <= max_c |(S R)_c| |q|, each with 0.1 % room for rounding.
+// The score operands of every slot over one 32-channel block kb (K
+// positions 32 kb .. 32 kb + 31 of the score products), from the block's
+// q~ (tq[h * tstride + c]) and q^ (hq[h * hstride + c]), c = channel within
+// the block. K position f of a block holds channel 4 (f % 8) + f / 8 (the
+// key operand's bit order, expand_key_bits). Per (slot, head) the block's
+// values are scaled by a power of two that puts the largest in [1, 2) and
+// split into four fp6 e2m3 digits, each carrying the rounding of the ones
+// before it times 32 (a digit below 2 is exact to 1/16 in the subnormal and
+// first binades, so every digit stays at most 2 and adds 5 bits; error at
+// most 2^-20 of the block's largest); lane 16 kb + 4 h + m of the slot's
+// 64 x 8 dwords holds digit m of head h (bits 6 f .. 6 f + 5 of dwords 0..5)
+// and, in dword 6, the E8M0 scale that undoes both (the slot's other lanes
+// are written by the other blocks' workgroups).
+__device__ __forceinline__ void write_block_operands(const Args& a, int key, int kb, int gsl, const float* tq, int tstride,
+                                                     const float* hq, int hstride,
+                                                     uint8_t (&codes)[kMaxSlots][kHT][4][32], int (&escl)[kMaxSlots][kHT]) {
+  const int tid = threadIdx.x, nslots = a.nslots;
+  // unit (slot, head, f): the 32 positions of a (slot, head) are 32
+  // consecutive lanes of one wave
+  for (int unit = tid; unit < nslots * kHT * 32; unit += kQtThreads) {
+    const int f = unit & 31, h = (unit >> 5) & 3, s2 = unit >> 7;
+    const Slot sl = slot_of(a, s2);
+    const int c = 4 * (f & 7) + (f >> 3);
+    float v = 0.f;
+    if (sl.group == gsl) v = sl.qjl ? hq[h * hstride + c] : sl.alpha * tq[h * tstride + c];
+    float mx = fabsf(v);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 8, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 4, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 2, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 32));
+    const int e = exponent_of(mx);  // the largest lies in [2^(e-1), 2^e)
+    float x = ldexpf(v, 1 - e);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t code = e2m3_of(x);
+      codes[s2][h][m][f] = (uint8_t)code;
+      x = (x - e2m3_value(code)) * kScoreDigitStep;
+    }
+    if (f == 0) escl[s2][h] = e;
+  }
+  __syncthreads();
+  // unit (slot, head, digit, dword)
+  for (int unit = tid; unit < nslots * kHT * 4 * 8; unit += kQtThreads) {
+    const int j = unit & 7, m = (unit >> 3) & 3, h = (unit >> 5) & 3, s2 = unit >> 7;
+    uint32_t w = 0u;
+    if (j < 6) {
+#pragma unroll
+      for (int f = 0; f < 32; ++f) {
+        const int bit = 6 * f - 32 * j;  // position of code f within dword j
+        const uint32_t code = codes[s2][h][m][f];
+        if (bit >= 0 && bit < 32)
+          w |= code << bit;
+        else if (bit < 0 && bit > -6)
+          w |= code >> (-bit);
+      }
+    } else if (j == 6) {
+      w = (uint32_t)max(127 + escl[s2][h] - 1 - 5 * m, 0);
+    }
+    a.aops[((int64_t)key * nslots + s2) * 512 + (16 * kb + 4 * h + m) * 8 + j] = w;
+  }
+}
+
+// Both transforms in one pass when S R is available: workgroup (key, 32-row
+// slice) forms rows of q~ = R q and q^ = (S R) q, the slice being one
+// 32-channel block of the score products, and writes the fp6 digit
+// operands of every slot for its block (write_block_operands).
 __device__ __forceinline__ void qfused_body(const Args& a, const int key, const int slice) {
   __shared__ float qts[kHT][kRowSlice], qhs[kHT][kRowSlice];
-  __shared__ float sc_mse[kHT], sc_qjl[kHT];
-  const int nk = a.nk, Hkv = a.Hkv, HT = a.HT, G = a.G, Hq = a.Hq, qbf16 = a.qbf16, nslots = a.nslots;
+  __shared__ uint8_t codes[kMaxSlots][kHT][4][32];
+  __shared__ int escl[kMaxSlots][kHT];
+  const int nk = a.nk, Hkv = a.Hkv, HT = a.HT, G = a.G, Hq = a.Hq, qbf16 = a.qbf16;
   const int k1ch = a.k[1].ch, k0d = a.k[0].d, k1d = a.k[1].d, k0p = a.k[0].prod, k1p = a.k[1].prod;
   const float* R0 = a.k[0].R;
   const float* R1 = a.k[1].R;
   const float* F0 = a.k[0].SR;
   const float* F1 = a.k[1].SR;
-  const float amax0 = a.k[0].amax, amax1 = a.k[1].amax;
   const int b = key / (Hkv * HT);
   const int g = (key / HT) % Hkv;
   const int ht = key % HT;
   const int h0 = g * G + ht * kHT;
   const int nh = min(kHT, G - ht * kHT);
   const int tid = threadIdx.x, cb = tid & 15;
-  const int i = slice * kRowSlice + (tid >> 4);
   const int gsl = ((nk > 1) & (slice * kRowSlice >= k1ch)) ? 1 : 0;
   const bool g1 = gsl == 1;
   const int d = g1 ? k1d : k0d, ch = g1 ? k1ch : 0;
@@ -306,16 +419,22 @@ __device__ __forceinline__ void qfused_body(const Args& a, const int key, const 
   const float* Fm = g1 ? F1 : F0;
   const bool on = 8 * cb < d;
   const int col = ch + min(8 * cb, d - 8);
-  const int r = i - ch;
 
   // every load unconditional and of one shape (a group without a sketch
-  // reads R in place of S R and ignores it), so that none waits on another
+  // reads R in place of S R and ignores it), so that none waits on another;
+  // thread t takes rows 16 half + t / 16 of the slice
   const float* Fsrc = prod ? Fm : Rm;
-  const float4* rr = reinterpret_cast<const float4*>(Rm + (int64_t)r * d + (col - ch));
-  const float4* fr = reinterpret_cast<const float4*>(Fsrc + (int64_t)r * d + (col - ch));
-  const float4 m0 = rr[0], m1 = rr[1];
-  float4 f0 = fr[0], f1 = fr[1];
-  float fmax = Fsrc[prod ? (int64_t)d * d : 0];
+  float4 m0[2], m1[2], f0[2], f1[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int r = slice * kRowSlice + 16 * hf + (tid >> 4) - ch;
+    const float4* rr = reinterpret_cast<const float4*>(Rm + (int64_t)r * d + (col - ch));
+    const float4* fr = reinterpret_cast<const float4*>(Fsrc + (int64_t)r * d + (col - ch));
+    m0[hf] = rr[0];
+    m1[hf] = rr[1];
+    f0[hf] = fr[0];
+    f1[hf] = fr[1];
+  }
   float x[kHT][8];
   if (qbf16) {
 #pragma unroll
@@ -339,80 +458,35 @@ __device__ __forceinline__ void qfused_body(const Args& a, const int key, const 
       x[h][4] = v.x; x[h][5] = v.y; x[h][6] = v.z; x[h][7] = v.w;
     }
   }
-  if (!prod) {
-    f0 = f1 = make_float4(0.f, 0.f, 0.f, 0.f);
-    fmax = 0.f;
-  }
-  float ot = 0.f, oh = 0.f, on2 = 0.f;
 #pragma unroll
-  for (int h = 0; h < kHT; ++h) {
-    const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    const float fv[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-    float t = 0.f, u = 0.f, n2 = 0.f;
+  for (int hf = 0; hf < 2; ++hf) {
+    float ot = 0.f, oh = 0.f;
+    const float mv[8] = {m0[hf].x, m0[hf].y, m0[hf].z, m0[hf].w, m1[hf].x, m1[hf].y, m1[hf].z, m1[hf].w};
+    const float fv[8] = {f0[hf].x, f0[hf].y, f0[hf].z, f0[hf].w, f1[hf].x, f1[hf].y, f1[hf].z, f1[hf].w};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      t = fmaf(mv[k], x[h][k], t);
-      u = fmaf(fv[k], x[h][k], u);
-      n2 = fmaf(x[h][k], x[h][k], n2);
-    }
-    const bool use = on && h < nh;
-    t = use ? t : 0.f;
-    u = use ? u : 0.f;
-    n2 = use ? n2 : 0.f;
-    // the 16 lanes of a row hold the 16 column blocks: row rotations sum them
-    t = row16_sum(t);
-    u = row16_sum(u);
-    n2 = row16_sum(n2);
-    if (cb == h) {
-      ot = t;
-      oh = u;
-      on2 = n2;
-    }
-  }
-  if (cb < kHT) {
-    qts[cb][tid >> 4] = ot;
-    qhs[cb][tid >> 4] = oh;
-    if ((tid >> 4) == 0) {  // |q| of head cb over the group's channels -> the two scales
-      const float qn = sqrtf(on2) * 1.001f;
-      const float mt = qn * (g1 ? amax1 : amax0), mh = qn * fmax;
-      const float sm = mt > 0.f ? ldexpf(1.f, 6 - exponent_of(mt)) : 1.f;
-      const float sq = mh > 0.f ? ldexpf(1.f, 6 - exponent_of(mh)) : 1.f;
-      sc_mse[cb] = sm;
-      sc_qjl[cb] = sq;
-      if (slice == ch / kRowSlice) {
-        a.ascale[(((int64_t)key * kHT + cb) * kMaxKG + gsl) * 2 + 0] = 1.f / sm;
-        a.ascale[(((int64_t)key * kHT + cb) * kMaxKG + gsl) * 2 + 1] = 1.f / sq;
+    for (int h = 0; h < kHT; ++h) {
+      float t = 0.f, u = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        t = fmaf(mv[k], x[h][k], t);
+        u = fmaf(fv[k], x[h][k], u);
       }
+      const bool use = on && h < nh;
+      // the 16 lanes of a row hold the 16 column blocks: row rotations sum them
+      t = row16_sum(use ? t : 0.f);
+      u = row16_sum(use && prod ? u : 0.f);
+      if (cb == h) {
+        ot = t;
+        oh = u;
+      }
+    }
+    if (cb < kHT) {
+      qts[cb][16 * hf + (tid >> 4)] = ot;
+      qhs[cb][16 * hf + (tid >> 4)] = oh;
     }
   }
   __syncthreads();
-  // unit (slot, head, r): coordinates c = 16 slice + r + 4 u, u = 0..3 (4
-  // consecutive operand bytes kappa0 + u of the head's 4 digit rows); slots
-  // of the other key group get zeros here
-  const int cg = slice >> 1;
-  for (int unit = tid; unit < nslots * kHT * 4; unit += kQtThreads) {
-    const int s2 = unit >> 4, h = (unit >> 2) & 3, rq = unit & 3;
-    const Slot sl = slot_of(a, s2);
-    const int kappa0 = 32 * cg + 8 * rq + 4 * (slice & 1);
-    const int gp = (kappa0 & 63) >> 4, byte0 = (kappa0 & 15) + 16 * (kappa0 >> 6);
-    const float sc = (sl.qjl ? sc_qjl[h] : sl.alpha * sc_mse[h]) * inv_v(rq);
-    uint32_t dw[4] = {0u, 0u, 0u, 0u};
-    if (sl.group == gsl) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float v = (sl.qjl ? qhs[h][rq + 4 * u] : qts[h][rq + 4 * u]) * sc;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t d8 = fp8_of(v);
-          v = (v - f32_of_fp8(d8)) * kDigitStep;
-          dw[m] |= d8 << (8 * u);
-        }
-      }
-    }
-    uint32_t* dst = a.aops + ((int64_t)key * nslots + s2) * 512;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) dst[(16 * gp + 4 * h + m) * 8 + byte0 / 4] = dw[m];
-  }
+  write_block_operands(a, key, slice, gsl, &qts[0][0], kRowSlice, &qhs[0][0], kRowSlice, codes, escl);
 }
 
 __global__ __launch_bounds__(kQtThreads) void qfused_kernel(Args a) { qfused_body(a, blockIdx.x, blockIdx.y); }
@@ -449,10 +523,10 @@ __global__ __launch_bounds__(kQtThreads) void qfused_step_kernel(Args a, StepApp
 
 template <bool PROJECT>
 __global__ __launch_bounds__(kQtThreads) void qtransform_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) float qts[kHT][kD];  // q~ of the slice's key group (project)
-  __shared__ float sc_mse[kHT], sc_qjl[kHT];
+  __shared__ __attribute__((aligned(16))) float qts[kHT][kD];  // q~ of the key (project)
   __shared__ float qhs[kHT][kRowSlice];
-  __shared__ float wred[kQtThreads / 64];
+  __shared__ uint8_t codes[kMaxSlots][kHT][4][32];
+  __shared__ int escl[kMaxSlots][kHT];
   // every argument field this kernel needs is read up front and
   // unconditionally (both groups), so the reads overlap instead of chaining
   const int nk = a.nk, Hkv = a.Hkv, HT = a.HT, G = a.G, Hq = a.Hq, qbf16 = a.qbf16;
@@ -465,19 +539,13 @@ __global__ __launch_bounds__(kQtThreads) void qtransform_kernel(Args a) {
   const void* qsrc = a.q;
   float* qt = a.qt;
   float* qh = a.qh;
-  float* srow = a.srow;
-  float* ascale = a.ascale;
-  uint32_t* aops = a.aops;
-  const int nslots = a.nslots;
-  const float amax0 = a.k[0].amax, amax1 = a.k[1].amax;
   const int key = blockIdx.x, slice = blockIdx.y;
   const int b = key / (Hkv * HT);
   const int g = (key / HT) % Hkv;
   const int ht = key % HT;
   const int h0 = g * G + ht * kHT;
   const int nh = min(kHT, G - ht * kHT);
-  const int tid = threadIdx.x, cb = tid & 15, lane = tid & 63, wv = tid >> 6;
-  const int i = slice * kRowSlice + (tid >> 4);  // output channel (stacked row)
+  const int tid = threadIdx.x, cb = tid & 15;
   // the slice lies in one key group (group sizes are multiples of 32)
   const int gsl = ((nk > 1) & (slice * kRowSlice >= k1ch)) ? 1 : 0;
   const bool g1 = gsl == 1;
@@ -487,20 +555,19 @@ __global__ __launch_bounds__(kQtThreads) void qtransform_kernel(Args a) {
   const float* Sm = g1 ? S1 : S0;
   const bool on = 8 * cb < d;
   const int col = ch + min(8 * cb, d - 8);  // clamped so that every load is in range
-  const int r = i - ch;
 
-  // this thread's 8 entries of row r of R (rotate) or S (project); the
-  // rotate launch also reads S to bound |S q~| by its row norms
-  float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0, s0v = m0, s1v = m0;
-  if (!PROJECT || prod) {
-    const float4* mr = reinterpret_cast<const float4*>((PROJECT ? Sm : Rm) + (int64_t)r * d + (col - ch));
-    m0 = mr[0];
-    m1 = mr[1];
-  }
-  if (!PROJECT && prod && key == 0) {
-    const float4* sr = reinterpret_cast<const float4*>(Sm + (int64_t)r * d + (col - ch));
-    s0v = sr[0];
-    s1v = sr[1];
+  // this thread's 8 entries of rows 16 half + t / 16 of the slice of R
+  // (rotate) or S (project)
+  float4 m0[2], m1[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    m0[hf] = m1[hf] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!PROJECT || prod) {
+      const int r = slice * kRowSlice + 16 * hf + (tid >> 4) - ch;
+      const float4* mr = reinterpret_cast<const float4*>((PROJECT ? Sm : Rm) + (int64_t)r * d + (col - ch));
+      m0[hf] = mr[0];
+      m1[hf] = mr[1];
+    }
   }
   float x[kHT][8];
   if (PROJECT) {
@@ -535,125 +602,50 @@ __global__ __launch_bounds__(kQtThreads) void qtransform_kernel(Args a) {
       x[h][4] = v.x; x[h][5] = v.y; x[h][6] = v.z; x[h][7] = v.w;
     }
   }
-  // (project) the slot table, read one entry per thread, and the S row-norm
-  // maxima of the group's slices, both in flight with the loads above
-  float srow_v = 0.f;
-  if (PROJECT) {
-    const int q = min(ch / kRowSlice + (tid & 7), (ch + d) / kRowSlice - 1);
-    srow_v = srow[q];
-  }
-  float acc[kHT];
 #pragma unroll
-  for (int h = 0; h < kHT; ++h) {
-    float s0 = m0.x * x[h][0], s1 = m0.y * x[h][1];
-    s0 = fmaf(m0.z, x[h][2], s0);
-    s1 = fmaf(m0.w, x[h][3], s1);
-    s0 = fmaf(m1.x, x[h][4], s0);
-    s1 = fmaf(m1.y, x[h][5], s1);
-    s0 = fmaf(m1.z, x[h][6], s0);
-    s1 = fmaf(m1.w, x[h][7], s1);
-    float v = on && h < nh ? s0 + s1 : 0.f;
-    v += __shfl_xor(v, 8, 16);
-    v += __shfl_xor(v, 4, 16);
-    v += __shfl_xor(v, 2, 16);
-    v += __shfl_xor(v, 1, 16);
-    acc[h] = v;
-  }
-  float out = acc[0];
+  for (int hf = 0; hf < 2; ++hf) {
+    const int i = slice * kRowSlice + 16 * hf + (tid >> 4);  // output channel (stacked row)
+    float acc[kHT];
 #pragma unroll
-  for (int h = 1; h < kHT; ++h)
-    if (cb == h) out = acc[h];
-  if (!PROJECT) {
-    if (cb < kHT) qt[((int64_t)key * kHT + cb) * kD + i] = out;
-    if (key == 0) {  // row norms of S in this slice (the same for every key)
-      float n2 = 0.f;
-      if (on && prod) {
-        n2 = s0v.x * s0v.x + s0v.y * s0v.y + s0v.z * s0v.z + s0v.w * s0v.w + s1v.x * s1v.x + s1v.y * s1v.y +
-             s1v.z * s1v.z + s1v.w * s1v.w;
-      }
-      n2 += __shfl_xor(n2, 8, 16);
-      n2 += __shfl_xor(n2, 4, 16);
-      n2 += __shfl_xor(n2, 2, 16);
-      n2 += __shfl_xor(n2, 1, 16);
-      const float mx = tqd::wave_max(n2);
-      if (lane == 0) wred[wv] = mx;
-      __syncthreads();
-      if (tid == 0) srow[slice] = sqrtf(fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3])));
+    for (int h = 0; h < kHT; ++h) {
+      float s0 = m0[hf].x * x[h][0], s1 = m0[hf].y * x[h][1];
+      s0 = fmaf(m0[hf].z, x[h][2], s0);
+      s1 = fmaf(m0[hf].w, x[h][3], s1);
+      s0 = fmaf(m1[hf].x, x[h][4], s0);
+      s1 = fmaf(m1[hf].y, x[h][5], s1);
+      s0 = fmaf(m1[hf].z, x[h][6], s0);
+      s1 = fmaf(m1[hf].w, x[h][7], s1);
+      float v = on && h < nh ? s0 + s1 : 0.f;
+      v += __shfl_xor(v, 8, 16);
+      v += __shfl_xor(v, 4, 16);
+      v += __shfl_xor(v, 2, 16);
+      v += __shfl_xor(v, 1, 16);
+      acc[h] = v;
     }
-    return;
+    float out = acc[0];
+#pragma unroll
+    for (int h = 1; h < kHT; ++h)
+      if (cb == h) out = acc[h];
+    if (!PROJECT) {
+      if (cb < kHT) qt[((int64_t)key * kHT + cb) * kD + i] = out;
+    } else if (cb < kHT) {
+      qh[((int64_t)key * kHT + cb) * kD + i] = prod ? out : 0.f;
+      qhs[cb][16 * hf + (tid >> 4)] = prod ? out : 0.f;
+    }
   }
+  if (!PROJECT) return;
 
-  // ---- project only: q^ rows and the operands (fp8 digits) of every slot
-  // for this slice's coordinates. Codebook slots: scale from the largest
-  // |q~| of the group times the largest |Walsh coefficient|. QJL slot: scale
-  // from the bound |(S q~)_c| <= |S_c| |q~| with the largest row norm of S.
-  if (cb < kHT) {
-    qh[((int64_t)key * kHT + cb) * kD + i] = prod ? out : 0.f;
-    qhs[cb][tid >> 4] = prod ? out : 0.f;
-  }
+  // ---- project only: the fp6 operands of every slot over this slice's
+  // block, from q~ (all of the key's channels, staged here) and the
+  // slice's rows of q^
   if ((tid >> 4) == 0 && on) {
 #pragma unroll
     for (int h = 0; h < kHT; ++h)
 #pragma unroll
       for (int k = 0; k < 8; ++k) qts[h][col + k] = x[h][k];
   }
-  // lanes 0..7 of each wave hold the (clamped) slices of the group
-  float smax = srow_v;
-  smax = fmaxf(smax, __shfl_xor(smax, 4, 8));
-  smax = fmaxf(smax, __shfl_xor(smax, 2, 8));
-  smax = fmaxf(smax, __shfl_xor(smax, 1, 8));
   __syncthreads();
-  {
-    // wave w: head w; max and norm over the group's channels
-    float mt = 0.f, n2 = 0.f;
-    for (int c = ch + lane; c < ch + d; c += 64) {
-      const float v = qts[wv][c];
-      mt = fmaxf(mt, fabsf(v));
-      n2 = fmaf(v, v, n2);
-    }
-    mt = tqd::wave_max(mt) * (g1 ? amax1 : amax0);
-    n2 = tqd::wave_sum(n2);
-    if (lane == 0) {
-      const float mq = sqrtf(n2) * smax * 1.0001f;  // the bound, with room for rounding
-      const float sm = mt > 0.f ? ldexpf(1.f, 5 - exponent_of(mt)) : 1.f;
-      const float sq = mq > 0.f ? ldexpf(1.f, 5 - exponent_of(mq)) : 1.f;
-      sc_mse[wv] = sm;
-      sc_qjl[wv] = sq;
-      if (slice == ch / kRowSlice) {
-        ascale[(((int64_t)key * kHT + wv) * kMaxKG + gsl) * 2 + 0] = 1.f / sm;
-        ascale[(((int64_t)key * kHT + wv) * kMaxKG + gsl) * 2 + 1] = 1.f / sq;
-      }
-    }
-  }
-  __syncthreads();
-  // unit (slot, head, r): coordinates c = 32 cg + r + 16 (slice & 1) + 4 u,
-  // u = 0..3, i.e. 4 consecutive operand bytes kappa0 + u of the head's 4
-  // digit rows; slots of the other key group get zeros here
-  const int cg = slice >> 1;
-  for (int unit = tid; unit < nslots * kHT * 4; unit += kQtThreads) {
-    const int s2 = unit >> 4, h = (unit >> 2) & 3, rr = unit & 3;
-    const Slot sl = slot_of(a, s2);
-    const int kappa0 = 32 * cg + 8 * rr + 4 * (slice & 1);
-    const int gp = (kappa0 & 63) >> 4, byte0 = (kappa0 & 15) + 16 * (kappa0 >> 6);
-    const float sc = (sl.qjl ? sc_qjl[h] : sl.alpha * sc_mse[h]) * inv_v(rr);
-    uint32_t dw[4] = {0u, 0u, 0u, 0u};
-    if (sl.group == gsl) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = 32 * cg + rr + 16 * (slice & 1) + 4 * u;
-        float v = (sl.qjl ? qhs[h][c - slice * kRowSlice] : qts[h][c]) * sc;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t d8 = fp8_of(v);
-          v = (v - f32_of_fp8(d8)) * kDigitStep;
-          dw[m] |= d8 << (8 * u);
-        }
-      }
-    }
-    uint32_t* dst = aops + ((int64_t)key * nslots + s2) * 512;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) dst[(16 * gp + 4 * h + m) * 8 + byte0 / 4] = dw[m];
-  }
+  write_block_operands(a, key, slice, gsl, &qts[0][slice * kRowSlice], kD, &qhs[0][0], kRowSlice, codes, escl);
 }
 
 // P consecutive 32-bit words with one vector load (P = 1..5).
@@ -940,11 +932,13 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   // they complete first
   const int key = bg * a.HT + ht;
   v8i aop[NS];
+  int esc[NS];  // E8M0 scale of this lane's operand row and K block, per slot
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const v4i* src = reinterpret_cast<const v4i*>(a.aops + (((int64_t)key * NS + s) * 64 + lane) * 8);
     const v4i lo = src[0], hi = src[1];
-    aop[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    aop[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+    esc[s] = hi[2];
   }
   // ---- the first chunk's loads: clamped to the cache's extent (T_max) rather
   // than to the sequence's length, so that they need no value read from
@@ -953,18 +947,6 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   VChunk vv;
   load_k<NK, NV, KB0 + KP0, KB1 + KP1, KP0, KP1>(kA, ka, na, ts - tok_base, rel_first_last, w, lane);
   load_v<NV, VB0, VB1>(vv, va, ts - tok_base, lane);
-  // E8M0 scales of this lane's query-operand rows (row lane % 16 = 4 head +
-  // digit): the digit's weight 16^-digit times the head's inverse operand
-  // scale, a power of two (the query transforms choose it so), per (group,
-  // class); the score MFMAs then return the estimate's terms directly.
-  int esc_mse[NK], esc_qjl[NK];
-#pragma unroll
-  for (int gi = 0; gi < NK; ++gi) {
-    const int hr = (lane & 15) >> 2, dg = lane & 3;
-    const float2 sc = *reinterpret_cast<const float2*>(a.ascale + (((int64_t)key * kHT + hr) * kMaxKG + gi) * 2);
-    esc_mse[gi] = max((int)(__float_as_uint(sc.x) >> 23) - 4 * dg, 0);
-    esc_qjl[gi] = max((int)(__float_as_uint(sc.y) >> 23) - 4 * dg, 0);
-  }
   // the sequence length, read through a buffer resource that is empty when
   // no lengths are given (the read then returns 0 without touching memory),
   // so that no branch holds the loads above behind it
@@ -980,7 +962,7 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   // constant parts of the fp4 encoding, per (group, class); scales of this lane's head
   float cm[NK], cq[NK], gam[NK];
   {
-    const v8i cop = const_operand();
+    const v8i khi = key_const_hi(), klo = key_const_lo();
 #pragma unroll
     for (int gi = 0; gi < NK; ++gi) {
       cm[gi] = cq[gi] = 0.f;
@@ -990,7 +972,7 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
     for (int s = 0; s < NS; ++s) {
       const int gi = s < NS0 ? 0 : 1;
       const bool q = (gi == 0) ? (KP0 && s == NS0 - 1) : (KP1 && s == NS - 1);
-      const float c4 = 0.25f * sum4(mfma_fp8_fp4_sa(aop[s], cop, v4f{0.f, 0.f, 0.f, 0.f}, q ? esc_qjl[gi] : esc_mse[gi]));
+      const float c4 = sum4(mfma_fp6_fp4_sa(aop[s], khi, mfma_fp6_fp4_sa(aop[s], klo, v4f{0.f, 0.f, 0.f, 0.f}, esc[s]), esc[s]));
       if (q)
         cq[gi] += c4;
       else
@@ -1045,9 +1027,9 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
 #pragma unroll
         for (int p = 0; p < 5; ++p)
           if ((m >> p) & 1) word ^= wd[p];
-        dm[0] = mfma_fp8_fp4_sa(aop[t], expand_bits(word), dm[0], esc_mse[0]);
+        dm[0] = mfma_fp6_fp4_sa(aop[t], expand_key_bits(word), dm[0], esc[t]);
       }
-      if constexpr (KP0) dq[0] = mfma_fp8_fp4_sa(aop[NS0 - 1], expand_bits(wd[KB0]), dq[0], esc_qjl[0]);
+      if constexpr (KP0) dq[0] = mfma_fp6_fp4_sa(aop[NS0 - 1], expand_key_bits(wd[KB0]), dq[0], esc[NS0 - 1]);
       if constexpr (KB1 > 0) {
 #pragma unroll
         for (int t = 0; t < n_odd(KB1); ++t) {
@@ -1056,9 +1038,9 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
 #pragma unroll
           for (int p = 0; p < 5; ++p)
             if ((m >> p) & 1) word ^= wd[p];
-          dm[NK - 1] = mfma_fp8_fp4_sa(aop[NS0 + t], expand_bits(word), dm[NK - 1], esc_mse[NK - 1]);
+          dm[NK - 1] = mfma_fp6_fp4_sa(aop[NS0 + t], expand_key_bits(word), dm[NK - 1], esc[NS0 + t]);
         }
-        if constexpr (KP1) dq[NK - 1] = mfma_fp8_fp4_sa(aop[NS - 1], expand_bits(wd[KB1]), dq[NK - 1], esc_qjl[NK - 1]);
+        if constexpr (KP1) dq[NK - 1] = mfma_fp6_fp4_sa(aop[NS - 1], expand_key_bits(wd[KB1]), dq[NK - 1], esc[NS - 1]);
       }
       float sc = 0.f;
 #pragma unroll
@@ -1638,24 +1620,18 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   // query operands of every slot and their scales (from the query transform)
   const int key = bg * a.HT + ht;
   v8i aop[NS];
+  int esc[NS];  // E8M0 scale of this lane's operand row and K block, per slot
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const v4i* src = reinterpret_cast<const v4i*>(a.aops + (((int64_t)key * NS + s) * 64 + lane) * 8);
     const v4i lo = src[0], hi = src[1];
-    aop[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    aop[s] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+    esc[s] = hi[2];
   }
   PKeys<NK> kA;
   PVals<NV> vd;
   pload_keys<NK, P0, P1, KP0, KP1>(kA, ka, na, ts - tok_base, rel_first_last, w, lane, kg1);
   pload_vnorms<NV>(vd, na, ts - tok_base, rel_first_last, w, lane);
-  int esc_mse[NK], esc_qjl[NK];
-#pragma unroll
-  for (int gi = 0; gi < NK; ++gi) {
-    const int hr = (lane & 15) >> 2, dg = lane & 3;
-    const float2 sc = *reinterpret_cast<const float2*>(a.ascale + (((int64_t)key * kHT + hr) * kMaxKG + gi) * 2);
-    esc_mse[gi] = max((int)(__float_as_uint(sc.x) >> 23) - 4 * dg, 0);
-    esc_qjl[gi] = max((int)(__float_as_uint(sc.y) >> 23) - 4 * dg, 0);
-  }
   const uint32_t lraw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
       make_rsrc(a.seq_lens, a.seq_lens ? (uint32_t)(4 * a.B) : 0u), 4u * (uint32_t)b, 0u, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -1669,7 +1645,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   v4f cinit_m[NK], cinit_q[NK];
   float gam[NK];
   {
-    const v8i cop = const_operand();
+    const v8i khi = key_const_hi(), klo = key_const_lo();
 #pragma unroll
     for (int gi = 0; gi < NK; ++gi) {
       cinit_m[gi] = cinit_q[gi] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -1679,11 +1655,11 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     for (int s = 0; s < NS; ++s) {
       const int gi = s < NS0 ? 0 : 1;
       const bool q = (gi == 0) ? (KP0 && s == NS0 - 1) : (KP1 && s == NS - 1);
-      const v4f c = mfma_fp8_fp4_sa(aop[s], cop, v4f{0.f, 0.f, 0.f, 0.f}, q ? esc_qjl[gi] : esc_mse[gi]);
+      const v4f c = mfma_fp6_fp4_sa(aop[s], khi, mfma_fp6_fp4_sa(aop[s], klo, v4f{0.f, 0.f, 0.f, 0.f}, esc[s]), esc[s]);
       if (q)
-        cinit_q[gi] -= 0.25f * c;
+        cinit_q[gi] -= c;
       else
-        cinit_m[gi] -= 0.25f * c;
+        cinit_m[gi] -= c;
     }
   }
   // fp4 register of this lane's tokens in the value step: token t of a
@@ -1769,9 +1745,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
           for (int p = 0; p < 5; ++p)
             if ((m >> p) & 1) word ^= wd[p];
-          dm[0] = mfma_fp8_fp4_sa(aop[t], expand_bits(word), dm[0], esc_mse[0]);
+          dm[0] = mfma_fp6_fp4_sa(aop[t], expand_key_bits(word), dm[0], esc[t]);
         }
-        if constexpr (KP0) dq[0] = mfma_fp8_fp4_sa(aop[NS0 - 1], expand_bits(wd[KB0]), dq[0], esc_qjl[0]);
+        if constexpr (KP0) dq[0] = mfma_fp6_fp4_sa(aop[NS0 - 1], expand_key_bits(wd[KB0]), dq[0], esc[NS0 - 1]);
         if constexpr (KB1 > 0) {
 #pragma unroll
           for (int t = 0; t < n_odd(KB1); ++t) {
@@ -1780,10 +1756,10 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
             for (int p = 0; p < 5; ++p)
               if ((m >> p) & 1) word ^= wd[p];
-            dm[NK - 1] = mfma_fp8_fp4_sa(aop[NS0 + t], expand_bits(word), dm[NK - 1], esc_mse[NK - 1]);
+            dm[NK - 1] = mfma_fp6_fp4_sa(aop[NS0 + t], expand_key_bits(word), dm[NK - 1], esc[NS0 + t]);
           }
           if constexpr (KP1)
-            dq[NK - 1] = mfma_fp8_fp4_sa(aop[NS - 1], expand_bits(wd[KB1]), dq[NK - 1], esc_qjl[NK - 1]);
+            dq[NK - 1] = mfma_fp6_fp4_sa(aop[NS - 1], expand_key_bits(wd[KB1]), dq[NK - 1], esc[NS - 1]);
         }
         float sc = 0.f;
 #pragma unroll

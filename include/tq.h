@@ -245,11 +245,11 @@ size_t tq_decode_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B
  *   scores_out NULL or [B, Hq, T_max] fp32: the raw estimates s_t (t < len)
  *   ws, ws_bytes: device workspace of at least tq_decode_workspace_bytes.
  * Keys must use TQ_LAYOUT_KEYS, values TQ_LAYOUT_VALUES and TQ_MSE.
- * Accumulation is fp32 (operands as fp8 digits: four for the query, three for
- * the softmax weights); measured against an fp64 evaluation of the same codes,
- * outputs are within 5.1e-4 (normwise, per query head) and scores within
- * 1.2e-4 of the row's largest score across the test cases, inside the 2e-3
- * acceptance bound. */
+ * Accumulation is fp32 (operands as digits: four fp6 digits per 32-channel
+ * block for the query, three fp8 digits for the softmax weights); measured
+ * against an fp64 evaluation of the same codes, outputs are within 4.9e-4
+ * (normwise, per query head) and scores within 3.4e-4 of the row's largest
+ * score across the test cases, inside the 2e-3 acceptance bound. */
 int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype,
                    int B, int Hq, int Hkv, int T_max, const int32_t* seq_lens, float scale,
                    float* out, float* scores_out, void* ws, size_t ws_bytes, void* stream);
