@@ -41,7 +41,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 METRIC = "compressed-KV decode attn HBM GB/s (% of peak); quantize tokens/s"
 # the decode's arithmetic: query and softmax-weight digits in fp8 e4m3 times
 # fp4-encoded code bit-planes on the matrix cores, fp32 accumulation
-DECODE_DTYPE = "fp8e4m3 x fp4 mfma, fp32 accumulate"
+DECODE_DTYPE = "fp6e2m3 (scores) and fp8e4m3 (value sums) x fp4 mfma, fp32 accumulate"
 
 
 def log(*a):

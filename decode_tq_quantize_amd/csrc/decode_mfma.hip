@@ -353,12 +353,8 @@ __device__ __forceinline__ void write_block_operands(const Args& a, int key, int
     const int c = 4 * (f & 7) + (f >> 3);
     float v = 0.f;
     if (sl.group == gsl) v = sl.qjl ? hq[h * hstride + c] : sl.alpha * tq[h * tstride + c];
-    float mx = fabsf(v);
+    float mx = row16_max(fabsf(v));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 32));
-    mx = fmaxf(mx, __shfl_xor(mx, 8, 32));
-    mx = fmaxf(mx, __shfl_xor(mx, 4, 32));
-    mx = fmaxf(mx, __shfl_xor(mx, 2, 32));
-    mx = fmaxf(mx, __shfl_xor(mx, 1, 32));
     const int e = exponent_of(mx);  // the largest lies in [2^(e-1), 2^e)
     float x = ldexpf(v, 1 - e);
 #pragma unroll
@@ -370,24 +366,25 @@ __device__ __forceinline__ void write_block_operands(const Args& a, int key, int
     if (f == 0) escl[s2][h] = e;
   }
   __syncthreads();
-  // unit (slot, head, digit, dword)
-  for (int unit = tid; unit < nslots * kHT * 4 * 8; unit += kQtThreads) {
-    const int j = unit & 7, m = (unit >> 3) & 3, h = (unit >> 5) & 3, s2 = unit >> 7;
-    uint32_t w = 0u;
-    if (j < 6) {
+  // unit (slot, head, digit): the row's 32 codes packed into dwords 0..5,
+  // its scale into dword 6
+  for (int unit = tid; unit < nslots * kHT * 4; unit += kQtThreads) {
+    const int m = unit & 3, h = (unit >> 2) & 3, s2 = unit >> 4;
+    const uint4* src = reinterpret_cast<const uint4*>(&codes[s2][h][m][0]);
+    const uint4 c0 = src[0], c1 = src[1];
+    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int f = 0; f < 32; ++f) {
-        const int bit = 6 * f - 32 * j;  // position of code f within dword j
-        const uint32_t code = codes[s2][h][m][f];
-        if (bit >= 0 && bit < 32)
-          w |= code << bit;
-        else if (bit < 0 && bit > -6)
-          w |= code >> (-bit);
-      }
-    } else if (j == 6) {
-      w = (uint32_t)max(127 + escl[s2][h] - 1 - 5 * m, 0);
+    for (int f = 0; f < 32; ++f) {
+      const uint32_t code = (cw[f >> 2] >> (8 * (f & 3))) & 63u;
+      const int bit = 6 * f;
+      w[bit >> 5] |= code << (bit & 31);
+      if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
     }
-    a.aops[((int64_t)key * nslots + s2) * 512 + (16 * kb + 4 * h + m) * 8 + j] = w;
+    w[6] = (uint32_t)max(127 + escl[s2][h] - 1 - 5 * m, 0);
+    uint4* dst = reinterpret_cast<uint4*>(a.aops + ((int64_t)key * nslots + s2) * 512 + (16 * kb + 4 * h + m) * 8);
+    dst[0] = uint4{w[0], w[1], w[2], w[3]};
+    dst[1] = uint4{w[4], w[5], w[6], w[7]};
   }
 }
 
@@ -397,7 +394,7 @@ __device__ __forceinline__ void write_block_operands(const Args& a, int key, int
 // operands of every slot for its block (write_block_operands).
 __device__ __forceinline__ void qfused_body(const Args& a, const int key, const int slice) {
   __shared__ float qts[kHT][kRowSlice], qhs[kHT][kRowSlice];
-  __shared__ uint8_t codes[kMaxSlots][kHT][4][32];
+  __shared__ __attribute__((aligned(16))) uint8_t codes[kMaxSlots][kHT][4][32];
   __shared__ int escl[kMaxSlots][kHT];
   const int nk = a.nk, Hkv = a.Hkv, HT = a.HT, G = a.G, Hq = a.Hq, qbf16 = a.qbf16;
   const int k1ch = a.k[1].ch, k0d = a.k[0].d, k1d = a.k[1].d, k0p = a.k[0].prod, k1p = a.k[1].prod;
@@ -525,7 +522,7 @@ template <bool PROJECT>
 __global__ __launch_bounds__(kQtThreads) void qtransform_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) float qts[kHT][kD];  // q~ of the key (project)
   __shared__ float qhs[kHT][kRowSlice];
-  __shared__ uint8_t codes[kMaxSlots][kHT][4][32];
+  __shared__ __attribute__((aligned(16))) uint8_t codes[kMaxSlots][kHT][4][32];
   __shared__ int escl[kMaxSlots][kHT];
   // every argument field this kernel needs is read up front and
   // unconditionally (both groups), so the reads overlap instead of chaining
