@@ -381,7 +381,15 @@ __device__ __forceinline__ void write_block_operands(const Args& a, int key, int
       w[bit >> 5] |= code << (bit & 31);
       if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
     }
-    w[6] = (uint32_t)max(127 + escl[s2][h] - 1 - 5 * m, 0);
+    // a digit whose scale would fall below E8M0's 2^-127 (blocks whose
+    // largest magnitude is under about 2^-110) is left out rather than
+    // weighted wrongly
+    const int sc = 127 + escl[s2][h] - 1 - 5 * m;
+    if (sc < 0) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) w[i] = 0u;
+    }
+    w[6] = (uint32_t)max(sc, 0);
     uint4* dst = reinterpret_cast<uint4*>(a.aops + ((int64_t)key * nslots + s2) * 512 + (16 * kb + 4 * h + m) * 8);
     dst[0] = uint4{w[0], w[1], w[2], w[3]};
     dst[1] = uint4{w[4], w[5], w[6], w[7]};

@@ -249,7 +249,11 @@ size_t tq_decode_workspace_bytes(const tq_kv_desc* k, const tq_kv_desc* v, int B
  * block for the query, three fp8 digits for the softmax weights); measured
  * against an fp64 evaluation of the same codes, outputs are within 4.9e-4
  * (normwise, per query head) and scores within 3.4e-4 of the row's largest
- * score across the test cases, inside the 2e-3 acceptance bound. */
+ * score across the test cases, inside the 2e-3 acceptance bound. Each
+ * 32-channel block of a query head is scaled by its own power of two, so the
+ * bound holds for any mix of magnitudes down to blocks whose largest entry is
+ * about 2^-110 (below that the trailing digits, and then the block, drop to
+ * zero). */
 int tq_decode_attn(const tq_kv_desc* k, const tq_kv_desc* v, const void* q, tq_dtype q_dtype,
                    int B, int Hq, int Hkv, int T_max, const int32_t* seq_lens, float scale,
                    float* out, float* scores_out, void* ws, size_t ws_bytes, void* stream);

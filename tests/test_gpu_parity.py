@@ -598,6 +598,35 @@ def test_decode_ignores_rows_past_the_length(bits, split):
                      [otq.Group(s[0], gq.oq, c) for s, gq, c in zip(specs_v, vq, vcodes)], qry, Hkv, lens)
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_decode_query_dynamic_range(split):
+    # the score operands carry one power-of-two scale per 32-channel block of
+    # each query head: a head of zeros, a zero block beside normal ones, a
+    # block whose largest entry is 1e4 times the rest, and heads scaled by
+    # 2^-100 and 2^100 must all score like the oracle
+    print(f"decode query dynamic range: groups {2 if split else 1}", flush=True)
+    B, Hq, Hkv, T, d = 2, 8, 2, 512, 128
+    lens = [512, 77]
+    K, V = make_kv(B, Hkv, T, d, seed=41)
+    specs_k, specs_v = SPECS_SPLIT if split else SPECS_ONE
+    kq, kcodes = _groups(specs_k, K, "keys")
+    vq, vcodes = _groups(specs_v, V, "values")
+    kcs = [Cache(gq, specs_k[i][0], kcodes[i], T, "keys") for i, gq in enumerate(kq)]
+    vcs = [Cache(gq, specs_v[i][0], vcodes[i], T, "values") for i, gq in enumerate(vq)]
+    qry = synth.rng(41, 32).standard_normal((B, Hq, d)).astype(np.float32)
+    qry[0, 0] = 0.0
+    qry[0, 1, 32:64] = 0.0
+    qry[0, 2, 64:96] *= 1e-4
+    qry[0, 2, 70] = 3.0
+    qry[1, 3] *= np.float32(2.0 ** -100)
+    qry[1, 5] *= np.float32(2.0 ** 100)
+    out, sc = run_decode(kcs, vcs, qry, Hkv, T, lens, "f32")
+    assert np.isfinite(out).all()
+    assert np.all(sc[0, 0, :lens[0]] == 0.0)
+    check_decode(out, sc, [otq.Group(s[0], gq.oq, c) for s, gq, c in zip(specs_k, kq, kcodes)],
+                 [otq.Group(s[0], gq.oq, c) for s, gq, c in zip(specs_v, vq, vcodes)], qry, Hkv, lens)
+
+
 @pytest.mark.parametrize("bits", [0x7E00, 0x8001])
 def test_paged_decode_ignores_rows_past_the_length(bits):
     print(f"paged decode rows past the length: norm bits {bits:#06x}", flush=True)
