@@ -120,8 +120,6 @@ struct Args {
   float* scores_out;
   float* qt;         // [keys][4 heads][kD] q~ = R q per key group
   float* qh;         // [keys][4 heads][kD] q^ = S q~ (PROD groups, else 0)
-  float* srow;       // [kD / kRowSlice] largest row norm of S in each row slice
-  float* ascale;     // [keys][4 heads][kMaxKG][2] inverse operand scales (codebook, QJL)
   uint32_t* aops;    // [keys][nslots][64 lanes][8 dwords] query operands of every slot
   float* partial;    // [B * Hq][splits][kD + 2] (max, sum, rotated accumulator)
   float* out;
@@ -868,7 +866,7 @@ __global__ __launch_bounds__(kThreads, (KB0 >= 4 && VB0 >= 4) ? 1 : 2) void deco
   const int split = blockIdx.x, ht = blockIdx.y, bg = blockIdx.z;
   // the argument fields that the first loads depend on, fetched in one batch
   // (left to itself the compiler fetches them in several dependent rounds)
-  asm volatile("" ::"s"(a.Hkv), "s"(a.HT), "s"(a.split_len), "s"(a.T_max), "s"(a.aops), "s"(a.ascale),
+  asm volatile("" ::"s"(a.Hkv), "s"(a.HT), "s"(a.split_len), "s"(a.T_max), "s"(a.aops),
                "s"(a.k[0].packed), "s"(a.k[0].norm), "s"(a.k[0].rnorm), "s"(a.k[0].seq_stride), "s"(a.k[0].d),
                "s"(a.k[0].ch), "s"(a.v[0].packed), "s"(a.v[0].norm), "s"(a.v[0].seq_stride), "s"(a.v[0].d),
                "s"(a.v[0].B), "s"(a.v[0].ch), "s"(a.seq_lens), "s"(a.B), "s"(a.G), "s"(a.block_table));
@@ -1568,7 +1566,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6) ^ (lin & 1);
   const int hl = lane >> 4, tl = lane & 15;
   const int split = blockIdx.x, ht = blockIdx.y, bg = blockIdx.z;
-  asm volatile("" ::"s"(a.Hkv), "s"(a.HT), "s"(a.split_len), "s"(a.T_max), "s"(a.aops), "s"(a.ascale),
+  asm volatile("" ::"s"(a.Hkv), "s"(a.HT), "s"(a.split_len), "s"(a.T_max), "s"(a.aops),
                "s"(a.k[0].packed), "s"(a.k[0].norm), "s"(a.k[0].rnorm), "s"(a.k[0].seq_stride), "s"(a.k[0].d),
                "s"(a.k[0].ch), "s"(a.v[0].packed), "s"(a.v[0].norm), "s"(a.v[0].seq_stride), "s"(a.v[0].d),
                "s"(a.v[0].B), "s"(a.v[0].ch), "s"(a.seq_lens), "s"(a.B), "s"(a.G), "s"(a.block_table));
@@ -2151,10 +2149,9 @@ DecodePlan plan_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, int B, int
   int slots = 0;
   for (int i = 0; i < k.n_groups; ++i) slots += n_odd(k.g[i].q.mse_bits) + (k.g[i].q.variant == TQ_PROD ? 1 : 0);
   const size_t keys = (size_t)B * Hkv * HT;
-  // q~, q^ [keys][4][kD]; S row-norm maxima [kD / 16]; inverse scales
-  // [keys][4][kMaxKG][2]; operands [keys][slots][512]; then the split
+  // q~, q^ [keys][4][kD]; operands [keys][slots][512]; then the split
   // partials
-  p.qprep_floats = 2 * keys * kHT * kD + kD / kRowSlice + keys * kHT * kMaxKG * 2 + keys * slots * 512;
+  p.qprep_floats = 2 * keys * kHT * kD + keys * slots * 512;
   p.qprep_floats = (p.qprep_floats + 3) / 4 * 4;
   p.partial_floats = (size_t)B * Hq * p.splits * (kD + 2);
   return p;
@@ -2240,9 +2237,7 @@ hipError_t launch_decode_mfma(const tq_kv_desc& k, const tq_kv_desc& v, const vo
   float* wsf = static_cast<float*>(ws);
   a.qt = wsf;
   a.qh = a.qt + keys * kHT * kD;
-  a.srow = a.qh + keys * kHT * kD;
-  a.ascale = a.srow + kD / kRowSlice;
-  a.aops = reinterpret_cast<uint32_t*>(a.ascale + keys * kHT * kMaxKG * 2);
+  a.aops = reinterpret_cast<uint32_t*>(a.qh + keys * kHT * kD);
   a.partial = wsf + plan.qprep_floats;
   a.out = out;
   const dim3 qgrid((unsigned)keys, kD / kRowSlice);
